@@ -1,0 +1,221 @@
+"""Benchmark: KDA chunked prefill (and decode) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+A step is one kda_chunk_fwd call over the prefill workload B=4, H=16, T=4096,
+dk=dv=128, bf16 q/k/v/g/beta, fp32 initial and final states (every prefill row
+of the hot path: decay factors, intra-chunk products, UT transform, inter-chunk
+state propagation, state in/out).  W untimed steps, then K timed steps between
+two device synchronisations; inputs are resident in HBM before timing starts
+and two input sets alternate so consecutive steps do not reuse cached inputs.
+The decode row (single-token update of 256 x 32 fp32 states, d=128, 64
+consecutive kda_decode_step calls) is timed in the same run and reported in the
+"decode" object.  Kernel durations come from HIP events recorded on the stream
+the library launches on; "roofline" relates the prefill kernel's algorithmic
+HBM bytes to its average duration.  "cpu_baseline" times the fp64 CPU oracle on
+a bounded sample of the same workload.  One JSON line is printed.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
+CHUNK = 64
+METRIC = "KDA prefill tokens/s + % bf16 MFMA peak; decode state GB/s + % HBM peak"
+
+
+def prefill_bytes(B, T, H, d, elt, state_in=True, state_out=True):
+    """Algorithmic HBM bytes of one prefill: q, k, g, v, beta read once, out written
+    once, states read/written once (per token-head (3d + 2d + 1) * elt)."""
+    tok = B * T * H * (5 * d + 1) * elt
+    st = B * H * d * d * 4 * (int(state_in) + int(state_out))
+    return tok + st
+
+
+def prefill_flops(B, T, H, d):
+    """Triangle-aware flops of the chunked algorithm as implemented, per token-head:
+    Cd (key Gram) + Cd (query-key) + 4d^2 ([Q;K] S) + Cd (T X) + Cd (M Delta)
+    + 2d^2 (K^T Delta) + C^2/3 (triangular inverse) = 4Cd + 6d^2 + C^2/3; the
+    full-rectangle count doubles the four triangular products: 8Cd + 6d^2 + C^2/3."""
+    C = CHUNK
+    tri = 4 * C * d + 6 * d * d + C * C / 3
+    full = 8 * C * d + 6 * d * d + C * C / 3
+    n = B * T * H
+    return n * tri, n * full
+
+
+def decode_bytes(B, H, d, elt):
+    """Per step: the fp32 state read and written once, plus the token's inputs/output."""
+    state = B * H * d * d * 4 * 2
+    return state, state + B * H * (5 * d + 1) * elt
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-reps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the KDA path here has no multi-GPU mode "
+              "(sequences and heads shard across GPUs with no communication). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from gated_delta_rule_102_amd import inputs as kin
+    from gated_delta_rule_102_amd import kda
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    kda.load_library()
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w = kin.WORKLOADS["prefill_4x4096"]
+    B, T, H, d = w.B, w.T, w.H, w.dk
+    sets = [kin.make_workload(w, device=dev, seed=w.seed + i) for i in range(2)]
+    outs = [torch.empty((B, T, H, d), dtype=w.dtype, device=dev) for _ in sets]
+    finals = [torch.empty((B, H, d, d), dtype=torch.float32, device=dev) for _ in sets]
+    scale = w.scale_value()
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        s = sets[i % 2]
+        kda.kda_chunk_fwd(s["q"], s["k"], s["v"], s["g"], s["beta"], scale,
+                          s["initial_state"], out=outs[i % 2], final_state=finals[i % 2])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    kern_avg_s = sum(kern_ms) / len(kern_ms) / 1e3
+
+    tokens = B * T
+    value = tokens * args.steps / wall
+    nbytes = prefill_bytes(B, T, H, d, 2)
+    fl_tri, fl_full = prefill_flops(B, T, H, d)
+    achieved_gbs = nbytes / kern_avg_s / 1e9
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill_4x4096", "B": B, "T": T, "H": H, "dk": d, "dv": d,
+                   "chunk": CHUNK, "state": "fp32, initial ~0.1 N(0,1), final returned",
+                   "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "prefill_kernel<128,32,bf16>", "kernel_ms": kern_avg_s * 1e3,
+                     "algorithmic_bytes": nbytes},
+        "prefill": {
+            "kernel_ms_avg": kern_avg_s * 1e3, "kernel_ms_min": min(kern_ms),
+            "token_heads_per_s": tokens * H / kern_avg_s,
+            "tflops_tri": fl_tri / kern_avg_s / 1e12, "tflops_full": fl_full / kern_avg_s / 1e12,
+            "mfma_frac_tri": fl_tri / kern_avg_s / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+            "mfma_frac_full": fl_full / kern_avg_s / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+            "flop_convention": "tri = 4Cd + 6d^2 + C^2/3 per token-head (C=64); "
+                               "full = 8Cd + 6d^2 + C^2/3",
+        },
+    }
+    del sets, outs, finals
+    torch.cuda.empty_cache()
+
+    if not args.no_decode:
+        wd = kin.WORKLOADS["decode_256x32"]
+        dd = kin.make_decode(wd.steps, wd.B, wd.H, wd.dk, wd.dv, dtype=wd.dtype, seed=wd.seed,
+                             device=dev)
+        state = dd["state"]
+        dout = torch.empty((wd.B, wd.H, wd.dv), dtype=wd.dtype, device=dev)
+        per_step = [dd[x].unbind(0) for x in ("q", "k", "v", "g", "beta")]
+
+        def dstep(s):
+            kda.kda_decode_step(per_step[0][s], per_step[1][s], per_step[2][s], per_step[3][s],
+                                per_step[4][s], state, scale=wd.scale_value(), out=dout)
+
+        for s in range(4):
+            dstep(s)
+        torch.cuda.synchronize()
+        dev_ms = []
+        walls = []
+        for rep in range(args.decode_reps):
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(wd.steps)]
+            torch.cuda.synchronize()
+            tw = time.perf_counter()
+            for s in range(wd.steps):
+                evs[s][0].record(stream)
+                dstep(s)
+                evs[s][1].record(stream)
+            torch.cuda.synchronize()
+            walls.append(time.perf_counter() - tw)
+            dev_ms += [a.elapsed_time(b) for a, b in evs]
+        step_s = sum(dev_ms) / len(dev_ms) / 1e3
+        sb, tb = decode_bytes(wd.B, wd.H, wd.dk, 2)
+        result["decode"] = {
+            "workload": "decode_256x32", "B": wd.B, "H": wd.H, "d": wd.dk,
+            "steps_per_rep": wd.steps, "reps": args.decode_reps,
+            "kernel_us_avg": step_s * 1e6,
+            "state_GBps": sb / step_s / 1e9, "total_GBps": tb / step_s / 1e9,
+            "hbm_frac": tb / step_s / 1e9 / HBM_PEAK_GBS,
+            "wall_ms_per_64_steps": min(walls) * 1e3,
+        }
+        del dd, state
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        from oracle import oracle_forward  # the CPU baseline leg may load the oracle
+        cores = max(1, min(os.cpu_count() or 1, 16))
+        wcpu = kin.make_workload(w, device=dev)
+        npairs = 2 * cores
+        pairs = [(i % B, (i * 7) % H) for i in range(npairs)]
+        qc, kc, vc, gc, bc = (wcpu[x].cpu() for x in ("q", "k", "v", "g", "beta"))
+        s0 = wcpu["initial_state"].cpu()
+        tc = time.perf_counter()
+        oracle_forward(qc, kc, vc, gc, bc, scale, B=B, T=T, initial_state=s0, pairs=pairs,
+                       store_out=True, nthreads=cores)
+        cpu_s = time.perf_counter() - tc
+        result["cpu_baseline"] = {
+            "value": npairs * T / H / cpu_s, "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{npairs} of the {B * H} (sequence, head) pairs of prefill_4x4096 at "
+                      f"full length T={T} (fp64 sequential recurrence, OpenMP over pairs); "
+                      f"rate scaled to tokens/s of all {H} heads; {cpu_s:.2f} s wall",
+        }
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,18 @@
+"""Kimi Delta Attention (KDA) for AMD Instinct MI355X (gfx950).
+
+The compute path is ``libkda.so`` (hand-written HIP kernels behind a C ABI,
+declared in ``include/kda.h``); :mod:`gated_delta_rule_102_amd.kda` is its thin
+Python binding and :mod:`gated_delta_rule_102_amd.inputs` draws seeded inputs.
+"""
+from .kda import (  # noqa: F401
+    KDAError,
+    chunk_fwd,
+    chunk_fwd_varlen,
+    decode_step,
+    kda_abi_version,
+    kda_chunk_fwd,
+    kda_chunk_fwd_varlen,
+    kda_decode_step,
+    kda_status_string,
+    load_library,
+)

@@ -1,0 +1,148 @@
+// C ABI of libkda.so: argument checks, then one kernel launch on the caller's
+// stream.  The contract of every entry point is documented in include/kda.h.
+
+#include "kda.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <atomic>
+#include <initializer_list>
+#include <cstdint>
+#include <cstring>
+
+#include "kda_launch.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = not checked yet, 1 = gfx950, -1 = another architecture.
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return KDA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return KDA_ERR_NO_DEVICE;
+  int state = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return KDA_ERR_HIP;
+    state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    g_arch_ok[dev].store(state, std::memory_order_relaxed);
+  }
+  return state == 1 ? KDA_OK : KDA_ERR_NO_DEVICE;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_common(int dk, int dv, int H, int dtype) {
+  if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_DTYPE;
+  if (dk != dv || (dk != 64 && dk != 128)) return KDA_ERR_HEAD_DIM;
+  if (H <= 0) return KDA_ERR_SHAPE;
+  return KDA_OK;
+}
+
+struct PtrReq {
+  const void* p;
+  uintptr_t align;
+  bool required;
+};
+
+int check_ptrs(std::initializer_list<PtrReq> ptrs) {
+  for (const PtrReq& r : ptrs) {
+    if (r.p == nullptr) {
+      if (r.required) return KDA_ERR_NULL;
+      continue;
+    }
+    if (!aligned(r.p, r.align)) return KDA_ERR_ALIGN;
+  }
+  return KDA_OK;
+}
+
+// Prefill pointer rules: q, k, g are read two elements at a time (4 bytes),
+// beta one element at a time, v and out 16 bytes at a time, states as fp32.
+int check_prefill_ptrs(const void* q, const void* k, const void* v, const void* g,
+                       const void* beta, const void* s0, const void* out, const void* sT,
+                       int dtype) {
+  const uintptr_t elt = dtype == KDA_F32 ? 4 : 2;
+  return check_ptrs({{q, 4, true}, {k, 4, true}, {g, 4, true}, {beta, elt, true},
+                     {v, 16, true}, {out, 16, true}, {s0, 4, false}, {sT, 4, false}});
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_string(int status) {
+  switch (status) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL: return "a required pointer is NULL";
+    case KDA_ERR_SHAPE: return "a size is non-positive or too large";
+    case KDA_ERR_HEAD_DIM: return "dk and dv must be equal and 64 or 128 (64 for fp32 prefill)";
+    case KDA_ERR_DTYPE: return "dtype must be KDA_BF16 or KDA_F32";
+    case KDA_ERR_ALIGN: return "a pointer is not aligned as required";
+    case KDA_ERR_HIP: return "the HIP runtime reported an error";
+    case KDA_ERR_NO_DEVICE: return "the current device is not gfx950";
+    default: return "unknown status";
+  }
+}
+
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
+                  const void* beta, const float* initial_state, void* out,
+                  float* final_state, int B, int T, int H, int dk, int dv, float scale,
+                  int dtype, hipStream_t stream) {
+  int rc = check_common(dk, dv, H, dtype);
+  if (rc != KDA_OK) return rc;
+  if (dtype == KDA_F32 && dk != 64) return KDA_ERR_HEAD_DIM;
+  if (B <= 0 || T <= 0) return KDA_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * T > INT32_MAX / 2) return KDA_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * H > (1 << 24)) return KDA_ERR_SHAPE;
+  rc = check_prefill_ptrs(q, k, v, g, beta, initial_state, out, final_state, dtype);
+  if (rc != KDA_OK) return rc;
+  rc = check_device();
+  if (rc != KDA_OK) return rc;
+  kda::PrefillArgs a{q, k, v, g, beta, initial_state, out, final_state, nullptr,
+                     B, T, B * T, H, dk, scale, dtype == KDA_F32, stream};
+  return kda::launch_prefill(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void* g,
+                         const void* beta, const float* initial_state, void* out,
+                         float* final_state, const int32_t* cu_seqlens, int N,
+                         int total_T, int H, int dk, int dv, float scale, int dtype,
+                         hipStream_t stream) {
+  int rc = check_common(dk, dv, H, dtype);
+  if (rc != KDA_OK) return rc;
+  if (dtype == KDA_F32 && dk != 64) return KDA_ERR_HEAD_DIM;
+  if (N <= 0 || total_T <= 0 || total_T > INT32_MAX / 2) return KDA_ERR_SHAPE;
+  if (static_cast<int64_t>(N) * H > (1 << 24)) return KDA_ERR_SHAPE;
+  if (cu_seqlens == nullptr) return KDA_ERR_NULL;
+  rc = check_prefill_ptrs(q, k, v, g, beta, initial_state, out, final_state, dtype);
+  if (rc == KDA_OK && !aligned(cu_seqlens, 4)) rc = KDA_ERR_ALIGN;
+  if (rc != KDA_OK) return rc;
+  rc = check_device();
+  if (rc != KDA_OK) return rc;
+  kda::PrefillArgs a{q, k, v, g, beta, initial_state, out, final_state, cu_seqlens,
+                     N, 0, total_T, H, dk, scale, dtype == KDA_F32, stream};
+  return kda::launch_prefill(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_decode_step(const void* q, const void* k, const void* v, const void* g,
+                    const void* beta, float* state, void* out, int B, int H, int dk, int dv,
+                    float scale, int dtype, hipStream_t stream) {
+  int rc = check_common(dk, dv, H, dtype);
+  if (rc != KDA_OK) return rc;
+  if (B <= 0) return KDA_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * H > INT32_MAX / 2) return KDA_ERR_SHAPE;
+  const uintptr_t elt = dtype == KDA_F32 ? 4 : 2;
+  rc = check_ptrs({{q, elt, true}, {k, elt, true}, {v, elt, true}, {g, elt, true},
+                   {beta, elt, true}, {state, 16, true}, {out, elt, true}});
+  if (rc != KDA_OK) return rc;
+  rc = check_device();
+  if (rc != KDA_OK) return rc;
+  kda::DecodeArgs a{q, k, v, g, beta, state, out, B, H, dk, scale, dtype == KDA_F32, stream};
+  return kda::launch_decode(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,130 @@
+// Single-token KDA decode step on gfx950.
+//
+// For every (sequence b, head h), with the fp32 state S (D x D, row i = key
+// channel i) held in HBM:
+//     S' = Diag(exp g) S;  u = S'^T k;  p = S'^T q;  delta = beta (v - u)
+//     S  = S' + k delta^T;  o = scale (p + delta (k . q))
+// (the per-token rule of KDA: forget per key channel, then a delta-rule write;
+// neurohive.io Kimi K3 review, section "Sequence length: hybrid KDA and Gated
+// MLA attention"; one fixed-size state per request, neurohive.io section
+// "Training and inference infrastructure").  o reads the state after the write:
+// S^T q = S'^T q + delta (k . q).
+//
+// The step is bound by HBM: every state element is read once and written once
+// (8 bytes) for about 7 flops.  One 256-thread workgroup owns one state.  Thread
+// (rg, cg) holds rows [rg*R, rg*R+R) of column quad cg as float4 registers, so a
+// wavefront reads and writes whole 512-byte rows with 16-byte accesses.  The
+// column reductions over rows (S'^T k, S'^T q) are summed inside the thread over
+// its R rows, then across the row groups through LDS.  The state makes exactly
+// one trip through registers: load, decay, reduce, update, store.
+
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+namespace {
+
+template <int D, typename T>
+__global__ __launch_bounds__(256) void decode_step_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ g, const T* __restrict__ beta, float* __restrict__ state,
+    T* __restrict__ out, float scale) {
+  constexpr int CG = D / 4;          // column quads per row
+  constexpr int RG = 256 / CG;       // row groups
+  constexpr int R = D / RG;          // rows per thread
+  static_assert(R * RG == D && CG * 4 == D, "tile shape");
+
+  __shared__ float red_u[RG][D];
+  __shared__ float red_p[RG][D];
+  __shared__ float red_kq[RG];
+
+  const int bh = blockIdx.x;         // b * H + h
+  const int tid = threadIdx.x;
+  const int cg = tid % CG;
+  const int rg = tid / CG;
+  const int row0 = rg * R;
+
+  float4* S = reinterpret_cast<float4*>(state + static_cast<int64_t>(bh) * D * D);
+  const T* qh = q + static_cast<int64_t>(bh) * D;
+  const T* kh = k + static_cast<int64_t>(bh) * D;
+  const T* gh = g + static_cast<int64_t>(bh) * D;
+
+  float4 s[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) s[r] = S[(row0 + r) * CG + cg];
+
+  float kr[R], qr[R];
+  float4 u = {0.f, 0.f, 0.f, 0.f}, p = {0.f, 0.f, 0.f, 0.f};
+  float kq = 0.f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float dec = fast_exp2(to_f32(gh[row0 + r]) * kLog2e);
+    kr[r] = to_f32(kh[row0 + r]);
+    qr[r] = to_f32(qh[row0 + r]);
+    s[r].x *= dec; s[r].y *= dec; s[r].z *= dec; s[r].w *= dec;
+    u.x += s[r].x * kr[r]; u.y += s[r].y * kr[r]; u.z += s[r].z * kr[r]; u.w += s[r].w * kr[r];
+    p.x += s[r].x * qr[r]; p.y += s[r].y * qr[r]; p.z += s[r].z * qr[r]; p.w += s[r].w * qr[r];
+    kq += kr[r] * qr[r];
+  }
+  *reinterpret_cast<float4*>(&red_u[rg][4 * cg]) = u;
+  *reinterpret_cast<float4*>(&red_p[rg][4 * cg]) = p;
+  if (cg == 0) red_kq[rg] = kq;
+  __syncthreads();
+
+  u = float4{0.f, 0.f, 0.f, 0.f};
+  p = float4{0.f, 0.f, 0.f, 0.f};
+  kq = 0.f;
+#pragma unroll
+  for (int j = 0; j < RG; ++j) {
+    const float4 a = *reinterpret_cast<const float4*>(&red_u[j][4 * cg]);
+    const float4 c = *reinterpret_cast<const float4*>(&red_p[j][4 * cg]);
+    u.x += a.x; u.y += a.y; u.z += a.z; u.w += a.w;
+    p.x += c.x; p.y += c.y; p.z += c.z; p.w += c.w;
+    kq += red_kq[j];
+  }
+
+  const float b = to_f32(beta[bh]);
+  const T* vh = v + static_cast<int64_t>(bh) * D + 4 * cg;
+  float4 dl;
+  dl.x = b * (to_f32(vh[0]) - u.x);
+  dl.y = b * (to_f32(vh[1]) - u.y);
+  dl.z = b * (to_f32(vh[2]) - u.z);
+  dl.w = b * (to_f32(vh[3]) - u.w);
+
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    s[r].x += kr[r] * dl.x; s[r].y += kr[r] * dl.y;
+    s[r].z += kr[r] * dl.z; s[r].w += kr[r] * dl.w;
+    S[(row0 + r) * CG + cg] = s[r];
+  }
+
+  if (rg == 0) {
+    T* oh = out + static_cast<int64_t>(bh) * D + 4 * cg;
+    oh[0] = Elem<T>::from(scale * (p.x + dl.x * kq));
+    oh[1] = Elem<T>::from(scale * (p.y + dl.y * kq));
+    oh[2] = Elem<T>::from(scale * (p.z + dl.z * kq));
+    oh[3] = Elem<T>::from(scale * (p.w + dl.w * kq));
+  }
+}
+
+template <int D, typename T>
+hipError_t launch_decode_t(const DecodeArgs& a) {
+  const int nbh = a.B * a.H;
+  hipLaunchKernelGGL((decode_step_kernel<D, T>), dim3(nbh), dim3(256), 0, a.stream,
+                     static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                     static_cast<const T*>(a.v), static_cast<const T*>(a.g),
+                     static_cast<const T*>(a.beta), a.state, static_cast<T*>(a.out), a.scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a) {
+  if (a.d == 128) {
+    return a.dtype_f32 ? launch_decode_t<128, float>(a) : launch_decode_t<128, bf16_t>(a);
+  }
+  return a.dtype_f32 ? launch_decode_t<64, float>(a) : launch_decode_t<64, bf16_t>(a);
+}
+
+}  // namespace kda

@@ -1,0 +1,38 @@
+// Internal launcher interface between the C ABI shim and the HIP kernels.
+// Arguments arrive here already validated by kda_api.cpp.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct DecodeArgs {
+  const void *q, *k, *v, *g, *beta;
+  float* state;
+  void* out;
+  int B, H, d;
+  float scale;
+  bool dtype_f32;
+  hipStream_t stream;
+};
+
+struct PrefillArgs {
+  const void *q, *k, *v, *g, *beta;
+  const float* initial_state;  // may be null
+  void* out;
+  float* final_state;          // may be null; may alias initial_state
+  const int32_t* cu_seqlens;   // device offsets (varlen) or null (fixed length)
+  int N;                       // sequences
+  int T;                       // tokens per sequence (fixed length)
+  int total_T;                 // tokens in the packed buffers
+  int H, d;
+  float scale;
+  bool dtype_f32;
+  hipStream_t stream;
+};
+
+hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_prefill(const PrefillArgs& a);
+
+}  // namespace kda

@@ -1,0 +1,915 @@
+// Chunked KDA prefill on gfx950: a chunk-parallel preparation kernel and a
+// serial state-scan kernel (chunk = 64 tokens, 16-row sub-tiles).
+//
+// The token rule (neurohive.io Kimi K3 review, section "Sequence length: hybrid
+// KDA and Gated MLA attention": a delta rule that forgets and writes, with a
+// per-key-channel retention factor whose log is bounded below at -5)
+//     S_t = (I - beta_t k_t k_t^T) Diag(exp g_t) S_{t-1} + beta_t k_t v_t^T,
+//     o_t = S_t^T (scale q_t)
+// is applied 64 tokens at a time.  With G the cumulative log-decay inside a
+// chunk (per token and key channel, zero before the chunk):
+//     A[t,s] = beta_t sum_c k_tc k_sc e^{G_tc - G_sc}   (s < t)   decayed key Gram
+//     M[t,s] =        sum_c q_tc k_sc e^{G_tc - G_sc}   (s <= t)  decayed query-key
+//     Tb     = (I + A)^{-1} Diag(beta)                  (UT transform)
+//     W      = Tb (K e^G),   P = scale M Tb,   Q' = scale (Q e^G) - P (K e^G)
+//     Kt     = K e^{G_n - G}, Lambda = e^{G_n}
+// all of which are independent of the state, and then, chunk after chunk,
+//     Delta = Tb V - W S,   O = Q' S + P V,   S <- Diag(Lambda) S + Kt^T Delta.
+// Unrolling the recurrence inside the chunk gives (I + A) Delta = Diag(beta)(V -
+// (K e^G) S), so the result equals the token-by-token one up to rounding.
+//
+// Kernel 1 (chunk_prep_kernel) does all state-independent work, one workgroup
+// per (chunk, head), fully parallel: the elementwise decay factors, A and M on
+// v_mfma_f32_16x16x32_bf16, the fp32 inverse, and W, Q', P, Tb.  It writes them,
+// in the layouts the matrix cores read, to a stream-ordered workspace.
+// Kernel 2 (state_scan_kernel) walks the chunks of one (sequence, head) and one
+// dv slice; the dv columns of S evolve independently, so slices never talk.  Per
+// chunk it only runs the four state products, reading operand fragments straight
+// from the workspace into registers.
+//
+// The -5 bound is what lets every tile be a plain bf16 matrix-core product: over
+// a whole chunk e^{-G} reaches e^{320}, so A and M are built from 16-row sub-tiles
+// referenced to the cumulative decay at the end of their own sub-tile -- row side
+// e^{G_t - R_I} in [1, e^80], column side e^{R_I - G_s} <= 1, both in bf16 range.
+
+#include <type_traits>
+
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int kC = 64;
+constexpr int kThreads = 256;
+
+// ---------------------------------------------------------------- helpers
+
+// Byte offset of (row, byte) in an LDS tile whose rows are RB bytes long, with the
+// 16-byte chunks of each row permuted by the row index (conflict-free column reads).
+template <int RB>
+__device__ __forceinline__ int swz(int row, int byte) {
+  constexpr int NCH = RB / 16;
+  static_assert(NCH == 4 || NCH == 8 || NCH == 16, "row length");
+  return row * RB + ((((byte >> 4) ^ (row & (NCH - 1)))) << 4) + (byte & 15);
+}
+
+template <bool F32> struct Frag;
+template <> struct Frag<false> { bf16x8_t v; };
+template <> struct Frag<true> { float v[8]; };
+
+template <bool F32>
+__device__ __forceinline__ f32x4_t mma32(f32x4_t acc, const Frag<F32>& a, const Frag<F32>& b) {
+  if constexpr (F32) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[i], b.v[i], acc, 0, 0, 0);
+    return acc;
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+  }
+}
+
+// 8 consecutive operand elements (16 bytes bf16, 32 bytes fp32) of a swizzled tile.
+template <bool F32, int RB>
+__device__ __forceinline__ Frag<F32> lds_frag(const char* base, int row, int byte) {
+  Frag<F32> f;
+  if constexpr (F32) {
+    const float4 a = *reinterpret_cast<const float4*>(base + swz<RB>(row, byte));
+    const float4 b = *reinterpret_cast<const float4*>(base + swz<RB>(row, byte + 16));
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+  } else {
+    f.v = *reinterpret_cast<const bf16x8_t*>(base + swz<RB>(row, byte));
+  }
+  return f;
+}
+
+// Same, from global memory through a buffer resource (byte offset).
+template <bool F32>
+__device__ __forceinline__ Frag<F32> buf_frag(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  Frag<F32> f;
+  if constexpr (F32) {
+    const i32x4_t a = buf_ld128(r, voff, soff);
+    const i32x4_t b = buf_ld128(r, voff + 16, soff);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { f.v[i] = __int_as_float(a[i]); f.v[4 + i] = __int_as_float(b[i]); }
+  } else {
+    f.v = __builtin_bit_cast(bf16x8_t, buf_ld128(r, voff, soff));
+  }
+  return f;
+}
+
+template <bool F32>
+__device__ __forceinline__ Frag<F32> frag_from_f32(const float* x) {
+  Frag<F32> f;
+  if constexpr (F32) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f.v[i] = x[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f.v[i] = static_cast<__bf16>(x[i]);
+  }
+  return f;
+}
+
+template <bool F32>
+__device__ __forceinline__ void frag_to_f32(const Frag<F32>& f, float* x) {
+  if constexpr (F32) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = f.v[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = static_cast<float>(f.v[i]);
+  }
+}
+
+// 4 consecutive values as operand elements: 8 bytes (bf16) or 16 bytes (fp32).
+template <bool F32>
+__device__ __forceinline__ void lds_put4(char* p, float a, float b, float c, float d) {
+  if constexpr (F32) {
+    *reinterpret_cast<float4*>(p) = float4{a, b, c, d};
+  } else {
+    *reinterpret_cast<uint2*>(p) = uint2{pack_bf16x2(a, b), pack_bf16x2(c, d)};
+  }
+}
+template <bool F32>
+__device__ __forceinline__ void buf_put4(__amdgpu_buffer_rsrc_t r, uint32_t voff, float a, float b,
+                                         float c, float d) {
+  if constexpr (F32) {
+    buf_st128(i32x4_t{__float_as_int(a), __float_as_int(b), __float_as_int(c), __float_as_int(d)},
+              r, voff, 0);
+  } else {
+    buf_st64(i32x2_t{static_cast<int>(pack_bf16x2(a, b)), static_cast<int>(pack_bf16x2(c, d))}, r,
+             voff, 0);
+  }
+}
+
+template <bool F32>
+__device__ __forceinline__ float lds_get1(const char* p) {
+  if constexpr (F32) return *reinterpret_cast<const float*>(p);
+  else return __uint_as_float(static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(p)) << 16);
+}
+
+template <bool F32>
+__device__ __forceinline__ void lds_set1(char* p, float x) {
+  if constexpr (F32) *reinterpret_cast<float*>(p) = x;
+  else *reinterpret_cast<uint16_t*>(p) = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+// Sub-tile pairs (I, J), J <= I, in the order (0,0),(1,0),(1,1),(2,0),...,(3,3).
+__device__ __forceinline__ void pair_of(int p, int& I, int& J) {
+  I = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3;
+  J = p - I * (I + 1) / 2;
+}
+// Off-diagonal pairs J < I -> 0..5.
+__device__ __forceinline__ constexpr int offdiag_index(int I, int J) { return I * (I - 1) / 2 + J; }
+// Strictly-upper sub-tile pairs (I, J), J > I, numbered 0..5.
+__device__ __forceinline__ void upper_pair(int b, int& I, int& J) {
+  I = b < 3 ? 0 : b < 5 ? 1 : 2;
+  J = b < 3 ? b + 1 : b < 5 ? b - 1 : 3;
+}
+
+// ---------------------------------------------------------------- sequences
+
+struct SeqArgs {
+  const int32_t* cu;   // varlen offsets, or null
+  int N, T, total_T, H;
+};
+
+__device__ __forceinline__ void seq_bounds(const SeqArgs& a, int n, int& tok0, int& len) {
+  if (a.cu == nullptr) {
+    tok0 = n * a.T;
+    len = a.T;
+  } else {
+    const int x0 = min(max(a.cu[n], 0), a.total_T);
+    const int x1 = min(max(a.cu[n + 1], x0), a.total_T);
+    tok0 = x0;
+    len = x1 - x0;
+  }
+}
+
+// Workspace slots: sequence n owns [floor(tok0/64) + n, ... + ceil(len/64)); these
+// ranges never overlap and all lie below ceil(total_T/64) + N.
+__device__ __forceinline__ int slot_base(int tok0, int n) { return tok0 / kC + n; }
+
+// Which (sequence, chunk) a workspace slot holds; false for unused slots.
+__device__ __forceinline__ bool locate_slot(const SeqArgs& a, int slot, int& n, int& chunk,
+                                            int& tok0, int& len) {
+  int lo = 0, hi = a.N - 1;            // largest n with slot_base(n) <= slot
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    int t0, l;
+    seq_bounds(a, mid, t0, l);
+    if (slot_base(t0, mid) <= slot) lo = mid; else hi = mid - 1;
+  }
+  n = lo;
+  seq_bounds(a, n, tok0, len);
+  chunk = slot - slot_base(tok0, n);
+  return chunk >= 0 && chunk * kC < len;
+}
+
+// ---------------------------------------------------------------- workspace slot
+
+template <int D, bool F32>
+struct Slot {
+  static constexpr int E = F32 ? 4 : 2;
+  static constexpr int W = 0;                          // [64][D]  W
+  static constexpr int QP = W + kC * D * E;            // [64][D]  Q'
+  static constexpr int KT = QP + kC * D * E;           // [D][64]  Kt^T
+  static constexpr int TB = KT + D * kC * E;           // [64][64] Tb
+  static constexpr int PP = TB + kC * kC * E;          // [64][64] P
+  static constexpr int LAM = PP + kC * kC * E;         // [D] fp32 Lambda
+  static constexpr int BYTES = (LAM + D * 4 + 255) / 256 * 256;
+};
+
+// ================================================================= kernel 1
+
+template <int D, typename TIn>
+struct PrepCfg {
+  static constexpr bool F32 = std::is_same<TIn, float>::value;
+  static constexpr int E = F32 ? 4 : 2;          // operand element bytes
+  static constexpr int EI = sizeof(TIn);         // input element bytes
+  static constexpr int CPL = D / 64;             // key channels per lane
+  static constexpr int RBD = D * E;              // bytes per row of [64][D]
+  static constexpr int RBC = kC * E;             // bytes per row of [D][64], [64][64]
+  static constexpr int NKK = D / 32;
+  // R1, phase 1: sub-tile referenced operands
+  static constexpr int QS = 0, KS = QS + kC * RBD, KT = KS + kC * RBD, R1A = KT + kC * RBD;
+  // R1, phase 2: chunk-referenced operands and P
+  static constexpr int QB = 0, KBT = QB + kC * RBD, PB = KBT + D * RBC, R1B = PB + kC * RBC;
+  static constexpr int R1 = R1A > R1B ? R1A : R1B;
+  static constexpr int AT = R1;                  // [64][64] fp32: A, then T in place
+  static constexpr int MB = AT + kC * kC * 4;    // [64][64] operand: M
+  static constexpr int FIJ = MB + kC * RBC;      // [6][D] fp32 pair factors
+  static constexpr int BTOT = FIJ + 6 * D * 4;   // [4][D] fp32 sub-tile totals
+  static constexpr int BETA = BTOT + 4 * D * 4;  // [64] fp32
+  static constexpr int LDS = BETA + kC * 4;
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+struct PrepParams {
+  const void *q, *k, *g, *beta;
+  char* ws;
+  SeqArgs sa;
+  float scale;
+};
+
+template <int D, typename TIn>
+__global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepParams p) {
+  using CF = PrepCfg<D, TIn>;
+  using SL = Slot<D, CF::F32>;
+  constexpr bool F32 = CF::F32;
+  constexpr int CPL = CF::CPL;
+  constexpr int E = CF::E;
+  constexpr int EI = CF::EI;
+  __shared__ __attribute__((aligned(16))) char smem[CF::LDS];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int H = p.sa.H;
+  const int slot = blockIdx.x / H;
+  const int h = blockIdx.x % H;
+  int n, chunk, stok0, slen;
+  if (!locate_slot(p.sa, slot, n, chunk, stok0, slen)) return;
+  const int t0 = stok0 + chunk * kC;
+  const int nrow = min(kC, slen - chunk * kC);
+
+  const uint32_t rs_qk = static_cast<uint32_t>(H) * D * EI;    // row stride (bytes)
+  const int64_t base_qk = (static_cast<int64_t>(t0) * H + h) * D;
+  const uint32_t bytes_qk = (nrow - 1) * rs_qk + D * EI;
+  const auto rq = make_rsrc(static_cast<const TIn*>(p.q) + base_qk, bytes_qk);
+  const auto rk = make_rsrc(static_cast<const TIn*>(p.k) + base_qk, bytes_qk);
+  const auto rg = make_rsrc(static_cast<const TIn*>(p.g) + base_qk, bytes_qk);
+  const auto rb = make_rsrc(static_cast<const TIn*>(p.beta) + static_cast<int64_t>(t0) * H + h,
+                            (nrow - 1) * H * EI + EI);
+  const auto rw = make_rsrc(p.ws + (static_cast<int64_t>(slot) * H + h) * SL::BYTES, SL::BYTES);
+
+  char* atc = smem + CF::AT;
+  float* btot = reinterpret_cast<float*>(smem + CF::BTOT);
+  float* betas = reinterpret_cast<float*>(smem + CF::BETA);
+  float* fij = reinterpret_cast<float*>(smem + CF::FIJ);
+
+  // the strictly-upper sub-tiles of A/T and of M are read as zeros
+  for (int e = tid; e < 6 * 256; e += kThreads) {
+    int I, J;
+    upper_pair(e >> 8, I, J);
+    const int row = 16 * I + ((e >> 4) & 15), col = 16 * J + (e & 15);
+    *reinterpret_cast<float*>(atc + swz<256>(row, col * 4)) = 0.f;
+    lds_set1<F32>(smem + CF::MB + swz<CF::RBC>(row, col * E), 0.f);
+  }
+
+  // ------------------------------------------------ phase E: decay factors
+  // wavefront `wave` owns token rows 16*wave .. +15; lane owns key channels
+  // lane*CPL .. +CPL-1; the cumulative decay is a running product over the rows.
+  float kf[16][CPL], qf[16][CPL], rowf[16][CPL], colf[16][CPL];
+  {
+    float ed[16][CPL];
+    const uint32_t vo = lane * CPL * EI;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const uint32_t so = (16 * wave + r) * rs_qk;
+      if constexpr (F32) {
+        ed[r][0] = fast_exp2(__uint_as_float(buf_ld32(rg, vo, so)) * kLog2e);
+        kf[r][0] = __uint_as_float(buf_ld32(rk, vo, so));
+        qf[r][0] = __uint_as_float(buf_ld32(rq, vo, so));
+      } else if constexpr (CPL == 2) {
+        const uint32_t gw = buf_ld32(rg, vo, so), kw = buf_ld32(rk, vo, so), qw = buf_ld32(rq, vo, so);
+        ed[r][0] = fast_exp2(bf16lo(gw) * kLog2e);
+        ed[r][1] = fast_exp2(bf16hi(gw) * kLog2e);
+        kf[r][0] = bf16lo(kw); kf[r][1] = bf16hi(kw);
+        qf[r][0] = bf16lo(qw); qf[r][1] = bf16hi(qw);
+      } else {
+        ed[r][0] = fast_exp2(__uint_as_float(uint32_t(buf_ld16(rg, vo, so)) << 16) * kLog2e);
+        kf[r][0] = __uint_as_float(uint32_t(buf_ld16(rk, vo, so)) << 16);
+        qf[r][0] = __uint_as_float(uint32_t(buf_ld16(rq, vo, so)) << 16);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) {
+      float run = 1.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { run *= ed[r][e]; rowf[r][e] = run; }      // e^{G_t - R_w}
+      btot[wave * D + lane * CPL + e] = run;                                    // e^{R_{w+1} - R_w}
+      float back = 1.f;
+#pragma unroll
+      for (int r = 15; r >= 0; --r) { colf[r][e] = back; back *= ed[r][e]; }   // e^{R_{w+1} - G_t}
+    }
+    if (tid < kC) {
+      float b;
+      if constexpr (F32) b = __uint_as_float(buf_ld32(rb, tid * H * EI, 0));
+      else b = __uint_as_float(uint32_t(buf_ld16(rb, tid * H * EI, 0)) << 16);
+      betas[tid] = b;
+    }
+  }
+  __syncthreads();
+
+  float eR1[CPL], fI3[CPL];
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) {
+    const int c = lane * CPL + e;
+    float b4[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) b4[m] = btot[m * D + c];
+    float pre = 1.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) if (m <= wave) pre *= b4[m];
+    eR1[e] = pre;                                    // e^{R_{w+1}}
+    const float inv_bt = 1.f / b4[wave];
+    float acc = 1.f;
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      if (I > wave) {
+        acc *= b4[I];
+        fij[offdiag_index(I, wave) * D + c] = acc;   // e^{R_{I+1} - R_{w+1}}
+      }
+    }
+    fI3[e] = acc;                                    // e^{G_n - R_{w+1}}
+    if (wave == 0) {
+      const float lam = b4[0] * b4[1] * b4[2] * b4[3];
+      buf_st32(__float_as_uint(lam), rw, SL::LAM + c * 4, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) rowf[r][e] *= inv_bt;   // now e^{G_t - R_{w+1}} in [1, e^80]
+  }
+  // row-side operands (referenced to the end of the own sub-tile) and the
+  // column-side keys of the diagonal pairs
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int t = 16 * wave + r;
+    const int byte = lane * CPL * E;
+    if constexpr (CPL == 2 && !F32) {
+      *reinterpret_cast<uint32_t*>(smem + CF::QS + swz<CF::RBD>(t, byte)) =
+          pack_bf16x2(qf[r][0] * rowf[r][0], qf[r][1] * rowf[r][1]);
+      *reinterpret_cast<uint32_t*>(smem + CF::KS + swz<CF::RBD>(t, byte)) =
+          pack_bf16x2(kf[r][0] * rowf[r][0], kf[r][1] * rowf[r][1]);
+      *reinterpret_cast<uint32_t*>(smem + CF::KT + swz<CF::RBD>(t, byte)) =
+          pack_bf16x2(kf[r][0] * colf[r][0], kf[r][1] * colf[r][1]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) {
+        const int b = byte + e * E;
+        lds_set1<F32>(smem + CF::QS + swz<CF::RBD>(t, b), qf[r][e] * rowf[r][e]);
+        lds_set1<F32>(smem + CF::KS + swz<CF::RBD>(t, b), kf[r][e] * rowf[r][e]);
+        lds_set1<F32>(smem + CF::KT + swz<CF::RBD>(t, b), kf[r][e] * colf[r][e]);
+      }
+    }
+  }
+  // Kt^T = (K e^{G_n - G})^T straight to the workspace: 16 consecutive tokens per channel
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) {
+    const int c = lane * CPL + e;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = kf[r][e] * colf[r][e] * fI3[e];
+    const uint32_t off = SL::KT + (c * kC + 16 * wave) * E;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+      buf_put4<F32>(rw, off + 4 * q4 * E, x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]);
+  }
+  __syncthreads();
+
+  // ------------------------------------------------ phase AM: A and M
+  // computed transposed (rows s) so each lane stores 4 consecutive s of row t
+#pragma unroll
+  for (int pp = 0; pp < 3; ++pp) {
+    const int pr = wave + 4 * pp;
+    if (pr < 10) {
+      int I, J;
+      pair_of(pr, I, J);
+      f32x4_t aA = {0.f, 0.f, 0.f, 0.f}, aM = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < CF::NKK; ++kk) {
+        const int kb = (kk * 32 + g4 * 8) * E;
+        Frag<F32> a = lds_frag<F32, CF::RBD>(smem + CF::KT, 16 * J + l16, kb);
+        if (J < I) {   // carry column sub-tile J to row sub-tile I's reference
+          const float* f = fij + offdiag_index(I, J) * D + kk * 32 + g4 * 8;
+          float x[8];
+          frag_to_f32<F32>(a, x);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] *= f[e];
+          a = frag_from_f32<F32>(x);
+        }
+        const Frag<F32> bk = lds_frag<F32, CF::RBD>(smem + CF::KS, 16 * I + l16, kb);
+        const Frag<F32> bq = lds_frag<F32, CF::RBD>(smem + CF::QS, 16 * I + l16, kb);
+        aA = mma32<F32>(aA, a, bk);
+        aM = mma32<F32>(aM, a, bq);
+      }
+      const int t = 16 * I + l16, s0 = 16 * J + 4 * g4;
+      const float bt = betas[t];
+      float av[4], mv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        av[i] = (s0 + i < t) ? bt * aA[i] : 0.f;
+        mv[i] = (s0 + i <= t) ? aM[i] : 0.f;
+      }
+      *reinterpret_cast<float4*>(atc + swz<256>(t, s0 * 4)) = float4{av[0], av[1], av[2], av[3]};
+      lds_put4<F32>(smem + CF::MB + swz<CF::RBC>(t, s0 * E), mv[0], mv[1], mv[2], mv[3]);
+    }
+  }
+  __syncthreads();
+
+  // ------------------------------------------------ phase E2 + diagonal inverses
+  // chunk-referenced Q e^G ([t][c]) and (K e^G)^T ([c][t]) into region 1
+#pragma unroll
+  for (int e = 0; e < CPL; ++e) {
+    const int c = lane * CPL + e;
+    float kb[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int t = 16 * wave + r;
+      const float ef = rowf[r][e] * eR1[e];           // e^{G_t}
+      lds_set1<F32>(smem + CF::QB + swz<CF::RBD>(t, c * E), qf[r][e] * ef);
+      kb[r] = kf[r][e] * ef;
+    }
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+      lds_put4<F32>(smem + CF::KBT + swz<CF::RBC>(c, (16 * wave + 4 * q4) * E),
+                    kb[4 * q4], kb[4 * q4 + 1], kb[4 * q4 + 2], kb[4 * q4 + 3]);
+  }
+  if (lane < 16) {   // T_ww = (I + A_ww)^{-1}, lane j computes column j
+    const int base = 16 * wave;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float arow[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 v = *reinterpret_cast<const float4*>(atc + swz<256>(base + i, (base + 4 * q4) * 4));
+        arow[4 * q4] = v.x; arow[4 * q4 + 1] = v.y; arow[4 * q4 + 2] = v.z; arow[4 * q4 + 3] = v.w;
+      }
+      float s = 0.f;
+#pragma unroll
+      for (int m = 0; m < i; ++m) s += arow[m] * x[m];
+      x[i] = (i == lane) ? 1.f : -s;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      *reinterpret_cast<float*>(atc + swz<256>(base + i, (base + lane) * 4)) = x[i];
+  }
+  __syncthreads();
+
+  // ------------------------------------------------ off-diagonal inverse blocks
+  // T_IJ = -T_II sum_{m=J}^{I-1} A_Im T_mJ, row sub-tile by row sub-tile, in place
+#pragma unroll
+  for (int I = 1; I < 4; ++I) {
+    f32x4_t tt = {0.f, 0.f, 0.f, 0.f};
+    const int J = wave;
+    if (J < I) {
+      f32x4_t y = {0.f, 0.f, 0.f, 0.f};
+      for (int m = J; m < I; ++m) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const int kx = 4 * g4 + st;
+          const float a = *reinterpret_cast<const float*>(atc + swz<256>(16 * I + l16, (16 * m + kx) * 4));
+          const float b = *reinterpret_cast<const float*>(atc + swz<256>(16 * m + kx, (16 * J + l16) * 4));
+          y = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, y, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const float a = *reinterpret_cast<const float*>(atc + swz<256>(16 * I + l16, (16 * I + 4 * g4 + st) * 4));
+        tt = __builtin_amdgcn_mfma_f32_16x16x4f32(a, y[st], tt, 0, 0, 0);
+      }
+    }
+    __syncthreads();
+    if (J < I) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<float*>(atc + swz<256>(16 * I + 4 * g4 + i, (16 * J + l16) * 4)) = -tt[i];
+    }
+    __syncthreads();
+  }
+
+  // ------------------------------------------------ P = scale M Tb, stored as P[t][t']
+  // computed transposed: P^T[t'][t] = sum_s Tb[s][t'] M[t][s], nonzero for t' <= t
+#pragma unroll
+  for (int pp = 0; pp < 3; ++pp) {
+    const int pr = wave + 4 * pp;
+    if (pr < 10) {
+      int C, R;
+      pair_of(pr, C, R);
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int sb = kk * 32 + g4 * 8;
+        float x[8];
+        const float bcol = betas[16 * R + l16];     // Tb[s][t'] = T[s][t'] beta_t'
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          x[e] = *reinterpret_cast<const float*>(atc + swz<256>(sb + e, (16 * R + l16) * 4)) * bcol;
+        const Frag<F32> a = frag_from_f32<F32>(x);
+        const Frag<F32> b = lds_frag<F32, CF::RBC>(smem + CF::MB, 16 * C + l16, sb * E);
+        acc = mma32<F32>(acc, a, b);
+      }
+      const int t = 16 * C + l16, tp = 16 * R + 4 * g4;
+      lds_put4<F32>(smem + CF::PB + swz<CF::RBC>(t, tp * E), acc[0], acc[1], acc[2], acc[3]);
+      buf_put4<F32>(rw, SL::PP + (t * kC + tp) * E, p.scale * acc[0], p.scale * acc[1],
+                    p.scale * acc[2], p.scale * acc[3]);
+    }
+  }
+  for (int e = tid; e < 6 * 64; e += kThreads) {   // P[t][t'] = 0 for t' sub-tile > t sub-tile
+    int C, R;
+    upper_pair(e >> 6, C, R);
+    const int t = 16 * C + ((e >> 2) & 15), tp = 16 * R + 4 * (e & 3);
+    lds_put4<F32>(smem + CF::PB + swz<CF::RBC>(t, tp * E), 0.f, 0.f, 0.f, 0.f);
+    buf_put4<F32>(rw, SL::PP + (t * kC + tp) * E, 0.f, 0.f, 0.f, 0.f);
+  }
+  __syncthreads();
+
+  // ------------------------------------------------ W and Q'
+  // W^T = (K e^G)^T Tb^T and Q'^T = scale ((Q e^G)^T - (K e^G)^T P^T); lane holds
+  // 4 consecutive channels of one token row -> 4-element stores of W[t][c], Q'[t][c]
+  {
+    constexpr int RPW = D / 64;        // 16-row channel tiles per wavefront
+    f32x4_t aw[RPW][4], aq[RPW][4];
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        aw[rr][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        aq[rr][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const int t = 16 * ct + l16;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        if (kk == 1 && ct < 2) continue;     // Tb[t][s] = P[t][s] = 0 for s > t
+        const int sb = kk * 32 + g4 * 8;
+        float x[8];
+        {
+          const float4 u0 = *reinterpret_cast<const float4*>(atc + swz<256>(t, sb * 4));
+          const float4 u1 = *reinterpret_cast<const float4*>(atc + swz<256>(t, sb * 4 + 16));
+          const float4 b0 = *reinterpret_cast<const float4*>(betas + sb);
+          const float4 b1 = *reinterpret_cast<const float4*>(betas + sb + 4);
+          x[0] = u0.x * b0.x; x[1] = u0.y * b0.y; x[2] = u0.z * b0.z; x[3] = u0.w * b0.w;
+          x[4] = u1.x * b1.x; x[5] = u1.y * b1.y; x[6] = u1.z * b1.z; x[7] = u1.w * b1.w;
+        }
+        const Frag<F32> bw = frag_from_f32<F32>(x);
+        const Frag<F32> bq = lds_frag<F32, CF::RBC>(smem + CF::PB, t, sb * E);
+#pragma unroll
+        for (int rr = 0; rr < RPW; ++rr) {
+          const int c = 16 * (wave * RPW + rr) + l16;
+          const Frag<F32> a = lds_frag<F32, CF::RBC>(smem + CF::KBT, c, sb * E);
+          aw[rr][ct] = mma32<F32>(aw[rr][ct], a, bw);
+          aq[rr][ct] = mma32<F32>(aq[rr][ct], a, bq);
+        }
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) {
+      const int c = 16 * (wave * RPW + rr) + 4 * g4;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int t = 16 * ct + l16;
+        buf_put4<F32>(rw, SL::W + (t * D + c) * E, aw[rr][ct][0], aw[rr][ct][1], aw[rr][ct][2],
+                      aw[rr][ct][3]);
+        float qb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qb[i] = lds_get1<F32>(smem + CF::QB + swz<CF::RBD>(t, (c + i) * E));
+        buf_put4<F32>(rw, SL::QP + (t * D + c) * E, p.scale * (qb[0] - aq[rr][ct][0]),
+                      p.scale * (qb[1] - aq[rr][ct][1]), p.scale * (qb[2] - aq[rr][ct][2]),
+                      p.scale * (qb[3] - aq[rr][ct][3]));
+      }
+    }
+  }
+  // Tb = T Diag(beta) -> workspace, 16 consecutive entries per thread
+  {
+    const int t = tid >> 2, s0 = (tid & 3) * 16;
+    float x[16];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 u = *reinterpret_cast<const float4*>(atc + swz<256>(t, (s0 + 4 * q4) * 4));
+      const float4 b = *reinterpret_cast<const float4*>(betas + s0 + 4 * q4);
+      x[4 * q4] = u.x * b.x; x[4 * q4 + 1] = u.y * b.y; x[4 * q4 + 2] = u.z * b.z; x[4 * q4 + 3] = u.w * b.w;
+    }
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+      buf_put4<F32>(rw, SL::TB + (t * kC + s0 + 4 * q4) * E, x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2],
+                    x[4 * q4 + 3]);
+  }
+}
+
+// ================================================================= kernel 2
+
+template <int D, int DVS, typename TIn>
+struct ScanCfg {
+  static constexpr bool F32 = std::is_same<TIn, float>::value;
+  static constexpr int E = F32 ? 4 : 2;
+  static constexpr int EI = sizeof(TIn);
+  static constexpr int NJT = DVS / 16;
+  static constexpr int NKK = D / 32;
+  static constexpr int RT = D / 64;             // state row tiles per wavefront
+  static constexpr int NSPLIT = D / DVS;
+  static constexpr int RBD = D * E;             // SB rows [j][c]
+  static constexpr int RBC = kC * E;            // VT, DT rows [j][t]
+  static constexpr int RBO = DVS * E + 16;      // OST rows [t][j] (padded)
+  static constexpr int SB = 0;
+  static constexpr int VT = SB + DVS * RBD;
+  static constexpr int DT = VT + DVS * RBC;
+  static constexpr int OST = DT + DVS * RBC;
+  static constexpr int ORD = OST + kC * RBO;
+  static constexpr int LDS = ORD + 256 * 4;
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+struct ScanParams {
+  const void* v;
+  const float* s0;
+  void* out;
+  float* sT;
+  const char* ws;
+  SeqArgs sa;
+};
+
+template <int D, int DVS, typename TIn>
+__global__ __launch_bounds__(kThreads, 1) void state_scan_kernel(ScanParams p) {
+  using CF = ScanCfg<D, DVS, TIn>;
+  using SL = Slot<D, CF::F32>;
+  constexpr bool F32 = CF::F32;
+  constexpr int E = CF::E, EI = CF::EI, NJT = CF::NJT, NKK = CF::NKK, RT = CF::RT;
+  __shared__ __attribute__((aligned(16))) char smem[CF::LDS];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int H = p.sa.H, N = p.sa.N;
+
+  // XCD-aware placement: the dv slices of one (sequence, head) land on one XCD
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, r8 = bid >> 3;
+  const int grp = (r8 / CF::NSPLIT) * 8 + xcd;
+  const int split = r8 % CF::NSPLIT;
+  if (grp >= N * H) return;
+  const int rank = grp / H, h = grp % H;
+  int n = rank;
+  if (p.sa.cu != nullptr && N <= 256) {   // longest sequence first
+    int* ord = reinterpret_cast<int*>(smem + CF::ORD);
+    int mylen = 0;
+    if (tid < N) {
+      int a, l;
+      seq_bounds(p.sa, tid, a, l);
+      mylen = l;
+      ord[tid] = l;
+    }
+    __syncthreads();
+    int rk = 0;
+    if (tid < N)
+      for (int m = 0; m < N; ++m) {
+        const int lm = ord[m];
+        rk += (lm > mylen) || (lm == mylen && m < tid);
+      }
+    __syncthreads();
+    if (tid < N) ord[rk] = tid;
+    __syncthreads();
+    n = ord[rank];
+    __syncthreads();
+  }
+  int tok0, len;
+  seq_bounds(p.sa, n, tok0, len);
+  const int nchunks = (len + kC - 1) / kC;
+  const int sbase = slot_base(tok0, n);
+  const int j0 = split * DVS;
+
+  // state tiles (rt, jt): rows c = 16*rt + 4*g4 + i, columns j = 16*jt + l16
+  f32x4_t S[RT][NJT];
+  {
+    const float* s0 = p.s0 ? p.s0 + (static_cast<int64_t>(n) * H + h) * D * D : nullptr;
+#pragma unroll
+    for (int ri = 0; ri < RT; ++ri)
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt) {
+        const int rt = wave * RT + ri;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          S[ri][jt][i] = s0 ? s0[(16 * rt + 4 * g4 + i) * D + j0 + 16 * jt + l16] : 0.f;
+        lds_put4<F32>(smem + CF::SB + swz<CF::RBD>(16 * jt + l16, (16 * rt + 4 * g4) * E),
+                      S[ri][jt][0], S[ri][jt][1], S[ri][jt][2], S[ri][jt][3]);
+      }
+  }
+  __syncthreads();
+
+  const uint32_t rs_v = static_cast<uint32_t>(H) * D * EI;
+  constexpr int VPR = DVS / 8;                          // 8-value pieces per V row
+
+  for (int ci = 0; ci < nchunks; ++ci) {
+    const int t0 = tok0 + ci * kC;
+    const int nrow = min(kC, len - ci * kC);
+    const auto rw = make_rsrc(p.ws + (static_cast<int64_t>(sbase + ci) * H + h) * SL::BYTES, SL::BYTES);
+    const int64_t vbase = (static_cast<int64_t>(t0) * H + h) * D + j0;
+    const uint32_t vbytes = (nrow - 1) * rs_v + DVS * EI;
+    const auto rv = make_rsrc(static_cast<const TIn*>(p.v) + vbase, vbytes);
+    const auto ro = make_rsrc(static_cast<TIn*>(p.out) + vbase, vbytes);
+
+    // operand fragments straight from the workspace
+    Frag<F32> fw[NKK], fq[NKK], ftb[2], fpp[2], fkt[RT][2];
+    const int trow = 16 * wave + l16;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const uint32_t o = (trow * D + kk * 32 + g4 * 8) * E;
+      fw[kk] = buf_frag<F32>(rw, SL::W + o, 0);
+      fq[kk] = buf_frag<F32>(rw, SL::QP + o, 0);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const uint32_t o = (trow * kC + kk * 32 + g4 * 8) * E;
+      ftb[kk] = buf_frag<F32>(rw, SL::TB + o, 0);
+      fpp[kk] = buf_frag<F32>(rw, SL::PP + o, 0);
+#pragma unroll
+      for (int ri = 0; ri < RT; ++ri) {
+        const int c = 16 * (wave * RT + ri) + l16;
+        fkt[ri][kk] = buf_frag<F32>(rw, SL::KT + (c * kC + kk * 32 + g4 * 8) * E, 0);
+      }
+    }
+    float lam[RT][4];
+#pragma unroll
+    for (int ri = 0; ri < RT; ++ri) {
+      const i32x4_t l4 = buf_ld128(rw, SL::LAM + (16 * (wave * RT + ri) + 4 * g4) * 4, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lam[ri][i] = __int_as_float(l4[i]);
+    }
+    // V slice, transposed to [j][t] (rows past the sequence end read as zero)
+    for (int pc = tid; pc < kC * VPR; pc += kThreads) {
+      const int vrow = pc / VPR, vcol = (pc % VPR) * 8;
+      if constexpr (F32) {
+        const i32x4_t a = buf_ld128(rv, vcol * 4, vrow * rs_v);
+        const i32x4_t b = buf_ld128(rv, vcol * 4 + 16, vrow * rs_v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          *reinterpret_cast<int*>(smem + CF::VT + swz<CF::RBC>(vcol + i, vrow * 4)) = a[i];
+          *reinterpret_cast<int*>(smem + CF::VT + swz<CF::RBC>(vcol + 4 + i, vrow * 4)) = b[i];
+        }
+      } else {
+        const i32x4_t a = buf_ld128(rv, vcol * 2, vrow * rs_v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          *reinterpret_cast<uint16_t*>(smem + CF::VT + swz<CF::RBC>(vcol + e, vrow * 2)) =
+              static_cast<uint16_t>(static_cast<uint32_t>(a[e >> 1]) >> (16 * (e & 1)));
+      }
+    }
+    __syncthreads();
+
+    // U = Tb V and O_v = P V (state independent), W S and Q' S (state products)
+#pragma unroll
+    for (int jt = 0; jt < NJT; ++jt) {
+      f32x4_t u = {0.f, 0.f, 0.f, 0.f}, ov = u, ws = u, qs = u;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const Frag<F32> b = lds_frag<F32, CF::RBC>(smem + CF::VT, 16 * jt + l16, (kk * 32 + g4 * 8) * E);
+        u = mma32<F32>(u, ftb[kk], b);
+        ov = mma32<F32>(ov, fpp[kk], b);
+      }
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const Frag<F32> b = lds_frag<F32, CF::RBD>(smem + CF::SB, 16 * jt + l16, (kk * 32 + g4 * 8) * E);
+        ws = mma32<F32>(ws, fw[kk], b);
+        qs = mma32<F32>(qs, fq[kk], b);
+      }
+      // Delta = U - W S -> [j][t];  O = Q' S + P V -> [t][j]
+      const int j = 16 * jt + l16, t = 16 * wave + 4 * g4;
+      lds_put4<F32>(smem + CF::DT + swz<CF::RBC>(j, t * E), u[0] - ws[0], u[1] - ws[1],
+                    u[2] - ws[2], u[3] - ws[3]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lds_set1<F32>(smem + CF::OST + (t + i) * CF::RBO + j * E, qs[i] + ov[i]);
+    }
+    __syncthreads();
+
+    // S <- Diag(Lambda) S + Kt^T Delta
+#pragma unroll
+    for (int ri = 0; ri < RT; ++ri) {
+      const int rt = wave * RT + ri;
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt) {
+        f32x4_t acc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = S[ri][jt][i] * lam[ri][i];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const Frag<F32> b = lds_frag<F32, CF::RBC>(smem + CF::DT, 16 * jt + l16, (kk * 32 + g4 * 8) * E);
+          acc = mma32<F32>(acc, fkt[ri][kk], b);
+        }
+        S[ri][jt] = acc;
+        lds_put4<F32>(smem + CF::SB + swz<CF::RBD>(16 * jt + l16, (16 * rt + 4 * g4) * E),
+                      acc[0], acc[1], acc[2], acc[3]);
+      }
+    }
+    // output rows as 16-byte pieces; rows past the sequence end are dropped
+    {
+      constexpr int PPR = DVS * E / 16;
+      for (int pc = tid; pc < kC * PPR; pc += kThreads) {
+        const int t = pc / PPR, part = pc % PPR;
+        const i32x4_t val = *reinterpret_cast<const i32x4_t*>(smem + CF::OST + t * CF::RBO + part * 16);
+        buf_st128(val, ro, part * 16, t * rs_v);
+      }
+    }
+    __syncthreads();
+  }
+
+  if (p.sT) {
+    float* sT = p.sT + (static_cast<int64_t>(n) * H + h) * D * D;
+#pragma unroll
+    for (int ri = 0; ri < RT; ++ri)
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sT[(16 * (wave * RT + ri) + 4 * g4 + i) * D + j0 + 16 * jt + l16] = S[ri][jt][i];
+  }
+}
+
+// ---------------------------------------------------------------- launch
+
+template <int D, int DVS, typename TIn>
+hipError_t launch_scan(const PrefillArgs& a, const SeqArgs& sa, const char* ws) {
+  using CF = ScanCfg<D, DVS, TIn>;
+  const int groups = a.N * a.H;
+  const int grid = ((groups + 7) / 8) * 8 * CF::NSPLIT;
+  ScanParams sp{a.v, a.initial_state, a.out, a.final_state, ws, sa};
+  hipLaunchKernelGGL((state_scan_kernel<D, DVS, TIn>), dim3(grid), dim3(kThreads), 0, a.stream, sp);
+  return hipGetLastError();
+}
+
+template <int D, typename TIn>
+hipError_t launch_all(const PrefillArgs& a) {
+  constexpr bool F32 = std::is_same<TIn, float>::value;
+  using SL = Slot<D, F32>;
+  const SeqArgs sa{a.cu_seqlens, a.N, a.T, a.total_T, a.H};
+  const int64_t slots = (a.total_T + kC - 1) / kC + a.N;
+  const size_t ws_bytes = static_cast<size_t>(slots) * a.H * SL::BYTES;
+  char* ws = nullptr;
+  hipError_t err = hipMallocAsync(reinterpret_cast<void**>(&ws), ws_bytes, a.stream);
+  if (err != hipSuccess) return err;
+  PrepParams pp{a.q, a.k, a.g, a.beta, ws, sa, a.scale};
+  hipLaunchKernelGGL((chunk_prep_kernel<D, TIn>), dim3(static_cast<unsigned>(slots * a.H)),
+                     dim3(kThreads), 0, a.stream, pp);
+  err = hipGetLastError();
+  if (err == hipSuccess) {
+    // enough (sequence, head, dv slice) workgroups to cover the machine's 256 CUs
+    const int streams = a.N * a.H;
+    if constexpr (D == 128) {
+      if (streams < 64) err = launch_scan<D, 16, TIn>(a, sa, ws);
+      else if (streams < 128) err = launch_scan<D, 32, TIn>(a, sa, ws);
+      else if (streams < 512) err = launch_scan<D, 64, TIn>(a, sa, ws);
+      else err = launch_scan<D, 128, TIn>(a, sa, ws);
+    } else {
+      if (streams < 64) err = launch_scan<D, 16, TIn>(a, sa, ws);
+      else if (streams < 256) err = launch_scan<D, 32, TIn>(a, sa, ws);
+      else err = launch_scan<D, 64, TIn>(a, sa, ws);
+    }
+  }
+  const hipError_t ferr = hipFreeAsync(ws, a.stream);
+  return err != hipSuccess ? err : ferr;
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a) {
+  if (a.dtype_f32) {
+    if (a.d == 64) return launch_all<64, float>(a);
+    return hipErrorNotSupported;
+  }
+  if (a.d == 128) return launch_all<128, bf16_t>(a);
+  return launch_all<64, bf16_t>(a);
+}
+
+}  // namespace kda

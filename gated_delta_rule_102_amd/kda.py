@@ -1,0 +1,198 @@
+"""Thin ctypes binding over libkda.so with the same entry-point names as the C ABI.
+
+This module only marshals arguments: it checks devices, dtypes, shapes and
+contiguity, allocates outputs with PyTorch (device memory is PyTorch's job here),
+and passes raw device pointers plus the current HIP stream to the library.
+Every step of KDA runs in the library's HIP kernels.  There is no fallback: if
+libkda.so is missing or the device is not gfx950, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_BF16, KDA_F32 = 0, 1
+_lib = None
+
+EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd",
+           "kda_chunk_fwd_varlen", "kda_decode_step")
+
+
+class KDAError(RuntimeError):
+    """A non-zero status returned by libkda.so."""
+
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} failed: {status} ({status_string(status)})")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libkda.so (built in-tree by ``python -m gated_delta_rule_102_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m gated_delta_rule_102_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.kda_abi_version.argtypes = []
+    lib.kda_abi_version.restype = i32
+    lib.kda_status_string.argtypes = [i32]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                  f32, i32, vp]
+    lib.kda_chunk_fwd.restype = i32
+    lib.kda_chunk_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                         i32, i32, f32, i32, vp]
+    lib.kda_chunk_fwd_varlen.restype = i32
+    lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp]
+    lib.kda_decode_step.restype = i32
+    _lib = lib
+    return lib
+
+
+def kda_abi_version() -> int:
+    return load_library().kda_abi_version()
+
+
+def status_string(status: int) -> str:
+    return load_library().kda_status_string(int(status)).decode()
+
+
+kda_status_string = status_string
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"KDA inputs must be bfloat16 or float32, got {t.dtype}")
+
+
+def _check(ts, dtype, device):
+    for name, t in ts.items():
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+        if t.dtype != dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def _check_state(name, t, shape, device):
+    if t is None:
+        return
+    if t.device != device or t.dtype != torch.float32 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 tensor on {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _raise(fn, rc):
+    if rc != 0:
+        raise KDAError(fn, rc)
+
+
+def kda_chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=True,
+                  out=None, final_state=None):
+    """Chunked prefill.  q, k, g: [B,T,H,dk]; v: [B,T,H,dv]; beta: [B,T,H].
+
+    Returns ``(out [B,T,H,dv], final_state [B,H,dk,dv] fp32 or None)``.
+    ``final_state`` may be passed (and may be ``initial_state`` for in-place use).
+    """
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dtype, device = q.dtype, q.device
+    _check(dict(q=q, k=k, v=v, g=g, beta=beta), dtype, device)
+    if k.shape != q.shape or g.shape != q.shape or v.shape[:3] != q.shape[:3] \
+            or beta.shape != q.shape[:3]:
+        raise ValueError("shape mismatch among q, k, v, g, beta")
+    _check_state("initial_state", initial_state, (B, H, dk, dv), device)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=dtype, device=device)
+    _check(dict(out=out), dtype, device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=device)
+    _check_state("final_state", final_state, (B, H, dk, dv), device)
+    scale = 1.0 / math.sqrt(dk) if scale is None else float(scale)
+    rc = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                           _ptr(out), _ptr(final_state), B, T, H, dk, dv, scale,
+                           _dtype_code(q), _stream(q))
+    _raise("kda_chunk_fwd", rc)
+    return out, final_state
+
+
+def kda_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, scale=None, initial_state=None,
+                         output_final_state=True, out=None, final_state=None):
+    """Packed variable-length prefill.  q, k, g: [1,total_T,H,dk] (or [total_T,H,dk]);
+    cu_seqlens: int32 [N+1] on the device.  Returns ``(out, final_state [N,H,dk,dv])``."""
+    lib = load_library()
+    H, dk = q.shape[-2], q.shape[-1]
+    dv = v.shape[-1]
+    total_T = q.numel() // (H * dk)
+    N = cu_seqlens.numel() - 1
+    dtype, device = q.dtype, q.device
+    _check(dict(q=q, k=k, v=v, g=g, beta=beta), dtype, device)
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != device:
+        raise ValueError("cu_seqlens must be int32 on the same device")
+    if k.shape != q.shape or g.shape != q.shape or v.numel() != total_T * H * dv \
+            or beta.numel() != total_T * H:
+        raise ValueError("shape mismatch among q, k, v, g, beta")
+    _check_state("initial_state", initial_state, (N, H, dk, dv), device)
+    if out is None:
+        out = torch.empty(v.shape, dtype=dtype, device=device)
+    _check(dict(out=out), dtype, device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=device)
+    _check_state("final_state", final_state, (N, H, dk, dv), device)
+    scale = 1.0 / math.sqrt(dk) if scale is None else float(scale)
+    rc = lib.kda_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                  _ptr(initial_state), _ptr(out), _ptr(final_state),
+                                  _ptr(cu_seqlens.contiguous()), N, total_T, H, dk, dv, scale,
+                                  _dtype_code(q), _stream(q))
+    _raise("kda_chunk_fwd_varlen", rc)
+    return out, final_state
+
+
+def kda_decode_step(q, k, v, g, beta, state, scale=None, out=None):
+    """One decode token.  q, k, g: [B,H,dk]; v: [B,H,dv]; beta: [B,H];
+    state: [B,H,dk,dv] fp32, updated in place.  Returns out [B,H,dv]."""
+    lib = load_library()
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dtype, device = q.dtype, q.device
+    _check(dict(q=q, k=k, v=v, g=g, beta=beta), dtype, device)
+    if k.shape != q.shape or g.shape != q.shape or v.shape[:2] != q.shape[:2] \
+            or beta.shape != q.shape[:2]:
+        raise ValueError("shape mismatch among q, k, v, g, beta")
+    _check_state("state", state, (B, H, dk, dv), device)
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=dtype, device=device)
+    _check(dict(out=out), dtype, device)
+    scale = 1.0 / math.sqrt(dk) if scale is None else float(scale)
+    rc = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
+                             _ptr(out), B, H, dk, dv, scale, _dtype_code(q), _stream(q))
+    _raise("kda_decode_step", rc)
+    return out
+
+
+# short aliases
+chunk_fwd = kda_chunk_fwd
+chunk_fwd_varlen = kda_chunk_fwd_varlen
+decode_step = kda_decode_step

@@ -1,0 +1,133 @@
+/*
+ * kda.h -- C ABI of libkda.so: Kimi Delta Attention (KDA) on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * KDA is linear attention with one fixed-size state per (sequence, head): a
+ * dk x dv fp32 matrix S whose rows are key channels.  Each token forgets old
+ * content per key channel and writes new content by a delta rule:
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(exp g_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T (scale * q_t)
+ *
+ * Sources (page title, section):
+ *  - neurohive.io Kimi K3 review, "Sequence length: hybrid KDA and Gated MLA
+ *    attention": delta rule (forget + write), retention factor per channel, log
+ *    decay bounded below at -5, every tile on dense matrix multiplies.
+ *  - best.xiaohu.ai "Kimi K3 tech report", "Sequence length: replacing most
+ *    attention layers with fixed-size memory": state size independent of context
+ *    length; older context decays gradually across channels.
+ *  - neurohive.io review, "Training and inference infrastructure", and
+ *    best.xiaohu.ai, "Infrastructure efficiency": one fixed-size state per
+ *    request, restored from snapshots for prefix caching (state in -> state out).
+ * The pages give the rule in words; the equation above is its plainest reading
+ * (decay first, then the delta correction on the decayed state; the output reads
+ * the state after the token's own write).
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers owned by the caller, contiguous and
+ *    row-major.  Nothing is allocated or freed by the library.
+ *  - Alignment (KDA_ERR_ALIGN otherwise): prefill v and out 16 bytes, q, k, g and
+ *    the states 4 bytes, beta its element size; decode state 16 bytes, every
+ *    other pointer its element size.
+ *  - Layouts: q, k, g  [tokens, H, dk];  v, out [tokens, H, dv];  beta [tokens, H];
+ *    states [seqs, H, dk, dv] fp32 (row i = key channel i).
+ *  - `dtype` (KDA_BF16 or KDA_F32) is the element type of q, k, v, g, beta and
+ *    out.  States are always fp32.  Arithmetic is fp32 with bf16 matrix-core
+ *    operands for KDA_BF16 and fp32 matrix-core operands for KDA_F32.
+ *  - q and k are used as given (the library does not normalise them) and no
+ *    output gate or norm is applied.
+ *  - Value preconditions, not checked: -5 <= g <= 0, 0 <= beta <= 1, all finite,
+ *    |k| <= 1.  Outside them the result is unspecified (never a memory fault).
+ *  - Work is enqueued on `stream` and returns immediately; execution errors
+ *    surface at the caller's next synchronisation.  No entry point keeps state
+ *    between calls, so calls on different streams may overlap when their
+ *    buffers do not.
+ *  - Return value: KDA_OK, or a negative KDA_ERR_* code.  When a code other
+ *    than KDA_OK is returned nothing was launched.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+enum kda_dtype { KDA_BF16 = 0, KDA_F32 = 1 };
+
+enum kda_status {
+  KDA_OK = 0,
+  KDA_ERR_NULL = -1,        /* a required pointer is NULL                    */
+  KDA_ERR_SHAPE = -2,       /* a size is <= 0, or too large for 32-bit grids */
+  KDA_ERR_HEAD_DIM = -3,    /* dk or dv not in {64, 128}, dk != dv, or fp32
+                               prefill with dk != 64                        */
+  KDA_ERR_DTYPE = -4,       /* dtype is not KDA_BF16 or KDA_F32              */
+  KDA_ERR_ALIGN = -5,       /* a pointer is not aligned as required          */
+  KDA_ERR_HIP = -6,         /* the HIP runtime reported a launch error       */
+  KDA_ERR_NO_DEVICE = -7    /* the current device is not gfx950              */
+};
+
+/* ABI version of the loaded library (KDA_ABI_VERSION). */
+int kda_abi_version(void);
+
+/* Static, human-readable text for a kda_status value. */
+const char* kda_status_string(int status);
+
+/*
+ * Chunked prefill over B sequences of T tokens each (chunk = 64 tokens).
+ *
+ *  q, k, g        [B, T, H, dk]  (dtype)
+ *  v              [B, T, H, dv]  (dtype)
+ *  beta           [B, T, H]      (dtype)
+ *  initial_state  [B, H, dk, dv] fp32, or NULL for a zero state
+ *  out            [B, T, H, dv]  (dtype), written for every token
+ *  final_state    [B, H, dk, dv] fp32, or NULL to skip; may equal
+ *                 initial_state (updated in place)
+ *  scale          multiplies q (typically 1/sqrt(dk))
+ * dk == dv, both 64 or 128 (KDA_F32: 64 only).  Produces the same result as
+ * running the recurrence token by token, up to floating-point rounding.
+ */
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
+                  const void* beta, const float* initial_state, void* out,
+                  float* final_state, int B, int T, int H, int dk, int dv,
+                  float scale, int dtype, hipStream_t stream);
+
+/*
+ * Chunked prefill over N packed sequences of different lengths.
+ *
+ *  cu_seqlens     int32 DEVICE array of N+1 non-decreasing token offsets,
+ *                 cu_seqlens[0] == 0, cu_seqlens[N] == total_T.  A sequence of
+ *                 length 0 gets out untouched and final_state = initial_state.
+ *  q, k, g        [total_T, H, dk]; v, out [total_T, H, dv]; beta [total_T, H]
+ *  initial_state  [N, H, dk, dv] fp32 or NULL;  final_state [N, H, dk, dv] or NULL
+ * Chunks restart at every sequence start and no state crosses a sequence
+ * boundary.  Sequences are scheduled longest first when N <= 256.  The offsets
+ * are read on the device only; inconsistent offsets are clamped to [0, total_T].
+ * Head sizes as for kda_chunk_fwd.
+ */
+int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void* g,
+                         const void* beta, const float* initial_state, void* out,
+                         float* final_state, const int32_t* cu_seqlens, int N,
+                         int total_T, int H, int dk, int dv, float scale, int dtype,
+                         hipStream_t stream);
+
+/*
+ * One decode token for B sequences, updating `state` in place.
+ *
+ *  q, k, g  [B, H, dk] (dtype);  v, out [B, H, dv] (dtype);  beta [B, H] (dtype)
+ *  state    [B, H, dk, dv] fp32, read and overwritten with the new state
+ * Same result as kda_chunk_fwd with T = 1 and final_state == initial_state.
+ */
+int kda_decode_step(const void* q, const void* k, const void* v, const void* g,
+                    const void* beta, float* state, void* out, int B, int H, int dk,
+                    int dv, float scale, int dtype, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */
