@@ -1,0 +1,93 @@
+"""Host-side checks of libkda.so that need no GPU.
+
+The library must load, export every function include/kda.h declares, and
+reject bad arguments with its documented codes before touching any device.
+The Python binding must refuse to run without the library (no fallback).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+LIB = os.path.join(ROOT, "gated_delta_rule_102_amd", "libkda.so")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from gated_delta_rule_102_amd import build
+        build.build()
+    return ctypes.CDLL(LIB)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted([
+        "kda_abi_version", "kda_status_string", "kda_chunk_fwd", "kda_chunk_fwd_varlen",
+        "kda_decode_step"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in exported, f"{name} is declared in kda.h but not exported"
+        assert hasattr(lib, name)
+
+
+def test_version_and_status_strings(lib):
+    lib.kda_abi_version.restype = ctypes.c_int
+    lib.kda_status_string.restype = ctypes.c_char_p
+    assert lib.kda_abi_version() == 1
+    for code in range(-7, 1):
+        assert lib.kda_status_string(code)
+    assert lib.kda_status_string(-99) == b"unknown status"
+
+
+def test_argument_checks_precede_any_device_call(lib):
+    """Invalid arguments are rejected with their codes on a machine with no GPU."""
+    f = lib.kda_chunk_fwd
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    f.argtypes = [vp] * 8 + [i32] * 5 + [f32, i32, vp]
+    f.restype = i32
+    p = vp(4096)      # an aligned address that is never dereferenced
+    mis = vp(4098)
+    assert f(None, p, p, p, p, None, p, None, 1, 64, 1, 128, 128, 0.1, 0, None) == -1
+    assert f(p, p, p, p, p, None, p, None, 0, 64, 1, 128, 128, 0.1, 0, None) == -2
+    assert f(p, p, p, p, p, None, p, None, 1, 64, 1, 100, 100, 0.1, 0, None) == -3
+    assert f(p, p, p, p, p, None, p, None, 1, 64, 1, 128, 128, 0.1, 1, None) == -3
+    assert f(p, p, p, p, p, None, p, None, 1, 64, 1, 128, 128, 0.1, 9, None) == -4
+    assert f(mis, p, p, p, p, None, p, None, 1, 64, 1, 128, 128, 0.1, 0, None) == -5
+    # valid arguments reach the device check, which fails without a gfx950 device
+    assert f(p, p, p, p, p, None, p, None, 1, 64, 1, 128, 128, 0.1, 0, None) in (-6, -7)
+    d = lib.kda_decode_step
+    d.argtypes = [vp] * 7 + [i32] * 4 + [f32, i32, vp]
+    d.restype = i32
+    assert d(p, p, p, p, p, None, p, 2, 2, 128, 128, 0.1, 0, None) == -1
+    assert d(p, p, p, p, p, vp(4104), p, 2, 2, 128, 128, 0.1, 0, None) == -5
+    v = lib.kda_chunk_fwd_varlen
+    v.argtypes = [vp] * 9 + [i32] * 5 + [f32, i32, vp]
+    v.restype = i32
+    assert v(p, p, p, p, p, None, p, None, None, 2, 64, 1, 128, 128, 0.1, 0, None) == -1
+    assert v(p, p, p, p, p, None, p, None, p, 0, 64, 1, 128, 128, 0.1, 0, None) == -2
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    from gated_delta_rule_102_amd import kda
+    saved = kda._lib
+    try:
+        kda._lib = None
+        with pytest.raises(RuntimeError, match="not built"):
+            kda.load_library(str(tmp_path / "missing.so"))
+    finally:
+        kda._lib = saved
