@@ -85,17 +85,18 @@ __device__ __forceinline__ Frag<F32> lds_frag(const char* base, int row, int byt
   return f;
 }
 
-// Same, from global memory through a buffer resource (byte offset).
+// One fragment stored in fragment order at byte offset voff (lane's 16 bytes; the
+// fp32 second half sits 1 KB further).
 template <bool F32>
-__device__ __forceinline__ Frag<F32> buf_frag(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+__device__ __forceinline__ Frag<F32> buf_frag2(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
   Frag<F32> f;
   if constexpr (F32) {
-    const i32x4_t a = buf_ld128(r, voff, soff);
-    const i32x4_t b = buf_ld128(r, voff + 16, soff);
+    const i32x4_t a = buf_ld128(r, voff, 0);
+    const i32x4_t b = buf_ld128(r, voff + 1024, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) { f.v[i] = __int_as_float(a[i]); f.v[4 + i] = __int_as_float(b[i]); }
   } else {
-    f.v = __builtin_bit_cast(bf16x8_t, buf_ld128(r, voff, soff));
+    f.v = __builtin_bit_cast(bf16x8_t, buf_ld128(r, voff, 0));
   }
   return f;
 }
@@ -223,6 +224,20 @@ struct Slot {
   static constexpr int BYTES = (LAM + D * 4 + 255) / 256 * 256;
 };
 
+// Byte offset of element (row, k) of a workspace operand stored in fragment order:
+// the operand is cut into 16-row x 32-k fragments (f = (row/16) * (K/32) + k/32), and
+// each fragment is laid out exactly as a wavefront holds it for the matrix cores --
+// lane (k%32)/8*16 + row%16 owns 8 consecutive k -- so one 16-byte load per lane
+// reads a contiguous 1 KB (fp32: two such halves of 4 elements each).
+template <int K, bool F32>
+__device__ __forceinline__ uint32_t frag_off(int row, int k) {
+  const int f = (row >> 4) * (K / 32) + (k >> 5);
+  const int l = ((k & 31) >> 3) * 16 + (row & 15);
+  const int e = k & 7;
+  if constexpr (F32) return static_cast<uint32_t>(((f * 2 + (e >> 2)) * 64 + l) * 16 + (e & 3) * 4);
+  else return static_cast<uint32_t>((f * 64 + l) * 16 + e * 2);
+}
+
 // ================================================================= kernel 1
 
 template <int D, typename TIn>
@@ -236,9 +251,11 @@ struct PrepCfg {
   static constexpr int NKK = D / 32;
   // R1, phase 1: sub-tile referenced operands
   static constexpr int QS = 0, KS = QS + kC * RBD, KT = KS + kC * RBD, R1A = KT + kC * RBD;
-  // R1, phase 2: chunk-referenced operands and P
-  static constexpr int QB = 0, KBT = QB + kC * RBD, PB = KBT + D * RBC, R1B = PB + kC * RBC;
-  static constexpr int R1 = R1A > R1B ? R1A : R1B;
+  // R1, phase 2: chunk-referenced operands, P, and the 32x32 inverse intermediate
+  static constexpr int QB = 0, KBT = QB + kC * RBD, PB = KBT + D * RBC, XS = PB + kC * RBC;
+  static constexpr int XLD = 17;                 // fp32 row stride of the 16x16 X tiles
+  static constexpr int R1B = XS + 4 * 16 * XLD * 4;
+  static constexpr int R1 = (R1A > R1B ? R1A : R1B + 15) / 16 * 16;
   static constexpr int AT = R1;                  // [64][64] fp32: A, then T in place
   static constexpr int MB = AT + kC * kC * 4;    // [64][64] operand: M
   static constexpr int FIJ = MB + kC * RBC;      // [6][D] fp32 pair factors
@@ -253,12 +270,47 @@ struct PrepParams {
   char* ws;
   SeqArgs sa;
   float scale;
+  int items;       // workspace slots x heads
 };
 
+// Raw input words of one token row for the CPL channels a lane owns.
+template <typename TIn, int CPL> struct RawRow;
+template <> struct RawRow<bf16_t, 2> { using type = uint32_t; };
+template <> struct RawRow<bf16_t, 1> { using type = uint16_t; };
+template <> struct RawRow<float, 1> { using type = uint32_t; };
+
+template <typename TIn, int CPL>
+struct RawChunk {
+  using R = typename RawRow<TIn, CPL>::type;
+  R g[16], k[16], q[16];
+  uint32_t beta;
+};
+
+// Everything that names one (chunk, head) work item.
+struct PrepItem {
+  bool valid;
+  int slot, h, t0, nrow;
+};
+
+__device__ __forceinline__ PrepItem prep_item(const PrepParams& p, int item) {
+  PrepItem it{false, 0, 0, 0, 0};
+  if (item >= p.items) return it;
+  it.slot = item / p.sa.H;
+  it.h = item % p.sa.H;
+  int n, chunk, tok0, len;
+  if (!locate_slot(p.sa, it.slot, n, chunk, tok0, len)) return it;
+  it.valid = true;
+  it.t0 = tok0 + chunk * kC;
+  it.nrow = min(kC, len - chunk * kC);
+  return it;
+}
+
+// One workgroup per (chunk, head) work item.
 template <int D, typename TIn>
 __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepParams p) {
   using CF = PrepCfg<D, TIn>;
   using SL = Slot<D, CF::F32>;
+  using RC = RawChunk<TIn, CF::CPL>;
   constexpr bool F32 = CF::F32;
   constexpr int CPL = CF::CPL;
   constexpr int E = CF::E;
@@ -268,366 +320,416 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepParams p) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, g4 = lane >> 4;
   const int H = p.sa.H;
-  const int slot = blockIdx.x / H;
-  const int h = blockIdx.x % H;
-  int n, chunk, stok0, slen;
-  if (!locate_slot(p.sa, slot, n, chunk, stok0, slen)) return;
-  const int t0 = stok0 + chunk * kC;
-  const int nrow = min(kC, slen - chunk * kC);
-
-  const uint32_t rs_qk = static_cast<uint32_t>(H) * D * EI;    // row stride (bytes)
-  const int64_t base_qk = (static_cast<int64_t>(t0) * H + h) * D;
-  const uint32_t bytes_qk = (nrow - 1) * rs_qk + D * EI;
-  const auto rq = make_rsrc(static_cast<const TIn*>(p.q) + base_qk, bytes_qk);
-  const auto rk = make_rsrc(static_cast<const TIn*>(p.k) + base_qk, bytes_qk);
-  const auto rg = make_rsrc(static_cast<const TIn*>(p.g) + base_qk, bytes_qk);
-  const auto rb = make_rsrc(static_cast<const TIn*>(p.beta) + static_cast<int64_t>(t0) * H + h,
-                            (nrow - 1) * H * EI + EI);
-  const auto rw = make_rsrc(p.ws + (static_cast<int64_t>(slot) * H + h) * SL::BYTES, SL::BYTES);
+  const uint32_t rs_qk = static_cast<uint32_t>(H) * D * EI;    // token row stride (bytes)
 
   char* atc = smem + CF::AT;
   float* btot = reinterpret_cast<float*>(smem + CF::BTOT);
   float* betas = reinterpret_cast<float*>(smem + CF::BETA);
   float* fij = reinterpret_cast<float*>(smem + CF::FIJ);
+  auto at_el = [&](int row, int col) -> float& {
+    return *reinterpret_cast<float*>(atc + swz<256>(row, col * 4));
+  };
 
-  // the strictly-upper sub-tiles of A/T and of M are read as zeros
+  // the strictly-upper sub-tiles of A/T and of M are read as zeros; nothing else
+  // writes them, so clearing them once serves every item of this workgroup
   for (int e = tid; e < 6 * 256; e += kThreads) {
     int I, J;
     upper_pair(e >> 8, I, J);
     const int row = 16 * I + ((e >> 4) & 15), col = 16 * J + (e & 15);
-    *reinterpret_cast<float*>(atc + swz<256>(row, col * 4)) = 0.f;
+    at_el(row, col) = 0.f;
     lds_set1<F32>(smem + CF::MB + swz<CF::RBC>(row, col * E), 0.f);
   }
 
-  // ------------------------------------------------ phase E: decay factors
-  // wavefront `wave` owns token rows 16*wave .. +15; lane owns key channels
-  // lane*CPL .. +CPL-1; the cumulative decay is a running product over the rows.
-  float kf[16][CPL], qf[16][CPL], rowf[16][CPL], colf[16][CPL];
-  {
-    float ed[16][CPL];
+  auto load_raw = [&](const PrepItem& it, RC& rc) {
+    if (!it.valid) return;
+    const int64_t base_qk = (static_cast<int64_t>(it.t0) * H + it.h) * D;
+    const uint32_t bytes_qk = (it.nrow - 1) * rs_qk + D * EI;   // rows past the end read 0
+    const auto rq = make_rsrc(static_cast<const TIn*>(p.q) + base_qk, bytes_qk);
+    const auto rk = make_rsrc(static_cast<const TIn*>(p.k) + base_qk, bytes_qk);
+    const auto rg = make_rsrc(static_cast<const TIn*>(p.g) + base_qk, bytes_qk);
     const uint32_t vo = lane * CPL * EI;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const uint32_t so = (16 * wave + r) * rs_qk;
-      if constexpr (F32) {
-        ed[r][0] = fast_exp2(__uint_as_float(buf_ld32(rg, vo, so)) * kLog2e);
-        kf[r][0] = __uint_as_float(buf_ld32(rk, vo, so));
-        qf[r][0] = __uint_as_float(buf_ld32(rq, vo, so));
-      } else if constexpr (CPL == 2) {
-        const uint32_t gw = buf_ld32(rg, vo, so), kw = buf_ld32(rk, vo, so), qw = buf_ld32(rq, vo, so);
-        ed[r][0] = fast_exp2(bf16lo(gw) * kLog2e);
-        ed[r][1] = fast_exp2(bf16hi(gw) * kLog2e);
-        kf[r][0] = bf16lo(kw); kf[r][1] = bf16hi(kw);
-        qf[r][0] = bf16lo(qw); qf[r][1] = bf16hi(qw);
+      if constexpr (!F32 && CPL == 1) {
+        rc.g[r] = buf_ld16(rg, vo, so); rc.k[r] = buf_ld16(rk, vo, so); rc.q[r] = buf_ld16(rq, vo, so);
       } else {
-        ed[r][0] = fast_exp2(__uint_as_float(uint32_t(buf_ld16(rg, vo, so)) << 16) * kLog2e);
-        kf[r][0] = __uint_as_float(uint32_t(buf_ld16(rk, vo, so)) << 16);
-        qf[r][0] = __uint_as_float(uint32_t(buf_ld16(rq, vo, so)) << 16);
+        rc.g[r] = buf_ld32(rg, vo, so); rc.k[r] = buf_ld32(rk, vo, so); rc.q[r] = buf_ld32(rq, vo, so);
       }
-    }
-#pragma unroll
-    for (int e = 0; e < CPL; ++e) {
-      float run = 1.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { run *= ed[r][e]; rowf[r][e] = run; }      // e^{G_t - R_w}
-      btot[wave * D + lane * CPL + e] = run;                                    // e^{R_{w+1} - R_w}
-      float back = 1.f;
-#pragma unroll
-      for (int r = 15; r >= 0; --r) { colf[r][e] = back; back *= ed[r][e]; }   // e^{R_{w+1} - G_t}
     }
     if (tid < kC) {
-      float b;
-      if constexpr (F32) b = __uint_as_float(buf_ld32(rb, tid * H * EI, 0));
-      else b = __uint_as_float(uint32_t(buf_ld16(rb, tid * H * EI, 0)) << 16);
-      betas[tid] = b;
+      const auto rb = make_rsrc(static_cast<const TIn*>(p.beta) + static_cast<int64_t>(it.t0) * H + it.h,
+                                (it.nrow - 1) * H * EI + EI);
+      if constexpr (F32) rc.beta = buf_ld32(rb, tid * H * EI, 0);
+      else rc.beta = static_cast<uint32_t>(buf_ld16(rb, tid * H * EI, 0)) << 16;
     }
-  }
-  __syncthreads();
+  };
 
-  float eR1[CPL], fI3[CPL];
+  const PrepItem cur_it = prep_item(p, blockIdx.x);
+  if (!cur_it.valid) return;         // unused workspace slot
+  RC cur;
+  load_raw(cur_it, cur);
+  {
+    const auto rw = make_rsrc(p.ws + (static_cast<int64_t>(cur_it.slot) * H + cur_it.h) * SL::BYTES,
+                              SL::BYTES);
+
+    // ------------------------------------------------ phase E: decay factors
+    // wavefront `wave` owns token rows 16*wave .. +15; lane owns key channels
+    // lane*CPL .. +CPL-1; the cumulative decay is a running product over the rows.
+    // q and k stay in their packed input words (cur.q, cur.k) and are widened where
+    // used, which keeps the live register set small across the matrix-core phases
+    auto kval = [&](int r, int e) -> float {
+      if constexpr (F32) return __uint_as_float(cur.k[r]);
+      else if constexpr (CPL == 1) return __uint_as_float(uint32_t(cur.k[r]) << 16);
+      else return e ? bf16hi(cur.k[r]) : bf16lo(cur.k[r]);
+    };
+    auto qval = [&](int r, int e) -> float {
+      if constexpr (F32) return __uint_as_float(cur.q[r]);
+      else if constexpr (CPL == 1) return __uint_as_float(uint32_t(cur.q[r]) << 16);
+      else return e ? bf16hi(cur.q[r]) : bf16lo(cur.q[r]);
+    };
+    float rowf[16][CPL], colf[16][CPL];
+    {
+      float ed[16][CPL];
 #pragma unroll
-  for (int e = 0; e < CPL; ++e) {
-    const int c = lane * CPL + e;
-    float b4[4];
+      for (int r = 0; r < 16; ++r) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) b4[m] = btot[m * D + c];
-    float pre = 1.f;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) if (m <= wave) pre *= b4[m];
-    eR1[e] = pre;                                    // e^{R_{w+1}}
-    const float inv_bt = 1.f / b4[wave];
-    float acc = 1.f;
-#pragma unroll
-    for (int I = 0; I < 4; ++I) {
-      if (I > wave) {
-        acc *= b4[I];
-        fij[offdiag_index(I, wave) * D + c] = acc;   // e^{R_{I+1} - R_{w+1}}
+        for (int e = 0; e < CPL; ++e) {
+          float gv;
+          if constexpr (F32) gv = __uint_as_float(cur.g[r]);
+          else if constexpr (CPL == 1) gv = __uint_as_float(uint32_t(cur.g[r]) << 16);
+          else gv = e ? bf16hi(cur.g[r]) : bf16lo(cur.g[r]);
+          ed[r][e] = fast_exp2(gv * kLog2e);
+        }
       }
-    }
-    fI3[e] = acc;                                    // e^{G_n - R_{w+1}}
-    if (wave == 0) {
-      const float lam = b4[0] * b4[1] * b4[2] * b4[3];
-      buf_st32(__float_as_uint(lam), rw, SL::LAM + c * 4, 0);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) rowf[r][e] *= inv_bt;   // now e^{G_t - R_{w+1}} in [1, e^80]
-  }
-  // row-side operands (referenced to the end of the own sub-tile) and the
-  // column-side keys of the diagonal pairs
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int t = 16 * wave + r;
-    const int byte = lane * CPL * E;
-    if constexpr (CPL == 2 && !F32) {
-      *reinterpret_cast<uint32_t*>(smem + CF::QS + swz<CF::RBD>(t, byte)) =
-          pack_bf16x2(qf[r][0] * rowf[r][0], qf[r][1] * rowf[r][1]);
-      *reinterpret_cast<uint32_t*>(smem + CF::KS + swz<CF::RBD>(t, byte)) =
-          pack_bf16x2(kf[r][0] * rowf[r][0], kf[r][1] * rowf[r][1]);
-      *reinterpret_cast<uint32_t*>(smem + CF::KT + swz<CF::RBD>(t, byte)) =
-          pack_bf16x2(kf[r][0] * colf[r][0], kf[r][1] * colf[r][1]);
-    } else {
+      if (tid < kC) betas[tid] = __uint_as_float(cur.beta);
 #pragma unroll
       for (int e = 0; e < CPL; ++e) {
-        const int b = byte + e * E;
-        lds_set1<F32>(smem + CF::QS + swz<CF::RBD>(t, b), qf[r][e] * rowf[r][e]);
-        lds_set1<F32>(smem + CF::KS + swz<CF::RBD>(t, b), kf[r][e] * rowf[r][e]);
-        lds_set1<F32>(smem + CF::KT + swz<CF::RBD>(t, b), kf[r][e] * colf[r][e]);
+        float run = 1.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { run *= ed[r][e]; rowf[r][e] = run; }      // e^{G_t - R_w}
+        btot[wave * D + lane * CPL + e] = run;                                    // e^{R_{w+1} - R_w}
+        float back = 1.f;
+#pragma unroll
+        for (int r = 15; r >= 0; --r) { colf[r][e] = back; back *= ed[r][e]; }   // e^{R_{w+1} - G_t}
       }
     }
-  }
-  // Kt^T = (K e^{G_n - G})^T straight to the workspace: 16 consecutive tokens per channel
-#pragma unroll
-  for (int e = 0; e < CPL; ++e) {
-    const int c = lane * CPL + e;
-    float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = kf[r][e] * colf[r][e] * fI3[e];
-    const uint32_t off = SL::KT + (c * kC + 16 * wave) * E;
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
-      buf_put4<F32>(rw, off + 4 * q4 * E, x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]);
-  }
-  __syncthreads();
+    __syncthreads();
 
-  // ------------------------------------------------ phase AM: A and M
-  // computed transposed (rows s) so each lane stores 4 consecutive s of row t
+    float eR1[CPL], fI3[CPL];
 #pragma unroll
-  for (int pp = 0; pp < 3; ++pp) {
-    const int pr = wave + 4 * pp;
-    if (pr < 10) {
-      int I, J;
-      pair_of(pr, I, J);
-      f32x4_t aA = {0.f, 0.f, 0.f, 0.f}, aM = {0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < CPL; ++e) {
+      const int c = lane * CPL + e;
+      float b4[4];
 #pragma unroll
-      for (int kk = 0; kk < CF::NKK; ++kk) {
-        const int kb = (kk * 32 + g4 * 8) * E;
-        Frag<F32> a = lds_frag<F32, CF::RBD>(smem + CF::KT, 16 * J + l16, kb);
-        if (J < I) {   // carry column sub-tile J to row sub-tile I's reference
-          const float* f = fij + offdiag_index(I, J) * D + kk * 32 + g4 * 8;
-          float x[8];
-          frag_to_f32<F32>(a, x);
+      for (int m = 0; m < 4; ++m) b4[m] = btot[m * D + c];
+      float pre = 1.f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] *= f[e];
-          a = frag_from_f32<F32>(x);
+      for (int m = 0; m < 4; ++m) if (m <= wave) pre *= b4[m];
+      eR1[e] = pre;                                    // e^{R_{w+1}}
+      const float inv_bt = 1.f / b4[wave];
+      float acc = 1.f;
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        if (I > wave) {
+          acc *= b4[I];
+          fij[offdiag_index(I, wave) * D + c] = acc;   // e^{R_{I+1} - R_{w+1}}
         }
-        const Frag<F32> bk = lds_frag<F32, CF::RBD>(smem + CF::KS, 16 * I + l16, kb);
-        const Frag<F32> bq = lds_frag<F32, CF::RBD>(smem + CF::QS, 16 * I + l16, kb);
-        aA = mma32<F32>(aA, a, bk);
-        aM = mma32<F32>(aM, a, bq);
       }
-      const int t = 16 * I + l16, s0 = 16 * J + 4 * g4;
-      const float bt = betas[t];
-      float av[4], mv[4];
+      fI3[e] = acc;                                    // e^{G_n - R_{w+1}}
+      if (wave == 0) {
+        const float lam = b4[0] * b4[1] * b4[2] * b4[3];
+        buf_st32(__float_as_uint(lam), rw, SL::LAM + c * 4, 0);
+      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        av[i] = (s0 + i < t) ? bt * aA[i] : 0.f;
-        mv[i] = (s0 + i <= t) ? aM[i] : 0.f;
-      }
-      *reinterpret_cast<float4*>(atc + swz<256>(t, s0 * 4)) = float4{av[0], av[1], av[2], av[3]};
-      lds_put4<F32>(smem + CF::MB + swz<CF::RBC>(t, s0 * E), mv[0], mv[1], mv[2], mv[3]);
+      for (int r = 0; r < 16; ++r) rowf[r][e] *= inv_bt;   // now e^{G_t - R_{w+1}} in [1, e^80]
     }
-  }
-  __syncthreads();
-
-  // ------------------------------------------------ phase E2 + diagonal inverses
-  // chunk-referenced Q e^G ([t][c]) and (K e^G)^T ([c][t]) into region 1
-#pragma unroll
-  for (int e = 0; e < CPL; ++e) {
-    const int c = lane * CPL + e;
-    float kb[16];
+    // row-side operands (referenced to the end of the own sub-tile) and the
+    // column-side keys of the diagonal pairs
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int t = 16 * wave + r;
-      const float ef = rowf[r][e] * eR1[e];           // e^{G_t}
-      lds_set1<F32>(smem + CF::QB + swz<CF::RBD>(t, c * E), qf[r][e] * ef);
-      kb[r] = kf[r][e] * ef;
-    }
+      const int byte = lane * CPL * E;
+      if constexpr (CPL == 2 && !F32) {
+        const float k0 = kval(r, 0), k1 = kval(r, 1), q0 = qval(r, 0), q1 = qval(r, 1);
+        *reinterpret_cast<uint32_t*>(smem + CF::QS + swz<CF::RBD>(t, byte)) =
+            pack_bf16x2(q0 * rowf[r][0], q1 * rowf[r][1]);
+        *reinterpret_cast<uint32_t*>(smem + CF::KS + swz<CF::RBD>(t, byte)) =
+            pack_bf16x2(k0 * rowf[r][0], k1 * rowf[r][1]);
+        *reinterpret_cast<uint32_t*>(smem + CF::KT + swz<CF::RBD>(t, byte)) =
+            pack_bf16x2(k0 * colf[r][0], k1 * colf[r][1]);
+      } else {
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
-      lds_put4<F32>(smem + CF::KBT + swz<CF::RBC>(c, (16 * wave + 4 * q4) * E),
-                    kb[4 * q4], kb[4 * q4 + 1], kb[4 * q4 + 2], kb[4 * q4 + 3]);
-  }
-  if (lane < 16) {   // T_ww = (I + A_ww)^{-1}, lane j computes column j
-    const int base = 16 * wave;
-    float x[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float arow[16];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 v = *reinterpret_cast<const float4*>(atc + swz<256>(base + i, (base + 4 * q4) * 4));
-        arow[4 * q4] = v.x; arow[4 * q4 + 1] = v.y; arow[4 * q4 + 2] = v.z; arow[4 * q4 + 3] = v.w;
+        for (int e = 0; e < CPL; ++e) {
+          const int b = byte + e * E;
+          lds_set1<F32>(smem + CF::QS + swz<CF::RBD>(t, b), qval(r, e) * rowf[r][e]);
+          lds_set1<F32>(smem + CF::KS + swz<CF::RBD>(t, b), kval(r, e) * rowf[r][e]);
+          lds_set1<F32>(smem + CF::KT + swz<CF::RBD>(t, b), kval(r, e) * colf[r][e]);
+        }
       }
-      float s = 0.f;
-#pragma unroll
-      for (int m = 0; m < i; ++m) s += arow[m] * x[m];
-      x[i] = (i == lane) ? 1.f : -s;
     }
+    // Kt^T = (K e^{G_n - G})^T straight to the workspace: 16 consecutive tokens per channel
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      *reinterpret_cast<float*>(atc + swz<256>(base + i, (base + lane) * 4)) = x[i];
-  }
-  __syncthreads();
+    for (int e = 0; e < CPL; ++e) {
+      const int c = lane * CPL + e;
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = kval(r, e) * colf[r][e] * fI3[e];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        buf_put4<F32>(rw, SL::KT + frag_off<kC, F32>(c, 16 * wave + 4 * q4), x[4 * q4], x[4 * q4 + 1],
+                      x[4 * q4 + 2], x[4 * q4 + 3]);
+    }
+    __syncthreads();
 
-  // ------------------------------------------------ off-diagonal inverse blocks
-  // T_IJ = -T_II sum_{m=J}^{I-1} A_Im T_mJ, row sub-tile by row sub-tile, in place
+    // ------------------------------------------------ phase AM: A and M
+    // computed transposed (rows s) so each lane stores 4 consecutive s of row t
 #pragma unroll
-  for (int I = 1; I < 4; ++I) {
-    f32x4_t tt = {0.f, 0.f, 0.f, 0.f};
-    const int J = wave;
-    if (J < I) {
-      f32x4_t y = {0.f, 0.f, 0.f, 0.f};
-      for (int m = J; m < I; ++m) {
+    for (int pp = 0; pp < 3; ++pp) {
+      const int pr = wave + 4 * pp;
+      if (pr < 10) {
+        int I, J;
+        pair_of(pr, I, J);
+        f32x4_t aA = {0.f, 0.f, 0.f, 0.f}, aM = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const int kx = 4 * g4 + st;
-          const float a = *reinterpret_cast<const float*>(atc + swz<256>(16 * I + l16, (16 * m + kx) * 4));
-          const float b = *reinterpret_cast<const float*>(atc + swz<256>(16 * m + kx, (16 * J + l16) * 4));
-          y = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, y, 0, 0, 0);
+        for (int kk = 0; kk < CF::NKK; ++kk) {
+          const int kb = (kk * 32 + g4 * 8) * E;
+          Frag<F32> a = lds_frag<F32, CF::RBD>(smem + CF::KT, 16 * J + l16, kb);
+          if (J < I) {   // carry column sub-tile J to row sub-tile I's reference
+            const float* f = fij + offdiag_index(I, J) * D + kk * 32 + g4 * 8;
+            float x[8];
+            frag_to_f32<F32>(a, x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] *= f[e];
+            a = frag_from_f32<F32>(x);
+          }
+          const Frag<F32> bk = lds_frag<F32, CF::RBD>(smem + CF::KS, 16 * I + l16, kb);
+          const Frag<F32> bq = lds_frag<F32, CF::RBD>(smem + CF::QS, 16 * I + l16, kb);
+          aA = mma32<F32>(aA, a, bk);
+          aM = mma32<F32>(aM, a, bq);
+        }
+        const int t = 16 * I + l16, s0 = 16 * J + 4 * g4;
+        const float bt = betas[t];
+        float av[4], mv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          av[i] = (s0 + i < t) ? bt * aA[i] : 0.f;
+          mv[i] = (s0 + i <= t) ? aM[i] : 0.f;
+        }
+        *reinterpret_cast<float4*>(atc + swz<256>(t, s0 * 4)) = float4{av[0], av[1], av[2], av[3]};
+        lds_put4<F32>(smem + CF::MB + swz<CF::RBC>(t, s0 * E), mv[0], mv[1], mv[2], mv[3]);
+      }
+    }
+    __syncthreads();
+
+    // ------------------------------------------------ phase E2 + diagonal inverses
+    // chunk-referenced Q e^G ([t][c]) and (K e^G)^T ([c][t]) into region 1
+    {
+      float kb[CPL][16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = 16 * wave + r;
+        float qv[CPL];
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) {
+          const float ef = rowf[r][e] * eR1[e];          // e^{G_t}
+          qv[e] = qval(r, e) * ef;
+          kb[e][r] = kval(r, e) * ef;
+        }
+        if constexpr (CPL == 2 && !F32) {
+          *reinterpret_cast<uint32_t*>(smem + CF::QB + swz<CF::RBD>(t, lane * 4)) = pack_bf16x2(qv[0], qv[1]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) lds_set1<F32>(smem + CF::QB + swz<CF::RBD>(t, (lane * CPL + e) * E), qv[e]);
         }
       }
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const float a = *reinterpret_cast<const float*>(atc + swz<256>(16 * I + l16, (16 * I + 4 * g4 + st) * 4));
-        tt = __builtin_amdgcn_mfma_f32_16x16x4f32(a, y[st], tt, 0, 0, 0);
+      for (int e = 0; e < CPL; ++e)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          lds_put4<F32>(smem + CF::KBT + swz<CF::RBC>(lane * CPL + e, (16 * wave + 4 * q4) * E),
+                        kb[e][4 * q4], kb[e][4 * q4 + 1], kb[e][4 * q4 + 2], kb[e][4 * q4 + 3]);
+    }
+    if (lane < 16) {   // T_ww = (I + A_ww)^{-1}, lane j computes column j
+      const int base = 16 * wave;
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float arow[16];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 v = *reinterpret_cast<const float4*>(atc + swz<256>(base + i, (base + 4 * q4) * 4));
+          arow[4 * q4] = v.x; arow[4 * q4 + 1] = v.y; arow[4 * q4 + 2] = v.z; arow[4 * q4 + 3] = v.w;
+        }
+        float sacc = 0.f;
+#pragma unroll
+        for (int m = 0; m < i; ++m) sacc += arow[m] * x[m];
+        x[i] = (i == lane) ? 1.f : -sacc;
       }
-    }
-    __syncthreads();
-    if (J < I) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<float*>(atc + swz<256>(16 * I + 4 * g4 + i, (16 * J + l16) * 4)) = -tt[i];
+      for (int i = 0; i < 16; ++i) at_el(base + i, base + lane) = x[i];
     }
     __syncthreads();
-  }
 
-  // ------------------------------------------------ P = scale M Tb, stored as P[t][t']
-  // computed transposed: P^T[t'][t] = sum_s Tb[s][t'] M[t][s], nonzero for t' <= t
+    // ------------------------------------------------ off-diagonal inverse blocks
+    // I + A = [[L1, 0], [B, L2]] in 32x32 halves: the inverse is
+    // [[L1^-1, 0], [-L2^-1 B L1^-1, L2^-1]], with L1^-1 and L2^-1 from their
+    // diagonal 16x16 inverses (fp32 16x16x4 matrix-core products, in place of A)
+    if (wave < 2) {   // T_10 = -T_11 A_10 T_00 and T_32 = -T_33 A_32 T_22
+      const int I = wave ? 3 : 1, J = I - 1;
+      f32x4_t y = {0.f, 0.f, 0.f, 0.f}, tt = y;
 #pragma unroll
-  for (int pp = 0; pp < 3; ++pp) {
-    const int pr = wave + 4 * pp;
-    if (pr < 10) {
-      int C, R;
-      pair_of(pr, C, R);
+      for (int st = 0; st < 4; ++st)
+        y = __builtin_amdgcn_mfma_f32_16x16x4f32(at_el(16 * I + l16, 16 * J + 4 * g4 + st),
+                                                 at_el(16 * J + 4 * g4 + st, 16 * J + l16), y, 0, 0, 0);
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        tt = __builtin_amdgcn_mfma_f32_16x16x4f32(at_el(16 * I + l16, 16 * I + 4 * g4 + st), y[st], tt, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) at_el(16 * I + 4 * g4 + i, 16 * J + l16) = -tt[i];
+    }
+    __syncthreads();
+    float* xs = reinterpret_cast<float*>(smem + CF::XS);
+    const int bi = 2 + (wave >> 1), bj = wave & 1;      // lower-left 16x16 block of this wave
+    {   // X_{bi,bj} = sum_{m=bj}^{1} A_{bi,m} T_{m,bj}
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int sb = kk * 32 + g4 * 8;
-        float x[8];
+      for (int m = 0; m < 2; ++m) {
+        if (m >= bj) {
+#pragma unroll
+          for (int st = 0; st < 4; ++st)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(at_el(16 * bi + l16, 16 * m + 4 * g4 + st),
+                                                       at_el(16 * m + 4 * g4 + st, 16 * bj + l16), acc, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xs[(wave * 16 + 4 * g4 + i) * CF::XLD + l16] = acc[i];
+    }
+    __syncthreads();
+    {   // T_{bi,bj} = -sum_{m=2}^{bi} T_{bi,m} X_{m,bj}
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 2; m < 4; ++m) {
+        if (m <= bi) {
+          const int xw = (m - 2) * 2 + bj;
+#pragma unroll
+          for (int st = 0; st < 4; ++st)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(at_el(16 * bi + l16, 16 * m + 4 * g4 + st),
+                                                       xs[(xw * 16 + 4 * g4 + st) * CF::XLD + l16], acc, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) at_el(16 * bi + 4 * g4 + i, 16 * bj + l16) = -acc[i];
+    }
+    __syncthreads();
+
+    // ------------------------------------------------ P = scale M Tb, stored as P[t][t']
+    // computed transposed: P^T[t'][t] = sum_s Tb[s][t'] M[t][s], nonzero for t' <= t
+#pragma unroll
+    for (int pp = 0; pp < 3; ++pp) {
+      const int pr = wave + 4 * pp;
+      if (pr < 10) {
+        int C, R;
+        pair_of(pr, C, R);
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
         const float bcol = betas[16 * R + l16];     // Tb[s][t'] = T[s][t'] beta_t'
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          x[e] = *reinterpret_cast<const float*>(atc + swz<256>(sb + e, (16 * R + l16) * 4)) * bcol;
-        const Frag<F32> a = frag_from_f32<F32>(x);
-        const Frag<F32> b = lds_frag<F32, CF::RBC>(smem + CF::MB, 16 * C + l16, sb * E);
-        acc = mma32<F32>(acc, a, b);
+        for (int kk = 0; kk < 2; ++kk) {
+          const int sb = kk * 32 + g4 * 8;
+          float x[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = at_el(sb + e, 16 * R + l16) * bcol;
+          const Frag<F32> a = frag_from_f32<F32>(x);
+          const Frag<F32> bm = lds_frag<F32, CF::RBC>(smem + CF::MB, 16 * C + l16, sb * E);
+          acc = mma32<F32>(acc, a, bm);
+        }
+        const int t = 16 * C + l16, tp = 16 * R + 4 * g4;
+        lds_put4<F32>(smem + CF::PB + swz<CF::RBC>(t, tp * E), acc[0], acc[1], acc[2], acc[3]);
+        buf_put4<F32>(rw, SL::PP + frag_off<kC, F32>(t, tp), p.scale * acc[0], p.scale * acc[1],
+                      p.scale * acc[2], p.scale * acc[3]);
       }
-      const int t = 16 * C + l16, tp = 16 * R + 4 * g4;
-      lds_put4<F32>(smem + CF::PB + swz<CF::RBC>(t, tp * E), acc[0], acc[1], acc[2], acc[3]);
-      buf_put4<F32>(rw, SL::PP + (t * kC + tp) * E, p.scale * acc[0], p.scale * acc[1],
-                    p.scale * acc[2], p.scale * acc[3]);
     }
-  }
-  for (int e = tid; e < 6 * 64; e += kThreads) {   // P[t][t'] = 0 for t' sub-tile > t sub-tile
-    int C, R;
-    upper_pair(e >> 6, C, R);
-    const int t = 16 * C + ((e >> 2) & 15), tp = 16 * R + 4 * (e & 3);
-    lds_put4<F32>(smem + CF::PB + swz<CF::RBC>(t, tp * E), 0.f, 0.f, 0.f, 0.f);
-    buf_put4<F32>(rw, SL::PP + (t * kC + tp) * E, 0.f, 0.f, 0.f, 0.f);
-  }
-  __syncthreads();
+    for (int e = tid; e < 6 * 64; e += kThreads) {   // P[t][t'] = 0 for t' sub-tile > t sub-tile
+      int C, R;
+      upper_pair(e >> 6, C, R);
+      const int t = 16 * C + ((e >> 2) & 15), tp = 16 * R + 4 * (e & 3);
+      lds_put4<F32>(smem + CF::PB + swz<CF::RBC>(t, tp * E), 0.f, 0.f, 0.f, 0.f);
+      buf_put4<F32>(rw, SL::PP + frag_off<kC, F32>(t, tp), 0.f, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();
 
-  // ------------------------------------------------ W and Q'
-  // W^T = (K e^G)^T Tb^T and Q'^T = scale ((Q e^G)^T - (K e^G)^T P^T); lane holds
-  // 4 consecutive channels of one token row -> 4-element stores of W[t][c], Q'[t][c]
-  {
-    constexpr int RPW = D / 64;        // 16-row channel tiles per wavefront
-    f32x4_t aw[RPW][4], aq[RPW][4];
+    // ------------------------------------------------ W and Q'
+    // W^T = (K e^G)^T Tb^T and Q'^T = scale ((Q e^G)^T - (K e^G)^T P^T); lane holds
+    // 4 consecutive channels of one token row -> 4-element stores of W[t][c], Q'[t][c]
+    {
+      constexpr int RPW = D / 64;        // 16-row channel tiles per wavefront
+      f32x4_t aw[RPW][4], aq[RPW][4];
 #pragma unroll
-    for (int rr = 0; rr < RPW; ++rr)
+      for (int rr = 0; rr < RPW; ++rr)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        aw[rr][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        aq[rr][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const int t = 16 * ct + l16;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        if (kk == 1 && ct < 2) continue;     // Tb[t][s] = P[t][s] = 0 for s > t
-        const int sb = kk * 32 + g4 * 8;
-        float x[8];
-        {
-          const float4 u0 = *reinterpret_cast<const float4*>(atc + swz<256>(t, sb * 4));
-          const float4 u1 = *reinterpret_cast<const float4*>(atc + swz<256>(t, sb * 4 + 16));
-          const float4 b0 = *reinterpret_cast<const float4*>(betas + sb);
-          const float4 b1 = *reinterpret_cast<const float4*>(betas + sb + 4);
-          x[0] = u0.x * b0.x; x[1] = u0.y * b0.y; x[2] = u0.z * b0.z; x[3] = u0.w * b0.w;
-          x[4] = u1.x * b1.x; x[5] = u1.y * b1.y; x[6] = u1.z * b1.z; x[7] = u1.w * b1.w;
+        for (int ct = 0; ct < 4; ++ct) {
+          aw[rr][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          aq[rr][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
-        const Frag<F32> bw = frag_from_f32<F32>(x);
-        const Frag<F32> bq = lds_frag<F32, CF::RBC>(smem + CF::PB, t, sb * E);
-#pragma unroll
-        for (int rr = 0; rr < RPW; ++rr) {
-          const int c = 16 * (wave * RPW + rr) + l16;
-          const Frag<F32> a = lds_frag<F32, CF::RBC>(smem + CF::KBT, c, sb * E);
-          aw[rr][ct] = mma32<F32>(aw[rr][ct], a, bw);
-          aq[rr][ct] = mma32<F32>(aq[rr][ct], a, bq);
-        }
-      }
-    }
-#pragma unroll
-    for (int rr = 0; rr < RPW; ++rr) {
-      const int c = 16 * (wave * RPW + rr) + 4 * g4;
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
         const int t = 16 * ct + l16;
-        buf_put4<F32>(rw, SL::W + (t * D + c) * E, aw[rr][ct][0], aw[rr][ct][1], aw[rr][ct][2],
-                      aw[rr][ct][3]);
-        float qb[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) qb[i] = lds_get1<F32>(smem + CF::QB + swz<CF::RBD>(t, (c + i) * E));
-        buf_put4<F32>(rw, SL::QP + (t * D + c) * E, p.scale * (qb[0] - aq[rr][ct][0]),
-                      p.scale * (qb[1] - aq[rr][ct][1]), p.scale * (qb[2] - aq[rr][ct][2]),
-                      p.scale * (qb[3] - aq[rr][ct][3]));
+        for (int kk = 0; kk < 2; ++kk) {
+          if (kk == 1 && ct < 2) continue;     // Tb[t][s] = P[t][s] = 0 for s > t
+          const int sb = kk * 32 + g4 * 8;
+          float x[8];
+          {
+            const float4 u0 = *reinterpret_cast<const float4*>(atc + swz<256>(t, sb * 4));
+            const float4 u1 = *reinterpret_cast<const float4*>(atc + swz<256>(t, sb * 4 + 16));
+            const float4 b0 = *reinterpret_cast<const float4*>(betas + sb);
+            const float4 b1 = *reinterpret_cast<const float4*>(betas + sb + 4);
+            x[0] = u0.x * b0.x; x[1] = u0.y * b0.y; x[2] = u0.z * b0.z; x[3] = u0.w * b0.w;
+            x[4] = u1.x * b1.x; x[5] = u1.y * b1.y; x[6] = u1.z * b1.z; x[7] = u1.w * b1.w;
+          }
+          const Frag<F32> bw = frag_from_f32<F32>(x);
+          const Frag<F32> bq = lds_frag<F32, CF::RBC>(smem + CF::PB, t, sb * E);
+#pragma unroll
+          for (int rr = 0; rr < RPW; ++rr) {
+            const int c = 16 * (wave * RPW + rr) + l16;
+            const Frag<F32> a = lds_frag<F32, CF::RBC>(smem + CF::KBT, c, sb * E);
+            aw[rr][ct] = mma32<F32>(aw[rr][ct], a, bw);
+            aq[rr][ct] = mma32<F32>(aq[rr][ct], a, bq);
+          }
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < RPW; ++rr) {
+        const int c = 16 * (wave * RPW + rr) + 4 * g4;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const int t = 16 * ct + l16;
+          buf_put4<F32>(rw, SL::W + frag_off<D, F32>(t, c), aw[rr][ct][0], aw[rr][ct][1],
+                        aw[rr][ct][2], aw[rr][ct][3]);
+          float qb[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) qb[i] = lds_get1<F32>(smem + CF::QB + swz<CF::RBD>(t, (c + i) * E));
+          buf_put4<F32>(rw, SL::QP + frag_off<D, F32>(t, c), p.scale * (qb[0] - aq[rr][ct][0]),
+                        p.scale * (qb[1] - aq[rr][ct][1]), p.scale * (qb[2] - aq[rr][ct][2]),
+                        p.scale * (qb[3] - aq[rr][ct][3]));
+        }
       }
     }
-  }
-  // Tb = T Diag(beta) -> workspace, 16 consecutive entries per thread
-  {
-    const int t = tid >> 2, s0 = (tid & 3) * 16;
-    float x[16];
+    // Tb = T Diag(beta) -> workspace, 16 consecutive entries per thread
+    {
+      const int t = tid >> 2, s0 = (tid & 3) * 16;
+      float x[16];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const float4 u = *reinterpret_cast<const float4*>(atc + swz<256>(t, (s0 + 4 * q4) * 4));
-      const float4 b = *reinterpret_cast<const float4*>(betas + s0 + 4 * q4);
-      x[4 * q4] = u.x * b.x; x[4 * q4 + 1] = u.y * b.y; x[4 * q4 + 2] = u.z * b.z; x[4 * q4 + 3] = u.w * b.w;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 u = *reinterpret_cast<const float4*>(atc + swz<256>(t, (s0 + 4 * q4) * 4));
+        const float4 b = *reinterpret_cast<const float4*>(betas + s0 + 4 * q4);
+        x[4 * q4] = u.x * b.x; x[4 * q4 + 1] = u.y * b.y; x[4 * q4 + 2] = u.z * b.z; x[4 * q4 + 3] = u.w * b.w;
+      }
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        buf_put4<F32>(rw, SL::TB + frag_off<kC, F32>(t, s0 + 4 * q4), x[4 * q4], x[4 * q4 + 1],
+                      x[4 * q4 + 2], x[4 * q4 + 3]);
     }
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
-      buf_put4<F32>(rw, SL::TB + (t * kC + s0 + 4 * q4) * E, x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2],
-                    x[4 * q4 + 3]);
   }
 }
 
@@ -730,61 +832,79 @@ __global__ __launch_bounds__(kThreads, 1) void state_scan_kernel(ScanParams p) {
   __syncthreads();
 
   const uint32_t rs_v = static_cast<uint32_t>(H) * D * EI;
-  constexpr int VPR = DVS / 8;                          // 8-value pieces per V row
+  constexpr int VPR = DVS / 8;                      // 8-value pieces per V row
+  constexpr int VPT = (kC * VPR + kThreads - 1) / kThreads;   // pieces per thread
 
-  for (int ci = 0; ci < nchunks; ++ci) {
+  // Everything one chunk needs from memory, held in registers so the next chunk's
+  // loads can be issued before the current chunk's products start.
+  struct ChunkRegs {
+    Frag<F32> fw[NKK], fq[NKK], ftb[2], fpp[2], fkt[RT][2];
+    i32x4_t lam[RT];
+    i32x4_t vv[VPT][F32 ? 2 : 1];
+  };
+  auto load_chunk = [&](int ci, ChunkRegs& cr) {
     const int t0 = tok0 + ci * kC;
     const int nrow = min(kC, len - ci * kC);
     const auto rw = make_rsrc(p.ws + (static_cast<int64_t>(sbase + ci) * H + h) * SL::BYTES, SL::BYTES);
     const int64_t vbase = (static_cast<int64_t>(t0) * H + h) * D + j0;
-    const uint32_t vbytes = (nrow - 1) * rs_v + DVS * EI;
-    const auto rv = make_rsrc(static_cast<const TIn*>(p.v) + vbase, vbytes);
-    const auto ro = make_rsrc(static_cast<TIn*>(p.out) + vbase, vbytes);
-
-    // operand fragments straight from the workspace
-    Frag<F32> fw[NKK], fq[NKK], ftb[2], fpp[2], fkt[RT][2];
-    const int trow = 16 * wave + l16;
+    const auto rv = make_rsrc(static_cast<const TIn*>(p.v) + vbase, (nrow - 1) * rs_v + DVS * EI);
+    // every fragment is one contiguous 1 KB per wavefront (see frag_off)
+    constexpr uint32_t FB = F32 ? 2048 : 1024;      // bytes per fragment
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      const uint32_t o = (trow * D + kk * 32 + g4 * 8) * E;
-      fw[kk] = buf_frag<F32>(rw, SL::W + o, 0);
-      fq[kk] = buf_frag<F32>(rw, SL::QP + o, 0);
+      const uint32_t o = (wave * NKK + kk) * FB + lane * 16;
+      cr.fw[kk] = buf_frag2<F32>(rw, SL::W + o);
+      cr.fq[kk] = buf_frag2<F32>(rw, SL::QP + o);
     }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const uint32_t o = (trow * kC + kk * 32 + g4 * 8) * E;
-      ftb[kk] = buf_frag<F32>(rw, SL::TB + o, 0);
-      fpp[kk] = buf_frag<F32>(rw, SL::PP + o, 0);
+      const uint32_t o = (wave * 2 + kk) * FB + lane * 16;
+      cr.ftb[kk] = buf_frag2<F32>(rw, SL::TB + o);
+      cr.fpp[kk] = buf_frag2<F32>(rw, SL::PP + o);
 #pragma unroll
-      for (int ri = 0; ri < RT; ++ri) {
-        const int c = 16 * (wave * RT + ri) + l16;
-        fkt[ri][kk] = buf_frag<F32>(rw, SL::KT + (c * kC + kk * 32 + g4 * 8) * E, 0);
-      }
+      for (int ri = 0; ri < RT; ++ri)
+        cr.fkt[ri][kk] = buf_frag2<F32>(rw, SL::KT + ((wave * RT + ri) * 2 + kk) * FB + lane * 16);
     }
-    float lam[RT][4];
 #pragma unroll
-    for (int ri = 0; ri < RT; ++ri) {
-      const i32x4_t l4 = buf_ld128(rw, SL::LAM + (16 * (wave * RT + ri) + 4 * g4) * 4, 0);
+    for (int ri = 0; ri < RT; ++ri)
+      cr.lam[ri] = buf_ld128(rw, SL::LAM + (16 * (wave * RT + ri) + 4 * g4) * 4, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lam[ri][i] = __int_as_float(l4[i]);
+    for (int pi = 0; pi < VPT; ++pi) {
+      // pieces beyond the tile (narrow slices) re-read the last row; they are not stored
+      const int pc = min(tid + pi * kThreads, kC * VPR - 1);
+      const int vrow = pc / VPR, vcol = (pc % VPR) * 8;   // rows past the end read zero
+      cr.vv[pi][0] = buf_ld128(rv, vcol * EI, vrow * rs_v);
+      if constexpr (F32) cr.vv[pi][1] = buf_ld128(rv, vcol * EI + 16, vrow * rs_v);
     }
-    // V slice, transposed to [j][t] (rows past the sequence end read as zero)
-    for (int pc = tid; pc < kC * VPR; pc += kThreads) {
-      const int vrow = pc / VPR, vcol = (pc % VPR) * 8;
-      if constexpr (F32) {
-        const i32x4_t a = buf_ld128(rv, vcol * 4, vrow * rs_v);
-        const i32x4_t b = buf_ld128(rv, vcol * 4 + 16, vrow * rs_v);
+  };
+
+  // Two register sets alternate: while chunk ci is computed from one, the loads of
+  // chunk ci+1 fill the other.  The loads are unconditional (the last chunk
+  // re-reads itself), so no branch sits between a load and its first use.
+  auto process = [&](const int ci, const ChunkRegs& cur) {
+    const int t0 = tok0 + ci * kC;
+    const int nrow = min(kC, len - ci * kC);
+    const int64_t vbase = (static_cast<int64_t>(t0) * H + h) * D + j0;
+    const auto ro = make_rsrc(static_cast<TIn*>(p.out) + vbase, (nrow - 1) * rs_v + DVS * EI);
+
+    // V slice, transposed to [j][t]
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          *reinterpret_cast<int*>(smem + CF::VT + swz<CF::RBC>(vcol + i, vrow * 4)) = a[i];
-          *reinterpret_cast<int*>(smem + CF::VT + swz<CF::RBC>(vcol + 4 + i, vrow * 4)) = b[i];
+    for (int pi = 0; pi < VPT; ++pi) {
+      const int pc = tid + pi * kThreads;
+      if ((kC * VPR) % kThreads == 0 || pc < kC * VPR) {
+        const int vrow = pc / VPR, vcol = (pc % VPR) * 8;
+        if constexpr (F32) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            *reinterpret_cast<int*>(smem + CF::VT + swz<CF::RBC>(vcol + i, vrow * 4)) = cur.vv[pi][0][i];
+            *reinterpret_cast<int*>(smem + CF::VT + swz<CF::RBC>(vcol + 4 + i, vrow * 4)) = cur.vv[pi][1][i];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            *reinterpret_cast<uint16_t*>(smem + CF::VT + swz<CF::RBC>(vcol + e, vrow * 2)) =
+                static_cast<uint16_t>(static_cast<uint32_t>(cur.vv[pi][0][e >> 1]) >> (16 * (e & 1)));
         }
-      } else {
-        const i32x4_t a = buf_ld128(rv, vcol * 2, vrow * rs_v);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          *reinterpret_cast<uint16_t*>(smem + CF::VT + swz<CF::RBC>(vcol + e, vrow * 2)) =
-              static_cast<uint16_t>(static_cast<uint32_t>(a[e >> 1]) >> (16 * (e & 1)));
       }
     }
     __syncthreads();
@@ -796,14 +916,14 @@ __global__ __launch_bounds__(kThreads, 1) void state_scan_kernel(ScanParams p) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const Frag<F32> b = lds_frag<F32, CF::RBC>(smem + CF::VT, 16 * jt + l16, (kk * 32 + g4 * 8) * E);
-        u = mma32<F32>(u, ftb[kk], b);
-        ov = mma32<F32>(ov, fpp[kk], b);
+        u = mma32<F32>(u, cur.ftb[kk], b);
+        ov = mma32<F32>(ov, cur.fpp[kk], b);
       }
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         const Frag<F32> b = lds_frag<F32, CF::RBD>(smem + CF::SB, 16 * jt + l16, (kk * 32 + g4 * 8) * E);
-        ws = mma32<F32>(ws, fw[kk], b);
-        qs = mma32<F32>(qs, fq[kk], b);
+        ws = mma32<F32>(ws, cur.fw[kk], b);
+        qs = mma32<F32>(qs, cur.fq[kk], b);
       }
       // Delta = U - W S -> [j][t];  O = Q' S + P V -> [t][j]
       const int j = 16 * jt + l16, t = 16 * wave + 4 * g4;
@@ -822,11 +942,11 @@ __global__ __launch_bounds__(kThreads, 1) void state_scan_kernel(ScanParams p) {
       for (int jt = 0; jt < NJT; ++jt) {
         f32x4_t acc;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = S[ri][jt][i] * lam[ri][i];
+        for (int i = 0; i < 4; ++i) acc[i] = S[ri][jt][i] * __int_as_float(cur.lam[ri][i]);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           const Frag<F32> b = lds_frag<F32, CF::RBC>(smem + CF::DT, 16 * jt + l16, (kk * 32 + g4 * 8) * E);
-          acc = mma32<F32>(acc, fkt[ri][kk], b);
+          acc = mma32<F32>(acc, cur.fkt[ri][kk], b);
         }
         S[ri][jt] = acc;
         lds_put4<F32>(smem + CF::SB + swz<CF::RBD>(16 * jt + l16, (16 * rt + 4 * g4) * E),
@@ -843,6 +963,16 @@ __global__ __launch_bounds__(kThreads, 1) void state_scan_kernel(ScanParams p) {
       }
     }
     __syncthreads();
+  };
+
+  ChunkRegs bufA, bufB;
+  if (nchunks > 0) load_chunk(0, bufA);
+  for (int ci = 0; ci < nchunks; ci += 2) {
+    load_chunk(min(ci + 1, nchunks - 1), bufB);
+    process(ci, bufA);
+    if (ci + 1 >= nchunks) break;
+    load_chunk(min(ci + 2, nchunks - 1), bufA);
+    process(ci + 1, bufB);
   }
 
   if (p.sT) {
@@ -879,9 +1009,10 @@ hipError_t launch_all(const PrefillArgs& a) {
   char* ws = nullptr;
   hipError_t err = hipMallocAsync(reinterpret_cast<void**>(&ws), ws_bytes, a.stream);
   if (err != hipSuccess) return err;
-  PrepParams pp{a.q, a.k, a.g, a.beta, ws, sa, a.scale};
-  hipLaunchKernelGGL((chunk_prep_kernel<D, TIn>), dim3(static_cast<unsigned>(slots * a.H)),
-                     dim3(kThreads), 0, a.stream, pp);
+  const int64_t items = slots * a.H;
+  PrepParams pp{a.q, a.k, a.g, a.beta, ws, sa, a.scale, static_cast<int>(items)};
+  const unsigned prep_grid = static_cast<unsigned>(items);
+  hipLaunchKernelGGL((chunk_prep_kernel<D, TIn>), dim3(prep_grid), dim3(kThreads), 0, a.stream, pp);
   err = hipGetLastError();
   if (err == hipSuccess) {
     // enough (sequence, head, dv slice) workgroups to cover the machine's 256 CUs
