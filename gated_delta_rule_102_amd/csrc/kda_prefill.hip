@@ -32,6 +32,7 @@
 // referenced to the cumulative decay at the end of their own sub-tile -- row side
 // e^{G_t - R_I} in [1, e^80], column side e^{R_I - G_s} <= 1, both in bf16 range.
 
+#include <cstdlib>
 #include <type_traits>
 
 #include "kda_device.h"
@@ -255,7 +256,10 @@ struct PrepCfg {
   static constexpr int QB = 0, KBT = QB + kC * RBD, PB = KBT + D * RBC, XS = PB + kC * RBC;
   static constexpr int XLD = 17;                 // fp32 row stride of the 16x16 X tiles
   static constexpr int R1B = XS + 4 * 16 * XLD * 4;
-  static constexpr int R1 = (R1A > R1B ? R1A : R1B + 15) / 16 * 16;
+  static constexpr int RAW = 0;                  // q, k, g of the chunk as loaded
+  static constexpr int R1R = 3 * kC * D * (F32 ? 4 : 2);
+  static constexpr int R1AB = R1A > R1B ? R1A : R1B;
+  static constexpr int R1 = ((R1AB > R1R ? R1AB : R1R) + 15) / 16 * 16;
   static constexpr int AT = R1;                  // [64][64] fp32: A, then T in place
   static constexpr int MB = AT + kC * kC * 4;    // [64][64] operand: M
   static constexpr int FIJ = MB + kC * RBC;      // [6][D] fp32 pair factors
@@ -340,21 +344,29 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepParams p) {
     lds_set1<F32>(smem + CF::MB + swz<CF::RBC>(row, col * E), 0.f);
   }
 
+  // q, k, g of the chunk go straight from memory into region 1 (16 bytes per lane,
+  // 1 KB contiguous per instruction); each lane then picks up its own channels.
   auto load_raw = [&](const PrepItem& it, RC& rc) {
-    if (!it.valid) return;
     const int64_t base_qk = (static_cast<int64_t>(it.t0) * H + it.h) * D;
     const uint32_t bytes_qk = (it.nrow - 1) * rs_qk + D * EI;   // rows past the end read 0
-    const auto rq = make_rsrc(static_cast<const TIn*>(p.q) + base_qk, bytes_qk);
-    const auto rk = make_rsrc(static_cast<const TIn*>(p.k) + base_qk, bytes_qk);
-    const auto rg = make_rsrc(static_cast<const TIn*>(p.g) + base_qk, bytes_qk);
-    const uint32_t vo = lane * CPL * EI;
+    const __amdgpu_buffer_rsrc_t rsrc[3] = {
+        make_rsrc(static_cast<const TIn*>(p.g) + base_qk, bytes_qk),
+        make_rsrc(static_cast<const TIn*>(p.k) + base_qk, bytes_qk),
+        make_rsrc(static_cast<const TIn*>(p.q) + base_qk, bytes_qk)};
+    constexpr int RBI = D * EI;                 // bytes of one token row of one head
+    constexpr int RPI = 1024 / RBI;             // rows per 1 KB instruction
+    constexpr int LPR = RBI / 16;               // lanes per row
+    const int uw = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const uint32_t so = (16 * wave + r) * rs_qk;
-      if constexpr (!F32 && CPL == 1) {
-        rc.g[r] = buf_ld16(rg, vo, so); rc.k[r] = buf_ld16(rk, vo, so); rc.q[r] = buf_ld16(rq, vo, so);
-      } else {
-        rc.g[r] = buf_ld32(rg, vo, so); rc.k[r] = buf_ld32(rk, vo, so); rc.q[r] = buf_ld32(rq, vo, so);
+    for (int x = 0; x < 3; ++x) {
+#pragma unroll
+      for (int j = 0; j < 16 / RPI; ++j) {
+        const int row0 = 16 * uw + j * RPI;
+        const int row = row0 + lane / LPR;
+        char* dst = smem + CF::RAW + x * kC * RBI + row0 * RBI;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc[x], (__attribute__((address_space(3))) void*)dst, 16,
+            row * rs_qk + (lane % LPR) * 16, 0, 0, 0);
       }
     }
     if (tid < kC) {
@@ -362,6 +374,21 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepParams p) {
                                 (it.nrow - 1) * H * EI + EI);
       if constexpr (F32) rc.beta = buf_ld32(rb, tid * H * EI, 0);
       else rc.beta = static_cast<uint32_t>(buf_ld16(rb, tid * H * EI, 0)) << 16;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int off = (16 * wave + r) * RBI + lane * CPL * EI;
+      if constexpr (!F32 && CPL == 1) {
+        rc.g[r] = *reinterpret_cast<const uint16_t*>(smem + CF::RAW + 0 * kC * RBI + off);
+        rc.k[r] = *reinterpret_cast<const uint16_t*>(smem + CF::RAW + 1 * kC * RBI + off);
+        rc.q[r] = *reinterpret_cast<const uint16_t*>(smem + CF::RAW + 2 * kC * RBI + off);
+      } else {
+        rc.g[r] = *reinterpret_cast<const uint32_t*>(smem + CF::RAW + 0 * kC * RBI + off);
+        rc.k[r] = *reinterpret_cast<const uint32_t*>(smem + CF::RAW + 1 * kC * RBI + off);
+        rc.q[r] = *reinterpret_cast<const uint32_t*>(smem + CF::RAW + 2 * kC * RBI + off);
+      }
     }
   };
 
@@ -1017,7 +1044,13 @@ hipError_t launch_all(const PrefillArgs& a) {
   if (err == hipSuccess) {
     // enough (sequence, head, dv slice) workgroups to cover the machine's 256 CUs
     const int streams = a.N * a.H;
-    if constexpr (D == 128) {
+    // KDA_SCAN_DVS (16/32/64/128) overrides the slice width for tuning runs
+    static const int forced = [] { const char* e = std::getenv("KDA_SCAN_DVS"); return e ? std::atoi(e) : 0; }();
+    if (forced == 16) err = launch_scan<D, 16, TIn>(a, sa, ws);
+    else if (forced == 32) err = launch_scan<D, 32, TIn>(a, sa, ws);
+    else if (forced == 64) err = launch_scan<D, 64, TIn>(a, sa, ws);
+    else if (forced == 128 && D == 128) err = launch_scan<D, D, TIn>(a, sa, ws);
+    else if constexpr (D == 128) {
       if (streams < 64) err = launch_scan<D, 16, TIn>(a, sa, ws);
       else if (streams < 128) err = launch_scan<D, 32, TIn>(a, sa, ws);
       else if (streams < 512) err = launch_scan<D, 64, TIn>(a, sa, ws);
