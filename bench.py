@@ -18,8 +18,8 @@ a bounded sample of the same workload.  One JSON line is printed.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -53,6 +53,44 @@ def prefill_flops(B, T, H, d):
     return n * tri, n * full
 
 
+PREFILL_SRC = os.path.join(ROOT, "gated_delta_rule_102_amd", "csrc", "kda_prefill.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_4x4096_hbm_traffic.txt")
+
+
+def source_digest(path=PREFILL_SRC):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per prefill call from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, scaled by the plain-copy calibration; None if that summary was taken
+    on a different version of the prefill kernels."""
+    try:
+        vals = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    key, val = line.split(":", 1)
+                    vals[key.strip()] = val.strip()
+        if vals.get("kernel_source_sha256") != source_digest():
+            return None
+        return float(vals["hbm_bytes_per_call"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def pmc_copy(torch, nbytes=256 << 20, reps=3):
+    """A plain device copy of known size, for scaling the PMC byte counters."""
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_copy_bytes_read": nbytes, "pmc_copy_bytes_written": nbytes,
+                      "reps": reps}))
+
+
 def decode_bytes(B, H, d, elt):
     """Per step: the fp32 state read and written once, plus the token's inputs/output."""
     state = B * H * d * d * 4 * 2
@@ -67,6 +105,8 @@ def main():
     ap.add_argument("--decode-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--pmc-copy", action="store_true",
+                    help="only run a plain 256 MiB copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the KDA path here has no multi-GPU mode "
@@ -82,6 +122,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.pmc_copy:
+        pmc_copy(torch)
+        return
     kda.load_library()
     dev = "cuda:0"
     torch.cuda.set_device(0)
@@ -137,9 +180,12 @@ def main():
                    "chunk": CHUNK, "state": "fp32, initial ~0.1 N(0,1), final returned",
                    "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "prefill_kernel<128,32,bf16>", "kernel_ms": kern_avg_s * 1e3,
-                     "algorithmic_bytes": nbytes},
+                     "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(),
+                     "kernel": "kda_chunk_fwd = chunk_prep_kernel<128,bf16> + "
+                               "state_scan_kernel<128,32,bf16>",
+                     "kernel_ms": kern_avg_s * 1e3, "algorithmic_bytes": nbytes,
+                     "kernel_source_sha256": source_digest()},
         "prefill": {
             "kernel_ms_avg": kern_avg_s * 1e3, "kernel_ms_min": min(kern_ms),
             "token_heads_per_s": tokens * H / kern_avg_s,
@@ -199,20 +245,23 @@ def main():
         from oracle import oracle_forward  # the CPU baseline leg may load the oracle
         cores = max(1, min(os.cpu_count() or 1, 16))
         wcpu = kin.make_workload(w, device=dev)
-        npairs = 2 * cores
-        pairs = [(i % B, (i * 7) % H) for i in range(npairs)]
         qc, kc, vc, gc, bc = (wcpu[x].cpu() for x in ("q", "k", "v", "g", "beta"))
         s0 = wcpu["initial_state"].cpu()
-        tc = time.perf_counter()
-        oracle_forward(qc, kc, vc, gc, bc, scale, B=B, T=T, initial_state=s0, pairs=pairs,
-                       store_out=True, nthreads=cores)
-        cpu_s = time.perf_counter() - tc
+        # the whole workload (all B*H pairs at full length), repeated until about
+        # 10 s of CPU work have been timed
+        reps, cpu_s = 0, 0.0
+        while reps < 1 or (cpu_s * cores < 10.0 and reps < 8):
+            tc = time.perf_counter()
+            oracle_forward(qc, kc, vc, gc, bc, scale, B=B, T=T, initial_state=s0,
+                           store_out=True, nthreads=cores)
+            cpu_s += time.perf_counter() - tc
+            reps += 1
         result["cpu_baseline"] = {
-            "value": npairs * T / H / cpu_s, "unit": "tokens/s", "cores": cores,
+            "value": reps * B * T / cpu_s, "unit": "tokens/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"{npairs} of the {B * H} (sequence, head) pairs of prefill_4x4096 at "
-                      f"full length T={T} (fp64 sequential recurrence, OpenMP over pairs); "
-                      f"rate scaled to tokens/s of all {H} heads; {cpu_s:.2f} s wall",
+            "sample": f"the full prefill_4x4096 workload ({B * H} (sequence, head) pairs, "
+                      f"T={T}) run {reps} times by the fp64 sequential recurrence with "
+                      f"OpenMP over pairs: {cpu_s:.2f} s wall on {cores} threads",
         }
     print(json.dumps(result))
 

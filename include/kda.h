@@ -25,7 +25,11 @@
  *
  * Conventions shared by every entry point
  *  - All tensor pointers are DEVICE pointers owned by the caller, contiguous and
- *    row-major.  Nothing is allocated or freed by the library.
+ *    row-major.  The prefill entry points allocate one workspace per call with
+ *    hipMallocAsync on `stream` and release it with hipFreeAsync on the same
+ *    stream (66,048 bytes per 64-token chunk per head for bf16 at d = 128;
+ *    chunks counted per sequence); an allocation failure returns KDA_ERR_HIP.
+ *    Decode allocates nothing.
  *  - Alignment (KDA_ERR_ALIGN otherwise): prefill v and out 16 bytes, q, k, g and
  *    the states 4 bytes, beta its element size; decode state 16 bytes, every
  *    other pointer its element size.
