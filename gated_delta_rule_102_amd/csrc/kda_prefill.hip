@@ -900,8 +900,11 @@ __global__ __launch_bounds__(kThreads, 1) void state_scan_kernel(ScanParams p) {
       // pieces beyond the tile (narrow slices) re-read the last row; they are not stored
       const int pc = min(tid + pi * kThreads, kC * VPR - 1);
       const int vrow = pc / VPR, vcol = (pc % VPR) * 8;   // rows past the end read zero
-      cr.vv[pi][0] = buf_ld128(rv, vcol * EI, vrow * rs_v);
-      if constexpr (F32) cr.vv[pi][1] = buf_ld128(rv, vcol * EI + 16, vrow * rs_v);
+      // per-lane offsets go in the vector offset (a per-lane scalar offset would
+      // serialise the instruction over the distinct values)
+      const uint32_t vo = vrow * rs_v + vcol * EI;
+      cr.vv[pi][0] = buf_ld128(rv, vo, 0);
+      if constexpr (F32) cr.vv[pi][1] = buf_ld128(rv, vo + 16, 0);
     }
   };
 
@@ -936,21 +939,30 @@ __global__ __launch_bounds__(kThreads, 1) void state_scan_kernel(ScanParams p) {
     }
     __syncthreads();
 
-    // U = Tb V and O_v = P V (state independent), W S and Q' S (state products)
+    // U = Tb V and O_v = P V (state independent), W S and Q' S (state products).
+    // All B fragments are read from LDS first so their latencies overlap.
+    Frag<F32> bv[NJT][2], bs[NJT][NKK];
+#pragma unroll
+    for (int jt = 0; jt < NJT; ++jt) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        bv[jt][kk] = lds_frag<F32, CF::RBC>(smem + CF::VT, 16 * jt + l16, (kk * 32 + g4 * 8) * E);
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        bs[jt][kk] = lds_frag<F32, CF::RBD>(smem + CF::SB, 16 * jt + l16, (kk * 32 + g4 * 8) * E);
+    }
 #pragma unroll
     for (int jt = 0; jt < NJT; ++jt) {
       f32x4_t u = {0.f, 0.f, 0.f, 0.f}, ov = u, ws = u, qs = u;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const Frag<F32> b = lds_frag<F32, CF::RBC>(smem + CF::VT, 16 * jt + l16, (kk * 32 + g4 * 8) * E);
-        u = mma32<F32>(u, cur.ftb[kk], b);
-        ov = mma32<F32>(ov, cur.fpp[kk], b);
+        u = mma32<F32>(u, cur.ftb[kk], bv[jt][kk]);
+        ov = mma32<F32>(ov, cur.fpp[kk], bv[jt][kk]);
       }
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        const Frag<F32> b = lds_frag<F32, CF::RBD>(smem + CF::SB, 16 * jt + l16, (kk * 32 + g4 * 8) * E);
-        ws = mma32<F32>(ws, cur.fw[kk], b);
-        qs = mma32<F32>(qs, cur.fq[kk], b);
+        ws = mma32<F32>(ws, cur.fw[kk], bs[jt][kk]);
+        qs = mma32<F32>(qs, cur.fq[kk], bs[jt][kk]);
       }
       // Delta = U - W S -> [j][t];  O = Q' S + P V -> [t][j]
       const int j = 16 * jt + l16, t = 16 * wave + 4 * g4;
@@ -962,6 +974,12 @@ __global__ __launch_bounds__(kThreads, 1) void state_scan_kernel(ScanParams p) {
     __syncthreads();
 
     // S <- Diag(Lambda) S + Kt^T Delta
+    Frag<F32> bd[NJT][2];
+#pragma unroll
+    for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        bd[jt][kk] = lds_frag<F32, CF::RBC>(smem + CF::DT, 16 * jt + l16, (kk * 32 + g4 * 8) * E);
 #pragma unroll
     for (int ri = 0; ri < RT; ++ri) {
       const int rt = wave * RT + ri;
@@ -971,10 +989,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_scan_kernel(ScanParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i] = S[ri][jt][i] * __int_as_float(cur.lam[ri][i]);
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const Frag<F32> b = lds_frag<F32, CF::RBC>(smem + CF::DT, 16 * jt + l16, (kk * 32 + g4 * 8) * E);
-          acc = mma32<F32>(acc, cur.fkt[ri][kk], b);
-        }
+        for (int kk = 0; kk < 2; ++kk) acc = mma32<F32>(acc, cur.fkt[ri][kk], bd[jt][kk]);
         S[ri][jt] = acc;
         lds_put4<F32>(smem + CF::SB + swz<CF::RBD>(16 * jt + l16, (16 * rt + 4 * g4) * E),
                       acc[0], acc[1], acc[2], acc[3]);
@@ -986,7 +1001,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_scan_kernel(ScanParams p) {
       for (int pc = tid; pc < kC * PPR; pc += kThreads) {
         const int t = pc / PPR, part = pc % PPR;
         const i32x4_t val = *reinterpret_cast<const i32x4_t*>(smem + CF::OST + t * CF::RBO + part * 16);
-        buf_st128(val, ro, part * 16, t * rs_v);
+        buf_st128(val, ro, t * rs_v + part * 16, 0);
       }
     }
     __syncthreads();
