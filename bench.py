@@ -182,8 +182,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
                      "traffic": measured_traffic(),
-                     "kernel": "kda_chunk_fwd = chunk_prep_kernel<128,bf16> + "
-                               "state_scan_kernel<128,32,bf16>",
+                     "kernel": "kda_chunk_fwd = 5 launches of prefill_group_kernel<128,32,bf16> "
+                               "(4 windows of 16 chunks: preparation of window k with the "
+                               "state scan of window k-1)",
                      "kernel_ms": kern_avg_s * 1e3, "algorithmic_bytes": nbytes,
                      "kernel_source_sha256": source_digest()},
         "prefill": {

@@ -274,7 +274,8 @@ struct PrepParams {
   char* ws;
   SeqArgs sa;
   float scale;
-  int items;       // workspace slots x heads
+  int items;       // work items of the launch
+  int c_lo, cg;    // cg > 0: items cover chunks [c_lo, c_lo + cg) of every sequence
 };
 
 // Raw input words of one token row for the CPL channels a lane owns.
@@ -309,9 +310,31 @@ __device__ __forceinline__ PrepItem prep_item(const PrepParams& p, int item) {
   return it;
 }
 
-// One workgroup per (chunk, head) work item.
+// Group mode: item -> (sequence n, chunk c_lo + lc, head h), written to slot
+// (n * cg + lc) * H + h of the launch's group workspace; chunks past the end of
+// the sequence are no work.
+__device__ __forceinline__ PrepItem prep_group_item(const PrepParams& p, int item, int& slot) {
+  PrepItem it{false, 0, 0, 0, 0};
+  const int H = p.sa.H;
+  if (item >= p.items) return it;
+  it.h = item % H;
+  const int lc = (item / H) % p.cg, n = item / (H * p.cg);
+  int tok0, len;
+  seq_bounds(p.sa, n, tok0, len);
+  const int c = p.c_lo + lc;
+  if (c * kC >= len) return it;
+  it.valid = true;
+  it.t0 = tok0 + c * kC;
+  it.nrow = min(kC, len - c * kC);
+  slot = n * p.cg + lc;
+  return it;
+}
+
+// All state-independent work of one (chunk, head) item, by one workgroup; the
+// results go to the workspace slot at `slot_ptr`.
 template <int D, typename TIn>
-__global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepParams p) {
+__device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const PrepItem& cur_it,
+                                          char* slot_ptr) {
   using CF = PrepCfg<D, TIn>;
   using SL = Slot<D, CF::F32>;
   using RC = RawChunk<TIn, CF::CPL>;
@@ -319,9 +342,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepParams p) {
   constexpr int CPL = CF::CPL;
   constexpr int E = CF::E;
   constexpr int EI = CF::EI;
-  __shared__ __attribute__((aligned(16))) char smem[CF::LDS];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the wavefront index is uniform: keeping it scalar makes per-wavefront branches
+  // and offsets scalar work
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l16 = lane & 15, g4 = lane >> 4;
   const int H = p.sa.H;
   const uint32_t rs_qk = static_cast<uint32_t>(H) * D * EI;    // token row stride (bytes)
@@ -392,13 +416,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepParams p) {
     }
   };
 
-  const PrepItem cur_it = prep_item(p, blockIdx.x);
-  if (!cur_it.valid) return;         // unused workspace slot
   RC cur;
   load_raw(cur_it, cur);
   {
-    const auto rw = make_rsrc(p.ws + (static_cast<int64_t>(cur_it.slot) * H + cur_it.h) * SL::BYTES,
-                              SL::BYTES);
+    const auto rw = make_rsrc(slot_ptr, SL::BYTES);
 
     // ------------------------------------------------ phase E: decay factors
     // wavefront `wave` owns token rows 16*wave .. +15; lane owns key channels
@@ -454,7 +475,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepParams p) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) if (m <= wave) pre *= b4[m];
       eR1[e] = pre;                                    // e^{R_{w+1}}
-      const float inv_bt = 1.f / b4[wave];
+      const float inv_bt = __builtin_amdgcn_rcpf(b4[wave]);   // b4 in [e^-80, 1]
       float acc = 1.f;
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
@@ -760,6 +781,17 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepParams p) {
   }
 }
 
+// One workgroup per (workspace slot, head) item.
+template <int D, typename TIn>
+__global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[PrepCfg<D, TIn>::LDS];
+  const PrepItem it = prep_item(p, blockIdx.x);
+  if (!it.valid) return;         // unused workspace slot
+  prep_body<D, TIn>(p, smem, it,
+                    p.ws + (static_cast<int64_t>(it.slot) * p.sa.H + it.h) *
+                               Slot<D, std::is_same<TIn, float>::value>::BYTES);
+}
+
 // ================================================================= kernel 2
 
 template <int D, int DVS, typename TIn>
@@ -778,34 +810,42 @@ struct ScanCfg {
   static constexpr int VT = SB + DVS * RBD;
   static constexpr int DT = VT + DVS * RBC;
   static constexpr int OST = DT + DVS * RBC;
-  static constexpr int ORD = OST + kC * RBO;
+  static constexpr int OSTB = kC * RBO;         // one output stage; two alternate
+  static constexpr int ORD = OST + 2 * OSTB;
   static constexpr int LDS = ORD + 256 * 4;
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
 struct ScanParams {
   const void* v;
-  const float* s0;
+  const float* s0;     // initial states (null: zero), read by the window holding chunk 0
   void* out;
-  float* sT;
+  float* sT;           // final states (null: not written), written by the window holding
+                       // a sequence's last chunk
+  float* sbuf;         // states carried between windows
   const char* ws;
   SeqArgs sa;
+  int c_lo, c_hi;      // chunk window [c_lo, c_hi) of every sequence
+  int cg;              // > 0: group workspace, slot (n * cg + c - c_lo) * H + h;
+                       // 0: slot (tok0 / 64 + n + c) * H + h
 };
 
+// The chunks of one window of one (sequence, head, dv slice), in order, by one
+// workgroup (`bid` numbers the scan workgroups of the launch from 0).
 template <int D, int DVS, typename TIn>
-__global__ __launch_bounds__(kThreads, 1) void state_scan_kernel(ScanParams p) {
+__device__ __forceinline__ void scan_body(const ScanParams& p, char* smem, const int bid) {
   using CF = ScanCfg<D, DVS, TIn>;
   using SL = Slot<D, CF::F32>;
   constexpr bool F32 = CF::F32;
   constexpr int E = CF::E, EI = CF::EI, NJT = CF::NJT, NKK = CF::NKK, RT = CF::RT;
-  __shared__ __attribute__((aligned(16))) char smem[CF::LDS];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the wavefront index is uniform: keeping it scalar makes per-wavefront branches
+  // and offsets scalar work
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l16 = lane & 15, g4 = lane >> 4;
   const int H = p.sa.H, N = p.sa.N;
 
   // XCD-aware placement: the dv slices of one (sequence, head) land on one XCD
-  const int bid = blockIdx.x;
   const int xcd = bid & 7, r8 = bid >> 3;
   const int grp = (r8 / CF::NSPLIT) * 8 + xcd;
   const int split = r8 % CF::NSPLIT;
@@ -837,13 +877,17 @@ __global__ __launch_bounds__(kThreads, 1) void state_scan_kernel(ScanParams p) {
   int tok0, len;
   seq_bounds(p.sa, n, tok0, len);
   const int nchunks = (len + kC - 1) / kC;
-  const int sbase = slot_base(tok0, n);
+  const int c_begin = p.c_lo, c_end = min(p.c_hi, nchunks);
+  if (c_begin >= c_end && c_begin > 0) return;   // the sequence ended in an earlier window
+  const int sbase = p.cg > 0 ? n * p.cg - p.c_lo : slot_base(tok0, n);
   const int j0 = split * DVS;
+  const float* s_in = c_begin == 0 ? p.s0 : p.sbuf;
+  float* s_out = p.c_hi >= nchunks ? p.sT : p.sbuf;
 
   // state tiles (rt, jt): rows c = 16*rt + 4*g4 + i, columns j = 16*jt + l16
   f32x4_t S[RT][NJT];
   {
-    const float* s0 = p.s0 ? p.s0 + (static_cast<int64_t>(n) * H + h) * D * D : nullptr;
+    const float* s0 = s_in ? s_in + (static_cast<int64_t>(n) * H + h) * D * D : nullptr;
 #pragma unroll
     for (int ri = 0; ri < RT; ++ri)
 #pragma unroll
@@ -869,32 +913,21 @@ __global__ __launch_bounds__(kThreads, 1) void state_scan_kernel(ScanParams p) {
     i32x4_t lam[RT];
     i32x4_t vv[VPT][F32 ? 2 : 1];
   };
-  auto load_chunk = [&](int ci, ChunkRegs& cr) {
+  // Loads of one chunk come in three groups, issued at three points of the previous
+  // step so that the memory pipeline streams while the wavefront computes instead of
+  // stalling the wavefront at issue: V, Tb and P (first used at the top of the step),
+  // W and Q' (first products), Kt and Lambda (state update).  Vector-memory counters
+  // retire in order, so each use waits only for its own group.
+  constexpr uint32_t FB = F32 ? 2048 : 1024;      // bytes per fragment (see frag_off)
+  auto slot_rsrc = [&](int ci) {
+    return make_rsrc(p.ws + (static_cast<int64_t>(sbase + ci) * H + h) * SL::BYTES, SL::BYTES);
+  };
+  auto load_group1 = [&](int ci, ChunkRegs& cr) {
     const int t0 = tok0 + ci * kC;
     const int nrow = min(kC, len - ci * kC);
-    const auto rw = make_rsrc(p.ws + (static_cast<int64_t>(sbase + ci) * H + h) * SL::BYTES, SL::BYTES);
+    const auto rw = slot_rsrc(ci);
     const int64_t vbase = (static_cast<int64_t>(t0) * H + h) * D + j0;
     const auto rv = make_rsrc(static_cast<const TIn*>(p.v) + vbase, (nrow - 1) * rs_v + DVS * EI);
-    // every fragment is one contiguous 1 KB per wavefront (see frag_off)
-    constexpr uint32_t FB = F32 ? 2048 : 1024;      // bytes per fragment
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const uint32_t o = (wave * NKK + kk) * FB + lane * 16;
-      cr.fw[kk] = buf_frag2<F32>(rw, SL::W + o);
-      cr.fq[kk] = buf_frag2<F32>(rw, SL::QP + o);
-    }
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const uint32_t o = (wave * 2 + kk) * FB + lane * 16;
-      cr.ftb[kk] = buf_frag2<F32>(rw, SL::TB + o);
-      cr.fpp[kk] = buf_frag2<F32>(rw, SL::PP + o);
-#pragma unroll
-      for (int ri = 0; ri < RT; ++ri)
-        cr.fkt[ri][kk] = buf_frag2<F32>(rw, SL::KT + ((wave * RT + ri) * 2 + kk) * FB + lane * 16);
-    }
-#pragma unroll
-    for (int ri = 0; ri < RT; ++ri)
-      cr.lam[ri] = buf_ld128(rw, SL::LAM + (16 * (wave * RT + ri) + 4 * g4) * 4, 0);
 #pragma unroll
     for (int pi = 0; pi < VPT; ++pi) {
       // pieces beyond the tile (narrow slices) re-read the last row; they are not stored
@@ -906,17 +939,56 @@ __global__ __launch_bounds__(kThreads, 1) void state_scan_kernel(ScanParams p) {
       cr.vv[pi][0] = buf_ld128(rv, vo, 0);
       if constexpr (F32) cr.vv[pi][1] = buf_ld128(rv, vo + 16, 0);
     }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const uint32_t o = (wave * 2 + kk) * FB + lane * 16;
+      cr.ftb[kk] = buf_frag2<F32>(rw, SL::TB + o);
+      cr.fpp[kk] = buf_frag2<F32>(rw, SL::PP + o);
+    }
+  };
+  auto load_group2 = [&](int ci, ChunkRegs& cr) {
+    const auto rw = slot_rsrc(ci);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const uint32_t o = (wave * NKK + kk) * FB + lane * 16;
+      cr.fw[kk] = buf_frag2<F32>(rw, SL::W + o);
+      cr.fq[kk] = buf_frag2<F32>(rw, SL::QP + o);
+    }
+  };
+  auto load_group3 = [&](int ci, ChunkRegs& cr) {
+    const auto rw = slot_rsrc(ci);
+#pragma unroll
+    for (int ri = 0; ri < RT; ++ri)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        cr.fkt[ri][kk] = buf_frag2<F32>(rw, SL::KT + ((wave * RT + ri) * 2 + kk) * FB + lane * 16);
+#pragma unroll
+    for (int ri = 0; ri < RT; ++ri)
+      cr.lam[ri] = buf_ld128(rw, SL::LAM + (16 * (wave * RT + ri) + 4 * g4) * 4, 0);
   };
 
-  // Two register sets alternate: while chunk ci is computed from one, the loads of
-  // chunk ci+1 fill the other.  The loads are unconditional (the last chunk
-  // re-reads itself), so no branch sits between a load and its first use.
-  auto process = [&](const int ci, const ChunkRegs& cur) {
-    const int t0 = tok0 + ci * kC;
-    const int nrow = min(kC, len - ci * kC);
+  // Output of chunk cj, staged in LDS by its step, is written one step later, after
+  // that step's loads have been waited for: stores share the loads' counter, so a
+  // store issued just before a wait would make the wait cover its completion.
+  auto store_out = [&](const int cj) {
+    const int t0 = tok0 + cj * kC;
+    const int nrow = min(kC, len - cj * kC);
     const int64_t vbase = (static_cast<int64_t>(t0) * H + h) * D + j0;
     const auto ro = make_rsrc(static_cast<TIn*>(p.out) + vbase, (nrow - 1) * rs_v + DVS * EI);
+    const char* ost = smem + CF::OST + (cj & 1) * CF::OSTB;
+    constexpr int PPR = DVS * E / 16;    // 16-byte pieces per output row
+    for (int pc = tid; pc < kC * PPR; pc += kThreads) {
+      const int t = pc / PPR, part = pc % PPR;
+      const i32x4_t val = *reinterpret_cast<const i32x4_t*>(ost + t * CF::RBO + part * 16);
+      buf_st128(val, ro, t * rs_v + part * 16, 0);   // rows past the sequence end are dropped
+    }
+  };
 
+  // Two register sets alternate.  Step ci computes from `cur` while the loads of chunk cn (ci + 1, clamped so the
+  // last step re-reads itself and no load sits behind a branch) fill `nxt`.
+  auto process = [&](const int ci, const ChunkRegs& cur, const int cn, ChunkRegs& nxt) {
+    load_group1(cn, nxt);
+    __builtin_amdgcn_sched_barrier(0);
     // V slice, transposed to [j][t]
 #pragma unroll
     for (int pi = 0; pi < VPT; ++pi) {
@@ -937,6 +1009,7 @@ __global__ __launch_bounds__(kThreads, 1) void state_scan_kernel(ScanParams p) {
         }
       }
     }
+    if (ci > c_begin) store_out(ci - 1);
     __syncthreads();
 
     // U = Tb V and O_v = P V (state independent), W S and Q' S (state products).
@@ -951,6 +1024,9 @@ __global__ __launch_bounds__(kThreads, 1) void state_scan_kernel(ScanParams p) {
       for (int kk = 0; kk < NKK; ++kk)
         bs[jt][kk] = lds_frag<F32, CF::RBD>(smem + CF::SB, 16 * jt + l16, (kk * 32 + g4 * 8) * E);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    load_group2(cn, nxt);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int jt = 0; jt < NJT; ++jt) {
       f32x4_t u = {0.f, 0.f, 0.f, 0.f}, ov = u, ws = u, qs = u;
@@ -969,11 +1045,14 @@ __global__ __launch_bounds__(kThreads, 1) void state_scan_kernel(ScanParams p) {
       lds_put4<F32>(smem + CF::DT + swz<CF::RBC>(j, t * E), u[0] - ws[0], u[1] - ws[1],
                     u[2] - ws[2], u[3] - ws[3]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lds_set1<F32>(smem + CF::OST + (t + i) * CF::RBO + j * E, qs[i] + ov[i]);
+      for (int i = 0; i < 4; ++i)
+        lds_set1<F32>(smem + CF::OST + (ci & 1) * CF::OSTB + (t + i) * CF::RBO + j * E, qs[i] + ov[i]);
     }
     __syncthreads();
 
     // S <- Diag(Lambda) S + Kt^T Delta
+    load_group3(cn, nxt);
+    __builtin_amdgcn_sched_barrier(0);
     Frag<F32> bd[NJT][2];
 #pragma unroll
     for (int jt = 0; jt < NJT; ++jt)
@@ -995,30 +1074,24 @@ __global__ __launch_bounds__(kThreads, 1) void state_scan_kernel(ScanParams p) {
                       acc[0], acc[1], acc[2], acc[3]);
       }
     }
-    // output rows as 16-byte pieces; rows past the sequence end are dropped
-    {
-      constexpr int PPR = DVS * E / 16;
-      for (int pc = tid; pc < kC * PPR; pc += kThreads) {
-        const int t = pc / PPR, part = pc % PPR;
-        const i32x4_t val = *reinterpret_cast<const i32x4_t*>(smem + CF::OST + t * CF::RBO + part * 16);
-        buf_st128(val, ro, t * rs_v + part * 16, 0);
-      }
-    }
     __syncthreads();
   };
 
   ChunkRegs bufA, bufB;
-  if (nchunks > 0) load_chunk(0, bufA);
-  for (int ci = 0; ci < nchunks; ci += 2) {
-    load_chunk(min(ci + 1, nchunks - 1), bufB);
-    process(ci, bufA);
-    if (ci + 1 >= nchunks) break;
-    load_chunk(min(ci + 2, nchunks - 1), bufA);
-    process(ci + 1, bufB);
+  if (c_end > c_begin) {
+    load_group1(c_begin, bufA);
+    load_group2(c_begin, bufA);
+    load_group3(c_begin, bufA);
   }
+  for (int ci = c_begin; ci < c_end; ci += 2) {
+    process(ci, bufA, min(ci + 1, c_end - 1), bufB);
+    if (ci + 1 >= c_end) break;
+    process(ci + 1, bufB, min(ci + 2, c_end - 1), bufA);
+  }
+  if (c_end > c_begin) store_out(c_end - 1);
 
-  if (p.sT) {
-    float* sT = p.sT + (static_cast<int64_t>(n) * H + h) * D * D;
+  if (s_out) {
+    float* sT = s_out + (static_cast<int64_t>(n) * H + h) * D * D;
 #pragma unroll
     for (int ri = 0; ri < RT; ++ri)
 #pragma unroll
@@ -1029,22 +1102,123 @@ __global__ __launch_bounds__(kThreads, 1) void state_scan_kernel(ScanParams p) {
   }
 }
 
+template <int D, int DVS, typename TIn>
+__global__ __launch_bounds__(kThreads, 1) void state_scan_kernel(ScanParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[ScanCfg<D, DVS, TIn>::LDS];
+  scan_body<D, DVS, TIn>(p, smem, blockIdx.x);
+}
+
+// ================================================================= grouped launch
+// Fixed-length prefill runs in windows of cg chunks.  Launch k carries the scan of
+// window k-1 (workgroups 0 .. nscan-1) and the preparation of window k (the rest),
+// whose workspaces alternate between two buffers.  The two roles are independent
+// within a launch -- the scan reads what the previous launch prepared -- so the
+// memory-bound scan and the arithmetic-bound preparation share the CUs, and the
+// workspace a scan reads was written one launch earlier, small enough to still be
+// in cache.
+struct GroupParams {
+  PrepParams pp;
+  ScanParams sp;
+  int nscan;
+};
+
+template <int D, int DVS, typename TIn>
+struct GroupCfg {
+  static constexpr int A = PrepCfg<D, TIn>::LDS, B = ScanCfg<D, DVS, TIn>::LDS;
+  static constexpr int LDS = A > B ? A : B;
+};
+
+template <int D, int DVS, typename TIn>
+__global__ __launch_bounds__(kThreads, 2) void prefill_group_kernel(GroupParams g) {
+  __shared__ __attribute__((aligned(16))) char smem[GroupCfg<D, DVS, TIn>::LDS];
+  const int bid = blockIdx.x;
+  if (bid < g.nscan) {
+    scan_body<D, DVS, TIn>(g.sp, smem, bid);
+    return;
+  }
+  int slot = 0;
+  const PrepItem it = prep_group_item(g.pp, bid - g.nscan, slot);
+  if (!it.valid) return;
+  prep_body<D, TIn>(g.pp, smem, it,
+                    g.pp.ws + (static_cast<int64_t>(slot) * g.pp.sa.H + it.h) *
+                                  Slot<D, std::is_same<TIn, float>::value>::BYTES);
+}
+
 // ---------------------------------------------------------------- launch
+
+// Scan workgroups for N*H (sequence, head) streams cut into D/DVS slices, padded so
+// that the slices of one stream share an XCD.
+template <int D, int DVS>
+int scan_grid(int streams) { return ((streams + 7) / 8) * 8 * (D / DVS); }
 
 template <int D, int DVS, typename TIn>
 hipError_t launch_scan(const PrefillArgs& a, const SeqArgs& sa, const char* ws) {
-  using CF = ScanCfg<D, DVS, TIn>;
-  const int groups = a.N * a.H;
-  const int grid = ((groups + 7) / 8) * 8 * CF::NSPLIT;
-  ScanParams sp{a.v, a.initial_state, a.out, a.final_state, ws, sa};
-  hipLaunchKernelGGL((state_scan_kernel<D, DVS, TIn>), dim3(grid), dim3(kThreads), 0, a.stream, sp);
+  const ScanParams sp{a.v, a.initial_state, a.out, a.final_state, nullptr, ws, sa, 0, 1 << 30, 0};
+  hipLaunchKernelGGL((state_scan_kernel<D, DVS, TIn>), dim3(scan_grid<D, DVS>(a.N * a.H)),
+                     dim3(kThreads), 0, a.stream, sp);
   return hipGetLastError();
+}
+
+// Chunks per window of the grouped launch (KDA_GROUP_CHUNKS overrides it for tuning
+// runs; 0 selects the two-kernel schedule).
+inline int group_chunks(int nchunks) {
+  static const int forced = [] {
+    const char* e = std::getenv("KDA_GROUP_CHUNKS");
+    return e ? std::atoi(e) : -1;
+  }();
+  if (forced >= 0) return forced == 0 ? 0 : std::min(forced, nchunks);
+  // at most 8 windows (each launch boundary drains the machine) and at least 16
+  // chunks per window (the scan role needs enough steps to amortise its state
+  // round trip through memory)
+  const int cg = std::max(16, (nchunks + 7) / 8);
+  return std::min(cg, nchunks);
+}
+
+template <int D, int DVS, typename TIn>
+hipError_t launch_grouped(const PrefillArgs& a, int cg) {
+  constexpr bool F32 = std::is_same<TIn, float>::value;
+  using SL = Slot<D, F32>;
+  const SeqArgs sa{a.cu_seqlens, a.N, a.T, a.total_T, a.H};
+  const int nchunks = (a.T + kC - 1) / kC;
+  const int windows = (nchunks + cg - 1) / cg;
+  const size_t wbytes = static_cast<size_t>(a.N) * cg * a.H * SL::BYTES;
+  const size_t sbytes = windows > 1 ? static_cast<size_t>(a.N) * a.H * D * D * 4 : 0;
+  const int nbuf = windows > 1 ? 2 : 1;
+  char* ws = nullptr;
+  hipError_t err = hipMallocAsync(reinterpret_cast<void**>(&ws), nbuf * wbytes + sbytes, a.stream);
+  if (err != hipSuccess) return err;
+  float* sbuf = sbytes ? reinterpret_cast<float*>(ws + nbuf * wbytes) : nullptr;
+  const int nscan = scan_grid<D, DVS>(a.N * a.H);
+  const int items = a.N * cg * a.H;
+  for (int k = 0; k <= windows && err == hipSuccess; ++k) {
+    GroupParams gp{};
+    gp.nscan = k >= 1 ? nscan : 0;
+    gp.sp = ScanParams{a.v, a.initial_state, a.out, a.final_state, sbuf,
+                       ws + ((k + 1) % nbuf) * wbytes, sa, (k - 1) * cg, k * cg, cg};
+    gp.pp = PrepParams{a.q, a.k, a.g, a.beta, ws + (k % nbuf) * wbytes, sa, a.scale,
+                       k < windows ? items : 0, k * cg, cg};
+    const int grid = gp.nscan + gp.pp.items;
+    hipLaunchKernelGGL((prefill_group_kernel<D, DVS, TIn>), dim3(grid), dim3(kThreads), 0,
+                       a.stream, gp);
+    err = hipGetLastError();
+  }
+  const hipError_t ferr = hipFreeAsync(ws, a.stream);
+  return err != hipSuccess ? err : ferr;
 }
 
 template <int D, typename TIn>
 hipError_t launch_all(const PrefillArgs& a) {
   constexpr bool F32 = std::is_same<TIn, float>::value;
   using SL = Slot<D, F32>;
+  if (a.cu_seqlens == nullptr) {   // fixed length: windows of cg chunks
+    const int cg = group_chunks((a.T + kC - 1) / kC);
+    if (cg > 0) {
+      // slices of at most 32 columns keep the scan role within 256 registers, so a
+      // scan and a preparation workgroup fit on one CU together
+      if (a.N * a.H < 64) return launch_grouped<D, 16, TIn>(a, cg);
+      return launch_grouped<D, 32, TIn>(a, cg);
+    }
+  }
   const SeqArgs sa{a.cu_seqlens, a.N, a.T, a.total_T, a.H};
   const int64_t slots = (a.total_T + kC - 1) / kC + a.N;
   const size_t ws_bytes = static_cast<size_t>(slots) * a.H * SL::BYTES;
@@ -1052,7 +1226,7 @@ hipError_t launch_all(const PrefillArgs& a) {
   hipError_t err = hipMallocAsync(reinterpret_cast<void**>(&ws), ws_bytes, a.stream);
   if (err != hipSuccess) return err;
   const int64_t items = slots * a.H;
-  PrepParams pp{a.q, a.k, a.g, a.beta, ws, sa, a.scale, static_cast<int>(items)};
+  PrepParams pp{a.q, a.k, a.g, a.beta, ws, sa, a.scale, static_cast<int>(items), 0, 0};
   const unsigned prep_grid = static_cast<unsigned>(items);
   hipLaunchKernelGGL((chunk_prep_kernel<D, TIn>), dim3(prep_grid), dim3(kThreads), 0, a.stream, pp);
   err = hipGetLastError();
