@@ -107,6 +107,32 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
   return kda::launch_prefill(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+int kda_chunk_fwd_snapshots(const void* q, const void* k, const void* v, const void* g,
+                            const void* beta, const float* initial_state, void* out,
+                            float* final_state, float* snapshots, int snapshot_tokens, int B,
+                            int T, int H, int dk, int dv, float scale, int dtype,
+                            hipStream_t stream) {
+  int rc = check_common(dk, dv, H, dtype);
+  if (rc != KDA_OK) return rc;
+  if (dtype == KDA_F32 && dk != 64) return KDA_ERR_HEAD_DIM;
+  if (B <= 0 || T <= 0) return KDA_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * T > INT32_MAX / 2) return KDA_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * H > (1 << 24)) return KDA_ERR_SHAPE;
+  if (snapshot_tokens <= 0 || snapshot_tokens % 64 != 0) return KDA_ERR_SHAPE;
+  if (snapshots == nullptr) return KDA_ERR_NULL;
+  rc = check_prefill_ptrs(q, k, v, g, beta, initial_state, out, final_state, dtype);
+  if (rc == KDA_OK && !aligned(snapshots, 4)) rc = KDA_ERR_ALIGN;
+  if (rc != KDA_OK) return rc;
+  rc = check_device();
+  if (rc != KDA_OK) return rc;
+  kda::PrefillArgs a{q, k, v, g, beta, initial_state, out, final_state, nullptr,
+                     B, T, B * T, H, dk, scale, dtype == KDA_F32, stream};
+  a.snapshots = snapshots;
+  a.snap_chunks = snapshot_tokens / 64;
+  a.nsnap = (T + snapshot_tokens - 1) / snapshot_tokens;
+  return kda::launch_prefill(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void* g,
                          const void* beta, const float* initial_state, void* out,
                          float* final_state, const int32_t* cu_seqlens, int N,

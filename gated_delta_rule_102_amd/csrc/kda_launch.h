@@ -30,6 +30,9 @@ struct PrefillArgs {
   float scale;
   bool dtype_f32;
   hipStream_t stream;
+  float* snapshots = nullptr;  // fixed length only: [N, H, nsnap, d, d] or null
+  int snap_chunks = 0;         // snapshot every snap_chunks chunks (and at the end)
+  int nsnap = 0;
 };
 
 hipError_t launch_decode(const DecodeArgs& a);

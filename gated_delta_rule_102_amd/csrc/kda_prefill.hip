@@ -828,6 +828,9 @@ struct ScanParams {
   int c_lo, c_hi;      // chunk window [c_lo, c_hi) of every sequence
   int cg;              // > 0: group workspace, slot (n * cg + c - c_lo) * H + h;
                        // 0: slot (tok0 / 64 + n + c) * H + h
+  float* snap;         // [N, H, nsnap, D, D]: state after every snap_chunks chunks and
+  int snap_chunks;     // after the last chunk; null: none
+  int nsnap;
 };
 
 // The chunks of one window of one (sequence, head, dv slice), in order, by one
@@ -984,6 +987,17 @@ __device__ __forceinline__ void scan_body(const ScanParams& p, char* smem, const
     }
   };
 
+  // This workgroup's columns of the state, to a [D][D] fp32 matrix.
+  auto store_state = [&](float* dst) {
+#pragma unroll
+    for (int ri = 0; ri < RT; ++ri)
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dst[(16 * (wave * RT + ri) + 4 * g4 + i) * D + j0 + 16 * jt + l16] = S[ri][jt][i];
+  };
+
   // Two register sets alternate.  Step ci computes from `cur` while the loads of chunk cn (ci + 1, clamped so the
   // last step re-reads itself and no load sits behind a branch) fill `nxt`.
   auto process = [&](const int ci, const ChunkRegs& cur, const int cn, ChunkRegs& nxt) {
@@ -1074,6 +1088,11 @@ __device__ __forceinline__ void scan_body(const ScanParams& p, char* smem, const
                       acc[0], acc[1], acc[2], acc[3]);
       }
     }
+    if (p.snap != nullptr && (ci + 1 == nchunks || (ci + 1) % p.snap_chunks == 0)) {
+      // state after chunk ci: a prefix-cache snapshot
+      const int si = ci + 1 == nchunks ? p.nsnap - 1 : (ci + 1) / p.snap_chunks - 1;
+      store_state(p.snap + ((static_cast<int64_t>(n) * H + h) * p.nsnap + si) * D * D);
+    }
     __syncthreads();
   };
 
@@ -1090,16 +1109,7 @@ __device__ __forceinline__ void scan_body(const ScanParams& p, char* smem, const
   }
   if (c_end > c_begin) store_out(c_end - 1);
 
-  if (s_out) {
-    float* sT = s_out + (static_cast<int64_t>(n) * H + h) * D * D;
-#pragma unroll
-    for (int ri = 0; ri < RT; ++ri)
-#pragma unroll
-      for (int jt = 0; jt < NJT; ++jt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sT[(16 * (wave * RT + ri) + 4 * g4 + i) * D + j0 + 16 * jt + l16] = S[ri][jt][i];
-  }
+  if (s_out) store_state(s_out + (static_cast<int64_t>(n) * H + h) * D * D);
 }
 
 template <int D, int DVS, typename TIn>
@@ -1153,7 +1163,8 @@ int scan_grid(int streams) { return ((streams + 7) / 8) * 8 * (D / DVS); }
 
 template <int D, int DVS, typename TIn>
 hipError_t launch_scan(const PrefillArgs& a, const SeqArgs& sa, const char* ws) {
-  const ScanParams sp{a.v, a.initial_state, a.out, a.final_state, nullptr, ws, sa, 0, 1 << 30, 0};
+  const ScanParams sp{a.v, a.initial_state, a.out, a.final_state, nullptr, ws, sa, 0, 1 << 30, 0,
+                      a.snapshots, std::max(a.snap_chunks, 1), a.nsnap};
   hipLaunchKernelGGL((state_scan_kernel<D, DVS, TIn>), dim3(scan_grid<D, DVS>(a.N * a.H)),
                      dim3(kThreads), 0, a.stream, sp);
   return hipGetLastError();
@@ -1194,7 +1205,8 @@ hipError_t launch_grouped(const PrefillArgs& a, int cg) {
     GroupParams gp{};
     gp.nscan = k >= 1 ? nscan : 0;
     gp.sp = ScanParams{a.v, a.initial_state, a.out, a.final_state, sbuf,
-                       ws + ((k + 1) % nbuf) * wbytes, sa, (k - 1) * cg, k * cg, cg};
+                       ws + ((k + 1) % nbuf) * wbytes, sa, (k - 1) * cg, k * cg, cg,
+                       a.snapshots, std::max(a.snap_chunks, 1), a.nsnap};
     gp.pp = PrepParams{a.q, a.k, a.g, a.beta, ws + (k % nbuf) * wbytes, sa, a.scale,
                        k < windows ? items : 0, k * cg, cg};
     const int grid = gp.nscan + gp.pp.items;

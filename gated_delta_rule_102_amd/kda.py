@@ -21,7 +21,7 @@ KDA_BF16, KDA_F32 = 0, 1
 _lib = None
 
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd",
-           "kda_chunk_fwd_varlen", "kda_decode_step")
+           "kda_chunk_fwd_snapshots", "kda_chunk_fwd_varlen", "kda_decode_step")
 
 
 class KDAError(RuntimeError):
@@ -48,6 +48,9 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                   f32, i32, vp]
     lib.kda_chunk_fwd.restype = i32
+    lib.kda_chunk_fwd_snapshots.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                            i32, i32, i32, f32, i32, vp]
+    lib.kda_chunk_fwd_snapshots.restype = i32
     lib.kda_chunk_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                          i32, i32, f32, i32, vp]
     lib.kda_chunk_fwd_varlen.restype = i32
@@ -138,6 +141,41 @@ def kda_chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final
     return out, final_state
 
 
+def kda_chunk_fwd_snapshots(q, k, v, g, beta, scale=None, initial_state=None,
+                            snapshot_tokens=512, output_final_state=True, out=None,
+                            final_state=None, snapshots=None):
+    """kda_chunk_fwd that also returns the state after every ``snapshot_tokens``
+    tokens (a multiple of 64) and at the end.  Returns ``(out, final_state,
+    snapshots [B,H,ceil(T/snapshot_tokens),dk,dv] fp32)``."""
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dtype, device = q.dtype, q.device
+    _check(dict(q=q, k=k, v=v, g=g, beta=beta), dtype, device)
+    if k.shape != q.shape or g.shape != q.shape or v.shape[:3] != q.shape[:3] \
+            or beta.shape != q.shape[:3]:
+        raise ValueError("shape mismatch among q, k, v, g, beta")
+    _check_state("initial_state", initial_state, (B, H, dk, dv), device)
+    snapshot_tokens = int(snapshot_tokens)
+    nsnap = -(-T // snapshot_tokens) if snapshot_tokens > 0 else 0
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=dtype, device=device)
+    _check(dict(out=out), dtype, device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=device)
+    _check_state("final_state", final_state, (B, H, dk, dv), device)
+    if snapshots is None and nsnap > 0:
+        snapshots = torch.empty((B, H, nsnap, dk, dv), dtype=torch.float32, device=device)
+    _check_state("snapshots", snapshots, (B, H, nsnap, dk, dv), device)
+    scale = 1.0 / math.sqrt(dk) if scale is None else float(scale)
+    rc = lib.kda_chunk_fwd_snapshots(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                     _ptr(initial_state), _ptr(out), _ptr(final_state),
+                                     _ptr(snapshots), snapshot_tokens, B, T, H, dk, dv, scale,
+                                     _dtype_code(q), _stream(q))
+    _raise("kda_chunk_fwd_snapshots", rc)
+    return out, final_state, snapshots
+
+
 def kda_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, scale=None, initial_state=None,
                          output_final_state=True, out=None, final_state=None):
     """Packed variable-length prefill.  q, k, g: [1,total_T,H,dk] (or [total_T,H,dk]);
@@ -195,4 +233,5 @@ def kda_decode_step(q, k, v, g, beta, state, scale=None, out=None):
 # short aliases
 chunk_fwd = kda_chunk_fwd
 chunk_fwd_varlen = kda_chunk_fwd_varlen
+chunk_fwd_snapshots = kda_chunk_fwd_snapshots
 decode_step = kda_decode_step

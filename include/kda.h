@@ -101,6 +101,27 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
                   float scale, int dtype, hipStream_t stream);
 
 /*
+ * kda_chunk_fwd that also keeps the state at regular token boundaries, for
+ * prefix caching: one fixed-size state per request is restored from the nearest
+ * snapshot instead of re-running the prefix (neurohive.io Kimi K3 review,
+ * "Training and inference infrastructure"; best.xiaohu.ai "Kimi K3 tech
+ * report", "Infrastructure efficiency": state checkpoints at sparse boundaries).
+ *
+ *  snapshots        [B, H, ceil(T / snapshot_tokens), dk, dv] fp32, required.
+ *                   Snapshot i is the state after min((i + 1) * snapshot_tokens,
+ *                   T) tokens, i.e. exactly the final state of a run over that
+ *                   prefix; the last one equals final_state.
+ *  snapshot_tokens  > 0 and a multiple of 64 (chunk-aligned), else KDA_ERR_SHAPE.
+ * Every other argument, and the values of out and final_state, are exactly as
+ * for kda_chunk_fwd.
+ */
+int kda_chunk_fwd_snapshots(const void* q, const void* k, const void* v, const void* g,
+                            const void* beta, const float* initial_state, void* out,
+                            float* final_state, float* snapshots, int snapshot_tokens,
+                            int B, int T, int H, int dk, int dv, float scale, int dtype,
+                            hipStream_t stream);
+
+/*
  * Chunked prefill over N packed sequences of different lengths.
  *
  *  cu_seqlens     int32 DEVICE array of N+1 non-decreasing token offsets,

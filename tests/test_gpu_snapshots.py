@@ -1,0 +1,92 @@
+"""GPU tests of prefill state snapshots (kda_chunk_fwd_snapshots, through the C ABI).
+
+Snapshot i must be the state after min((i + 1) * S, T) tokens, i.e. the final
+state the fp64 oracle computes on that prefix, within the same tolerances as any
+final state; the last snapshot is the final state itself, and asking for
+snapshots changes neither the outputs nor the final state.
+"""
+import math
+
+import pytest
+import torch
+
+from gated_delta_rule_102_amd import inputs as kin
+from tests.parity import assert_close, oracle_fixed, oracle_pair_slices
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible MI355X")
+    from gated_delta_rule_102_amd import kda
+    kda.load_library()
+    torch.cuda.set_device(0)
+    yield
+
+
+def _run(d, S):
+    from gated_delta_rule_102_amd import kda
+    g = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    args = (g["q"], g["k"], g["v"], g["g"], g["beta"])
+    out, fs, snaps = kda.kda_chunk_fwd_snapshots(*args, scale=d["scale"],
+                                                 initial_state=g.get("initial_state"),
+                                                 snapshot_tokens=S)
+    out2, fs2 = kda.kda_chunk_fwd(*args, scale=d["scale"], initial_state=g.get("initial_state"))
+    torch.cuda.synchronize()
+    return out, fs, snaps, out2, fs2
+
+
+def _prefix(d, t):
+    return {k: (v[:, :t].contiguous() if isinstance(v, torch.Tensor) and k != "initial_state"
+                else v) for k, v in d.items()}
+
+
+@pytest.mark.parametrize("T,S,D,dtype", [(300, 128, 128, torch.bfloat16),
+                                         (256, 64, 128, torch.bfloat16),
+                                         (200, 512, 128, torch.bfloat16),
+                                         (1100, 256, 64, torch.bfloat16),
+                                         (190, 64, 64, torch.float32)])
+def test_snapshots_match_oracle_on_prefixes(T, S, D, dtype):
+    B, H = 2, 3
+    d = kin.make_prefill(B, T, H, D, D, dtype=dtype, seed=31 + T, nonzero_state=True)
+    d["scale"] = 1.0 / math.sqrt(D)
+    out, fs, snaps, out2, fs2 = _run(d, S)
+    nsnap = -(-T // S)
+    assert tuple(snaps.shape) == (B, H, nsnap, D, D)
+    assert torch.equal(out, out2) and torch.equal(fs, fs2), "snapshots changed the results"
+    assert torch.equal(snaps[:, :, -1], fs), "last snapshot differs from the final state"
+    for i in range(nsnap):
+        t = min((i + 1) * S, T)
+        _, ref_s = oracle_fixed(_prefix(d, t))
+        assert_close(f"snapshot {i} (t={t})", snaps[:, :, i], ref_s.reshape(B, H, D, D), dtype)
+
+
+def test_snapshots_4x4096_full_size_sampled():
+    """512-token snapshots of the 4 x 4096 x 16-head workload, on sampled pairs; the
+    boundaries fall both inside and at the edges of the prefill's chunk windows."""
+    w = kin.WORKLOADS["prefill_4x4096"]
+    d = kin.make_workload(w)
+    d["scale"] = w.scale_value()
+    S = 512
+    out, fs, snaps, out2, fs2 = _run(d, S)
+    assert torch.equal(out, out2) and torch.equal(fs, fs2)
+    pairs = [(0, 0), (1, 7), (3, 15)]
+    for i in (0, 1, 3, 7):
+        t = (i + 1) * S
+        refs = oracle_pair_slices(d, pairs, [(n * w.T, t) for n in range(w.B)])
+        got = torch.stack([snaps[n, h, i] for n, h in pairs])
+        ref = torch.stack([torch.as_tensor(r[1]) for r in refs])
+        assert_close(f"snapshot {i}", got, ref.numpy(), w.dtype)
+
+
+def test_snapshot_interval_must_be_chunk_aligned():
+    from gated_delta_rule_102_amd import kda
+    d = kin.make_prefill(1, 128, 1, 128, 128, dtype=torch.bfloat16, seed=3, device=DEV)
+    with pytest.raises(kda.KDAError) as e:
+        kda.kda_chunk_fwd_snapshots(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                    snapshot_tokens=100)
+    assert e.value.status == -2
