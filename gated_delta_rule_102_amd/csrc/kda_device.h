@@ -81,4 +81,13 @@ __device__ __forceinline__ void buf_st128(i32x4_t v, __amdgpu_buffer_rsrc_t r, u
   __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, 0);
 }
 
+// Stores with the non-temporal hint: for data this kernel does not read again
+// (streamed past the caches, which keeps HBM writes at full rate).
+__device__ __forceinline__ void buf_st64_nt(i32x2_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, soff, 2);
+}
+__device__ __forceinline__ void buf_st128_nt(i32x4_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, 2);
+}
+
 }  // namespace kda

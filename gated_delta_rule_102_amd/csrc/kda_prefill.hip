@@ -983,7 +983,9 @@ __device__ __forceinline__ void scan_body(const ScanParams& p, char* smem, const
     for (int pc = tid; pc < kC * PPR; pc += kThreads) {
       const int t = pc / PPR, part = pc % PPR;
       const i32x4_t val = *reinterpret_cast<const i32x4_t*>(ost + t * CF::RBO + part * 16);
-      buf_st128(val, ro, t * rs_v + part * 16, 0);   // rows past the sequence end are dropped
+      // outputs are not read again here: non-temporal stores; rows past the
+      // sequence end are dropped by the range check
+      buf_st128_nt(val, ro, t * rs_v + part * 16, 0);
     }
   };
 
