@@ -12,7 +12,9 @@ The decode row (single-token update of 256 x 32 fp32 states, d=128, 64
 consecutive kda_decode_step calls) is timed in the same run and reported in the
 "decode" object.  Kernel durations come from HIP events recorded on the stream
 the library launches on; "roofline" relates the prefill kernel's algorithmic
-HBM bytes to its average duration.  "cpu_baseline" times the fp64 CPU oracle on
+HBM bytes to its average duration.  The "prologue" object times the same prefill
+from raw activations through kda_chunk_fwd_prologue (gate and normalisation
+fused into the kernels' loads).  "cpu_baseline" times the fp64 CPU oracle on
 a bounded sample of the same workload.  One JSON line is printed.
 """
 from __future__ import annotations
@@ -105,6 +107,7 @@ def main():
     ap.add_argument("--decode-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-prologue", action="store_true")
     ap.add_argument("--pmc-copy", action="store_true",
                     help="only run a plain 256 MiB copy (counter calibration)")
     args = ap.parse_args()
@@ -199,6 +202,38 @@ def main():
     }
     del sets, outs, finals
     torch.cuda.empty_cache()
+
+    if not args.no_prologue:
+        # the same prefill from raw activations, with the gate/normalisation prologue
+        # fused into the kernels' loads (kda_chunk_fwd_prologue): same bytes moved
+        raw = [kin.make_prefill_raw(B, T, H, d, d, dtype=w.dtype, seed=w.seed + 10 + i,
+                                    device=dev, nonzero_state=True) for i in range(2)]
+        pout = torch.empty((B, T, H, d), dtype=w.dtype, device=dev)
+        pfin = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+
+        def pstep(i):
+            r = raw[i % 2]
+            kda.kda_chunk_fwd_prologue(r["q_raw"], r["k_raw"], r["v"], r["g_raw"], r["beta_raw"],
+                                       scale, r["initial_state"], out=pout, final_state=pfin)
+
+        for i in range(args.warmup):
+            pstep(i)
+        torch.cuda.synchronize()
+        pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for i in range(args.steps):
+            pev[i][0].record(stream)
+            pstep(i)
+            pev[i][1].record(stream)
+        torch.cuda.synchronize()
+        p_s = sum(a.elapsed_time(b) for a, b in pev) / len(pev) / 1e3
+        result["prologue"] = {
+            "entry_point": "kda_chunk_fwd_prologue", "workload": "prefill_4x4096 (raw activations)",
+            "kernel_ms_avg": p_s * 1e3, "tokens_per_s": B * T / p_s,
+            "achieved_GBps": nbytes / p_s / 1e9, "hbm_frac": nbytes / p_s / 1e9 / HBM_PEAK_GBS,
+        }
+        del raw, pout, pfin
+        torch.cuda.empty_cache()
 
     if not args.no_decode:
         wd = kin.WORKLOADS["decode_256x32"]

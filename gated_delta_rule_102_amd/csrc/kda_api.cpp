@@ -107,6 +107,26 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
   return kda::launch_prefill(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+int kda_chunk_fwd_prologue(const void* q_raw, const void* k_raw, const void* v,
+                           const void* g_raw, const void* beta_raw, const float* initial_state,
+                           void* out, float* final_state, int B, int T, int H, int dk, int dv,
+                           float scale, int dtype, hipStream_t stream) {
+  int rc = check_common(dk, dv, H, dtype);
+  if (rc != KDA_OK) return rc;
+  if (dtype == KDA_F32 && dk != 64) return KDA_ERR_HEAD_DIM;
+  if (B <= 0 || T <= 0) return KDA_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * T > INT32_MAX / 2) return KDA_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * H > (1 << 24)) return KDA_ERR_SHAPE;
+  rc = check_prefill_ptrs(q_raw, k_raw, v, g_raw, beta_raw, initial_state, out, final_state, dtype);
+  if (rc != KDA_OK) return rc;
+  rc = check_device();
+  if (rc != KDA_OK) return rc;
+  kda::PrefillArgs a{q_raw, k_raw, v, g_raw, beta_raw, initial_state, out, final_state, nullptr,
+                     B, T, B * T, H, dk, scale, dtype == KDA_F32, stream};
+  a.prologue = true;
+  return kda::launch_prefill(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 int kda_chunk_fwd_snapshots(const void* q, const void* k, const void* v, const void* g,
                             const void* beta, const float* initial_state, void* out,
                             float* final_state, float* snapshots, int snapshot_tokens, int B,

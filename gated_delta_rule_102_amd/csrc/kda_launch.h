@@ -33,6 +33,7 @@ struct PrefillArgs {
   float* snapshots = nullptr;  // fixed length only: [N, H, nsnap, d, d] or null
   int snap_chunks = 0;         // snapshot every snap_chunks chunks (and at the end)
   int nsnap = 0;
+  bool prologue = false;       // q, k, g, beta raw: normalise / gate in the kernel
 };
 
 hipError_t launch_decode(const DecodeArgs& a);

@@ -43,6 +43,10 @@ namespace kda {
 namespace {
 
 constexpr int kC = 64;
+// Prologue constants: the retention factor's lower bound e^-5 (log-decay >= -5) and
+// the epsilon inside the L2 norm of q and k.
+constexpr float kMinRetention = 0.006737946999085467f;
+constexpr float kNormEps = 1e-6f;
 constexpr int kThreads = 256;
 
 // ---------------------------------------------------------------- helpers
@@ -276,6 +280,7 @@ struct PrepParams {
   float scale;
   int items;       // work items of the launch
   int c_lo, cg;    // cg > 0: items cover chunks [c_lo, c_lo + cg) of every sequence
+  int prologue;    // 1: q, k, g, beta are raw (see kda_chunk_fwd_prologue)
 };
 
 // Raw input words of one token row for the CPL channels a lane owns.
@@ -401,6 +406,35 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (p.prologue) {
+      // unit L2 norm of q and k per (token, head): two threads per row sum squares
+      // over half the channels, straight from the raw tiles (the FIJ region is
+      // free until the decay phase)
+      float* nrm = reinterpret_cast<float*>(smem + CF::FIJ);   // [k, q][64]
+      const int x = 1 + (tid >> 7), row = (tid & 127) >> 1, half = tid & 1;
+      const char* src = smem + CF::RAW + x * kC * RBI + row * RBI + half * (RBI / 2);
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < RBI / 2; i += 16) {
+        const i32x4_t w4 = *reinterpret_cast<const i32x4_t*>(src + i);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (F32) {
+            const float f = __int_as_float(w4[j]);
+            ss += f * f;
+          } else {
+            // the element goes through a scalar first: a bit cast applied directly
+            // to a vector-element expression compiled to a read of element 0
+            const int wj = w4[j];
+            const bf16x2_t b2 = __builtin_bit_cast(bf16x2_t, wj);
+            ss = __builtin_amdgcn_fdot2_f32_bf16(b2, b2, ss, false);
+          }
+        }
+      }
+      ss += __shfl_xor(ss, 1);
+      if (half == 0) nrm[(x - 1) * kC + row] = __builtin_amdgcn_rsqf(ss + kNormEps);
+      __syncthreads();
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int off = (16 * wave + r) * RBI + lane * CPL * EI;
@@ -412,6 +446,20 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
         rc.g[r] = *reinterpret_cast<const uint32_t*>(smem + CF::RAW + 0 * kC * RBI + off);
         rc.k[r] = *reinterpret_cast<const uint32_t*>(smem + CF::RAW + 1 * kC * RBI + off);
         rc.q[r] = *reinterpret_cast<const uint32_t*>(smem + CF::RAW + 2 * kC * RBI + off);
+      }
+      if (p.prologue) {   // normalised q, k kept in the input precision
+        const float* nrm = reinterpret_cast<const float*>(smem + CF::FIJ);
+        const float fk = nrm[16 * wave + r], fq = nrm[kC + 16 * wave + r];
+        if constexpr (F32) {
+          rc.k[r] = __float_as_uint(__uint_as_float(rc.k[r]) * fk);
+          rc.q[r] = __float_as_uint(__uint_as_float(rc.q[r]) * fq);
+        } else if constexpr (CPL == 1) {
+          rc.k[r] = static_cast<uint16_t>(pack_bf16x2(__uint_as_float(uint32_t(rc.k[r]) << 16) * fk, 0.f));
+          rc.q[r] = static_cast<uint16_t>(pack_bf16x2(__uint_as_float(uint32_t(rc.q[r]) << 16) * fq, 0.f));
+        } else {
+          rc.k[r] = pack_bf16x2(bf16lo(rc.k[r]) * fk, bf16hi(rc.k[r]) * fk);
+          rc.q[r] = pack_bf16x2(bf16lo(rc.q[r]) * fq, bf16hi(rc.q[r]) * fq);
+        }
       }
     }
   };
@@ -447,10 +495,19 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
           if constexpr (F32) gv = __uint_as_float(cur.g[r]);
           else if constexpr (CPL == 1) gv = __uint_as_float(uint32_t(cur.g[r]) << 16);
           else gv = e ? bf16hi(cur.g[r]) : bf16lo(cur.g[r]);
-          ed[r][e] = fast_exp2(gv * kLog2e);
+          // prologue: g = max(-5, -softplus(x)), so e^g = max(e^-5, 1 / (1 + e^x));
+          // rows past the sequence end keep retention 1, as g = 0 does without it
+          ed[r][e] = !p.prologue ? fast_exp2(gv * kLog2e)
+                     : 16 * wave + r < cur_it.nrow
+                         ? fmaxf(kMinRetention, __builtin_amdgcn_rcpf(1.f + fast_exp2(gv * kLog2e)))
+                         : 1.f;
         }
       }
-      if (tid < kC) betas[tid] = __uint_as_float(cur.beta);
+      if (tid < kC) {   // prologue: beta = sigmoid(x)
+        const float bx = __uint_as_float(cur.beta);
+        betas[tid] = !p.prologue ? bx
+                     : tid < cur_it.nrow ? __builtin_amdgcn_rcpf(1.f + fast_exp2(-bx * kLog2e)) : 0.f;
+      }
 #pragma unroll
       for (int e = 0; e < CPL; ++e) {
         float run = 1.f;
@@ -1210,7 +1267,7 @@ hipError_t launch_grouped(const PrefillArgs& a, int cg) {
                        ws + ((k + 1) % nbuf) * wbytes, sa, (k - 1) * cg, k * cg, cg,
                        a.snapshots, std::max(a.snap_chunks, 1), a.nsnap};
     gp.pp = PrepParams{a.q, a.k, a.g, a.beta, ws + (k % nbuf) * wbytes, sa, a.scale,
-                       k < windows ? items : 0, k * cg, cg};
+                       k < windows ? items : 0, k * cg, cg, a.prologue ? 1 : 0};
     const int grid = gp.nscan + gp.pp.items;
     hipLaunchKernelGGL((prefill_group_kernel<D, DVS, TIn>), dim3(grid), dim3(kThreads), 0,
                        a.stream, gp);
@@ -1240,7 +1297,8 @@ hipError_t launch_all(const PrefillArgs& a) {
   hipError_t err = hipMallocAsync(reinterpret_cast<void**>(&ws), ws_bytes, a.stream);
   if (err != hipSuccess) return err;
   const int64_t items = slots * a.H;
-  PrepParams pp{a.q, a.k, a.g, a.beta, ws, sa, a.scale, static_cast<int>(items), 0, 0};
+  PrepParams pp{a.q, a.k, a.g, a.beta, ws, sa, a.scale, static_cast<int>(items), 0, 0,
+                a.prologue ? 1 : 0};
   const unsigned prep_grid = static_cast<unsigned>(items);
   hipLaunchKernelGGL((chunk_prep_kernel<D, TIn>), dim3(prep_grid), dim3(kThreads), 0, a.stream, pp);
   err = hipGetLastError();

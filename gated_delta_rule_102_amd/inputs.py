@@ -132,6 +132,26 @@ def make_prefill(B, T, H, dk, dv, dtype=torch.bfloat16, seed=0, device="cpu",
     return dict(q=q, k=k, v=v, g=g, beta=beta, initial_state=s0)
 
 
+def make_prefill_raw(B, T, H, dk, dv, dtype=torch.bfloat16, seed=0, device="cpu",
+                     nonzero_state=False, spread=2.0):
+    """Raw activations for the fused prologue: q_raw, k_raw, g_raw [B,T,H,dk] and
+    beta_raw [B,T,H] drawn N(0, spread^2) (q, k not normalised, gates not applied),
+    v ~ N(0, 1), optional state ~ 0.1 N(0, 1).  Only random draws: the prologue's
+    arithmetic is not done here."""
+    gen = _gen(device, seed)
+    f32 = torch.float32
+    q = spread * torch.randn((B, T, H, dk), generator=gen, device=device, dtype=f32)
+    k = spread * torch.randn((B, T, H, dk), generator=gen, device=device, dtype=f32)
+    v = torch.randn((B, T, H, dv), generator=gen, device=device, dtype=f32)
+    g = spread * torch.randn((B, T, H, dk), generator=gen, device=device, dtype=f32)
+    b = spread * torch.randn((B, T, H), generator=gen, device=device, dtype=f32)
+    s0 = None
+    if nonzero_state:
+        s0 = 0.1 * torch.randn((B, H, dk, dv), generator=gen, device=device, dtype=f32)
+    return dict(q_raw=q.to(dtype), k_raw=k.to(dtype), v=v.to(dtype), g_raw=g.to(dtype),
+                beta_raw=b.to(dtype), initial_state=s0)
+
+
 def make_varlen(lengths, H, dk, dv, dtype=torch.bfloat16, seed=0, device="cpu",
                 nonzero_state=False, split_decay=False):
     """Packed inputs [1, total_T, H, .] for the given sequence lengths."""

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 KDA_BF16, KDA_F32 = 0, 1
 _lib = None
 
-EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd",
+EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd", "kda_chunk_fwd_prologue",
            "kda_chunk_fwd_snapshots", "kda_chunk_fwd_varlen", "kda_decode_step")
 
 
@@ -48,6 +48,9 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                   f32, i32, vp]
     lib.kda_chunk_fwd.restype = i32
+    lib.kda_chunk_fwd_prologue.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                           i32, f32, i32, vp]
+    lib.kda_chunk_fwd_prologue.restype = i32
     lib.kda_chunk_fwd_snapshots.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                             i32, i32, i32, f32, i32, vp]
     lib.kda_chunk_fwd_snapshots.restype = i32
@@ -138,6 +141,35 @@ def kda_chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final
                            _ptr(out), _ptr(final_state), B, T, H, dk, dv, scale,
                            _dtype_code(q), _stream(q))
     _raise("kda_chunk_fwd", rc)
+    return out, final_state
+
+
+def kda_chunk_fwd_prologue(q_raw, k_raw, v, g_raw, beta_raw, scale=None, initial_state=None,
+                           output_final_state=True, out=None, final_state=None):
+    """kda_chunk_fwd on raw activations: the kernels normalise q and k (unit L2 norm
+    per token and head), form g = max(-5, -softplus(g_raw)) and beta =
+    sigmoid(beta_raw) while loading them.  Shapes as for kda_chunk_fwd."""
+    lib = load_library()
+    B, T, H, dk = q_raw.shape
+    dv = v.shape[-1]
+    dtype, device = q_raw.dtype, q_raw.device
+    _check(dict(q_raw=q_raw, k_raw=k_raw, v=v, g_raw=g_raw, beta_raw=beta_raw), dtype, device)
+    if k_raw.shape != q_raw.shape or g_raw.shape != q_raw.shape or v.shape[:3] != q_raw.shape[:3] \
+            or beta_raw.shape != q_raw.shape[:3]:
+        raise ValueError("shape mismatch among q_raw, k_raw, v, g_raw, beta_raw")
+    _check_state("initial_state", initial_state, (B, H, dk, dv), device)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=dtype, device=device)
+    _check(dict(out=out), dtype, device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=device)
+    _check_state("final_state", final_state, (B, H, dk, dv), device)
+    scale = 1.0 / math.sqrt(dk) if scale is None else float(scale)
+    rc = lib.kda_chunk_fwd_prologue(_ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(g_raw),
+                                    _ptr(beta_raw), _ptr(initial_state), _ptr(out),
+                                    _ptr(final_state), B, T, H, dk, dv, scale,
+                                    _dtype_code(q_raw), _stream(q_raw))
+    _raise("kda_chunk_fwd_prologue", rc)
     return out, final_state
 
 
@@ -234,4 +266,5 @@ def kda_decode_step(q, k, v, g, beta, state, scale=None, out=None):
 chunk_fwd = kda_chunk_fwd
 chunk_fwd_varlen = kda_chunk_fwd_varlen
 chunk_fwd_snapshots = kda_chunk_fwd_snapshots
+chunk_fwd_prologue = kda_chunk_fwd_prologue
 decode_step = kda_decode_step

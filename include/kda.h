@@ -101,6 +101,27 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
                   float scale, int dtype, hipStream_t stream);
 
 /*
+ * kda_chunk_fwd with the gate and normalisation prologue fused into the kernels'
+ * loads, so the activations that produce q, k, g and beta are not written out
+ * and read back.  The pages bound the log of the per-channel retention factor
+ * below at -5 (neurohive.io Kimi K3 review, "Sequence length: hybrid KDA and
+ * Gated MLA attention") but give no gate formula; the plainest reading, used
+ * here, is
+ *     q = q_raw / sqrt(|q_raw|^2 + 1e-6),   k = k_raw / sqrt(|k_raw|^2 + 1e-6)
+ *                                           (per token and head, over dk)
+ *     g = max(-5, -softplus(g_raw)) = max(-5, -log(1 + exp(g_raw)))   (per channel)
+ *     beta = sigmoid(beta_raw) = 1 / (1 + exp(-beta_raw))
+ * followed by exactly the computation of kda_chunk_fwd.  Normalised q and k are
+ * rounded to the input precision before use (as if they had been stored in it);
+ * g and beta are used in fp32.  Arguments, layouts and codes are those of
+ * kda_chunk_fwd, with the raw tensors in place of q, k, g and beta.
+ */
+int kda_chunk_fwd_prologue(const void* q_raw, const void* k_raw, const void* v,
+                           const void* g_raw, const void* beta_raw, const float* initial_state,
+                           void* out, float* final_state, int B, int T, int H, int dk, int dv,
+                           float scale, int dtype, hipStream_t stream);
+
+/*
  * kda_chunk_fwd that also keeps the state at regular token boundaries, for
  * prefix caching: one fixed-size state per request is restored from the nearest
  * snapshot instead of re-running the prefix (neurohive.io Kimi K3 review,

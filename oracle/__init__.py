@@ -13,6 +13,8 @@ Contents
     used only to cross-check the C library on small shapes.
   * :func:`unrolled_np` -- the closed form obtained by unrolling the recurrence
     into products of the per-token transition matrices (brute force, T <= 8).
+  * :func:`prologue_np` -- the gate/normalisation prologue (unit-norm q and k,
+    g = max(-5, -softplus(x)), beta = sigmoid(x)) in fp64, for the fused path.
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 against closed forms, special cases and invariants; see the test docstrings.
@@ -21,6 +23,7 @@ from .ref import (  # noqa: F401
     build,
     load,
     oracle_forward,
+    prologue_np,
     recurrence_np,
     unrolled_np,
     widen_np,

@@ -211,3 +211,22 @@ def unrolled_np(q, k, v, g, beta, scale, initial_state=None):
             if t == T - 1:
                 final[h] = St
     return out, final
+
+
+def prologue_np(q_raw, k_raw, g_raw, beta_raw, eps=1e-6, floor=-5.0):
+    """The gate/normalisation prologue, in fp64, written out from its definitions.
+
+    The pages bound the log of KDA's per-channel retention factor below at -5
+    (neurohive.io Kimi K3 review, "Sequence length: hybrid KDA and Gated MLA
+    attention") but print no gate formula; the reading used is
+        q = q_raw / sqrt(sum_c q_raw^2 + eps),  k likewise (per token and head),
+        g = max(floor, -softplus(g_raw)),  softplus(x) = log(1 + e^x),
+        beta = sigmoid(beta_raw) = 1 / (1 + e^-x).
+    Inputs are widened exactly (bf16 bits or fp32) to fp64; returns fp64 arrays.
+    """
+    q, k, g, b = (widen_np(x) for x in (q_raw, k_raw, g_raw, beta_raw))
+    qn = q / np.sqrt((q * q).sum(-1, keepdims=True) + eps)
+    kn = k / np.sqrt((k * k).sum(-1, keepdims=True) + eps)
+    gg = np.maximum(floor, -np.logaddexp(0.0, g))      # log(1 + e^x) without overflow
+    bb = 0.5 * (1.0 + np.tanh(0.5 * b))                # = 1 / (1 + e^-x), no overflow
+    return qn, kn, gg, bb

@@ -32,8 +32,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
-        "kda_abi_version", "kda_status_string", "kda_chunk_fwd", "kda_chunk_fwd_snapshots",
-        "kda_chunk_fwd_varlen", "kda_decode_step"])
+        "kda_abi_version", "kda_status_string", "kda_chunk_fwd", "kda_chunk_fwd_prologue",
+        "kda_chunk_fwd_snapshots", "kda_chunk_fwd_varlen", "kda_decode_step"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -80,6 +80,13 @@ def test_argument_checks_precede_any_device_call(lib):
     v.restype = i32
     assert v(p, p, p, p, p, None, p, None, None, 2, 64, 1, 128, 128, 0.1, 0, None) == -1
     assert v(p, p, p, p, p, None, p, None, p, 0, 64, 1, 128, 128, 0.1, 0, None) == -2
+    pr = lib.kda_chunk_fwd_prologue
+    pr.argtypes = [vp] * 8 + [i32] * 5 + [f32, i32, vp]
+    pr.restype = i32
+    assert pr(None, p, p, p, p, None, p, None, 1, 64, 1, 128, 128, 0.1, 0, None) == -1
+    assert pr(p, p, p, p, p, None, p, None, 1, 64, 1, 128, 128, 0.1, 1, None) == -3
+    assert pr(mis, p, p, p, p, None, p, None, 1, 64, 1, 128, 128, 0.1, 0, None) == -5
+    assert pr(p, p, p, p, p, None, p, None, 1, 64, 1, 128, 128, 0.1, 0, None) in (-6, -7)
     s = lib.kda_chunk_fwd_snapshots
     s.argtypes = [vp] * 9 + [i32] * 6 + [f32, i32, vp]
     s.restype = i32

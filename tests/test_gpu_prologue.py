@@ -1,0 +1,102 @@
+"""GPU tests of the fused gate/normalisation prologue (kda_chunk_fwd_prologue).
+
+The kernels take raw activations and form unit-norm q and k, g = max(-5,
+-softplus(g_raw)) and beta = sigmoid(beta_raw) while loading them; the oracle
+applies the same definitions in fp64 (oracle.prologue_np) and then runs the
+recurrence.  Outputs and final states must meet the usual tolerances.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_102_amd import inputs as kin
+from oracle import oracle_forward, prologue_np, widen_np
+from tests.parity import assert_close
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible MI355X")
+    from gated_delta_rule_102_amd import kda
+    kda.load_library()
+    torch.cuda.set_device(0)
+    yield
+
+
+def _gpu_run(d, scale):
+    from gated_delta_rule_102_amd import kda
+    g = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    out, fs = kda.kda_chunk_fwd_prologue(g["q_raw"], g["k_raw"], g["v"], g["g_raw"], g["beta_raw"],
+                                         scale=scale, initial_state=g.get("initial_state"))
+    torch.cuda.synchronize()
+    return out, fs
+
+
+def _oracle(d, scale, pairs=None):
+    q, k, g, b = prologue_np(d["q_raw"], d["k_raw"], d["g_raw"], d["beta_raw"])
+    B, T = q.shape[:2]
+    v = widen_np(d["v"])      # exact; the oracle takes one precision for all inputs
+    return oracle_forward(q, k, v, g, b, scale, B=B, T=T, initial_state=d.get("initial_state"),
+                          pairs=pairs)
+
+
+@pytest.mark.parametrize("T,D,dtype", [(1, 128, torch.bfloat16), (77, 128, torch.bfloat16),
+                                       (200, 64, torch.bfloat16), (130, 64, torch.float32)])
+def test_prologue_matches_oracle(T, D, dtype):
+    B, H = 2, 3
+    d = kin.make_prefill_raw(B, T, H, D, D, dtype=dtype, seed=50 + T, nonzero_state=True)
+    scale = 1.0 / math.sqrt(D)
+    out, fs = _gpu_run(d, scale)
+    ref_o, ref_s = _oracle(d, scale)
+    assert_close("prologue out", out, ref_o.reshape(B, T, H, D), dtype)
+    assert_close("prologue state", fs, ref_s.reshape(B, H, D, D), dtype)
+
+
+def test_prologue_gate_extremes():
+    """Raw gates far past both ends: the floor (-5) and full retention (g -> 0)."""
+    B, T, H, D = 1, 150, 2, 128
+    d = kin.make_prefill_raw(B, T, H, D, D, dtype=torch.bfloat16, seed=61, spread=30.0)
+    scale = 1.0 / math.sqrt(D)
+    out, fs = _gpu_run(d, scale)
+    ref_o, ref_s = _oracle(d, scale)
+    assert_close("extreme out", out, ref_o.reshape(B, T, H, D), torch.bfloat16)
+    assert_close("extreme state", fs, ref_s.reshape(B, H, D, D), torch.bfloat16)
+
+
+def test_prologue_equals_unfused_path():
+    """The fused path against kda_chunk_fwd on prologue outputs computed separately
+    (rounded to bf16 once, as a separate pass would store them)."""
+    from gated_delta_rule_102_amd import kda
+    B, T, H, D = 2, 256, 4, 128
+    d = kin.make_prefill_raw(B, T, H, D, D, dtype=torch.bfloat16, seed=62, nonzero_state=True)
+    scale = 1.0 / math.sqrt(D)
+    out_f, fs_f = _gpu_run(d, scale)
+    q, k, g, b = (torch.from_numpy(x).to(torch.bfloat16).to(DEV)
+                  for x in prologue_np(d["q_raw"], d["k_raw"], d["g_raw"], d["beta_raw"]))
+    out_u, fs_u = kda.kda_chunk_fwd(q, k, d["v"].to(DEV), g, b, scale=scale,
+                                    initial_state=d["initial_state"].to(DEV))
+    torch.cuda.synchronize()
+    assert_close("fused vs unfused out", out_f, out_u.float().cpu().numpy(), torch.bfloat16)
+    assert_close("fused vs unfused state", fs_f, fs_u.cpu().numpy(), torch.bfloat16)
+
+
+def test_prologue_4x4096_full_size_sampled():
+    B, T, H, D = 4, 4096, 16, 128
+    d = kin.make_prefill_raw(B, T, H, D, D, dtype=torch.bfloat16, seed=1001, nonzero_state=True,
+                             spread=1.0)
+    scale = 1.0 / math.sqrt(D)
+    out, fs = _gpu_run(d, scale)
+    pairs = [(0, 0), (2, 9), (3, 15)]
+    ref_o, ref_s = _oracle(d, scale, pairs=pairs)
+    got_o = torch.stack([out[n, :, h] for n, h in pairs])
+    got_s = torch.stack([fs[n, h] for n, h in pairs])
+    ref_sel = np.stack([ref_o[n * T:(n + 1) * T, h] for n, h in pairs])   # [B*T, H, dv] layout
+    assert_close("4x4096 out (sampled)", got_o, ref_sel, torch.bfloat16)
+    assert_close("4x4096 state (sampled)", got_s, ref_s, torch.bfloat16)

@@ -411,3 +411,39 @@ def test_pins_catch_planted_mistakes(kind):
     out, _ = fwd(k, k, v, g, np.ones((10, 1)), 1.0, rng.standard_normal((1, 4, 4)))
     failures += not np.allclose(out, v, atol=1e-9)
     assert failures >= 1
+
+
+# ---------------------------------------------------------------- prologue
+
+
+def test_prologue_against_library_routines():
+    """q, k: same direction as the input with unit norm (torch's normalize, where the
+    norm dwarfs the epsilon); g: torch's softplus with the -5 clamp; beta: sigmoid."""
+    import torch
+    from oracle import prologue_np
+    rng = np.random.default_rng(40)
+    q, k, g, b = (rng.standard_normal(s) * 2.0 for s in ((7, 3, 16), (7, 3, 16), (7, 3, 16), (7, 3)))
+    qn, kn, gg, bb = prologue_np(q, k, g, b)
+    tq = torch.nn.functional.normalize(torch.tensor(q), dim=-1).numpy()
+    tk = torch.nn.functional.normalize(torch.tensor(k), dim=-1).numpy()
+    np.testing.assert_allclose(qn, tq, rtol=1e-6, atol=0)
+    np.testing.assert_allclose(kn, tk, rtol=1e-6, atol=0)
+    np.testing.assert_allclose(np.linalg.norm(qn, axis=-1), 1.0, rtol=1e-6)
+    tg = torch.clamp(-torch.nn.functional.softplus(torch.tensor(g)), min=-5.0).numpy()
+    np.testing.assert_allclose(gg, tg, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(bb, torch.sigmoid(torch.tensor(b)).numpy(), rtol=1e-14, atol=0)
+
+
+def test_prologue_special_values():
+    from oracle import prologue_np
+    x = np.array([0.0, 100.0, -100.0, np.log(np.expm1(5.0)), 3.0])
+    _, _, g, b = prologue_np(np.ones((1, 2)), np.ones((1, 2)), x, x)
+    assert g[0] == pytest.approx(-np.log(2.0), abs=1e-15)     # softplus(0) = ln 2
+    assert g[1] == -5.0                                         # clamped at the floor
+    assert -1e-40 < g[2] <= 0.0                                 # retention -> 1
+    assert g[3] == pytest.approx(-5.0, abs=1e-12)               # exactly at the floor
+    assert b[0] == 0.5 and b[1] == 1.0 and b[2] < 1e-40
+    assert b[4] == pytest.approx(1.0 - b[4] * np.exp(-3.0), abs=1e-15)   # beta = 1/(1+e^-x)
+    # a zero vector stays zero instead of dividing by zero
+    qn, _, _, _ = prologue_np(np.zeros((1, 4)), np.ones((1, 4)), x[:1], x[:1])
+    assert np.all(qn == 0.0)
