@@ -362,6 +362,10 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
   auto at_el = [&](int row, int col) -> float& {
     return *reinterpret_cast<float*>(atc + swz<256>(row, col * 4));
   };
+  // elements col0 .. col0+3 of a row (col0 a multiple of 4: one 16-byte chunk)
+  auto at_row4 = [&](int row, int col0) -> float4 {
+    return *reinterpret_cast<const float4*>(atc + swz<256>(row, col0 * 4));
+  };
 
   // the strictly-upper sub-tiles of A/T and of M are read as zeros; nothing else
   // writes them, so clearing them once serves every item of this workgroup
@@ -616,10 +620,18 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
         const int t = 16 * I + l16, s0 = 16 * J + 4 * g4;
         const float bt = betas[t];
         float av[4], mv[4];
+        if (I == J) {   // diagonal sub-tile: A strictly lower, M lower
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          av[i] = (s0 + i < t) ? bt * aA[i] : 0.f;
-          mv[i] = (s0 + i <= t) ? aM[i] : 0.f;
+          for (int i = 0; i < 4; ++i) {
+            av[i] = (s0 + i < t) ? bt * aA[i] : 0.f;
+            mv[i] = (s0 + i <= t) ? aM[i] : 0.f;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            av[i] = bt * aA[i];
+            mv[i] = aM[i];
+          }
         }
         *reinterpret_cast<float4*>(atc + swz<256>(t, s0 * 4)) = float4{av[0], av[1], av[2], av[3]};
         lds_put4<F32>(smem + CF::MB + swz<CF::RBC>(t, s0 * E), mv[0], mv[1], mv[2], mv[3]);
@@ -683,13 +695,15 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
     if (wave < 2) {   // T_10 = -T_11 A_10 T_00 and T_32 = -T_33 A_32 T_22
       const int I = wave ? 3 : 1, J = I - 1;
       f32x4_t y = {0.f, 0.f, 0.f, 0.f}, tt = y;
+      const float4 aIJ = at_row4(16 * I + l16, 16 * J + 4 * g4);
+      const float4 aII = at_row4(16 * I + l16, 16 * I + 4 * g4);
+      const float aij[4] = {aIJ.x, aIJ.y, aIJ.z, aIJ.w}, aii[4] = {aII.x, aII.y, aII.z, aII.w};
 #pragma unroll
       for (int st = 0; st < 4; ++st)
-        y = __builtin_amdgcn_mfma_f32_16x16x4f32(at_el(16 * I + l16, 16 * J + 4 * g4 + st),
-                                                 at_el(16 * J + 4 * g4 + st, 16 * J + l16), y, 0, 0, 0);
+        y = __builtin_amdgcn_mfma_f32_16x16x4f32(aij[st], at_el(16 * J + 4 * g4 + st, 16 * J + l16), y, 0, 0, 0);
 #pragma unroll
       for (int st = 0; st < 4; ++st)
-        tt = __builtin_amdgcn_mfma_f32_16x16x4f32(at_el(16 * I + l16, 16 * I + 4 * g4 + st), y[st], tt, 0, 0, 0);
+        tt = __builtin_amdgcn_mfma_f32_16x16x4f32(aii[st], y[st], tt, 0, 0, 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) at_el(16 * I + 4 * g4 + i, 16 * J + l16) = -tt[i];
     }
@@ -701,10 +715,11 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         if (m >= bj) {
+          const float4 a4 = at_row4(16 * bi + l16, 16 * m + 4 * g4);
+          const float a[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
           for (int st = 0; st < 4; ++st)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(at_el(16 * bi + l16, 16 * m + 4 * g4 + st),
-                                                       at_el(16 * m + 4 * g4 + st, 16 * bj + l16), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], at_el(16 * m + 4 * g4 + st, 16 * bj + l16), acc, 0, 0, 0);
         }
       }
 #pragma unroll
@@ -717,16 +732,43 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
       for (int m = 2; m < 4; ++m) {
         if (m <= bi) {
           const int xw = (m - 2) * 2 + bj;
+          const float4 a4 = at_row4(16 * bi + l16, 16 * m + 4 * g4);
+          const float a[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
           for (int st = 0; st < 4; ++st)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(at_el(16 * bi + l16, 16 * m + 4 * g4 + st),
-                                                       xs[(xw * 16 + 4 * g4 + st) * CF::XLD + l16], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], xs[(xw * 16 + 4 * g4 + st) * CF::XLD + l16],
+                                                       acc, 0, 0, 0);
         }
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) at_el(16 * bi + 4 * g4 + i, 16 * bj + l16) = -acc[i];
     }
     __syncthreads();
+    // bf16 operands: Tb = T Diag(beta) row-major (TBR) and transposed (TBT), in place
+    // of the fp32 T, so the later products read whole 16-byte fragments
+    char* tbr = atc;
+    char* tbt = atc + kC * CF::RBC;
+    if constexpr (!F32) {
+      const int t = tid >> 2, s0 = (tid & 3) * 16;
+      float x[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 u = at_row4(t, s0 + 4 * q4);
+        const float4 b = *reinterpret_cast<const float4*>(betas + s0 + 4 * q4);
+        x[4 * q4] = u.x * b.x; x[4 * q4 + 1] = u.y * b.y; x[4 * q4 + 2] = u.z * b.z; x[4 * q4 + 3] = u.w * b.w;
+      }
+      __syncthreads();   // all of T is read before its space is reused
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        const int o = 8 * h8;
+        *reinterpret_cast<i32x4_t*>(tbr + swz<CF::RBC>(t, (s0 + o) * 2)) = i32x4_t{
+            static_cast<int>(pack_bf16x2(x[o], x[o + 1])), static_cast<int>(pack_bf16x2(x[o + 2], x[o + 3])),
+            static_cast<int>(pack_bf16x2(x[o + 4], x[o + 5])), static_cast<int>(pack_bf16x2(x[o + 6], x[o + 7]))};
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) lds_set1<false>(tbt + swz<CF::RBC>(s0 + e, t * 2), x[e]);
+      __syncthreads();
+    }
 
     // ------------------------------------------------ P = scale M Tb, stored as P[t][t']
     // computed transposed: P^T[t'][t] = sum_s Tb[s][t'] M[t][s], nonzero for t' <= t
@@ -737,14 +779,19 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
         int C, R;
         pair_of(pr, C, R);
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        const float bcol = betas[16 * R + l16];     // Tb[s][t'] = T[s][t'] beta_t'
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           const int sb = kk * 32 + g4 * 8;
-          float x[8];
+          Frag<F32> a;
+          if constexpr (F32) {
+            const float bcol = betas[16 * R + l16];     // Tb[s][t'] = T[s][t'] beta_t'
+            float x[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = at_el(sb + e, 16 * R + l16) * bcol;
-          const Frag<F32> a = frag_from_f32<F32>(x);
+            for (int e = 0; e < 8; ++e) x[e] = at_el(sb + e, 16 * R + l16) * bcol;
+            a = frag_from_f32<F32>(x);
+          } else {
+            a = lds_frag<F32, CF::RBC>(tbt, 16 * R + l16, sb * E);
+          }
           const Frag<F32> bm = lds_frag<F32, CF::RBC>(smem + CF::MB, 16 * C + l16, sb * E);
           acc = mma32<F32>(acc, a, bm);
         }
@@ -783,16 +830,19 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
         for (int kk = 0; kk < 2; ++kk) {
           if (kk == 1 && ct < 2) continue;     // Tb[t][s] = P[t][s] = 0 for s > t
           const int sb = kk * 32 + g4 * 8;
-          float x[8];
-          {
+          Frag<F32> bw;
+          if constexpr (F32) {
+            float x[8];
             const float4 u0 = *reinterpret_cast<const float4*>(atc + swz<256>(t, sb * 4));
             const float4 u1 = *reinterpret_cast<const float4*>(atc + swz<256>(t, sb * 4 + 16));
             const float4 b0 = *reinterpret_cast<const float4*>(betas + sb);
             const float4 b1 = *reinterpret_cast<const float4*>(betas + sb + 4);
             x[0] = u0.x * b0.x; x[1] = u0.y * b0.y; x[2] = u0.z * b0.z; x[3] = u0.w * b0.w;
             x[4] = u1.x * b1.x; x[5] = u1.y * b1.y; x[6] = u1.z * b1.z; x[7] = u1.w * b1.w;
+            bw = frag_from_f32<F32>(x);
+          } else {
+            bw = lds_frag<F32, CF::RBC>(tbr, t, sb * E);
           }
-          const Frag<F32> bw = frag_from_f32<F32>(x);
           const Frag<F32> bq = lds_frag<F32, CF::RBC>(smem + CF::PB, t, sb * E);
 #pragma unroll
           for (int rr = 0; rr < RPW; ++rr) {
@@ -821,7 +871,15 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
       }
     }
     // Tb = T Diag(beta) -> workspace, 16 consecutive entries per thread
-    {
+    if constexpr (!F32) {
+      const int t = tid >> 2, s0 = (tid & 3) * 16;
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        const i32x4_t w = *reinterpret_cast<const i32x4_t*>(tbr + swz<CF::RBC>(t, (s0 + 8 * h8) * 2));
+        buf_st64(i32x2_t{w[0], w[1]}, rw, SL::TB + frag_off<kC, F32>(t, s0 + 8 * h8), 0);
+        buf_st64(i32x2_t{w[2], w[3]}, rw, SL::TB + frag_off<kC, F32>(t, s0 + 8 * h8 + 4), 0);
+      }
+    } else {
       const int t = tid >> 2, s0 = (tid & 3) * 16;
       float x[16];
 #pragma unroll
