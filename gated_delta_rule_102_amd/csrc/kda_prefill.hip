@@ -592,11 +592,15 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
     __syncthreads();
 
     // ------------------------------------------------ phase AM: A and M
-    // computed transposed (rows s) so each lane stores 4 consecutive s of row t
+    // computed transposed (rows s) so each lane stores 4 consecutive s of row t.
+    // Off-diagonal pairs cost about twice a diagonal one (their column operand is
+    // rescaled), so each wavefront takes two off-diagonal pairs or one off-diagonal
+    // and two diagonal ones: pair numbers from pair_of, -1 = none.
+    constexpr int kPairs[4][3] = {{1, 3, -1}, {4, 6, -1}, {7, 0, 2}, {8, 5, 9}};
 #pragma unroll
     for (int pp = 0; pp < 3; ++pp) {
-      const int pr = wave + 4 * pp;
-      if (pr < 10) {
+      const int pr = kPairs[wave][pp];
+      if (pr >= 0) {
         int I, J;
         pair_of(pr, I, J);
         f32x4_t aA = {0.f, 0.f, 0.f, 0.f}, aM = {0.f, 0.f, 0.f, 0.f};
@@ -667,24 +671,55 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
           lds_put4<F32>(smem + CF::KBT + swz<CF::RBC>(lane * CPL + e, (16 * wave + 4 * q4) * E),
                         kb[e][4 * q4], kb[e][4 * q4 + 1], kb[e][4 * q4 + 2], kb[e][4 * q4 + 3]);
     }
-    if (lane < 16) {   // T_ww = (I + A_ww)^{-1}, lane j computes column j
+    {   // T_ww = (I + A_ww)^{-1} = (I - A)(I + A^2)(I + A^4)(I + A^8): A_ww is strictly
+        // lower, so A^16 = 0.  Six 16x16 products on fp32 matrix cores per wavefront.
+        // A 16x16x4 product reads its A operand in row layout (lane: row l16, columns
+        // 4*g4 .. +3) and its B operand in the accumulator layout (lane: rows 4*g4 ..
+        // +3 of column l16), so a result feeds the next product's B side directly and
+        // its A side after a transpose through this wavefront's 16x17 scratch.
       const int base = 16 * wave;
-      float x[16];
+      float* sc = reinterpret_cast<float*>(smem + CF::XS) + wave * 16 * CF::XLD;
+      auto mm = [&](const float (&xr)[4], const float (&yc)[4]) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float arow[16];
+        for (int st = 0; st < 4; ++st) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xr[st], yc[st], acc, 0, 0, 0);
+        return acc;
+      };
+      auto to_row = [&](const f32x4_t& c, float (&r)[4]) {
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const float4 v = *reinterpret_cast<const float4*>(atc + swz<256>(base + i, (base + 4 * q4) * 4));
-          arow[4 * q4] = v.x; arow[4 * q4 + 1] = v.y; arow[4 * q4 + 2] = v.z; arow[4 * q4 + 3] = v.w;
-        }
-        float sacc = 0.f;
+        for (int i = 0; i < 4; ++i) sc[(4 * g4 + i) * CF::XLD + l16] = c[i];
 #pragma unroll
-        for (int m = 0; m < i; ++m) sacc += arow[m] * x[m];
-        x[i] = (i == lane) ? 1.f : -sacc;
-      }
+        for (int i = 0; i < 4; ++i) r[i] = sc[l16 * CF::XLD + 4 * g4 + i];
+      };
+      const float4 ar4 = at_row4(base + l16, base + 4 * g4);
+      const float a_r[4] = {ar4.x, ar4.y, ar4.z, ar4.w};
+      float a_c[4];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) at_el(base + i, base + lane) = x[i];
+      for (int i = 0; i < 4; ++i) a_c[i] = at_el(base + 4 * g4 + i, base + l16);
+      const f32x4_t p1 = mm(a_r, a_c);                         // A^2
+      const float p1_c[4] = {p1[0], p1[1], p1[2], p1[3]};
+      float p1_r[4];
+      to_row(p1, p1_r);
+      const f32x4_t p2 = mm(p1_r, p1_c);                       // A^4
+      const f32x4_t a3 = mm(a_r, p1_c);                        // A^3
+      const float p2_c[4] = {p2[0], p2[1], p2[2], p2[3]};
+      float p2_r[4];
+      to_row(p2, p2_r);
+      const f32x4_t p3 = mm(p2_r, p2_c);                       // A^8
+      const float p3_c[4] = {p3[0], p3[1], p3[2], p3[3]};
+      f32x4_t t1;                                              // I - A + A^2 - A^3
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t1[i] = (4 * g4 + i == l16 ? 1.f : 0.f) - a_c[i] + p1[i] - a3[i];
+      float t1_r[4];
+      to_row(t1, t1_r);
+      f32x4_t t2 = mm(t1_r, p2_c);                             // T1 (I + A^4)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t2[i] += t1[i];
+      float t2_r[4];
+      to_row(t2, t2_r);
+      f32x4_t t3 = mm(t2_r, p3_c);                             // T2 (I + A^8)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) at_el(base + 4 * g4 + i, base + l16) = t3[i] + t2[i];
     }
     __syncthreads();
 
