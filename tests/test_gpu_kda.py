@@ -334,3 +334,12 @@ def test_abi_error_codes_launch_nothing():
     torch.cuda.synchronize()
     assert torch.all(o == 7.0), "a rejected call wrote its output"
     assert kda.kda_status_string(-3).startswith("dk and dv")
+
+
+def test_prefill_several_windows_small():
+    """Fixed-length prefill longer than one 16-chunk window (T = 2100: three
+    windows, the last one ragged) with a nonzero state, element by element against
+    the oracle: exercises the state carried between windows."""
+    d = kin.make_prefill(2, 2100, 2, 128, 128, dtype=torch.bfloat16, seed=77, nonzero_state=True)
+    d["scale"] = 1.0 / math.sqrt(128)
+    _compare_fixed(d, "3 windows")

@@ -90,3 +90,17 @@ def test_snapshot_interval_must_be_chunk_aligned():
         kda.kda_chunk_fwd_snapshots(d["q"], d["k"], d["v"], d["g"], d["beta"],
                                     snapshot_tokens=100)
     assert e.value.status == -2
+
+
+def test_snapshots_across_windows():
+    """T = 2100 spans three 16-chunk windows; snapshots every 512 tokens fall inside
+    and at the edges of windows (the first window ends at token 1024)."""
+    B, T, H, D, S = 1, 2100, 2, 128, 512
+    d = kin.make_prefill(B, T, H, D, D, dtype=torch.bfloat16, seed=78, nonzero_state=True)
+    d["scale"] = 1.0 / math.sqrt(D)
+    out, fs, snaps, out2, fs2 = _run(d, S)
+    assert torch.equal(out, out2) and torch.equal(fs, fs2)
+    for i in range(-(-T // S)):
+        t = min((i + 1) * S, T)
+        _, ref_s = oracle_fixed(_prefix(d, t))
+        assert_close(f"snapshot {i} (t={t})", snaps[:, :, i], ref_s.reshape(B, H, D, D), torch.bfloat16)
