@@ -15,6 +15,8 @@ Contents
     into products of the per-token transition matrices (brute force, T <= 8).
   * :func:`prologue_np` -- the gate/normalisation prologue (unit-norm q and k,
     g = max(-5, -softplus(x)), beta = sigmoid(x)) in fp64, for the fused path.
+  * :func:`backward_oracle` -- gradients of the recurrence (dq, dk, dv, dg,
+    dbeta, dS_0) by fp64 reverse-mode autodiff on the CPU (``grad.py``).
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 against closed forms, special cases and invariants; see the test docstrings.
@@ -28,3 +30,4 @@ from .ref import (  # noqa: F401
     unrolled_np,
     widen_np,
 )
+from .grad import backward_oracle  # noqa: F401

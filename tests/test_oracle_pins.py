@@ -447,3 +447,113 @@ def test_prologue_special_values():
     # a zero vector stays zero instead of dividing by zero
     qn, _, _, _ = prologue_np(np.zeros((1, 4)), np.ones((1, 4)), x[:1], x[:1])
     assert np.all(qn == 0.0)
+
+
+# ---------------------------------------------------------------- backward
+
+
+def _loss_fd_setup(seed, T=7, H=2, dk=3, dv=2):
+    rng = np.random.default_rng(seed)
+    q, k, v, g, beta = _rand_inputs(T, H, dk, dv, rng, beta_lo=0.05, beta_hi=0.95)
+    s0 = rng.standard_normal((H, dk, dv)) * 0.3
+    d_out = rng.standard_normal((T, H, dv))
+    d_fin = rng.standard_normal((H, dk, dv))
+    return dict(q=q, k=k, v=v, g=g, beta=beta, s0=s0), d_out, d_fin
+
+
+def _loss(x, d_out, d_fin, scale):
+    out, sT = run(x["q"], x["k"], x["v"], x["g"], x["beta"], scale, x["s0"])
+    return float((out * d_out).sum() + (sT.reshape(d_fin.shape) * d_fin).sum())
+
+
+@pytest.mark.parametrize("seed", [50, 51])
+def test_backward_matches_finite_differences(seed):
+    """Every gradient of the autodiff oracle equals the central finite difference of
+    the C oracle's forward loss (a separate implementation of the recurrence),
+    element by element: error O(h^2) + rounding, well under 1e-7 relative."""
+    from oracle import backward_oracle
+    x, d_out, d_fin = _loss_fd_setup(seed)
+    scale = 0.7
+    gr = backward_oracle(x["q"][None], x["k"][None], x["v"][None], x["g"][None],
+                         x["beta"][None], scale, d_out[None], x["s0"][None], d_fin[None])
+    names = dict(q="dq", k="dk", v="dv", g="dg", beta="dbeta", s0="ds0")
+    h = 1e-5
+    for name, key in names.items():
+        got = gr[key][0]
+        fd = np.zeros_like(x[name])
+        for idx in np.ndindex(*x[name].shape):
+            xp = {kk: vv.copy() for kk, vv in x.items()}
+            xm = {kk: vv.copy() for kk, vv in x.items()}
+            xp[name][idx] += h
+            xm[name][idx] -= h
+            fd[idx] = (_loss(xp, d_out, d_fin, scale) - _loss(xm, d_out, d_fin, scale)) / (2 * h)
+        err = np.max(np.abs(got - fd)) / max(1.0, np.max(np.abs(fd)))
+        assert err < 1e-7, f"d{name}: {err:.3e}"
+
+
+def test_backward_beta_zero_closed_form():
+    """With beta = 0 nothing is written: S_t = Diag(exp G_t) S_0 with G_t the running
+    sum of g, so o_t = scale S_t^T q_t.  Then dk = dv = 0 exactly,
+    dq_t = scale Diag(exp G_t) S_0 dO_t, dS_0 = sum_t scale exp(G_t) * q_t dO_t^T +
+    exp(G_T) * dS_T (products with exp per row), and dg_t = sum over u >= t of the
+    row-wise terms of <dS_u, ...>, checked here through dg_t = sum_{u>=t} r_u with
+    r_u = scale q_u * (S_u dO_u) and the final-state term on the last token."""
+    from oracle import backward_oracle
+    rng = np.random.default_rng(52)
+    T, H, dk, dv, scale = 6, 2, 4, 3, 0.9
+    q, k, v, g, _ = _rand_inputs(T, H, dk, dv, rng)
+    beta = np.zeros((T, H))
+    s0 = rng.standard_normal((H, dk, dv))
+    d_out = rng.standard_normal((T, H, dv))
+    d_fin = rng.standard_normal((H, dk, dv))
+    gr = backward_oracle(q[None], k[None], v[None], g[None], beta[None], scale, d_out[None],
+                         s0[None], d_fin[None])
+    assert np.all(gr["dk"] == 0.0) and np.all(gr["dv"] == 0.0)
+    G = np.cumsum(g, axis=0)                                   # [T, H, dk]
+    St = np.exp(G)[..., None] * s0[None]                       # [T, H, dk, dv]
+    dq = scale * np.einsum("thij,thj->thi", St, d_out)
+    np.testing.assert_allclose(gr["dq"][0], dq, rtol=1e-12, atol=1e-12)
+    ds0 = (scale * np.exp(G)[..., None] * q[..., None] * d_out[:, :, None, :]).sum(0) \
+        + np.exp(G[-1])[..., None] * d_fin
+    np.testing.assert_allclose(gr["ds0"][0], ds0, rtol=1e-12, atol=1e-12)
+    r = scale * q * np.einsum("thij,thj->thi", St, d_out)      # d<dO_u, o_u>/dG_u
+    r[-1] += np.einsum("hij,hij->hi", St[-1], d_fin)           # final-state term
+    dg = np.cumsum(r[::-1], axis=0)[::-1]
+    np.testing.assert_allclose(gr["dg"][0], dg, rtol=1e-12, atol=1e-12)
+    # dbeta: d<...>/dbeta_t with nothing written = <k_t (v_t - S_t^T k_t)^T, cotangent of S_t>
+    assert np.all(np.isfinite(gr["dbeta"]))
+
+
+@pytest.mark.parametrize("kind", ["sign_flip", "decay_after_write"])
+def test_backward_pins_catch_planted_mistakes(kind, monkeypatch):
+    """A plausible mistake planted in the autodiff oracle's recurrence makes its
+    gradients disagree with the finite differences of the C oracle."""
+    import torch
+    from oracle import backward_oracle, grad
+
+    def mutant(q, k, v, g, beta, scale, s0):
+        S, outs = s0, []
+        for t in range(q.shape[1]):
+            d = torch.exp(g[:, t])[:, :, None]
+            if kind != "decay_after_write":
+                S = S * d
+            recall = (S * k[:, t, :, None]).sum(1)
+            sgn = 1.0 if kind == "sign_flip" else -1.0
+            write = beta[:, t, None] * (v[:, t] + sgn * recall)
+            S = S + k[:, t, :, None] * write[:, None, :]
+            if kind == "decay_after_write":
+                S = S * d
+            outs.append((S * (scale * q[:, t, :, None])).sum(1))
+        return torch.stack(outs, 1), S
+
+    monkeypatch.setattr(grad, "_recurrence", mutant)
+    x, d_out, d_fin = _loss_fd_setup(53)
+    gr = backward_oracle(x["q"][None], x["k"][None], x["v"][None], x["g"][None],
+                         x["beta"][None], 0.7, d_out[None], x["s0"][None], d_fin[None])
+    h, idx = 1e-5, (3, 1, 2)
+    xp = {kk: vv.copy() for kk, vv in x.items()}
+    xm = {kk: vv.copy() for kk, vv in x.items()}
+    xp["k"][idx] += h
+    xm["k"][idx] -= h
+    fd = (_loss(xp, d_out, d_fin, 0.7) - _loss(xm, d_out, d_fin, 0.7)) / (2 * h)
+    assert abs(gr["dk"][0][idx] - fd) > 1e-4
