@@ -6,12 +6,14 @@ Python binding and :mod:`gated_delta_rule_102_amd.inputs` draws seeded inputs.
 """
 from .kda import (  # noqa: F401
     KDAError,
+    chunk_bwd,
     chunk_fwd,
     chunk_fwd_prologue,
     chunk_fwd_snapshots,
     chunk_fwd_varlen,
     decode_step,
     kda_abi_version,
+    kda_chunk_bwd,
     kda_chunk_fwd,
     kda_chunk_fwd_prologue,
     kda_chunk_fwd_snapshots,

@@ -25,7 +25,7 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
-SOURCES = ["kda_prefill.hip", "kda_decode.hip"]
+SOURCES = ["kda_prefill.hip", "kda_decode.hip", "kda_backward.hip"]
 HOST_SOURCES = ["kda_api.cpp"]
 
 

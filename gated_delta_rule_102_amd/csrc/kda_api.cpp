@@ -174,6 +174,31 @@ int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void
   return kda::launch_prefill(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                  const float* initial_state, const void* grad_out,
+                  const float* grad_final_state, void* grad_q, void* grad_k, void* grad_v,
+                  void* grad_g, void* grad_beta, float* grad_initial_state, int B, int T, int H,
+                  int dk, int dv, float scale, int dtype, hipStream_t stream) {
+  int rc = check_common(dk, dv, H, dtype);
+  if (rc != KDA_OK) return rc;
+  if (B <= 0 || T <= 0) return KDA_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * T > INT32_MAX / 2) return KDA_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * H > (1 << 24)) return KDA_ERR_SHAPE;
+  const uintptr_t elt = dtype == KDA_F32 ? 4 : 2;
+  rc = check_ptrs({{q, elt, true}, {k, elt, true}, {v, elt, true}, {g, elt, true},
+                   {beta, elt, true}, {grad_out, elt, true}, {grad_q, elt, true},
+                   {grad_k, elt, true}, {grad_v, elt, true}, {grad_g, elt, true},
+                   {grad_beta, elt, true}, {initial_state, 4, false},
+                   {grad_final_state, 4, false}, {grad_initial_state, 4, false}});
+  if (rc != KDA_OK) return rc;
+  rc = check_device();
+  if (rc != KDA_OK) return rc;
+  kda::BackwardArgs a{q, k, v, g, beta, initial_state, grad_out, grad_final_state,
+                      grad_q, grad_k, grad_v, grad_g, grad_beta, grad_initial_state,
+                      B, T, H, dk, scale, dtype == KDA_F32, stream};
+  return kda::launch_backward(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 int kda_decode_step(const void* q, const void* k, const void* v, const void* g,
                     const void* beta, float* state, void* out, int B, int H, int dk, int dv,
                     float scale, int dtype, hipStream_t stream) {

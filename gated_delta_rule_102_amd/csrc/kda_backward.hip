@@ -1,0 +1,932 @@
+// Backward pass of chunked KDA on gfx950: gradients of
+//     L = sum_t <dO_t, o_t> + <dS_T, S_T>
+// with respect to q, k, v, g, beta and the initial state, for fixed-length
+// sequences.  The pages train KDA at up to 1M tokens of context (best.xiaohu.ai
+// "Kimi K3 tech report", context-curriculum section) but print no backward; the
+// gradients are the plain derivatives of the forward rule (neurohive.io Kimi K3
+// review, section "Sequence length: hybrid KDA and Gated MLA attention").
+//
+// Per (sequence, head), every 64-token chunk is an affine map of the entering
+// state S and the chunk's values V, written with operands that depend only on
+// the chunk's q, k, g, beta (G = running sum of g inside the chunk):
+//     A'[t,s] = sum_c k_tc k_sc e^{G_tc - G_sc} (s < t),  Ti = (I + Diag(beta) A')^-1
+//     M'[t,s] = sum_c q_tc k_sc e^{G_tc - G_sc} (s <= t), Tb = Ti Diag(beta)
+//     W = Tb (k e^G),  P = scale M' Tb,  Q' = scale q e^G - P (k e^G),
+//     Kt = k e^{G_last - G},  Lam = e^{G_last}
+//     Delta = Tb V - W S,   O = Q' S + P V,   S_next = Lam S + Kt^T Delta.
+// The backward runs in six launches:
+//   bwd_prep     per chunk: the operands above (fp32, to a workspace);
+//   bwd_fwd_scan per (sequence, head, 32 value columns): S at every chunk start
+//                and Delta, walking the chunks forwards;
+//   bwd_scan     the same grid walking backwards from dS_T:
+//                dU = Kt dS, dV = P^T dO + Tb^T dU, dS <- Lam dS + Q'^T dO - W^T dU;
+//   bwd_grad_dv  per chunk: the operand gradients, contractions over the value
+//                columns: dQ' = dO S^T, dW = -dU S^T, dKt = Delta dS^T,
+//                dLam = rowsum(S * dS), dP = dO V^T, dTb = dU V^T;
+//   bwd_grad_nn  per chunk: the 64 x 64 algebra through P, Q', W, Tb and the
+//                inverse (dP_tot, dKg, dTb_tot, dM', dA', dbeta);
+//   bwd_grad_decay per chunk: the decayed products of dA' and dM' with k and q,
+//                and the chain to dq, dk and dg (a reverse running sum).
+// Every product runs on the fp32 16x16x4 matrix cores from LDS.  Decayed
+// products use 16-row sub-tile references (G at each sub-tile's last row) so
+// that every factor stays inside fp32's range when the log-decay is >= -5.
+
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int CR = 64;    // rows per chunk
+constexpr int SL = 32;    // value columns per scan workgroup / per contraction slice
+constexpr int LS = 68;    // leading dimension of 64 x 64 LDS matrices
+constexpr int LV = 36;    // leading dimension of 32-column LDS slices
+
+template <int D>
+struct BwdLayout {
+  static constexpr int LD = D + 4;   // leading dimension of 64 x D LDS matrices
+  // workspace per chunk, written by bwd_prep (floats, row-major)
+  static constexpr int TB = 0, TI = 4096, AP = 8192, MP = 12288, PP = 16384;
+  static constexpr int W = 20480, QP = W + CR * D, KT = QP + CR * D, G = KT + CR * D;
+  static constexpr int LAM = G + CR * D, WS = LAM + D;
+  // operand gradients per chunk, written by bwd_grad_dv
+  static constexpr int DQP = 0, DW = CR * D, DKT = 2 * CR * D, DP = 3 * CR * D;
+  static constexpr int DTB = DP + 4096, DLAM = DTB + 4096, G1 = DLAM + D;
+  // written by bwd_grad_nn
+  static constexpr int DKG = 0, DMP = CR * D, DAP = DMP + 4096, G2 = DAP + 4096;
+};
+
+__device__ __forceinline__ int lane16() { return threadIdx.x & 15; }
+__device__ __forceinline__ int lane_g4() { return (threadIdx.x >> 4) & 3; }
+
+// acc += op(A) op(B) for one 16 x 16 output tile; K is a multiple of 16.
+//   op(A)(r, k) = TA ? a[k * lda + r] : a[r * lda + k]     (r < 16, k < K)
+//   op(B)(k, c) = TB ? b[c * ldb + k] : b[k * ldb + c]     (c < 16)
+// With KS, op(A)(r, k) is multiplied by ks[k].  At step j of each 16-wide block
+// lane (g4, l16) feeds A(l16, k0 + 4 g4 + j) and B(k0 + 4 g4 + j, l16); the
+// result is acc[i] = C(4 g4 + i, l16).
+template <bool TA, bool TB, bool KS = false>
+__device__ __forceinline__ f32x4_t mm(f32x4_t acc, const float* a, int lda, const float* b,
+                                      int ldb, int K, const float* ks = nullptr) {
+  const int l16 = lane16(), g4 = lane_g4();
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    const int kb = k0 + 4 * g4;
+    float av[4], bv[4];
+    if constexpr (TA) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) av[j] = a[(kb + j) * lda + l16];
+    } else {
+      const float4 t = *reinterpret_cast<const float4*>(a + l16 * lda + kb);
+      av[0] = t.x; av[1] = t.y; av[2] = t.z; av[3] = t.w;
+    }
+    if constexpr (TB) {
+      const float4 t = *reinterpret_cast<const float4*>(b + l16 * ldb + kb);
+      bv[0] = t.x; bv[1] = t.y; bv[2] = t.z; bv[3] = t.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bv[j] = b[(kb + j) * ldb + l16];
+    }
+    if constexpr (KS) {
+      const float4 s = *reinterpret_cast<const float4*>(ks + kb);
+      av[0] *= s.x; av[1] *= s.y; av[2] *= s.z; av[3] *= s.w;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], bv[j], acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
+
+// tile (accumulator layout) <-> memory at the tile's origin with leading dimension ld
+__device__ __forceinline__ void put(float* dst, int ld, const f32x4_t& v) {
+  const int l16 = lane16(), g4 = lane_g4();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dst[(4 * g4 + i) * ld + l16] = v[i];
+}
+__device__ __forceinline__ f32x4_t get(const float* src, int ld) {
+  const int l16 = lane16(), g4 = lane_g4();
+  f32x4_t v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = src[(4 * g4 + i) * ld + l16];
+  return v;
+}
+
+// rows x cols fp32 (cols % 4 == 0, both sides 16-byte aligned) global -> LDS
+template <int NT>
+__device__ __forceinline__ void g2l(float* dst, int lld, const float* src, int64_t gld, int rows,
+                                    int cols) {
+  const int c4 = cols / 4;
+  for (int e = threadIdx.x; e < rows * c4; e += NT) {
+    const int r = e / c4, c = (e - r * c4) * 4;
+    *reinterpret_cast<float4*>(dst + r * lld + c) =
+        *reinterpret_cast<const float4*>(src + r * gld + c);
+  }
+}
+template <int NT>
+__device__ __forceinline__ void l2g(float* dst, int64_t gld, const float* src, int lld, int rows,
+                                    int cols) {
+  const int c4 = cols / 4;
+  for (int e = threadIdx.x; e < rows * c4; e += NT) {
+    const int r = e / c4, c = (e - r * c4) * 4;
+    *reinterpret_cast<float4*>(dst + r * gld + c) =
+        *reinterpret_cast<const float4*>(src + r * lld + c);
+  }
+}
+// 64 x cols input rows (bf16 or fp32) -> fp32 LDS, rows >= nrow read as zero
+template <int NT, typename TIn>
+__device__ __forceinline__ void in2l(float* dst, int lld, const TIn* src, int64_t row_stride,
+                                     int nrow, int cols) {
+  for (int e = threadIdx.x; e < CR * cols; e += NT) {
+    const int r = e / cols, c = e - r * cols;
+    dst[r * lld + c] = r < nrow ? to_f32(src[r * row_stride + c]) : 0.f;
+  }
+}
+
+// sub-tile pairs J < I of a 64-row chunk -> 0..5
+__device__ __forceinline__ int pair_index(int I, int J) { return I * (I - 1) / 2 + J; }
+
+struct ChunkPos {
+  int b, h, c, nrow;
+  int64_t row0;   // (b * T + first token) * H + h: token-row index of the chunk's row 0
+};
+__device__ __forceinline__ ChunkPos chunk_pos(int item, int T, int H, int nc) {
+  ChunkPos p;
+  p.c = item % nc;
+  const int bh = item / nc;
+  p.b = bh / H;
+  p.h = bh - p.b * H;
+  p.nrow = min(CR, T - p.c * CR);
+  p.row0 = (static_cast<int64_t>(p.b) * T + static_cast<int64_t>(p.c) * CR) * H + p.h;
+  return p;
+}
+
+// ---------------------------------------------------------------- bwd_prep
+
+template <int D, typename TIn>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const TIn* __restrict__ q,
+                                                       const TIn* __restrict__ k,
+                                                       const TIn* __restrict__ g,
+                                                       const TIn* __restrict__ beta,
+                                                       float* __restrict__ ws, int T, int H,
+                                                       int nc, float scale) {
+  using L = BwdLayout<D>;
+  constexpr int LD = L::LD;
+  __shared__ __attribute__((aligned(16))) float sm[3 * CR * LD + 3 * CR * LS + 6 * D + CR];
+  float* R0 = sm;                 // G, then (phase 5 on) unused
+  float* R1 = R0 + CR * LD;       // k rowf -> q rowf -> k e^G
+  float* R2 = R1 + CR * LD;       // k colf -> inverse scratch -> scale q e^G
+  float* S0 = R2 + CR * LD;       // A' -> P
+  float* S1 = S0 + CR * LS;       // M'
+  float* S2 = S1 + CR * LS;       // Ti
+  float* FP = S2 + CR * LS;       // [6][D] pair factors e^{R_I - R_J}
+  float* BT = FP + 6 * D;         // beta
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l16 = lane16(), g4 = lane_g4();
+  const ChunkPos p = chunk_pos(blockIdx.x, T, H, nc);
+  const int64_t rs = static_cast<int64_t>(H) * D;
+  const TIn* qc = q + p.row0 * D;
+  const TIn* kc = k + p.row0 * D;
+  const TIn* gc = g + p.row0 * D;
+  float* w = ws + static_cast<int64_t>(blockIdx.x) * L::WS;
+
+  for (int e = tid; e < 3 * CR * LS; e += 256) S0[e] = 0.f;
+  if (tid < CR) BT[tid] = tid < p.nrow ? to_f32(beta[p.row0 + static_cast<int64_t>(tid) * H]) : 0.f;
+  if (tid < D) {   // running sum of g down the chunk (padding rows add 0)
+    float acc = 0.f;
+    for (int t = 0; t < CR; ++t) {
+      acc += t < p.nrow ? to_f32(gc[t * rs + tid]) : 0.f;
+      R0[t * LD + tid] = acc;
+    }
+  }
+  __syncthreads();
+
+  if (tid < D) {
+    for (int I = 1; I < 4; ++I)
+      for (int J = 0; J < I; ++J)
+        FP[pair_index(I, J) * D + tid] =
+            expf(R0[(16 * I + 15) * LD + tid] - R0[(16 * J + 15) * LD + tid]);
+    w[L::LAM + tid] = expf(R0[(CR - 1) * LD + tid]);
+  }
+  for (int e = tid; e < CR * D; e += 256) {
+    const int t = e / D, i = e - t * D;
+    const float G = R0[t * LD + i], RI = R0[(t | 15) * LD + i], Gl = R0[(CR - 1) * LD + i];
+    const float kv = t < p.nrow ? to_f32(kc[t * rs + i]) : 0.f;
+    R1[t * LD + i] = kv * expf(G - RI);
+    R2[t * LD + i] = kv * expf(RI - G);
+    w[L::KT + e] = kv * expf(Gl - G);
+    w[L::G + e] = G;
+  }
+  __syncthreads();
+
+  // A' and M' by sub-tile pairs (I, J), J <= I: 10 tiles each
+  auto pair_gram = [&](float* dst, bool strict) {
+    for (int pt = wave; pt < 10; pt += 4) {
+      int I = 0;
+      while ((I + 1) * (I + 2) / 2 <= pt) ++I;
+      const int J = pt - I * (I + 1) / 2;
+      f32x4_t acc = zero4();
+      if (I == J) {
+        acc = mm<false, true>(acc, R1 + 16 * I * LD, LD, R2 + 16 * J * LD, LD, D);
+      } else {
+        acc = mm<false, true, true>(acc, R1 + 16 * I * LD, LD, R2 + 16 * J * LD, LD, D,
+                                    FP + pair_index(I, J) * D);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * I + 4 * g4 + i, s = 16 * J + l16;
+        dst[t * LS + s] = (strict ? s < t : s <= t) ? acc[i] : 0.f;
+      }
+    }
+  };
+  pair_gram(S0, true);
+  __syncthreads();
+  for (int e = tid; e < CR * D; e += 256) {   // q rowf into R1
+    const int t = e / D, i = e - t * D;
+    const float G = R0[t * LD + i], RI = R0[(t | 15) * LD + i];
+    const float qv = t < p.nrow ? to_f32(qc[t * rs + i]) : 0.f;
+    R1[t * LD + i] = qv * expf(G - RI);
+  }
+  __syncthreads();
+  pair_gram(S1, false);
+  __syncthreads();
+  l2g<256>(w + L::AP, CR, S0, LS, CR, CR);
+  l2g<256>(w + L::MP, CR, S1, LS, CR, CR);
+
+  // Ti = (I + Diag(beta) A')^-1: diagonal 16 x 16 blocks by substitution (one
+  // column per lane), then the blocks below them level by level:
+  //   Ti_IJ = -Ti_II Diag(beta_I) sum_{J <= m < I} A'_Im Ti_mJ
+  if (lane < 16) {
+    const int I = wave, j = lane;
+    float x[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      float s = t == j ? 1.f : 0.f;
+      const float bt = BT[16 * I + t];
+#pragma unroll
+      for (int u = 0; u < t; ++u) s -= bt * S0[(16 * I + t) * LS + 16 * I + u] * x[u];
+      x[t] = s;
+    }
+#pragma unroll
+    for (int t = 0; t < 16; ++t) S2[(16 * I + t) * LS + 16 * I + j] = x[t];
+  }
+  __syncthreads();
+  float* xs = R2 + wave * 16 * 17;
+  for (int I = 1; I < 4; ++I) {
+    if (wave < I) {
+      const int J = wave;
+      f32x4_t y = mm<false, false>(zero4(), S0 + 16 * I * LS + 16 * J, LS,
+                                   S2 + 16 * J * LS + 16 * J, LS, 16 * (I - J));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] *= BT[16 * I + 4 * g4 + i];
+      put(xs, 17, y);
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      const f32x4_t tt = mm<false, false>(zero4(), S2 + 16 * I * LS + 16 * I, LS, xs, 17, 16);
+      put(S2 + 16 * I * LS + 16 * J, LS, -tt);
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < CR * CR; e += 256) {
+    const int t = e / CR, s = e - t * CR;
+    const float ti = S2[t * LS + s];
+    w[L::TI + e] = ti;
+    w[L::TB + e] = ti * BT[s];
+  }
+  for (int e = tid; e < CR * D; e += 256) {   // k e^G into R1, scale q e^G into R2
+    const int t = e / D, i = e - t * D;
+    const float eg = expf(R0[t * LD + i]);
+    const bool ok = t < p.nrow;
+    R1[t * LD + i] = ok ? to_f32(kc[t * rs + i]) * eg : 0.f;
+    R2[t * LD + i] = ok ? scale * to_f32(qc[t * rs + i]) * eg : 0.f;
+  }
+  __syncthreads();
+
+  // P = scale M' Tb (into S0 and the workspace); W = Tb (k e^G)
+  for (int j = wave; j < 16; j += 4) {
+    const int rt = j >> 2, ct = j & 3;
+    f32x4_t acc = mm<false, false>(zero4(), S1 + 16 * rt * LS, LS, S2 + 16 * ct, LS, CR);
+    const float f = scale * BT[16 * ct + l16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] *= f;
+    put(S0 + 16 * rt * LS + 16 * ct, LS, acc);
+    put(w + L::PP + 16 * rt * CR + 16 * ct, CR, acc);
+  }
+  constexpr int CT = D / 16;
+  for (int j = wave; j < 4 * CT; j += 4) {
+    const int rt = j / CT, ct = j - rt * CT;
+    const f32x4_t acc = mm<false, false, true>(zero4(), S2 + 16 * rt * LS, LS, R1 + 16 * ct, LD,
+                                               CR, BT);
+    put(w + L::W + 16 * rt * D + 16 * ct, D, acc);
+  }
+  __syncthreads();
+  // Q' = scale q e^G - P (k e^G)
+  for (int j = wave; j < 4 * CT; j += 4) {
+    const int rt = j / CT, ct = j - rt * CT;
+    const f32x4_t pk = mm<false, false>(zero4(), S0 + 16 * rt * LS, LS, R1 + 16 * ct, LD, CR);
+    f32x4_t acc = get(R2 + 16 * rt * LD + 16 * ct, LD);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] -= pk[i];
+    put(w + L::QP + 16 * rt * D + 16 * ct, D, acc);
+  }
+}
+
+// ---------------------------------------------------------------- scans
+
+// State tiles of one workgroup: D x 32 columns = (D/16) x 2 tiles, D/32 per wave.
+template <int D>
+struct ScanTiles {
+  static constexpr int NTW = D / 32;
+  static __device__ __forceinline__ int rt(int wave, int x) { return (wave * NTW + x) >> 1; }
+  static __device__ __forceinline__ int ct(int wave, int x) { return (wave * NTW + x) & 1; }
+};
+
+template <int D, typename TIn>
+__global__ __launch_bounds__(256) void bwd_fwd_scan_kernel(const TIn* __restrict__ v,
+                                                           const float* __restrict__ s0,
+                                                           const float* __restrict__ ws,
+                                                           float* __restrict__ st,
+                                                           float* __restrict__ dl, int T, int H,
+                                                           int nc) {
+  using L = BwdLayout<D>;
+  using ST = ScanTiles<D>;
+  constexpr int LD = L::LD;
+  __shared__ __attribute__((aligned(16))) float sm[CR * LS + 2 * CR * LD + 2 * CR * LV + D * LV + D];
+  float* TBs = sm;
+  float* Ws = TBs + CR * LS;
+  float* KTs = Ws + CR * LD;
+  float* Vs = KTs + CR * LD;
+  float* Dls = Vs + CR * LV;
+  float* Ss = Dls + CR * LV;
+  float* Lm = Ss + D * LV;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int l16 = lane16(), g4 = lane_g4();
+  constexpr int NSL = D / SL;
+  const int bh = blockIdx.x / NSL, c0 = (blockIdx.x - bh * NSL) * SL;
+  const int b = bh / H, h = bh - b * H;
+
+  f32x4_t S[ST::NTW];
+#pragma unroll
+  for (int x = 0; x < ST::NTW; ++x) {
+    const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
+    S[x] = s0 ? get(s0 + static_cast<int64_t>(bh) * D * D + 16 * rt * D + c0 + 16 * ct, D) : zero4();
+  }
+  for (int c = 0; c < nc; ++c) {
+    const int64_t item = static_cast<int64_t>(bh) * nc + c;
+    const float* w = ws + item * L::WS;
+    const int nrow = min(CR, T - c * CR);
+    g2l<256>(TBs, LS, w + L::TB, CR, CR, CR);
+    g2l<256>(Ws, LD, w + L::W, D, CR, D);
+    g2l<256>(KTs, LD, w + L::KT, D, CR, D);
+    if (tid < D) Lm[tid] = w[L::LAM + tid];
+    const int64_t row0 = (static_cast<int64_t>(b) * T + static_cast<int64_t>(c) * CR) * H + h;
+    in2l<256>(Vs, LV, v + row0 * D + c0, static_cast<int64_t>(H) * D, nrow, SL);
+#pragma unroll
+    for (int x = 0; x < ST::NTW; ++x) {
+      const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
+      put(Ss + 16 * rt * LV + 16 * ct, LV, S[x]);
+      put(st + item * D * D + 16 * rt * D + c0 + 16 * ct, D, S[x]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int y = 0; y < 2; ++y) {   // Delta = Tb V - W S: 4 x 2 tiles
+      const int j = wave * 2 + y, rt = j >> 1, ct = j & 1;
+      const f32x4_t tv = mm<false, false>(zero4(), TBs + 16 * rt * LS, LS, Vs + 16 * ct, LV, CR);
+      const f32x4_t wsv = mm<false, false>(zero4(), Ws + 16 * rt * LD, LD, Ss + 16 * ct, LV, D);
+      f32x4_t d;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d[i] = tv[i] - wsv[i];
+      put(Dls + 16 * rt * LV + 16 * ct, LV, d);
+      put(dl + item * CR * D + 16 * rt * D + c0 + 16 * ct, D, d);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < ST::NTW; ++x) {   // S = Lam S + Kt^T Delta
+      const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
+      f32x4_t acc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = Lm[16 * rt + 4 * g4 + i] * S[x][i];
+      S[x] = mm<true, false>(acc, KTs + 16 * rt, LD, Dls + 16 * ct, LV, CR);
+    }
+    __syncthreads();
+  }
+  (void)l16;
+}
+
+template <int D, typename TIn>
+__global__ __launch_bounds__(256) void bwd_scan_kernel(const TIn* __restrict__ dout,
+                                                       const float* __restrict__ dsT,
+                                                       const float* __restrict__ ws,
+                                                       float* __restrict__ dst,
+                                                       float* __restrict__ du,
+                                                       TIn* __restrict__ dv,
+                                                       float* __restrict__ ds0, int T, int H,
+                                                       int nc) {
+  using L = BwdLayout<D>;
+  using ST = ScanTiles<D>;
+  constexpr int LD = L::LD;
+  __shared__ __attribute__((aligned(16))) float sm[2 * CR * LD + 2 * CR * LS + 2 * CR * LV + D * LV + D];
+  float* KQs = sm;                 // Kt, then Q'
+  float* Ws = KQs + CR * LD;
+  float* Ps = Ws + CR * LD;
+  float* TBs = Ps + CR * LS;
+  float* dOs = TBs + CR * LS;
+  float* dUs = dOs + CR * LV;
+  float* dSs = dUs + CR * LV;
+  float* Lm = dSs + D * LV;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int l16 = lane16(), g4 = lane_g4();
+  constexpr int NSL = D / SL;
+  const int bh = blockIdx.x / NSL, c0 = (blockIdx.x - bh * NSL) * SL;
+  const int b = bh / H, h = bh - b * H;
+  const int64_t rs = static_cast<int64_t>(H) * D;
+
+  f32x4_t dS[ST::NTW];
+#pragma unroll
+  for (int x = 0; x < ST::NTW; ++x) {
+    const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
+    dS[x] = dsT ? get(dsT + static_cast<int64_t>(bh) * D * D + 16 * rt * D + c0 + 16 * ct, D) : zero4();
+  }
+  for (int c = nc - 1; c >= 0; --c) {
+    const int64_t item = static_cast<int64_t>(bh) * nc + c;
+    const float* w = ws + item * L::WS;
+    const int nrow = min(CR, T - c * CR);
+    const int64_t row0 = (static_cast<int64_t>(b) * T + static_cast<int64_t>(c) * CR) * H + h;
+    g2l<256>(KQs, LD, w + L::KT, D, CR, D);
+    g2l<256>(Ws, LD, w + L::W, D, CR, D);
+    g2l<256>(Ps, LS, w + L::PP, CR, CR, CR);
+    g2l<256>(TBs, LS, w + L::TB, CR, CR, CR);
+    if (tid < D) Lm[tid] = w[L::LAM + tid];
+    in2l<256>(dOs, LV, dout + row0 * D + c0, rs, nrow, SL);
+#pragma unroll
+    for (int x = 0; x < ST::NTW; ++x) {
+      const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
+      put(dSs + 16 * rt * LV + 16 * ct, LV, dS[x]);
+      put(dst + item * D * D + 16 * rt * D + c0 + 16 * ct, D, dS[x]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int y = 0; y < 2; ++y) {   // dU = Kt dS
+      const int j = wave * 2 + y, rt = j >> 1, ct = j & 1;
+      const f32x4_t u = mm<false, false>(zero4(), KQs + 16 * rt * LD, LD, dSs + 16 * ct, LV, D);
+      put(dUs + 16 * rt * LV + 16 * ct, LV, u);
+      put(du + item * CR * D + 16 * rt * D + c0 + 16 * ct, D, u);
+    }
+    __syncthreads();
+    g2l<256>(KQs, LD, w + L::QP, D, CR, D);
+#pragma unroll
+    for (int y = 0; y < 2; ++y) {   // dV = P^T dO + Tb^T dU
+      const int j = wave * 2 + y, rt = j >> 1, ct = j & 1;
+      f32x4_t acc = mm<true, false>(zero4(), Ps + 16 * rt, LS, dOs + 16 * ct, LV, CR);
+      acc = mm<true, false>(acc, TBs + 16 * rt, LS, dUs + 16 * ct, LV, CR);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * rt + 4 * g4 + i;
+        if (t < nrow) dv[(row0 + static_cast<int64_t>(t) * H) * D + c0 + 16 * ct + l16] = Elem<TIn>::from(acc[i]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < ST::NTW; ++x) {   // dS = Lam dS + Q'^T dO - W^T dU
+      const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
+      f32x4_t acc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = Lm[16 * rt + 4 * g4 + i] * dS[x][i];
+      acc = mm<true, false>(acc, KQs + 16 * rt, LD, dOs + 16 * ct, LV, CR);
+      const f32x4_t wu = mm<true, false>(zero4(), Ws + 16 * rt, LD, dUs + 16 * ct, LV, CR);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dS[x][i] = acc[i] - wu[i];
+    }
+    __syncthreads();
+  }
+  if (ds0) {
+#pragma unroll
+    for (int x = 0; x < ST::NTW; ++x) {
+      const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
+      put(ds0 + static_cast<int64_t>(bh) * D * D + 16 * rt * D + c0 + 16 * ct, D, dS[x]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- operand gradients
+
+template <int D, typename TIn>
+__global__ __launch_bounds__(512) void bwd_grad_dv_kernel(const TIn* __restrict__ v,
+                                                          const TIn* __restrict__ dout,
+                                                          const float* __restrict__ st,
+                                                          const float* __restrict__ dst,
+                                                          const float* __restrict__ dl,
+                                                          const float* __restrict__ du,
+                                                          float* __restrict__ g1, int T, int H,
+                                                          int nc) {
+  using L = BwdLayout<D>;
+  __shared__ __attribute__((aligned(16))) float sm[2 * D * LV + 4 * CR * LV];
+  float* Ss = sm;
+  float* dSs = Ss + D * LV;
+  float* dOs = dSs + D * LV;
+  float* dUs = dOs + CR * LV;
+  float* Dls = dUs + CR * LV;
+  float* Vs = Dls + CR * LV;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const ChunkPos p = chunk_pos(blockIdx.x, T, H, nc);
+  const int64_t item = blockIdx.x;
+  const int64_t rs = static_cast<int64_t>(H) * D;
+  constexpr int CT = D / 16;
+  constexpr int NBIG = 4 * CT;                     // tiles of a 64 x D matrix
+  constexpr int NTOT = 3 * NBIG + 32, NTW = NTOT / 8;
+  static_assert(NTOT % 8 == 0, "tile split");
+
+  f32x4_t acc[NTW];
+#pragma unroll
+  for (int x = 0; x < NTW; ++x) acc[x] = zero4();
+  float dlam = 0.f;
+  for (int c0 = 0; c0 < D; c0 += SL) {
+    g2l<512>(Ss, LV, st + item * D * D + c0, D, D, SL);
+    g2l<512>(dSs, LV, dst + item * D * D + c0, D, D, SL);
+    g2l<512>(Dls, LV, dl + item * CR * D + c0, D, CR, SL);
+    g2l<512>(dUs, LV, du + item * CR * D + c0, D, CR, SL);
+    in2l<512>(dOs, LV, dout + p.row0 * D + c0, rs, p.nrow, SL);
+    in2l<512>(Vs, LV, v + p.row0 * D + c0, rs, p.nrow, SL);
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < NTW; ++x) {
+      const int j = wave + 8 * x;
+      if (j < 3 * NBIG) {   // dQ' = dO S^T, -dW = dU S^T, dKt = Delta dS^T
+        const int m = j / NBIG, r = j - m * NBIG, rt = r / CT, ct = r - rt * CT;
+        const float* A = (m == 0 ? dOs : m == 1 ? dUs : Dls) + 16 * rt * LV;
+        const float* Bm = (m == 2 ? dSs : Ss) + 16 * ct * LV;
+        acc[x] = mm<false, true>(acc[x], A, LV, Bm, LV, SL);
+      } else {              // dP = dO V^T, dTb = dU V^T
+        const int j2 = j - 3 * NBIG, m = j2 >> 4, rt = (j2 & 15) >> 2, ct = j2 & 3;
+        acc[x] = mm<false, true>(acc[x], (m == 0 ? dOs : dUs) + 16 * rt * LV, LV,
+                                 Vs + 16 * ct * LV, LV, SL);
+      }
+    }
+    if (tid < D) {
+#pragma unroll 8
+      for (int jj = 0; jj < SL; ++jj) dlam += Ss[tid * LV + jj] * dSs[tid * LV + jj];
+    }
+    __syncthreads();
+  }
+  float* o = g1 + item * L::G1;
+#pragma unroll
+  for (int x = 0; x < NTW; ++x) {
+    const int j = wave + 8 * x;
+    if (j < 3 * NBIG) {
+      const int m = j / NBIG, r = j - m * NBIG, rt = r / CT, ct = r - rt * CT;
+      f32x4_t vv = acc[x];
+      if (m == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vv[i] = -vv[i];
+      }
+      put(o + m * CR * D + 16 * rt * D + 16 * ct, D, vv);
+    } else {
+      const int j2 = j - 3 * NBIG, m = j2 >> 4, rt = (j2 & 15) >> 2, ct = j2 & 3;
+      put(o + (m == 0 ? L::DP : L::DTB) + 16 * rt * CR + 16 * ct, CR, acc[x]);
+    }
+  }
+  if (tid < D) o[L::DLAM + tid] = dlam;
+}
+
+// ---------------------------------------------------------------- 64 x 64 algebra
+
+template <int D>
+struct NnLds {
+  static constexpr int LD = D + 4;
+  static constexpr int A = 3 * CR * LD + CR * LS, B = 5 * CR * LS;
+  static constexpr int FRONT = A > B ? A : B;      // phase A: Kg, dQ', dW, P; phase B: 5 matrices
+  static constexpr int TOTAL = FRONT + CR * LS + CR;
+};
+
+template <int D, typename TIn>
+__global__ __launch_bounds__(256) void bwd_grad_nn_kernel(const TIn* __restrict__ k,
+                                                          const TIn* __restrict__ beta,
+                                                          const float* __restrict__ ws,
+                                                          const float* __restrict__ g1,
+                                                          float* __restrict__ g2,
+                                                          TIn* __restrict__ dbeta, int T, int H,
+                                                          int nc, float scale) {
+  using L = BwdLayout<D>;
+  using NL = NnLds<D>;
+  constexpr int LD = L::LD;
+  __shared__ __attribute__((aligned(16))) float sm[NL::TOTAL];
+  // phase A
+  float* Kg = sm;
+  float* dQ = Kg + CR * LD;
+  float* dW = dQ + CR * LD;
+  float* Ps = dW + CR * LD;
+  float* TBs = sm + NL::FRONT;   // kept through phase B
+  float* BT = TBs + CR * LS;
+  // phase B
+  float* B0 = sm;                // dP_tot, then X = dTi Ti^T
+  float* B1 = B0 + CR * LS;      // M', then dA
+  float* B2 = B1 + CR * LS;      // Ti
+  float* B3 = B2 + CR * LS;      // dTb_tot
+  float* B4 = B3 + CR * LS;      // dTi
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int l16 = lane16(), g4 = lane_g4();
+  const ChunkPos p = chunk_pos(blockIdx.x, T, H, nc);
+  const int64_t item = blockIdx.x;
+  const int64_t rs = static_cast<int64_t>(H) * D;
+  const float* w = ws + item * L::WS;
+  const float* a1 = g1 + item * L::G1;
+  float* a2 = g2 + item * L::G2;
+  const TIn* kc = k + p.row0 * D;
+  constexpr int CT = D / 16;
+
+  for (int e = tid; e < CR * D; e += 256) {
+    const int t = e / D, i = e - t * D;
+    Kg[t * LD + i] = t < p.nrow ? to_f32(kc[t * rs + i]) * expf(w[L::G + e]) : 0.f;
+  }
+  g2l<256>(dQ, LD, a1 + L::DQP, D, CR, D);
+  g2l<256>(dW, LD, a1 + L::DW, D, CR, D);
+  g2l<256>(Ps, LS, w + L::PP, CR, CR, CR);
+  g2l<256>(TBs, LS, w + L::TB, CR, CR, CR);
+  if (tid < CR) BT[tid] = tid < p.nrow ? to_f32(beta[p.row0 + static_cast<int64_t>(tid) * H]) : 0.f;
+  __syncthreads();
+
+  // dP_tot = dP - dQ' Kg^T and dTb_part = dTb + dW Kg^T (tiles wave + 4x)
+  f32x4_t dPt[4], dTt[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int j = wave + 4 * x, rt = j >> 2, ct = j & 3;
+    const f32x4_t qk = mm<false, true>(zero4(), dQ + 16 * rt * LD, LD, Kg + 16 * ct * LD, LD, D);
+    const f32x4_t wk = mm<false, true>(zero4(), dW + 16 * rt * LD, LD, Kg + 16 * ct * LD, LD, D);
+    dPt[x] = get(a1 + L::DP + 16 * rt * CR + 16 * ct, CR);
+    dTt[x] = get(a1 + L::DTB + 16 * rt * CR + 16 * ct, CR);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      dPt[x][i] -= qk[i];
+      dTt[x][i] += wk[i];
+    }
+  }
+  // dKg = -P^T dQ' + Tb^T dW
+  for (int j = wave; j < 4 * CT; j += 4) {
+    const int rt = j / CT, ct = j - rt * CT;
+    const f32x4_t pq = mm<true, false>(zero4(), Ps + 16 * rt, LS, dQ + 16 * ct, LD, CR);
+    f32x4_t acc = mm<true, false>(zero4(), TBs + 16 * rt, LS, dW + 16 * ct, LD, CR);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] -= pq[i];
+    put(a2 + L::DKG + 16 * rt * D + 16 * ct, D, acc);
+  }
+  __syncthreads();
+
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int j = wave + 4 * x, rt = j >> 2, ct = j & 3;
+    put(B0 + 16 * rt * LS + 16 * ct, LS, dPt[x]);
+  }
+  g2l<256>(B1, LS, w + L::MP, CR, CR, CR);
+  g2l<256>(B2, LS, w + L::TI, CR, CR, CR);
+  __syncthreads();
+  // dTb_tot = dTb_part + scale M'^T dP_tot;  dM' = scale (dP_tot Tb^T) on s <= t
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int j = wave + 4 * x, rt = j >> 2, ct = j & 3;
+    const f32x4_t mp = mm<true, false>(zero4(), B1 + 16 * rt, LS, B0 + 16 * ct, LS, CR);
+    f32x4_t dm = mm<false, true>(zero4(), B0 + 16 * rt * LS, LS, TBs + 16 * ct * LS, LS, CR);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * rt + 4 * g4 + i, s = 16 * ct + l16;
+      dTt[x][i] += scale * mp[i];
+      dm[i] = s <= t ? scale * dm[i] : 0.f;
+    }
+    put(a2 + L::DMP + 16 * rt * CR + 16 * ct, CR, dm);
+    put(B3 + 16 * rt * LS + 16 * ct, LS, dTt[x]);
+    f32x4_t dti = dTt[x];
+    const float bc = BT[16 * ct + l16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dti[i] *= bc;
+    put(B4 + 16 * rt * LS + 16 * ct, LS, dti);
+  }
+  __syncthreads();
+  // dbeta_s (through Tb = Ti Diag(beta)) = sum_t Ti[t,s] dTb_tot[t,s]
+  float db = 0.f;
+  if (tid < CR) {
+    for (int t = 0; t < CR; ++t) db += B2[t * LS + tid] * B3[t * LS + tid];
+  }
+  f32x4_t X[4];   // X = dTi Ti^T
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int j = wave + 4 * x, rt = j >> 2, ct = j & 3;
+    X[x] = mm<false, true>(zero4(), B4 + 16 * rt * LS, LS, B2 + 16 * ct * LS, LS, CR);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int j = wave + 4 * x, rt = j >> 2, ct = j & 3;
+    put(B0 + 16 * rt * LS + 16 * ct, LS, X[x]);
+  }
+  __syncthreads();
+  // dA = -Ti^T X on s < t;  dA' = Diag(beta) dA
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int j = wave + 4 * x, rt = j >> 2, ct = j & 3;
+    f32x4_t da = mm<true, false>(zero4(), B2 + 16 * rt, LS, B0 + 16 * ct, LS, CR);
+    f32x4_t dap;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * rt + 4 * g4 + i, s = 16 * ct + l16;
+      da[i] = s < t ? -da[i] : 0.f;
+      dap[i] = BT[t] * da[i];
+    }
+    put(B1 + 16 * rt * LS + 16 * ct, LS, da);
+    put(a2 + L::DAP + 16 * rt * CR + 16 * ct, CR, dap);
+  }
+  __syncthreads();
+  if (tid < p.nrow) {   // dbeta_t (through A = Diag(beta) A') += sum_s dA[t,s] A'[t,s]
+    const float* ap = w + L::AP + tid * CR;
+    for (int s = 0; s < CR; ++s) db += B1[tid * LS + s] * ap[s];
+    dbeta[p.row0 + static_cast<int64_t>(tid) * H] = Elem<TIn>::from(db);
+  }
+}
+
+// ---------------------------------------------------------------- decayed products
+
+template <int D, typename TIn>
+__global__ __launch_bounds__(512) void bwd_grad_decay_kernel(const TIn* __restrict__ q,
+                                                             const TIn* __restrict__ k,
+                                                             const float* __restrict__ ws,
+                                                             const float* __restrict__ g1,
+                                                             const float* __restrict__ g2,
+                                                             TIn* __restrict__ dq,
+                                                             TIn* __restrict__ dk,
+                                                             TIn* __restrict__ dg, int T, int H,
+                                                             int nc, float scale) {
+  using L = BwdLayout<D>;
+  constexpr int LD = L::LD;
+  __shared__ __attribute__((aligned(16))) float sm[3 * CR * LD + 2 * CR * LS + 10 * D];
+  float* Ki = sm;               // k e^{R - G}  (column side)
+  float* Ko = Ki + CR * LD;     // k e^{G - R}  (row side), later dG
+  float* Qo = Ko + CR * LD;     // q e^{G - R}  (row side), later dKt Kt
+  float* dAs = Qo + CR * LD;
+  float* dMs = dAs + CR * LS;
+  float* Rf = dMs + CR * LS;    // [4][D] G at each sub-tile's last row
+  float* FP = Rf + 4 * D;       // [6][D] e^{R_I - R_J}
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int l16 = lane16(), g4 = lane_g4();
+  const ChunkPos p = chunk_pos(blockIdx.x, T, H, nc);
+  const int64_t item = blockIdx.x;
+  const int64_t rs = static_cast<int64_t>(H) * D;
+  const float* w = ws + item * L::WS;
+  const float* a1 = g1 + item * L::G1;
+  const float* a2 = g2 + item * L::G2;
+  const TIn* qc = q + p.row0 * D;
+  const TIn* kc = k + p.row0 * D;
+  constexpr int CT = D / 16;
+
+  if (tid < D) {
+#pragma unroll
+    for (int I = 0; I < 4; ++I) Rf[I * D + tid] = w[L::G + (16 * I + 15) * D + tid];
+    for (int I = 1; I < 4; ++I)
+      for (int J = 0; J < I; ++J)
+        FP[pair_index(I, J) * D + tid] = expf(Rf[I * D + tid] - Rf[J * D + tid]);
+  }
+  g2l<512>(dAs, LS, a2 + L::DAP, CR, CR, CR);
+  g2l<512>(dMs, LS, a2 + L::DMP, CR, CR, CR);
+  __syncthreads();
+  for (int e = tid; e < CR * D; e += 512) {
+    const int t = e / D, i = e - t * D;
+    const float G = w[L::G + e], RI = Rf[(t >> 4) * D + i];
+    const bool ok = t < p.nrow;
+    const float kv = ok ? to_f32(kc[t * rs + i]) : 0.f, qv = ok ? to_f32(qc[t * rs + i]) : 0.f;
+    const float rowf = expf(G - RI), colf = expf(RI - G);
+    Ki[t * LD + i] = kv * colf;
+    Ko[t * LD + i] = kv * rowf;
+    Qo[t * LD + i] = qv * rowf;
+  }
+  __syncthreads();
+
+  // Output tile (R, cc) of the 64 x D results; X-side sums run over column
+  // sub-tiles J <= R, Z-side sums over row sub-tiles I >= R.
+  constexpr int NTW = 4 * CT / 8;
+  f32x4_t xa[NTW], xm[NTW], za[NTW], zm[NTW];
+#pragma unroll
+  for (int x = 0; x < NTW; ++x) {
+    const int j = wave + 8 * x, R = j / CT, cc = j - R * CT;
+    xa[x] = xm[x] = za[x] = zm[x] = zero4();
+    for (int J = 0; J <= R; ++J) {
+      const float* kb = Ki + 16 * J * LD + 16 * cc;
+      const f32x4_t ta = mm<false, false>(zero4(), dAs + 16 * R * LS + 16 * J, LS, kb, LD, 16);
+      const f32x4_t tm = mm<false, false>(zero4(), dMs + 16 * R * LS + 16 * J, LS, kb, LD, 16);
+      const float f = J < R ? FP[pair_index(R, J) * D + 16 * cc + l16] : 1.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xa[x][i] += f * ta[i];
+        xm[x][i] += f * tm[i];
+      }
+    }
+    for (int I = R; I < 4; ++I) {
+      const f32x4_t ta = mm<true, false>(zero4(), dAs + 16 * I * LS + 16 * R, LS,
+                                         Ko + 16 * I * LD + 16 * cc, LD, 16);
+      const f32x4_t tm = mm<true, false>(zero4(), dMs + 16 * I * LS + 16 * R, LS,
+                                         Qo + 16 * I * LD + 16 * cc, LD, 16);
+      const float f = I > R ? FP[pair_index(I, R) * D + 16 * cc + l16] : 1.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        za[x][i] += f * ta[i];
+        zm[x][i] += f * tm[i];
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < NTW; ++x) {
+    const int j = wave + 8 * x, R = j / CT, cc = j - R * CT;
+    const int col = 16 * cc + l16;
+    const float RI = Rf[R * D + col], Gl = Rf[3 * D + col];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * R + 4 * g4 + i;
+      const int e = t * D + col;
+      const float G = w[L::G + e];
+      const float rowf = expf(G - RI), colf = expf(RI - G), eg = expf(G), et = expf(Gl - G);
+      const float XA = rowf * xa[x][i], XM = rowf * xm[x][i];
+      const float ZA = colf * za[x][i], ZM = colf * zm[x][i];
+      const bool ok = t < p.nrow;
+      const float kv = ok ? to_f32(kc[t * rs + col]) : 0.f, qv = ok ? to_f32(qc[t * rs + col]) : 0.f;
+      const float dKg = a2[L::DKG + e], dKt = a1[L::DKT + e];
+      const float dqv = scale * a1[L::DQP + e] * eg + XM;
+      const float kg = dKg * eg, kt = dKt * et;
+      const float dkv = kg + kt + XA + ZA + ZM;
+      Ko[t * LD + col] = qv * dqv + kv * (kg + XA - kt - ZA - ZM);
+      Qo[t * LD + col] = kv * kt;
+      if (ok) {
+        dq[(p.row0 + static_cast<int64_t>(t) * H) * D + col] = Elem<TIn>::from(dqv);
+        dk[(p.row0 + static_cast<int64_t>(t) * H) * D + col] = Elem<TIn>::from(dkv);
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < D) {   // dg = reverse running sum of dG, with the last row's extra terms
+    float run = a1[L::DLAM + tid] * w[L::LAM + tid];
+    for (int t = 0; t < CR; ++t) run += Qo[t * LD + tid];
+    for (int t = CR - 1; t >= 0; --t) {
+      run += Ko[t * LD + tid];
+      if (t < p.nrow) dg[(p.row0 + static_cast<int64_t>(t) * H) * D + tid] = Elem<TIn>::from(run);
+    }
+  }
+}
+
+template <int D, typename TIn>
+hipError_t launch_backward_t(const BackwardArgs& a) {
+  using L = BwdLayout<D>;
+  const int nc = (a.T + CR - 1) / CR;
+  const int64_t items = static_cast<int64_t>(a.B) * a.H * nc;
+  const int64_t per = L::WS + 2 * D * D + 2 * CR * D + L::G1 + L::G2;
+  float* buf = nullptr;
+  hipError_t err = hipMallocAsync(reinterpret_cast<void**>(&buf), items * per * sizeof(float), a.stream);
+  if (err != hipSuccess) return err;
+  float* ws = buf;
+  float* st = ws + items * L::WS;
+  float* dst = st + items * D * D;
+  float* dl = dst + items * D * D;
+  float* du = dl + items * CR * D;
+  float* g1 = du + items * CR * D;
+  float* g2 = g1 + items * L::G1;
+  const TIn* q = static_cast<const TIn*>(a.q);
+  const TIn* k = static_cast<const TIn*>(a.k);
+  const TIn* v = static_cast<const TIn*>(a.v);
+  const TIn* g = static_cast<const TIn*>(a.g);
+  const TIn* beta = static_cast<const TIn*>(a.beta);
+  const TIn* dout = static_cast<const TIn*>(a.d_out);
+  const int scan_blocks = a.B * a.H * (D / SL);
+  hipLaunchKernelGGL((bwd_prep_kernel<D, TIn>), dim3(items), dim3(256), 0, a.stream, q, k, g, beta,
+                     ws, a.T, a.H, nc, a.scale);
+  hipLaunchKernelGGL((bwd_fwd_scan_kernel<D, TIn>), dim3(scan_blocks), dim3(256), 0, a.stream, v,
+                     a.initial_state, ws, st, dl, a.T, a.H, nc);
+  hipLaunchKernelGGL((bwd_scan_kernel<D, TIn>), dim3(scan_blocks), dim3(256), 0, a.stream, dout,
+                     a.d_final_state, ws, dst, du, static_cast<TIn*>(a.dv), a.d_initial_state,
+                     a.T, a.H, nc);
+  hipLaunchKernelGGL((bwd_grad_dv_kernel<D, TIn>), dim3(items), dim3(512), 0, a.stream, v, dout,
+                     st, dst, dl, du, g1, a.T, a.H, nc);
+  hipLaunchKernelGGL((bwd_grad_nn_kernel<D, TIn>), dim3(items), dim3(256), 0, a.stream, k, beta,
+                     ws, g1, g2, static_cast<TIn*>(a.dbeta), a.T, a.H, nc, a.scale);
+  hipLaunchKernelGGL((bwd_grad_decay_kernel<D, TIn>), dim3(items), dim3(512), 0, a.stream, q, k,
+                     ws, g1, g2, static_cast<TIn*>(a.dq), static_cast<TIn*>(a.dk),
+                     static_cast<TIn*>(a.dg), a.T, a.H, nc, a.scale);
+  err = hipGetLastError();
+  const hipError_t ferr = hipFreeAsync(buf, a.stream);
+  return err != hipSuccess ? err : ferr;
+}
+
+}  // namespace
+
+hipError_t launch_backward(const BackwardArgs& a) {
+  if (a.d == 128) {
+    return a.dtype_f32 ? launch_backward_t<128, float>(a) : launch_backward_t<128, bf16_t>(a);
+  }
+  return a.dtype_f32 ? launch_backward_t<64, float>(a) : launch_backward_t<64, bf16_t>(a);
+}
+
+int64_t backward_workspace_bytes(int B, int T, int H, int d) {
+  const int64_t nc = (T + CR - 1) / CR;
+  const int64_t items = static_cast<int64_t>(B) * H * nc;
+  const int64_t per = d == 128
+      ? BwdLayout<128>::WS + 2 * 128 * 128 + 2 * CR * 128 + BwdLayout<128>::G1 + BwdLayout<128>::G2
+      : BwdLayout<64>::WS + 2 * 64 * 64 + 2 * CR * 64 + BwdLayout<64>::G1 + BwdLayout<64>::G2;
+  return items * per * static_cast<int64_t>(sizeof(float));
+}
+
+}  // namespace kda

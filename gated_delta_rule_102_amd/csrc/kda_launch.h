@@ -36,7 +36,23 @@ struct PrefillArgs {
   bool prologue = false;       // q, k, g, beta raw: normalise / gate in the kernel
 };
 
+struct BackwardArgs {
+  const void *q, *k, *v, *g, *beta;
+  const float* initial_state;   // may be null (zero)
+  const void* d_out;            // cotangent of out, same layout and dtype as v
+  const float* d_final_state;   // may be null (zero)
+  void *dq, *dk, *dv, *dg, *dbeta;
+  float* d_initial_state;       // may be null (not written)
+  int B, T, H, d;
+  float scale;
+  bool dtype_f32;
+  hipStream_t stream;
+};
+
 hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_backward(const BackwardArgs& a);
+// device scratch the backward allocates (and frees) on the stream, in bytes
+int64_t backward_workspace_bytes(int B, int T, int H, int d);
 hipError_t launch_prefill(const PrefillArgs& a);
 
 }  // namespace kda

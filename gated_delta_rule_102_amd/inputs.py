@@ -168,6 +168,18 @@ def make_varlen(lengths, H, dk, dv, dtype=torch.bfloat16, seed=0, device="cpu",
     return dict(q=q, k=k, v=v, g=g, beta=beta, initial_state=s0, cu_seqlens=cu)
 
 
+def make_cotangents(B, T, H, dk, dv, dtype=torch.bfloat16, seed=0, device="cpu",
+                    final_state=True):
+    """Cotangents for the backward: grad_out [B,T,H,dv] ~ N(0,1) in dtype and
+    grad_final_state [B,H,dk,dv] ~ N(0,1) fp32 (or None)."""
+    gen = _gen(device, seed)
+    d_out = torch.randn((B, T, H, dv), generator=gen, device=device, dtype=torch.float32)
+    d_fin = None
+    if final_state:
+        d_fin = torch.randn((B, H, dk, dv), generator=gen, device=device, dtype=torch.float32)
+    return dict(grad_out=d_out.to(dtype), grad_final_state=d_fin)
+
+
 def make_decode(steps, B, H, dk, dv, dtype=torch.bfloat16, seed=0, device="cpu"):
     """Decode inputs: per-step q, k, g [steps,B,H,dk]; v [steps,B,H,dv];
     beta [steps,B,H]; state [B,H,dk,dv] fp32 ~ 0.1 N(0,1)."""

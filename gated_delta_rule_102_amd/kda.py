@@ -21,7 +21,7 @@ KDA_BF16, KDA_F32 = 0, 1
 _lib = None
 
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd", "kda_chunk_fwd_prologue",
-           "kda_chunk_fwd_snapshots", "kda_chunk_fwd_varlen", "kda_decode_step")
+           "kda_chunk_fwd_snapshots", "kda_chunk_fwd_varlen", "kda_decode_step", "kda_chunk_bwd")
 
 
 class KDAError(RuntimeError):
@@ -59,6 +59,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd_varlen.restype = i32
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp]
     lib.kda_decode_step.restype = i32
+    lib.kda_chunk_bwd.argtypes = [vp] * 14 + [i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.kda_chunk_bwd.restype = i32
     _lib = lib
     return lib
 
@@ -262,9 +264,37 @@ def kda_decode_step(q, k, v, g, beta, state, scale=None, out=None):
     return out
 
 
+def kda_chunk_bwd(q, k, v, g, beta, grad_out, scale=None, initial_state=None,
+                  grad_final_state=None, need_initial_state_grad=True):
+    """Gradients of sum(grad_out * out) + sum(grad_final_state * final_state) for
+    kda_chunk_fwd's inputs (same shapes and dtype).  Returns ``(grad_q, grad_k,
+    grad_v, grad_g, grad_beta, grad_initial_state or None)``; the initial-state
+    gradient is fp32 [B,H,dk,dv]."""
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dtype, device = q.dtype, q.device
+    _check(dict(q=q, k=k, v=v, g=g, beta=beta, grad_out=grad_out), dtype, device)
+    if k.shape != q.shape or g.shape != q.shape or v.shape[:3] != q.shape[:3] \
+            or beta.shape != q.shape[:3] or grad_out.shape != v.shape:
+        raise ValueError("shape mismatch among q, k, v, g, beta, grad_out")
+    _check_state("initial_state", initial_state, (B, H, dk, dv), device)
+    _check_state("grad_final_state", grad_final_state, (B, H, dk, dv), device)
+    grads = [torch.empty_like(x) for x in (q, k, v, g, beta)]
+    ds0 = torch.empty((B, H, dk, dv), dtype=torch.float32, device=device) \
+        if need_initial_state_grad else None
+    scale = 1.0 / math.sqrt(dk) if scale is None else float(scale)
+    rc = lib.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                           _ptr(grad_out), _ptr(grad_final_state), *(_ptr(x) for x in grads),
+                           _ptr(ds0), B, T, H, dk, dv, scale, _dtype_code(q), _stream(q))
+    _raise("kda_chunk_bwd", rc)
+    return (*grads, ds0)
+
+
 # short aliases
 chunk_fwd = kda_chunk_fwd
 chunk_fwd_varlen = kda_chunk_fwd_varlen
 chunk_fwd_snapshots = kda_chunk_fwd_snapshots
 chunk_fwd_prologue = kda_chunk_fwd_prologue
 decode_step = kda_decode_step
+chunk_bwd = kda_chunk_bwd

@@ -162,6 +162,35 @@ int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void
                          hipStream_t stream);
 
 /*
+ * Backward pass of kda_chunk_fwd (fixed length): the gradients of
+ *     L = sum over tokens of <grad_out, out> + <grad_final_state, final_state>
+ * with respect to q, k, v, g, beta and initial_state.  The pages train KDA at up
+ * to 1M tokens of context (best.xiaohu.ai "Kimi K3 tech report", context
+ * curriculum) but print no backward; the gradients are the plain derivatives of
+ * the recurrence above.
+ *
+ *  q, k, v, g, beta, initial_state, B, T, H, dk, dv, scale, dtype: the forward
+ *                      call's arguments (initial_state NULL = zero).
+ *  grad_out            [B, T, H, dv] (dtype), required.
+ *  grad_final_state    [B, H, dk, dv] fp32 or NULL (zero).
+ *  grad_q, grad_k, grad_g [B, T, H, dk]; grad_v [B, T, H, dv]; grad_beta [B, T, H]
+ *                      (dtype), required, fully overwritten.
+ *  grad_initial_state  [B, H, dk, dv] fp32 or NULL (not computed).
+ * dk == dv in {64, 128} for both dtypes.  Every pointer needs only its element
+ * alignment.  The forward is recomputed inside the call (nothing is kept from
+ * kda_chunk_fwd).  All arithmetic is fp32 (fp32 matrix cores), also for bf16
+ * inputs.  The call allocates a workspace with hipMallocAsync on `stream` and
+ * frees it on the same stream: 607,232 bytes per 64-token chunk per head at
+ * d = 128 (344,576 at d = 64); an allocation failure returns KDA_ERR_HIP.
+ * Outputs must not alias inputs.
+ */
+int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                  const float* initial_state, const void* grad_out,
+                  const float* grad_final_state, void* grad_q, void* grad_k, void* grad_v,
+                  void* grad_g, void* grad_beta, float* grad_initial_state, int B, int T, int H,
+                  int dk, int dv, float scale, int dtype, hipStream_t stream);
+
+/*
  * One decode token for B sequences, updating `state` in place.
  *
  *  q, k, g  [B, H, dk] (dtype);  v, out [B, H, dv] (dtype);  beta [B, H] (dtype)

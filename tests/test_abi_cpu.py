@@ -33,7 +33,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "kda_abi_version", "kda_status_string", "kda_chunk_fwd", "kda_chunk_fwd_prologue",
-        "kda_chunk_fwd_snapshots", "kda_chunk_fwd_varlen", "kda_decode_step"])
+        "kda_chunk_fwd_snapshots", "kda_chunk_fwd_varlen", "kda_decode_step", "kda_chunk_bwd"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -95,6 +95,25 @@ def test_argument_checks_precede_any_device_call(lib):
         assert s(p, p, p, p, p, None, p, None, p, bad, 1, 64, 1, 128, 128, 0.1, 0, None) == -2
     assert s(p, p, p, p, p, None, p, None, mis, 512, 1, 64, 1, 128, 128, 0.1, 0, None) == -5
     assert s(p, p, p, p, p, None, p, None, p, 512, 1, 64, 1, 128, 128, 0.1, 0, None) in (-6, -7)
+    bw = lib.kda_chunk_bwd
+    bw.argtypes = [vp] * 14 + [i32] * 5 + [f32, i32, vp]
+    bw.restype = i32
+    ok = [p, p, p, p, p, None, p, None, p, p, p, p, p, None]
+    assert bw(*ok, 1, 64, 1, 128, 128, 0.1, 0, None) in (-6, -7)
+    assert bw(*ok, 1, 64, 1, 128, 128, 0.1, 1, None) in (-6, -7)    # fp32 at d = 128 is allowed
+    for i in (0, 1, 2, 3, 4, 6, 8, 9, 10, 11, 12):                    # every required pointer
+        args = list(ok)
+        args[i] = None
+        assert bw(*args, 1, 64, 1, 128, 128, 0.1, 0, None) == -1
+    assert bw(*ok, 1, 0, 1, 128, 128, 0.1, 0, None) == -2
+    assert bw(*ok, 1, 64, 1, 64, 128, 0.1, 0, None) == -3
+    assert bw(*ok, 1, 64, 1, 128, 128, 0.1, 3, None) == -4
+    args = list(ok)
+    args[8] = vp(4097)                                                 # grad_q misaligned
+    assert bw(*args, 1, 64, 1, 128, 128, 0.1, 0, None) == -5
+    args = list(ok)
+    args[13] = vp(4098)                                                # fp32 state misaligned
+    assert bw(*args, 1, 64, 1, 128, 128, 0.1, 0, None) == -5
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

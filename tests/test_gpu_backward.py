@@ -1,0 +1,123 @@
+"""GPU parity of the backward pass (kda_chunk_bwd, through the C ABI) against the
+oracle's fp64 gradients (reverse-mode autodiff of the recurrence on the CPU).
+
+Tolerances for gradients (the kernels compute in fp32; bf16 results carry one
+bf16 rounding): rel-L2 <= 1e-2 and max-abs <= 2e-2 * max|reference| for bf16
+inputs; rel-L2 <= 1e-4 for fp32 inputs.  The max-abs bound is relative to the
+tensor's largest entry because gradient magnitudes grow with the chunk length
+(dg sums over the tokens that follow) where the forward's outputs stay O(1).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_102_amd import inputs as kin
+from oracle import backward_oracle
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "ds0")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible MI355X")
+    from gated_delta_rule_102_amd import kda
+    kda.load_library()
+    torch.cuda.set_device(0)
+    yield
+
+
+def grad_close(name, got, ref, dtype):
+    got = got.detach().double().cpu().numpy() if isinstance(got, torch.Tensor) else got
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    diff = got - ref
+    nref = np.linalg.norm(ref)
+    rel = np.linalg.norm(diff) / (nref if nref > 0 else 1.0)
+    mx = float(np.max(np.abs(diff))) if diff.size else 0.0
+    top = float(np.max(np.abs(ref))) if ref.size else 0.0
+    msg = f"{name}: rel_l2={rel:.3e} max_abs={mx:.3e} (max|ref|={top:.3e})"
+    if dtype == torch.bfloat16:
+        assert rel <= 1e-2 and mx <= 2e-2 * max(top, 1e-30), msg
+    else:
+        assert rel <= 1e-4, msg
+    return rel
+
+
+def run_gpu(d, c, scale, need_ds0=True):
+    from gated_delta_rule_102_amd import kda
+    dev = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in {**d, **c}.items()}
+    out = kda.kda_chunk_bwd(dev["q"], dev["k"], dev["v"], dev["g"], dev["beta"], dev["grad_out"],
+                            scale, dev.get("initial_state"), dev.get("grad_final_state"),
+                            need_initial_state_grad=need_ds0)
+    torch.cuda.synchronize()
+    return dict(zip(NAMES, out))
+
+
+def run_oracle(d, c, scale):
+    return backward_oracle(d["q"], d["k"], d["v"], d["g"], d["beta"], scale, c["grad_out"],
+                           d.get("initial_state"), c.get("grad_final_state"))
+
+
+def check(d, c, scale, dtype, names=NAMES):
+    got = run_gpu(d, c, scale)
+    ref = run_oracle(d, c, scale)
+    rels = {}
+    for n in names:
+        if n == "ds0" and got[n] is None:
+            continue
+        rels[n] = grad_close(n, got[n], ref[n], dtype)
+    print({n: f"{r:.2e}" for n, r in rels.items()}, flush=True)
+    return got, ref
+
+
+@pytest.mark.parametrize("T", [1, 64, 65, 150])
+def test_backward_bf16_d128(T):
+    d = kin.make_prefill(2, T, 2, 128, 128, dtype=torch.bfloat16, seed=300 + T, nonzero_state=True)
+    c = kin.make_cotangents(2, T, 2, 128, 128, dtype=torch.bfloat16, seed=400 + T)
+    check(d, c, 1.0 / math.sqrt(128), torch.bfloat16)
+
+
+def test_backward_bf16_d64_several_chunks():
+    d = kin.make_prefill(1, 300, 3, 64, 64, dtype=torch.bfloat16, seed=310, nonzero_state=True)
+    c = kin.make_cotangents(1, 300, 3, 64, 64, dtype=torch.bfloat16, seed=410)
+    check(d, c, 0.125, torch.bfloat16)
+
+
+@pytest.mark.parametrize("D,T", [(64, 130), (128, 100)])
+def test_backward_fp32(D, T):
+    d = kin.make_prefill(2, T, 2, D, D, dtype=torch.float32, seed=320 + D, nonzero_state=True)
+    c = kin.make_cotangents(2, T, 2, D, D, dtype=torch.float32, seed=420 + D)
+    check(d, c, 1.0 / math.sqrt(D), torch.float32)
+
+
+def test_backward_without_states():
+    """initial_state, grad_final_state and the initial-state gradient all absent."""
+    d = kin.make_prefill(1, 200, 2, 128, 128, dtype=torch.bfloat16, seed=330, nonzero_state=False)
+    c = kin.make_cotangents(1, 200, 2, 128, 128, dtype=torch.bfloat16, seed=430, final_state=False)
+    got = run_gpu(d, c, 0.088, need_ds0=False)
+    assert got["ds0"] is None
+    ref = run_oracle(d, c, 0.088)
+    for n in NAMES[:5]:
+        grad_close(n, got[n], ref[n], torch.bfloat16)
+
+
+def test_backward_decay_floor():
+    """Every log-decay at the -5 floor in half the heads (strongest forgetting)."""
+    d = kin.make_prefill(1, 160, 2, 128, 128, dtype=torch.bfloat16, seed=340, nonzero_state=True)
+    d["g"][:, :, 0] = -5.0
+    c = kin.make_cotangents(1, 160, 2, 128, 128, dtype=torch.bfloat16, seed=440)
+    check(d, c, 1.0 / math.sqrt(128), torch.bfloat16)
+
+
+def test_backward_deterministic():
+    d = kin.make_prefill(1, 130, 2, 128, 128, dtype=torch.bfloat16, seed=350, nonzero_state=True)
+    c = kin.make_cotangents(1, 130, 2, 128, 128, dtype=torch.bfloat16, seed=450)
+    a = run_gpu(d, c, 0.1)
+    b = run_gpu(d, c, 0.1)
+    for n in NAMES:
+        assert torch.equal(a[n], b[n]), n
