@@ -113,36 +113,94 @@ __device__ __forceinline__ f32x4_t get(const float* src, int ld) {
   return v;
 }
 
-// rows x cols fp32 (cols % 4 == 0, both sides 16-byte aligned) global -> LDS
-template <int NT>
-__device__ __forceinline__ void g2l(float* dst, int lld, const float* src, int64_t gld, int rows,
-                                    int cols) {
-  const int c4 = cols / 4;
-  for (int e = threadIdx.x; e < rows * c4; e += NT) {
-    const int r = e / c4, c = (e - r * c4) * 4;
-    *reinterpret_cast<float4*>(dst + r * lld + c) =
-        *reinterpret_cast<const float4*>(src + r * gld + c);
+// Pins a loaded value: the empty asm consumes and redefines it, so the load
+// that produced it is issued before this point and cannot be sunk next to its
+// use.  Pinning a group of tile loads keeps all of them in flight together.
+template <typename V>
+__device__ __forceinline__ void pin(V& v) { asm volatile("" : "+v"(v)); }
+
+// ROWS x COLS fp32 global -> LDS (COLS % 4 == 0, both sides 16-byte aligned).
+// load() issues every global load of the tile before store() writes LDS, so a
+// thread has all its loads in flight at once; several tiles can be loaded
+// before any of them is stored.
+template <int NT, int ROWS, int COLS>
+struct GTile {
+  static constexpr int C4 = COLS / 4, N = ROWS * C4, PER = (N + NT - 1) / NT;
+  f32x4_t r[PER];
+  __device__ __forceinline__ void load(const float* src, int64_t gld) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = static_cast<int>(threadIdx.x) + j * NT;
+      if (N % NT == 0 || e < N) {
+        const int rr = e / C4, c = (e - rr * C4) * 4;
+        r[j] = *reinterpret_cast<const f32x4_t*>(src + rr * gld + c);
+      }
+    }
+  }
+  __device__ __forceinline__ void pin_all() {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) pin(r[j]);
+  }
+  __device__ __forceinline__ void store(float* dst, int lld) const {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = static_cast<int>(threadIdx.x) + j * NT;
+      if (N % NT == 0 || e < N) {
+        const int rr = e / C4, c = (e - rr * C4) * 4;
+        *reinterpret_cast<f32x4_t*>(dst + rr * lld + c) = r[j];
+      }
+    }
+  }
+};
+template <int NT, int ROWS, int COLS>
+__device__ __forceinline__ void g2l(float* dst, int lld, const float* src, int64_t gld) {
+  GTile<NT, ROWS, COLS> t;
+  t.load(src, gld);
+  t.pin_all();
+  t.store(dst, lld);
+}
+template <int NT, int ROWS, int COLS>
+__device__ __forceinline__ void l2g(float* dst, int64_t gld, const float* src, int lld) {
+  constexpr int C4 = COLS / 4, N = ROWS * C4;
+#pragma unroll
+  for (int j = 0; j < (N + NT - 1) / NT; ++j) {
+    const int e = static_cast<int>(threadIdx.x) + j * NT;
+    if (N % NT == 0 || e < N) {
+      const int r = e / C4, c = (e - r * C4) * 4;
+      *reinterpret_cast<float4*>(dst + r * gld + c) = *reinterpret_cast<const float4*>(src + r * lld + c);
+    }
   }
 }
-template <int NT>
-__device__ __forceinline__ void l2g(float* dst, int64_t gld, const float* src, int lld, int rows,
-                                    int cols) {
-  const int c4 = cols / 4;
-  for (int e = threadIdx.x; e < rows * c4; e += NT) {
-    const int r = e / c4, c = (e - r * c4) * 4;
-    *reinterpret_cast<float4*>(dst + r * gld + c) =
-        *reinterpret_cast<const float4*>(src + r * lld + c);
+// 64 x COLS input rows (bf16 or fp32) -> fp32 in LDS; rows >= nrow read as zero.
+// The row index is clamped so every load is unconditional (a load under a
+// branch is waited for inside the branch, which serialises the loads).
+template <int NT, int COLS, typename TIn>
+struct ITile {
+  static constexpr int N = CR * COLS, PER = N / NT;
+  static_assert(N % NT == 0, "tile split");
+  float r[PER];
+  __device__ __forceinline__ void load(const TIn* src, int64_t row_stride, int nrow) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = static_cast<int>(threadIdx.x) + j * NT;
+      const int rr = e / COLS, c = e - rr * COLS;
+      const float x = to_f32(src[min(rr, nrow - 1) * row_stride + c]);
+      r[j] = rr < nrow ? x : 0.f;
+    }
   }
-}
-// 64 x cols input rows (bf16 or fp32) -> fp32 LDS, rows >= nrow read as zero
-template <int NT, typename TIn>
-__device__ __forceinline__ void in2l(float* dst, int lld, const TIn* src, int64_t row_stride,
-                                     int nrow, int cols) {
-  for (int e = threadIdx.x; e < CR * cols; e += NT) {
-    const int r = e / cols, c = e - r * cols;
-    dst[r * lld + c] = r < nrow ? to_f32(src[r * row_stride + c]) : 0.f;
+  __device__ __forceinline__ void pin_all() {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) pin(r[j]);
   }
-}
+  __device__ __forceinline__ void store(float* dst, int lld) const {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = static_cast<int>(threadIdx.x) + j * NT;
+      const int rr = e / COLS, c = e - rr * COLS;
+      dst[rr * lld + c] = r[j];
+    }
+  }
+};
 
 // sub-tile pairs J < I of a 64-row chunk -> 0..5
 __device__ __forceinline__ int pair_index(int I, int J) { return I * (I - 1) / 2 + J; }
@@ -191,12 +249,21 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const TIn* __restrict__ q
   const TIn* gc = g + p.row0 * D;
   float* w = ws + static_cast<int64_t>(blockIdx.x) * L::WS;
 
-  for (int e = tid; e < 3 * CR * LS; e += 256) S0[e] = 0.f;
-  if (tid < CR) BT[tid] = tid < p.nrow ? to_f32(beta[p.row0 + static_cast<int64_t>(tid) * H]) : 0.f;
-  if (tid < D) {   // running sum of g down the chunk (padding rows add 0)
+  {
+    ITile<256, D, TIn> gt;
+    gt.load(gc, rs, p.nrow);
+    gt.pin_all();
+    for (int e = tid; e < 3 * CR * LS; e += 256) S0[e] = 0.f;
+    const float bt = to_f32(beta[p.row0 + static_cast<int64_t>(min(tid & (CR - 1), p.nrow - 1)) * H]);
+    if (tid < CR) BT[tid] = tid < p.nrow ? bt : 0.f;
+    gt.store(R0, LD);
+  }
+  __syncthreads();
+  if (tid < D) {   // running sum of g down the chunk (padding rows hold 0)
     float acc = 0.f;
+#pragma unroll 8
     for (int t = 0; t < CR; ++t) {
-      acc += t < p.nrow ? to_f32(gc[t * rs + tid]) : 0.f;
+      acc += R0[t * LD + tid];
       R0[t * LD + tid] = acc;
     }
   }
@@ -209,14 +276,20 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const TIn* __restrict__ q
             expf(R0[(16 * I + 15) * LD + tid] - R0[(16 * J + 15) * LD + tid]);
     w[L::LAM + tid] = expf(R0[(CR - 1) * LD + tid]);
   }
-  for (int e = tid; e < CR * D; e += 256) {
-    const int t = e / D, i = e - t * D;
-    const float G = R0[t * LD + i], RI = R0[(t | 15) * LD + i], Gl = R0[(CR - 1) * LD + i];
-    const float kv = t < p.nrow ? to_f32(kc[t * rs + i]) : 0.f;
-    R1[t * LD + i] = kv * expf(G - RI);
-    R2[t * LD + i] = kv * expf(RI - G);
-    w[L::KT + e] = kv * expf(Gl - G);
-    w[L::G + e] = G;
+  {
+    ITile<256, D, TIn> kt;
+    kt.load(kc, rs, p.nrow);
+    kt.pin_all();
+#pragma unroll
+    for (int j = 0; j < kt.PER; ++j) {
+      const int e = tid + j * 256, t = e / D, i = e - t * D;
+      const float G = R0[t * LD + i], RI = R0[(t | 15) * LD + i], Gl = R0[(CR - 1) * LD + i];
+      const float kv = kt.r[j];
+      R1[t * LD + i] = kv * expf(G - RI);
+      R2[t * LD + i] = kv * expf(RI - G);
+      w[L::KT + e] = kv * expf(Gl - G);
+      w[L::G + e] = G;
+    }
   }
   __syncthreads();
 
@@ -242,17 +315,22 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const TIn* __restrict__ q
   };
   pair_gram(S0, true);
   __syncthreads();
-  for (int e = tid; e < CR * D; e += 256) {   // q rowf into R1
-    const int t = e / D, i = e - t * D;
-    const float G = R0[t * LD + i], RI = R0[(t | 15) * LD + i];
-    const float qv = t < p.nrow ? to_f32(qc[t * rs + i]) : 0.f;
-    R1[t * LD + i] = qv * expf(G - RI);
+  {   // q rowf into R1
+    ITile<256, D, TIn> qt;
+    qt.load(qc, rs, p.nrow);
+    qt.pin_all();
+#pragma unroll
+    for (int j = 0; j < qt.PER; ++j) {
+      const int e = tid + j * 256, t = e / D, i = e - t * D;
+      const float G = R0[t * LD + i], RI = R0[(t | 15) * LD + i];
+      R1[t * LD + i] = qt.r[j] * expf(G - RI);
+    }
   }
   __syncthreads();
   pair_gram(S1, false);
   __syncthreads();
-  l2g<256>(w + L::AP, CR, S0, LS, CR, CR);
-  l2g<256>(w + L::MP, CR, S1, LS, CR, CR);
+  l2g<256, CR, CR>(w + L::AP, CR, S0, LS);
+  l2g<256, CR, CR>(w + L::MP, CR, S1, LS);
 
   // Ti = (I + Diag(beta) A')^-1: diagonal 16 x 16 blocks by substitution (one
   // column per lane), then the blocks below them level by level:
@@ -294,12 +372,19 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const TIn* __restrict__ q
     w[L::TI + e] = ti;
     w[L::TB + e] = ti * BT[s];
   }
-  for (int e = tid; e < CR * D; e += 256) {   // k e^G into R1, scale q e^G into R2
-    const int t = e / D, i = e - t * D;
-    const float eg = expf(R0[t * LD + i]);
-    const bool ok = t < p.nrow;
-    R1[t * LD + i] = ok ? to_f32(kc[t * rs + i]) * eg : 0.f;
-    R2[t * LD + i] = ok ? scale * to_f32(qc[t * rs + i]) * eg : 0.f;
+  {   // k e^G into R1, scale q e^G into R2
+    ITile<256, D, TIn> kt, qt;
+    kt.load(kc, rs, p.nrow);
+    qt.load(qc, rs, p.nrow);
+    kt.pin_all();
+    qt.pin_all();
+#pragma unroll
+    for (int j = 0; j < kt.PER; ++j) {
+      const int e = tid + j * 256, t = e / D, i = e - t * D;
+      const float eg = expf(R0[t * LD + i]);
+      R1[t * LD + i] = kt.r[j] * eg;
+      R2[t * LD + i] = scale * qt.r[j] * eg;
+    }
   }
   __syncthreads();
 
@@ -376,12 +461,27 @@ __global__ __launch_bounds__(256) void bwd_fwd_scan_kernel(const TIn* __restrict
     const int64_t item = static_cast<int64_t>(bh) * nc + c;
     const float* w = ws + item * L::WS;
     const int nrow = min(CR, T - c * CR);
-    g2l<256>(TBs, LS, w + L::TB, CR, CR, CR);
-    g2l<256>(Ws, LD, w + L::W, D, CR, D);
-    g2l<256>(KTs, LD, w + L::KT, D, CR, D);
-    if (tid < D) Lm[tid] = w[L::LAM + tid];
     const int64_t row0 = (static_cast<int64_t>(b) * T + static_cast<int64_t>(c) * CR) * H + h;
-    in2l<256>(Vs, LV, v + row0 * D + c0, static_cast<int64_t>(H) * D, nrow, SL);
+    {
+      GTile<256, CR, CR> t_tb;
+      GTile<256, CR, D> t_w, t_kt;
+      ITile<256, SL, TIn> t_v;
+      t_tb.load(w + L::TB, CR);
+      t_w.load(w + L::W, D);
+      t_kt.load(w + L::KT, D);
+      t_v.load(v + row0 * D + c0, static_cast<int64_t>(H) * D, nrow);
+      float lm = w[L::LAM + (tid & (D - 1))];
+      t_tb.pin_all();
+      t_w.pin_all();
+      t_kt.pin_all();
+      t_v.pin_all();
+      pin(lm);
+      t_tb.store(TBs, LS);
+      t_w.store(Ws, LD);
+      t_kt.store(KTs, LD);
+      t_v.store(Vs, LV);
+      if (tid < D) Lm[tid] = lm;
+    }
 #pragma unroll
     for (int x = 0; x < ST::NTW; ++x) {
       const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
@@ -453,12 +553,29 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(const TIn* __restrict__ d
     const float* w = ws + item * L::WS;
     const int nrow = min(CR, T - c * CR);
     const int64_t row0 = (static_cast<int64_t>(b) * T + static_cast<int64_t>(c) * CR) * H + h;
-    g2l<256>(KQs, LD, w + L::KT, D, CR, D);
-    g2l<256>(Ws, LD, w + L::W, D, CR, D);
-    g2l<256>(Ps, LS, w + L::PP, CR, CR, CR);
-    g2l<256>(TBs, LS, w + L::TB, CR, CR, CR);
-    if (tid < D) Lm[tid] = w[L::LAM + tid];
-    in2l<256>(dOs, LV, dout + row0 * D + c0, rs, nrow, SL);
+    {
+      GTile<256, CR, D> t_kt, t_w;
+      GTile<256, CR, CR> t_p, t_tb;
+      ITile<256, SL, TIn> t_do;
+      t_kt.load(w + L::KT, D);
+      t_w.load(w + L::W, D);
+      t_p.load(w + L::PP, CR);
+      t_tb.load(w + L::TB, CR);
+      t_do.load(dout + row0 * D + c0, rs, nrow);
+      float lm = w[L::LAM + (tid & (D - 1))];
+      t_kt.pin_all();
+      t_w.pin_all();
+      t_p.pin_all();
+      t_tb.pin_all();
+      t_do.pin_all();
+      pin(lm);
+      t_kt.store(KQs, LD);
+      t_w.store(Ws, LD);
+      t_p.store(Ps, LS);
+      t_tb.store(TBs, LS);
+      t_do.store(dOs, LV);
+      if (tid < D) Lm[tid] = lm;
+    }
 #pragma unroll
     for (int x = 0; x < ST::NTW; ++x) {
       const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
@@ -474,7 +591,7 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(const TIn* __restrict__ d
       put(du + item * CR * D + 16 * rt * D + c0 + 16 * ct, D, u);
     }
     __syncthreads();
-    g2l<256>(KQs, LD, w + L::QP, D, CR, D);
+    g2l<256, CR, D>(KQs, LD, w + L::QP, D);
 #pragma unroll
     for (int y = 0; y < 2; ++y) {   // dV = P^T dO + Tb^T dU
       const int j = wave * 2 + y, rt = j >> 1, ct = j & 1;
@@ -542,12 +659,29 @@ __global__ __launch_bounds__(512) void bwd_grad_dv_kernel(const TIn* __restrict_
   for (int x = 0; x < NTW; ++x) acc[x] = zero4();
   float dlam = 0.f;
   for (int c0 = 0; c0 < D; c0 += SL) {
-    g2l<512>(Ss, LV, st + item * D * D + c0, D, D, SL);
-    g2l<512>(dSs, LV, dst + item * D * D + c0, D, D, SL);
-    g2l<512>(Dls, LV, dl + item * CR * D + c0, D, CR, SL);
-    g2l<512>(dUs, LV, du + item * CR * D + c0, D, CR, SL);
-    in2l<512>(dOs, LV, dout + p.row0 * D + c0, rs, p.nrow, SL);
-    in2l<512>(Vs, LV, v + p.row0 * D + c0, rs, p.nrow, SL);
+    {
+      GTile<512, D, SL> t_s, t_ds;
+      GTile<512, CR, SL> t_dl, t_du;
+      ITile<512, SL, TIn> t_do, t_v;
+      t_s.load(st + item * D * D + c0, D);
+      t_ds.load(dst + item * D * D + c0, D);
+      t_dl.load(dl + item * CR * D + c0, D);
+      t_du.load(du + item * CR * D + c0, D);
+      t_do.load(dout + p.row0 * D + c0, rs, p.nrow);
+      t_v.load(v + p.row0 * D + c0, rs, p.nrow);
+      t_s.pin_all();
+      t_ds.pin_all();
+      t_dl.pin_all();
+      t_du.pin_all();
+      t_do.pin_all();
+      t_v.pin_all();
+      t_s.store(Ss, LV);
+      t_ds.store(dSs, LV);
+      t_dl.store(Dls, LV);
+      t_du.store(dUs, LV);
+      t_do.store(dOs, LV);
+      t_v.store(Vs, LV);
+    }
     __syncthreads();
 #pragma unroll
     for (int x = 0; x < NTW; ++x) {
@@ -635,15 +769,43 @@ __global__ __launch_bounds__(256) void bwd_grad_nn_kernel(const TIn* __restrict_
   const TIn* kc = k + p.row0 * D;
   constexpr int CT = D / 16;
 
-  for (int e = tid; e < CR * D; e += 256) {
-    const int t = e / D, i = e - t * D;
-    Kg[t * LD + i] = t < p.nrow ? to_f32(kc[t * rs + i]) * expf(w[L::G + e]) : 0.f;
+  {
+    GTile<256, CR, D> t_g, t_dq;
+    GTile<256, CR, CR> t_p;
+    t_g.load(w + L::G, D);
+    t_dq.load(a1 + L::DQP, D);
+    t_p.load(w + L::PP, CR);
+    float bt0 = to_f32(beta[p.row0 + static_cast<int64_t>(min(tid & (CR - 1), p.nrow - 1)) * H]);
+    t_g.pin_all();
+    t_dq.pin_all();
+    t_p.pin_all();
+    pin(bt0);
+    t_g.store(Kg, LD);
+    t_dq.store(dQ, LD);
+    t_p.store(Ps, LS);
+    if (tid < CR) BT[tid] = tid < p.nrow ? bt0 : 0.f;
   }
-  g2l<256>(dQ, LD, a1 + L::DQP, D, CR, D);
-  g2l<256>(dW, LD, a1 + L::DW, D, CR, D);
-  g2l<256>(Ps, LS, w + L::PP, CR, CR, CR);
-  g2l<256>(TBs, LS, w + L::TB, CR, CR, CR);
-  if (tid < CR) BT[tid] = tid < p.nrow ? to_f32(beta[p.row0 + static_cast<int64_t>(tid) * H]) : 0.f;
+  {
+    GTile<256, CR, D> t_dw;
+    GTile<256, CR, CR> t_tb;
+    t_dw.load(a1 + L::DW, D);
+    t_tb.load(w + L::TB, CR);
+    t_dw.pin_all();
+    t_tb.pin_all();
+    t_dw.store(dW, LD);
+    t_tb.store(TBs, LS);
+  }
+  __syncthreads();
+  {   // Kg = k e^G in place of G (each element read and written by one thread)
+    ITile<256, D, TIn> kt;
+    kt.load(kc, rs, p.nrow);
+    kt.pin_all();
+#pragma unroll
+    for (int j = 0; j < kt.PER; ++j) {
+      const int e = tid + j * 256, t = e / D, i = e - t * D;
+      Kg[t * LD + i] = kt.r[j] * expf(Kg[t * LD + i]);
+    }
+  }
   __syncthreads();
 
   // dP_tot = dP - dQ' Kg^T and dTb_part = dTb + dW Kg^T (tiles wave + 4x)
@@ -677,8 +839,13 @@ __global__ __launch_bounds__(256) void bwd_grad_nn_kernel(const TIn* __restrict_
     const int j = wave + 4 * x, rt = j >> 2, ct = j & 3;
     put(B0 + 16 * rt * LS + 16 * ct, LS, dPt[x]);
   }
-  g2l<256>(B1, LS, w + L::MP, CR, CR, CR);
-  g2l<256>(B2, LS, w + L::TI, CR, CR, CR);
+  {
+    GTile<256, CR, CR> t_m, t_ti;
+    t_m.load(w + L::MP, CR);
+    t_ti.load(w + L::TI, CR);
+    t_m.store(B1, LS);
+    t_ti.store(B2, LS);
+  }
   __syncthreads();
   // dTb_tot = dTb_part + scale M'^T dP_tot;  dM' = scale (dP_tot Tb^T) on s <= t
 #pragma unroll
@@ -783,18 +950,35 @@ __global__ __launch_bounds__(512) void bwd_grad_decay_kernel(const TIn* __restri
       for (int J = 0; J < I; ++J)
         FP[pair_index(I, J) * D + tid] = expf(Rf[I * D + tid] - Rf[J * D + tid]);
   }
-  g2l<512>(dAs, LS, a2 + L::DAP, CR, CR, CR);
-  g2l<512>(dMs, LS, a2 + L::DMP, CR, CR, CR);
+  {
+    GTile<512, CR, CR> t_da, t_dm;
+    GTile<512, CR, D> t_g;
+    t_da.load(a2 + L::DAP, CR);
+    t_dm.load(a2 + L::DMP, CR);
+    t_g.load(w + L::G, D);
+    t_da.pin_all();
+    t_dm.pin_all();
+    t_g.pin_all();
+    t_da.store(dAs, LS);
+    t_dm.store(dMs, LS);
+    t_g.store(Qo, LD);
+  }
   __syncthreads();
-  for (int e = tid; e < CR * D; e += 512) {
-    const int t = e / D, i = e - t * D;
-    const float G = w[L::G + e], RI = Rf[(t >> 4) * D + i];
-    const bool ok = t < p.nrow;
-    const float kv = ok ? to_f32(kc[t * rs + i]) : 0.f, qv = ok ? to_f32(qc[t * rs + i]) : 0.f;
-    const float rowf = expf(G - RI), colf = expf(RI - G);
-    Ki[t * LD + i] = kv * colf;
-    Ko[t * LD + i] = kv * rowf;
-    Qo[t * LD + i] = qv * rowf;
+  {   // G (parked in Qo) -> k colf, k rowf, q rowf; each element read and written by one thread
+    ITile<512, D, TIn> kt, qt;
+    kt.load(kc, rs, p.nrow);
+    qt.load(qc, rs, p.nrow);
+    kt.pin_all();
+    qt.pin_all();
+#pragma unroll
+    for (int j = 0; j < kt.PER; ++j) {
+      const int e = tid + j * 512, t = e / D, i = e - t * D;
+      const float G = Qo[t * LD + i], RI = Rf[(t >> 4) * D + i];
+      const float rowf = expf(G - RI), colf = expf(RI - G);
+      Ki[t * LD + i] = kt.r[j] * colf;
+      Ko[t * LD + i] = kt.r[j] * rowf;
+      Qo[t * LD + i] = qt.r[j] * rowf;
+    }
   }
   __syncthreads();
 
@@ -845,7 +1029,9 @@ __global__ __launch_bounds__(512) void bwd_grad_decay_kernel(const TIn* __restri
       const float XA = rowf * xa[x][i], XM = rowf * xm[x][i];
       const float ZA = colf * za[x][i], ZM = colf * zm[x][i];
       const bool ok = t < p.nrow;
-      const float kv = ok ? to_f32(kc[t * rs + col]) : 0.f, qv = ok ? to_f32(qc[t * rs + col]) : 0.f;
+      const int tc = min(t, p.nrow - 1);
+      const float kraw = to_f32(kc[tc * rs + col]), qraw = to_f32(qc[tc * rs + col]);
+      const float kv = ok ? kraw : 0.f, qv = ok ? qraw : 0.f;
       const float dKg = a2[L::DKG + e], dKt = a1[L::DKT + e];
       const float dqv = scale * a1[L::DQP + e] * eg + XM;
       const float kg = dKg * eg, kt = dKt * et;
