@@ -14,7 +14,9 @@ consecutive kda_decode_step calls) is timed in the same run and reported in the
 the library launches on; "roofline" relates the prefill kernel's algorithmic
 HBM bytes to its average duration.  The "prologue" object times the same prefill
 from raw activations through kda_chunk_fwd_prologue (gate and normalisation
-fused into the kernels' loads).  "cpu_baseline" times the fp64 CPU oracle on
+fused into the kernels' loads).  The "backward" object times kda_chunk_bwd (all
+gradients of the same prefill) and relates the fp32 matrix-core work it issues
+to the fp32 matrix peak.  "cpu_baseline" times the fp64 CPU oracle on
 a bounded sample of the same workload.  One JSON line is printed.
 """
 from __future__ import annotations
@@ -31,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
+FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix, published
 CHUNK = 64
 METRIC = "KDA prefill tokens/s + % bf16 MFMA peak; decode state GB/s + % HBM peak"
 
@@ -93,6 +96,17 @@ def pmc_copy(torch, nbytes=256 << 20, reps=3):
                       "reps": reps}))
 
 
+def backward_flops(B, T, H, d):
+    """fp32 matrix-core flops the backward issues: 16x16x4 products (2048 flops
+    each) per 64-token chunk and head, summed over its six kernels at d = 128:
+    operand prep 1984, forward state scan 2560, reverse scan 4096, operand
+    gradients 4096, 64x64 algebra 3072, decayed products 1280 (dense tiles,
+    including the zero upper triangles of the triangular factors)."""
+    assert d == 128
+    per_chunk = (1984 + 2560 + 4096 + 4096 + 3072 + 1280) * 2048
+    return B * H * (-(-T // CHUNK)) * per_chunk
+
+
 def decode_bytes(B, H, d, elt):
     """Per step: the fp32 state read and written once, plus the token's inputs/output."""
     state = B * H * d * d * 4 * 2
@@ -108,6 +122,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-prologue", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--pmc-copy", action="store_true",
                     help="only run a plain 256 MiB copy (counter calibration)")
     args = ap.parse_args()
@@ -233,6 +248,41 @@ def main():
             "achieved_GBps": nbytes / p_s / 1e9, "hbm_frac": nbytes / p_s / 1e9 / HBM_PEAK_GBS,
         }
         del raw, pout, pfin
+        torch.cuda.empty_cache()
+
+    if not args.no_backward:
+        # all gradients of the same prefill (kda_chunk_bwd): forward recomputed
+        # inside, fp32 arithmetic on the fp32 matrix cores
+        bset = kin.make_workload(w, device=dev)
+        cot = kin.make_cotangents(B, T, H, d, d, dtype=w.dtype, seed=w.seed + 20, device=dev)
+
+        def bstep():
+            return kda.kda_chunk_bwd(bset["q"], bset["k"], bset["v"], bset["g"], bset["beta"],
+                                     cot["grad_out"], scale, bset["initial_state"],
+                                     cot["grad_final_state"])
+
+        for _ in range(2):
+            bstep()
+        torch.cuda.synchronize()
+        nb = max(3, min(args.steps, 10))
+        bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(nb)]
+        for i in range(nb):
+            bev[i][0].record(stream)
+            grads = bstep()
+            bev[i][1].record(stream)
+            del grads
+        torch.cuda.synchronize()
+        b_s = sum(a.elapsed_time(b) for a, b in bev) / nb / 1e3
+        bfl = backward_flops(B, T, H, d)
+        result["backward"] = {
+            "entry_point": "kda_chunk_bwd", "workload": "prefill_4x4096 gradients",
+            "calls": nb, "call_ms_avg": b_s * 1e3, "tokens_per_s": B * T / b_s,
+            "fp32_mfma_tflops": bfl / b_s / 1e12,
+            "fp32_mfma_frac": bfl / b_s / 1e12 / FP32_MFMA_PEAK_TFLOPS,
+            "flop_convention": "fp32 16x16x4 matrix products issued, 17088 per chunk and head",
+        }
+        del bset, cot
         torch.cuda.empty_cache()
 
     if not args.no_decode:
