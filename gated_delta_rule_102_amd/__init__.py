@@ -7,6 +7,7 @@ Python binding and :mod:`gated_delta_rule_102_amd.inputs` draws seeded inputs.
 from .kda import (  # noqa: F401
     KDAError,
     chunk_bwd,
+    chunk_fwd_context_parallel,
     chunk_fwd,
     chunk_fwd_prologue,
     chunk_fwd_snapshots,
@@ -14,11 +15,13 @@ from .kda import (  # noqa: F401
     decode_step,
     kda_abi_version,
     kda_chunk_bwd,
+    kda_chunk_transition,
     kda_chunk_fwd,
     kda_chunk_fwd_prologue,
     kda_chunk_fwd_snapshots,
     kda_chunk_fwd_varlen,
     kda_decode_step,
+    kda_state_compose,
     kda_status_string,
     load_library,
 )

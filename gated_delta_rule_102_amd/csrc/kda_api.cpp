@@ -199,6 +199,41 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, co
   return kda::launch_backward(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+int kda_chunk_transition(const void* q, const void* k, const void* g, const void* beta,
+                         float* transition, int B, int T, int H, int dk, int dv, int dtype,
+                         hipStream_t stream) {
+  int rc = check_common(dk, dv, H, dtype);
+  if (rc != KDA_OK) return rc;
+  if (B <= 0 || T <= 0) return KDA_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * T > INT32_MAX / 2) return KDA_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * H > (1 << 24)) return KDA_ERR_SHAPE;
+  const uintptr_t elt = dtype == KDA_F32 ? 4 : 2;
+  rc = check_ptrs({{q, elt, true}, {k, elt, true}, {g, elt, true}, {beta, elt, true},
+                   {transition, 4, true}});
+  if (rc != KDA_OK) return rc;
+  rc = check_device();
+  if (rc != KDA_OK) return rc;
+  kda::TransitionArgs a{q, k, g, beta, transition, B, T, H, dk, dtype == KDA_F32, stream};
+  return kda::launch_transition(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_state_compose(const float* transitions, const float* partial_states,
+                      const float* initial_state, float* entry_states, int R, int B, int H,
+                      int dk, int dv, hipStream_t stream) {
+  int rc = check_common(dk, dv, H, KDA_F32);
+  if (rc != KDA_OK) return rc;
+  if (R <= 0 || B <= 0) return KDA_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * H > (1 << 24)) return KDA_ERR_SHAPE;
+  if (static_cast<int64_t>(R + 1) * B * H * dk * dv > (int64_t{1} << 40)) return KDA_ERR_SHAPE;
+  rc = check_ptrs({{transitions, 16, true}, {partial_states, 16, true},
+                   {initial_state, 16, false}, {entry_states, 16, true}});
+  if (rc != KDA_OK) return rc;
+  rc = check_device();
+  if (rc != KDA_OK) return rc;
+  kda::ComposeArgs a{transitions, partial_states, initial_state, entry_states, R, B, H, dk, stream};
+  return kda::launch_compose(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 int kda_decode_step(const void* q, const void* k, const void* v, const void* g,
                     const void* beta, float* state, void* out, int B, int H, int dk, int dv,
                     float scale, int dtype, hipStream_t stream) {

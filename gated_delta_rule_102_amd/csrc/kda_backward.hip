@@ -6,16 +6,10 @@
 // gradients are the plain derivatives of the forward rule (neurohive.io Kimi K3
 // review, section "Sequence length: hybrid KDA and Gated MLA attention").
 //
-// Per (sequence, head), every 64-token chunk is an affine map of the entering
-// state S and the chunk's values V, written with operands that depend only on
-// the chunk's q, k, g, beta (G = running sum of g inside the chunk):
-//     A'[t,s] = sum_c k_tc k_sc e^{G_tc - G_sc} (s < t),  Ti = (I + Diag(beta) A')^-1
-//     M'[t,s] = sum_c q_tc k_sc e^{G_tc - G_sc} (s <= t), Tb = Ti Diag(beta)
-//     W = Tb (k e^G),  P = scale M' Tb,  Q' = scale q e^G - P (k e^G),
-//     Kt = k e^{G_last - G},  Lam = e^{G_last}
-//     Delta = Tb V - W S,   O = Q' S + P V,   S_next = Lam S + Kt^T Delta.
-// The backward runs in six launches:
-//   bwd_prep     per chunk: the operands above (fp32, to a workspace);
+// With each chunk written as the affine map of kda_chunk_ops.h
+//     Delta = Tb V - W S,   O = Q' S + P V,   S_next = Lam S + Kt^T Delta,
+// the backward runs in six launches:
+//   chunk_ops    per chunk: Tb, Ti, A', M', P, W, Q', Kt, G, Lam (fp32 workspace);
 //   bwd_fwd_scan per (sequence, head, 32 value columns): S at every chunk start
 //                and Delta, walking the chunks forwards;
 //   bwd_scan     the same grid walking backwards from dS_T:
@@ -27,395 +21,14 @@
 //                inverse (dP_tot, dKg, dTb_tot, dM', dA', dbeta);
 //   bwd_grad_decay per chunk: the decayed products of dA' and dM' with k and q,
 //                and the chain to dq, dk and dg (a reverse running sum).
-// Every product runs on the fp32 16x16x4 matrix cores from LDS.  Decayed
-// products use 16-row sub-tile references (G at each sub-tile's last row) so
-// that every factor stays inside fp32's range when the log-decay is >= -5.
+// Every product runs on the fp32 16x16x4 matrix cores from LDS.
 
-#include "kda_device.h"
+#include "kda_chunk_ops.h"
 #include "kda_launch.h"
 
 namespace kda {
 
 namespace {
-
-constexpr int CR = 64;    // rows per chunk
-constexpr int SL = 32;    // value columns per scan workgroup / per contraction slice
-constexpr int LS = 68;    // leading dimension of 64 x 64 LDS matrices
-constexpr int LV = 36;    // leading dimension of 32-column LDS slices
-
-template <int D>
-struct BwdLayout {
-  static constexpr int LD = D + 4;   // leading dimension of 64 x D LDS matrices
-  // workspace per chunk, written by bwd_prep (floats, row-major)
-  static constexpr int TB = 0, TI = 4096, AP = 8192, MP = 12288, PP = 16384;
-  static constexpr int W = 20480, QP = W + CR * D, KT = QP + CR * D, G = KT + CR * D;
-  static constexpr int LAM = G + CR * D, WS = LAM + D;
-  // operand gradients per chunk, written by bwd_grad_dv
-  static constexpr int DQP = 0, DW = CR * D, DKT = 2 * CR * D, DP = 3 * CR * D;
-  static constexpr int DTB = DP + 4096, DLAM = DTB + 4096, G1 = DLAM + D;
-  // written by bwd_grad_nn
-  static constexpr int DKG = 0, DMP = CR * D, DAP = DMP + 4096, G2 = DAP + 4096;
-};
-
-__device__ __forceinline__ int lane16() { return threadIdx.x & 15; }
-__device__ __forceinline__ int lane_g4() { return (threadIdx.x >> 4) & 3; }
-
-// acc += op(A) op(B) for one 16 x 16 output tile; K is a multiple of 16.
-//   op(A)(r, k) = TA ? a[k * lda + r] : a[r * lda + k]     (r < 16, k < K)
-//   op(B)(k, c) = TB ? b[c * ldb + k] : b[k * ldb + c]     (c < 16)
-// With KS, op(A)(r, k) is multiplied by ks[k].  At step j of each 16-wide block
-// lane (g4, l16) feeds A(l16, k0 + 4 g4 + j) and B(k0 + 4 g4 + j, l16); the
-// result is acc[i] = C(4 g4 + i, l16).
-template <bool TA, bool TB, bool KS = false>
-__device__ __forceinline__ f32x4_t mm(f32x4_t acc, const float* a, int lda, const float* b,
-                                      int ldb, int K, const float* ks = nullptr) {
-  const int l16 = lane16(), g4 = lane_g4();
-  for (int k0 = 0; k0 < K; k0 += 16) {
-    const int kb = k0 + 4 * g4;
-    float av[4], bv[4];
-    if constexpr (TA) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) av[j] = a[(kb + j) * lda + l16];
-    } else {
-      const float4 t = *reinterpret_cast<const float4*>(a + l16 * lda + kb);
-      av[0] = t.x; av[1] = t.y; av[2] = t.z; av[3] = t.w;
-    }
-    if constexpr (TB) {
-      const float4 t = *reinterpret_cast<const float4*>(b + l16 * ldb + kb);
-      bv[0] = t.x; bv[1] = t.y; bv[2] = t.z; bv[3] = t.w;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bv[j] = b[(kb + j) * ldb + l16];
-    }
-    if constexpr (KS) {
-      const float4 s = *reinterpret_cast<const float4*>(ks + kb);
-      av[0] *= s.x; av[1] *= s.y; av[2] *= s.z; av[3] *= s.w;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], bv[j], acc, 0, 0, 0);
-  }
-  return acc;
-}
-
-__device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
-
-// tile (accumulator layout) <-> memory at the tile's origin with leading dimension ld
-__device__ __forceinline__ void put(float* dst, int ld, const f32x4_t& v) {
-  const int l16 = lane16(), g4 = lane_g4();
-#pragma unroll
-  for (int i = 0; i < 4; ++i) dst[(4 * g4 + i) * ld + l16] = v[i];
-}
-__device__ __forceinline__ f32x4_t get(const float* src, int ld) {
-  const int l16 = lane16(), g4 = lane_g4();
-  f32x4_t v;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = src[(4 * g4 + i) * ld + l16];
-  return v;
-}
-
-// Pins a loaded value: the empty asm consumes and redefines it, so the load
-// that produced it is issued before this point and cannot be sunk next to its
-// use.  Pinning a group of tile loads keeps all of them in flight together.
-template <typename V>
-__device__ __forceinline__ void pin(V& v) { asm volatile("" : "+v"(v)); }
-
-// ROWS x COLS fp32 global -> LDS (COLS % 4 == 0, both sides 16-byte aligned).
-// load() issues every global load of the tile before store() writes LDS, so a
-// thread has all its loads in flight at once; several tiles can be loaded
-// before any of them is stored.
-template <int NT, int ROWS, int COLS>
-struct GTile {
-  static constexpr int C4 = COLS / 4, N = ROWS * C4, PER = (N + NT - 1) / NT;
-  f32x4_t r[PER];
-  __device__ __forceinline__ void load(const float* src, int64_t gld) {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int e = static_cast<int>(threadIdx.x) + j * NT;
-      if (N % NT == 0 || e < N) {
-        const int rr = e / C4, c = (e - rr * C4) * 4;
-        r[j] = *reinterpret_cast<const f32x4_t*>(src + rr * gld + c);
-      }
-    }
-  }
-  __device__ __forceinline__ void pin_all() {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) pin(r[j]);
-  }
-  __device__ __forceinline__ void store(float* dst, int lld) const {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int e = static_cast<int>(threadIdx.x) + j * NT;
-      if (N % NT == 0 || e < N) {
-        const int rr = e / C4, c = (e - rr * C4) * 4;
-        *reinterpret_cast<f32x4_t*>(dst + rr * lld + c) = r[j];
-      }
-    }
-  }
-};
-template <int NT, int ROWS, int COLS>
-__device__ __forceinline__ void g2l(float* dst, int lld, const float* src, int64_t gld) {
-  GTile<NT, ROWS, COLS> t;
-  t.load(src, gld);
-  t.pin_all();
-  t.store(dst, lld);
-}
-template <int NT, int ROWS, int COLS>
-__device__ __forceinline__ void l2g(float* dst, int64_t gld, const float* src, int lld) {
-  constexpr int C4 = COLS / 4, N = ROWS * C4;
-#pragma unroll
-  for (int j = 0; j < (N + NT - 1) / NT; ++j) {
-    const int e = static_cast<int>(threadIdx.x) + j * NT;
-    if (N % NT == 0 || e < N) {
-      const int r = e / C4, c = (e - r * C4) * 4;
-      *reinterpret_cast<float4*>(dst + r * gld + c) = *reinterpret_cast<const float4*>(src + r * lld + c);
-    }
-  }
-}
-// 64 x COLS input rows (bf16 or fp32) -> fp32 in LDS; rows >= nrow read as zero.
-// The row index is clamped so every load is unconditional (a load under a
-// branch is waited for inside the branch, which serialises the loads).
-template <int NT, int COLS, typename TIn>
-struct ITile {
-  static constexpr int N = CR * COLS, PER = N / NT;
-  static_assert(N % NT == 0, "tile split");
-  float r[PER];
-  __device__ __forceinline__ void load(const TIn* src, int64_t row_stride, int nrow) {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int e = static_cast<int>(threadIdx.x) + j * NT;
-      const int rr = e / COLS, c = e - rr * COLS;
-      const float x = to_f32(src[min(rr, nrow - 1) * row_stride + c]);
-      r[j] = rr < nrow ? x : 0.f;
-    }
-  }
-  __device__ __forceinline__ void pin_all() {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) pin(r[j]);
-  }
-  __device__ __forceinline__ void store(float* dst, int lld) const {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int e = static_cast<int>(threadIdx.x) + j * NT;
-      const int rr = e / COLS, c = e - rr * COLS;
-      dst[rr * lld + c] = r[j];
-    }
-  }
-};
-
-// sub-tile pairs J < I of a 64-row chunk -> 0..5
-__device__ __forceinline__ int pair_index(int I, int J) { return I * (I - 1) / 2 + J; }
-
-struct ChunkPos {
-  int b, h, c, nrow;
-  int64_t row0;   // (b * T + first token) * H + h: token-row index of the chunk's row 0
-};
-__device__ __forceinline__ ChunkPos chunk_pos(int item, int T, int H, int nc) {
-  ChunkPos p;
-  p.c = item % nc;
-  const int bh = item / nc;
-  p.b = bh / H;
-  p.h = bh - p.b * H;
-  p.nrow = min(CR, T - p.c * CR);
-  p.row0 = (static_cast<int64_t>(p.b) * T + static_cast<int64_t>(p.c) * CR) * H + p.h;
-  return p;
-}
-
-// ---------------------------------------------------------------- bwd_prep
-
-template <int D, typename TIn>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const TIn* __restrict__ q,
-                                                       const TIn* __restrict__ k,
-                                                       const TIn* __restrict__ g,
-                                                       const TIn* __restrict__ beta,
-                                                       float* __restrict__ ws, int T, int H,
-                                                       int nc, float scale) {
-  using L = BwdLayout<D>;
-  constexpr int LD = L::LD;
-  __shared__ __attribute__((aligned(16))) float sm[3 * CR * LD + 3 * CR * LS + 6 * D + CR];
-  float* R0 = sm;                 // G, then (phase 5 on) unused
-  float* R1 = R0 + CR * LD;       // k rowf -> q rowf -> k e^G
-  float* R2 = R1 + CR * LD;       // k colf -> inverse scratch -> scale q e^G
-  float* S0 = R2 + CR * LD;       // A' -> P
-  float* S1 = S0 + CR * LS;       // M'
-  float* S2 = S1 + CR * LS;       // Ti
-  float* FP = S2 + CR * LS;       // [6][D] pair factors e^{R_I - R_J}
-  float* BT = FP + 6 * D;         // beta
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int l16 = lane16(), g4 = lane_g4();
-  const ChunkPos p = chunk_pos(blockIdx.x, T, H, nc);
-  const int64_t rs = static_cast<int64_t>(H) * D;
-  const TIn* qc = q + p.row0 * D;
-  const TIn* kc = k + p.row0 * D;
-  const TIn* gc = g + p.row0 * D;
-  float* w = ws + static_cast<int64_t>(blockIdx.x) * L::WS;
-
-  {
-    ITile<256, D, TIn> gt;
-    gt.load(gc, rs, p.nrow);
-    gt.pin_all();
-    for (int e = tid; e < 3 * CR * LS; e += 256) S0[e] = 0.f;
-    const float bt = to_f32(beta[p.row0 + static_cast<int64_t>(min(tid & (CR - 1), p.nrow - 1)) * H]);
-    if (tid < CR) BT[tid] = tid < p.nrow ? bt : 0.f;
-    gt.store(R0, LD);
-  }
-  __syncthreads();
-  if (tid < D) {   // running sum of g down the chunk (padding rows hold 0)
-    float acc = 0.f;
-#pragma unroll 8
-    for (int t = 0; t < CR; ++t) {
-      acc += R0[t * LD + tid];
-      R0[t * LD + tid] = acc;
-    }
-  }
-  __syncthreads();
-
-  if (tid < D) {
-    for (int I = 1; I < 4; ++I)
-      for (int J = 0; J < I; ++J)
-        FP[pair_index(I, J) * D + tid] =
-            expf(R0[(16 * I + 15) * LD + tid] - R0[(16 * J + 15) * LD + tid]);
-    w[L::LAM + tid] = expf(R0[(CR - 1) * LD + tid]);
-  }
-  {
-    ITile<256, D, TIn> kt;
-    kt.load(kc, rs, p.nrow);
-    kt.pin_all();
-#pragma unroll
-    for (int j = 0; j < kt.PER; ++j) {
-      const int e = tid + j * 256, t = e / D, i = e - t * D;
-      const float G = R0[t * LD + i], RI = R0[(t | 15) * LD + i], Gl = R0[(CR - 1) * LD + i];
-      const float kv = kt.r[j];
-      R1[t * LD + i] = kv * expf(G - RI);
-      R2[t * LD + i] = kv * expf(RI - G);
-      w[L::KT + e] = kv * expf(Gl - G);
-      w[L::G + e] = G;
-    }
-  }
-  __syncthreads();
-
-  // A' and M' by sub-tile pairs (I, J), J <= I: 10 tiles each
-  auto pair_gram = [&](float* dst, bool strict) {
-    for (int pt = wave; pt < 10; pt += 4) {
-      int I = 0;
-      while ((I + 1) * (I + 2) / 2 <= pt) ++I;
-      const int J = pt - I * (I + 1) / 2;
-      f32x4_t acc = zero4();
-      if (I == J) {
-        acc = mm<false, true>(acc, R1 + 16 * I * LD, LD, R2 + 16 * J * LD, LD, D);
-      } else {
-        acc = mm<false, true, true>(acc, R1 + 16 * I * LD, LD, R2 + 16 * J * LD, LD, D,
-                                    FP + pair_index(I, J) * D);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * I + 4 * g4 + i, s = 16 * J + l16;
-        dst[t * LS + s] = (strict ? s < t : s <= t) ? acc[i] : 0.f;
-      }
-    }
-  };
-  pair_gram(S0, true);
-  __syncthreads();
-  {   // q rowf into R1
-    ITile<256, D, TIn> qt;
-    qt.load(qc, rs, p.nrow);
-    qt.pin_all();
-#pragma unroll
-    for (int j = 0; j < qt.PER; ++j) {
-      const int e = tid + j * 256, t = e / D, i = e - t * D;
-      const float G = R0[t * LD + i], RI = R0[(t | 15) * LD + i];
-      R1[t * LD + i] = qt.r[j] * expf(G - RI);
-    }
-  }
-  __syncthreads();
-  pair_gram(S1, false);
-  __syncthreads();
-  l2g<256, CR, CR>(w + L::AP, CR, S0, LS);
-  l2g<256, CR, CR>(w + L::MP, CR, S1, LS);
-
-  // Ti = (I + Diag(beta) A')^-1: diagonal 16 x 16 blocks by substitution (one
-  // column per lane), then the blocks below them level by level:
-  //   Ti_IJ = -Ti_II Diag(beta_I) sum_{J <= m < I} A'_Im Ti_mJ
-  if (lane < 16) {
-    const int I = wave, j = lane;
-    float x[16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      float s = t == j ? 1.f : 0.f;
-      const float bt = BT[16 * I + t];
-#pragma unroll
-      for (int u = 0; u < t; ++u) s -= bt * S0[(16 * I + t) * LS + 16 * I + u] * x[u];
-      x[t] = s;
-    }
-#pragma unroll
-    for (int t = 0; t < 16; ++t) S2[(16 * I + t) * LS + 16 * I + j] = x[t];
-  }
-  __syncthreads();
-  float* xs = R2 + wave * 16 * 17;
-  for (int I = 1; I < 4; ++I) {
-    if (wave < I) {
-      const int J = wave;
-      f32x4_t y = mm<false, false>(zero4(), S0 + 16 * I * LS + 16 * J, LS,
-                                   S2 + 16 * J * LS + 16 * J, LS, 16 * (I - J));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) y[i] *= BT[16 * I + 4 * g4 + i];
-      put(xs, 17, y);
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      const f32x4_t tt = mm<false, false>(zero4(), S2 + 16 * I * LS + 16 * I, LS, xs, 17, 16);
-      put(S2 + 16 * I * LS + 16 * J, LS, -tt);
-    }
-    __syncthreads();
-  }
-  for (int e = tid; e < CR * CR; e += 256) {
-    const int t = e / CR, s = e - t * CR;
-    const float ti = S2[t * LS + s];
-    w[L::TI + e] = ti;
-    w[L::TB + e] = ti * BT[s];
-  }
-  {   // k e^G into R1, scale q e^G into R2
-    ITile<256, D, TIn> kt, qt;
-    kt.load(kc, rs, p.nrow);
-    qt.load(qc, rs, p.nrow);
-    kt.pin_all();
-    qt.pin_all();
-#pragma unroll
-    for (int j = 0; j < kt.PER; ++j) {
-      const int e = tid + j * 256, t = e / D, i = e - t * D;
-      const float eg = expf(R0[t * LD + i]);
-      R1[t * LD + i] = kt.r[j] * eg;
-      R2[t * LD + i] = scale * qt.r[j] * eg;
-    }
-  }
-  __syncthreads();
-
-  // P = scale M' Tb (into S0 and the workspace); W = Tb (k e^G)
-  for (int j = wave; j < 16; j += 4) {
-    const int rt = j >> 2, ct = j & 3;
-    f32x4_t acc = mm<false, false>(zero4(), S1 + 16 * rt * LS, LS, S2 + 16 * ct, LS, CR);
-    const float f = scale * BT[16 * ct + l16];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] *= f;
-    put(S0 + 16 * rt * LS + 16 * ct, LS, acc);
-    put(w + L::PP + 16 * rt * CR + 16 * ct, CR, acc);
-  }
-  constexpr int CT = D / 16;
-  for (int j = wave; j < 4 * CT; j += 4) {
-    const int rt = j / CT, ct = j - rt * CT;
-    const f32x4_t acc = mm<false, false, true>(zero4(), S2 + 16 * rt * LS, LS, R1 + 16 * ct, LD,
-                                               CR, BT);
-    put(w + L::W + 16 * rt * D + 16 * ct, D, acc);
-  }
-  __syncthreads();
-  // Q' = scale q e^G - P (k e^G)
-  for (int j = wave; j < 4 * CT; j += 4) {
-    const int rt = j / CT, ct = j - rt * CT;
-    const f32x4_t pk = mm<false, false>(zero4(), S0 + 16 * rt * LS, LS, R1 + 16 * ct, LD, CR);
-    f32x4_t acc = get(R2 + 16 * rt * LD + 16 * ct, LD);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] -= pk[i];
-    put(w + L::QP + 16 * rt * D + 16 * ct, D, acc);
-  }
-}
 
 // ---------------------------------------------------------------- scans
 
@@ -1078,7 +691,7 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
   const TIn* beta = static_cast<const TIn*>(a.beta);
   const TIn* dout = static_cast<const TIn*>(a.d_out);
   const int scan_blocks = a.B * a.H * (D / SL);
-  hipLaunchKernelGGL((bwd_prep_kernel<D, TIn>), dim3(items), dim3(256), 0, a.stream, q, k, g, beta,
+  hipLaunchKernelGGL((chunk_ops_kernel<D, TIn>), dim3(items), dim3(256), 0, a.stream, q, k, g, beta,
                      ws, a.T, a.H, nc, a.scale);
   hipLaunchKernelGGL((bwd_fwd_scan_kernel<D, TIn>), dim3(scan_blocks), dim3(256), 0, a.stream, v,
                      a.initial_state, ws, st, dl, a.T, a.H, nc);

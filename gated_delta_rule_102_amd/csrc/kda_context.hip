@@ -1,0 +1,188 @@
+// Context-parallel building blocks for one long sequence split into segments.
+//
+// A segment of KDA (any run of tokens) maps its entry state to its exit state
+// affinely: S_exit = P S_entry + R, where R is the exit state from a zero entry
+// (an ordinary prefill with no initial state) and P, the segment's transition,
+// is the exit state obtained with v = 0 from the identity.  Chunk by chunk (the
+// operands of kda_chunk_ops.h) P is the product of the chunk maps
+// Diag(Lam) - Kt^T W, since with V = 0 a chunk sends S to Lam S - Kt^T W S.
+// Segments are then joined by the sequential composition
+//     S_entry(0) = S_0,   S_entry(r + 1) = P_r S_entry(r) + R_r,
+// after which every segment reruns its prefill from its own entry state.  The
+// pages give KDA's state as one fixed-size matrix per request that a prefix
+// cache can restore (neurohive.io Kimi K3 review, "Training and inference
+// infrastructure"), which is what makes a segment's effect a fixed-size affine
+// map; they describe no context-parallel scheme, so this is a plain reading of
+// the chunked form.
+//
+//   transition_scan_kernel: per (sequence, head, 32 columns of P) the scan
+//       S <- Lam S - Kt^T (W S) from the identity's columns, fp32 throughout.
+//   compose_kernel: per (sequence, head, 32 value columns) the composition over
+//       the segments, S <- P_r S + R_r, writing every entry state and the exit
+//       state of the last segment.
+
+#include "kda_chunk_ops.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+namespace {
+
+template <int D>
+__global__ __launch_bounds__(256) void transition_scan_kernel(const float* __restrict__ ws,
+                                                              float* __restrict__ trans,
+                                                              int nc) {
+  using L = BwdLayout<D>;
+  constexpr int LD = L::LD;
+  constexpr int NTW = D / 32;   // state tiles per wave: (D/16) x 2 tiles over 4 waves
+  __shared__ __attribute__((aligned(16))) float sm[2 * CR * LD + CR * LV + D * LV + D];
+  float* Ws = sm;
+  float* KTs = Ws + CR * LD;
+  float* Dls = KTs + CR * LD;
+  float* Ss = Dls + CR * LV;
+  float* Lm = Ss + D * LV;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int l16 = lane16(), g4 = lane_g4();
+  constexpr int NSL = D / SL;
+  const int bh = blockIdx.x / NSL, c0 = (blockIdx.x - bh * NSL) * SL;
+
+  f32x4_t S[NTW];
+#pragma unroll
+  for (int x = 0; x < NTW; ++x) {   // columns c0 .. c0 + 31 of the identity
+    const int j = wave * NTW + x, rt = j >> 1, ct = j & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) S[x][i] = (16 * rt + 4 * g4 + i == c0 + 16 * ct + l16) ? 1.f : 0.f;
+  }
+  for (int c = 0; c < nc; ++c) {
+    const float* w = ws + (static_cast<int64_t>(bh) * nc + c) * L::WS;
+    {
+      GTile<256, CR, D> t_w, t_kt;
+      t_w.load(w + L::W, D);
+      t_kt.load(w + L::KT, D);
+      float lm = w[L::LAM + (tid & (D - 1))];
+      t_w.pin_all();
+      t_kt.pin_all();
+      pin(lm);
+      t_w.store(Ws, LD);
+      t_kt.store(KTs, LD);
+      if (tid < D) Lm[tid] = lm;
+    }
+#pragma unroll
+    for (int x = 0; x < NTW; ++x) {
+      const int j = wave * NTW + x, rt = j >> 1, ct = j & 1;
+      put(Ss + 16 * rt * LV + 16 * ct, LV, S[x]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int y = 0; y < 2; ++y) {   // W S: 4 x 2 tiles (Delta = -W S)
+      const int j = wave * 2 + y, rt = j >> 1, ct = j & 1;
+      const f32x4_t d = mm<false, false>(zero4(), Ws + 16 * rt * LD, LD, Ss + 16 * ct, LV, D);
+      put(Dls + 16 * rt * LV + 16 * ct, LV, d);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < NTW; ++x) {   // S = Lam S - Kt^T (W S)
+      const int j = wave * NTW + x, rt = j >> 1, ct = j & 1;
+      const f32x4_t kd = mm<true, false>(zero4(), KTs + 16 * rt, LD, Dls + 16 * ct, LV, CR);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[x][i] = Lm[16 * rt + 4 * g4 + i] * S[x][i] - kd[i];
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int x = 0; x < NTW; ++x) {
+    const int j = wave * NTW + x, rt = j >> 1, ct = j & 1;
+    put(trans + static_cast<int64_t>(bh) * D * D + 16 * rt * D + c0 + 16 * ct, D, S[x]);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void compose_kernel(const float* __restrict__ trans,
+                                                      const float* __restrict__ part,
+                                                      const float* __restrict__ s0,
+                                                      float* __restrict__ entry, int R,
+                                                      int BH) {
+  constexpr int LD = D + 4;
+  constexpr int NTW = D / 32;
+  __shared__ __attribute__((aligned(16))) float sm[D * LD + D * LV];
+  float* Ps = sm;
+  float* Ss = Ps + D * LD;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  constexpr int NSL = D / SL;
+  const int bh = blockIdx.x / NSL, c0 = (blockIdx.x - bh * NSL) * SL;
+  const int64_t DD = static_cast<int64_t>(D) * D;
+  const int64_t off = static_cast<int64_t>(bh) * DD + c0;
+
+  f32x4_t S[NTW];
+#pragma unroll
+  for (int x = 0; x < NTW; ++x) {
+    const int j = wave * NTW + x, rt = j >> 1, ct = j & 1;
+    S[x] = s0 ? get(s0 + off + 16 * rt * D + 16 * ct, D) : zero4();
+    put(entry + off + 16 * rt * D + 16 * ct, D, S[x]);
+  }
+  for (int r = 0; r < R; ++r) {
+    const int64_t seg = static_cast<int64_t>(r) * BH * DD;
+    {
+      GTile<256, D, D> t_p;
+      t_p.load(trans + seg + static_cast<int64_t>(bh) * DD, D);
+      t_p.pin_all();
+      t_p.store(Ps, LD);
+    }
+#pragma unroll
+    for (int x = 0; x < NTW; ++x) {
+      const int j = wave * NTW + x, rt = j >> 1, ct = j & 1;
+      put(Ss + 16 * rt * LV + 16 * ct, LV, S[x]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < NTW; ++x) {   // S = P_r S + R_r
+      const int j = wave * NTW + x, rt = j >> 1, ct = j & 1;
+      f32x4_t acc = get(part + seg + off + 16 * rt * D + 16 * ct, D);
+      S[x] = mm<false, false>(acc, Ps + 16 * rt * LD, LD, Ss + 16 * ct, LV, D);
+      put(entry + seg + BH * DD + off + 16 * rt * D + 16 * ct, D, S[x]);
+    }
+    __syncthreads();
+  }
+}
+
+template <int D, typename TIn>
+hipError_t launch_transition_t(const TransitionArgs& a) {
+  using L = BwdLayout<D>;
+  const int nc = (a.T + CR - 1) / CR;
+  const int64_t items = static_cast<int64_t>(a.B) * a.H * nc;
+  float* ws = nullptr;
+  hipError_t err = hipMallocAsync(reinterpret_cast<void**>(&ws), items * L::WS * sizeof(float), a.stream);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((chunk_ops_kernel<D, TIn>), dim3(items), dim3(256), 0, a.stream,
+                     static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
+                     static_cast<const TIn*>(a.g), static_cast<const TIn*>(a.beta), ws, a.T, a.H,
+                     nc, 1.0f);
+  hipLaunchKernelGGL((transition_scan_kernel<D>), dim3(a.B * a.H * (D / SL)), dim3(256), 0,
+                     a.stream, ws, a.transition, nc);
+  err = hipGetLastError();
+  const hipError_t ferr = hipFreeAsync(ws, a.stream);
+  return err != hipSuccess ? err : ferr;
+}
+
+}  // namespace
+
+hipError_t launch_transition(const TransitionArgs& a) {
+  if (a.d == 128) {
+    return a.dtype_f32 ? launch_transition_t<128, float>(a) : launch_transition_t<128, bf16_t>(a);
+  }
+  return a.dtype_f32 ? launch_transition_t<64, float>(a) : launch_transition_t<64, bf16_t>(a);
+}
+
+hipError_t launch_compose(const ComposeArgs& a) {
+  const int BH = a.B * a.H;
+  if (a.d == 128) {
+    hipLaunchKernelGGL((compose_kernel<128>), dim3(BH * (128 / SL)), dim3(256), 0, a.stream,
+                       a.transitions, a.partial_states, a.initial_state, a.entry_states, a.R, BH);
+  } else {
+    hipLaunchKernelGGL((compose_kernel<64>), dim3(BH * (64 / SL)), dim3(256), 0, a.stream,
+                       a.transitions, a.partial_states, a.initial_state, a.entry_states, a.R, BH);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kda

@@ -49,7 +49,26 @@ struct BackwardArgs {
   hipStream_t stream;
 };
 
+struct TransitionArgs {
+  const void *q, *k, *g, *beta;
+  float* transition;            // [B, H, d, d]
+  int B, T, H, d;
+  bool dtype_f32;
+  hipStream_t stream;
+};
+
+struct ComposeArgs {
+  const float* transitions;     // [R, B, H, d, d]
+  const float* partial_states;  // [R, B, H, d, d]
+  const float* initial_state;   // [B, H, d, d] or null (zero)
+  float* entry_states;          // [R + 1, B, H, d, d]
+  int R, B, H, d;
+  hipStream_t stream;
+};
+
 hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_transition(const TransitionArgs& a);
+hipError_t launch_compose(const ComposeArgs& a);
 hipError_t launch_backward(const BackwardArgs& a);
 // device scratch the backward allocates (and frees) on the stream, in bytes
 int64_t backward_workspace_bytes(int B, int T, int H, int d);

@@ -21,7 +21,8 @@ KDA_BF16, KDA_F32 = 0, 1
 _lib = None
 
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd", "kda_chunk_fwd_prologue",
-           "kda_chunk_fwd_snapshots", "kda_chunk_fwd_varlen", "kda_decode_step", "kda_chunk_bwd")
+           "kda_chunk_fwd_snapshots", "kda_chunk_fwd_varlen", "kda_decode_step", "kda_chunk_bwd",
+           "kda_chunk_transition", "kda_state_compose")
 
 
 class KDAError(RuntimeError):
@@ -61,6 +62,10 @@ def load_library(path: str = LIB_PATH):
     lib.kda_decode_step.restype = i32
     lib.kda_chunk_bwd.argtypes = [vp] * 14 + [i32, i32, i32, i32, i32, f32, i32, vp]
     lib.kda_chunk_bwd.restype = i32
+    lib.kda_chunk_transition.argtypes = [vp] * 5 + [i32] * 6 + [vp]
+    lib.kda_chunk_transition.restype = i32
+    lib.kda_state_compose.argtypes = [vp] * 4 + [i32] * 5 + [vp]
+    lib.kda_state_compose.restype = i32
     _lib = lib
     return lib
 
@@ -291,6 +296,82 @@ def kda_chunk_bwd(q, k, v, g, beta, grad_out, scale=None, initial_state=None,
     return (*grads, ds0)
 
 
+def kda_chunk_transition(q, k, g, beta, transition=None):
+    """Transition of each of B segments: the exit state with v = 0 from the identity,
+    P [B,H,dk,dk] fp32 (so that S_exit = P S_entry + the zero-entry exit state)."""
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dtype, device = q.dtype, q.device
+    _check(dict(q=q, k=k, g=g, beta=beta), dtype, device)
+    if k.shape != q.shape or g.shape != q.shape or beta.shape != q.shape[:3]:
+        raise ValueError("shape mismatch among q, k, g, beta")
+    if transition is None:
+        transition = torch.empty((B, H, dk, dk), dtype=torch.float32, device=device)
+    _check_state("transition", transition, (B, H, dk, dk), device)
+    rc = lib.kda_chunk_transition(_ptr(q), _ptr(k), _ptr(g), _ptr(beta), _ptr(transition),
+                                  B, T, H, dk, dk, _dtype_code(q), _stream(q))
+    _raise("kda_chunk_transition", rc)
+    return transition
+
+
+def kda_state_compose(transitions, partial_states, initial_state=None, entry_states=None):
+    """Entry state of every segment: transitions [R,B,H,dk,dk] and partial_states
+    [R,B,H,dk,dv] fp32 -> entry_states [R+1,B,H,dk,dv] with entry[0] = initial_state
+    (zero if None) and entry[r+1] = transitions[r] @ entry[r] + partial_states[r]."""
+    lib = load_library()
+    R, B, H, dk, _ = transitions.shape
+    dv = partial_states.shape[-1]
+    device = transitions.device
+    _check_state("transitions", transitions, (R, B, H, dk, dk), device)
+    _check_state("partial_states", partial_states, (R, B, H, dk, dv), device)
+    _check_state("initial_state", initial_state, (B, H, dk, dv), device)
+    if entry_states is None:
+        entry_states = torch.empty((R + 1, B, H, dk, dv), dtype=torch.float32, device=device)
+    _check_state("entry_states", entry_states, (R + 1, B, H, dk, dv), device)
+    rc = lib.kda_state_compose(_ptr(transitions), _ptr(partial_states), _ptr(initial_state),
+                               _ptr(entry_states), R, B, H, dk, dv, _stream(transitions))
+    _raise("kda_state_compose", rc)
+    return entry_states
+
+
+def chunk_fwd_context_parallel(q, k, v, g, beta, segment_tokens, scale=None,
+                               initial_state=None):
+    """kda_chunk_fwd over segments of ``segment_tokens`` tokens scheduled as context
+    parallelism would place them on several GPUs, here all on q's device:
+      1. per segment (independent): its zero-entry exit state (kda_chunk_fwd) and
+         its transition (kda_chunk_transition);
+      2. the entry state of every segment (kda_state_compose) -- across GPUs this
+         is where the per-segment (transition, exit state) pairs are all-gathered;
+      3. per segment (independent): kda_chunk_fwd from its entry state.
+    Returns ``(out [B,T,H,dv], final_state [B,H,dk,dv], entry_states [R+1,B,H,dk,dv])``."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    seg = int(segment_tokens)
+    if seg <= 0:
+        raise ValueError("segment_tokens must be positive")
+    bounds = [(t0, min(T, t0 + seg)) for t0 in range(0, T, seg)]
+    R = len(bounds)
+
+    def piece(x, t0, t1):
+        return x[:, t0:t1].contiguous()
+
+    parts = [{n: piece(x, t0, t1) for n, x in (("q", q), ("k", k), ("v", v), ("g", g),
+                                                 ("beta", beta))} for t0, t1 in bounds]
+    trans = torch.empty((R, B, H, dk, dk), dtype=torch.float32, device=q.device)
+    exits = torch.empty((R, B, H, dk, dv), dtype=torch.float32, device=q.device)
+    for r, p in enumerate(parts):                                  # phase 1
+        kda_chunk_fwd(p["q"], p["k"], p["v"], p["g"], p["beta"], scale, None,
+                      final_state=exits[r])
+        kda_chunk_transition(p["q"], p["k"], p["g"], p["beta"], transition=trans[r])
+    entry = kda_state_compose(trans, exits, initial_state)         # phase 2
+    out = torch.empty((B, T, H, dv), dtype=v.dtype, device=v.device)
+    for r, ((t0, t1), p) in enumerate(zip(bounds, parts)):         # phase 3
+        o, _ = kda_chunk_fwd(p["q"], p["k"], p["v"], p["g"], p["beta"], scale, entry[r],
+                             output_final_state=False)
+        out[:, t0:t1] = o
+    return out, entry[R], entry
+
+
 # short aliases
 chunk_fwd = kda_chunk_fwd
 chunk_fwd_varlen = kda_chunk_fwd_varlen
@@ -298,3 +379,5 @@ chunk_fwd_snapshots = kda_chunk_fwd_snapshots
 chunk_fwd_prologue = kda_chunk_fwd_prologue
 decode_step = kda_decode_step
 chunk_bwd = kda_chunk_bwd
+chunk_transition = kda_chunk_transition
+state_compose = kda_state_compose

@@ -191,6 +191,50 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, co
                   int dk, int dv, float scale, int dtype, hipStream_t stream);
 
 /*
+ * Context parallelism for one long sequence split into R segments (design for
+ * several GPUs, one segment per GPU; every step also runs on one GPU).  A
+ * segment maps its entry state affinely to its exit state,
+ *     S_exit = P S_entry + R_part,
+ * where R_part is the final state of kda_chunk_fwd over the segment with no
+ * initial state and P is the segment's transition.  The pages keep one
+ * fixed-size state per request that a prefix cache can restore (neurohive.io
+ * Kimi K3 review, "Training and inference infrastructure"); they describe no
+ * context-parallel scheme, so this is a plain reading of the chunked form.  The
+ * steps: every segment computes R_part (kda_chunk_fwd) and P
+ * (kda_chunk_transition); the (P, R_part) of all segments are gathered;
+ * kda_state_compose gives every entry state; every segment reruns kda_chunk_fwd
+ * from its entry state for its outputs.
+ *
+ * kda_chunk_transition: P for each of B independent segments.
+ *  q, k, g, beta   as for kda_chunk_fwd ([B, T, H, .], dtype); v is not needed.
+ *  transition      [B, H, dk, dk] fp32, required: the exit state of the segment
+ *                  run with v = 0 from the identity, i.e. the product of its
+ *                  per-token maps (I - beta_t k_t k_t^T) Diag(exp g_t), latest
+ *                  token leftmost.
+ * dk == dv in {64, 128} for both dtypes; arithmetic is fp32.  Allocates a
+ * workspace of 213,504 bytes per 64-token chunk per head at d = 128 (147,712 at
+ * d = 64) with hipMallocAsync on `stream`, freed on the same stream.
+ */
+int kda_chunk_transition(const void* q, const void* k, const void* g, const void* beta,
+                         float* transition, int B, int T, int H, int dk, int dv, int dtype,
+                         hipStream_t stream);
+
+/*
+ * kda_state_compose: the sequential composition over R segments,
+ *     entry_states[0] = initial_state (NULL = zero),
+ *     entry_states[r + 1] = transitions[r] entry_states[r] + partial_states[r],
+ * so entry_states[r] is the state entering segment r and entry_states[R] the
+ * state after the last one.
+ *  transitions     [R, B, H, dk, dk] fp32;  partial_states [R, B, H, dk, dv] fp32;
+ *  initial_state   [B, H, dk, dv] fp32 or NULL;  entry_states [R + 1, B, H, dk, dv].
+ * All fp32, 16-byte aligned; entry_states must not alias the inputs.  dk == dv in
+ * {64, 128}.  Allocates nothing.
+ */
+int kda_state_compose(const float* transitions, const float* partial_states,
+                      const float* initial_state, float* entry_states, int R, int B, int H,
+                      int dk, int dv, hipStream_t stream);
+
+/*
  * One decode token for B sequences, updating `state` in place.
  *
  *  q, k, g  [B, H, dk] (dtype);  v, out [B, H, dv] (dtype);  beta [B, H] (dtype)

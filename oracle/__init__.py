@@ -15,6 +15,8 @@ Contents
     into products of the per-token transition matrices (brute force, T <= 8).
   * :func:`prologue_np` -- the gate/normalisation prologue (unit-norm q and k,
     g = max(-5, -softplus(x)), beta = sigmoid(x)) in fp64, for the fused path.
+  * :func:`transition_np` -- a segment's transition (the product of the
+    per-token maps with v = 0), for context parallelism, in fp64.
   * :func:`backward_oracle` -- gradients of the recurrence (dq, dk, dv, dg,
     dbeta, dS_0) by fp64 reverse-mode autodiff on the CPU (``grad.py``).
 
@@ -27,6 +29,7 @@ from .ref import (  # noqa: F401
     oracle_forward,
     prologue_np,
     recurrence_np,
+    transition_np,
     unrolled_np,
     widen_np,
 )

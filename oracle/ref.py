@@ -213,6 +213,22 @@ def unrolled_np(q, k, v, g, beta, scale, initial_state=None):
     return out, final
 
 
+def transition_np(k, g, beta):
+    """Transition of one segment, in fp64, from its definition: with v = 0 a token
+    maps the state by M_t = (I - beta_t k_t k_t^T) Diag(exp g_t) (the recurrence of
+    the C oracle with its write term removed), so the segment's exit state from an
+    entry state S is P S with P = M_{T-1} ... M_1 M_0.  k, g: [T, H, dk];
+    beta: [T, H].  Returns P [H, dk, dk].  Used for context parallelism, where a
+    segment's exit state is P S_entry plus its zero-entry exit state."""
+    k, g, beta = (widen_np(x) for x in (k, g, beta))
+    T, H, dk = k.shape
+    P = np.broadcast_to(np.eye(dk), (H, dk, dk)).copy()
+    for t in range(T):
+        P = P * np.exp(g[t])[:, :, None]                                  # Diag(e^g) P
+        P = P - beta[t][:, None, None] * k[t][:, :, None] * np.einsum("hi,hij->hj", k[t], P)[:, None, :]
+    return P
+
+
 def prologue_np(q_raw, k_raw, g_raw, beta_raw, eps=1e-6, floor=-5.0):
     """The gate/normalisation prologue, in fp64, written out from its definitions.
 

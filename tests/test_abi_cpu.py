@@ -33,7 +33,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "kda_abi_version", "kda_status_string", "kda_chunk_fwd", "kda_chunk_fwd_prologue",
-        "kda_chunk_fwd_snapshots", "kda_chunk_fwd_varlen", "kda_decode_step", "kda_chunk_bwd"])
+        "kda_chunk_fwd_snapshots", "kda_chunk_fwd_varlen", "kda_decode_step", "kda_chunk_bwd",
+        "kda_chunk_transition", "kda_state_compose"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -114,6 +115,22 @@ def test_argument_checks_precede_any_device_call(lib):
     args = list(ok)
     args[13] = vp(4098)                                                # fp32 state misaligned
     assert bw(*args, 1, 64, 1, 128, 128, 0.1, 0, None) == -5
+    tr = lib.kda_chunk_transition
+    tr.argtypes = [vp] * 5 + [i32] * 6 + [vp]
+    tr.restype = i32
+    assert tr(p, p, p, p, p, 1, 64, 1, 128, 128, 0, None) in (-6, -7)
+    assert tr(p, p, p, p, None, 1, 64, 1, 128, 128, 0, None) == -1
+    assert tr(p, p, p, p, p, 1, 64, 1, 128, 64, 0, None) == -3
+    assert tr(p, p, p, p, p, 1, -1, 1, 128, 128, 0, None) == -2
+    assert tr(p, p, p, p, vp(4098), 1, 64, 1, 128, 128, 0, None) == -5
+    co = lib.kda_state_compose
+    co.argtypes = [vp] * 4 + [i32] * 5 + [vp]
+    co.restype = i32
+    assert co(p, p, None, p, 3, 1, 2, 128, 128, None) in (-6, -7)
+    assert co(p, p, None, None, 3, 1, 2, 128, 128, None) == -1
+    assert co(p, p, None, p, 0, 1, 2, 128, 128, None) == -2
+    assert co(p, p, vp(4100), p, 3, 1, 2, 128, 128, None) == -5      # states need 16 bytes
+    assert co(p, p, None, p, 3, 1, 2, 96, 96, None) == -3
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

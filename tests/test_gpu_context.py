@@ -1,0 +1,118 @@
+"""GPU tests of the context-parallel building blocks (through the C ABI):
+kda_chunk_transition against the oracle's transition_np, kda_state_compose
+against the composition written out in numpy, and the whole schedule
+(chunk_fwd_context_parallel: segment exit states and transitions, composition,
+reruns from the entry states) against the oracle and the single-pass prefill.
+
+Transitions and compositions are computed in fp32 from exactly widened inputs,
+so they are held to the fp32 bar (rel-L2 <= 1e-4) for either input dtype;
+outputs and final states of the schedule to the prefill tolerances.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_102_amd import inputs as kin
+from oracle import transition_np
+from tests.parity import assert_close, errors, oracle_fixed, oracle_pair_slices
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible MI355X")
+    from gated_delta_rule_102_amd import kda
+    kda.load_library()
+    torch.cuda.set_device(0)
+    yield
+
+
+@pytest.mark.parametrize("dtype,D,T", [(torch.bfloat16, 128, 150), (torch.bfloat16, 64, 64),
+                                       (torch.float32, 64, 131), (torch.bfloat16, 128, 1)])
+def test_transition_matches_oracle(dtype, D, T):
+    """Standard decays (g = max(-5, -softplus(N(0,1)))) forget fast: after ~100 tokens
+    every entry of P lies below fp32's normal range (max |P| ~ 1e-42 at T = 150), so
+    the check there is absolute.  With slow decay (g ~ U(-0.05, 0)) P stays O(1) and
+    the fp32 relative bar applies."""
+    from gated_delta_rule_102_amd import kda
+    B, H = 2, 2
+    d = kin.make_prefill(B, T, H, D, D, dtype=dtype, seed=500 + T + D)
+    gen = torch.Generator().manual_seed(600 + T + D)
+    slow = (-0.05 * torch.rand(d["g"].shape, generator=gen)).to(dtype)
+    for name, g, rel_bar in (("standard decay", d["g"], None), ("slow decay", slow, 1e-4)):
+        P = kda.kda_chunk_transition(d["q"].to(DEV), d["k"].to(DEV), g.to(DEV), d["beta"].to(DEV))
+        torch.cuda.synchronize()
+        for b in range(B):
+            ref = transition_np(d["k"][b], g[b], d["beta"][b])
+            mx, rel = errors(P[b].cpu().numpy(), ref)
+            assert mx <= 1e-5, f"{name} b={b}: max_abs {mx:.3e}"
+            if rel_bar is not None:
+                assert rel <= rel_bar, f"{name} b={b}: rel_l2 {rel:.3e}"
+
+
+def test_compose_matches_numpy():
+    from gated_delta_rule_102_amd import kda
+    R, B, H, D = 5, 2, 3, 128
+    gen = torch.Generator().manual_seed(510)
+    P = 0.1 * torch.randn((R, B, H, D, D), generator=gen)
+    Rp = torch.randn((R, B, H, D, D), generator=gen)
+    s0 = torch.randn((B, H, D, D), generator=gen)
+    for init in (s0, None):
+        ent = kda.kda_state_compose(P.to(DEV), Rp.to(DEV), None if init is None else init.to(DEV))
+        torch.cuda.synchronize()
+        S = np.zeros((B, H, D, D)) if init is None else init.double().numpy()
+        assert np.allclose(ent[0].cpu().numpy(), S)
+        for r in range(R):
+            S = np.einsum("bhij,bhjk->bhik", P[r].double().numpy(), S) + Rp[r].double().numpy()
+            _, rel = errors(ent[r + 1].cpu().numpy(), S)
+            assert rel <= 1e-5, f"entry {r + 1}: {rel:.3e}"
+
+
+@pytest.mark.parametrize("T,seg", [(1000, 256), (777, 300), (200, 64)])
+def test_context_parallel_schedule_small(T, seg):
+    """Segments of 256 (ragged last), 300 (not chunk-aligned) and 64 tokens."""
+    from gated_delta_rule_102_amd import kda
+    B, H, D = 2, 2, 128
+    d = kin.make_prefill(B, T, H, D, D, dtype=torch.bfloat16, seed=520 + T, nonzero_state=True)
+    d["scale"] = 1.0 / math.sqrt(D)
+    gd = {x: d[x].to(DEV) for x in ("q", "k", "v", "g", "beta", "initial_state")}
+    out, fin, entry = kda.chunk_fwd_context_parallel(gd["q"], gd["k"], gd["v"], gd["g"], gd["beta"],
+                                                     seg, d["scale"], gd["initial_state"])
+    out1, fin1 = kda.kda_chunk_fwd(gd["q"], gd["k"], gd["v"], gd["g"], gd["beta"], d["scale"],
+                                   gd["initial_state"])
+    torch.cuda.synchronize()
+    ref_o, ref_s = oracle_fixed(d)
+    assert_close("cp out", out, ref_o.reshape(out.shape), torch.bfloat16)
+    assert_close("cp final", fin, ref_s.reshape(fin.shape), torch.bfloat16)
+    assert entry.shape[0] == -(-T // seg) + 1
+    # against the single pass: the same bf16 kernels on different chunk boundaries
+    assert_close("cp vs single out", out, out1.float().cpu().numpy(), torch.bfloat16)
+    assert_close("cp vs single final", fin, fin1.cpu().numpy(), torch.bfloat16)
+
+
+def test_context_parallel_long_sequence():
+    """One sequence of 65536 tokens, 32 heads, d = 128, in 8 segments of 8192: the
+    final state against the single-pass prefill everywhere and against the oracle on
+    two sampled heads, with the outputs of those heads."""
+    from gated_delta_rule_102_amd import kda
+    B, T, H, D = 1, 65536, 32, 128
+    d = kin.make_prefill(B, T, H, D, D, dtype=torch.bfloat16, seed=530, device=DEV)
+    scale = 1.0 / math.sqrt(D)
+    out, fin, _ = kda.chunk_fwd_context_parallel(d["q"], d["k"], d["v"], d["g"], d["beta"],
+                                                 8192, scale)
+    _, fin1 = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], scale)
+    torch.cuda.synchronize()
+    assert_close("cp vs single final", fin, fin1.cpu().numpy(), torch.bfloat16)
+    pairs = [(0, 5), (0, 30)]
+    dc = {k: d[k].cpu() for k in ("q", "k", "v", "g", "beta")}
+    dc["scale"] = scale
+    refs = oracle_pair_slices(dc, pairs, [(0, T)], workers=2)
+    for (b, h), (ro, rs) in zip(pairs, refs):
+        assert_close(f"cp out h={h}", out[b, :, h], ro, torch.bfloat16)
+        assert_close(f"cp final h={h}", fin[b, h], rs, torch.bfloat16)

@@ -557,3 +557,44 @@ def test_backward_pins_catch_planted_mistakes(kind, monkeypatch):
     xm["k"][idx] -= h
     fd = (_loss(xp, d_out, d_fin, 0.7) - _loss(xm, d_out, d_fin, 0.7)) / (2 * h)
     assert abs(gr["dk"][0][idx] - fd) > 1e-4
+
+
+# ---------------------------------------------------------------- transition (context parallelism)
+
+
+def test_transition_is_the_linear_part_of_the_c_oracle():
+    """The C oracle's exit state is affine in the entry state: S_T(S0) - S_T(0) = P S0
+    with P from transition_np, for random entry states (a separate implementation of
+    the recurrence on each side)."""
+    from oracle import transition_np
+    rng = np.random.default_rng(60)
+    T, H, dk, dv = 23, 2, 6, 5
+    q, k, v, g, beta = _rand_inputs(T, H, dk, dv, rng)
+    P = transition_np(k, g, beta)
+    _, s_zero = run(q, k, v, g, beta, 0.5, np.zeros((H, dk, dv)))
+    for _ in range(2):
+        s0 = rng.standard_normal((H, dk, dv))
+        _, s_t = run(q, k, v, g, beta, 0.5, s0)
+        np.testing.assert_allclose(s_t.reshape(H, dk, dv) - s_zero.reshape(H, dk, dv),
+                                   np.einsum("hij,hjk->hik", P, s0), rtol=1e-10, atol=1e-12)
+
+
+def test_transition_special_cases():
+    """beta = 0: pure decay, P = Diag(exp(sum g)).  One token with g = 0, beta = 1 and
+    a unit key: the projector I - k k^T (P k = 0, P^2 = P).  Segments compose: the
+    transition of a concatenation is the later transition times the earlier one."""
+    from oracle import transition_np
+    rng = np.random.default_rng(61)
+    T, H, dk = 9, 2, 5
+    _, k, _, g, _ = _rand_inputs(T, H, dk, 3, rng)
+    P = transition_np(k, g, np.zeros((T, H)))
+    for h in range(H):
+        np.testing.assert_allclose(P[h], np.diag(np.exp(g[:, h].sum(0))), rtol=1e-13, atol=0)
+    P1 = transition_np(k[:1], np.zeros((1, H, dk)), np.ones((1, H)))
+    for h in range(H):
+        np.testing.assert_allclose(P1[h] @ k[0, h], 0.0, atol=1e-14)
+        np.testing.assert_allclose(P1[h] @ P1[h], P1[h], atol=1e-14)
+    beta = rng.uniform(0, 1, (T, H))
+    Pa, Pb, Pab = transition_np(k[:4], g[:4], beta[:4]), transition_np(k[4:], g[4:], beta[4:]), \
+        transition_np(k, g, beta)
+    np.testing.assert_allclose(Pab, np.einsum("hij,hjk->hik", Pb, Pa), rtol=1e-12, atol=1e-14)
