@@ -32,16 +32,21 @@ namespace {
 
 // ---------------------------------------------------------------- scans
 
-// State tiles of one workgroup: D x 32 columns = (D/16) x 2 tiles, D/32 per wave.
+// Scan workgroups have 8 wavefronts (two per SIMD, so one's LDS and memory waits
+// overlap the other's matrix work).  State tiles of one workgroup: D x 32 columns
+// = (D/16) x 2 tiles, D/64 per wavefront; the 64 x 32 per-chunk products are
+// 4 x 2 tiles, one per wavefront.
+constexpr int kScanThreads = 512;
+
 template <int D>
 struct ScanTiles {
-  static constexpr int NTW = D / 32;
+  static constexpr int NTW = D / 64;
   static __device__ __forceinline__ int rt(int wave, int x) { return (wave * NTW + x) >> 1; }
   static __device__ __forceinline__ int ct(int wave, int x) { return (wave * NTW + x) & 1; }
 };
 
 template <int D, typename TIn>
-__global__ __launch_bounds__(256) void bwd_fwd_scan_kernel(const TIn* __restrict__ v,
+__global__ __launch_bounds__(kScanThreads) void bwd_fwd_scan_kernel(const TIn* __restrict__ v,
                                                            const float* __restrict__ s0,
                                                            const float* __restrict__ ws,
                                                            float* __restrict__ st,
@@ -70,20 +75,24 @@ __global__ __launch_bounds__(256) void bwd_fwd_scan_kernel(const TIn* __restrict
     const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
     S[x] = s0 ? get(s0 + static_cast<int64_t>(bh) * D * D + 16 * rt * D + c0 + 16 * ct, D) : zero4();
   }
+  // the next chunk's operands are loaded into registers while this chunk computes
+  GTile<kScanThreads, CR, CR> t_tb;
+  GTile<kScanThreads, CR, D> t_w, t_kt;
+  ITile<kScanThreads, SL, TIn> t_v;
+  float lm;
+  auto issue = [&](int c) {
+    const float* w = ws + (static_cast<int64_t>(bh) * nc + c) * L::WS;
+    const int64_t row0 = (static_cast<int64_t>(b) * T + static_cast<int64_t>(c) * CR) * H + h;
+    t_tb.load(w + L::TB, CR);
+    t_w.load(w + L::W, D);
+    t_kt.load(w + L::KT, D);
+    t_v.load(v + row0 * D + c0, static_cast<int64_t>(H) * D, min(CR, T - c * CR));
+    lm = w[L::LAM + (tid & (D - 1))];
+  };
+  issue(0);
   for (int c = 0; c < nc; ++c) {
     const int64_t item = static_cast<int64_t>(bh) * nc + c;
-    const float* w = ws + item * L::WS;
-    const int nrow = min(CR, T - c * CR);
-    const int64_t row0 = (static_cast<int64_t>(b) * T + static_cast<int64_t>(c) * CR) * H + h;
     {
-      GTile<256, CR, CR> t_tb;
-      GTile<256, CR, D> t_w, t_kt;
-      ITile<256, SL, TIn> t_v;
-      t_tb.load(w + L::TB, CR);
-      t_w.load(w + L::W, D);
-      t_kt.load(w + L::KT, D);
-      t_v.load(v + row0 * D + c0, static_cast<int64_t>(H) * D, nrow);
-      float lm = w[L::LAM + (tid & (D - 1))];
       t_tb.pin_all();
       t_w.pin_all();
       t_kt.pin_all();
@@ -95,6 +104,9 @@ __global__ __launch_bounds__(256) void bwd_fwd_scan_kernel(const TIn* __restrict
       t_v.store(Vs, LV);
       if (tid < D) Lm[tid] = lm;
     }
+    // the next chunk's loads go out before this step's stores: loads and stores
+    // retire in order, so the next wait for those loads does not wait for the stores
+    if (c + 1 < nc) issue(c + 1);
 #pragma unroll
     for (int x = 0; x < ST::NTW; ++x) {
       const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
@@ -102,9 +114,8 @@ __global__ __launch_bounds__(256) void bwd_fwd_scan_kernel(const TIn* __restrict
       put(st + item * D * D + 16 * rt * D + c0 + 16 * ct, D, S[x]);
     }
     __syncthreads();
-#pragma unroll
-    for (int y = 0; y < 2; ++y) {   // Delta = Tb V - W S: 4 x 2 tiles
-      const int j = wave * 2 + y, rt = j >> 1, ct = j & 1;
+    {   // Delta = Tb V - W S: 4 x 2 tiles
+      const int j = wave, rt = j >> 1, ct = j & 1;
       const f32x4_t tv = mm<false, false>(zero4(), TBs + 16 * rt * LS, LS, Vs + 16 * ct, LV, CR);
       const f32x4_t wsv = mm<false, false>(zero4(), Ws + 16 * rt * LD, LD, Ss + 16 * ct, LV, D);
       f32x4_t d;
@@ -128,7 +139,7 @@ __global__ __launch_bounds__(256) void bwd_fwd_scan_kernel(const TIn* __restrict
 }
 
 template <int D, typename TIn>
-__global__ __launch_bounds__(256) void bwd_scan_kernel(const TIn* __restrict__ dout,
+__global__ __launch_bounds__(kScanThreads) void bwd_scan_kernel(const TIn* __restrict__ dout,
                                                        const float* __restrict__ dsT,
                                                        const float* __restrict__ ws,
                                                        float* __restrict__ dst,
@@ -161,22 +172,30 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(const TIn* __restrict__ d
     const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
     dS[x] = dsT ? get(dsT + static_cast<int64_t>(bh) * D * D + 16 * rt * D + c0 + 16 * ct, D) : zero4();
   }
+  // the previous chunk's operands are loaded into registers while this chunk computes
+  GTile<kScanThreads, CR, D> t_kt, t_w, t_qp;
+  GTile<kScanThreads, CR, CR> t_p, t_tb;
+  ITile<kScanThreads, SL, TIn> t_do;
+  float lm;
+  auto issue = [&](int c) {
+    const float* w = ws + (static_cast<int64_t>(bh) * nc + c) * L::WS;
+    const int64_t row0 = (static_cast<int64_t>(b) * T + static_cast<int64_t>(c) * CR) * H + h;
+    t_kt.load(w + L::KT, D);
+    t_qp.load(w + L::QP, D);
+    t_w.load(w + L::W, D);
+    t_p.load(w + L::PP, CR);
+    t_tb.load(w + L::TB, CR);
+    t_do.load(dout + row0 * D + c0, rs, min(CR, T - c * CR));
+    lm = w[L::LAM + (tid & (D - 1))];
+  };
+  issue(nc - 1);
   for (int c = nc - 1; c >= 0; --c) {
     const int64_t item = static_cast<int64_t>(bh) * nc + c;
-    const float* w = ws + item * L::WS;
     const int nrow = min(CR, T - c * CR);
     const int64_t row0 = (static_cast<int64_t>(b) * T + static_cast<int64_t>(c) * CR) * H + h;
     {
-      GTile<256, CR, D> t_kt, t_w;
-      GTile<256, CR, CR> t_p, t_tb;
-      ITile<256, SL, TIn> t_do;
-      t_kt.load(w + L::KT, D);
-      t_w.load(w + L::W, D);
-      t_p.load(w + L::PP, CR);
-      t_tb.load(w + L::TB, CR);
-      t_do.load(dout + row0 * D + c0, rs, nrow);
-      float lm = w[L::LAM + (tid & (D - 1))];
       t_kt.pin_all();
+      t_qp.pin_all();
       t_w.pin_all();
       t_p.pin_all();
       t_tb.pin_all();
@@ -193,21 +212,30 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(const TIn* __restrict__ d
     for (int x = 0; x < ST::NTW; ++x) {
       const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
       put(dSs + 16 * rt * LV + 16 * ct, LV, dS[x]);
+    }
+    __syncthreads();
+    f32x4_t u;
+    {   // dU = Kt dS
+      const int j = wave, rt = j >> 1, ct = j & 1;
+      u = mm<false, false>(zero4(), KQs + 16 * rt * LD, LD, dSs + 16 * ct, LV, D);
+      put(dUs + 16 * rt * LV + 16 * ct, LV, u);
+    }
+    __syncthreads();
+    t_qp.store(KQs, LD);   // Kt is no longer needed
+    // every prefetched register is now consumed: the previous chunk's loads go out
+    // before this step's global stores, which then never hold up the next wait
+    if (c > 0) issue(c - 1);
+#pragma unroll
+    for (int x = 0; x < ST::NTW; ++x) {
+      const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
       put(dst + item * D * D + 16 * rt * D + c0 + 16 * ct, D, dS[x]);
     }
-    __syncthreads();
-#pragma unroll
-    for (int y = 0; y < 2; ++y) {   // dU = Kt dS
-      const int j = wave * 2 + y, rt = j >> 1, ct = j & 1;
-      const f32x4_t u = mm<false, false>(zero4(), KQs + 16 * rt * LD, LD, dSs + 16 * ct, LV, D);
-      put(dUs + 16 * rt * LV + 16 * ct, LV, u);
+    {
+      const int j = wave, rt = j >> 1, ct = j & 1;
       put(du + item * CR * D + 16 * rt * D + c0 + 16 * ct, D, u);
     }
-    __syncthreads();
-    g2l<256, CR, D>(KQs, LD, w + L::QP, D);
-#pragma unroll
-    for (int y = 0; y < 2; ++y) {   // dV = P^T dO + Tb^T dU
-      const int j = wave * 2 + y, rt = j >> 1, ct = j & 1;
+    {   // dV = P^T dO + Tb^T dU
+      const int j = wave, rt = j >> 1, ct = j & 1;
       f32x4_t acc = mm<true, false>(zero4(), Ps + 16 * rt, LS, dOs + 16 * ct, LV, CR);
       acc = mm<true, false>(acc, TBs + 16 * rt, LS, dUs + 16 * ct, LV, CR);
 #pragma unroll
@@ -338,6 +366,8 @@ __global__ __launch_bounds__(512) void bwd_grad_dv_kernel(const TIn* __restrict_
 
 // ---------------------------------------------------------------- 64 x 64 algebra
 
+constexpr int kNnThreads = 512;   // 8 wavefronts: two per SIMD
+
 template <int D>
 struct NnLds {
   static constexpr int LD = D + 4;
@@ -347,7 +377,7 @@ struct NnLds {
 };
 
 template <int D, typename TIn>
-__global__ __launch_bounds__(256) void bwd_grad_nn_kernel(const TIn* __restrict__ k,
+__global__ __launch_bounds__(kNnThreads) void bwd_grad_nn_kernel(const TIn* __restrict__ k,
                                                           const TIn* __restrict__ beta,
                                                           const float* __restrict__ ws,
                                                           const float* __restrict__ g1,
@@ -383,8 +413,8 @@ __global__ __launch_bounds__(256) void bwd_grad_nn_kernel(const TIn* __restrict_
   constexpr int CT = D / 16;
 
   {
-    GTile<256, CR, D> t_g, t_dq;
-    GTile<256, CR, CR> t_p;
+    GTile<kNnThreads, CR, D> t_g, t_dq;
+    GTile<kNnThreads, CR, CR> t_p;
     t_g.load(w + L::G, D);
     t_dq.load(a1 + L::DQP, D);
     t_p.load(w + L::PP, CR);
@@ -399,8 +429,8 @@ __global__ __launch_bounds__(256) void bwd_grad_nn_kernel(const TIn* __restrict_
     if (tid < CR) BT[tid] = tid < p.nrow ? bt0 : 0.f;
   }
   {
-    GTile<256, CR, D> t_dw;
-    GTile<256, CR, CR> t_tb;
+    GTile<kNnThreads, CR, D> t_dw;
+    GTile<kNnThreads, CR, CR> t_tb;
     t_dw.load(a1 + L::DW, D);
     t_tb.load(w + L::TB, CR);
     t_dw.pin_all();
@@ -410,22 +440,22 @@ __global__ __launch_bounds__(256) void bwd_grad_nn_kernel(const TIn* __restrict_
   }
   __syncthreads();
   {   // Kg = k e^G in place of G (each element read and written by one thread)
-    ITile<256, D, TIn> kt;
+    ITile<kNnThreads, D, TIn> kt;
     kt.load(kc, rs, p.nrow);
     kt.pin_all();
 #pragma unroll
     for (int j = 0; j < kt.PER; ++j) {
-      const int e = tid + j * 256, t = e / D, i = e - t * D;
+      const int e = tid + j * kNnThreads, t = e / D, i = e - t * D;
       Kg[t * LD + i] = kt.r[j] * expf(Kg[t * LD + i]);
     }
   }
   __syncthreads();
 
-  // dP_tot = dP - dQ' Kg^T and dTb_part = dTb + dW Kg^T (tiles wave + 4x)
-  f32x4_t dPt[4], dTt[4];
+  // dP_tot = dP - dQ' Kg^T and dTb_part = dTb + dW Kg^T (tiles wave + 8x)
+  f32x4_t dPt[2], dTt[2];
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    const int j = wave + 4 * x, rt = j >> 2, ct = j & 3;
+  for (int x = 0; x < 2; ++x) {
+    const int j = wave + 8 * x, rt = j >> 2, ct = j & 3;
     const f32x4_t qk = mm<false, true>(zero4(), dQ + 16 * rt * LD, LD, Kg + 16 * ct * LD, LD, D);
     const f32x4_t wk = mm<false, true>(zero4(), dW + 16 * rt * LD, LD, Kg + 16 * ct * LD, LD, D);
     dPt[x] = get(a1 + L::DP + 16 * rt * CR + 16 * ct, CR);
@@ -437,7 +467,7 @@ __global__ __launch_bounds__(256) void bwd_grad_nn_kernel(const TIn* __restrict_
     }
   }
   // dKg = -P^T dQ' + Tb^T dW
-  for (int j = wave; j < 4 * CT; j += 4) {
+  for (int j = wave; j < 4 * CT; j += 8) {
     const int rt = j / CT, ct = j - rt * CT;
     const f32x4_t pq = mm<true, false>(zero4(), Ps + 16 * rt, LS, dQ + 16 * ct, LD, CR);
     f32x4_t acc = mm<true, false>(zero4(), TBs + 16 * rt, LS, dW + 16 * ct, LD, CR);
@@ -448,12 +478,12 @@ __global__ __launch_bounds__(256) void bwd_grad_nn_kernel(const TIn* __restrict_
   __syncthreads();
 
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    const int j = wave + 4 * x, rt = j >> 2, ct = j & 3;
+  for (int x = 0; x < 2; ++x) {
+    const int j = wave + 8 * x, rt = j >> 2, ct = j & 3;
     put(B0 + 16 * rt * LS + 16 * ct, LS, dPt[x]);
   }
   {
-    GTile<256, CR, CR> t_m, t_ti;
+    GTile<kNnThreads, CR, CR> t_m, t_ti;
     t_m.load(w + L::MP, CR);
     t_ti.load(w + L::TI, CR);
     t_m.store(B1, LS);
@@ -462,8 +492,8 @@ __global__ __launch_bounds__(256) void bwd_grad_nn_kernel(const TIn* __restrict_
   __syncthreads();
   // dTb_tot = dTb_part + scale M'^T dP_tot;  dM' = scale (dP_tot Tb^T) on s <= t
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    const int j = wave + 4 * x, rt = j >> 2, ct = j & 3;
+  for (int x = 0; x < 2; ++x) {
+    const int j = wave + 8 * x, rt = j >> 2, ct = j & 3;
     const f32x4_t mp = mm<true, false>(zero4(), B1 + 16 * rt, LS, B0 + 16 * ct, LS, CR);
     f32x4_t dm = mm<false, true>(zero4(), B0 + 16 * rt * LS, LS, TBs + 16 * ct * LS, LS, CR);
 #pragma unroll
@@ -486,23 +516,23 @@ __global__ __launch_bounds__(256) void bwd_grad_nn_kernel(const TIn* __restrict_
   if (tid < CR) {
     for (int t = 0; t < CR; ++t) db += B2[t * LS + tid] * B3[t * LS + tid];
   }
-  f32x4_t X[4];   // X = dTi Ti^T
+  f32x4_t X[2];   // X = dTi Ti^T
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    const int j = wave + 4 * x, rt = j >> 2, ct = j & 3;
+  for (int x = 0; x < 2; ++x) {
+    const int j = wave + 8 * x, rt = j >> 2, ct = j & 3;
     X[x] = mm<false, true>(zero4(), B4 + 16 * rt * LS, LS, B2 + 16 * ct * LS, LS, CR);
   }
   __syncthreads();
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    const int j = wave + 4 * x, rt = j >> 2, ct = j & 3;
+  for (int x = 0; x < 2; ++x) {
+    const int j = wave + 8 * x, rt = j >> 2, ct = j & 3;
     put(B0 + 16 * rt * LS + 16 * ct, LS, X[x]);
   }
   __syncthreads();
   // dA = -Ti^T X on s < t;  dA' = Diag(beta) dA
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    const int j = wave + 4 * x, rt = j >> 2, ct = j & 3;
+  for (int x = 0; x < 2; ++x) {
+    const int j = wave + 8 * x, rt = j >> 2, ct = j & 3;
     f32x4_t da = mm<true, false>(zero4(), B2 + 16 * rt, LS, B0 + 16 * ct, LS, CR);
     f32x4_t dap;
 #pragma unroll
@@ -691,16 +721,16 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
   const TIn* beta = static_cast<const TIn*>(a.beta);
   const TIn* dout = static_cast<const TIn*>(a.d_out);
   const int scan_blocks = a.B * a.H * (D / SL);
-  hipLaunchKernelGGL((chunk_ops_kernel<D, TIn>), dim3(items), dim3(256), 0, a.stream, q, k, g, beta,
+  hipLaunchKernelGGL((chunk_ops_kernel<D, TIn>), dim3(items), dim3(kOpsThreads), 0, a.stream, q, k, g, beta,
                      ws, a.T, a.H, nc, a.scale);
-  hipLaunchKernelGGL((bwd_fwd_scan_kernel<D, TIn>), dim3(scan_blocks), dim3(256), 0, a.stream, v,
+  hipLaunchKernelGGL((bwd_fwd_scan_kernel<D, TIn>), dim3(scan_blocks), dim3(kScanThreads), 0, a.stream, v,
                      a.initial_state, ws, st, dl, a.T, a.H, nc);
-  hipLaunchKernelGGL((bwd_scan_kernel<D, TIn>), dim3(scan_blocks), dim3(256), 0, a.stream, dout,
+  hipLaunchKernelGGL((bwd_scan_kernel<D, TIn>), dim3(scan_blocks), dim3(kScanThreads), 0, a.stream, dout,
                      a.d_final_state, ws, dst, du, static_cast<TIn*>(a.dv), a.d_initial_state,
                      a.T, a.H, nc);
   hipLaunchKernelGGL((bwd_grad_dv_kernel<D, TIn>), dim3(items), dim3(512), 0, a.stream, v, dout,
                      st, dst, dl, du, g1, a.T, a.H, nc);
-  hipLaunchKernelGGL((bwd_grad_nn_kernel<D, TIn>), dim3(items), dim3(256), 0, a.stream, k, beta,
+  hipLaunchKernelGGL((bwd_grad_nn_kernel<D, TIn>), dim3(items), dim3(kNnThreads), 0, a.stream, k, beta,
                      ws, g1, g2, static_cast<TIn*>(a.dbeta), a.T, a.H, nc, a.scale);
   hipLaunchKernelGGL((bwd_grad_decay_kernel<D, TIn>), dim3(items), dim3(512), 0, a.stream, q, k,
                      ws, g1, g2, static_cast<TIn*>(a.dq), static_cast<TIn*>(a.dk),

@@ -205,10 +205,15 @@ __device__ __forceinline__ ChunkPos chunk_pos(int item, int T, int H, int nc) {
   return p;
 }
 
+// Threads of one chunk_ops workgroup: 8 wavefronts, two per SIMD, so that one
+// wavefront's LDS and memory latency hides behind the other's work.
+constexpr int kOpsThreads = 512;
+constexpr int kOpsWaves = kOpsThreads / 64;
+
 // ---------------------------------------------------------------- chunk operands
 
 template <int D, typename TIn>
-__global__ __launch_bounds__(256) void chunk_ops_kernel(const TIn* __restrict__ q,
+__global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __restrict__ q,
                                                        const TIn* __restrict__ k,
                                                        const TIn* __restrict__ g,
                                                        const TIn* __restrict__ beta,
@@ -235,10 +240,10 @@ __global__ __launch_bounds__(256) void chunk_ops_kernel(const TIn* __restrict__ 
   float* w = ws + static_cast<int64_t>(blockIdx.x) * L::WS;
 
   {
-    ITile<256, D, TIn> gt;
+    ITile<kOpsThreads, D, TIn> gt;
     gt.load(gc, rs, p.nrow);
     gt.pin_all();
-    for (int e = tid; e < 3 * CR * LS; e += 256) S0[e] = 0.f;
+    for (int e = tid; e < 3 * CR * LS; e += kOpsThreads) S0[e] = 0.f;
     const float bt = to_f32(beta[p.row0 + static_cast<int64_t>(min(tid & (CR - 1), p.nrow - 1)) * H]);
     if (tid < CR) BT[tid] = tid < p.nrow ? bt : 0.f;
     gt.store(R0, LD);
@@ -262,12 +267,12 @@ __global__ __launch_bounds__(256) void chunk_ops_kernel(const TIn* __restrict__ 
     w[L::LAM + tid] = expf(R0[(CR - 1) * LD + tid]);
   }
   {
-    ITile<256, D, TIn> kt;
+    ITile<kOpsThreads, D, TIn> kt;
     kt.load(kc, rs, p.nrow);
     kt.pin_all();
 #pragma unroll
     for (int j = 0; j < kt.PER; ++j) {
-      const int e = tid + j * 256, t = e / D, i = e - t * D;
+      const int e = tid + j * kOpsThreads, t = e / D, i = e - t * D;
       const float G = R0[t * LD + i], RI = R0[(t | 15) * LD + i], Gl = R0[(CR - 1) * LD + i];
       const float kv = kt.r[j];
       R1[t * LD + i] = kv * expf(G - RI);
@@ -280,7 +285,7 @@ __global__ __launch_bounds__(256) void chunk_ops_kernel(const TIn* __restrict__ 
 
   // A' and M' by sub-tile pairs (I, J), J <= I: 10 tiles each
   auto pair_gram = [&](float* dst, bool strict) {
-    for (int pt = wave; pt < 10; pt += 4) {
+    for (int pt = wave; pt < 10; pt += kOpsWaves) {
       int I = 0;
       while ((I + 1) * (I + 2) / 2 <= pt) ++I;
       const int J = pt - I * (I + 1) / 2;
@@ -301,12 +306,12 @@ __global__ __launch_bounds__(256) void chunk_ops_kernel(const TIn* __restrict__ 
   pair_gram(S0, true);
   __syncthreads();
   {   // q rowf into R1
-    ITile<256, D, TIn> qt;
+    ITile<kOpsThreads, D, TIn> qt;
     qt.load(qc, rs, p.nrow);
     qt.pin_all();
 #pragma unroll
     for (int j = 0; j < qt.PER; ++j) {
-      const int e = tid + j * 256, t = e / D, i = e - t * D;
+      const int e = tid + j * kOpsThreads, t = e / D, i = e - t * D;
       const float G = R0[t * LD + i], RI = R0[(t | 15) * LD + i];
       R1[t * LD + i] = qt.r[j] * expf(G - RI);
     }
@@ -314,13 +319,13 @@ __global__ __launch_bounds__(256) void chunk_ops_kernel(const TIn* __restrict__ 
   __syncthreads();
   pair_gram(S1, false);
   __syncthreads();
-  l2g<256, CR, CR>(w + L::AP, CR, S0, LS);
-  l2g<256, CR, CR>(w + L::MP, CR, S1, LS);
+  l2g<kOpsThreads, CR, CR>(w + L::AP, CR, S0, LS);
+  l2g<kOpsThreads, CR, CR>(w + L::MP, CR, S1, LS);
 
   // Ti = (I + Diag(beta) A')^-1: diagonal 16 x 16 blocks by substitution (one
   // column per lane), then the blocks below them level by level:
   //   Ti_IJ = -Ti_II Diag(beta_I) sum_{J <= m < I} A'_Im Ti_mJ
-  if (lane < 16) {
+  if (wave < 4 && lane < 16) {
     const int I = wave, j = lane;
     float x[16];
 #pragma unroll
@@ -351,21 +356,21 @@ __global__ __launch_bounds__(256) void chunk_ops_kernel(const TIn* __restrict__ 
     }
     __syncthreads();
   }
-  for (int e = tid; e < CR * CR; e += 256) {
+  for (int e = tid; e < CR * CR; e += kOpsThreads) {
     const int t = e / CR, s = e - t * CR;
     const float ti = S2[t * LS + s];
     w[L::TI + e] = ti;
     w[L::TB + e] = ti * BT[s];
   }
   {   // k e^G into R1, scale q e^G into R2
-    ITile<256, D, TIn> kt, qt;
+    ITile<kOpsThreads, D, TIn> kt, qt;
     kt.load(kc, rs, p.nrow);
     qt.load(qc, rs, p.nrow);
     kt.pin_all();
     qt.pin_all();
 #pragma unroll
     for (int j = 0; j < kt.PER; ++j) {
-      const int e = tid + j * 256, t = e / D, i = e - t * D;
+      const int e = tid + j * kOpsThreads, t = e / D, i = e - t * D;
       const float eg = expf(R0[t * LD + i]);
       R1[t * LD + i] = kt.r[j] * eg;
       R2[t * LD + i] = scale * qt.r[j] * eg;
@@ -374,7 +379,7 @@ __global__ __launch_bounds__(256) void chunk_ops_kernel(const TIn* __restrict__ 
   __syncthreads();
 
   // P = scale M' Tb (into S0 and the workspace); W = Tb (k e^G)
-  for (int j = wave; j < 16; j += 4) {
+  for (int j = wave; j < 16; j += kOpsWaves) {
     const int rt = j >> 2, ct = j & 3;
     f32x4_t acc = mm<false, false>(zero4(), S1 + 16 * rt * LS, LS, S2 + 16 * ct, LS, CR);
     const float f = scale * BT[16 * ct + l16];
@@ -384,7 +389,7 @@ __global__ __launch_bounds__(256) void chunk_ops_kernel(const TIn* __restrict__ 
     put(w + L::PP + 16 * rt * CR + 16 * ct, CR, acc);
   }
   constexpr int CT = D / 16;
-  for (int j = wave; j < 4 * CT; j += 4) {
+  for (int j = wave; j < 4 * CT; j += kOpsWaves) {
     const int rt = j / CT, ct = j - rt * CT;
     const f32x4_t acc = mm<false, false, true>(zero4(), S2 + 16 * rt * LS, LS, R1 + 16 * ct, LD,
                                                CR, BT);
@@ -392,7 +397,7 @@ __global__ __launch_bounds__(256) void chunk_ops_kernel(const TIn* __restrict__ 
   }
   __syncthreads();
   // Q' = scale q e^G - P (k e^G)
-  for (int j = wave; j < 4 * CT; j += 4) {
+  for (int j = wave; j < 4 * CT; j += kOpsWaves) {
     const int rt = j / CT, ct = j - rt * CT;
     const f32x4_t pk = mm<false, false>(zero4(), S0 + 16 * rt * LS, LS, R1 + 16 * ct, LD, CR);
     f32x4_t acc = get(R2 + 16 * rt * LD + 16 * ct, LD);
