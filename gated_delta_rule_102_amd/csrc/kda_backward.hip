@@ -52,6 +52,7 @@ __global__ __launch_bounds__(kScanThreads) void bwd_fwd_scan_kernel(const TIn* _
                                                            float* __restrict__ st,
                                                            float* __restrict__ dl, int T, int H,
                                                            int nc) {
+  constexpr bool BF = IsBf16<TIn>::value;   // bf16 matrix-core operands for bf16 inputs
   using L = BwdLayout<D>;
   using ST = ScanTiles<D>;
   constexpr int LD = L::LD;
@@ -116,8 +117,8 @@ __global__ __launch_bounds__(kScanThreads) void bwd_fwd_scan_kernel(const TIn* _
     __syncthreads();
     {   // Delta = Tb V - W S: 4 x 2 tiles
       const int j = wave, rt = j >> 1, ct = j & 1;
-      const f32x4_t tv = mm<false, false>(zero4(), TBs + 16 * rt * LS, LS, Vs + 16 * ct, LV, CR);
-      const f32x4_t wsv = mm<false, false>(zero4(), Ws + 16 * rt * LD, LD, Ss + 16 * ct, LV, D);
+      const f32x4_t tv = mmx<BF, false, false>(zero4(), TBs + 16 * rt * LS, LS, Vs + 16 * ct, LV, CR);
+      const f32x4_t wsv = mmx<BF, false, false>(zero4(), Ws + 16 * rt * LD, LD, Ss + 16 * ct, LV, D);
       f32x4_t d;
 #pragma unroll
       for (int i = 0; i < 4; ++i) d[i] = tv[i] - wsv[i];
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(kScanThreads) void bwd_fwd_scan_kernel(const TIn* _
       f32x4_t acc;
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = Lm[16 * rt + 4 * g4 + i] * S[x][i];
-      S[x] = mm<true, false>(acc, KTs + 16 * rt, LD, Dls + 16 * ct, LV, CR);
+      S[x] = mmx<BF, true, false>(acc, KTs + 16 * rt, LD, Dls + 16 * ct, LV, CR);
     }
     __syncthreads();
   }
@@ -147,6 +148,8 @@ __global__ __launch_bounds__(kScanThreads) void bwd_scan_kernel(const TIn* __res
                                                        TIn* __restrict__ dv,
                                                        float* __restrict__ ds0, int T, int H,
                                                        int nc) {
+  // fp32 operands throughout: the bf16 form needs more registers than the two
+  // wavefronts per SIMD leave, and spills cost more than it saves
   using L = BwdLayout<D>;
   using ST = ScanTiles<D>;
   constexpr int LD = L::LD;
@@ -173,7 +176,7 @@ __global__ __launch_bounds__(kScanThreads) void bwd_scan_kernel(const TIn* __res
     dS[x] = dsT ? get(dsT + static_cast<int64_t>(bh) * D * D + 16 * rt * D + c0 + 16 * ct, D) : zero4();
   }
   // the previous chunk's operands are loaded into registers while this chunk computes
-  GTile<kScanThreads, CR, D> t_kt, t_w, t_qp;
+  GTile<kScanThreads, CR, D> t_kt, t_w;
   GTile<kScanThreads, CR, CR> t_p, t_tb;
   ITile<kScanThreads, SL, TIn> t_do;
   float lm;
@@ -181,7 +184,6 @@ __global__ __launch_bounds__(kScanThreads) void bwd_scan_kernel(const TIn* __res
     const float* w = ws + (static_cast<int64_t>(bh) * nc + c) * L::WS;
     const int64_t row0 = (static_cast<int64_t>(b) * T + static_cast<int64_t>(c) * CR) * H + h;
     t_kt.load(w + L::KT, D);
-    t_qp.load(w + L::QP, D);
     t_w.load(w + L::W, D);
     t_p.load(w + L::PP, CR);
     t_tb.load(w + L::TB, CR);
@@ -195,7 +197,6 @@ __global__ __launch_bounds__(kScanThreads) void bwd_scan_kernel(const TIn* __res
     const int64_t row0 = (static_cast<int64_t>(b) * T + static_cast<int64_t>(c) * CR) * H + h;
     {
       t_kt.pin_all();
-      t_qp.pin_all();
       t_w.pin_all();
       t_p.pin_all();
       t_tb.pin_all();
@@ -221,10 +222,14 @@ __global__ __launch_bounds__(kScanThreads) void bwd_scan_kernel(const TIn* __res
       put(dUs + 16 * rt * LV + 16 * ct, LV, u);
     }
     __syncthreads();
-    t_qp.store(KQs, LD);   // Kt is no longer needed
-    // every prefetched register is now consumed: the previous chunk's loads go out
-    // before this step's global stores, which then never hold up the next wait
-    if (c > 0) issue(c - 1);
+    {   // Q' replaces Kt (no longer needed); its loads and the previous chunk's go
+        // out before this step's global stores, so no wait holds for those stores
+      GTile<kScanThreads, CR, D> t_qp;
+      t_qp.load(ws + item * L::WS + L::QP, D);
+      if (c > 0) issue(c - 1);
+      t_qp.pin_all();
+      t_qp.store(KQs, LD);
+    }
 #pragma unroll
     for (int x = 0; x < ST::NTW; ++x) {
       const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
@@ -278,6 +283,7 @@ __global__ __launch_bounds__(512) void bwd_grad_dv_kernel(const TIn* __restrict_
                                                           const float* __restrict__ du,
                                                           float* __restrict__ g1, int T, int H,
                                                           int nc) {
+  constexpr bool BF = IsBf16<TIn>::value;   // bf16 matrix-core operands for bf16 inputs
   using L = BwdLayout<D>;
   __shared__ __attribute__((aligned(16))) float sm[2 * D * LV + 4 * CR * LV];
   float* Ss = sm;
@@ -331,10 +337,10 @@ __global__ __launch_bounds__(512) void bwd_grad_dv_kernel(const TIn* __restrict_
         const int m = j / NBIG, r = j - m * NBIG, rt = r / CT, ct = r - rt * CT;
         const float* A = (m == 0 ? dOs : m == 1 ? dUs : Dls) + 16 * rt * LV;
         const float* Bm = (m == 2 ? dSs : Ss) + 16 * ct * LV;
-        acc[x] = mm<false, true>(acc[x], A, LV, Bm, LV, SL);
+        acc[x] = mmx<BF, false, true>(acc[x], A, LV, Bm, LV, SL);
       } else {              // dP = dO V^T, dTb = dU V^T
         const int j2 = j - 3 * NBIG, m = j2 >> 4, rt = (j2 & 15) >> 2, ct = j2 & 3;
-        acc[x] = mm<false, true>(acc[x], (m == 0 ? dOs : dUs) + 16 * rt * LV, LV,
+        acc[x] = mmx<BF, false, true>(acc[x], (m == 0 ? dOs : dUs) + 16 * rt * LV, LV,
                                  Vs + 16 * ct * LV, LV, SL);
       }
     }
@@ -384,6 +390,7 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_nn_kernel(const TIn* __re
                                                           float* __restrict__ g2,
                                                           TIn* __restrict__ dbeta, int T, int H,
                                                           int nc, float scale) {
+  constexpr bool BF = IsBf16<TIn>::value;   // bf16 matrix-core operands for bf16 inputs
   using L = BwdLayout<D>;
   using NL = NnLds<D>;
   constexpr int LD = L::LD;
@@ -456,8 +463,8 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_nn_kernel(const TIn* __re
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     const int j = wave + 8 * x, rt = j >> 2, ct = j & 3;
-    const f32x4_t qk = mm<false, true>(zero4(), dQ + 16 * rt * LD, LD, Kg + 16 * ct * LD, LD, D);
-    const f32x4_t wk = mm<false, true>(zero4(), dW + 16 * rt * LD, LD, Kg + 16 * ct * LD, LD, D);
+    const f32x4_t qk = mmx<BF, false, true>(zero4(), dQ + 16 * rt * LD, LD, Kg + 16 * ct * LD, LD, D);
+    const f32x4_t wk = mmx<BF, false, true>(zero4(), dW + 16 * rt * LD, LD, Kg + 16 * ct * LD, LD, D);
     dPt[x] = get(a1 + L::DP + 16 * rt * CR + 16 * ct, CR);
     dTt[x] = get(a1 + L::DTB + 16 * rt * CR + 16 * ct, CR);
 #pragma unroll
@@ -469,8 +476,8 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_nn_kernel(const TIn* __re
   // dKg = -P^T dQ' + Tb^T dW
   for (int j = wave; j < 4 * CT; j += 8) {
     const int rt = j / CT, ct = j - rt * CT;
-    const f32x4_t pq = mm<true, false>(zero4(), Ps + 16 * rt, LS, dQ + 16 * ct, LD, CR);
-    f32x4_t acc = mm<true, false>(zero4(), TBs + 16 * rt, LS, dW + 16 * ct, LD, CR);
+    const f32x4_t pq = mmx<BF, true, false>(zero4(), Ps + 16 * rt, LS, dQ + 16 * ct, LD, CR);
+    f32x4_t acc = mmx<BF, true, false>(zero4(), TBs + 16 * rt, LS, dW + 16 * ct, LD, CR);
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] -= pq[i];
     put(a2 + L::DKG + 16 * rt * D + 16 * ct, D, acc);
@@ -494,8 +501,8 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_nn_kernel(const TIn* __re
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     const int j = wave + 8 * x, rt = j >> 2, ct = j & 3;
-    const f32x4_t mp = mm<true, false>(zero4(), B1 + 16 * rt, LS, B0 + 16 * ct, LS, CR);
-    f32x4_t dm = mm<false, true>(zero4(), B0 + 16 * rt * LS, LS, TBs + 16 * ct * LS, LS, CR);
+    const f32x4_t mp = mmx<BF, true, false>(zero4(), B1 + 16 * rt, LS, B0 + 16 * ct, LS, CR);
+    f32x4_t dm = mmx<BF, false, true>(zero4(), B0 + 16 * rt * LS, LS, TBs + 16 * ct * LS, LS, CR);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = 16 * rt + 4 * g4 + i, s = 16 * ct + l16;
@@ -520,7 +527,7 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_nn_kernel(const TIn* __re
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     const int j = wave + 8 * x, rt = j >> 2, ct = j & 3;
-    X[x] = mm<false, true>(zero4(), B4 + 16 * rt * LS, LS, B2 + 16 * ct * LS, LS, CR);
+    X[x] = mmx<BF, false, true>(zero4(), B4 + 16 * rt * LS, LS, B2 + 16 * ct * LS, LS, CR);
   }
   __syncthreads();
 #pragma unroll
@@ -533,7 +540,7 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_nn_kernel(const TIn* __re
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     const int j = wave + 8 * x, rt = j >> 2, ct = j & 3;
-    f32x4_t da = mm<true, false>(zero4(), B2 + 16 * rt, LS, B0 + 16 * ct, LS, CR);
+    f32x4_t da = mmx<BF, true, false>(zero4(), B2 + 16 * rt, LS, B0 + 16 * ct, LS, CR);
     f32x4_t dap;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -564,6 +571,7 @@ __global__ __launch_bounds__(512) void bwd_grad_decay_kernel(const TIn* __restri
                                                              TIn* __restrict__ dk,
                                                              TIn* __restrict__ dg, int T, int H,
                                                              int nc, float scale) {
+  constexpr bool BF = IsBf16<TIn>::value;   // bf16 matrix-core operands for bf16 inputs
   using L = BwdLayout<D>;
   constexpr int LD = L::LD;
   __shared__ __attribute__((aligned(16))) float sm[3 * CR * LD + 2 * CR * LS + 10 * D];
@@ -721,7 +729,7 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
   const TIn* beta = static_cast<const TIn*>(a.beta);
   const TIn* dout = static_cast<const TIn*>(a.d_out);
   const int scan_blocks = a.B * a.H * (D / SL);
-  hipLaunchKernelGGL((chunk_ops_kernel<D, TIn>), dim3(items), dim3(kOpsThreads), 0, a.stream, q, k, g, beta,
+  hipLaunchKernelGGL((chunk_ops_kernel<D, TIn, false>), dim3(items), dim3(kOpsThreads), 0, a.stream, q, k, g, beta,
                      ws, a.T, a.H, nc, a.scale);
   hipLaunchKernelGGL((bwd_fwd_scan_kernel<D, TIn>), dim3(scan_blocks), dim3(kScanThreads), 0, a.stream, v,
                      a.initial_state, ws, st, dl, a.T, a.H, nc);

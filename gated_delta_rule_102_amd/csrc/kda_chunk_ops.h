@@ -82,6 +82,62 @@ __device__ __forceinline__ f32x4_t mm(f32x4_t acc, const float* a, int lda, cons
   return acc;
 }
 
+// mm with bf16 operands when BF: the fp32 LDS operands are rounded to bf16 (round
+// to nearest even) and fed to the 16x16x32 bf16 matrix cores with fp32
+// accumulation, 8x the work per instruction of the fp32 16x16x4 form.  K is a
+// multiple of 32; lane (g4, l16) feeds A(l16, k0 + 8 g4 + j) and
+// B(k0 + 8 g4 + j, l16), j < 8, and the result layout is mm's.
+template <bool BF, bool TA, bool TB, bool KS = false>
+__device__ __forceinline__ f32x4_t mmx(f32x4_t acc, const float* a, int lda, const float* b,
+                                       int ldb, int K, const float* ks = nullptr) {
+  if constexpr (!BF) {
+    return mm<TA, TB, KS>(acc, a, lda, b, ldb, K, ks);
+  } else {
+    const int l16 = lane16(), g4 = lane_g4();
+    for (int k0 = 0; k0 < K; k0 += 32) {
+      const int kb = k0 + 8 * g4;
+      float av[8], bv[8];
+      if constexpr (TA) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) av[j] = a[(kb + j) * lda + l16];
+      } else {
+        const float4 t0 = *reinterpret_cast<const float4*>(a + l16 * lda + kb);
+        const float4 t1 = *reinterpret_cast<const float4*>(a + l16 * lda + kb + 4);
+        av[0] = t0.x; av[1] = t0.y; av[2] = t0.z; av[3] = t0.w;
+        av[4] = t1.x; av[5] = t1.y; av[6] = t1.z; av[7] = t1.w;
+      }
+      if constexpr (TB) {
+        const float4 t0 = *reinterpret_cast<const float4*>(b + l16 * ldb + kb);
+        const float4 t1 = *reinterpret_cast<const float4*>(b + l16 * ldb + kb + 4);
+        bv[0] = t0.x; bv[1] = t0.y; bv[2] = t0.z; bv[3] = t0.w;
+        bv[4] = t1.x; bv[5] = t1.y; bv[6] = t1.z; bv[7] = t1.w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bv[j] = b[(kb + j) * ldb + l16];
+      }
+      if constexpr (KS) {
+        const float4 s0 = *reinterpret_cast<const float4*>(ks + kb);
+        const float4 s1 = *reinterpret_cast<const float4*>(ks + kb + 4);
+        av[0] *= s0.x; av[1] *= s0.y; av[2] *= s0.z; av[3] *= s0.w;
+        av[4] *= s1.x; av[5] *= s1.y; av[6] *= s1.z; av[7] *= s1.w;
+      }
+      bf16x8_t A, B;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        A[j] = static_cast<__bf16>(av[j]);
+        B[j] = static_cast<__bf16>(bv[j]);
+      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc, 0, 0, 0);
+    }
+    return acc;
+  }
+}
+
+template <typename TIn>
+struct IsBf16 { static constexpr bool value = false; };
+template <>
+struct IsBf16<bf16_t> { static constexpr bool value = true; };
+
 __device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
 
 // tile (accumulator layout) <-> memory at the tile's origin with leading dimension ld
@@ -212,13 +268,16 @@ constexpr int kOpsWaves = kOpsThreads / 64;
 
 // ---------------------------------------------------------------- chunk operands
 
-template <int D, typename TIn>
+// EXACT keeps every product on fp32 operands; otherwise bf16 inputs use bf16
+// matrix-core operands (fp32 accumulation) for the products over 32 or more terms.
+template <int D, typename TIn, bool EXACT>
 __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __restrict__ q,
                                                        const TIn* __restrict__ k,
                                                        const TIn* __restrict__ g,
                                                        const TIn* __restrict__ beta,
                                                        float* __restrict__ ws, int T, int H,
                                                        int nc, float scale) {
+  constexpr bool BF = IsBf16<TIn>::value && !EXACT;
   using L = BwdLayout<D>;
   constexpr int LD = L::LD;
   __shared__ __attribute__((aligned(16))) float sm[3 * CR * LD + 3 * CR * LS + 6 * D + CR];
@@ -291,9 +350,9 @@ __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __res
       const int J = pt - I * (I + 1) / 2;
       f32x4_t acc = zero4();
       if (I == J) {
-        acc = mm<false, true>(acc, R1 + 16 * I * LD, LD, R2 + 16 * J * LD, LD, D);
+        acc = mmx<BF, false, true>(acc, R1 + 16 * I * LD, LD, R2 + 16 * J * LD, LD, D);
       } else {
-        acc = mm<false, true, true>(acc, R1 + 16 * I * LD, LD, R2 + 16 * J * LD, LD, D,
+        acc = mmx<BF, false, true, true>(acc, R1 + 16 * I * LD, LD, R2 + 16 * J * LD, LD, D,
                                     FP + pair_index(I, J) * D);
       }
 #pragma unroll
@@ -381,7 +440,7 @@ __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __res
   // P = scale M' Tb (into S0 and the workspace); W = Tb (k e^G)
   for (int j = wave; j < 16; j += kOpsWaves) {
     const int rt = j >> 2, ct = j & 3;
-    f32x4_t acc = mm<false, false>(zero4(), S1 + 16 * rt * LS, LS, S2 + 16 * ct, LS, CR);
+    f32x4_t acc = mmx<BF, false, false>(zero4(), S1 + 16 * rt * LS, LS, S2 + 16 * ct, LS, CR);
     const float f = scale * BT[16 * ct + l16];
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] *= f;
@@ -391,7 +450,7 @@ __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __res
   constexpr int CT = D / 16;
   for (int j = wave; j < 4 * CT; j += kOpsWaves) {
     const int rt = j / CT, ct = j - rt * CT;
-    const f32x4_t acc = mm<false, false, true>(zero4(), S2 + 16 * rt * LS, LS, R1 + 16 * ct, LD,
+    const f32x4_t acc = mmx<BF, false, false, true>(zero4(), S2 + 16 * rt * LS, LS, R1 + 16 * ct, LD,
                                                CR, BT);
     put(w + L::W + 16 * rt * D + 16 * ct, D, acc);
   }
@@ -399,7 +458,7 @@ __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __res
   // Q' = scale q e^G - P (k e^G)
   for (int j = wave; j < 4 * CT; j += kOpsWaves) {
     const int rt = j / CT, ct = j - rt * CT;
-    const f32x4_t pk = mm<false, false>(zero4(), S0 + 16 * rt * LS, LS, R1 + 16 * ct, LD, CR);
+    const f32x4_t pk = mmx<BF, false, false>(zero4(), S0 + 16 * rt * LS, LS, R1 + 16 * ct, LD, CR);
     f32x4_t acc = get(R2 + 16 * rt * LD + 16 * ct, LD);
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] -= pk[i];

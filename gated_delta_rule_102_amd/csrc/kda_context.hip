@@ -153,7 +153,7 @@ hipError_t launch_transition_t(const TransitionArgs& a) {
   float* ws = nullptr;
   hipError_t err = hipMallocAsync(reinterpret_cast<void**>(&ws), items * L::WS * sizeof(float), a.stream);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((chunk_ops_kernel<D, TIn>), dim3(items), dim3(kOpsThreads), 0, a.stream,
+  hipLaunchKernelGGL((chunk_ops_kernel<D, TIn, true>), dim3(items), dim3(kOpsThreads), 0, a.stream,
                      static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
                      static_cast<const TIn*>(a.g), static_cast<const TIn*>(a.beta), ws, a.T, a.H,
                      nc, 1.0f);
