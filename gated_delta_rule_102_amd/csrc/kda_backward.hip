@@ -666,32 +666,65 @@ __global__ __launch_bounds__(512) void bwd_grad_decay_kernel(const TIn* __restri
     }
   }
   __syncthreads();
+  // the inputs of two tiles' elements are loaded first (rows clamped into the chunk,
+  // all loads in flight together), then those elements are formed and stored
+  constexpr int XG = 2;
 #pragma unroll
-  for (int x = 0; x < NTW; ++x) {
-    const int j = wave + 8 * x, R = j / CT, cc = j - R * CT;
-    const int col = 16 * cc + l16;
-    const float RI = Rf[R * D + col], Gl = Rf[3 * D + col];
+  for (int x0 = 0; x0 < NTW; x0 += XG) {
+    float eG[XG][4], eQ[XG][4], eKg[XG][4], eKt[XG][4], eq[XG][4], ek[XG][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 16 * R + 4 * g4 + i;
-      const int e = t * D + col;
-      const float G = w[L::G + e];
-      const float rowf = expf(G - RI), colf = expf(RI - G), eg = expf(G), et = expf(Gl - G);
-      const float XA = rowf * xa[x][i], XM = rowf * xm[x][i];
-      const float ZA = colf * za[x][i], ZM = colf * zm[x][i];
-      const bool ok = t < p.nrow;
-      const int tc = min(t, p.nrow - 1);
-      const float kraw = to_f32(kc[tc * rs + col]), qraw = to_f32(qc[tc * rs + col]);
-      const float kv = ok ? kraw : 0.f, qv = ok ? qraw : 0.f;
-      const float dKg = a2[L::DKG + e], dKt = a1[L::DKT + e];
-      const float dqv = scale * a1[L::DQP + e] * eg + XM;
-      const float kg = dKg * eg, kt = dKt * et;
-      const float dkv = kg + kt + XA + ZA + ZM;
-      Ko[t * LD + col] = qv * dqv + kv * (kg + XA - kt - ZA - ZM);
-      Qo[t * LD + col] = kv * kt;
-      if (ok) {
-        dq[(p.row0 + static_cast<int64_t>(t) * H) * D + col] = Elem<TIn>::from(dqv);
-        dk[(p.row0 + static_cast<int64_t>(t) * H) * D + col] = Elem<TIn>::from(dkv);
+    for (int xx = 0; xx < XG; ++xx) {
+      const int x = xx, j = wave + 8 * (x0 + xx), R = j / CT, cc = j - R * CT;
+      const int col = 16 * cc + l16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * R + 4 * g4 + i;
+        const int e = t * D + col;
+        const int tc = min(t, p.nrow - 1);
+        eG[x][i] = w[L::G + e];
+        eQ[x][i] = a1[L::DQP + e];
+        eKg[x][i] = a2[L::DKG + e];
+        eKt[x][i] = a1[L::DKT + e];
+        eq[x][i] = to_f32(qc[tc * rs + col]);
+        ek[x][i] = to_f32(kc[tc * rs + col]);
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < XG; ++x) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pin(eG[x][i]);
+        pin(eQ[x][i]);
+        pin(eKg[x][i]);
+        pin(eKt[x][i]);
+        pin(eq[x][i]);
+        pin(ek[x][i]);
+      }
+    }
+#pragma unroll
+    for (int xx = 0; xx < XG; ++xx) {
+      const int x = x0 + xx, j = wave + 8 * x, R = j / CT, cc = j - R * CT;
+      const int col = 16 * cc + l16;
+      const float RI = Rf[R * D + col], Gl = Rf[3 * D + col];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * R + 4 * g4 + i;
+        const float G = eG[xx][i];
+        const float rowf = expf(G - RI), colf = expf(RI - G), eg = expf(G), et = expf(Gl - G);
+        const float XA = rowf * xa[x][i], XM = rowf * xm[x][i];
+        const float ZA = colf * za[x][i], ZM = colf * zm[x][i];
+        const bool ok = t < p.nrow;
+        const float kv = ok ? ek[xx][i] : 0.f, qv = ok ? eq[xx][i] : 0.f;
+        const float dKg = eKg[xx][i], dKt = eKt[xx][i];
+        const float dqv = scale * eQ[xx][i] * eg + XM;
+        const float kg = dKg * eg, kt = dKt * et;
+        const float dkv = kg + kt + XA + ZA + ZM;
+        Ko[t * LD + col] = qv * dqv + kv * (kg + XA - kt - ZA - ZM);
+        Qo[t * LD + col] = kv * kt;
+        if (ok) {
+          dq[(p.row0 + static_cast<int64_t>(t) * H) * D + col] = Elem<TIn>::from(dqv);
+          dk[(p.row0 + static_cast<int64_t>(t) * H) * D + col] = Elem<TIn>::from(dkv);
+        }
       }
     }
   }
