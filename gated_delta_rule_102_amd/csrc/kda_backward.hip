@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kScanThreads) void bwd_fwd_scan_kernel(const TIn* _
                                                            const float* __restrict__ ws,
                                                            float* __restrict__ st,
                                                            float* __restrict__ dl, int T, int H,
-                                                           int nc) {
+                                                           int nc, int BH) {
   constexpr bool BF = IsBf16<TIn>::value;   // bf16 matrix-core operands for bf16 inputs
   using L = BwdLayout<D>;
   using ST = ScanTiles<D>;
@@ -67,7 +67,8 @@ __global__ __launch_bounds__(kScanThreads) void bwd_fwd_scan_kernel(const TIn* _
   const int tid = threadIdx.x, wave = tid >> 6;
   const int l16 = lane16(), g4 = lane_g4();
   constexpr int NSL = D / SL;
-  const int bh = blockIdx.x / NSL, c0 = (blockIdx.x - bh * NSL) * SL;
+  int bh, c0;
+  if (!scan_block<NSL>(BH, bh, c0)) return;
   const int b = bh / H, h = bh - b * H;
 
   f32x4_t S[ST::NTW];
@@ -147,7 +148,7 @@ __global__ __launch_bounds__(kScanThreads) void bwd_scan_kernel(const TIn* __res
                                                        float* __restrict__ du,
                                                        TIn* __restrict__ dv,
                                                        float* __restrict__ ds0, int T, int H,
-                                                       int nc) {
+                                                       int nc, int BH) {
   // fp32 operands throughout: the bf16 form needs more registers than the two
   // wavefronts per SIMD leave, and spills cost more than it saves
   using L = BwdLayout<D>;
@@ -165,7 +166,8 @@ __global__ __launch_bounds__(kScanThreads) void bwd_scan_kernel(const TIn* __res
   const int tid = threadIdx.x, wave = tid >> 6;
   const int l16 = lane16(), g4 = lane_g4();
   constexpr int NSL = D / SL;
-  const int bh = blockIdx.x / NSL, c0 = (blockIdx.x - bh * NSL) * SL;
+  int bh, c0;
+  if (!scan_block<NSL>(BH, bh, c0)) return;
   const int b = bh / H, h = bh - b * H;
   const int64_t rs = static_cast<int64_t>(H) * D;
 
@@ -258,6 +260,276 @@ __global__ __launch_bounds__(kScanThreads) void bwd_scan_kernel(const TIn* __res
       for (int i = 0; i < 4; ++i) acc[i] = Lm[16 * rt + 4 * g4 + i] * dS[x][i];
       acc = mm<true, false>(acc, KQs + 16 * rt, LD, dOs + 16 * ct, LV, CR);
       const f32x4_t wu = mm<true, false>(zero4(), Ws + 16 * rt, LD, dUs + 16 * ct, LV, CR);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dS[x][i] = acc[i] - wu[i];
+    }
+    __syncthreads();
+  }
+  if (ds0) {
+#pragma unroll
+    for (int x = 0; x < ST::NTW; ++x) {
+      const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
+      put(ds0 + static_cast<int64_t>(bh) * D * D + 16 * rt * D + c0 + 16 * ct, D, dS[x]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- scans, bf16 operands
+//
+// For bf16 inputs both scans keep every matrix-core operand in LDS as bf16, laid
+// out so that each is k-contiguous: a lane reads one 16-byte run per operand per
+// 16x16x32 product.  Operands whose contraction index is their row index are
+// transposed while they are staged (Kt, V and Delta in the forward scan; W, P,
+// Tb, Q', dO and dU in the reverse one), and the fp32 state goes to LDS as its
+// bf16 transpose.  The values rounded are the ones the fp32-staged form rounds,
+// so the results are the same.
+
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+
+// acc += A B, A(r, k) = a[r * lda + k], B(k, c) = b[c * ldb + k] (bf16 in LDS)
+template <int K>
+__device__ __forceinline__ f32x4_t mmb(f32x4_t acc, const __bf16* a, int lda, const __bf16* b,
+                                       int ldb) {
+  const int l16 = lane16(), g4 = lane_g4();
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    const int kb = k0 + 8 * g4;
+    const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(a + l16 * lda + kb);
+    const bf16x8_t B = *reinterpret_cast<const bf16x8_t*>(b + l16 * ldb + kb);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+// a fp32 GTile to bf16 LDS, as loaded ([r][c]) or transposed ([c][r])
+template <int NT, int ROWS, int COLS>
+__device__ __forceinline__ void stage_bf16(const GTile<NT, ROWS, COLS>& t, __bf16* dst, int ld) {
+  using G = GTile<NT, ROWS, COLS>;
+#pragma unroll
+  for (int j = 0; j < G::PER; ++j) {
+    const int e = static_cast<int>(threadIdx.x) + j * NT;
+    const int rr = e / G::C4, c = (e - rr * G::C4) * 4;
+    const bf16x4_t w = {static_cast<__bf16>(t.r[j][0]), static_cast<__bf16>(t.r[j][1]),
+                        static_cast<__bf16>(t.r[j][2]), static_cast<__bf16>(t.r[j][3])};
+    *reinterpret_cast<bf16x4_t*>(dst + rr * ld + c) = w;
+  }
+}
+template <int NT, int ROWS, int COLS>
+__device__ __forceinline__ void stage_bf16_t(const GTile<NT, ROWS, COLS>& t, __bf16* dst, int ld) {
+  using G = GTile<NT, ROWS, COLS>;
+#pragma unroll
+  for (int j = 0; j < G::PER; ++j) {
+    const int e = static_cast<int>(threadIdx.x) + j * NT;
+    const int rr = e / G::C4, c = (e - rr * G::C4) * 4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dst[(c + q) * ld + rr] = static_cast<__bf16>(t.r[j][q]);
+  }
+}
+template <int NT, int COLS>
+__device__ __forceinline__ void stage_bf16_t(const ITile<NT, COLS, bf16_t>& t, __bf16* dst, int ld) {
+  using I = ITile<NT, COLS, bf16_t>;
+#pragma unroll
+  for (int j = 0; j < I::PER; ++j) {
+    const int e = static_cast<int>(threadIdx.x) + j * NT;
+    const int rr = e / COLS, c = e - rr * COLS;
+    dst[c * ld + rr] = static_cast<__bf16>(t.r[j]);
+  }
+}
+// an accumulator tile (rows r0.., cols c0..) to bf16 LDS transposed; dst points at
+// element (c0, r0) of the transposed matrix
+__device__ __forceinline__ void put_t_bf16(__bf16* dst, int ld, const f32x4_t& v) {
+  const int l16 = lane16(), g4 = lane_g4();
+  const bf16x4_t w = {static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]),
+                      static_cast<__bf16>(v[2]), static_cast<__bf16>(v[3])};
+  *reinterpret_cast<bf16x4_t*>(dst + l16 * ld + 4 * g4) = w;
+}
+
+template <int D>
+__global__ __launch_bounds__(kScanThreads) void bwd_fwd_scan_bf16_kernel(
+    const bf16_t* __restrict__ v, const float* __restrict__ s0, const float* __restrict__ ws,
+    float* __restrict__ st, float* __restrict__ dl, int T, int H, int nc, int BH) {
+  using L = BwdLayout<D>;
+  using ST = ScanTiles<D>;
+  constexpr int LB = D + 8, L64 = CR + 8;   // bf16 leading dimensions (16-byte rows)
+  __shared__ __attribute__((aligned(16))) __bf16 sb[CR * L64 + CR * LB + D * L64 + SL * L64 + SL * LB + SL * L64];
+  __shared__ float Lm[D];
+  __bf16* TBs = sb;                 // Tb      [t][s]
+  __bf16* Ws = TBs + CR * L64;      // W       [t][i]
+  __bf16* KTT = Ws + CR * LB;       // Kt^T    [i][s]
+  __bf16* VT = KTT + D * L64;       // V^T     [j][s]
+  __bf16* STr = VT + SL * L64;      // S^T     [j][i]
+  __bf16* DT = STr + SL * LB;       // Delta^T [j][s]
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int g4 = lane_g4();
+  constexpr int NSL = D / SL;
+  int bh, c0;
+  if (!scan_block<NSL>(BH, bh, c0)) return;
+  const int b = bh / H, h = bh - b * H;
+
+  f32x4_t S[ST::NTW];
+#pragma unroll
+  for (int x = 0; x < ST::NTW; ++x) {
+    const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
+    S[x] = s0 ? get(s0 + static_cast<int64_t>(bh) * D * D + 16 * rt * D + c0 + 16 * ct, D) : zero4();
+  }
+  GTile<kScanThreads, CR, CR> t_tb;
+  GTile<kScanThreads, CR, D> t_w, t_kt;
+  ITile<kScanThreads, SL, bf16_t> t_v;
+  float lm;
+  auto issue = [&](int c) {
+    const float* w = ws + (static_cast<int64_t>(bh) * nc + c) * L::WS;
+    const int64_t row0 = (static_cast<int64_t>(b) * T + static_cast<int64_t>(c) * CR) * H + h;
+    t_tb.load(w + L::TB, CR);
+    t_w.load(w + L::W, D);
+    t_kt.load(w + L::KT, D);
+    t_v.load(v + row0 * D + c0, static_cast<int64_t>(H) * D, min(CR, T - c * CR));
+    lm = w[L::LAM + (tid & (D - 1))];
+  };
+  issue(0);
+  for (int c = 0; c < nc; ++c) {
+    const int64_t item = static_cast<int64_t>(bh) * nc + c;
+    t_tb.pin_all();
+    t_w.pin_all();
+    t_kt.pin_all();
+    t_v.pin_all();
+    pin(lm);
+    stage_bf16(t_tb, TBs, L64);
+    stage_bf16(t_w, Ws, LB);
+    stage_bf16_t(t_kt, KTT, L64);
+    stage_bf16_t(t_v, VT, L64);
+    if (tid < D) Lm[tid] = lm;
+    // the next chunk's loads go out before this step's global stores
+    if (c + 1 < nc) issue(c + 1);
+#pragma unroll
+    for (int x = 0; x < ST::NTW; ++x) {
+      const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
+      put_t_bf16(STr + 16 * ct * LB + 16 * rt, LB, S[x]);
+      put(st + item * D * D + 16 * rt * D + c0 + 16 * ct, D, S[x]);
+    }
+    __syncthreads();
+    {   // Delta = Tb V - W S: 4 x 2 tiles, one per wavefront
+      const int rt = wave >> 1, ct = wave & 1;
+      const f32x4_t tv = mmb<CR>(zero4(), TBs + 16 * rt * L64, L64, VT + 16 * ct * L64, L64);
+      const f32x4_t wsv = mmb<D>(zero4(), Ws + 16 * rt * LB, LB, STr + 16 * ct * LB, LB);
+      f32x4_t d;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d[i] = tv[i] - wsv[i];
+      put_t_bf16(DT + 16 * ct * L64 + 16 * rt, L64, d);
+      put(dl + item * CR * D + 16 * rt * D + c0 + 16 * ct, D, d);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < ST::NTW; ++x) {   // S = Lam S + Kt^T Delta
+      const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
+      f32x4_t acc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = Lm[16 * rt + 4 * g4 + i] * S[x][i];
+      S[x] = mmb<CR>(acc, KTT + 16 * rt * L64, L64, DT + 16 * ct * L64, L64);
+    }
+    __syncthreads();
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kScanThreads) void bwd_scan_bf16_kernel(
+    const bf16_t* __restrict__ dout, const float* __restrict__ dsT, const float* __restrict__ ws,
+    float* __restrict__ dst, float* __restrict__ du, bf16_t* __restrict__ dv,
+    float* __restrict__ ds0, int T, int H, int nc, int BH) {
+  using L = BwdLayout<D>;
+  using ST = ScanTiles<D>;
+  constexpr int LB = D + 8, L64 = CR + 8;
+  __shared__ __attribute__((aligned(16))) __bf16 sb[CR * LB + SL * LB + 2 * CR * L64 + 2 * SL * L64 + 2 * D * L64];
+  __shared__ float Lm[D];
+  __bf16* KTs = sb;                 // Kt    [t][i]
+  __bf16* dST = KTs + CR * LB;      // dS^T  [j][i]
+  __bf16* PT = dST + SL * LB;       // P^T   [t'][t]
+  __bf16* TBT = PT + CR * L64;      // Tb^T  [t'][t]
+  __bf16* dOT = TBT + CR * L64;     // dO^T  [j][t]
+  __bf16* dUT = dOT + SL * L64;     // dU^T  [j][t]
+  __bf16* QPT = dUT + SL * L64;     // Q'^T  [i][t]
+  __bf16* WT = QPT + D * L64;       // W^T   [i][t]
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int l16 = lane16(), g4 = lane_g4();
+  constexpr int NSL = D / SL;
+  int bh, c0;
+  if (!scan_block<NSL>(BH, bh, c0)) return;
+  const int b = bh / H, h = bh - b * H;
+  const int64_t rs = static_cast<int64_t>(H) * D;
+
+  f32x4_t dS[ST::NTW];
+#pragma unroll
+  for (int x = 0; x < ST::NTW; ++x) {
+    const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
+    dS[x] = dsT ? get(dsT + static_cast<int64_t>(bh) * D * D + 16 * rt * D + c0 + 16 * ct, D) : zero4();
+  }
+  GTile<kScanThreads, CR, D> t_kt, t_w, t_qp;
+  GTile<kScanThreads, CR, CR> t_p, t_tb;
+  ITile<kScanThreads, SL, bf16_t> t_do;
+  float lm;
+  auto issue = [&](int c) {
+    const float* w = ws + (static_cast<int64_t>(bh) * nc + c) * L::WS;
+    const int64_t row0 = (static_cast<int64_t>(b) * T + static_cast<int64_t>(c) * CR) * H + h;
+    t_kt.load(w + L::KT, D);
+    t_w.load(w + L::W, D);
+    t_qp.load(w + L::QP, D);
+    t_p.load(w + L::PP, CR);
+    t_tb.load(w + L::TB, CR);
+    t_do.load(dout + row0 * D + c0, rs, min(CR, T - c * CR));
+    lm = w[L::LAM + (tid & (D - 1))];
+  };
+  issue(nc - 1);
+  for (int c = nc - 1; c >= 0; --c) {
+    const int64_t item = static_cast<int64_t>(bh) * nc + c;
+    const int nrow = min(CR, T - c * CR);
+    const int64_t row0 = (static_cast<int64_t>(b) * T + static_cast<int64_t>(c) * CR) * H + h;
+    t_kt.pin_all();
+    t_w.pin_all();
+    t_qp.pin_all();
+    t_p.pin_all();
+    t_tb.pin_all();
+    t_do.pin_all();
+    pin(lm);
+    stage_bf16(t_kt, KTs, LB);
+    stage_bf16_t(t_w, WT, L64);
+    stage_bf16_t(t_qp, QPT, L64);
+    stage_bf16_t(t_p, PT, L64);
+    stage_bf16_t(t_tb, TBT, L64);
+    stage_bf16_t(t_do, dOT, L64);
+    if (tid < D) Lm[tid] = lm;
+    // the previous chunk's loads go out before this step's global stores
+    if (c > 0) issue(c - 1);
+#pragma unroll
+    for (int x = 0; x < ST::NTW; ++x) {
+      const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
+      put_t_bf16(dST + 16 * ct * LB + 16 * rt, LB, dS[x]);
+      put(dst + item * D * D + 16 * rt * D + c0 + 16 * ct, D, dS[x]);
+    }
+    __syncthreads();
+    {   // dU = Kt dS: one tile per wavefront
+      const int rt = wave >> 1, ct = wave & 1;
+      const f32x4_t u = mmb<D>(zero4(), KTs + 16 * rt * LB, LB, dST + 16 * ct * LB, LB);
+      put_t_bf16(dUT + 16 * ct * L64 + 16 * rt, L64, u);
+      put(du + item * CR * D + 16 * rt * D + c0 + 16 * ct, D, u);
+    }
+    __syncthreads();
+    {   // dV = P^T dO + Tb^T dU
+      const int rt = wave >> 1, ct = wave & 1;
+      f32x4_t acc = mmb<CR>(zero4(), PT + 16 * rt * L64, L64, dOT + 16 * ct * L64, L64);
+      acc = mmb<CR>(acc, TBT + 16 * rt * L64, L64, dUT + 16 * ct * L64, L64);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * rt + 4 * g4 + i;
+        if (t < nrow) dv[(row0 + static_cast<int64_t>(t) * H) * D + c0 + 16 * ct + l16] = Elem<bf16_t>::from(acc[i]);
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < ST::NTW; ++x) {   // dS = Lam dS + Q'^T dO - W^T dU
+      const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
+      f32x4_t acc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = Lm[16 * rt + 4 * g4 + i] * dS[x][i];
+      acc = mmb<CR>(acc, QPT + 16 * rt * L64, L64, dOT + 16 * ct * L64, L64);
+      const f32x4_t wu = mmb<CR>(zero4(), WT + 16 * rt * L64, L64, dUT + 16 * ct * L64, L64);
 #pragma unroll
       for (int i = 0; i < 4; ++i) dS[x][i] = acc[i] - wu[i];
     }
@@ -761,14 +1033,23 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
   const TIn* g = static_cast<const TIn*>(a.g);
   const TIn* beta = static_cast<const TIn*>(a.beta);
   const TIn* dout = static_cast<const TIn*>(a.d_out);
-  const int scan_blocks = a.B * a.H * (D / SL);
+  const int BH = a.B * a.H;
+  const int scan_blocks = scan_grid(BH, D / SL);
   hipLaunchKernelGGL((chunk_ops_kernel<D, TIn, false>), dim3(items), dim3(kOpsThreads), 0, a.stream, q, k, g, beta,
                      ws, a.T, a.H, nc, a.scale);
-  hipLaunchKernelGGL((bwd_fwd_scan_kernel<D, TIn>), dim3(scan_blocks), dim3(kScanThreads), 0, a.stream, v,
-                     a.initial_state, ws, st, dl, a.T, a.H, nc);
-  hipLaunchKernelGGL((bwd_scan_kernel<D, TIn>), dim3(scan_blocks), dim3(kScanThreads), 0, a.stream, dout,
-                     a.d_final_state, ws, dst, du, static_cast<TIn*>(a.dv), a.d_initial_state,
-                     a.T, a.H, nc);
+  if constexpr (IsBf16<TIn>::value) {
+    hipLaunchKernelGGL((bwd_fwd_scan_bf16_kernel<D>), dim3(scan_blocks), dim3(kScanThreads), 0,
+                       a.stream, v, a.initial_state, ws, st, dl, a.T, a.H, nc, BH);
+    hipLaunchKernelGGL((bwd_scan_bf16_kernel<D>), dim3(scan_blocks), dim3(kScanThreads), 0,
+                       a.stream, dout, a.d_final_state, ws, dst, du, static_cast<TIn*>(a.dv),
+                       a.d_initial_state, a.T, a.H, nc, BH);
+  } else {
+    hipLaunchKernelGGL((bwd_fwd_scan_kernel<D, TIn>), dim3(scan_blocks), dim3(kScanThreads), 0, a.stream, v,
+                       a.initial_state, ws, st, dl, a.T, a.H, nc, BH);
+    hipLaunchKernelGGL((bwd_scan_kernel<D, TIn>), dim3(scan_blocks), dim3(kScanThreads), 0, a.stream, dout,
+                       a.d_final_state, ws, dst, du, static_cast<TIn*>(a.dv), a.d_initial_state,
+                       a.T, a.H, nc, BH);
+  }
   hipLaunchKernelGGL((bwd_grad_dv_kernel<D, TIn>), dim3(items), dim3(512), 0, a.stream, v, dout,
                      st, dst, dl, du, g1, a.T, a.H, nc);
   hipLaunchKernelGGL((bwd_grad_nn_kernel<D, TIn>), dim3(items), dim3(kNnThreads), 0, a.stream, k, beta,

@@ -243,6 +243,20 @@ struct ITile {
   }
 };
 
+// Block id -> (sequence-head bh, first column c0) for the column-sliced scans.
+// The NSL slices of one sequence-head get block ids that are equal mod 8, so the
+// round-robin dispatch over the eight XCDs puts them on one XCD, whose L2 then
+// serves their shared per-chunk operands once.  Grids have scan_grid(BH, NSL)
+// blocks; a block past the last sequence-head gets false and returns at once.
+template <int NSL>
+__device__ __forceinline__ bool scan_block(int BH, int& bh, int& c0) {
+  const int w = static_cast<int>(blockIdx.x), local = w >> 3;
+  bh = (local / NSL) * 8 + (w & 7);
+  c0 = (local % NSL) * SL;
+  return bh < BH;
+}
+inline int scan_grid(int BH, int nsl) { return (BH + 7) / 8 * 8 * nsl; }
+
 // sub-tile pairs J < I of a 64-row chunk -> 0..5
 __device__ __forceinline__ int pair_index(int I, int J) { return I * (I - 1) / 2 + J; }
 

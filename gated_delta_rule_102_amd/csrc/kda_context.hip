@@ -31,7 +31,7 @@ namespace {
 template <int D>
 __global__ __launch_bounds__(256) void transition_scan_kernel(const float* __restrict__ ws,
                                                               float* __restrict__ trans,
-                                                              int nc) {
+                                                              int nc, int BH) {
   using L = BwdLayout<D>;
   constexpr int LD = L::LD;
   constexpr int NTW = D / 32;   // state tiles per wave: (D/16) x 2 tiles over 4 waves
@@ -44,7 +44,8 @@ __global__ __launch_bounds__(256) void transition_scan_kernel(const float* __res
   const int tid = threadIdx.x, wave = tid >> 6;
   const int l16 = lane16(), g4 = lane_g4();
   constexpr int NSL = D / SL;
-  const int bh = blockIdx.x / NSL, c0 = (blockIdx.x - bh * NSL) * SL;
+  int bh, c0;
+  if (!scan_block<NSL>(BH, bh, c0)) return;
 
   f32x4_t S[NTW];
 #pragma unroll
@@ -109,7 +110,8 @@ __global__ __launch_bounds__(256) void compose_kernel(const float* __restrict__ 
   float* Ss = Ps + D * LD;
   const int tid = threadIdx.x, wave = tid >> 6;
   constexpr int NSL = D / SL;
-  const int bh = blockIdx.x / NSL, c0 = (blockIdx.x - bh * NSL) * SL;
+  int bh, c0;
+  if (!scan_block<NSL>(BH, bh, c0)) return;
   const int64_t DD = static_cast<int64_t>(D) * D;
   const int64_t off = static_cast<int64_t>(bh) * DD + c0;
 
@@ -157,8 +159,8 @@ hipError_t launch_transition_t(const TransitionArgs& a) {
                      static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
                      static_cast<const TIn*>(a.g), static_cast<const TIn*>(a.beta), ws, a.T, a.H,
                      nc, 1.0f);
-  hipLaunchKernelGGL((transition_scan_kernel<D>), dim3(a.B * a.H * (D / SL)), dim3(256), 0,
-                     a.stream, ws, a.transition, nc);
+  hipLaunchKernelGGL((transition_scan_kernel<D>), dim3(scan_grid(a.B * a.H, D / SL)), dim3(256),
+                     0, a.stream, ws, a.transition, nc, a.B * a.H);
   err = hipGetLastError();
   const hipError_t ferr = hipFreeAsync(ws, a.stream);
   return err != hipSuccess ? err : ferr;
@@ -176,10 +178,10 @@ hipError_t launch_transition(const TransitionArgs& a) {
 hipError_t launch_compose(const ComposeArgs& a) {
   const int BH = a.B * a.H;
   if (a.d == 128) {
-    hipLaunchKernelGGL((compose_kernel<128>), dim3(BH * (128 / SL)), dim3(256), 0, a.stream,
+    hipLaunchKernelGGL((compose_kernel<128>), dim3(scan_grid(BH, 128 / SL)), dim3(256), 0, a.stream,
                        a.transitions, a.partial_states, a.initial_state, a.entry_states, a.R, BH);
   } else {
-    hipLaunchKernelGGL((compose_kernel<64>), dim3(BH * (64 / SL)), dim3(256), 0, a.stream,
+    hipLaunchKernelGGL((compose_kernel<64>), dim3(scan_grid(BH, 64 / SL)), dim3(256), 0, a.stream,
                        a.transitions, a.partial_states, a.initial_state, a.entry_states, a.R, BH);
   }
   return hipGetLastError();
