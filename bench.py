@@ -15,8 +15,8 @@ the library launches on; "roofline" relates the prefill kernel's algorithmic
 HBM bytes to its average duration.  The "prologue" object times the same prefill
 from raw activations through kda_chunk_fwd_prologue (gate and normalisation
 fused into the kernels' loads).  The "backward" object times kda_chunk_bwd (all
-gradients of the same prefill) and relates the fp32 matrix-core work it issues
-to the fp32 matrix peak.  "cpu_baseline" times the fp64 CPU oracle on
+gradients of the same prefill) and relates its dense matrix work to the bf16 and
+fp32 matrix peaks.  "cpu_baseline" times the fp64 CPU oracle on
 a bounded sample of the same workload.  One JSON line is printed.
 """
 from __future__ import annotations
@@ -97,11 +97,12 @@ def pmc_copy(torch, nbytes=256 << 20, reps=3):
 
 
 def backward_flops(B, T, H, d):
-    """fp32 matrix-core flops the backward issues: 16x16x4 products (2048 flops
-    each) per 64-token chunk and head, summed over its six kernels at d = 128:
-    operand prep 1984, forward state scan 2560, reverse scan 4096, operand
+    """Dense matrix-product flops of the backward per 64-token chunk and head, summed
+    over its six kernels at d = 128 and counted in 16x16x4 products (2048 flops
+    each): operand prep 1984, forward state scan 2560, reverse scan 4096, operand
     gradients 4096, 64x64 algebra 3072, decayed products 1280 (dense tiles,
-    including the zero upper triangles of the triangular factors)."""
+    including the zero upper triangles of the triangular factors).  For bf16
+    inputs most of them run as bf16 16x16x32 products (8 of these each)."""
     assert d == 128
     per_chunk = (1984 + 2560 + 4096 + 4096 + 3072 + 1280) * 2048
     return B * H * (-(-T // CHUNK)) * per_chunk
@@ -278,9 +279,12 @@ def main():
         result["backward"] = {
             "entry_point": "kda_chunk_bwd", "workload": "prefill_4x4096 gradients",
             "calls": nb, "call_ms_avg": b_s * 1e3, "tokens_per_s": B * T / b_s,
-            "fp32_mfma_tflops": bfl / b_s / 1e12,
-            "fp32_mfma_frac": bfl / b_s / 1e12 / FP32_MFMA_PEAK_TFLOPS,
-            "flop_convention": "fp32 16x16x4 matrix products issued, 17088 per chunk and head",
+            "matrix_tflops": bfl / b_s / 1e12,
+            "frac_of_bf16_mfma_peak": bfl / b_s / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+            "frac_of_fp32_mfma_peak": bfl / b_s / 1e12 / FP32_MFMA_PEAK_TFLOPS,
+            "flop_convention": "dense matrix products, 35.0 MFLOP per chunk and head (17088 "
+                               "16x16x4 equivalents); bf16 operands with fp32 accumulation for "
+                               "the products over 32 or more terms, fp32 for the rest",
         }
         del bset, cot
         torch.cuda.empty_cache()
