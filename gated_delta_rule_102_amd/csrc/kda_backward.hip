@@ -278,13 +278,11 @@ __global__ __launch_bounds__(kScanThreads) void bwd_scan_kernel(const TIn* __res
 //
 // For bf16 inputs both scans keep every matrix-core operand in LDS as bf16, laid
 // out so that each is k-contiguous: a lane reads one 16-byte run per operand per
-// 16x16x32 product.  Operands whose contraction index is their row index are
-// transposed while they are staged (Kt, V and Delta in the forward scan; W, P,
-// Tb, Q', dO and dU in the reverse one), and the fp32 state goes to LDS as its
-// bf16 transpose.  The values rounded are the ones the fp32-staged form rounds,
-// so the results are the same.
-
-typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+// 16x16x32 product.  The chunk operands come from the bf16 copies chunk_ops
+// writes in exactly those layouts (Tb, W, Kt^T for the forward scan; Kt, W^T,
+// Q'^T, P^T, Tb^T for the reverse one) and are staged by plain 16-byte copies;
+// only V and dO are transposed while staged, and the fp32 state and the
+// per-step products (Delta, dU) go to LDS as bf16 transposes.
 
 // acc += A B, A(r, k) = a[r * lda + k], B(k, c) = b[c * ldb + k] (bf16 in LDS)
 template <int K>
@@ -301,30 +299,7 @@ __device__ __forceinline__ f32x4_t mmb(f32x4_t acc, const __bf16* a, int lda, co
   return acc;
 }
 
-// a fp32 GTile to bf16 LDS, as loaded ([r][c]) or transposed ([c][r])
-template <int NT, int ROWS, int COLS>
-__device__ __forceinline__ void stage_bf16(const GTile<NT, ROWS, COLS>& t, __bf16* dst, int ld) {
-  using G = GTile<NT, ROWS, COLS>;
-#pragma unroll
-  for (int j = 0; j < G::PER; ++j) {
-    const int e = static_cast<int>(threadIdx.x) + j * NT;
-    const int rr = e / G::C4, c = (e - rr * G::C4) * 4;
-    const bf16x4_t w = {static_cast<__bf16>(t.r[j][0]), static_cast<__bf16>(t.r[j][1]),
-                        static_cast<__bf16>(t.r[j][2]), static_cast<__bf16>(t.r[j][3])};
-    *reinterpret_cast<bf16x4_t*>(dst + rr * ld + c) = w;
-  }
-}
-template <int NT, int ROWS, int COLS>
-__device__ __forceinline__ void stage_bf16_t(const GTile<NT, ROWS, COLS>& t, __bf16* dst, int ld) {
-  using G = GTile<NT, ROWS, COLS>;
-#pragma unroll
-  for (int j = 0; j < G::PER; ++j) {
-    const int e = static_cast<int>(threadIdx.x) + j * NT;
-    const int rr = e / G::C4, c = (e - rr * G::C4) * 4;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) dst[(c + q) * ld + rr] = static_cast<__bf16>(t.r[j][q]);
-  }
-}
+// a 64 x COLS input tile (bf16) to LDS transposed ([c][r])
 template <int NT, int COLS>
 __device__ __forceinline__ void stage_bf16_t(const ITile<NT, COLS, bf16_t>& t, __bf16* dst, int ld) {
   using I = ITile<NT, COLS, bf16_t>;
@@ -335,19 +310,11 @@ __device__ __forceinline__ void stage_bf16_t(const ITile<NT, COLS, bf16_t>& t, _
     dst[c * ld + rr] = static_cast<__bf16>(t.r[j]);
   }
 }
-// an accumulator tile (rows r0.., cols c0..) to bf16 LDS transposed; dst points at
-// element (c0, r0) of the transposed matrix
-__device__ __forceinline__ void put_t_bf16(__bf16* dst, int ld, const f32x4_t& v) {
-  const int l16 = lane16(), g4 = lane_g4();
-  const bf16x4_t w = {static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]),
-                      static_cast<__bf16>(v[2]), static_cast<__bf16>(v[3])};
-  *reinterpret_cast<bf16x4_t*>(dst + l16 * ld + 4 * g4) = w;
-}
-
 template <int D>
 __global__ __launch_bounds__(kScanThreads) void bwd_fwd_scan_bf16_kernel(
     const bf16_t* __restrict__ v, const float* __restrict__ s0, const float* __restrict__ ws,
-    float* __restrict__ st, float* __restrict__ dl, int T, int H, int nc, int BH) {
+    const __bf16* __restrict__ wsb, float* __restrict__ st, float* __restrict__ dl, int T, int H,
+    int nc, int BH) {
   using L = BwdLayout<D>;
   using ST = ScanTiles<D>;
   constexpr int LB = D + 8, L64 = CR + 8;   // bf16 leading dimensions (16-byte rows)
@@ -372,30 +339,32 @@ __global__ __launch_bounds__(kScanThreads) void bwd_fwd_scan_bf16_kernel(
     const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
     S[x] = s0 ? get(s0 + static_cast<int64_t>(bh) * D * D + 16 * rt * D + c0 + 16 * ct, D) : zero4();
   }
-  GTile<kScanThreads, CR, CR> t_tb;
-  GTile<kScanThreads, CR, D> t_w, t_kt;
+  BTile<kScanThreads, CR, CR> t_tb;
+  BTile<kScanThreads, CR, D> t_w;
+  BTile<kScanThreads, D, CR> t_ktt;
   ITile<kScanThreads, SL, bf16_t> t_v;
   float lm;
   auto issue = [&](int c) {
-    const float* w = ws + (static_cast<int64_t>(bh) * nc + c) * L::WS;
+    const int64_t item = static_cast<int64_t>(bh) * nc + c;
+    const __bf16* wb = wsb + item * L::WSB;
     const int64_t row0 = (static_cast<int64_t>(b) * T + static_cast<int64_t>(c) * CR) * H + h;
-    t_tb.load(w + L::TB, CR);
-    t_w.load(w + L::W, D);
-    t_kt.load(w + L::KT, D);
+    t_tb.load(wb + L::BTB);
+    t_w.load(wb + L::BW);
+    t_ktt.load(wb + L::BKTT);
     t_v.load(v + row0 * D + c0, static_cast<int64_t>(H) * D, min(CR, T - c * CR));
-    lm = w[L::LAM + (tid & (D - 1))];
+    lm = ws[item * L::WS + L::LAM + (tid & (D - 1))];
   };
   issue(0);
   for (int c = 0; c < nc; ++c) {
     const int64_t item = static_cast<int64_t>(bh) * nc + c;
     t_tb.pin_all();
     t_w.pin_all();
-    t_kt.pin_all();
+    t_ktt.pin_all();
     t_v.pin_all();
     pin(lm);
-    stage_bf16(t_tb, TBs, L64);
-    stage_bf16(t_w, Ws, LB);
-    stage_bf16_t(t_kt, KTT, L64);
+    t_tb.store(TBs, L64);
+    t_w.store(Ws, LB);
+    t_ktt.store(KTT, L64);
     stage_bf16_t(t_v, VT, L64);
     if (tid < D) Lm[tid] = lm;
     // the next chunk's loads go out before this step's global stores
@@ -433,8 +402,8 @@ __global__ __launch_bounds__(kScanThreads) void bwd_fwd_scan_bf16_kernel(
 template <int D>
 __global__ __launch_bounds__(kScanThreads) void bwd_scan_bf16_kernel(
     const bf16_t* __restrict__ dout, const float* __restrict__ dsT, const float* __restrict__ ws,
-    float* __restrict__ dst, float* __restrict__ du, bf16_t* __restrict__ dv,
-    float* __restrict__ ds0, int T, int H, int nc, int BH) {
+    const __bf16* __restrict__ wsb, float* __restrict__ dst, float* __restrict__ du,
+    bf16_t* __restrict__ dv, float* __restrict__ ds0, int T, int H, int nc, int BH) {
   using L = BwdLayout<D>;
   using ST = ScanTiles<D>;
   constexpr int LB = D + 8, L64 = CR + 8;
@@ -462,20 +431,22 @@ __global__ __launch_bounds__(kScanThreads) void bwd_scan_bf16_kernel(
     const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
     dS[x] = dsT ? get(dsT + static_cast<int64_t>(bh) * D * D + 16 * rt * D + c0 + 16 * ct, D) : zero4();
   }
-  GTile<kScanThreads, CR, D> t_kt, t_w, t_qp;
-  GTile<kScanThreads, CR, CR> t_p, t_tb;
+  BTile<kScanThreads, CR, D> t_kt;
+  BTile<kScanThreads, D, CR> t_wt, t_qpt;
+  BTile<kScanThreads, CR, CR> t_pt, t_tbt;
   ITile<kScanThreads, SL, bf16_t> t_do;
   float lm;
   auto issue = [&](int c) {
-    const float* w = ws + (static_cast<int64_t>(bh) * nc + c) * L::WS;
+    const int64_t item = static_cast<int64_t>(bh) * nc + c;
+    const __bf16* wb = wsb + item * L::WSB;
     const int64_t row0 = (static_cast<int64_t>(b) * T + static_cast<int64_t>(c) * CR) * H + h;
-    t_kt.load(w + L::KT, D);
-    t_w.load(w + L::W, D);
-    t_qp.load(w + L::QP, D);
-    t_p.load(w + L::PP, CR);
-    t_tb.load(w + L::TB, CR);
+    t_kt.load(wb + L::BKT);
+    t_wt.load(wb + L::BWT);
+    t_qpt.load(wb + L::BQPT);
+    t_pt.load(wb + L::BPT);
+    t_tbt.load(wb + L::BTBT);
     t_do.load(dout + row0 * D + c0, rs, min(CR, T - c * CR));
-    lm = w[L::LAM + (tid & (D - 1))];
+    lm = ws[item * L::WS + L::LAM + (tid & (D - 1))];
   };
   issue(nc - 1);
   for (int c = nc - 1; c >= 0; --c) {
@@ -483,17 +454,17 @@ __global__ __launch_bounds__(kScanThreads) void bwd_scan_bf16_kernel(
     const int nrow = min(CR, T - c * CR);
     const int64_t row0 = (static_cast<int64_t>(b) * T + static_cast<int64_t>(c) * CR) * H + h;
     t_kt.pin_all();
-    t_w.pin_all();
-    t_qp.pin_all();
-    t_p.pin_all();
-    t_tb.pin_all();
+    t_wt.pin_all();
+    t_qpt.pin_all();
+    t_pt.pin_all();
+    t_tbt.pin_all();
     t_do.pin_all();
     pin(lm);
-    stage_bf16(t_kt, KTs, LB);
-    stage_bf16_t(t_w, WT, L64);
-    stage_bf16_t(t_qp, QPT, L64);
-    stage_bf16_t(t_p, PT, L64);
-    stage_bf16_t(t_tb, TBT, L64);
+    t_kt.store(KTs, LB);
+    t_wt.store(WT, L64);
+    t_qpt.store(QPT, L64);
+    t_pt.store(PT, L64);
+    t_tbt.store(TBT, L64);
     stage_bf16_t(t_do, dOT, L64);
     if (tid < D) Lm[tid] = lm;
     // the previous chunk's loads go out before this step's global stores
@@ -1016,7 +987,9 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
   using L = BwdLayout<D>;
   const int nc = (a.T + CR - 1) / CR;
   const int64_t items = static_cast<int64_t>(a.B) * a.H * nc;
-  const int64_t per = L::WS + 2 * D * D + 2 * CR * D + L::G1 + L::G2;
+  constexpr bool BF = IsBf16<TIn>::value;
+  // fp32 regions, then (bf16 inputs) the bf16 scan operands, WSB/2 floats per chunk
+  const int64_t per = L::WS + 2 * D * D + 2 * CR * D + L::G1 + L::G2 + (BF ? L::WSB / 2 : 0);
   float* buf = nullptr;
   hipError_t err = hipMallocAsync(reinterpret_cast<void**>(&buf), items * per * sizeof(float), a.stream);
   if (err != hipSuccess) return err;
@@ -1027,6 +1000,7 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
   float* du = dl + items * CR * D;
   float* g1 = du + items * CR * D;
   float* g2 = g1 + items * L::G1;
+  __bf16* wsb = BF ? reinterpret_cast<__bf16*>(g2 + items * L::G2) : nullptr;
   const TIn* q = static_cast<const TIn*>(a.q);
   const TIn* k = static_cast<const TIn*>(a.k);
   const TIn* v = static_cast<const TIn*>(a.v);
@@ -1036,13 +1010,13 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
   const int BH = a.B * a.H;
   const int scan_blocks = scan_grid(BH, D / SL);
   hipLaunchKernelGGL((chunk_ops_kernel<D, TIn, false>), dim3(items), dim3(kOpsThreads), 0, a.stream, q, k, g, beta,
-                     ws, a.T, a.H, nc, a.scale);
+                     ws, wsb, a.T, a.H, nc, a.scale);
   if constexpr (IsBf16<TIn>::value) {
     hipLaunchKernelGGL((bwd_fwd_scan_bf16_kernel<D>), dim3(scan_blocks), dim3(kScanThreads), 0,
-                       a.stream, v, a.initial_state, ws, st, dl, a.T, a.H, nc, BH);
+                       a.stream, v, a.initial_state, ws, wsb, st, dl, a.T, a.H, nc, BH);
     hipLaunchKernelGGL((bwd_scan_bf16_kernel<D>), dim3(scan_blocks), dim3(kScanThreads), 0,
-                       a.stream, dout, a.d_final_state, ws, dst, du, static_cast<TIn*>(a.dv),
-                       a.d_initial_state, a.T, a.H, nc, BH);
+                       a.stream, dout, a.d_final_state, ws, wsb, dst, du,
+                       static_cast<TIn*>(a.dv), a.d_initial_state, a.T, a.H, nc, BH);
   } else {
     hipLaunchKernelGGL((bwd_fwd_scan_kernel<D, TIn>), dim3(scan_blocks), dim3(kScanThreads), 0, a.stream, v,
                        a.initial_state, ws, st, dl, a.T, a.H, nc, BH);
@@ -1071,13 +1045,5 @@ hipError_t launch_backward(const BackwardArgs& a) {
   return a.dtype_f32 ? launch_backward_t<64, float>(a) : launch_backward_t<64, bf16_t>(a);
 }
 
-int64_t backward_workspace_bytes(int B, int T, int H, int d) {
-  const int64_t nc = (T + CR - 1) / CR;
-  const int64_t items = static_cast<int64_t>(B) * H * nc;
-  const int64_t per = d == 128
-      ? BwdLayout<128>::WS + 2 * 128 * 128 + 2 * CR * 128 + BwdLayout<128>::G1 + BwdLayout<128>::G2
-      : BwdLayout<64>::WS + 2 * 64 * 64 + 2 * CR * 64 + BwdLayout<64>::G1 + BwdLayout<64>::G2;
-  return items * per * static_cast<int64_t>(sizeof(float));
-}
 
 }  // namespace kda

@@ -40,6 +40,12 @@ struct BwdLayout {
   static constexpr int DTB = DP + 4096, DLAM = DTB + 4096, G1 = DLAM + D;
   // written by bwd_grad_nn
   static constexpr int DKG = 0, DMP = CR * D, DAP = DMP + 4096, G2 = DAP + 4096;
+  // bf16 copies of the scan operands per chunk, written by chunk_ops for bf16
+  // inputs (bf16 elements), each in the layout a scan reads k-contiguously:
+  // Tb, Tb^T, P^T, W, W^T, Kt, Kt^T, Q'^T
+  static constexpr int BTB = 0, BTBT = 4096, BPT = 8192, BW = 12288, BWT = BW + CR * D;
+  static constexpr int BKT = BWT + CR * D, BKTT = BKT + CR * D, BQPT = BKTT + CR * D;
+  static constexpr int WSB = BQPT + CR * D;
 };
 
 __device__ __forceinline__ int lane16() { return threadIdx.x & 15; }
@@ -257,6 +263,55 @@ __device__ __forceinline__ bool scan_block(int BH, int& bh, int& c0) {
 }
 inline int scan_grid(int BH, int nsl) { return (BH + 7) / 8 * 8 * nsl; }
 
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+
+// an accumulator tile (rows r0.., cols c0..) as bf16, transposed: dst points at
+// element (c0, r0) of the transposed matrix (8 contiguous bytes per lane)
+__device__ __forceinline__ void put_t_bf16(__bf16* dst, int ld, const f32x4_t& v) {
+  const int l16 = lane16(), g4 = lane_g4();
+  const bf16x4_t w = {static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]),
+                      static_cast<__bf16>(v[2]), static_cast<__bf16>(v[3])};
+  *reinterpret_cast<bf16x4_t*>(dst + l16 * ld + 4 * g4) = w;
+}
+// the same tile as bf16 in its own orientation; dst points at element (r0, c0)
+__device__ __forceinline__ void put_bf16(__bf16* dst, int ld, const f32x4_t& v) {
+  const int l16 = lane16(), g4 = lane_g4();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dst[(4 * g4 + i) * ld + l16] = static_cast<__bf16>(v[i]);
+}
+
+// ROWS x COLS bf16 (row stride COLS) global -> LDS (leading dimension ld), 16
+// bytes per lane; load(), pin_all() and store() as for GTile
+template <int NT, int ROWS, int COLS>
+struct BTile {
+  static constexpr int C8 = COLS / 8, N = ROWS * C8, PER = (N + NT - 1) / NT;
+  bf16x8_t r[PER];
+  __device__ __forceinline__ void load(const __bf16* src) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = static_cast<int>(threadIdx.x) + j * NT;
+      if (N % NT == 0 || e < N) {
+        const int rr = e / C8, c = (e - rr * C8) * 8;
+        r[j] = *reinterpret_cast<const bf16x8_t*>(src + rr * COLS + c);
+      }
+    }
+  }
+  __device__ __forceinline__ void pin_all() {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) pin(r[j]);
+  }
+  __device__ __forceinline__ void store(__bf16* dst, int ld) const {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = static_cast<int>(threadIdx.x) + j * NT;
+      if (N % NT == 0 || e < N) {
+        const int rr = e / C8, c = (e - rr * C8) * 8;
+        *reinterpret_cast<bf16x8_t*>(dst + rr * ld + c) = r[j];
+      }
+    }
+  }
+};
+
 // sub-tile pairs J < I of a 64-row chunk -> 0..5
 __device__ __forceinline__ int pair_index(int I, int J) { return I * (I - 1) / 2 + J; }
 
@@ -289,7 +344,8 @@ __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __res
                                                        const TIn* __restrict__ k,
                                                        const TIn* __restrict__ g,
                                                        const TIn* __restrict__ beta,
-                                                       float* __restrict__ ws, int T, int H,
+                                                       float* __restrict__ ws,
+                                                       __bf16* __restrict__ wsb, int T, int H,
                                                        int nc, float scale) {
   constexpr bool BF = IsBf16<TIn>::value && !EXACT;
   using L = BwdLayout<D>;
@@ -311,6 +367,7 @@ __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __res
   const TIn* kc = k + p.row0 * D;
   const TIn* gc = g + p.row0 * D;
   float* w = ws + static_cast<int64_t>(blockIdx.x) * L::WS;
+  __bf16* wb = BF ? wsb + static_cast<int64_t>(blockIdx.x) * L::WSB : nullptr;
 
   {
     ITile<kOpsThreads, D, TIn> gt;
@@ -350,8 +407,19 @@ __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __res
       const float kv = kt.r[j];
       R1[t * LD + i] = kv * expf(G - RI);
       R2[t * LD + i] = kv * expf(RI - G);
-      w[L::KT + e] = kv * expf(Gl - G);
+      const float ktv = kv * expf(Gl - G);
+      w[L::KT + e] = ktv;
       w[L::G + e] = G;
+      if constexpr (BF) wb[L::BKT + e] = static_cast<__bf16>(ktv);
+    }
+  }
+  if constexpr (BF) {   // Kt^T: consecutive threads take consecutive rows of one channel
+#pragma unroll
+    for (int j = 0; j < CR * D / kOpsThreads; ++j) {
+      const int e = tid + j * kOpsThreads, i = e / CR, t = e - i * CR;
+      const float x = to_f32(kc[min(t, p.nrow - 1) * rs + i]);
+      const float kv = t < p.nrow ? x : 0.f;
+      wb[L::BKTT + e] = static_cast<__bf16>(kv * expf(R0[(CR - 1) * LD + i] - R0[t * LD + i]));
     }
   }
   __syncthreads();
@@ -434,6 +502,13 @@ __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __res
     const float ti = S2[t * LS + s];
     w[L::TI + e] = ti;
     w[L::TB + e] = ti * BT[s];
+    if constexpr (BF) wb[L::BTB + e] = static_cast<__bf16>(ti * BT[s]);
+  }
+  if constexpr (BF) {   // Tb^T
+    for (int e = tid; e < CR * CR; e += kOpsThreads) {
+      const int s = e / CR, t = e - s * CR;
+      wb[L::BTBT + e] = static_cast<__bf16>(S2[t * LS + s] * BT[s]);
+    }
   }
   {   // k e^G into R1, scale q e^G into R2
     ITile<kOpsThreads, D, TIn> kt, qt;
@@ -460,6 +535,7 @@ __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __res
     for (int i = 0; i < 4; ++i) acc[i] *= f;
     put(S0 + 16 * rt * LS + 16 * ct, LS, acc);
     put(w + L::PP + 16 * rt * CR + 16 * ct, CR, acc);
+    if constexpr (BF) put_t_bf16(wb + L::BPT + 16 * ct * CR + 16 * rt, CR, acc);
   }
   constexpr int CT = D / 16;
   for (int j = wave; j < 4 * CT; j += kOpsWaves) {
@@ -467,6 +543,10 @@ __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __res
     const f32x4_t acc = mmx<BF, false, false, true>(zero4(), S2 + 16 * rt * LS, LS, R1 + 16 * ct, LD,
                                                CR, BT);
     put(w + L::W + 16 * rt * D + 16 * ct, D, acc);
+    if constexpr (BF) {
+      put_bf16(wb + L::BW + 16 * rt * D + 16 * ct, D, acc);
+      put_t_bf16(wb + L::BWT + 16 * ct * CR + 16 * rt, CR, acc);
+    }
   }
   __syncthreads();
   // Q' = scale q e^G - P (k e^G)
@@ -477,6 +557,7 @@ __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __res
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] -= pk[i];
     put(w + L::QP + 16 * rt * D + 16 * ct, D, acc);
+    if constexpr (BF) put_t_bf16(wb + L::BQPT + 16 * ct * CR + 16 * rt, CR, acc);
   }
 }
 

@@ -157,7 +157,7 @@ hipError_t launch_transition_t(const TransitionArgs& a) {
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((chunk_ops_kernel<D, TIn, true>), dim3(items), dim3(kOpsThreads), 0, a.stream,
                      static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
-                     static_cast<const TIn*>(a.g), static_cast<const TIn*>(a.beta), ws, a.T, a.H,
+                     static_cast<const TIn*>(a.g), static_cast<const TIn*>(a.beta), ws, nullptr, a.T, a.H,
                      nc, 1.0f);
   hipLaunchKernelGGL((transition_scan_kernel<D>), dim3(scan_grid(a.B * a.H, D / SL)), dim3(256),
                      0, a.stream, ws, a.transition, nc, a.B * a.H);

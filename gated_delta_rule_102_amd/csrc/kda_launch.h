@@ -70,8 +70,7 @@ hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_transition(const TransitionArgs& a);
 hipError_t launch_compose(const ComposeArgs& a);
 hipError_t launch_backward(const BackwardArgs& a);
-// device scratch the backward allocates (and frees) on the stream, in bytes
-int64_t backward_workspace_bytes(int B, int T, int H, int d);
+
 hipError_t launch_prefill(const PrefillArgs& a);
 
 }  // namespace kda
