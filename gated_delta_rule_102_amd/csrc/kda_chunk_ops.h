@@ -31,7 +31,8 @@ constexpr int LV = 36;    // leading dimension of 32-column LDS slices
 template <int D>
 struct BwdLayout {
   static constexpr int LD = D + 4;   // leading dimension of 64 x D LDS matrices
-  // workspace per chunk, written by bwd_prep (floats, row-major)
+  // workspace per chunk, written by chunk_ops (floats, row-major; for bf16 inputs
+  // W, QP and KT are written only as the bf16 copies below)
   static constexpr int TB = 0, TI = 4096, AP = 8192, MP = 12288, PP = 16384;
   static constexpr int W = 20480, QP = W + CR * D, KT = QP + CR * D, G = KT + CR * D;
   static constexpr int LAM = G + CR * D, WS = LAM + D;
@@ -408,18 +409,9 @@ __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __res
       R1[t * LD + i] = kv * expf(G - RI);
       R2[t * LD + i] = kv * expf(RI - G);
       const float ktv = kv * expf(Gl - G);
-      w[L::KT + e] = ktv;
+      if constexpr (!BF) w[L::KT + e] = ktv;   // bf16 inputs: only the bf16 copies are read
       w[L::G + e] = G;
       if constexpr (BF) wb[L::BKT + e] = static_cast<__bf16>(ktv);
-    }
-  }
-  if constexpr (BF) {   // Kt^T: consecutive threads take consecutive rows of one channel
-#pragma unroll
-    for (int j = 0; j < CR * D / kOpsThreads; ++j) {
-      const int e = tid + j * kOpsThreads, i = e / CR, t = e - i * CR;
-      const float x = to_f32(kc[min(t, p.nrow - 1) * rs + i]);
-      const float kv = t < p.nrow ? x : 0.f;
-      wb[L::BKTT + e] = static_cast<__bf16>(kv * expf(R0[(CR - 1) * LD + i] - R0[t * LD + i]));
     }
   }
   __syncthreads();
@@ -462,6 +454,16 @@ __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __res
   __syncthreads();
   l2g<kOpsThreads, CR, CR>(w + L::AP, CR, S0, LS);
   l2g<kOpsThreads, CR, CR>(w + L::MP, CR, S1, LS);
+  if constexpr (BF) {   // Kt in R1 (free until k e^G goes there), for its bf16 transpose
+    ITile<kOpsThreads, D, TIn> kt;
+    kt.load(kc, rs, p.nrow);
+    kt.pin_all();
+#pragma unroll
+    for (int j = 0; j < kt.PER; ++j) {
+      const int e = tid + j * kOpsThreads, t = e / D, i = e - t * D;
+      R1[t * LD + i] = kt.r[j] * expf(R0[(CR - 1) * LD + i] - R0[t * LD + i]);
+    }
+  }
 
   // Ti = (I + Diag(beta) A')^-1: diagonal 16 x 16 blocks by substitution (one
   // column per lane), then the blocks below them level by level:
@@ -504,11 +506,16 @@ __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __res
     w[L::TB + e] = ti * BT[s];
     if constexpr (BF) wb[L::BTB + e] = static_cast<__bf16>(ti * BT[s]);
   }
-  if constexpr (BF) {   // Tb^T
+  if constexpr (BF) {   // Tb^T and Kt^T (consecutive threads take consecutive rows)
     for (int e = tid; e < CR * CR; e += kOpsThreads) {
       const int s = e / CR, t = e - s * CR;
       wb[L::BTBT + e] = static_cast<__bf16>(S2[t * LS + s] * BT[s]);
     }
+    for (int e = tid; e < CR * D; e += kOpsThreads) {
+      const int i = e / CR, t = e - i * CR;
+      wb[L::BKTT + e] = static_cast<__bf16>(R1[t * LD + i]);
+    }
+    __syncthreads();   // R1 is rewritten next
   }
   {   // k e^G into R1, scale q e^G into R2
     ITile<kOpsThreads, D, TIn> kt, qt;
@@ -542,7 +549,7 @@ __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __res
     const int rt = j / CT, ct = j - rt * CT;
     const f32x4_t acc = mmx<BF, false, false, true>(zero4(), S2 + 16 * rt * LS, LS, R1 + 16 * ct, LD,
                                                CR, BT);
-    put(w + L::W + 16 * rt * D + 16 * ct, D, acc);
+    if constexpr (!BF) put(w + L::W + 16 * rt * D + 16 * ct, D, acc);
     if constexpr (BF) {
       put_bf16(wb + L::BW + 16 * rt * D + 16 * ct, D, acc);
       put_t_bf16(wb + L::BWT + 16 * ct * CR + 16 * rt, CR, acc);
@@ -556,7 +563,7 @@ __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __res
     f32x4_t acc = get(R2 + 16 * rt * LD + 16 * ct, LD);
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] -= pk[i];
-    put(w + L::QP + 16 * rt * D + 16 * ct, D, acc);
+    if constexpr (!BF) put(w + L::QP + 16 * rt * D + 16 * ct, D, acc);
     if constexpr (BF) put_t_bf16(wb + L::BQPT + 16 * ct * CR + 16 * rt, CR, acc);
   }
 }
