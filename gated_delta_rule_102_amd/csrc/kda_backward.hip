@@ -696,7 +696,7 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_nn_kernel(const TIn* __re
 #pragma unroll
     for (int j = 0; j < kt.PER; ++j) {
       const int e = tid + j * kNnThreads, t = e / D, i = e - t * D;
-      Kg[t * LD + i] = kt.r[j] * expf(Kg[t * LD + i]);
+      Kg[t * LD + i] = kt.r[j] * fexp(Kg[t * LD + i]);
     }
   }
   __syncthreads();
@@ -842,7 +842,7 @@ __global__ __launch_bounds__(512) void bwd_grad_decay_kernel(const TIn* __restri
     for (int I = 0; I < 4; ++I) Rf[I * D + tid] = w[L::G + (16 * I + 15) * D + tid];
     for (int I = 1; I < 4; ++I)
       for (int J = 0; J < I; ++J)
-        FP[pair_index(I, J) * D + tid] = expf(Rf[I * D + tid] - Rf[J * D + tid]);
+        FP[pair_index(I, J) * D + tid] = fexp(Rf[I * D + tid] - Rf[J * D + tid]);
   }
   {
     GTile<512, CR, CR> t_da, t_dm;
@@ -868,7 +868,7 @@ __global__ __launch_bounds__(512) void bwd_grad_decay_kernel(const TIn* __restri
     for (int j = 0; j < kt.PER; ++j) {
       const int e = tid + j * 512, t = e / D, i = e - t * D;
       const float G = Qo[t * LD + i], RI = Rf[(t >> 4) * D + i];
-      const float rowf = expf(G - RI), colf = expf(RI - G);
+      const float rowf = fexp(G - RI), colf = fexp(RI - G);
       Ki[t * LD + i] = kt.r[j] * colf;
       Ko[t * LD + i] = kt.r[j] * rowf;
       Qo[t * LD + i] = qt.r[j] * rowf;
@@ -953,7 +953,7 @@ __global__ __launch_bounds__(512) void bwd_grad_decay_kernel(const TIn* __restri
       for (int i = 0; i < 4; ++i) {
         const int t = 16 * R + 4 * g4 + i;
         const float G = eG[xx][i];
-        const float rowf = expf(G - RI), colf = expf(RI - G), eg = expf(G), et = expf(Gl - G);
+        const float rowf = fexp(G - RI), colf = fexp(RI - G), eg = fexp(G), et = fexp(Gl - G);
         const float XA = rowf * xa[x][i], XM = rowf * xm[x][i];
         const float ZA = colf * za[x][i], ZM = colf * zm[x][i];
         const bool ok = t < p.nrow;
