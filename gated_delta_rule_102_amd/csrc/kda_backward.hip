@@ -282,7 +282,9 @@ __global__ __launch_bounds__(kScanThreads) void bwd_scan_kernel(const TIn* __res
 // writes in exactly those layouts (Tb, W, Kt^T for the forward scan; Kt, W^T,
 // Q'^T, P^T, Tb^T for the reverse one) and are staged by plain 16-byte copies;
 // only V and dO are transposed while staged, and the fp32 state and the
-// per-step products (Delta, dU) go to LDS as bf16 transposes.
+// per-step products (Delta, dU) go to LDS as bf16 transposes.  The per-chunk
+// states and state gradients and Delta, dU are stored as bf16 for the operand
+// gradient kernel, which rounds them to bf16 for its products in any case.
 
 // acc += A B, A(r, k) = a[r * lda + k], B(k, c) = b[c * ldb + k] (bf16 in LDS)
 template <int K>
@@ -313,7 +315,7 @@ __device__ __forceinline__ void stage_bf16_t(const ITile<NT, COLS, bf16_t>& t, _
 template <int D>
 __global__ __launch_bounds__(kScanThreads) void bwd_fwd_scan_bf16_kernel(
     const bf16_t* __restrict__ v, const float* __restrict__ s0, const float* __restrict__ ws,
-    const __bf16* __restrict__ wsb, float* __restrict__ st, float* __restrict__ dl, int T, int H,
+    const __bf16* __restrict__ wsb, __bf16* __restrict__ st, __bf16* __restrict__ dl, int T, int H,
     int nc, int BH) {
   using L = BwdLayout<D>;
   using ST = ScanTiles<D>;
@@ -373,7 +375,7 @@ __global__ __launch_bounds__(kScanThreads) void bwd_fwd_scan_bf16_kernel(
     for (int x = 0; x < ST::NTW; ++x) {
       const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
       put_t_bf16(STr + 16 * ct * LB + 16 * rt, LB, S[x]);
-      put(st + item * D * D + 16 * rt * D + c0 + 16 * ct, D, S[x]);
+      put_bf16(st + item * D * D + 16 * rt * D + c0 + 16 * ct, D, S[x]);
     }
     __syncthreads();
     {   // Delta = Tb V - W S: 4 x 2 tiles, one per wavefront
@@ -384,7 +386,7 @@ __global__ __launch_bounds__(kScanThreads) void bwd_fwd_scan_bf16_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) d[i] = tv[i] - wsv[i];
       put_t_bf16(DT + 16 * ct * L64 + 16 * rt, L64, d);
-      put(dl + item * CR * D + 16 * rt * D + c0 + 16 * ct, D, d);
+      put_bf16(dl + item * CR * D + 16 * rt * D + c0 + 16 * ct, D, d);
     }
     __syncthreads();
 #pragma unroll
@@ -402,7 +404,7 @@ __global__ __launch_bounds__(kScanThreads) void bwd_fwd_scan_bf16_kernel(
 template <int D>
 __global__ __launch_bounds__(kScanThreads) void bwd_scan_bf16_kernel(
     const bf16_t* __restrict__ dout, const float* __restrict__ dsT, const float* __restrict__ ws,
-    const __bf16* __restrict__ wsb, float* __restrict__ dst, float* __restrict__ du,
+    const __bf16* __restrict__ wsb, __bf16* __restrict__ dst, __bf16* __restrict__ du,
     bf16_t* __restrict__ dv, float* __restrict__ ds0, int T, int H, int nc, int BH) {
   using L = BwdLayout<D>;
   using ST = ScanTiles<D>;
@@ -473,14 +475,14 @@ __global__ __launch_bounds__(kScanThreads) void bwd_scan_bf16_kernel(
     for (int x = 0; x < ST::NTW; ++x) {
       const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
       put_t_bf16(dST + 16 * ct * LB + 16 * rt, LB, dS[x]);
-      put(dst + item * D * D + 16 * rt * D + c0 + 16 * ct, D, dS[x]);
+      put_bf16(dst + item * D * D + 16 * rt * D + c0 + 16 * ct, D, dS[x]);
     }
     __syncthreads();
     {   // dU = Kt dS: one tile per wavefront
       const int rt = wave >> 1, ct = wave & 1;
       const f32x4_t u = mmb<D>(zero4(), KTs + 16 * rt * LB, LB, dST + 16 * ct * LB, LB);
       put_t_bf16(dUT + 16 * ct * L64 + 16 * rt, L64, u);
-      put(du + item * CR * D + 16 * rt * D + c0 + 16 * ct, D, u);
+      put_bf16(du + item * CR * D + 16 * rt * D + c0 + 16 * ct, D, u);
     }
     __syncthreads();
     {   // dV = P^T dO + Tb^T dU
@@ -590,6 +592,137 @@ __global__ __launch_bounds__(512) void bwd_grad_dv_kernel(const TIn* __restrict_
     if (tid < D) {
 #pragma unroll 8
       for (int jj = 0; jj < SL; ++jj) dlam += Ss[tid * LV + jj] * dSs[tid * LV + jj];
+    }
+    __syncthreads();
+  }
+  float* o = g1 + item * L::G1;
+#pragma unroll
+  for (int x = 0; x < NTW; ++x) {
+    const int j = wave + 8 * x;
+    if (j < 3 * NBIG) {
+      const int m = j / NBIG, r = j - m * NBIG, rt = r / CT, ct = r - rt * CT;
+      f32x4_t vv = acc[x];
+      if (m == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vv[i] = -vv[i];
+      }
+      put(o + m * CR * D + 16 * rt * D + 16 * ct, D, vv);
+    } else {
+      const int j2 = j - 3 * NBIG, m = j2 >> 4, rt = (j2 & 15) >> 2, ct = j2 & 3;
+      put(o + (m == 0 ? L::DP : L::DTB) + 16 * rt * CR + 16 * ct, CR, acc[x]);
+    }
+  }
+  if (tid < D) o[L::DLAM + tid] = dlam;
+}
+
+// bf16 inputs: the same contractions from bf16 per-chunk states (S, dS_next),
+// Delta, dU and the bf16 inputs, every product in natural row-major layouts
+// (A(r, k) row-major, B(k, c) = X[c][k] with X row-major) on bf16 matrix cores.
+template <int NT, int ROWS, int COLS>
+struct BTileS {   // ROWS x COLS bf16 slice of a matrix with row stride gld
+  static constexpr int C8 = COLS / 8, N = ROWS * C8, PER = (N + NT - 1) / NT;
+  bf16x8_t r[PER];
+  static __device__ __forceinline__ bool live(int e) { return N % NT == 0 || e < N; }
+  __device__ __forceinline__ void load(const __bf16* src, int64_t gld) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = static_cast<int>(threadIdx.x) + j * NT, rr = e / C8, c = (e - rr * C8) * 8;
+      if (live(e)) r[j] = *reinterpret_cast<const bf16x8_t*>(src + rr * gld + c);
+    }
+  }
+  // 64 input rows (row stride gld), rows >= nrow as zero (clamped loads)
+  __device__ __forceinline__ void load_rows(const bf16_t* src, int64_t gld, int nrow) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = static_cast<int>(threadIdx.x) + j * NT, rr = e / C8, c = (e - rr * C8) * 8;
+      if (live(e)) {
+        const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(
+            src + static_cast<int64_t>(min(rr, nrow - 1)) * gld + c);
+        r[j] = rr < nrow ? x : bf16x8_t{};
+      }
+    }
+  }
+  __device__ __forceinline__ void pin_all() {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) pin(r[j]);
+  }
+  __device__ __forceinline__ void store(__bf16* dst, int ld) const {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = static_cast<int>(threadIdx.x) + j * NT, rr = e / C8, c = (e - rr * C8) * 8;
+      if (live(e)) *reinterpret_cast<bf16x8_t*>(dst + rr * ld + c) = r[j];
+    }
+  }
+};
+
+template <int D>
+__global__ __launch_bounds__(512) void bwd_grad_dv_bf16_kernel(
+    const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout, const __bf16* __restrict__ st,
+    const __bf16* __restrict__ dst, const __bf16* __restrict__ dl, const __bf16* __restrict__ du,
+    float* __restrict__ g1, int T, int H, int nc) {
+  using L = BwdLayout<D>;
+  constexpr int LVB = SL + 8;   // bf16 leading dimension of the 32-column slices
+  __shared__ __attribute__((aligned(16))) __bf16 sm[2 * D * LVB + 4 * CR * LVB];
+  __bf16* Ss = sm;
+  __bf16* dSs = Ss + D * LVB;
+  __bf16* dOs = dSs + D * LVB;
+  __bf16* dUs = dOs + CR * LVB;
+  __bf16* Dls = dUs + CR * LVB;
+  __bf16* Vs = Dls + CR * LVB;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const ChunkPos p = chunk_pos(blockIdx.x, T, H, nc);
+  const int64_t item = blockIdx.x;
+  const int64_t rs = static_cast<int64_t>(H) * D;
+  constexpr int CT = D / 16;
+  constexpr int NBIG = 4 * CT;
+  constexpr int NTOT = 3 * NBIG + 32, NTW = NTOT / 8;
+  static_assert(NTOT % 8 == 0, "tile split");
+
+  f32x4_t acc[NTW];
+#pragma unroll
+  for (int x = 0; x < NTW; ++x) acc[x] = zero4();
+  float dlam = 0.f;
+  for (int c0 = 0; c0 < D; c0 += SL) {
+    {
+      BTileS<512, D, SL> t_s, t_ds;
+      BTileS<512, CR, SL> t_dl, t_du, t_do, t_v;
+      t_s.load(st + item * D * D + c0, D);
+      t_ds.load(dst + item * D * D + c0, D);
+      t_dl.load(dl + item * CR * D + c0, D);
+      t_du.load(du + item * CR * D + c0, D);
+      t_do.load_rows(dout + p.row0 * D + c0, rs, p.nrow);
+      t_v.load_rows(v + p.row0 * D + c0, rs, p.nrow);
+      t_s.pin_all();
+      t_ds.pin_all();
+      t_dl.pin_all();
+      t_du.pin_all();
+      t_do.pin_all();
+      t_v.pin_all();
+      t_s.store(Ss, LVB);
+      t_ds.store(dSs, LVB);
+      t_dl.store(Dls, LVB);
+      t_du.store(dUs, LVB);
+      t_do.store(dOs, LVB);
+      t_v.store(Vs, LVB);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < NTW; ++x) {
+      const int j = wave + 8 * x;
+      if (j < 3 * NBIG) {   // dQ' = dO S^T, -dW = dU S^T, dKt = Delta dS^T
+        const int m = j / NBIG, r = j - m * NBIG, rt = r / CT, ct = r - rt * CT;
+        const __bf16* A = (m == 0 ? dOs : m == 1 ? dUs : Dls) + 16 * rt * LVB;
+        const __bf16* Bm = (m == 2 ? dSs : Ss) + 16 * ct * LVB;
+        acc[x] = mmb<SL>(acc[x], A, LVB, Bm, LVB);
+      } else {              // dP = dO V^T, dTb = dU V^T
+        const int j2 = j - 3 * NBIG, m = j2 >> 4, rt = (j2 & 15) >> 2, ct = j2 & 3;
+        acc[x] = mmb<SL>(acc[x], (m == 0 ? dOs : dUs) + 16 * rt * LVB, LVB, Vs + 16 * ct * LVB, LVB);
+      }
+    }
+    if (tid < D) {
+#pragma unroll 8
+      for (int jj = 0; jj < SL; ++jj)
+        dlam += static_cast<float>(Ss[tid * LVB + jj]) * static_cast<float>(dSs[tid * LVB + jj]);
     }
     __syncthreads();
   }
@@ -988,19 +1121,28 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
   const int nc = (a.T + CR - 1) / CR;
   const int64_t items = static_cast<int64_t>(a.B) * a.H * nc;
   constexpr bool BF = IsBf16<TIn>::value;
-  // fp32 regions, then (bf16 inputs) the bf16 scan operands, WSB/2 floats per chunk
-  const int64_t per = L::WS + 2 * D * D + 2 * CR * D + L::G1 + L::G2 + (BF ? L::WSB / 2 : 0);
+  // per chunk, in floats: the fp32 operands, the operand gradients, then the states,
+  // state gradients, Delta and dU (fp32, or bf16 for bf16 inputs: half the floats),
+  // then for bf16 inputs the bf16 scan operands
+  const int64_t sdu = (BF ? 1 : 2) * (D * D + CR * D);
+  const int64_t per = L::WS + L::G1 + L::G2 + sdu + (BF ? L::WSB / 2 : 0);
   float* buf = nullptr;
   hipError_t err = hipMallocAsync(reinterpret_cast<void**>(&buf), items * per * sizeof(float), a.stream);
   if (err != hipSuccess) return err;
   float* ws = buf;
-  float* st = ws + items * L::WS;
+  float* g1 = ws + items * L::WS;
+  float* g2 = g1 + items * L::G1;
+  float* sreg = g2 + items * L::G2;   // S, dS, Delta, dU in the element type chosen above
+  __bf16* wsb = BF ? reinterpret_cast<__bf16*>(sreg + items * sdu) : nullptr;
+  float* st = sreg;
   float* dst = st + items * D * D;
   float* dl = dst + items * D * D;
   float* du = dl + items * CR * D;
-  float* g1 = du + items * CR * D;
-  float* g2 = g1 + items * L::G1;
-  __bf16* wsb = BF ? reinterpret_cast<__bf16*>(g2 + items * L::G2) : nullptr;
+  __bf16* sb = reinterpret_cast<__bf16*>(sreg);
+  __bf16* stb = sb;
+  __bf16* dstb = stb + items * D * D;
+  __bf16* dlb = dstb + items * D * D;
+  __bf16* dub = dlb + items * CR * D;
   const TIn* q = static_cast<const TIn*>(a.q);
   const TIn* k = static_cast<const TIn*>(a.k);
   const TIn* v = static_cast<const TIn*>(a.v);
@@ -1013,19 +1155,21 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
                      ws, wsb, a.T, a.H, nc, a.scale);
   if constexpr (IsBf16<TIn>::value) {
     hipLaunchKernelGGL((bwd_fwd_scan_bf16_kernel<D>), dim3(scan_blocks), dim3(kScanThreads), 0,
-                       a.stream, v, a.initial_state, ws, wsb, st, dl, a.T, a.H, nc, BH);
+                       a.stream, v, a.initial_state, ws, wsb, stb, dlb, a.T, a.H, nc, BH);
     hipLaunchKernelGGL((bwd_scan_bf16_kernel<D>), dim3(scan_blocks), dim3(kScanThreads), 0,
-                       a.stream, dout, a.d_final_state, ws, wsb, dst, du,
+                       a.stream, dout, a.d_final_state, ws, wsb, dstb, dub,
                        static_cast<TIn*>(a.dv), a.d_initial_state, a.T, a.H, nc, BH);
+    hipLaunchKernelGGL((bwd_grad_dv_bf16_kernel<D>), dim3(items), dim3(512), 0, a.stream, v, dout,
+                       stb, dstb, dlb, dub, g1, a.T, a.H, nc);
   } else {
     hipLaunchKernelGGL((bwd_fwd_scan_kernel<D, TIn>), dim3(scan_blocks), dim3(kScanThreads), 0, a.stream, v,
                        a.initial_state, ws, st, dl, a.T, a.H, nc, BH);
     hipLaunchKernelGGL((bwd_scan_kernel<D, TIn>), dim3(scan_blocks), dim3(kScanThreads), 0, a.stream, dout,
                        a.d_final_state, ws, dst, du, static_cast<TIn*>(a.dv), a.d_initial_state,
                        a.T, a.H, nc, BH);
+    hipLaunchKernelGGL((bwd_grad_dv_kernel<D, TIn>), dim3(items), dim3(512), 0, a.stream, v, dout,
+                       st, dst, dl, du, g1, a.T, a.H, nc);
   }
-  hipLaunchKernelGGL((bwd_grad_dv_kernel<D, TIn>), dim3(items), dim3(512), 0, a.stream, v, dout,
-                     st, dst, dl, du, g1, a.T, a.H, nc);
   hipLaunchKernelGGL((bwd_grad_nn_kernel<D, TIn>), dim3(items), dim3(kNnThreads), 0, a.stream, k, beta,
                      ws, g1, g2, static_cast<TIn*>(a.dbeta), a.T, a.H, nc, a.scale);
   hipLaunchKernelGGL((bwd_grad_decay_kernel<D, TIn>), dim3(items), dim3(512), 0, a.stream, q, k,
