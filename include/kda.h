@@ -180,8 +180,10 @@ int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void
  * alignment.  The forward is recomputed inside the call (nothing is kept from
  * kda_chunk_fwd).  All arithmetic is fp32 (fp32 matrix cores), also for bf16
  * inputs.  The call allocates a workspace with hipMallocAsync on `stream` and
- * frees it on the same stream: 607,232 bytes per 64-token chunk per head at
- * d = 128 (344,576 at d = 64); an allocation failure returns KDA_ERR_HIP.
+ * frees it on the same stream, per 64-token chunk per head: 615,424 bytes for
+ * bf16 and 607,232 for fp32 at d = 128 (377,344 and 344,576 at d = 64), so
+ * T = 65,536 with 32 heads needs about 20 GB; an allocation failure returns
+ * KDA_ERR_HIP.
  * Outputs must not alias inputs.
  */
 int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
