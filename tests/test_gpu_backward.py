@@ -121,3 +121,33 @@ def test_backward_deterministic():
     b = run_gpu(d, c, 0.1)
     for n in NAMES:
         assert torch.equal(a[n], b[n]), n
+
+
+def test_backward_full_size_sampled():
+    """4 sequences x 4096 tokens x 16 heads, d = 128, bf16, nonzero state: the whole
+    batch on the GPU in one call; two (sequence, head) pairs against the oracle."""
+    B, T, H, D = 4, 4096, 16, 128
+    d = kin.make_prefill(B, T, H, D, D, dtype=torch.bfloat16, seed=360, nonzero_state=True)
+    c = kin.make_cotangents(B, T, H, D, D, dtype=torch.bfloat16, seed=460)
+    got = run_gpu(d, c, 1.0 / math.sqrt(D))
+    for b, h in ((0, 3), (3, 14)):
+        sl = {k: d[k][b:b + 1, :, h:h + 1].contiguous() for k in ("q", "k", "v", "g", "beta")}
+        sl["initial_state"] = d["initial_state"][b:b + 1, h:h + 1].contiguous()
+        cs = dict(grad_out=c["grad_out"][b:b + 1, :, h:h + 1].contiguous(),
+                  grad_final_state=c["grad_final_state"][b:b + 1, h:h + 1].contiguous())
+        ref = run_oracle(sl, cs, 1.0 / math.sqrt(D))
+        for n in NAMES:
+            x = got[n][b:b + 1, h:h + 1] if n == "ds0" else got[n][b:b + 1, :, h:h + 1]
+            grad_close(f"{n} (b={b}, h={h})", x, ref[n], torch.bfloat16)
+
+
+@pytest.mark.parametrize("B,T,H,D,dtype", [(3, 63, 3, 64, torch.bfloat16),
+                                           (1, 129, 5, 128, torch.bfloat16),
+                                           (2, 191, 1, 64, torch.float32),
+                                           (5, 64, 2, 128, torch.float32)])
+def test_backward_odd_shapes(B, T, H, D, dtype):
+    """Odd batch and head counts (scan grids padded to whole XCD groups), lengths on
+    both sides of a chunk boundary, both dtypes."""
+    d = kin.make_prefill(B, T, H, D, D, dtype=dtype, seed=370 + T + H, nonzero_state=True)
+    c = kin.make_cotangents(B, T, H, D, D, dtype=dtype, seed=470 + T + H)
+    check(d, c, 1.0 / math.sqrt(D), dtype)
