@@ -32,19 +32,6 @@ namespace {
 
 // ---------------------------------------------------------------- scans
 
-// Scan workgroups have 8 wavefronts (two per SIMD, so one's LDS and memory waits
-// overlap the other's matrix work).  State tiles of one workgroup: D x 32 columns
-// = (D/16) x 2 tiles, D/64 per wavefront; the 64 x 32 per-chunk products are
-// 4 x 2 tiles, one per wavefront.
-constexpr int kScanThreads = 512;
-
-template <int D>
-struct ScanTiles {
-  static constexpr int NTW = D / 64;
-  static __device__ __forceinline__ int rt(int wave, int x) { return (wave * NTW + x) >> 1; }
-  static __device__ __forceinline__ int ct(int wave, int x) { return (wave * NTW + x) & 1; }
-};
-
 template <int D, typename TIn>
 __global__ __launch_bounds__(kScanThreads) void bwd_fwd_scan_kernel(const TIn* __restrict__ v,
                                                            const float* __restrict__ s0,
@@ -285,21 +272,6 @@ __global__ __launch_bounds__(kScanThreads) void bwd_scan_kernel(const TIn* __res
 // per-step products (Delta, dU) go to LDS as bf16 transposes.  The per-chunk
 // states and state gradients and Delta, dU are stored as bf16 for the operand
 // gradient kernel, which rounds them to bf16 for its products in any case.
-
-// acc += A B, A(r, k) = a[r * lda + k], B(k, c) = b[c * ldb + k] (bf16 in LDS)
-template <int K>
-__device__ __forceinline__ f32x4_t mmb(f32x4_t acc, const __bf16* a, int lda, const __bf16* b,
-                                       int ldb) {
-  const int l16 = lane16(), g4 = lane_g4();
-#pragma unroll
-  for (int k0 = 0; k0 < K; k0 += 32) {
-    const int kb = k0 + 8 * g4;
-    const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(a + l16 * lda + kb);
-    const bf16x8_t B = *reinterpret_cast<const bf16x8_t*>(b + l16 * ldb + kb);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc, 0, 0, 0);
-  }
-  return acc;
-}
 
 // a 64 x COLS input tile (bf16) to LDS transposed ([c][r])
 template <int NT, int COLS>

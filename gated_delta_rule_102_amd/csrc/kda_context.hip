@@ -16,7 +16,12 @@
 // the chunked form.
 //
 //   transition_scan_kernel: per (sequence, head, 32 columns of P) the scan
-//       S <- Lam S - Kt^T (W S) from the identity's columns, fp32 throughout.
+//       S <- Lam S - Kt^T (W S) from the identity's columns, fp32 throughout
+//       (fp32 inputs).
+//   transition_scan_bf16_kernel: the same scan for bf16 inputs with bf16
+//       matrix-core operands (W and Kt^T as the chunk operands' bf16 copies, the
+//       state and W S as bf16 transposes) and the fp32 state in registers, the
+//       precision of the bf16 prefill.
 //   compose_kernel: per (sequence, head, 32 value columns) the composition over
 //       the segments, S <- P_r S + R_r, writing every entry state and the exit
 //       state of the last segment.
@@ -98,6 +103,79 @@ __global__ __launch_bounds__(256) void transition_scan_kernel(const float* __res
 }
 
 template <int D>
+__global__ __launch_bounds__(kScanThreads) void transition_scan_bf16_kernel(
+    const float* __restrict__ ws, const __bf16* __restrict__ wsb, float* __restrict__ trans,
+    int nc, int BH) {
+  using L = BwdLayout<D>;
+  using ST = ScanTiles<D>;
+  constexpr int LB = D + 8, L64 = CR + 8;
+  __shared__ __attribute__((aligned(16))) __bf16 sb[CR * LB + D * L64 + SL * LB + SL * L64];
+  __shared__ float Lm[D];
+  __bf16* Ws = sb;                  // W      [t][i]
+  __bf16* KTT = Ws + CR * LB;       // Kt^T   [i][t]
+  __bf16* STr = KTT + D * L64;      // S^T    [j][i]
+  __bf16* UT = STr + SL * LB;       // (W S)^T [j][t]
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int l16 = lane16(), g4 = lane_g4();
+  constexpr int NSL = D / SL;
+  int bh, c0;
+  if (!scan_block<NSL>(BH, bh, c0)) return;
+
+  f32x4_t S[ST::NTW];
+#pragma unroll
+  for (int x = 0; x < ST::NTW; ++x) {   // columns c0 .. c0 + 31 of the identity
+    const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) S[x][i] = (16 * rt + 4 * g4 + i == c0 + 16 * ct + l16) ? 1.f : 0.f;
+  }
+  BTile<kScanThreads, CR, D> t_w;
+  BTile<kScanThreads, D, CR> t_ktt;
+  float lm;
+  auto issue = [&](int c) {
+    const int64_t item = static_cast<int64_t>(bh) * nc + c;
+    const __bf16* wb = wsb + item * L::WSB;
+    t_w.load(wb + L::BW);
+    t_ktt.load(wb + L::BKTT);
+    lm = ws[item * L::WS + L::LAM + (tid & (D - 1))];
+  };
+  issue(0);
+  for (int c = 0; c < nc; ++c) {
+    t_w.pin_all();
+    t_ktt.pin_all();
+    pin(lm);
+    t_w.store(Ws, LB);
+    t_ktt.store(KTT, L64);
+    if (tid < D) Lm[tid] = lm;
+    if (c + 1 < nc) issue(c + 1);
+#pragma unroll
+    for (int x = 0; x < ST::NTW; ++x) {
+      const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
+      put_t_bf16(STr + 16 * ct * LB + 16 * rt, LB, S[x]);
+    }
+    __syncthreads();
+    {   // W S: 4 x 2 tiles, one per wavefront
+      const int rt = wave >> 1, ct = wave & 1;
+      const f32x4_t u = mmb<D>(zero4(), Ws + 16 * rt * LB, LB, STr + 16 * ct * LB, LB);
+      put_t_bf16(UT + 16 * ct * L64 + 16 * rt, L64, u);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < ST::NTW; ++x) {   // S = Lam S - Kt^T (W S)
+      const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
+      const f32x4_t kd = mmb<CR>(zero4(), KTT + 16 * rt * L64, L64, UT + 16 * ct * L64, L64);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[x][i] = Lm[16 * rt + 4 * g4 + i] * S[x][i] - kd[i];
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int x = 0; x < ST::NTW; ++x) {
+    const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
+    put(trans + static_cast<int64_t>(bh) * D * D + 16 * rt * D + c0 + 16 * ct, D, S[x]);
+  }
+}
+
+template <int D>
 __global__ __launch_bounds__(256) void compose_kernel(const float* __restrict__ trans,
                                                       const float* __restrict__ part,
                                                       const float* __restrict__ s0,
@@ -152,15 +230,28 @@ hipError_t launch_transition_t(const TransitionArgs& a) {
   using L = BwdLayout<D>;
   const int nc = (a.T + CR - 1) / CR;
   const int64_t items = static_cast<int64_t>(a.B) * a.H * nc;
+  constexpr bool BF = IsBf16<TIn>::value;
   float* ws = nullptr;
-  hipError_t err = hipMallocAsync(reinterpret_cast<void**>(&ws), items * L::WS * sizeof(float), a.stream);
+  const int64_t per = L::WS + (BF ? L::WSB / 2 : 0);   // floats per chunk
+  hipError_t err = hipMallocAsync(reinterpret_cast<void**>(&ws), items * per * sizeof(float), a.stream);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((chunk_ops_kernel<D, TIn, true>), dim3(items), dim3(kOpsThreads), 0, a.stream,
-                     static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
-                     static_cast<const TIn*>(a.g), static_cast<const TIn*>(a.beta), ws, nullptr, a.T, a.H,
-                     nc, 1.0f);
-  hipLaunchKernelGGL((transition_scan_kernel<D>), dim3(scan_grid(a.B * a.H, D / SL)), dim3(256),
-                     0, a.stream, ws, a.transition, nc, a.B * a.H);
+  __bf16* wsb = BF ? reinterpret_cast<__bf16*>(ws + items * L::WS) : nullptr;
+  const int BH = a.B * a.H;
+  if constexpr (BF) {   // bf16 operands, the prefill's precision
+    hipLaunchKernelGGL((chunk_ops_kernel<D, TIn, false>), dim3(items), dim3(kOpsThreads), 0,
+                       a.stream, static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
+                       static_cast<const TIn*>(a.g), static_cast<const TIn*>(a.beta), ws, wsb, a.T,
+                       a.H, nc, 1.0f);
+    hipLaunchKernelGGL((transition_scan_bf16_kernel<D>), dim3(scan_grid(BH, D / SL)),
+                       dim3(kScanThreads), 0, a.stream, ws, wsb, a.transition, nc, BH);
+  } else {
+    hipLaunchKernelGGL((chunk_ops_kernel<D, TIn, true>), dim3(items), dim3(kOpsThreads), 0,
+                       a.stream, static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
+                       static_cast<const TIn*>(a.g), static_cast<const TIn*>(a.beta), ws, nullptr,
+                       a.T, a.H, nc, 1.0f);
+    hipLaunchKernelGGL((transition_scan_kernel<D>), dim3(scan_grid(BH, D / SL)), dim3(256), 0,
+                       a.stream, ws, a.transition, nc, BH);
+  }
   err = hipGetLastError();
   const hipError_t ferr = hipFreeAsync(ws, a.stream);
   return err != hipSuccess ? err : ferr;
