@@ -213,9 +213,12 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, co
  *                  run with v = 0 from the identity, i.e. the product of its
  *                  per-token maps (I - beta_t k_t k_t^T) Diag(exp g_t), latest
  *                  token leftmost.
- * dk == dv in {64, 128} for both dtypes; arithmetic is fp32.  Allocates a
- * workspace of 213,504 bytes per 64-token chunk per head at d = 128 (147,712 at
- * d = 64) with hipMallocAsync on `stream`, freed on the same stream.
+ * dk == dv in {64, 128} for both dtypes.  fp32 inputs are computed on fp32
+ * operands; bf16 inputs on bf16 matrix-core operands with fp32 accumulation and
+ * an fp32 state, the precision of the bf16 prefill.  Allocates a workspace per
+ * 64-token chunk per head of 213,504 bytes for fp32 and 320,000 for bf16 at
+ * d = 128 (147,712 and 213,248 at d = 64) with hipMallocAsync on `stream`, freed
+ * on the same stream.
  */
 int kda_chunk_transition(const void* q, const void* k, const void* g, const void* beta,
                          float* transition, int B, int T, int H, int dk, int dv, int dtype,
