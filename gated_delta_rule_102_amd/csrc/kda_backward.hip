@@ -919,7 +919,9 @@ __global__ __launch_bounds__(512) void bwd_grad_decay_kernel(const TIn* __restri
                                                              TIn* __restrict__ dk,
                                                              TIn* __restrict__ dg, int T, int H,
                                                              int nc, float scale) {
-  constexpr bool BF = IsBf16<TIn>::value;   // bf16 matrix-core operands for bf16 inputs
+  // Every product here stays on fp32 operands, also for bf16 inputs: dG combines
+  // the row-side and column-side products with opposite signs (X_A - Z_A - Z_M),
+  // and with bf16 operands that cancellation took dg past its tolerance.
   using L = BwdLayout<D>;
   constexpr int LD = L::LD;
   __shared__ __attribute__((aligned(16))) float sm[3 * CR * LD + 2 * CR * LS + 10 * D];

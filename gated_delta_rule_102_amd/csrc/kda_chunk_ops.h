@@ -207,13 +207,6 @@ struct GTile {
   }
 };
 template <int NT, int ROWS, int COLS>
-__device__ __forceinline__ void g2l(float* dst, int lld, const float* src, int64_t gld) {
-  GTile<NT, ROWS, COLS> t;
-  t.load(src, gld);
-  t.pin_all();
-  t.store(dst, lld);
-}
-template <int NT, int ROWS, int COLS>
 __device__ __forceinline__ void l2g(float* dst, int64_t gld, const float* src, int lld) {
   constexpr int C4 = COLS / 4, N = ROWS * C4;
 #pragma unroll
