@@ -21,7 +21,11 @@
 //                inverse (dP_tot, dKg, dTb_tot, dM', dA', dbeta);
 //   bwd_grad_decay per chunk: the decayed products of dA' and dM' with k and q,
 //                and the chain to dq, dk and dg (a reverse running sum).
-// Every product runs on the fp32 16x16x4 matrix cores from LDS.
+// Products run on the matrix cores from LDS: fp32 16x16x4 for fp32 inputs; for
+// bf16 inputs the scans and the operand-gradient and 64 x 64 kernels use bf16
+// operands (16x16x32) with fp32 accumulation, and the decayed products stay fp32.
+
+#include <type_traits>
 
 #include "kda_chunk_ops.h"
 #include "kda_launch.h"
@@ -730,6 +734,45 @@ struct NnLds {
   static constexpr int TOTAL = FRONT + CR * LS + CR;
 };
 
+// 64 x COLS input rows (bf16 or fp32) held as raw words, 4 consecutive elements per
+// thread in the GTile<NT, 64, COLS> element order; rows >= nrow read as zero.
+template <int NT, int COLS, typename TIn>
+struct ITile4 {
+  static constexpr int C4 = COLS / 4, N = CR * C4, PER = N / NT;
+  static_assert(N % NT == 0, "tile split");
+  static constexpr bool BF = IsBf16<TIn>::value;
+  using Raw = typename std::conditional<BF, i32x2_t, f32x4_t>::type;
+  Raw r[PER];
+  __device__ __forceinline__ void load(const TIn* src, int64_t row_stride, int nrow) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = static_cast<int>(threadIdx.x) + j * NT;
+      const int rr = e / C4, c = (e - rr * C4) * 4;
+      r[j] = *reinterpret_cast<const Raw*>(src + min(rr, nrow - 1) * row_stride + c);
+    }
+  }
+  __device__ __forceinline__ void pin_all() {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) pin(r[j]);
+  }
+  __device__ __forceinline__ f32x4_t get(int j, int nrow) const {
+    const int rr = (static_cast<int>(threadIdx.x) + j * NT) / C4;
+    f32x4_t x;
+    if constexpr (BF) {
+      const uint32_t w0 = static_cast<uint32_t>(r[j][0]), w1 = static_cast<uint32_t>(r[j][1]);
+      x = f32x4_t{bf16lo(w0), bf16hi(w0), bf16lo(w1), bf16hi(w1)};
+    } else {
+      x = r[j];
+    }
+    return rr < nrow ? x : zero4();
+  }
+};
+
+// One workgroup per (chunk, head).  Every global load of the item is issued at the
+// top in two register sets: X (G, dQ', dW, P, Tb, k), written to LDS at once, and
+// Y (dP, dTb, M', Ti, A', beta), used by the later phases.  Vector-memory counters
+// retire in order, so the first use of Y waits only for Y, whose latency hides
+// behind the phase-A products instead of stalling each phase in turn.
 template <int D, typename TIn>
 __global__ __launch_bounds__(kNnThreads) void bwd_grad_nn_kernel(const TIn* __restrict__ k,
                                                           const TIn* __restrict__ beta,
@@ -754,156 +797,166 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_nn_kernel(const TIn* __re
   float* B0 = sm;                // dP_tot, then X = dTi Ti^T
   float* B1 = B0 + CR * LS;      // M', then dA
   float* B2 = B1 + CR * LS;      // Ti
-  float* B3 = B2 + CR * LS;      // dTb_tot
+  float* B3 = B2 + CR * LS;      // dTb_tot, then A'
   float* B4 = B3 + CR * LS;      // dTi
   const int tid = threadIdx.x, wave = tid >> 6;
   const int l16 = lane16(), g4 = lane_g4();
-  const ChunkPos p = chunk_pos(blockIdx.x, T, H, nc);
-  const int64_t item = blockIdx.x;
   const int64_t rs = static_cast<int64_t>(H) * D;
-  const float* w = ws + item * L::WS;
-  const float* a1 = g1 + item * L::G1;
-  float* a2 = g2 + item * L::G2;
-  const TIn* kc = k + p.row0 * D;
   constexpr int CT = D / 16;
 
-  {
-    GTile<kNnThreads, CR, D> t_g, t_dq;
-    GTile<kNnThreads, CR, CR> t_p;
+  GTile<kNnThreads, CR, D> t_g, t_dq, t_dw;
+  GTile<kNnThreads, CR, CR> t_p, t_tb, t_m, t_ti, t_ap;
+  ITile4<kNnThreads, D, TIn> t_k;
+  f32x4_t y_dp[2], y_dtb[2];
+  float bt0;
+  auto load_x = [&](int it) {
+    const ChunkPos q = chunk_pos(it, T, H, nc);
+    const float* w = ws + static_cast<int64_t>(it) * L::WS;
+    const float* a1 = g1 + static_cast<int64_t>(it) * L::G1;
     t_g.load(w + L::G, D);
     t_dq.load(a1 + L::DQP, D);
-    t_p.load(w + L::PP, CR);
-    float bt0 = to_f32(beta[p.row0 + static_cast<int64_t>(min(tid & (CR - 1), p.nrow - 1)) * H]);
-    t_g.pin_all();
-    t_dq.pin_all();
-    t_p.pin_all();
-    pin(bt0);
-    t_g.store(Kg, LD);
-    t_dq.store(dQ, LD);
-    t_p.store(Ps, LS);
-    if (tid < CR) BT[tid] = tid < p.nrow ? bt0 : 0.f;
-  }
-  {
-    GTile<kNnThreads, CR, D> t_dw;
-    GTile<kNnThreads, CR, CR> t_tb;
     t_dw.load(a1 + L::DW, D);
+    t_p.load(w + L::PP, CR);
     t_tb.load(w + L::TB, CR);
-    t_dw.pin_all();
-    t_tb.pin_all();
-    t_dw.store(dW, LD);
-    t_tb.store(TBs, LS);
-  }
-  __syncthreads();
-  {   // Kg = k e^G in place of G (each element read and written by one thread)
-    ITile<kNnThreads, D, TIn> kt;
-    kt.load(kc, rs, p.nrow);
-    kt.pin_all();
+    t_k.load(k + q.row0 * D, rs, q.nrow);
+  };
+  auto load_y = [&](int it) {
+    const float* w = ws + static_cast<int64_t>(it) * L::WS;
+    const float* a1 = g1 + static_cast<int64_t>(it) * L::G1;
 #pragma unroll
-    for (int j = 0; j < kt.PER; ++j) {
-      const int e = tid + j * kNnThreads, t = e / D, i = e - t * D;
-      Kg[t * LD + i] = kt.r[j] * fexp(Kg[t * LD + i]);
+    for (int x = 0; x < 2; ++x) {
+      const int j = wave + 8 * x, rt = j >> 2, ct = j & 3;
+      y_dp[x] = get(a1 + L::DP + 16 * rt * CR + 16 * ct, CR);
+      y_dtb[x] = get(a1 + L::DTB + 16 * rt * CR + 16 * ct, CR);
     }
-  }
-  __syncthreads();
-
-  // dP_tot = dP - dQ' Kg^T and dTb_part = dTb + dW Kg^T (tiles wave + 8x)
-  f32x4_t dPt[2], dTt[2];
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int j = wave + 8 * x, rt = j >> 2, ct = j & 3;
-    const f32x4_t qk = mmx<BF, false, true>(zero4(), dQ + 16 * rt * LD, LD, Kg + 16 * ct * LD, LD, D);
-    const f32x4_t wk = mmx<BF, false, true>(zero4(), dW + 16 * rt * LD, LD, Kg + 16 * ct * LD, LD, D);
-    dPt[x] = get(a1 + L::DP + 16 * rt * CR + 16 * ct, CR);
-    dTt[x] = get(a1 + L::DTB + 16 * rt * CR + 16 * ct, CR);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      dPt[x][i] -= qk[i];
-      dTt[x][i] += wk[i];
-    }
-  }
-  // dKg = -P^T dQ' + Tb^T dW
-  for (int j = wave; j < 4 * CT; j += 8) {
-    const int rt = j / CT, ct = j - rt * CT;
-    const f32x4_t pq = mmx<BF, true, false>(zero4(), Ps + 16 * rt, LS, dQ + 16 * ct, LD, CR);
-    f32x4_t acc = mmx<BF, true, false>(zero4(), TBs + 16 * rt, LS, dW + 16 * ct, LD, CR);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] -= pq[i];
-    put(a2 + L::DKG + 16 * rt * D + 16 * ct, D, acc);
-  }
-  __syncthreads();
-
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int j = wave + 8 * x, rt = j >> 2, ct = j & 3;
-    put(B0 + 16 * rt * LS + 16 * ct, LS, dPt[x]);
-  }
-  {
-    GTile<kNnThreads, CR, CR> t_m, t_ti;
     t_m.load(w + L::MP, CR);
     t_ti.load(w + L::TI, CR);
+    t_ap.load(w + L::AP, CR);
+    const ChunkPos q = chunk_pos(it, T, H, nc);
+    bt0 = to_f32(beta[q.row0 + static_cast<int64_t>(min(tid & (CR - 1), q.nrow - 1)) * H]);
+  };
+
+  const int item = blockIdx.x;
+  const ChunkPos p = chunk_pos(item, T, H, nc);
+  float* a2 = g2 + static_cast<int64_t>(item) * L::G2;
+  load_x(item);
+  load_y(item);
+  {
+    t_g.pin_all();
+    t_dq.pin_all();
+    t_dw.pin_all();
+    t_p.pin_all();
+    t_tb.pin_all();
+    t_k.pin_all();
+    // Kg = k e^G (same element order in both tiles)
+#pragma unroll
+    for (int j = 0; j < t_g.PER; ++j) {
+      const f32x4_t kv = t_k.get(j, p.nrow);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t_g.r[j][i] = kv[i] * fexp(t_g.r[j][i]);
+    }
+    t_g.store(Kg, LD);
+    t_dq.store(dQ, LD);
+    t_dw.store(dW, LD);
+    t_p.store(Ps, LS);
+    t_tb.store(TBs, LS);
+    __syncthreads();
+
+    // dP_tot = dP - dQ' Kg^T and dTb_part = dTb + dW Kg^T (tiles wave + 8x)
+    f32x4_t dPt[2], dTt[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int j = wave + 8 * x, rt = j >> 2, ct = j & 3;
+      const f32x4_t qk = mmx<BF, false, true>(zero4(), dQ + 16 * rt * LD, LD, Kg + 16 * ct * LD, LD, D);
+      const f32x4_t wk = mmx<BF, false, true>(zero4(), dW + 16 * rt * LD, LD, Kg + 16 * ct * LD, LD, D);
+      dPt[x] = y_dp[x];
+      dTt[x] = y_dtb[x];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dPt[x][i] -= qk[i];
+        dTt[x][i] += wk[i];
+      }
+    }
+    // dKg = -P^T dQ' + Tb^T dW
+    for (int j = wave; j < 4 * CT; j += 8) {
+      const int rt = j / CT, ct = j - rt * CT;
+      const f32x4_t pq = mmx<BF, true, false>(zero4(), Ps + 16 * rt, LS, dQ + 16 * ct, LD, CR);
+      f32x4_t acc = mmx<BF, true, false>(zero4(), TBs + 16 * rt, LS, dW + 16 * ct, LD, CR);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] -= pq[i];
+      put(a2 + L::DKG + 16 * rt * D + 16 * ct, D, acc);
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int j = wave + 8 * x, rt = j >> 2, ct = j & 3;
+      put(B0 + 16 * rt * LS + 16 * ct, LS, dPt[x]);
+    }
     t_m.store(B1, LS);
     t_ti.store(B2, LS);
-  }
-  __syncthreads();
-  // dTb_tot = dTb_part + scale M'^T dP_tot;  dM' = scale (dP_tot Tb^T) on s <= t
+    if (tid < CR) BT[tid] = tid < p.nrow ? bt0 : 0.f;
+    __syncthreads();
+    // dTb_tot = dTb_part + scale M'^T dP_tot;  dM' = scale (dP_tot Tb^T) on s <= t
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int j = wave + 8 * x, rt = j >> 2, ct = j & 3;
-    const f32x4_t mp = mmx<BF, true, false>(zero4(), B1 + 16 * rt, LS, B0 + 16 * ct, LS, CR);
-    f32x4_t dm = mmx<BF, false, true>(zero4(), B0 + 16 * rt * LS, LS, TBs + 16 * ct * LS, LS, CR);
+    for (int x = 0; x < 2; ++x) {
+      const int j = wave + 8 * x, rt = j >> 2, ct = j & 3;
+      const f32x4_t mp = mmx<BF, true, false>(zero4(), B1 + 16 * rt, LS, B0 + 16 * ct, LS, CR);
+      f32x4_t dm = mmx<BF, false, true>(zero4(), B0 + 16 * rt * LS, LS, TBs + 16 * ct * LS, LS, CR);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 16 * rt + 4 * g4 + i, s = 16 * ct + l16;
-      dTt[x][i] += scale * mp[i];
-      dm[i] = s <= t ? scale * dm[i] : 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * rt + 4 * g4 + i, s = 16 * ct + l16;
+        dTt[x][i] += scale * mp[i];
+        dm[i] = s <= t ? scale * dm[i] : 0.f;
+      }
+      put(a2 + L::DMP + 16 * rt * CR + 16 * ct, CR, dm);
+      put(B3 + 16 * rt * LS + 16 * ct, LS, dTt[x]);
+      f32x4_t dti = dTt[x];
+      const float bc = BT[16 * ct + l16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dti[i] *= bc;
+      put(B4 + 16 * rt * LS + 16 * ct, LS, dti);
     }
-    put(a2 + L::DMP + 16 * rt * CR + 16 * ct, CR, dm);
-    put(B3 + 16 * rt * LS + 16 * ct, LS, dTt[x]);
-    f32x4_t dti = dTt[x];
-    const float bc = BT[16 * ct + l16];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dti[i] *= bc;
-    put(B4 + 16 * rt * LS + 16 * ct, LS, dti);
-  }
-  __syncthreads();
-  // dbeta_s (through Tb = Ti Diag(beta)) = sum_t Ti[t,s] dTb_tot[t,s]
-  float db = 0.f;
-  if (tid < CR) {
-    for (int t = 0; t < CR; ++t) db += B2[t * LS + tid] * B3[t * LS + tid];
-  }
-  f32x4_t X[2];   // X = dTi Ti^T
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int j = wave + 8 * x, rt = j >> 2, ct = j & 3;
-    X[x] = mmx<BF, false, true>(zero4(), B4 + 16 * rt * LS, LS, B2 + 16 * ct * LS, LS, CR);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int j = wave + 8 * x, rt = j >> 2, ct = j & 3;
-    put(B0 + 16 * rt * LS + 16 * ct, LS, X[x]);
-  }
-  __syncthreads();
-  // dA = -Ti^T X on s < t;  dA' = Diag(beta) dA
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int j = wave + 8 * x, rt = j >> 2, ct = j & 3;
-    f32x4_t da = mmx<BF, true, false>(zero4(), B2 + 16 * rt, LS, B0 + 16 * ct, LS, CR);
-    f32x4_t dap;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 16 * rt + 4 * g4 + i, s = 16 * ct + l16;
-      da[i] = s < t ? -da[i] : 0.f;
-      dap[i] = BT[t] * da[i];
+    __syncthreads();
+    // dbeta_s (through Tb = Ti Diag(beta)) = sum_t Ti[t,s] dTb_tot[t,s]
+    float db = 0.f;
+    if (tid < CR) {
+      for (int t = 0; t < CR; ++t) db += B2[t * LS + tid] * B3[t * LS + tid];
     }
-    put(B1 + 16 * rt * LS + 16 * ct, LS, da);
-    put(a2 + L::DAP + 16 * rt * CR + 16 * ct, CR, dap);
-  }
-  __syncthreads();
-  if (tid < p.nrow) {   // dbeta_t (through A = Diag(beta) A') += sum_s dA[t,s] A'[t,s]
-    const float* ap = w + L::AP + tid * CR;
-    for (int s = 0; s < CR; ++s) db += B1[tid * LS + s] * ap[s];
-    dbeta[p.row0 + static_cast<int64_t>(tid) * H] = Elem<TIn>::from(db);
+    f32x4_t X[2];   // X = dTi Ti^T
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int j = wave + 8 * x, rt = j >> 2, ct = j & 3;
+      X[x] = mmx<BF, false, true>(zero4(), B4 + 16 * rt * LS, LS, B2 + 16 * ct * LS, LS, CR);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int j = wave + 8 * x, rt = j >> 2, ct = j & 3;
+      put(B0 + 16 * rt * LS + 16 * ct, LS, X[x]);
+    }
+    t_ap.store(B3, LS);
+    __syncthreads();
+    // dA = -Ti^T X on s < t;  dA' = Diag(beta) dA
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int j = wave + 8 * x, rt = j >> 2, ct = j & 3;
+      f32x4_t da = mmx<BF, true, false>(zero4(), B2 + 16 * rt, LS, B0 + 16 * ct, LS, CR);
+      f32x4_t dap;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * rt + 4 * g4 + i, s = 16 * ct + l16;
+        da[i] = s < t ? -da[i] : 0.f;
+        dap[i] = BT[t] * da[i];
+      }
+      put(B1 + 16 * rt * LS + 16 * ct, LS, da);
+      put(a2 + L::DAP + 16 * rt * CR + 16 * ct, CR, dap);
+    }
+    __syncthreads();
+    if (tid < p.nrow) {   // dbeta_t (through A = Diag(beta) A') += sum_s dA[t,s] A'[t,s]
+      for (int s = 0; s < CR; ++s) db += B1[tid * LS + s] * B3[tid * LS + s];
+      dbeta[p.row0 + static_cast<int64_t>(tid) * H] = Elem<TIn>::from(db);
+    }
   }
 }
 
