@@ -185,8 +185,8 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, co
   if (static_cast<int64_t>(B) * T > INT32_MAX / 2) return KDA_ERR_SHAPE;
   if (static_cast<int64_t>(B) * H > (1 << 24)) return KDA_ERR_SHAPE;
   const uintptr_t elt = dtype == KDA_F32 ? 4 : 2;
-  rc = check_ptrs({{q, elt, true}, {k, elt, true}, {v, elt, true}, {g, elt, true},
-                   {beta, elt, true}, {grad_out, elt, true}, {grad_q, elt, true},
+  rc = check_ptrs({{q, elt, true}, {k, 16, true}, {v, 16, true}, {g, elt, true},
+                   {beta, elt, true}, {grad_out, 16, true}, {grad_q, elt, true},
                    {grad_k, elt, true}, {grad_v, elt, true}, {grad_g, elt, true},
                    {grad_beta, elt, true}, {initial_state, 4, false},
                    {grad_final_state, 4, false}, {grad_initial_state, 4, false}});

@@ -8,17 +8,17 @@
 //
 // With each chunk written as the affine map of kda_chunk_ops.h
 //     Delta = Tb V - W S,   O = Q' S + P V,   S_next = Lam S + Kt^T Delta,
-// the backward runs in six launches:
+// the backward runs in five launches:
 //   chunk_ops    per chunk: Tb, Ti, A', M', P, W, Q', Kt, G, Lam (fp32 workspace);
 //   bwd_fwd_scan per (sequence, head, 32 value columns): S at every chunk start
 //                and Delta, walking the chunks forwards;
 //   bwd_scan     the same grid walking backwards from dS_T:
 //                dU = Kt dS, dV = P^T dO + Tb^T dU, dS <- Lam dS + Q'^T dO - W^T dU;
-//   bwd_grad_dv  per chunk: the operand gradients, contractions over the value
-//                columns: dQ' = dO S^T, dW = -dU S^T, dKt = Delta dS^T,
-//                dLam = rowsum(S * dS), dP = dO V^T, dTb = dU V^T;
-//   bwd_grad_nn  per chunk: the 64 x 64 algebra through P, Q', W, Tb and the
-//                inverse (dP_tot, dKg, dTb_tot, dM', dA', dbeta);
+//   bwd_grad_chunk per chunk: the operand gradients, contractions over the value
+//                columns (dQ' = dO S^T, dW = -dU S^T, dKt = Delta dS^T,
+//                dLam = rowsum(S * dS), dP = dO V^T, dTb = dU V^T), then the
+//                64 x 64 algebra through P, Q', W, Tb and the inverse (dP_tot,
+//                dKg, dTb_tot, dM', dA', dbeta);
 //   bwd_grad_decay per chunk: the decayed products of dA' and dM' with k and q,
 //                and the chain to dq, dk and dg (a reverse running sum).
 // Products run on the matrix cores from LDS: fp32 16x16x4 for fp32 inputs; for
@@ -495,18 +495,30 @@ __global__ __launch_bounds__(kScanThreads) void bwd_scan_bf16_kernel(
 
 // ---------------------------------------------------------------- operand gradients
 
+// Tiles of the operand gradients: 16 x 16 tiles j = wave + 8x, x < NTW, of [dQ', -dW,
+// dKt] (64 x D each, NBIG tiles each) and then [dP, dTb] (64 x 64, 16 tiles each).
+// Wave w's tiles x = XP, XP + 1 are tiles w and w + 8 of dP; x = XP + 2, XP + 3 the
+// same tiles of dTb.  The first NBIG / 8 tiles (dQ') and the tiles from 2 NBIG / 8
+// (dKt) sit where the decayed-product stage wants them: tile j covers rows
+// 16 (j / CT) .., columns 16 (j % CT) ...
+template <int D>
+struct DvTiles {
+  static constexpr int CT = D / 16, NBIG = 4 * CT, NTOT = 3 * NBIG + 32, NTW = NTOT / 8;
+  static constexpr int XP = 3 * NBIG / 8;
+  static_assert(NTOT % 8 == 0 && (3 * NBIG) % 8 == 0, "tile split");
+};
+
+// fp32 per-chunk states: the contractions over the value columns, in 32-column
+// slices staged through LDS (2 D + 4 * 64 rows of LV floats); dlam (threads < D) =
+// rowsum(S * dS_next).  Ends with a barrier: LDS is free afterwards.
 template <int D, typename TIn>
-__global__ __launch_bounds__(512) void bwd_grad_dv_kernel(const TIn* __restrict__ v,
-                                                          const TIn* __restrict__ dout,
-                                                          const float* __restrict__ st,
-                                                          const float* __restrict__ dst,
-                                                          const float* __restrict__ dl,
-                                                          const float* __restrict__ du,
-                                                          float* __restrict__ g1, int T, int H,
-                                                          int nc) {
+__device__ __forceinline__ void dv_accumulate(float* sm, const TIn* v, const TIn* dout, const float* st,
+                                              const float* dst, const float* dl, const float* du,
+                                              int64_t item, const ChunkPos& p, int64_t rs,
+                                              f32x4_t (&acc)[DvTiles<D>::NTW], float& dlam) {
   constexpr bool BF = IsBf16<TIn>::value;   // bf16 matrix-core operands for bf16 inputs
-  using L = BwdLayout<D>;
-  __shared__ __attribute__((aligned(16))) float sm[2 * D * LV + 4 * CR * LV];
+  using DT = DvTiles<D>;
+  constexpr int CT = DT::CT, NBIG = DT::NBIG, NTW = DT::NTW;
   float* Ss = sm;
   float* dSs = Ss + D * LV;
   float* dOs = dSs + D * LV;
@@ -514,18 +526,9 @@ __global__ __launch_bounds__(512) void bwd_grad_dv_kernel(const TIn* __restrict_
   float* Dls = dUs + CR * LV;
   float* Vs = Dls + CR * LV;
   const int tid = threadIdx.x, wave = tid >> 6;
-  const ChunkPos p = chunk_pos(blockIdx.x, T, H, nc);
-  const int64_t item = blockIdx.x;
-  const int64_t rs = static_cast<int64_t>(H) * D;
-  constexpr int CT = D / 16;
-  constexpr int NBIG = 4 * CT;                     // tiles of a 64 x D matrix
-  constexpr int NTOT = 3 * NBIG + 32, NTW = NTOT / 8;
-  static_assert(NTOT % 8 == 0, "tile split");
-
-  f32x4_t acc[NTW];
 #pragma unroll
   for (int x = 0; x < NTW; ++x) acc[x] = zero4();
-  float dlam = 0.f;
+  dlam = 0.f;
   for (int c0 = 0; c0 < D; c0 += SL) {
     {
       GTile<512, D, SL> t_s, t_ds;
@@ -571,24 +574,6 @@ __global__ __launch_bounds__(512) void bwd_grad_dv_kernel(const TIn* __restrict_
     }
     __syncthreads();
   }
-  float* o = g1 + item * L::G1;
-#pragma unroll
-  for (int x = 0; x < NTW; ++x) {
-    const int j = wave + 8 * x;
-    if (j < 3 * NBIG) {
-      const int m = j / NBIG, r = j - m * NBIG, rt = r / CT, ct = r - rt * CT;
-      f32x4_t vv = acc[x];
-      if (m == 1) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vv[i] = -vv[i];
-      }
-      put(o + m * CR * D + 16 * rt * D + 16 * ct, D, vv);
-    } else {
-      const int j2 = j - 3 * NBIG, m = j2 >> 4, rt = (j2 & 15) >> 2, ct = j2 & 3;
-      put(o + (m == 0 ? L::DP : L::DTB) + 16 * rt * CR + 16 * ct, CR, acc[x]);
-    }
-  }
-  if (tid < D) o[L::DLAM + tid] = dlam;
 }
 
 // bf16 inputs: the same contractions from bf16 per-chunk states (S, dS_next),
@@ -631,14 +616,16 @@ struct BTileS {   // ROWS x COLS bf16 slice of a matrix with row stride gld
   }
 };
 
+constexpr int LVB = SL + 8;   // bf16 leading dimension of the 32-column slices
+
 template <int D>
-__global__ __launch_bounds__(512) void bwd_grad_dv_bf16_kernel(
-    const bf16_t* __restrict__ v, const bf16_t* __restrict__ dout, const __bf16* __restrict__ st,
-    const __bf16* __restrict__ dst, const __bf16* __restrict__ dl, const __bf16* __restrict__ du,
-    float* __restrict__ g1, int T, int H, int nc) {
-  using L = BwdLayout<D>;
-  constexpr int LVB = SL + 8;   // bf16 leading dimension of the 32-column slices
-  __shared__ __attribute__((aligned(16))) __bf16 sm[2 * D * LVB + 4 * CR * LVB];
+__device__ __forceinline__ void dv_accumulate_bf16(__bf16* sm, const bf16_t* v, const bf16_t* dout,
+                                                   const __bf16* st, const __bf16* dst,
+                                                   const __bf16* dl, const __bf16* du, int64_t item,
+                                                   const ChunkPos& p, int64_t rs,
+                                                   f32x4_t (&acc)[DvTiles<D>::NTW], float& dlam) {
+  using DT = DvTiles<D>;
+  constexpr int CT = DT::CT, NBIG = DT::NBIG, NTW = DT::NTW;
   __bf16* Ss = sm;
   __bf16* dSs = Ss + D * LVB;
   __bf16* dOs = dSs + D * LVB;
@@ -646,18 +633,9 @@ __global__ __launch_bounds__(512) void bwd_grad_dv_bf16_kernel(
   __bf16* Dls = dUs + CR * LVB;
   __bf16* Vs = Dls + CR * LVB;
   const int tid = threadIdx.x, wave = tid >> 6;
-  const ChunkPos p = chunk_pos(blockIdx.x, T, H, nc);
-  const int64_t item = blockIdx.x;
-  const int64_t rs = static_cast<int64_t>(H) * D;
-  constexpr int CT = D / 16;
-  constexpr int NBIG = 4 * CT;
-  constexpr int NTOT = 3 * NBIG + 32, NTW = NTOT / 8;
-  static_assert(NTOT % 8 == 0, "tile split");
-
-  f32x4_t acc[NTW];
 #pragma unroll
   for (int x = 0; x < NTW; ++x) acc[x] = zero4();
-  float dlam = 0.f;
+  dlam = 0.f;
   for (int c0 = 0; c0 < D; c0 += SL) {
     {
       BTileS<512, D, SL> t_s, t_ds;
@@ -702,24 +680,6 @@ __global__ __launch_bounds__(512) void bwd_grad_dv_bf16_kernel(
     }
     __syncthreads();
   }
-  float* o = g1 + item * L::G1;
-#pragma unroll
-  for (int x = 0; x < NTW; ++x) {
-    const int j = wave + 8 * x;
-    if (j < 3 * NBIG) {
-      const int m = j / NBIG, r = j - m * NBIG, rt = r / CT, ct = r - rt * CT;
-      f32x4_t vv = acc[x];
-      if (m == 1) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vv[i] = -vv[i];
-      }
-      put(o + m * CR * D + 16 * rt * D + 16 * ct, D, vv);
-    } else {
-      const int j2 = j - 3 * NBIG, m = j2 >> 4, rt = (j2 & 15) >> 2, ct = j2 & 3;
-      put(o + (m == 0 ? L::DP : L::DTB) + 16 * rt * CR + 16 * ct, CR, acc[x]);
-    }
-  }
-  if (tid < D) o[L::DLAM + tid] = dlam;
 }
 
 // ---------------------------------------------------------------- 64 x 64 algebra
@@ -732,6 +692,8 @@ struct NnLds {
   static constexpr int A = 3 * CR * LD + CR * LS, B = 5 * CR * LS;
   static constexpr int FRONT = A > B ? A : B;      // phase A: Kg, dQ', dW, P; phase B: 5 matrices
   static constexpr int TOTAL = FRONT + CR * LS + CR;
+  // the operand-gradient stage runs first in the same memory
+  static_assert(TOTAL >= (2 * D + 4 * CR) * LV, "operand-gradient slices fit");
 };
 
 // 64 x COLS input rows (bf16 or fp32) held as raw words, 4 consecutive elements per
@@ -768,22 +730,28 @@ struct ITile4 {
   }
 };
 
-// One workgroup per (chunk, head).  Every global load of the item is issued at the
-// top in two register sets: X (G, dQ', dW, P, Tb, k), written to LDS at once, and
-// Y (dP, dTb, M', Ti, A', beta), used by the later phases.  Vector-memory counters
-// retire in order, so the first use of Y waits only for Y, whose latency hides
-// behind the phase-A products instead of stalling each phase in turn.
+// Element type of the per-chunk states, Delta and dU the scans store.
+template <typename TIn>
+using StateElem = typename std::conditional<IsBf16<TIn>::value, __bf16, float>::type;
+
+// One workgroup per (chunk, head): the operand gradients (contractions over the
+// value columns) and then the 64 x 64 algebra, in one pass, so dW, dP and dTb never
+// leave the workgroup.  dQ', dKt and dLam go to the workspace for the decayed
+// products.  The algebra's inputs are loaded at the top in two register sets: X (G,
+// P, Tb, k), written to LDS right after the contractions, and Y (M', Ti, A', beta),
+// used by the later phases; vector-memory counters retire in order, so the first
+// use of Y waits only for Y, and both groups' latency hides behind the contractions.
 template <int D, typename TIn>
-__global__ __launch_bounds__(kNnThreads) void bwd_grad_nn_kernel(const TIn* __restrict__ k,
-                                                          const TIn* __restrict__ beta,
-                                                          const float* __restrict__ ws,
-                                                          const float* __restrict__ g1,
-                                                          float* __restrict__ g2,
-                                                          TIn* __restrict__ dbeta, int T, int H,
-                                                          int nc, float scale) {
+__global__ __launch_bounds__(kNnThreads) void bwd_grad_chunk_kernel(
+    const TIn* __restrict__ k, const TIn* __restrict__ beta, const TIn* __restrict__ v,
+    const TIn* __restrict__ dout, const StateElem<TIn>* __restrict__ st,
+    const StateElem<TIn>* __restrict__ dst, const StateElem<TIn>* __restrict__ dl,
+    const StateElem<TIn>* __restrict__ du, const float* __restrict__ ws, float* __restrict__ g1,
+    float* __restrict__ g2, TIn* __restrict__ dbeta, int T, int H, int nc, float scale) {
   constexpr bool BF = IsBf16<TIn>::value;   // bf16 matrix-core operands for bf16 inputs
   using L = BwdLayout<D>;
   using NL = NnLds<D>;
+  using DT = DvTiles<D>;
   constexpr int LD = L::LD;
   __shared__ __attribute__((aligned(16))) float sm[NL::TOTAL];
   // phase A
@@ -803,48 +771,52 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_nn_kernel(const TIn* __re
   const int l16 = lane16(), g4 = lane_g4();
   const int64_t rs = static_cast<int64_t>(H) * D;
   constexpr int CT = D / 16;
+  const int64_t item = blockIdx.x;
+  const ChunkPos p = chunk_pos(blockIdx.x, T, H, nc);
+  const float* w = ws + item * L::WS;
+  float* a1 = g1 + item * L::G1;
+  float* a2 = g2 + item * L::G2;
 
-  GTile<kNnThreads, CR, D> t_g, t_dq, t_dw;
+  GTile<kNnThreads, CR, D> t_g;
   GTile<kNnThreads, CR, CR> t_p, t_tb, t_m, t_ti, t_ap;
   ITile4<kNnThreads, D, TIn> t_k;
-  f32x4_t y_dp[2], y_dtb[2];
-  float bt0;
-  auto load_x = [&](int it) {
-    const ChunkPos q = chunk_pos(it, T, H, nc);
-    const float* w = ws + static_cast<int64_t>(it) * L::WS;
-    const float* a1 = g1 + static_cast<int64_t>(it) * L::G1;
-    t_g.load(w + L::G, D);
-    t_dq.load(a1 + L::DQP, D);
-    t_dw.load(a1 + L::DW, D);
-    t_p.load(w + L::PP, CR);
-    t_tb.load(w + L::TB, CR);
-    t_k.load(k + q.row0 * D, rs, q.nrow);
-  };
-  auto load_y = [&](int it) {
-    const float* w = ws + static_cast<int64_t>(it) * L::WS;
-    const float* a1 = g1 + static_cast<int64_t>(it) * L::G1;
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int j = wave + 8 * x, rt = j >> 2, ct = j & 3;
-      y_dp[x] = get(a1 + L::DP + 16 * rt * CR + 16 * ct, CR);
-      y_dtb[x] = get(a1 + L::DTB + 16 * rt * CR + 16 * ct, CR);
-    }
-    t_m.load(w + L::MP, CR);
-    t_ti.load(w + L::TI, CR);
-    t_ap.load(w + L::AP, CR);
-    const ChunkPos q = chunk_pos(it, T, H, nc);
-    bt0 = to_f32(beta[q.row0 + static_cast<int64_t>(min(tid & (CR - 1), q.nrow - 1)) * H]);
-  };
+  t_g.load(w + L::G, D);
+  t_p.load(w + L::PP, CR);
+  t_tb.load(w + L::TB, CR);
+  t_k.load(k + p.row0 * D, rs, p.nrow);
+  t_m.load(w + L::MP, CR);
+  t_ti.load(w + L::TI, CR);
+  t_ap.load(w + L::AP, CR);
+  const float bt0 = to_f32(beta[p.row0 + static_cast<int64_t>(min(tid & (CR - 1), p.nrow - 1)) * H]);
 
-  const int item = blockIdx.x;
-  const ChunkPos p = chunk_pos(item, T, H, nc);
-  float* a2 = g2 + static_cast<int64_t>(item) * L::G2;
-  load_x(item);
-  load_y(item);
+  f32x4_t acc[DT::NTW];
+  float dlam;
+  if constexpr (BF)
+    dv_accumulate_bf16<D>(reinterpret_cast<__bf16*>(sm), v, dout, st, dst, dl, du, item, p, rs, acc, dlam);
+  else
+    dv_accumulate<D, TIn>(sm, v, dout, st, dst, dl, du, item, p, rs, acc, dlam);
+
+  // dQ' to the workspace and LDS, dW to LDS, dKt and dLam to the workspace
+#pragma unroll
+  for (int x = 0; x < DT::XP; ++x) {
+    const int j = wave + 8 * x;
+    const int m = j / DT::NBIG, r = j - m * DT::NBIG, rt = r / CT, ct = r - rt * CT;
+    if (m == 0) {
+      put(a1 + L::DQP + 16 * rt * D + 16 * ct, D, acc[x]);
+      put(dQ + 16 * rt * LD + 16 * ct, LD, acc[x]);
+    } else if (m == 1) {
+      f32x4_t vv = acc[x];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vv[i] = -vv[i];
+      put(dW + 16 * rt * LD + 16 * ct, LD, vv);
+    } else {
+      put(a1 + L::DKT + 16 * rt * D + 16 * ct, D, acc[x]);
+    }
+  }
+  if (tid < D) a1[L::DLAM + tid] = dlam;
+
   {
     t_g.pin_all();
-    t_dq.pin_all();
-    t_dw.pin_all();
     t_p.pin_all();
     t_tb.pin_all();
     t_k.pin_all();
@@ -856,8 +828,6 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_nn_kernel(const TIn* __re
       for (int i = 0; i < 4; ++i) t_g.r[j][i] = kv[i] * fexp(t_g.r[j][i]);
     }
     t_g.store(Kg, LD);
-    t_dq.store(dQ, LD);
-    t_dw.store(dW, LD);
     t_p.store(Ps, LS);
     t_tb.store(TBs, LS);
     __syncthreads();
@@ -869,8 +839,8 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_nn_kernel(const TIn* __re
       const int j = wave + 8 * x, rt = j >> 2, ct = j & 3;
       const f32x4_t qk = mmx<BF, false, true>(zero4(), dQ + 16 * rt * LD, LD, Kg + 16 * ct * LD, LD, D);
       const f32x4_t wk = mmx<BF, false, true>(zero4(), dW + 16 * rt * LD, LD, Kg + 16 * ct * LD, LD, D);
-      dPt[x] = y_dp[x];
-      dTt[x] = y_dtb[x];
+      dPt[x] = acc[DT::XP + x];
+      dTt[x] = acc[DT::XP + 2 + x];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         dPt[x][i] -= qk[i];
@@ -881,10 +851,10 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_nn_kernel(const TIn* __re
     for (int j = wave; j < 4 * CT; j += 8) {
       const int rt = j / CT, ct = j - rt * CT;
       const f32x4_t pq = mmx<BF, true, false>(zero4(), Ps + 16 * rt, LS, dQ + 16 * ct, LD, CR);
-      f32x4_t acc = mmx<BF, true, false>(zero4(), TBs + 16 * rt, LS, dW + 16 * ct, LD, CR);
+      f32x4_t kg = mmx<BF, true, false>(zero4(), TBs + 16 * rt, LS, dW + 16 * ct, LD, CR);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] -= pq[i];
-      put(a2 + L::DKG + 16 * rt * D + 16 * ct, D, acc);
+      for (int i = 0; i < 4; ++i) kg[i] -= pq[i];
+      put(a2 + L::DKG + 16 * rt * D + 16 * ct, D, kg);
     }
     __syncthreads();
 
@@ -1186,19 +1156,19 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
     hipLaunchKernelGGL((bwd_scan_bf16_kernel<D>), dim3(scan_blocks), dim3(kScanThreads), 0,
                        a.stream, dout, a.d_final_state, ws, wsb, dstb, dub,
                        static_cast<TIn*>(a.dv), a.d_initial_state, a.T, a.H, nc, BH);
-    hipLaunchKernelGGL((bwd_grad_dv_bf16_kernel<D>), dim3(items), dim3(512), 0, a.stream, v, dout,
-                       stb, dstb, dlb, dub, g1, a.T, a.H, nc);
+    hipLaunchKernelGGL((bwd_grad_chunk_kernel<D, TIn>), dim3(items), dim3(kNnThreads), 0, a.stream, k,
+                       beta, v, dout, stb, dstb, dlb, dub, ws, g1, g2, static_cast<TIn*>(a.dbeta),
+                       a.T, a.H, nc, a.scale);
   } else {
     hipLaunchKernelGGL((bwd_fwd_scan_kernel<D, TIn>), dim3(scan_blocks), dim3(kScanThreads), 0, a.stream, v,
                        a.initial_state, ws, st, dl, a.T, a.H, nc, BH);
     hipLaunchKernelGGL((bwd_scan_kernel<D, TIn>), dim3(scan_blocks), dim3(kScanThreads), 0, a.stream, dout,
                        a.d_final_state, ws, dst, du, static_cast<TIn*>(a.dv), a.d_initial_state,
                        a.T, a.H, nc, BH);
-    hipLaunchKernelGGL((bwd_grad_dv_kernel<D, TIn>), dim3(items), dim3(512), 0, a.stream, v, dout,
-                       st, dst, dl, du, g1, a.T, a.H, nc);
+    hipLaunchKernelGGL((bwd_grad_chunk_kernel<D, TIn>), dim3(items), dim3(kNnThreads), 0, a.stream, k,
+                       beta, v, dout, st, dst, dl, du, ws, g1, g2, static_cast<TIn*>(a.dbeta), a.T,
+                       a.H, nc, a.scale);
   }
-  hipLaunchKernelGGL((bwd_grad_nn_kernel<D, TIn>), dim3(items), dim3(kNnThreads), 0, a.stream, k, beta,
-                     ws, g1, g2, static_cast<TIn*>(a.dbeta), a.T, a.H, nc, a.scale);
   hipLaunchKernelGGL((bwd_grad_decay_kernel<D, TIn>), dim3(items), dim3(512), 0, a.stream, q, k,
                      ws, g1, g2, static_cast<TIn*>(a.dq), static_cast<TIn*>(a.dk),
                      static_cast<TIn*>(a.dg), a.T, a.H, nc, a.scale);

@@ -176,14 +176,18 @@ int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void
  *  grad_q, grad_k, grad_g [B, T, H, dk]; grad_v [B, T, H, dv]; grad_beta [B, T, H]
  *                      (dtype), required, fully overwritten.
  *  grad_initial_state  [B, H, dk, dv] fp32 or NULL (not computed).
- * dk == dv in {64, 128} for both dtypes.  Every pointer needs only its element
- * alignment.  The forward is recomputed inside the call (nothing is kept from
- * kda_chunk_fwd).  All arithmetic is fp32 (fp32 matrix cores), also for bf16
- * inputs.  The call allocates a workspace with hipMallocAsync on `stream` and
- * frees it on the same stream, per 64-token chunk per head: 615,424 bytes for
- * bf16 and 607,232 for fp32 at d = 128 (377,344 and 344,576 at d = 64), so
- * T = 65,536 with 32 heads needs about 20 GB; an allocation failure returns
- * KDA_ERR_HIP.
+ * dk == dv in {64, 128} for both dtypes.  k, v and grad_out are read up to 16
+ * bytes at a time and must be 16-byte aligned; every other pointer needs only
+ * its element alignment (else KDA_ERR_ALIGN).  The forward is recomputed inside
+ * the call (nothing is kept from kda_chunk_fwd).  fp32 inputs: fp32 throughout
+ * (fp32 matrix cores).  bf16 inputs: every product over 32 or more terms takes
+ * bf16 operands rounded from fp32 values, with fp32 accumulation, and the
+ * per-chunk states, state gradients, Delta and dU are kept as bf16; the inverse,
+ * the 16-term sub-tile products and the decayed products stay fp32.  The call
+ * allocates a workspace with hipMallocAsync on `stream` and frees it on the same
+ * stream, per 64-token chunk per head: 549,888 bytes for bf16 and 541,696 for
+ * fp32 at d = 128 (328,192 and 295,424 at d = 64), so T = 65,536 with 32 heads
+ * needs about 18 GB; an allocation failure returns KDA_ERR_HIP.
  * Outputs must not alias inputs.
  */
 int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
