@@ -8,21 +8,22 @@
 //
 // With each chunk written as the affine map of kda_chunk_ops.h
 //     Delta = Tb V - W S,   O = Q' S + P V,   S_next = Lam S + Kt^T Delta,
-// the backward runs in five launches:
+// the backward runs in four launches:
 //   chunk_ops    per chunk: Tb, Ti, A', M', P, W, Q', Kt, G, Lam (fp32 workspace);
 //   bwd_fwd_scan per (sequence, head, 32 value columns): S at every chunk start
 //                and Delta, walking the chunks forwards;
 //   bwd_scan     the same grid walking backwards from dS_T:
 //                dU = Kt dS, dV = P^T dO + Tb^T dU, dS <- Lam dS + Q'^T dO - W^T dU;
-//   bwd_grad_chunk per chunk: the operand gradients, contractions over the value
-//                columns (dQ' = dO S^T, dW = -dU S^T, dKt = Delta dS^T,
-//                dLam = rowsum(S * dS), dP = dO V^T, dTb = dU V^T), then the
-//                64 x 64 algebra through P, Q', W, Tb and the inverse (dP_tot,
-//                dKg, dTb_tot, dM', dA', dbeta);
-//   bwd_grad_decay per chunk: the decayed products of dA' and dM' with k and q,
-//                and the chain to dq, dk and dg (a reverse running sum).
+//   bwd_grad_chunk per chunk, three stages in one workgroup: the operand
+//                gradients, contractions over the value columns (dQ' = dO S^T,
+//                dW = -dU S^T, dKt = Delta dS^T, dLam = rowsum(S * dS),
+//                dP = dO V^T, dTb = dU V^T); the 64 x 64 algebra through P, Q', W,
+//                Tb and the inverse (dP_tot, dKg, dTb_tot, dM', dA', dbeta); the
+//                decayed products of dA' and dM' with k and q, and the chain to
+//                dq, dk and dg (a reverse running sum).  The operand gradients
+//                never leave the workgroup.
 // Products run on the matrix cores from LDS: fp32 16x16x4 for fp32 inputs; for
-// bf16 inputs the scans and the operand-gradient and 64 x 64 kernels use bf16
+// bf16 inputs the scans, the operand gradients and the 64 x 64 algebra use bf16
 // operands (16x16x32) with fp32 accumulation, and the decayed products stay fp32.
 
 #include <type_traits>
@@ -692,8 +693,25 @@ struct NnLds {
   static constexpr int A = 3 * CR * LD + CR * LS, B = 5 * CR * LS;
   static constexpr int FRONT = A > B ? A : B;      // phase A: Kg, dQ', dW, P; phase B: 5 matrices
   static constexpr int TOTAL = FRONT + CR * LS + CR;
-  // the operand-gradient stage runs first in the same memory
+};
+
+// LDS of bwd_grad_chunk: the operand-gradient slices first, then the algebra
+// (NnLds), then the decayed products: k colf, k rowf, q rowf in the first
+// 3 * 64 * LD floats, dA' and dM' (written by the algebra's last phases, where
+// nothing live sits then: dM' over Tb, dA' over P, or past the algebra's region),
+// then G at the sub-tile ends and the pair factors.
+template <int D>
+struct ChunkLds {
+  using NL = NnLds<D>;
+  static constexpr int KQ = 3 * CR * (D + 4);
+  static constexpr bool DA_IN_FRONT = KQ >= 4 * CR * LS && KQ + CR * LS <= NL::FRONT;
+  static constexpr int DAS = DA_IN_FRONT ? KQ : NL::TOTAL;
+  static constexpr int DMS = NL::FRONT;
+  static constexpr int RF = NL::TOTAL > DAS + CR * LS ? NL::TOTAL : DAS + CR * LS;
+  static constexpr int TOTAL = RF + 10 * D;
+  static_assert(KQ <= DMS && KQ <= DAS, "decay operands below dA', dM'");
   static_assert(TOTAL >= (2 * D + 4 * CR) * LV, "operand-gradient slices fit");
+  static_assert(TOTAL * 4 <= 160 * 1024, "LDS budget");
 };
 
 // 64 x COLS input rows (bf16 or fp32) held as raw words, 4 consecutive elements per
@@ -735,25 +753,28 @@ template <typename TIn>
 using StateElem = typename std::conditional<IsBf16<TIn>::value, __bf16, float>::type;
 
 // One workgroup per (chunk, head): the operand gradients (contractions over the
-// value columns) and then the 64 x 64 algebra, in one pass, so dW, dP and dTb never
-// leave the workgroup.  dQ', dKt and dLam go to the workspace for the decayed
-// products.  The algebra's inputs are loaded at the top in two register sets: X (G,
-// P, Tb, k), written to LDS right after the contractions, and Y (M', Ti, A', beta),
-// used by the later phases; vector-memory counters retire in order, so the first
-// use of Y waits only for Y, and both groups' latency hides behind the contractions.
+// value columns), the 64 x 64 algebra and the decayed products, in one pass, so no
+// operand gradient leaves the workgroup: dQ', dKt and dKg stay in registers in the
+// accumulator tiles the last stage needs, dA' and dM' in LDS.  The algebra's inputs
+// are loaded at the top in two register sets: X (G, P, Tb, k), written to LDS
+// right after the contractions, and Y (M', Ti, A', beta), used by the later phases;
+// vector-memory counters retire in order, so the first use of Y waits only for Y,
+// and both groups' latency hides behind the contractions.
 template <int D, typename TIn>
 __global__ __launch_bounds__(kNnThreads) void bwd_grad_chunk_kernel(
-    const TIn* __restrict__ k, const TIn* __restrict__ beta, const TIn* __restrict__ v,
-    const TIn* __restrict__ dout, const StateElem<TIn>* __restrict__ st,
+    const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ beta,
+    const TIn* __restrict__ v, const TIn* __restrict__ dout, const StateElem<TIn>* __restrict__ st,
     const StateElem<TIn>* __restrict__ dst, const StateElem<TIn>* __restrict__ dl,
-    const StateElem<TIn>* __restrict__ du, const float* __restrict__ ws, float* __restrict__ g1,
-    float* __restrict__ g2, TIn* __restrict__ dbeta, int T, int H, int nc, float scale) {
+    const StateElem<TIn>* __restrict__ du, const float* __restrict__ ws, TIn* __restrict__ dq,
+    TIn* __restrict__ dk, TIn* __restrict__ dg, TIn* __restrict__ dbeta, int T, int H, int nc,
+    float scale) {
   constexpr bool BF = IsBf16<TIn>::value;   // bf16 matrix-core operands for bf16 inputs
   using L = BwdLayout<D>;
   using NL = NnLds<D>;
+  using CL = ChunkLds<D>;
   using DT = DvTiles<D>;
   constexpr int LD = L::LD;
-  __shared__ __attribute__((aligned(16))) float sm[NL::TOTAL];
+  __shared__ __attribute__((aligned(16))) float sm[CL::TOTAL];
   // phase A
   float* Kg = sm;
   float* dQ = Kg + CR * LD;
@@ -767,6 +788,14 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_chunk_kernel(
   float* B2 = B1 + CR * LS;      // Ti
   float* B3 = B2 + CR * LS;      // dTb_tot, then A'
   float* B4 = B3 + CR * LS;      // dTi
+  // decayed products
+  float* Ki = sm;                // k e^{R - G}  (column side)
+  float* Ko = Ki + CR * LD;      // k e^{G - R}  (row side), later dG
+  float* Qo = Ko + CR * LD;      // q e^{G - R}  (row side), later dKt Kt
+  float* dAs = sm + CL::DAS;     // dA', written by the algebra
+  float* dMs = sm + CL::DMS;     // dM', written by the algebra
+  float* Rf = sm + CL::RF;       // [4][D] G at each sub-tile's last row
+  float* FP = Rf + 4 * D;        // [6][D] e^{R_I - R_J}
   const int tid = threadIdx.x, wave = tid >> 6;
   const int l16 = lane16(), g4 = lane_g4();
   const int64_t rs = static_cast<int64_t>(H) * D;
@@ -774,8 +803,6 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_chunk_kernel(
   const int64_t item = blockIdx.x;
   const ChunkPos p = chunk_pos(blockIdx.x, T, H, nc);
   const float* w = ws + item * L::WS;
-  float* a1 = g1 + item * L::G1;
-  float* a2 = g2 + item * L::G2;
 
   GTile<kNnThreads, CR, D> t_g;
   GTile<kNnThreads, CR, CR> t_p, t_tb, t_m, t_ti, t_ap;
@@ -796,24 +823,20 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_chunk_kernel(
   else
     dv_accumulate<D, TIn>(sm, v, dout, st, dst, dl, du, item, p, rs, acc, dlam);
 
-  // dQ' to the workspace and LDS, dW to LDS, dKt and dLam to the workspace
+  // dQ' and dW to LDS; dQ' and dKt also stay in registers for the decayed products
 #pragma unroll
-  for (int x = 0; x < DT::XP; ++x) {
+  for (int x = 0; x < 2 * DT::NBIG / 8; ++x) {
     const int j = wave + 8 * x;
     const int m = j / DT::NBIG, r = j - m * DT::NBIG, rt = r / CT, ct = r - rt * CT;
     if (m == 0) {
-      put(a1 + L::DQP + 16 * rt * D + 16 * ct, D, acc[x]);
       put(dQ + 16 * rt * LD + 16 * ct, LD, acc[x]);
-    } else if (m == 1) {
+    } else {
       f32x4_t vv = acc[x];
 #pragma unroll
       for (int i = 0; i < 4; ++i) vv[i] = -vv[i];
       put(dW + 16 * rt * LD + 16 * ct, LD, vv);
-    } else {
-      put(a1 + L::DKT + 16 * rt * D + 16 * ct, D, acc[x]);
     }
   }
-  if (tid < D) a1[L::DLAM + tid] = dlam;
 
   {
     t_g.pin_all();
@@ -847,14 +870,15 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_chunk_kernel(
         dTt[x][i] += wk[i];
       }
     }
-    // dKg = -P^T dQ' + Tb^T dW
-    for (int j = wave; j < 4 * CT; j += 8) {
-      const int rt = j / CT, ct = j - rt * CT;
-      const f32x4_t pq = mmx<BF, true, false>(zero4(), Ps + 16 * rt, LS, dQ + 16 * ct, LD, CR);
-      f32x4_t kg = mmx<BF, true, false>(zero4(), TBs + 16 * rt, LS, dW + 16 * ct, LD, CR);
+    // dKg = -P^T dQ' + Tb^T dW, kept in registers for the decayed-product stage
+    f32x4_t dkg[DT::NBIG / 8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kg[i] -= pq[i];
-      put(a2 + L::DKG + 16 * rt * D + 16 * ct, D, kg);
+    for (int x = 0; x < DT::NBIG / 8; ++x) {
+      const int j = wave + 8 * x, rt = j / CT, ct = j - rt * CT;
+      const f32x4_t pq = mmx<BF, true, false>(zero4(), Ps + 16 * rt, LS, dQ + 16 * ct, LD, CR);
+      dkg[x] = mmx<BF, true, false>(zero4(), TBs + 16 * rt, LS, dW + 16 * ct, LD, CR);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dkg[x][i] -= pq[i];
     }
     __syncthreads();
 
@@ -868,18 +892,18 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_chunk_kernel(
     if (tid < CR) BT[tid] = tid < p.nrow ? bt0 : 0.f;
     __syncthreads();
     // dTb_tot = dTb_part + scale M'^T dP_tot;  dM' = scale (dP_tot Tb^T) on s <= t
+    f32x4_t dmv[2];
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       const int j = wave + 8 * x, rt = j >> 2, ct = j & 3;
       const f32x4_t mp = mmx<BF, true, false>(zero4(), B1 + 16 * rt, LS, B0 + 16 * ct, LS, CR);
-      f32x4_t dm = mmx<BF, false, true>(zero4(), B0 + 16 * rt * LS, LS, TBs + 16 * ct * LS, LS, CR);
+      dmv[x] = mmx<BF, false, true>(zero4(), B0 + 16 * rt * LS, LS, TBs + 16 * ct * LS, LS, CR);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 16 * rt + 4 * g4 + i, s = 16 * ct + l16;
         dTt[x][i] += scale * mp[i];
-        dm[i] = s <= t ? scale * dm[i] : 0.f;
+        dmv[x][i] = s <= t ? scale * dmv[x][i] : 0.f;
       }
-      put(a2 + L::DMP + 16 * rt * CR + 16 * ct, CR, dm);
       put(B3 + 16 * rt * LS + 16 * ct, LS, dTt[x]);
       f32x4_t dti = dTt[x];
       const float bc = BT[16 * ct + l16];
@@ -904,6 +928,7 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_chunk_kernel(
     for (int x = 0; x < 2; ++x) {
       const int j = wave + 8 * x, rt = j >> 2, ct = j & 3;
       put(B0 + 16 * rt * LS + 16 * ct, LS, X[x]);
+      put(dMs + 16 * rt * LS + 16 * ct, LS, dmv[x]);   // Tb is no longer read
     }
     t_ap.store(B3, LS);
     __syncthreads();
@@ -920,194 +945,155 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_chunk_kernel(
         dap[i] = BT[t] * da[i];
       }
       put(B1 + 16 * rt * LS + 16 * ct, LS, da);
-      put(a2 + L::DAP + 16 * rt * CR + 16 * ct, CR, dap);
+      put(dAs + 16 * rt * LS + 16 * ct, LS, dap);
     }
     __syncthreads();
     if (tid < p.nrow) {   // dbeta_t (through A = Diag(beta) A') += sum_s dA[t,s] A'[t,s]
       for (int s = 0; s < CR; ++s) db += B1[tid * LS + s] * B3[tid * LS + s];
       dbeta[p.row0 + static_cast<int64_t>(tid) * H] = Elem<TIn>::from(db);
     }
-  }
-}
+    __syncthreads();
 
-// ---------------------------------------------------------------- decayed products
-
-template <int D, typename TIn>
-__global__ __launch_bounds__(512) void bwd_grad_decay_kernel(const TIn* __restrict__ q,
-                                                             const TIn* __restrict__ k,
-                                                             const float* __restrict__ ws,
-                                                             const float* __restrict__ g1,
-                                                             const float* __restrict__ g2,
-                                                             TIn* __restrict__ dq,
-                                                             TIn* __restrict__ dk,
-                                                             TIn* __restrict__ dg, int T, int H,
-                                                             int nc, float scale) {
-  // Every product here stays on fp32 operands, also for bf16 inputs: dG combines
-  // the row-side and column-side products with opposite signs (X_A - Z_A - Z_M),
-  // and with bf16 operands that cancellation took dg past its tolerance.
-  using L = BwdLayout<D>;
-  constexpr int LD = L::LD;
-  __shared__ __attribute__((aligned(16))) float sm[3 * CR * LD + 2 * CR * LS + 10 * D];
-  float* Ki = sm;               // k e^{R - G}  (column side)
-  float* Ko = Ki + CR * LD;     // k e^{G - R}  (row side), later dG
-  float* Qo = Ko + CR * LD;     // q e^{G - R}  (row side), later dKt Kt
-  float* dAs = Qo + CR * LD;
-  float* dMs = dAs + CR * LS;
-  float* Rf = dMs + CR * LS;    // [4][D] G at each sub-tile's last row
-  float* FP = Rf + 4 * D;       // [6][D] e^{R_I - R_J}
-  const int tid = threadIdx.x, wave = tid >> 6;
-  const int l16 = lane16(), g4 = lane_g4();
-  const ChunkPos p = chunk_pos(blockIdx.x, T, H, nc);
-  const int64_t item = blockIdx.x;
-  const int64_t rs = static_cast<int64_t>(H) * D;
-  const float* w = ws + item * L::WS;
-  const float* a1 = g1 + item * L::G1;
-  const float* a2 = g2 + item * L::G2;
-  const TIn* qc = q + p.row0 * D;
-  const TIn* kc = k + p.row0 * D;
-  constexpr int CT = D / 16;
-
-  if (tid < D) {
+    // ---- decayed products of dA' and dM' with k and q, then dq, dk and dg.  Every
+    // product here stays on fp32 operands, also for bf16 inputs: dG combines the
+    // row-side and column-side products with opposite signs (X_A - Z_A - Z_M), and
+    // with bf16 operands that cancellation took dg past its tolerance.
+    const TIn* qc = q + p.row0 * D;
+    const TIn* kc = k + p.row0 * D;
+    if (tid < D) {
 #pragma unroll
-    for (int I = 0; I < 4; ++I) Rf[I * D + tid] = w[L::G + (16 * I + 15) * D + tid];
-    for (int I = 1; I < 4; ++I)
-      for (int J = 0; J < I; ++J)
-        FP[pair_index(I, J) * D + tid] = fexp(Rf[I * D + tid] - Rf[J * D + tid]);
-  }
-  {
-    GTile<512, CR, CR> t_da, t_dm;
-    GTile<512, CR, D> t_g;
-    t_da.load(a2 + L::DAP, CR);
-    t_dm.load(a2 + L::DMP, CR);
-    t_g.load(w + L::G, D);
-    t_da.pin_all();
-    t_dm.pin_all();
-    t_g.pin_all();
-    t_da.store(dAs, LS);
-    t_dm.store(dMs, LS);
-    t_g.store(Qo, LD);
-  }
-  __syncthreads();
-  {   // G (parked in Qo) -> k colf, k rowf, q rowf; each element read and written by one thread
-    ITile<512, D, TIn> kt, qt;
-    kt.load(kc, rs, p.nrow);
-    qt.load(qc, rs, p.nrow);
-    kt.pin_all();
-    qt.pin_all();
-#pragma unroll
-    for (int j = 0; j < kt.PER; ++j) {
-      const int e = tid + j * 512, t = e / D, i = e - t * D;
-      const float G = Qo[t * LD + i], RI = Rf[(t >> 4) * D + i];
-      const float rowf = fexp(G - RI), colf = fexp(RI - G);
-      Ki[t * LD + i] = kt.r[j] * colf;
-      Ko[t * LD + i] = kt.r[j] * rowf;
-      Qo[t * LD + i] = qt.r[j] * rowf;
+      for (int I = 0; I < 4; ++I) Rf[I * D + tid] = w[L::G + (16 * I + 15) * D + tid];
+      for (int I = 1; I < 4; ++I)
+        for (int J = 0; J < I; ++J)
+          FP[pair_index(I, J) * D + tid] = fexp(Rf[I * D + tid] - Rf[J * D + tid]);
     }
-  }
-  __syncthreads();
-
-  // Output tile (R, cc) of the 64 x D results; X-side sums run over column
-  // sub-tiles J <= R, Z-side sums over row sub-tiles I >= R.
-  constexpr int NTW = 4 * CT / 8;
-  f32x4_t xa[NTW], xm[NTW], za[NTW], zm[NTW];
+    {
+      GTile<kNnThreads, CR, D> t_gg;
+      ITile4<kNnThreads, D, TIn> t_kk, t_qq;
+      t_gg.load(w + L::G, D);
+      t_kk.load(kc, rs, p.nrow);
+      t_qq.load(qc, rs, p.nrow);
+      t_gg.pin_all();
+      t_kk.pin_all();
+      t_qq.pin_all();
+      __syncthreads();   // Rf
+      // k colf, k rowf, q rowf (same element order in the three tiles)
 #pragma unroll
-  for (int x = 0; x < NTW; ++x) {
-    const int j = wave + 8 * x, R = j / CT, cc = j - R * CT;
-    xa[x] = xm[x] = za[x] = zm[x] = zero4();
-    for (int J = 0; J <= R; ++J) {
-      const float* kb = Ki + 16 * J * LD + 16 * cc;
-      const f32x4_t ta = mm<false, false>(zero4(), dAs + 16 * R * LS + 16 * J, LS, kb, LD, 16);
-      const f32x4_t tm = mm<false, false>(zero4(), dMs + 16 * R * LS + 16 * J, LS, kb, LD, 16);
-      const float f = J < R ? FP[pair_index(R, J) * D + 16 * cc + l16] : 1.f;
+      for (int j = 0; j < t_gg.PER; ++j) {
+        const int e = tid + j * kNnThreads, t = e / (D / 4), i0 = (e - t * (D / 4)) * 4;
+        const f32x4_t kv = t_kk.get(j, p.nrow), qv = t_qq.get(j, p.nrow);
+        f32x4_t ki, ko, qo;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xa[x][i] += f * ta[i];
-        xm[x][i] += f * tm[i];
+        for (int i = 0; i < 4; ++i) {
+          const float G = t_gg.r[j][i], RI = Rf[(t >> 4) * D + i0 + i];
+          const float rowf = fexp(G - RI), colf = fexp(RI - G);
+          ki[i] = kv[i] * colf;
+          ko[i] = kv[i] * rowf;
+          qo[i] = qv[i] * rowf;
+        }
+        *reinterpret_cast<f32x4_t*>(Ki + t * LD + i0) = ki;
+        *reinterpret_cast<f32x4_t*>(Ko + t * LD + i0) = ko;
+        *reinterpret_cast<f32x4_t*>(Qo + t * LD + i0) = qo;
       }
     }
-    for (int I = R; I < 4; ++I) {
-      const f32x4_t ta = mm<true, false>(zero4(), dAs + 16 * I * LS + 16 * R, LS,
-                                         Ko + 16 * I * LD + 16 * cc, LD, 16);
-      const f32x4_t tm = mm<true, false>(zero4(), dMs + 16 * I * LS + 16 * R, LS,
-                                         Qo + 16 * I * LD + 16 * cc, LD, 16);
-      const float f = I > R ? FP[pair_index(I, R) * D + 16 * cc + l16] : 1.f;
+    __syncthreads();
+
+    // Output tile (R, cc) of the 64 x D results (the tiles of dQ', dKt, dKg above);
+    // X-side sums run over column sub-tiles J <= R, Z-side sums over row sub-tiles I >= R.
+    constexpr int NTD = DT::NBIG / 8;
+    f32x4_t xa[NTD], xm[NTD], za[NTD], zm[NTD];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        za[x][i] += f * ta[i];
-        zm[x][i] += f * tm[i];
+    for (int x = 0; x < NTD; ++x) {
+      const int j = wave + 8 * x, R = j / CT, cc = j - R * CT;
+      xa[x] = xm[x] = za[x] = zm[x] = zero4();
+      for (int J = 0; J <= R; ++J) {
+        const float* kb = Ki + 16 * J * LD + 16 * cc;
+        const f32x4_t ta = mm<false, false>(zero4(), dAs + 16 * R * LS + 16 * J, LS, kb, LD, 16);
+        const f32x4_t tm = mm<false, false>(zero4(), dMs + 16 * R * LS + 16 * J, LS, kb, LD, 16);
+        const float f = J < R ? FP[pair_index(R, J) * D + 16 * cc + l16] : 1.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          xa[x][i] += f * ta[i];
+          xm[x][i] += f * tm[i];
+        }
       }
-    }
-  }
-  __syncthreads();
-  // the inputs of two tiles' elements are loaded first (rows clamped into the chunk,
-  // all loads in flight together), then those elements are formed and stored
-  constexpr int XG = 2;
+      for (int I = R; I < 4; ++I) {
+        const f32x4_t ta = mm<true, false>(zero4(), dAs + 16 * I * LS + 16 * R, LS,
+                                           Ko + 16 * I * LD + 16 * cc, LD, 16);
+        const f32x4_t tm = mm<true, false>(zero4(), dMs + 16 * I * LS + 16 * R, LS,
+                                           Qo + 16 * I * LD + 16 * cc, LD, 16);
+        const float f = I > R ? FP[pair_index(I, R) * D + 16 * cc + l16] : 1.f;
 #pragma unroll
-  for (int x0 = 0; x0 < NTW; x0 += XG) {
-    float eG[XG][4], eQ[XG][4], eKg[XG][4], eKt[XG][4], eq[XG][4], ek[XG][4];
-#pragma unroll
-    for (int xx = 0; xx < XG; ++xx) {
-      const int x = xx, j = wave + 8 * (x0 + xx), R = j / CT, cc = j - R * CT;
-      const int col = 16 * cc + l16;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * R + 4 * g4 + i;
-        const int e = t * D + col;
-        const int tc = min(t, p.nrow - 1);
-        eG[x][i] = w[L::G + e];
-        eQ[x][i] = a1[L::DQP + e];
-        eKg[x][i] = a2[L::DKG + e];
-        eKt[x][i] = a1[L::DKT + e];
-        eq[x][i] = to_f32(qc[tc * rs + col]);
-        ek[x][i] = to_f32(kc[tc * rs + col]);
-      }
-    }
-#pragma unroll
-    for (int x = 0; x < XG; ++x) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pin(eG[x][i]);
-        pin(eQ[x][i]);
-        pin(eKg[x][i]);
-        pin(eKt[x][i]);
-        pin(eq[x][i]);
-        pin(ek[x][i]);
-      }
-    }
-#pragma unroll
-    for (int xx = 0; xx < XG; ++xx) {
-      const int x = x0 + xx, j = wave + 8 * x, R = j / CT, cc = j - R * CT;
-      const int col = 16 * cc + l16;
-      const float RI = Rf[R * D + col], Gl = Rf[3 * D + col];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * R + 4 * g4 + i;
-        const float G = eG[xx][i];
-        const float rowf = fexp(G - RI), colf = fexp(RI - G), eg = fexp(G), et = fexp(Gl - G);
-        const float XA = rowf * xa[x][i], XM = rowf * xm[x][i];
-        const float ZA = colf * za[x][i], ZM = colf * zm[x][i];
-        const bool ok = t < p.nrow;
-        const float kv = ok ? ek[xx][i] : 0.f, qv = ok ? eq[xx][i] : 0.f;
-        const float dKg = eKg[xx][i], dKt = eKt[xx][i];
-        const float dqv = scale * eQ[xx][i] * eg + XM;
-        const float kg = dKg * eg, kt = dKt * et;
-        const float dkv = kg + kt + XA + ZA + ZM;
-        Ko[t * LD + col] = qv * dqv + kv * (kg + XA - kt - ZA - ZM);
-        Qo[t * LD + col] = kv * kt;
-        if (ok) {
-          dq[(p.row0 + static_cast<int64_t>(t) * H) * D + col] = Elem<TIn>::from(dqv);
-          dk[(p.row0 + static_cast<int64_t>(t) * H) * D + col] = Elem<TIn>::from(dkv);
+        for (int i = 0; i < 4; ++i) {
+          za[x][i] += f * ta[i];
+          zm[x][i] += f * tm[i];
         }
       }
     }
-  }
-  __syncthreads();
-  if (tid < D) {   // dg = reverse running sum of dG, with the last row's extra terms
-    float run = a1[L::DLAM + tid] * w[L::LAM + tid];
-    for (int t = 0; t < CR; ++t) run += Qo[t * LD + tid];
-    for (int t = CR - 1; t >= 0; --t) {
-      run += Ko[t * LD + tid];
-      if (t < p.nrow) dg[(p.row0 + static_cast<int64_t>(t) * H) * D + tid] = Elem<TIn>::from(run);
+    __syncthreads();
+    // the element inputs of two tiles are loaded first (rows clamped into the chunk,
+    // all loads in flight together), then those elements are formed and stored
+    constexpr int XG = 2;
+#pragma unroll
+    for (int x0 = 0; x0 < NTD; x0 += XG) {
+      float eG[XG][4], eq[XG][4], ek[XG][4];
+#pragma unroll
+      for (int xx = 0; xx < XG; ++xx) {
+        const int j = wave + 8 * (x0 + xx), R = j / CT, cc = j - R * CT;
+        const int col = 16 * cc + l16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * R + 4 * g4 + i;
+          const int tc = min(t, p.nrow - 1);
+          eG[xx][i] = w[L::G + t * D + col];
+          eq[xx][i] = to_f32(qc[tc * rs + col]);
+          ek[xx][i] = to_f32(kc[tc * rs + col]);
+        }
+      }
+#pragma unroll
+      for (int xx = 0; xx < XG; ++xx) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pin(eG[xx][i]);
+          pin(eq[xx][i]);
+          pin(ek[xx][i]);
+        }
+      }
+#pragma unroll
+      for (int xx = 0; xx < XG; ++xx) {
+        const int x = x0 + xx, j = wave + 8 * x, R = j / CT, cc = j - R * CT;
+        const int col = 16 * cc + l16;
+        const float RI = Rf[R * D + col], Gl = Rf[3 * D + col];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * R + 4 * g4 + i;
+          const float G = eG[xx][i];
+          const float rowf = fexp(G - RI), colf = fexp(RI - G), eg = fexp(G), et = fexp(Gl - G);
+          const float XA = rowf * xa[x][i], XM = rowf * xm[x][i];
+          const float ZA = colf * za[x][i], ZM = colf * zm[x][i];
+          const bool ok = t < p.nrow;
+          const float kv = ok ? ek[xx][i] : 0.f, qv = ok ? eq[xx][i] : 0.f;
+          const float dKg = dkg[x][i], dKt = acc[2 * NTD + x][i];
+          const float dqv = scale * acc[x][i] * eg + XM;
+          const float kg = dKg * eg, kt = dKt * et;
+          const float dkv = kg + kt + XA + ZA + ZM;
+          Ko[t * LD + col] = qv * dqv + kv * (kg + XA - kt - ZA - ZM);
+          Qo[t * LD + col] = kv * kt;
+          if (ok) {
+            dq[(p.row0 + static_cast<int64_t>(t) * H) * D + col] = Elem<TIn>::from(dqv);
+            dk[(p.row0 + static_cast<int64_t>(t) * H) * D + col] = Elem<TIn>::from(dkv);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < D) {   // dg = reverse running sum of dG, with the last row's extra terms
+      float run = dlam * w[L::LAM + tid];
+      for (int t = 0; t < CR; ++t) run += Qo[t * LD + tid];
+      for (int t = CR - 1; t >= 0; --t) {
+        run += Ko[t * LD + tid];
+        if (t < p.nrow) dg[(p.row0 + static_cast<int64_t>(t) * H) * D + tid] = Elem<TIn>::from(run);
+      }
     }
   }
 }
@@ -1118,18 +1104,16 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
   const int nc = (a.T + CR - 1) / CR;
   const int64_t items = static_cast<int64_t>(a.B) * a.H * nc;
   constexpr bool BF = IsBf16<TIn>::value;
-  // per chunk, in floats: the fp32 operands, the operand gradients, then the states,
-  // state gradients, Delta and dU (fp32, or bf16 for bf16 inputs: half the floats),
-  // then for bf16 inputs the bf16 scan operands
+  // per chunk, in floats: the fp32 operands, then the states, state gradients, Delta
+  // and dU (fp32, or bf16 for bf16 inputs: half the floats), then for bf16 inputs the
+  // bf16 scan operands
   const int64_t sdu = (BF ? 1 : 2) * (D * D + CR * D);
-  const int64_t per = L::WS + L::G1 + L::G2 + sdu + (BF ? L::WSB / 2 : 0);
+  const int64_t per = L::WS + sdu + (BF ? L::WSB / 2 : 0);
   float* buf = nullptr;
   hipError_t err = hipMallocAsync(reinterpret_cast<void**>(&buf), items * per * sizeof(float), a.stream);
   if (err != hipSuccess) return err;
   float* ws = buf;
-  float* g1 = ws + items * L::WS;
-  float* g2 = g1 + items * L::G1;
-  float* sreg = g2 + items * L::G2;   // S, dS, Delta, dU in the element type chosen above
+  float* sreg = ws + items * L::WS;   // S, dS, Delta, dU in the element type chosen above
   __bf16* wsb = BF ? reinterpret_cast<__bf16*>(sreg + items * sdu) : nullptr;
   float* st = sreg;
   float* dst = st + items * D * D;
@@ -1156,8 +1140,9 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
     hipLaunchKernelGGL((bwd_scan_bf16_kernel<D>), dim3(scan_blocks), dim3(kScanThreads), 0,
                        a.stream, dout, a.d_final_state, ws, wsb, dstb, dub,
                        static_cast<TIn*>(a.dv), a.d_initial_state, a.T, a.H, nc, BH);
-    hipLaunchKernelGGL((bwd_grad_chunk_kernel<D, TIn>), dim3(items), dim3(kNnThreads), 0, a.stream, k,
-                       beta, v, dout, stb, dstb, dlb, dub, ws, g1, g2, static_cast<TIn*>(a.dbeta),
+    hipLaunchKernelGGL((bwd_grad_chunk_kernel<D, TIn>), dim3(items), dim3(kNnThreads), 0, a.stream, q,
+                       k, beta, v, dout, stb, dstb, dlb, dub, ws, static_cast<TIn*>(a.dq),
+                       static_cast<TIn*>(a.dk), static_cast<TIn*>(a.dg), static_cast<TIn*>(a.dbeta),
                        a.T, a.H, nc, a.scale);
   } else {
     hipLaunchKernelGGL((bwd_fwd_scan_kernel<D, TIn>), dim3(scan_blocks), dim3(kScanThreads), 0, a.stream, v,
@@ -1165,13 +1150,11 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
     hipLaunchKernelGGL((bwd_scan_kernel<D, TIn>), dim3(scan_blocks), dim3(kScanThreads), 0, a.stream, dout,
                        a.d_final_state, ws, dst, du, static_cast<TIn*>(a.dv), a.d_initial_state,
                        a.T, a.H, nc, BH);
-    hipLaunchKernelGGL((bwd_grad_chunk_kernel<D, TIn>), dim3(items), dim3(kNnThreads), 0, a.stream, k,
-                       beta, v, dout, st, dst, dl, du, ws, g1, g2, static_cast<TIn*>(a.dbeta), a.T,
-                       a.H, nc, a.scale);
+    hipLaunchKernelGGL((bwd_grad_chunk_kernel<D, TIn>), dim3(items), dim3(kNnThreads), 0, a.stream, q,
+                       k, beta, v, dout, st, dst, dl, du, ws, static_cast<TIn*>(a.dq),
+                       static_cast<TIn*>(a.dk), static_cast<TIn*>(a.dg), static_cast<TIn*>(a.dbeta),
+                       a.T, a.H, nc, a.scale);
   }
-  hipLaunchKernelGGL((bwd_grad_decay_kernel<D, TIn>), dim3(items), dim3(512), 0, a.stream, q, k,
-                     ws, g1, g2, static_cast<TIn*>(a.dq), static_cast<TIn*>(a.dk),
-                     static_cast<TIn*>(a.dg), a.T, a.H, nc, a.scale);
   err = hipGetLastError();
   const hipError_t ferr = hipFreeAsync(buf, a.stream);
   return err != hipSuccess ? err : ferr;

@@ -36,11 +36,6 @@ struct BwdLayout {
   static constexpr int TB = 0, TI = 4096, AP = 8192, MP = 12288, PP = 16384;
   static constexpr int W = 20480, QP = W + CR * D, KT = QP + CR * D, G = KT + CR * D;
   static constexpr int LAM = G + CR * D, WS = LAM + D;
-  // operand gradients per chunk that the decayed products read, written by
-  // bwd_grad_chunk (dW, dP and dTb stay inside that kernel)
-  static constexpr int DQP = 0, DKT = CR * D, DLAM = 2 * CR * D, G1 = DLAM + D;
-  // written by bwd_grad_chunk
-  static constexpr int DKG = 0, DMP = CR * D, DAP = DMP + 4096, G2 = DAP + 4096;
   // bf16 copies of the scan operands per chunk, written by chunk_ops for bf16
   // inputs (bf16 elements), each in the layout a scan reads k-contiguously:
   // Tb, Tb^T, P^T, W, W^T, Kt, Kt^T, Q'^T

@@ -185,9 +185,9 @@ int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void
  * per-chunk states, state gradients, Delta and dU are kept as bf16; the inverse,
  * the 16-term sub-tile products and the decayed products stay fp32.  The call
  * allocates a workspace with hipMallocAsync on `stream` and frees it on the same
- * stream, per 64-token chunk per head: 549,888 bytes for bf16 and 541,696 for
- * fp32 at d = 128 (328,192 and 295,424 at d = 64), so T = 65,536 with 32 heads
- * needs about 18 GB; an allocation failure returns KDA_ERR_HIP.
+ * stream, per 64-token chunk per head: 418,304 bytes for bf16 and 410,112 for
+ * fp32 at d = 128 (246,016 and 213,248 at d = 64), so T = 65,536 with 32 heads
+ * needs about 14 GB; an allocation failure returns KDA_ERR_HIP.
  * Outputs must not alias inputs.
  */
 int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
