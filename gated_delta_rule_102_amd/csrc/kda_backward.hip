@@ -637,29 +637,33 @@ __device__ __forceinline__ void dv_accumulate_bf16(__bf16* sm, const bf16_t* v, 
 #pragma unroll
   for (int x = 0; x < NTW; ++x) acc[x] = zero4();
   dlam = 0.f;
+  // the next slice's loads are issued before this slice's products (the last slice
+  // reloads itself, so no load sits behind a branch)
+  BTileS<512, D, SL> t_s, t_ds;
+  BTileS<512, CR, SL> t_dl, t_du, t_do, t_v;
+  auto load = [&](int c0) {
+    t_s.load(st + item * D * D + c0, D);
+    t_ds.load(dst + item * D * D + c0, D);
+    t_dl.load(dl + item * CR * D + c0, D);
+    t_du.load(du + item * CR * D + c0, D);
+    t_do.load_rows(dout + p.row0 * D + c0, rs, p.nrow);
+    t_v.load_rows(v + p.row0 * D + c0, rs, p.nrow);
+  };
+  load(0);
   for (int c0 = 0; c0 < D; c0 += SL) {
-    {
-      BTileS<512, D, SL> t_s, t_ds;
-      BTileS<512, CR, SL> t_dl, t_du, t_do, t_v;
-      t_s.load(st + item * D * D + c0, D);
-      t_ds.load(dst + item * D * D + c0, D);
-      t_dl.load(dl + item * CR * D + c0, D);
-      t_du.load(du + item * CR * D + c0, D);
-      t_do.load_rows(dout + p.row0 * D + c0, rs, p.nrow);
-      t_v.load_rows(v + p.row0 * D + c0, rs, p.nrow);
-      t_s.pin_all();
-      t_ds.pin_all();
-      t_dl.pin_all();
-      t_du.pin_all();
-      t_do.pin_all();
-      t_v.pin_all();
-      t_s.store(Ss, LVB);
-      t_ds.store(dSs, LVB);
-      t_dl.store(Dls, LVB);
-      t_du.store(dUs, LVB);
-      t_do.store(dOs, LVB);
-      t_v.store(Vs, LVB);
-    }
+    t_s.pin_all();
+    t_ds.pin_all();
+    t_dl.pin_all();
+    t_du.pin_all();
+    t_do.pin_all();
+    t_v.pin_all();
+    t_s.store(Ss, LVB);
+    t_ds.store(dSs, LVB);
+    t_dl.store(Dls, LVB);
+    t_du.store(dUs, LVB);
+    t_do.store(dOs, LVB);
+    t_v.store(Vs, LVB);
+    load(min(c0 + SL, D - SL));
     __syncthreads();
 #pragma unroll
     for (int x = 0; x < NTW; ++x) {
@@ -931,6 +935,14 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_chunk_kernel(
       put(dMs + 16 * rt * LS + 16 * ct, LS, dmv[x]);   // Tb is no longer read
     }
     t_ap.store(B3, LS);
+    // the decayed products' G, k and q, in flight while the algebra finishes
+    const TIn* qc = q + p.row0 * D;
+    const TIn* kc = k + p.row0 * D;
+    GTile<kNnThreads, CR, D> t_gg;
+    ITile4<kNnThreads, D, TIn> t_kk, t_qq;
+    t_gg.load(w + L::G, D);
+    t_kk.load(kc, rs, p.nrow);
+    t_qq.load(qc, rs, p.nrow);
     __syncthreads();
     // dA = -Ti^T X on s < t;  dA' = Diag(beta) dA
 #pragma unroll
@@ -958,8 +970,6 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_chunk_kernel(
     // product here stays on fp32 operands, also for bf16 inputs: dG combines the
     // row-side and column-side products with opposite signs (X_A - Z_A - Z_M), and
     // with bf16 operands that cancellation took dg past its tolerance.
-    const TIn* qc = q + p.row0 * D;
-    const TIn* kc = k + p.row0 * D;
     if (tid < D) {
 #pragma unroll
       for (int I = 0; I < 4; ++I) Rf[I * D + tid] = w[L::G + (16 * I + 15) * D + tid];
@@ -968,11 +978,6 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_chunk_kernel(
           FP[pair_index(I, J) * D + tid] = fexp(Rf[I * D + tid] - Rf[J * D + tid]);
     }
     {
-      GTile<kNnThreads, CR, D> t_gg;
-      ITile4<kNnThreads, D, TIn> t_kk, t_qq;
-      t_gg.load(w + L::G, D);
-      t_kk.load(kc, rs, p.nrow);
-      t_qq.load(qc, rs, p.nrow);
       t_gg.pin_all();
       t_kk.pin_all();
       t_qq.pin_all();
