@@ -718,40 +718,6 @@ struct ChunkLds {
   static_assert(TOTAL * 4 <= 160 * 1024, "LDS budget");
 };
 
-// 64 x COLS input rows (bf16 or fp32) held as raw words, 4 consecutive elements per
-// thread in the GTile<NT, 64, COLS> element order; rows >= nrow read as zero.
-template <int NT, int COLS, typename TIn>
-struct ITile4 {
-  static constexpr int C4 = COLS / 4, N = CR * C4, PER = N / NT;
-  static_assert(N % NT == 0, "tile split");
-  static constexpr bool BF = IsBf16<TIn>::value;
-  using Raw = typename std::conditional<BF, i32x2_t, f32x4_t>::type;
-  Raw r[PER];
-  __device__ __forceinline__ void load(const TIn* src, int64_t row_stride, int nrow) {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int e = static_cast<int>(threadIdx.x) + j * NT;
-      const int rr = e / C4, c = (e - rr * C4) * 4;
-      r[j] = *reinterpret_cast<const Raw*>(src + min(rr, nrow - 1) * row_stride + c);
-    }
-  }
-  __device__ __forceinline__ void pin_all() {
-#pragma unroll
-    for (int j = 0; j < PER; ++j) pin(r[j]);
-  }
-  __device__ __forceinline__ f32x4_t get(int j, int nrow) const {
-    const int rr = (static_cast<int>(threadIdx.x) + j * NT) / C4;
-    f32x4_t x;
-    if constexpr (BF) {
-      const uint32_t w0 = static_cast<uint32_t>(r[j][0]), w1 = static_cast<uint32_t>(r[j][1]);
-      x = f32x4_t{bf16lo(w0), bf16hi(w0), bf16lo(w1), bf16hi(w1)};
-    } else {
-      x = r[j];
-    }
-    return rr < nrow ? x : zero4();
-  }
-};
-
 // Element type of the per-chunk states, Delta and dU the scans store.
 template <typename TIn>
 using StateElem = typename std::conditional<IsBf16<TIn>::value, __bf16, float>::type;

@@ -17,6 +17,8 @@
 // every factor stays inside fp32's range when the log-decay is >= -5.
 #pragma once
 
+#include <type_traits>
+
 #include "kda_device.h"
 
 namespace kda {
@@ -244,6 +246,40 @@ struct ITile {
   }
 };
 
+// 64 x COLS input rows (bf16 or fp32) held as raw words, 4 consecutive elements per
+// thread in the GTile<NT, 64, COLS> element order; rows >= nrow read as zero.
+template <int NT, int COLS, typename TIn>
+struct ITile4 {
+  static constexpr int C4 = COLS / 4, N = CR * C4, PER = N / NT;
+  static_assert(N % NT == 0, "tile split");
+  static constexpr bool BF = IsBf16<TIn>::value;
+  using Raw = typename std::conditional<BF, i32x2_t, f32x4_t>::type;
+  Raw r[PER];
+  __device__ __forceinline__ void load(const TIn* src, int64_t row_stride, int nrow) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = static_cast<int>(threadIdx.x) + j * NT;
+      const int rr = e / C4, c = (e - rr * C4) * 4;
+      r[j] = *reinterpret_cast<const Raw*>(src + min(rr, nrow - 1) * row_stride + c);
+    }
+  }
+  __device__ __forceinline__ void pin_all() {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) pin(r[j]);
+  }
+  __device__ __forceinline__ f32x4_t get(int j, int nrow) const {
+    const int rr = (static_cast<int>(threadIdx.x) + j * NT) / C4;
+    f32x4_t x;
+    if constexpr (BF) {
+      const uint32_t w0 = static_cast<uint32_t>(r[j][0]), w1 = static_cast<uint32_t>(r[j][1]);
+      x = f32x4_t{bf16lo(w0), bf16hi(w0), bf16lo(w1), bf16hi(w1)};
+    } else {
+      x = r[j];
+    }
+    return rr < nrow ? x : zero4();
+  }
+};
+
 // Block id -> (sequence-head bh, first column c0) for the column-sliced scans.
 // The NSL slices of one sequence-head get block ids that are equal mod 8, so the
 // round-robin dispatch over the eight XCDs puts them on one XCD, whose L2 then
@@ -392,14 +428,24 @@ __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __res
   float* w = ws + static_cast<int64_t>(blockIdx.x) * L::WS;
   __bf16* wb = BF ? wsb + static_cast<int64_t>(blockIdx.x) * L::WSB : nullptr;
 
-  {
-    ITile<kOpsThreads, D, TIn> gt;
-    gt.load(gc, rs, p.nrow);
-    gt.pin_all();
-    for (int e = tid; e < 3 * CR * LS; e += kOpsThreads) S0[e] = 0.f;
-    const float bt = to_f32(beta[p.row0 + static_cast<int64_t>(min(tid & (CR - 1), p.nrow - 1)) * H]);
-    if (tid < CR) BT[tid] = tid < p.nrow ? bt : 0.f;
-    gt.store(R0, LD);
+  // g, k and q of the chunk, four consecutive channels per load, all in flight
+  // together; k and q stay in registers for every stage below
+  using IT = ITile4<kOpsThreads, D, TIn>;
+  constexpr int C4 = D / 4;
+  IT gt, kt, qt;
+  gt.load(gc, rs, p.nrow);
+  kt.load(kc, rs, p.nrow);
+  qt.load(qc, rs, p.nrow);
+  const float bt = to_f32(beta[p.row0 + static_cast<int64_t>(min(tid & (CR - 1), p.nrow - 1)) * H]);
+  for (int e = tid; e < 3 * CR * LS; e += kOpsThreads) S0[e] = 0.f;
+  gt.pin_all();
+  kt.pin_all();
+  qt.pin_all();
+  if (tid < CR) BT[tid] = tid < p.nrow ? bt : 0.f;
+#pragma unroll
+  for (int j = 0; j < IT::PER; ++j) {
+    const int e = tid + j * kOpsThreads, t = e / C4, i0 = (e - t * C4) * 4;
+    *reinterpret_cast<f32x4_t*>(R0 + t * LD + i0) = gt.get(j, p.nrow);
   }
   __syncthreads();
   if (tid < D) {   // running sum of g down the chunk (padding rows hold 0)
@@ -419,21 +465,31 @@ __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __res
             fexp(R0[(16 * I + 15) * LD + tid] - R0[(16 * J + 15) * LD + tid]);
     w[L::LAM + tid] = fexp(R0[(CR - 1) * LD + tid]);
   }
-  {
-    ITile<kOpsThreads, D, TIn> kt;
-    kt.load(kc, rs, p.nrow);
-    kt.pin_all();
+  // k rowf into R1, k colf into R2; G and Kt to the workspace
 #pragma unroll
-    for (int j = 0; j < kt.PER; ++j) {
-      const int e = tid + j * kOpsThreads, t = e / D, i = e - t * D;
-      const float G = R0[t * LD + i], RI = R0[(t | 15) * LD + i], Gl = R0[(CR - 1) * LD + i];
-      const float kv = kt.r[j];
-      R1[t * LD + i] = kv * fexp(G - RI);
-      R2[t * LD + i] = kv * fexp(RI - G);
-      const float ktv = kv * fexp(Gl - G);
-      if constexpr (!BF) w[L::KT + e] = ktv;   // bf16 inputs: only the bf16 copies are read
-      w[L::G + e] = G;
-      if constexpr (BF) wb[L::BKT + e] = static_cast<__bf16>(ktv);
+  for (int j = 0; j < IT::PER; ++j) {
+    const int e = tid + j * kOpsThreads, t = e / C4, i0 = (e - t * C4) * 4;
+    const f32x4_t G = *reinterpret_cast<const f32x4_t*>(R0 + t * LD + i0);
+    const f32x4_t RI = *reinterpret_cast<const f32x4_t*>(R0 + (t | 15) * LD + i0);
+    const f32x4_t Gl = *reinterpret_cast<const f32x4_t*>(R0 + (CR - 1) * LD + i0);
+    const f32x4_t kv = kt.get(j, p.nrow);
+    f32x4_t r1, r2, ktv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      r1[i] = kv[i] * fexp(G[i] - RI[i]);
+      r2[i] = kv[i] * fexp(RI[i] - G[i]);
+      ktv[i] = kv[i] * fexp(Gl[i] - G[i]);
+    }
+    *reinterpret_cast<f32x4_t*>(R1 + t * LD + i0) = r1;
+    *reinterpret_cast<f32x4_t*>(R2 + t * LD + i0) = r2;
+    *reinterpret_cast<f32x4_t*>(w + L::G + t * D + i0) = G;
+    if constexpr (!BF) {   // bf16 inputs: only the bf16 copies are read
+      *reinterpret_cast<f32x4_t*>(w + L::KT + t * D + i0) = ktv;
+    } else {
+      bf16x4_t kb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kb[i] = static_cast<__bf16>(ktv[i]);
+      *reinterpret_cast<bf16x4_t*>(wb + L::BKT + t * D + i0) = kb;
     }
   }
   __syncthreads();
@@ -460,16 +516,17 @@ __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __res
   };
   pair_gram(S0, true);
   __syncthreads();
-  {   // q rowf into R1
-    ITile<kOpsThreads, D, TIn> qt;
-    qt.load(qc, rs, p.nrow);
-    qt.pin_all();
+  // q rowf into R1
 #pragma unroll
-    for (int j = 0; j < qt.PER; ++j) {
-      const int e = tid + j * kOpsThreads, t = e / D, i = e - t * D;
-      const float G = R0[t * LD + i], RI = R0[(t | 15) * LD + i];
-      R1[t * LD + i] = qt.r[j] * fexp(G - RI);
-    }
+  for (int j = 0; j < IT::PER; ++j) {
+    const int e = tid + j * kOpsThreads, t = e / C4, i0 = (e - t * C4) * 4;
+    const f32x4_t G = *reinterpret_cast<const f32x4_t*>(R0 + t * LD + i0);
+    const f32x4_t RI = *reinterpret_cast<const f32x4_t*>(R0 + (t | 15) * LD + i0);
+    const f32x4_t qv = qt.get(j, p.nrow);
+    f32x4_t r1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r1[i] = qv[i] * fexp(G[i] - RI[i]);
+    *reinterpret_cast<f32x4_t*>(R1 + t * LD + i0) = r1;
   }
   __syncthreads();
   pair_gram(S1, false);
@@ -477,13 +534,16 @@ __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __res
   l2g<kOpsThreads, CR, CR>(w + L::AP, CR, S0, LS);
   l2g<kOpsThreads, CR, CR>(w + L::MP, CR, S1, LS);
   if constexpr (BF) {   // Kt in R1 (free until k e^G goes there), for its bf16 transpose
-    ITile<kOpsThreads, D, TIn> kt;
-    kt.load(kc, rs, p.nrow);
-    kt.pin_all();
 #pragma unroll
-    for (int j = 0; j < kt.PER; ++j) {
-      const int e = tid + j * kOpsThreads, t = e / D, i = e - t * D;
-      R1[t * LD + i] = kt.r[j] * fexp(R0[(CR - 1) * LD + i] - R0[t * LD + i]);
+    for (int j = 0; j < IT::PER; ++j) {
+      const int e = tid + j * kOpsThreads, t = e / C4, i0 = (e - t * C4) * 4;
+      const f32x4_t G = *reinterpret_cast<const f32x4_t*>(R0 + t * LD + i0);
+      const f32x4_t Gl = *reinterpret_cast<const f32x4_t*>(R0 + (CR - 1) * LD + i0);
+      const f32x4_t kv = kt.get(j, p.nrow);
+      f32x4_t r1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r1[i] = kv[i] * fexp(Gl[i] - G[i]);
+      *reinterpret_cast<f32x4_t*>(R1 + t * LD + i0) = r1;
     }
   }
 
@@ -539,19 +599,21 @@ __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __res
     }
     __syncthreads();   // R1 is rewritten next
   }
-  {   // k e^G into R1, scale q e^G into R2
-    ITile<kOpsThreads, D, TIn> kt, qt;
-    kt.load(kc, rs, p.nrow);
-    qt.load(qc, rs, p.nrow);
-    kt.pin_all();
-    qt.pin_all();
+  // k e^G into R1, scale q e^G into R2
 #pragma unroll
-    for (int j = 0; j < kt.PER; ++j) {
-      const int e = tid + j * kOpsThreads, t = e / D, i = e - t * D;
-      const float eg = fexp(R0[t * LD + i]);
-      R1[t * LD + i] = kt.r[j] * eg;
-      R2[t * LD + i] = scale * qt.r[j] * eg;
+  for (int j = 0; j < IT::PER; ++j) {
+    const int e = tid + j * kOpsThreads, t = e / C4, i0 = (e - t * C4) * 4;
+    const f32x4_t G = *reinterpret_cast<const f32x4_t*>(R0 + t * LD + i0);
+    const f32x4_t kv = kt.get(j, p.nrow), qv = qt.get(j, p.nrow);
+    f32x4_t r1, r2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float eg = fexp(G[i]);
+      r1[i] = kv[i] * eg;
+      r2[i] = scale * qv[i] * eg;
     }
+    *reinterpret_cast<f32x4_t*>(R1 + t * LD + i0) = r1;
+    *reinterpret_cast<f32x4_t*>(R2 + t * LD + i0) = r2;
   }
   __syncthreads();
 

@@ -176,8 +176,8 @@ int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void
  *  grad_q, grad_k, grad_g [B, T, H, dk]; grad_v [B, T, H, dv]; grad_beta [B, T, H]
  *                      (dtype), required, fully overwritten.
  *  grad_initial_state  [B, H, dk, dv] fp32 or NULL (not computed).
- * dk == dv in {64, 128} for both dtypes.  k, v and grad_out are read up to 16
- * bytes at a time and must be 16-byte aligned; every other pointer needs only
+ * dk == dv in {64, 128} for both dtypes.  q, k, v, g and grad_out are read up to
+ * 16 bytes at a time and must be 16-byte aligned; every other pointer needs only
  * its element alignment (else KDA_ERR_ALIGN).  The forward is recomputed inside
  * the call (nothing is kept from kda_chunk_fwd).  fp32 inputs: fp32 throughout
  * (fp32 matrix cores).  bf16 inputs: every product over 32 or more terms takes
@@ -212,7 +212,9 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, co
  * from its entry state for its outputs.
  *
  * kda_chunk_transition: P for each of B independent segments.
- *  q, k, g, beta   as for kda_chunk_fwd ([B, T, H, .], dtype); v is not needed.
+ *  q, k, g, beta   as for kda_chunk_fwd ([B, T, H, .], dtype), except that q, k
+ *                  and g are read four elements at a time and must be 16-byte
+ *                  aligned (else KDA_ERR_ALIGN); v is not needed.
  *  transition      [B, H, dk, dk] fp32, required: the exit state of the segment
  *                  run with v = 0 from the identity, i.e. the product of its
  *                  per-token maps (I - beta_t k_t k_t^T) Diag(exp g_t), latest
