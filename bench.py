@@ -98,11 +98,12 @@ def pmc_copy(torch, nbytes=256 << 20, reps=3):
 
 def backward_flops(B, T, H, d):
     """Dense matrix-product flops of the backward per 64-token chunk and head, summed
-    over its six kernels at d = 128 and counted in 16x16x4 products (2048 flops
-    each): operand prep 1984, forward state scan 2560, reverse scan 4096, operand
-    gradients 4096, 64x64 algebra 3072, decayed products 1280 (dense tiles,
-    including the zero upper triangles of the triangular factors).  For bf16
-    inputs most of them run as bf16 16x16x32 products (8 of these each)."""
+    over its four kernels at d = 128 and counted in 16x16x4 products (2048 flops
+    each): operand prep 1984, forward state scan 2560, reverse scan 4096, and in the
+    per-chunk gradient kernel operand gradients 4096, 64x64 algebra 3072 and
+    decayed products 1280 (dense tiles, including the zero upper triangles of the
+    triangular factors).  For bf16 inputs most of them run as bf16 16x16x32
+    products (8 of these each)."""
     assert d == 128
     per_chunk = (1984 + 2560 + 4096 + 4096 + 3072 + 1280) * 2048
     return B * H * (-(-T // CHUNK)) * per_chunk

@@ -208,7 +208,7 @@ int kda_chunk_transition(const void* q, const void* k, const void* g, const void
   if (static_cast<int64_t>(B) * T > INT32_MAX / 2) return KDA_ERR_SHAPE;
   if (static_cast<int64_t>(B) * H > (1 << 24)) return KDA_ERR_SHAPE;
   const uintptr_t elt = dtype == KDA_F32 ? 4 : 2;
-  rc = check_ptrs({{q, 16, true}, {k, 16, true}, {g, 16, true}, {beta, elt, true},
+  rc = check_ptrs({{q, 16, false}, {k, 16, true}, {g, 16, true}, {beta, elt, true},
                    {transition, 4, true}});
   if (rc != KDA_OK) return rc;
   rc = check_device();

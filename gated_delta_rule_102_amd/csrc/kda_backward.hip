@@ -1103,7 +1103,7 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
   const TIn* dout = static_cast<const TIn*>(a.d_out);
   const int BH = a.B * a.H;
   const int scan_blocks = scan_grid(BH, D / SL);
-  hipLaunchKernelGGL((chunk_ops_kernel<D, TIn, false>), dim3(items), dim3(kOpsThreads), 0, a.stream, q, k, g, beta,
+  hipLaunchKernelGGL((chunk_ops_kernel<D, TIn, false, true>), dim3(items), dim3(kOpsThreads), 0, a.stream, q, k, g, beta,
                      ws, wsb, a.T, a.H, nc, a.scale);
   if constexpr (IsBf16<TIn>::value) {
     hipLaunchKernelGGL((bwd_fwd_scan_bf16_kernel<D>), dim3(scan_blocks), dim3(kScanThreads), 0,

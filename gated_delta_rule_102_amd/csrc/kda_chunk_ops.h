@@ -398,7 +398,10 @@ constexpr int kOpsWaves = kOpsThreads / 64;
 
 // EXACT keeps every product on fp32 operands; otherwise bf16 inputs use bf16
 // matrix-core operands (fp32 accumulation) for the products over 32 or more terms.
-template <int D, typename TIn, bool EXACT>
+// FULL writes every operand the backward reads; otherwise only what a chunk's
+// transition Diag(Lam) - Kt^T W needs (W, Kt, Lam), skipping q, M', P, Q', G and
+// the inverse's copies.
+template <int D, typename TIn, bool EXACT, bool FULL>
 __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __restrict__ q,
                                                        const TIn* __restrict__ k,
                                                        const TIn* __restrict__ g,
@@ -435,12 +438,12 @@ __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __res
   IT gt, kt, qt;
   gt.load(gc, rs, p.nrow);
   kt.load(kc, rs, p.nrow);
-  qt.load(qc, rs, p.nrow);
+  if constexpr (FULL) qt.load(qc, rs, p.nrow);
   const float bt = to_f32(beta[p.row0 + static_cast<int64_t>(min(tid & (CR - 1), p.nrow - 1)) * H]);
   for (int e = tid; e < 3 * CR * LS; e += kOpsThreads) S0[e] = 0.f;
   gt.pin_all();
   kt.pin_all();
-  qt.pin_all();
+  if constexpr (FULL) qt.pin_all();
   if (tid < CR) BT[tid] = tid < p.nrow ? bt : 0.f;
 #pragma unroll
   for (int j = 0; j < IT::PER; ++j) {
@@ -482,10 +485,10 @@ __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __res
     }
     *reinterpret_cast<f32x4_t*>(R1 + t * LD + i0) = r1;
     *reinterpret_cast<f32x4_t*>(R2 + t * LD + i0) = r2;
-    *reinterpret_cast<f32x4_t*>(w + L::G + t * D + i0) = G;
+    if constexpr (FULL) *reinterpret_cast<f32x4_t*>(w + L::G + t * D + i0) = G;
     if constexpr (!BF) {   // bf16 inputs: only the bf16 copies are read
       *reinterpret_cast<f32x4_t*>(w + L::KT + t * D + i0) = ktv;
-    } else {
+    } else if constexpr (FULL) {
       bf16x4_t kb;
 #pragma unroll
       for (int i = 0; i < 4; ++i) kb[i] = static_cast<__bf16>(ktv[i]);
@@ -516,23 +519,25 @@ __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __res
   };
   pair_gram(S0, true);
   __syncthreads();
-  // q rowf into R1
+  if constexpr (FULL) {
+    // q rowf into R1
 #pragma unroll
-  for (int j = 0; j < IT::PER; ++j) {
-    const int e = tid + j * kOpsThreads, t = e / C4, i0 = (e - t * C4) * 4;
-    const f32x4_t G = *reinterpret_cast<const f32x4_t*>(R0 + t * LD + i0);
-    const f32x4_t RI = *reinterpret_cast<const f32x4_t*>(R0 + (t | 15) * LD + i0);
-    const f32x4_t qv = qt.get(j, p.nrow);
-    f32x4_t r1;
+    for (int j = 0; j < IT::PER; ++j) {
+      const int e = tid + j * kOpsThreads, t = e / C4, i0 = (e - t * C4) * 4;
+      const f32x4_t G = *reinterpret_cast<const f32x4_t*>(R0 + t * LD + i0);
+      const f32x4_t RI = *reinterpret_cast<const f32x4_t*>(R0 + (t | 15) * LD + i0);
+      const f32x4_t qv = qt.get(j, p.nrow);
+      f32x4_t r1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r1[i] = qv[i] * fexp(G[i] - RI[i]);
-    *reinterpret_cast<f32x4_t*>(R1 + t * LD + i0) = r1;
+      for (int i = 0; i < 4; ++i) r1[i] = qv[i] * fexp(G[i] - RI[i]);
+      *reinterpret_cast<f32x4_t*>(R1 + t * LD + i0) = r1;
+    }
+    __syncthreads();
+    pair_gram(S1, false);
+    __syncthreads();
+    l2g<kOpsThreads, CR, CR>(w + L::AP, CR, S0, LS);
+    l2g<kOpsThreads, CR, CR>(w + L::MP, CR, S1, LS);
   }
-  __syncthreads();
-  pair_gram(S1, false);
-  __syncthreads();
-  l2g<kOpsThreads, CR, CR>(w + L::AP, CR, S0, LS);
-  l2g<kOpsThreads, CR, CR>(w + L::MP, CR, S1, LS);
   if constexpr (BF) {   // Kt in R1 (free until k e^G goes there), for its bf16 transpose
 #pragma unroll
     for (int j = 0; j < IT::PER; ++j) {
@@ -581,17 +586,21 @@ __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __res
     }
     __syncthreads();
   }
-  for (int e = tid; e < CR * CR; e += kOpsThreads) {
-    const int t = e / CR, s = e - t * CR;
-    const float ti = S2[t * LS + s];
-    w[L::TI + e] = ti;
-    w[L::TB + e] = ti * BT[s];
-    if constexpr (BF) wb[L::BTB + e] = static_cast<__bf16>(ti * BT[s]);
+  if constexpr (FULL) {
+    for (int e = tid; e < CR * CR; e += kOpsThreads) {
+      const int t = e / CR, s = e - t * CR;
+      const float ti = S2[t * LS + s];
+      w[L::TI + e] = ti;
+      w[L::TB + e] = ti * BT[s];
+      if constexpr (BF) wb[L::BTB + e] = static_cast<__bf16>(ti * BT[s]);
+    }
   }
   if constexpr (BF) {   // Tb^T and Kt^T (consecutive threads take consecutive rows)
-    for (int e = tid; e < CR * CR; e += kOpsThreads) {
-      const int s = e / CR, t = e - s * CR;
-      wb[L::BTBT + e] = static_cast<__bf16>(S2[t * LS + s] * BT[s]);
+    if constexpr (FULL) {
+      for (int e = tid; e < CR * CR; e += kOpsThreads) {
+        const int s = e / CR, t = e - s * CR;
+        wb[L::BTBT + e] = static_cast<__bf16>(S2[t * LS + s] * BT[s]);
+      }
     }
     for (int e = tid; e < CR * D; e += kOpsThreads) {
       const int i = e / CR, t = e - i * CR;
@@ -604,21 +613,23 @@ __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __res
   for (int j = 0; j < IT::PER; ++j) {
     const int e = tid + j * kOpsThreads, t = e / C4, i0 = (e - t * C4) * 4;
     const f32x4_t G = *reinterpret_cast<const f32x4_t*>(R0 + t * LD + i0);
-    const f32x4_t kv = kt.get(j, p.nrow), qv = qt.get(j, p.nrow);
-    f32x4_t r1, r2;
+    const f32x4_t kv = kt.get(j, p.nrow);
+    f32x4_t r1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float eg = fexp(G[i]);
-      r1[i] = kv[i] * eg;
-      r2[i] = scale * qv[i] * eg;
-    }
+    for (int i = 0; i < 4; ++i) r1[i] = kv[i] * fexp(G[i]);
     *reinterpret_cast<f32x4_t*>(R1 + t * LD + i0) = r1;
-    *reinterpret_cast<f32x4_t*>(R2 + t * LD + i0) = r2;
+    if constexpr (FULL) {
+      const f32x4_t qv = qt.get(j, p.nrow);
+      f32x4_t r2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r2[i] = scale * qv[i] * fexp(G[i]);
+      *reinterpret_cast<f32x4_t*>(R2 + t * LD + i0) = r2;
+    }
   }
   __syncthreads();
 
   // P = scale M' Tb (into S0 and the workspace); W = Tb (k e^G)
-  for (int j = wave; j < 16; j += kOpsWaves) {
+  for (int j = wave; FULL && j < 16; j += kOpsWaves) {
     const int rt = j >> 2, ct = j & 3;
     f32x4_t acc = mmx<BF, false, false>(zero4(), S1 + 16 * rt * LS, LS, S2 + 16 * ct, LS, CR);
     const float f = scale * BT[16 * ct + l16];
@@ -636,9 +647,10 @@ __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __res
     if constexpr (!BF) put(w + L::W + 16 * rt * D + 16 * ct, D, acc);
     if constexpr (BF) {
       put_bf16(wb + L::BW + 16 * rt * D + 16 * ct, D, acc);
-      put_t_bf16(wb + L::BWT + 16 * ct * CR + 16 * rt, CR, acc);
+      if constexpr (FULL) put_t_bf16(wb + L::BWT + 16 * ct * CR + 16 * rt, CR, acc);
     }
   }
+  if constexpr (!FULL) return;
   __syncthreads();
   // Q' = scale q e^G - P (k e^G)
   for (int j = wave; j < 4 * CT; j += kOpsWaves) {

@@ -238,14 +238,14 @@ hipError_t launch_transition_t(const TransitionArgs& a) {
   __bf16* wsb = BF ? reinterpret_cast<__bf16*>(ws + items * L::WS) : nullptr;
   const int BH = a.B * a.H;
   if constexpr (BF) {   // bf16 operands, the prefill's precision
-    hipLaunchKernelGGL((chunk_ops_kernel<D, TIn, false>), dim3(items), dim3(kOpsThreads), 0,
+    hipLaunchKernelGGL((chunk_ops_kernel<D, TIn, false, false>), dim3(items), dim3(kOpsThreads), 0,
                        a.stream, static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
                        static_cast<const TIn*>(a.g), static_cast<const TIn*>(a.beta), ws, wsb, a.T,
                        a.H, nc, 1.0f);
     hipLaunchKernelGGL((transition_scan_bf16_kernel<D>), dim3(scan_grid(BH, D / SL)),
                        dim3(kScanThreads), 0, a.stream, ws, wsb, a.transition, nc, BH);
   } else {
-    hipLaunchKernelGGL((chunk_ops_kernel<D, TIn, true>), dim3(items), dim3(kOpsThreads), 0,
+    hipLaunchKernelGGL((chunk_ops_kernel<D, TIn, true, false>), dim3(items), dim3(kOpsThreads), 0,
                        a.stream, static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
                        static_cast<const TIn*>(a.g), static_cast<const TIn*>(a.beta), ws, nullptr,
                        a.T, a.H, nc, 1.0f);

@@ -212,9 +212,11 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, co
  * from its entry state for its outputs.
  *
  * kda_chunk_transition: P for each of B independent segments.
- *  q, k, g, beta   as for kda_chunk_fwd ([B, T, H, .], dtype), except that q, k
- *                  and g are read four elements at a time and must be 16-byte
- *                  aligned (else KDA_ERR_ALIGN); v is not needed.
+ *  k, g, beta      as for kda_chunk_fwd ([B, T, H, .], dtype), except that k and
+ *                  g are read four elements at a time and must be 16-byte
+ *                  aligned (else KDA_ERR_ALIGN).  The transition depends on
+ *                  neither q nor v: q is not read and may be NULL (if given, it
+ *                  must be 16-byte aligned); v is not an argument.
  *  transition      [B, H, dk, dk] fp32, required: the exit state of the segment
  *                  run with v = 0 from the identity, i.e. the product of its
  *                  per-token maps (I - beta_t k_t k_t^T) Diag(exp g_t), latest

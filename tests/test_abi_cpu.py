@@ -115,6 +115,10 @@ def test_argument_checks_precede_any_device_call(lib):
     args = list(ok)
     args[13] = vp(4098)                                                # fp32 state misaligned
     assert bw(*args, 1, 64, 1, 128, 128, 0.1, 0, None) == -5
+    for i in (0, 1, 2, 3, 6):   # q, k, v, g, grad_out are read 16 bytes at a time
+        args = list(ok)
+        args[i] = vp(4104)      # bf16-element aligned, not 16-byte aligned
+        assert bw(*args, 1, 64, 1, 128, 128, 0.1, 0, None) == -5
     tr = lib.kda_chunk_transition
     tr.argtypes = [vp] * 5 + [i32] * 6 + [vp]
     tr.restype = i32
@@ -123,6 +127,9 @@ def test_argument_checks_precede_any_device_call(lib):
     assert tr(p, p, p, p, p, 1, 64, 1, 128, 64, 0, None) == -3
     assert tr(p, p, p, p, p, 1, -1, 1, 128, 128, 0, None) == -2
     assert tr(p, p, p, p, vp(4098), 1, 64, 1, 128, 128, 0, None) == -5
+    assert tr(None, p, p, p, p, 1, 64, 1, 128, 128, 0, None) in (-6, -7)   # q is not read
+    assert tr(p, vp(4104), p, p, p, 1, 64, 1, 128, 128, 0, None) == -5     # k: 16 bytes
+    assert tr(p, p, vp(4104), p, p, 1, 64, 1, 128, 128, 0, None) == -5     # g: 16 bytes
     co = lib.kda_state_compose
     co.argtypes = [vp] * 4 + [i32] * 5 + [vp]
     co.restype = i32
