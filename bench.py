@@ -16,8 +16,12 @@ HBM bytes to its average duration.  The "prologue" object times the same prefill
 from raw activations through kda_chunk_fwd_prologue (gate and normalisation
 fused into the kernels' loads).  The "backward" object times kda_chunk_bwd (all
 gradients of the same prefill) and relates its dense matrix work to the bf16 and
-fp32 matrix peaks.  "cpu_baseline" times the fp64 CPU oracle on
-a bounded sample of the same workload.  One JSON line is printed.
+fp32 matrix peaks.  "snapshots" times the same prefill keeping the state every
+1024 tokens (kda_chunk_fwd_snapshots).  "context" times each step of the
+context-parallel schedule (segment prefill, kda_chunk_transition,
+kda_state_compose) at B=1, T=65536, H=32 in 8 segments, and the whole schedule
+on one GPU.  "cpu_baseline" times the fp64 CPU oracle on a bounded sample of the
+same workload.  One JSON line is printed.
 """
 from __future__ import annotations
 
@@ -125,6 +129,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-prologue", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-snapshots", action="store_true")
+    ap.add_argument("--no-context", action="store_true")
     ap.add_argument("--pmc-copy", action="store_true",
                     help="only run a plain 256 MiB copy (counter calibration)")
     args = ap.parse_args()
@@ -252,9 +258,38 @@ def main():
         del raw, pout, pfin
         torch.cuda.empty_cache()
 
+    def event_ms(fn, n):
+        """Mean duration of fn() on the stream over n calls after one warm-up call."""
+        fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / n
+
+    if not args.no_snapshots:
+        # the same prefill keeping the state every 1024 tokens (prefix-cache snapshots)
+        sset = kin.make_workload(w, device=dev)
+        snap_tokens = 1024
+        sms = event_ms(lambda: kda.kda_chunk_fwd_snapshots(
+            sset["q"], sset["k"], sset["v"], sset["g"], sset["beta"], scale,
+            sset["initial_state"], snapshot_tokens=snap_tokens), max(3, min(args.steps, 10)))
+        result["snapshots"] = {
+            "entry_point": "kda_chunk_fwd_snapshots", "workload": "prefill_4x4096",
+            "snapshot_tokens": snap_tokens, "snapshots_per_sequence": -(-T // snap_tokens),
+            "call_ms_avg": sms, "tokens_per_s": B * T / (sms / 1e3),
+            "vs_plain_prefill": sms / (kern_avg_s * 1e3),
+        }
+        del sset
+        torch.cuda.empty_cache()
+
     if not args.no_backward:
         # all gradients of the same prefill (kda_chunk_bwd): forward recomputed
-        # inside, fp32 arithmetic on the fp32 matrix cores
+        # inside; bf16 matrix-core operands with fp32 accumulation for bf16 inputs
         bset = kin.make_workload(w, device=dev)
         cot = kin.make_cotangents(B, T, H, d, d, dtype=w.dtype, seed=w.seed + 20, device=dev)
 
@@ -288,6 +323,37 @@ def main():
                                "the products over 32 or more terms, fp32 for the rest",
         }
         del bset, cot
+        torch.cuda.empty_cache()
+
+    if not args.no_context:
+        # context parallelism on one GPU, prefill_1x65536 in 8 segments of 8192 tokens:
+        # every step of the schedule, and the path one rank of eight would take
+        wc = kin.WORKLOADS["prefill_1x65536"]
+        cset = kin.make_workload(wc, device=dev)
+        Tc, nseg = cset["q"].shape[1], 8
+        seg = Tc // nseg
+        cq, ck, cv, cg, cb = (cset[x] for x in ("q", "k", "v", "g", "beta"))
+        sq, sk, sv, sg, sb = (x[:, :seg].contiguous() for x in (cq, ck, cv, cg, cb))
+        cscale = wc.scale_value()
+        single = event_ms(lambda: kda.kda_chunk_fwd(cq, ck, cv, cg, cb, cscale), 3)
+        seg_fwd = event_ms(lambda: kda.kda_chunk_fwd(sq, sk, sv, sg, sb, cscale), 5)
+        seg_tr = event_ms(lambda: kda.kda_chunk_transition(sq, sk, sg, sb), 5)
+        Pm = torch.randn((nseg, 1, wc.H, wc.dk, wc.dk), device=dev) * 0.01
+        Rm = torch.randn((nseg, 1, wc.H, wc.dk, wc.dv), device=dev)
+        comp = event_ms(lambda: kda.kda_state_compose(Pm, Rm), 5)
+        serial = event_ms(lambda: kda.chunk_fwd_context_parallel(cq, ck, cv, cg, cb, seg, cscale), 2)
+        result["context"] = {
+            "entry_points": "kda_chunk_transition, kda_state_compose (with kda_chunk_fwd)",
+            "workload": "prefill_1x65536 in 8 segments of 8192 tokens",
+            "single_pass_prefill_ms": single, "segment_prefill_ms": seg_fwd,
+            "segment_transition_ms": seg_tr, "compose_ms": comp,
+            "schedule_on_one_gpu_ms": serial,
+            "one_rank_of_8_path_ms": 2 * seg_fwd + seg_tr + comp,
+            "note": "one_rank_of_8_path_ms sums a rank's own steps (prefill, transition, "
+                    "compose, prefill from its entry state) and leaves out the all-gather "
+                    "of the 8 (transition, exit state) pairs, 4 MiB each",
+        }
+        del cset, sq, sk, sv, sg, sb, Pm, Rm
         torch.cuda.empty_cache()
 
     if not args.no_decode:
