@@ -162,27 +162,46 @@ def main():
     scale = w.scale_value()
     stream = torch.cuda.current_stream()
 
-    def step(i):
+    # one workspace, allocated before timing and reused by every call on this stream
+    # (kda_chunk_fwd_ws): the call then allocates and frees nothing
+    wsbuf = kda.chunk_fwd_workspace(sets[0]["q"], sets[0]["v"])
+
+    def step(i, workspace=wsbuf):
         s = sets[i % 2]
         kda.kda_chunk_fwd(s["q"], s["k"], s["v"], s["g"], s["beta"], scale,
-                          s["initial_state"], out=outs[i % 2], final_state=finals[i % 2])
+                          s["initial_state"], out=outs[i % 2], final_state=finals[i % 2],
+                          workspace=workspace)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    # one HIP event pair on the launch stream around the K timed steps: per-step
+    # events would put their own host cost between the calls
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(args.steps):
-        ev[i][0].record(stream)
         step(i)
-        ev[i][1].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = [a.elapsed_time(b) for a, b in ev]
-    kern_avg_s = sum(kern_ms) / len(kern_ms) / 1e3
+    kern_avg_s = ev0.elapsed_time(ev1) / args.steps / 1e3
+
+    # the same calls through the self-allocating entry point (kda_chunk_fwd), for context
+    for i in range(args.warmup):
+        step(i, None)
+    torch.cuda.synchronize()
+    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t1 = time.perf_counter()
+    ea.record(stream)
+    for i in range(args.steps):
+        step(i, None)
+    eb.record(stream)
+    torch.cuda.synchronize()
+    self_alloc_wall = (time.perf_counter() - t1) / args.steps
+    self_alloc_ms = ea.elapsed_time(eb) / args.steps
 
     tokens = B * T
     value = tokens * args.steps / wall
@@ -208,13 +227,20 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
                      "traffic": measured_traffic(),
-                     "kernel": "kda_chunk_fwd = 5 launches of prefill_group_kernel<128,32,bf16> "
+                     "kernel": "kda_chunk_fwd_ws = 5 launches of prefill_group_kernel<128,32,bf16> "
                                "(4 windows of 16 chunks: preparation of window k with the "
-                               "state scan of window k-1)",
+                               "state scan of window k-1); time per call from one HIP event "
+                               "pair around the timed steps",
                      "kernel_ms": kern_avg_s * 1e3, "algorithmic_bytes": nbytes,
                      "kernel_source_sha256": source_digest()},
         "prefill": {
-            "kernel_ms_avg": kern_avg_s * 1e3, "kernel_ms_min": min(kern_ms),
+            "entry_point": "kda_chunk_fwd_ws (caller workspace, "
+                           f"{wsbuf.numel() / 2**20:.0f} MiB)",
+            "kernel_ms_avg": kern_avg_s * 1e3,
+            "self_allocating_kda_chunk_fwd": {
+                "ms_per_call_events": self_alloc_ms, "ms_per_call_wall": self_alloc_wall * 1e3,
+                "note": "workspace from the library pool per call; hipFreeAsync blocks the "
+                        "host until the call's kernels ran, so the next call is enqueued late"},
             "token_heads_per_s": tokens * H / kern_avg_s,
             "tflops_tri": fl_tri / kern_avg_s / 1e12, "tflops_full": fl_full / kern_avg_s / 1e12,
             "mfma_frac_tri": fl_tri / kern_avg_s / 1e12 / BF16_MFMA_PEAK_TFLOPS,
@@ -223,7 +249,7 @@ def main():
                                "full = 8Cd + 6d^2 + C^2/3",
         },
     }
-    del sets, outs, finals
+    del sets, outs, finals, wsbuf
     torch.cuda.empty_cache()
 
     if not args.no_prologue:

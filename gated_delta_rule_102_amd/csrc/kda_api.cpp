@@ -9,6 +9,7 @@
 #include <initializer_list>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "kda_launch.h"
 
@@ -68,7 +69,51 @@ int check_prefill_ptrs(const void* q, const void* k, const void* v, const void* 
                      {v, 16, true}, {out, 16, true}, {s0, 4, false}, {sT, 4, false}});
 }
 
+// One workspace pool per device, created on first use and kept for the process.
+std::mutex g_pool_mu;
+hipMemPool_t g_pool[kMaxDevices];
+
+hipError_t device_pool(hipMemPool_t* out) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_pool_mu);
+  if (g_pool[dev] == nullptr) {
+    hipMemPoolProps props;
+    std::memset(&props, 0, sizeof(props));
+    props.allocType = hipMemAllocationTypePinned;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool = nullptr;
+    err = hipMemPoolCreate(&pool, &props);
+    if (err != hipSuccess) return err;
+    uint64_t keep = UINT64_MAX;
+    err = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+    if (err != hipSuccess) {
+      hipMemPoolDestroy(pool);
+      return err;
+    }
+    g_pool[dev] = pool;
+  }
+  *out = g_pool[dev];
+  return hipSuccess;
+}
+
 }  // namespace
+
+namespace kda {
+
+hipError_t ws_alloc(void** p, size_t bytes, hipStream_t stream) {
+  hipMemPool_t pool = nullptr;
+  const hipError_t err = device_pool(&pool);
+  if (err != hipSuccess) return err;
+  return hipMallocFromPoolAsync(p, bytes, pool, stream);
+}
+
+hipError_t ws_free(void* p, hipStream_t stream) { return hipFreeAsync(p, stream); }
+
+}  // namespace kda
 
 extern "C" {
 
@@ -84,6 +129,7 @@ const char* kda_status_string(int status) {
     case KDA_ERR_ALIGN: return "a pointer is not aligned as required";
     case KDA_ERR_HIP: return "the HIP runtime reported an error";
     case KDA_ERR_NO_DEVICE: return "the current device is not gfx950";
+    case KDA_ERR_WORKSPACE: return "the workspace is NULL, not 256-byte aligned or too small";
     default: return "unknown status";
   }
 }
@@ -104,6 +150,41 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
   if (rc != KDA_OK) return rc;
   kda::PrefillArgs a{q, k, v, g, beta, initial_state, out, final_state, nullptr,
                      B, T, B * T, H, dk, scale, dtype == KDA_F32, stream};
+  return kda::launch_prefill(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int dtype) {
+  if (check_common(dk, dv, H, dtype) != KDA_OK) return 0;
+  if (dtype == KDA_F32 && dk != 64) return 0;
+  if (B <= 0 || T <= 0) return 0;
+  if (static_cast<int64_t>(B) * T > INT32_MAX / 2) return 0;
+  if (static_cast<int64_t>(B) * H > (1 << 24)) return 0;
+  kda::PrefillArgs a{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                     B, T, B * T, H, dk, 1.f, dtype == KDA_F32, nullptr};
+  return kda::prefill_workspace_bytes(a);
+}
+
+int kda_chunk_fwd_ws(const void* q, const void* k, const void* v, const void* g,
+                     const void* beta, const float* initial_state, void* out,
+                     float* final_state, int B, int T, int H, int dk, int dv, float scale,
+                     int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int rc = check_common(dk, dv, H, dtype);
+  if (rc != KDA_OK) return rc;
+  if (dtype == KDA_F32 && dk != 64) return KDA_ERR_HEAD_DIM;
+  if (B <= 0 || T <= 0) return KDA_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * T > INT32_MAX / 2) return KDA_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * H > (1 << 24)) return KDA_ERR_SHAPE;
+  rc = check_prefill_ptrs(q, k, v, g, beta, initial_state, out, final_state, dtype);
+  if (rc != KDA_OK) return rc;
+  if (workspace == nullptr || !aligned(workspace, 256) ||
+      workspace_bytes < kda_chunk_fwd_workspace_size(B, T, H, dk, dv, dtype))
+    return KDA_ERR_WORKSPACE;
+  rc = check_device();
+  if (rc != KDA_OK) return rc;
+  kda::PrefillArgs a{q, k, v, g, beta, initial_state, out, final_state, nullptr,
+                     B, T, B * T, H, dk, scale, dtype == KDA_F32, stream};
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
   return kda::launch_prefill(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -1081,7 +1081,7 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
   const int64_t sdu = (BF ? 1 : 2) * (D * D + CR * D);
   const int64_t per = L::WS + sdu + (BF ? L::WSB / 2 : 0);
   float* buf = nullptr;
-  hipError_t err = hipMallocAsync(reinterpret_cast<void**>(&buf), items * per * sizeof(float), a.stream);
+  hipError_t err = ws_alloc(reinterpret_cast<void**>(&buf), items * per * sizeof(float), a.stream);
   if (err != hipSuccess) return err;
   float* ws = buf;
   float* sreg = ws + items * L::WS;   // S, dS, Delta, dU in the element type chosen above
@@ -1127,7 +1127,7 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
                        a.T, a.H, nc, a.scale);
   }
   err = hipGetLastError();
-  const hipError_t ferr = hipFreeAsync(buf, a.stream);
+  const hipError_t ferr = ws_free(buf, a.stream);
   return err != hipSuccess ? err : ferr;
 }
 

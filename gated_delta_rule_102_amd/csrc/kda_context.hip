@@ -233,7 +233,7 @@ hipError_t launch_transition_t(const TransitionArgs& a) {
   constexpr bool BF = IsBf16<TIn>::value;
   float* ws = nullptr;
   const int64_t per = L::WS + (BF ? L::WSB / 2 : 0);   // floats per chunk
-  hipError_t err = hipMallocAsync(reinterpret_cast<void**>(&ws), items * per * sizeof(float), a.stream);
+  hipError_t err = ws_alloc(reinterpret_cast<void**>(&ws), items * per * sizeof(float), a.stream);
   if (err != hipSuccess) return err;
   __bf16* wsb = BF ? reinterpret_cast<__bf16*>(ws + items * L::WS) : nullptr;
   const int BH = a.B * a.H;
@@ -253,7 +253,7 @@ hipError_t launch_transition_t(const TransitionArgs& a) {
                        a.stream, ws, a.transition, nc, BH);
   }
   err = hipGetLastError();
-  const hipError_t ferr = hipFreeAsync(ws, a.stream);
+  const hipError_t ferr = ws_free(ws, a.stream);
   return err != hipSuccess ? err : ferr;
 }
 

@@ -34,6 +34,8 @@ struct PrefillArgs {
   int snap_chunks = 0;         // snapshot every snap_chunks chunks (and at the end)
   int nsnap = 0;
   bool prologue = false;       // q, k, g, beta raw: normalise / gate in the kernel
+  void* workspace = nullptr;   // caller's workspace (null: the call allocates its own)
+  size_t workspace_bytes = 0;
 };
 
 struct BackwardArgs {
@@ -72,5 +74,14 @@ hipError_t launch_compose(const ComposeArgs& a);
 hipError_t launch_backward(const BackwardArgs& a);
 
 hipError_t launch_prefill(const PrefillArgs& a);
+// Workspace bytes launch_prefill needs for these arguments (0 if unsupported).
+size_t prefill_workspace_bytes(const PrefillArgs& a);
+
+// Stream-ordered workspace from the library's own memory pool on the current
+// device.  The pool keeps freed memory for reuse (its release threshold is the
+// maximum), so a free never waits for the stream to drain and the next call's
+// allocation of the same size is served from the pool.
+hipError_t ws_alloc(void** p, size_t bytes, hipStream_t stream);
+hipError_t ws_free(void* p, hipStream_t stream);
 
 }  // namespace kda

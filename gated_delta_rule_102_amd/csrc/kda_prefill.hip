@@ -1337,6 +1337,42 @@ inline int group_chunks(int nchunks) {
   return std::min(cg, nchunks);
 }
 
+// Workspace of a windowed call: two window buffers of slots (one if a single window
+// covers the sequences) and, with more than one window, the states carried between
+// windows.
+template <int D, typename TIn>
+size_t grouped_bytes(const PrefillArgs& a, int cg) {
+  using SL = Slot<D, std::is_same<TIn, float>::value>;
+  const int nchunks = (a.T + kC - 1) / kC;
+  const int windows = (nchunks + cg - 1) / cg;
+  const size_t wbytes = static_cast<size_t>(a.N) * cg * a.H * SL::BYTES;
+  const size_t sbytes = windows > 1 ? static_cast<size_t>(a.N) * a.H * D * D * 4 : 0;
+  return (windows > 1 ? 2 : 1) * wbytes + sbytes;
+}
+
+// Workspace of a two-kernel call: one slot for every chunk (see slot_base).
+template <int D, typename TIn>
+size_t all_chunks_bytes(const PrefillArgs& a) {
+  using SL = Slot<D, std::is_same<TIn, float>::value>;
+  const int64_t slots = (a.total_T + kC - 1) / kC + a.N;
+  return static_cast<size_t>(slots) * a.H * SL::BYTES;
+}
+
+// The caller's workspace when it passed one (too small: invalid value), else a
+// stream-ordered allocation that ws_release returns.
+hipError_t ws_acquire(const PrefillArgs& a, size_t bytes, char** p) {
+  if (a.workspace != nullptr) {
+    if (a.workspace_bytes < bytes) return hipErrorInvalidValue;
+    *p = static_cast<char*>(a.workspace);
+    return hipSuccess;
+  }
+  return ws_alloc(reinterpret_cast<void**>(p), bytes, a.stream);
+}
+
+hipError_t ws_release(const PrefillArgs& a, char* p) {
+  return a.workspace != nullptr ? hipSuccess : ws_free(p, a.stream);
+}
+
 template <int D, int DVS, typename TIn>
 hipError_t launch_grouped(const PrefillArgs& a, int cg) {
   constexpr bool F32 = std::is_same<TIn, float>::value;
@@ -1345,12 +1381,11 @@ hipError_t launch_grouped(const PrefillArgs& a, int cg) {
   const int nchunks = (a.T + kC - 1) / kC;
   const int windows = (nchunks + cg - 1) / cg;
   const size_t wbytes = static_cast<size_t>(a.N) * cg * a.H * SL::BYTES;
-  const size_t sbytes = windows > 1 ? static_cast<size_t>(a.N) * a.H * D * D * 4 : 0;
   const int nbuf = windows > 1 ? 2 : 1;
   char* ws = nullptr;
-  hipError_t err = hipMallocAsync(reinterpret_cast<void**>(&ws), nbuf * wbytes + sbytes, a.stream);
+  hipError_t err = ws_acquire(a, grouped_bytes<D, TIn>(a, cg), &ws);
   if (err != hipSuccess) return err;
-  float* sbuf = sbytes ? reinterpret_cast<float*>(ws + nbuf * wbytes) : nullptr;
+  float* sbuf = windows > 1 ? reinterpret_cast<float*>(ws + nbuf * wbytes) : nullptr;
   const int nscan = scan_grid<D, DVS>(a.N * a.H);
   const int items = a.N * cg * a.H;
   for (int k = 0; k <= windows && err == hipSuccess; ++k) {
@@ -1366,28 +1401,35 @@ hipError_t launch_grouped(const PrefillArgs& a, int cg) {
                        a.stream, gp);
     err = hipGetLastError();
   }
-  const hipError_t ferr = hipFreeAsync(ws, a.stream);
+  const hipError_t ferr = ws_release(a, ws);
   return err != hipSuccess ? err : ferr;
+}
+
+// Chunks per window of a fixed-length call; 0 selects the two-kernel schedule
+// (always used for varlen input).
+inline int prefill_cg(const PrefillArgs& a) {
+  return a.cu_seqlens == nullptr ? group_chunks((a.T + kC - 1) / kC) : 0;
+}
+
+template <int D, typename TIn>
+size_t workspace_bytes(const PrefillArgs& a) {
+  const int cg = prefill_cg(a);
+  return cg > 0 ? grouped_bytes<D, TIn>(a, cg) : all_chunks_bytes<D, TIn>(a);
 }
 
 template <int D, typename TIn>
 hipError_t launch_all(const PrefillArgs& a) {
-  constexpr bool F32 = std::is_same<TIn, float>::value;
-  using SL = Slot<D, F32>;
-  if (a.cu_seqlens == nullptr) {   // fixed length: windows of cg chunks
-    const int cg = group_chunks((a.T + kC - 1) / kC);
-    if (cg > 0) {
-      // slices of at most 32 columns keep the scan role within 256 registers, so a
-      // scan and a preparation workgroup fit on one CU together
-      if (a.N * a.H < 64) return launch_grouped<D, 16, TIn>(a, cg);
-      return launch_grouped<D, 32, TIn>(a, cg);
-    }
+  const int cg = prefill_cg(a);
+  if (cg > 0) {   // fixed length: windows of cg chunks
+    // slices of at most 32 columns keep the scan role within 256 registers, so a
+    // scan and a preparation workgroup fit on one CU together
+    if (a.N * a.H < 64) return launch_grouped<D, 16, TIn>(a, cg);
+    return launch_grouped<D, 32, TIn>(a, cg);
   }
   const SeqArgs sa{a.cu_seqlens, a.N, a.T, a.total_T, a.H};
   const int64_t slots = (a.total_T + kC - 1) / kC + a.N;
-  const size_t ws_bytes = static_cast<size_t>(slots) * a.H * SL::BYTES;
   char* ws = nullptr;
-  hipError_t err = hipMallocAsync(reinterpret_cast<void**>(&ws), ws_bytes, a.stream);
+  hipError_t err = ws_acquire(a, all_chunks_bytes<D, TIn>(a), &ws);
   if (err != hipSuccess) return err;
   const int64_t items = slots * a.H;
   PrepParams pp{a.q, a.k, a.g, a.beta, ws, sa, a.scale, static_cast<int>(items), 0, 0,
@@ -1408,11 +1450,17 @@ hipError_t launch_all(const PrefillArgs& a) {
     else if (streams < 64) err = launch_scan<D, 16, TIn>(a, sa, ws);
     else err = launch_scan<D, 32, TIn>(a, sa, ws);
   }
-  const hipError_t ferr = hipFreeAsync(ws, a.stream);
+  const hipError_t ferr = ws_release(a, ws);
   return err != hipSuccess ? err : ferr;
 }
 
 }  // namespace
+
+size_t prefill_workspace_bytes(const PrefillArgs& a) {
+  if (a.dtype_f32) return a.d == 64 ? workspace_bytes<64, float>(a) : 0;
+  if (a.d == 128) return workspace_bytes<128, bf16_t>(a);
+  return workspace_bytes<64, bf16_t>(a);
+}
 
 hipError_t launch_prefill(const PrefillArgs& a) {
   if (a.dtype_f32) {

@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 KDA_BF16, KDA_F32 = 0, 1
 _lib = None
 
-EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd", "kda_chunk_fwd_prologue",
+EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
+           "kda_chunk_fwd_ws", "kda_chunk_fwd_prologue",
            "kda_chunk_fwd_snapshots", "kda_chunk_fwd_varlen", "kda_decode_step", "kda_chunk_bwd",
            "kda_chunk_transition", "kda_state_compose")
 
@@ -49,6 +50,11 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                   f32, i32, vp]
     lib.kda_chunk_fwd.restype = i32
+    lib.kda_chunk_fwd_workspace_size.argtypes = [i32] * 6
+    lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_size_t
+    lib.kda_chunk_fwd_ws.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                     f32, i32, vp, ctypes.c_size_t, vp]
+    lib.kda_chunk_fwd_ws.restype = i32
     lib.kda_chunk_fwd_prologue.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                            i32, f32, i32, vp]
     lib.kda_chunk_fwd_prologue.restype = i32
@@ -121,12 +127,39 @@ def _raise(fn, rc):
         raise KDAError(fn, rc)
 
 
+def kda_chunk_fwd_workspace_size(B, T, H, dk, dv, dtype=torch.bfloat16) -> int:
+    """Workspace bytes kda_chunk_fwd_ws needs for these sizes (0: sizes not accepted)."""
+    code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32 if dtype == torch.float32 else -1
+    return int(load_library().kda_chunk_fwd_workspace_size(B, T, H, dk, dv, code))
+
+
+def chunk_fwd_workspace(q, v):
+    """A uint8 device tensor large enough to serve as the workspace of prefill calls
+    shaped like (q, v); allocated once and passed as ``workspace=`` to kda_chunk_fwd."""
+    B, T, H, dk = q.shape
+    n = kda_chunk_fwd_workspace_size(B, T, H, dk, v.shape[-1], q.dtype)
+    if n == 0:
+        raise ValueError("prefill sizes not accepted by the library")
+    return torch.empty(n + 256, dtype=torch.uint8, device=q.device)
+
+
+def kda_chunk_fwd_ws(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=True,
+                     out=None, final_state=None, workspace=None):
+    """kda_chunk_fwd on a caller-owned workspace (``chunk_fwd_workspace``)."""
+    if workspace is None:
+        raise ValueError("kda_chunk_fwd_ws needs a workspace tensor")
+    return kda_chunk_fwd(q, k, v, g, beta, scale, initial_state, output_final_state, out,
+                         final_state, workspace=workspace)
+
+
 def kda_chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=True,
-                  out=None, final_state=None):
+                  out=None, final_state=None, workspace=None):
     """Chunked prefill.  q, k, g: [B,T,H,dk]; v: [B,T,H,dv]; beta: [B,T,H].
 
     Returns ``(out [B,T,H,dv], final_state [B,H,dk,dv] fp32 or None)``.
     ``final_state`` may be passed (and may be ``initial_state`` for in-place use).
+    With ``workspace`` (a device uint8 tensor from ``chunk_fwd_workspace``) the call
+    goes to kda_chunk_fwd_ws and allocates nothing; without it, to kda_chunk_fwd.
     """
     lib = load_library()
     B, T, H, dk = q.shape
@@ -144,6 +177,19 @@ def kda_chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final
         final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=device)
     _check_state("final_state", final_state, (B, H, dk, dv), device)
     scale = 1.0 / math.sqrt(dk) if scale is None else float(scale)
+    if workspace is not None:
+        if workspace.device != device or workspace.dtype != torch.uint8:
+            raise ValueError(f"workspace must be a uint8 tensor on {device}")
+        # the library wants 256-byte alignment; chunk_fwd_workspace leaves 256 B of slack
+        base = workspace.data_ptr()
+        off = (-base) % 256
+        nbytes = workspace.numel() - off
+        rc = lib.kda_chunk_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                  _ptr(initial_state), _ptr(out), _ptr(final_state), B, T, H, dk,
+                                  dv, scale, _dtype_code(q), ctypes.c_void_p(base + off),
+                                  max(nbytes, 0), _stream(q))
+        _raise("kda_chunk_fwd_ws", rc)
+        return out, final_state
     rc = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
                            _ptr(out), _ptr(final_state), B, T, H, dk, dv, scale,
                            _dtype_code(q), _stream(q))

@@ -25,11 +25,16 @@
  *
  * Conventions shared by every entry point
  *  - All tensor pointers are DEVICE pointers owned by the caller, contiguous and
- *    row-major.  The prefill entry points allocate one workspace per call with
- *    hipMallocAsync on `stream` and release it with hipFreeAsync on the same
- *    stream (66,048 bytes per 64-token chunk per head for bf16 at d = 128;
- *    chunks counted per sequence); an allocation failure returns KDA_ERR_HIP.
- *    Decode allocates nothing.
+ *    row-major.  The prefill, backward and transition entry points take one
+ *    stream-ordered workspace per call from a memory pool the library creates on
+ *    each device it runs on (hipMallocFromPoolAsync on `stream`, returned with
+ *    hipFreeAsync on the same stream; the pool keeps freed memory for later
+ *    calls until the process ends).  Prefill needs 66,048 bytes per 64-token
+ *    chunk per head for bf16 at d = 128 (kda_chunk_fwd_workspace_size gives the
+ *    exact figure); an allocation failure returns KDA_ERR_HIP.  On ROCm 7
+ *    hipFreeAsync blocks the host until the call's kernels have run, so a caller
+ *    that enqueues calls back to back passes its own workspace to
+ *    kda_chunk_fwd_ws instead.  Decode allocates nothing.
  *  - Alignment (KDA_ERR_ALIGN otherwise): prefill v and out 16 bytes, q, k, g and
  *    the states 4 bytes, beta its element size; decode state 16 bytes, every
  *    other pointer its element size.
@@ -59,7 +64,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 enum kda_dtype { KDA_BF16 = 0, KDA_F32 = 1 };
 
@@ -72,7 +77,8 @@ enum kda_status {
   KDA_ERR_DTYPE = -4,       /* dtype is not KDA_BF16 or KDA_F32              */
   KDA_ERR_ALIGN = -5,       /* a pointer is not aligned as required          */
   KDA_ERR_HIP = -6,         /* the HIP runtime reported a launch error       */
-  KDA_ERR_NO_DEVICE = -7    /* the current device is not gfx950              */
+  KDA_ERR_NO_DEVICE = -7,   /* the current device is not gfx950              */
+  KDA_ERR_WORKSPACE = -8    /* workspace NULL, misaligned or too small       */
 };
 
 /* ABI version of the loaded library (KDA_ABI_VERSION). */
@@ -99,6 +105,28 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
                   const void* beta, const float* initial_state, void* out,
                   float* final_state, int B, int T, int H, int dk, int dv,
                   float scale, int dtype, hipStream_t stream);
+
+/*
+ * Bytes of workspace kda_chunk_fwd_ws needs for these sizes (the same schedule
+ * kda_chunk_fwd runs), or 0 when the sizes or dtype are not accepted by
+ * kda_chunk_fwd.  Pure host arithmetic: no device call.
+ */
+size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int dtype);
+
+/*
+ * kda_chunk_fwd on a workspace the caller owns, so the call allocates and frees
+ * nothing and returns as soon as its kernels are enqueued.
+ *  workspace        device memory of at least kda_chunk_fwd_workspace_size(B, T,
+ *                   H, dk, dv, dtype) bytes, 256-byte aligned; its contents on
+ *                   entry do not matter and are garbage on exit.  Calls that may
+ *                   overlap (other streams) need distinct workspaces.
+ *  workspace_bytes  its size; NULL, misaligned or too small -> KDA_ERR_WORKSPACE.
+ * Every other argument, and every result, is exactly as for kda_chunk_fwd.
+ */
+int kda_chunk_fwd_ws(const void* q, const void* k, const void* v, const void* g,
+                     const void* beta, const float* initial_state, void* out,
+                     float* final_state, int B, int T, int H, int dk, int dv, float scale,
+                     int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * kda_chunk_fwd with the gate and normalisation prologue fused into the kernels'

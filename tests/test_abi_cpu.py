@@ -32,7 +32,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
-        "kda_abi_version", "kda_status_string", "kda_chunk_fwd", "kda_chunk_fwd_prologue",
+        "kda_abi_version", "kda_status_string", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
+        "kda_chunk_fwd_ws", "kda_chunk_fwd_prologue",
         "kda_chunk_fwd_snapshots", "kda_chunk_fwd_varlen", "kda_decode_step", "kda_chunk_bwd",
         "kda_chunk_transition", "kda_state_compose"])
 
@@ -49,8 +50,8 @@ def test_library_exports_every_declared_symbol(lib):
 def test_version_and_status_strings(lib):
     lib.kda_abi_version.restype = ctypes.c_int
     lib.kda_status_string.restype = ctypes.c_char_p
-    assert lib.kda_abi_version() == 1
-    for code in range(-7, 1):
+    assert lib.kda_abi_version() == 2
+    for code in range(-8, 1):
         assert lib.kda_status_string(code)
     assert lib.kda_status_string(-99) == b"unknown status"
 
@@ -71,6 +72,16 @@ def test_argument_checks_precede_any_device_call(lib):
     assert f(mis, p, p, p, p, None, p, None, 1, 64, 1, 128, 128, 0.1, 0, None) == -5
     # valid arguments reach the device check, which fails without a gfx950 device
     assert f(p, p, p, p, p, None, p, None, 1, 64, 1, 128, 128, 0.1, 0, None) in (-6, -7)
+    ws = lib.kda_chunk_fwd_ws
+    ws.argtypes = [vp] * 8 + [i32] * 5 + [f32, i32, vp, ctypes.c_size_t, vp]
+    ws.restype = i32
+    big = 1 << 40
+    assert ws(p, p, p, p, p, None, p, None, 1, 64, 1, 100, 100, 0.1, 0, p, big, None) == -3
+    assert ws(p, p, p, p, p, None, p, None, 1, 64, 1, 128, 128, 0.1, 0, None, big, None) == -8
+    assert ws(p, p, p, p, p, None, p, None, 1, 64, 1, 128, 128, 0.1, 0, vp(4096 + 16), big,
+              None) == -8
+    assert ws(p, p, p, p, p, None, p, None, 1, 64, 1, 128, 128, 0.1, 0, p, 1024, None) == -8
+    assert ws(p, p, p, p, p, None, p, None, 1, 64, 1, 128, 128, 0.1, 0, p, big, None) in (-6, -7)
     d = lib.kda_decode_step
     d.argtypes = [vp] * 7 + [i32] * 4 + [f32, i32, vp]
     d.restype = i32
@@ -149,3 +160,18 @@ def test_binding_fails_loudly_without_library(tmp_path):
             kda.load_library(str(tmp_path / "missing.so"))
     finally:
         kda._lib = saved
+
+
+def test_workspace_size_is_host_arithmetic(lib):
+    """kda_chunk_fwd_workspace_size needs no device and follows the slot layout: 66,048
+    bytes per (chunk, head) for bf16 at d = 128 in two windows of 16 chunks plus the
+    carried fp32 states for B=4, T=4096, H=16; one slot per chunk for T=64."""
+    f = lib.kda_chunk_fwd_workspace_size
+    f.argtypes = [ctypes.c_int] * 6
+    f.restype = ctypes.c_size_t
+    assert f(4, 4096, 16, 128, 128, 0) == 2 * 4 * 16 * 16 * 66048 + 4 * 16 * 128 * 128 * 4
+    assert f(2, 64, 3, 128, 128, 0) == 2 * 3 * 66048
+    assert f(1, 64, 1, 128, 128, 1) == 0     # fp32 prefill is d = 64 only
+    assert f(1, 64, 1, 100, 100, 0) == 0
+    assert f(0, 64, 1, 128, 128, 0) == 0
+    assert f(1, 64, 1, 64, 64, 1) > 0

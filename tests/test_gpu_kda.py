@@ -343,3 +343,48 @@ def test_prefill_several_windows_small():
     d = kin.make_prefill(2, 2100, 2, 128, 128, dtype=torch.bfloat16, seed=77, nonzero_state=True)
     d["scale"] = 1.0 / math.sqrt(128)
     _compare_fixed(d, "3 windows")
+
+
+# ------------------------------------------------------------ caller workspace
+
+
+@pytest.mark.parametrize("B,T,H,D,dtype", [(2, 150, 3, 128, torch.bfloat16),
+                                           (1, 2100, 4, 128, torch.bfloat16),
+                                           (4, 4096, 16, 128, torch.bfloat16),
+                                           (1, 300, 2, 64, torch.float32)])
+def test_workspace_entry_point_equals_self_allocating(B, T, H, D, dtype):
+    """kda_chunk_fwd_ws on a caller workspace runs the same kernels as kda_chunk_fwd:
+    bitwise-equal outputs and states (one window, several windows with a ragged last
+    one, the bench workload, fp32), also when the workspace held garbage and when
+    two calls reuse it back to back; the first call is also checked against the
+    oracle on the small cases."""
+    from gated_delta_rule_102_amd import kda
+    d = kin.make_prefill(B, T, H, D, D, dtype=dtype, seed=31 + T, nonzero_state=True)
+    d["scale"] = 1.0 / math.sqrt(D)
+    g = _to(d, DEV)
+    args = (g["q"], g["k"], g["v"], g["g"], g["beta"])
+    ref_out, ref_fs = kda.kda_chunk_fwd(*args, scale=d["scale"], initial_state=g["initial_state"])
+    ws = kda.chunk_fwd_workspace(g["q"], g["v"])
+    ws.fill_(0xA5)
+    for rep in range(2):
+        out, fs = kda.kda_chunk_fwd(*args, scale=d["scale"], initial_state=g["initial_state"],
+                                    workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out), f"rep {rep}: out differs from kda_chunk_fwd"
+        assert torch.equal(fs, ref_fs), f"rep {rep}: final state differs from kda_chunk_fwd"
+    if B * T * H <= 4 * 2100:
+        o_ref, s_ref = oracle_fixed(d)
+        assert_close("ws out", out, o_ref.reshape(out.shape), dtype)
+        assert_close("ws state", fs, s_ref.reshape(fs.shape), dtype)
+
+
+def test_workspace_too_small_is_rejected():
+    from gated_delta_rule_102_amd import kda
+    d = kin.make_prefill(1, 128, 2, 128, 128, dtype=torch.bfloat16, seed=3)
+    g = _to(d, DEV)
+    need = kda.kda_chunk_fwd_workspace_size(1, 128, 2, 128, 128, torch.bfloat16)
+    assert need > 0
+    small = torch.empty(need // 2, dtype=torch.uint8, device=DEV)
+    with pytest.raises(kda.KDAError) as e:
+        kda.kda_chunk_fwd(g["q"], g["k"], g["v"], g["g"], g["beta"], workspace=small)
+    assert e.value.status == -8
