@@ -49,8 +49,9 @@
  *    |k| <= 1.  Outside them the result is unspecified (never a memory fault).
  *  - Work is enqueued on `stream` and returns immediately; execution errors
  *    surface at the caller's next synchronisation.  No entry point keeps state
- *    between calls, so calls on different streams may overlap when their
- *    buffers do not.
+ *    between calls other than the workspace pool above (stream-ordered, so
+ *    calls on different streams never share a live workspace); calls on
+ *    different streams may overlap when their buffers do not.
  *  - Return value: KDA_OK, or a negative KDA_ERR_* code.  When a code other
  *    than KDA_OK is returned nothing was launched.
  */
