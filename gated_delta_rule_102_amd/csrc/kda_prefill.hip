@@ -1322,13 +1322,19 @@ hipError_t launch_scan(const PrefillArgs& a, const SeqArgs& sa, const char* ws) 
   return hipGetLastError();
 }
 
-// Chunks per window of the grouped launch (KDA_GROUP_CHUNKS overrides it for tuning
-// runs; 0 selects the two-kernel schedule).
-inline int group_chunks(int nchunks) {
+// KDA_GROUP_CHUNKS overrides the window size for tuning runs (0 selects the
+// two-kernel schedule); -1 when it is not set.
+inline int forced_group_chunks() {
   static const int forced = [] {
     const char* e = std::getenv("KDA_GROUP_CHUNKS");
     return e ? std::atoi(e) : -1;
   }();
+  return forced;
+}
+
+// Chunks per window of the grouped launch.
+inline int group_chunks(int nchunks) {
+  const int forced = forced_group_chunks();
   if (forced >= 0) return forced == 0 ? 0 : std::min(forced, nchunks);
   // at most 8 windows (each launch boundary drains the machine) and at least 16
   // chunks per window (the scan role needs enough steps to amortise its state
@@ -1405,10 +1411,18 @@ hipError_t launch_grouped(const PrefillArgs& a, int cg) {
   return err != hipSuccess ? err : ferr;
 }
 
+// Streams from which the two-kernel schedule with 64-column scan slices is used:
+// 2 workgroups per stream then still cover the 256 CUs, and every chunk's operands
+// are read by 2 workgroups instead of 4 (a CU takes in operands at a fixed rate, so
+// the scan's time follows the operand bytes each CU moves).
+constexpr int kWideStreams = 128;
+
 // Chunks per window of a fixed-length call; 0 selects the two-kernel schedule
-// (always used for varlen input).
+// (always used for varlen input and from kWideStreams streams on).
 inline int prefill_cg(const PrefillArgs& a) {
-  return a.cu_seqlens == nullptr ? group_chunks((a.T + kC - 1) / kC) : 0;
+  if (a.cu_seqlens != nullptr) return 0;
+  const int cg = group_chunks((a.T + kC - 1) / kC);
+  return forced_group_chunks() < 0 && a.N * a.H >= kWideStreams ? 0 : cg;
 }
 
 template <int D, typename TIn>
@@ -1448,7 +1462,8 @@ hipError_t launch_all(const PrefillArgs& a) {
     else if (forced == 32) err = launch_scan<D, 32, TIn>(a, sa, ws);
     else if (forced == 64) err = launch_scan<D, 64, TIn>(a, sa, ws);
     else if (streams < 64) err = launch_scan<D, 16, TIn>(a, sa, ws);
-    else err = launch_scan<D, 32, TIn>(a, sa, ws);
+    else if (streams < kWideStreams) err = launch_scan<D, 32, TIn>(a, sa, ws);
+    else err = launch_scan<D, 64, TIn>(a, sa, ws);
   }
   const hipError_t ferr = ws_release(a, ws);
   return err != hipSuccess ? err : ferr;

@@ -133,6 +133,17 @@ def test_prefill_fp32_ragged(T):
     _compare_fixed(d, f"fp32 T={T}")
 
 
+@pytest.mark.parametrize("B,T,H,D,dtype", [(8, 200, 16, 128, torch.bfloat16),
+                                           (4, 65, 40, 128, torch.bfloat16),
+                                           (8, 130, 16, 64, torch.float32)])
+def test_prefill_many_streams(B, T, H, D, dtype):
+    """128 and more (sequence, head) streams: the two-kernel schedule with 64-column
+    scan slices (whole states at d = 64), ragged tails, nonzero initial state."""
+    d = kin.make_prefill(B, T, H, D, D, dtype=dtype, seed=300 + T, nonzero_state=True)
+    d["scale"] = 1.0 / math.sqrt(D)
+    _compare_fixed(d, f"{B}x{T}x{H} D={D} {dtype}")
+
+
 @pytest.mark.parametrize("mode", ["floor", "slow"])
 def test_prefill_decay_extremes(mode):
     """g = -5 everywhere (the bound: sub-tile factors reach e^80) and g in

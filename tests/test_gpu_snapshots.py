@@ -51,7 +51,15 @@ def _prefix(d, t):
                                          (1100, 256, 64, torch.bfloat16),
                                          (190, 64, 64, torch.float32)])
 def test_snapshots_match_oracle_on_prefixes(T, S, D, dtype):
-    B, H = 2, 3
+    _check_snapshots(2, 3, T, S, D, dtype)
+
+
+def test_snapshots_many_streams():
+    """128 streams: snapshots from the two-kernel schedule's 64-column slices."""
+    _check_snapshots(8, 16, 200, 64, 128, torch.bfloat16)
+
+
+def _check_snapshots(B, H, T, S, D, dtype):
     d = kin.make_prefill(B, T, H, D, D, dtype=dtype, seed=31 + T, nonzero_state=True)
     d["scale"] = 1.0 / math.sqrt(D)
     out, fs, snaps, out2, fs2 = _run(d, S)
