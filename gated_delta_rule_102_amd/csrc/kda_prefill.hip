@@ -1436,8 +1436,9 @@ hipError_t launch_all(const PrefillArgs& a) {
   const int cg = prefill_cg(a);
   if (cg > 0) {   // fixed length: windows of cg chunks
     // slices of at most 32 columns keep the scan role within 256 registers, so a
-    // scan and a preparation workgroup fit on one CU together
-    if (a.N * a.H < 64) return launch_grouped<D, 16, TIn>(a, cg);
+    // scan and a preparation workgroup fit on one CU together; 16-column slices
+    // only for fewer than 32 streams, where the scan's own latency dominates
+    if (a.N * a.H < 32) return launch_grouped<D, 16, TIn>(a, cg);
     return launch_grouped<D, 32, TIn>(a, cg);
   }
   const SeqArgs sa{a.cu_seqlens, a.N, a.T, a.total_T, a.H};

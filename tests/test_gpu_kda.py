@@ -133,6 +133,17 @@ def test_prefill_fp32_ragged(T):
     _compare_fixed(d, f"fp32 T={T}")
 
 
+@pytest.mark.parametrize("B,T,H,D,dtype", [(2, 1100, 16, 128, torch.bfloat16),
+                                           (1, 1100, 40, 64, torch.bfloat16),
+                                           (2, 1100, 16, 64, torch.float32)])
+def test_prefill_windows_32_streams(B, T, H, D, dtype):
+    """32 to 127 streams over two windows (the second ragged): the windowed schedule
+    with 32-column scan slices, both head sizes and dtypes."""
+    d = kin.make_prefill(B, T, H, D, D, dtype=dtype, seed=400 + H, nonzero_state=True)
+    d["scale"] = 1.0 / math.sqrt(D)
+    _compare_fixed(d, f"{B}x{T}x{H} D={D} {dtype}")
+
+
 @pytest.mark.parametrize("B,T,H,D,dtype", [(8, 200, 16, 128, torch.bfloat16),
                                            (4, 65, 40, 128, torch.bfloat16),
                                            (8, 130, 16, 64, torch.float32)])
