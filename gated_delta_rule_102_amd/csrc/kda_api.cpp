@@ -255,6 +255,52 @@ int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void
   return kda::launch_prefill(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+int kda_chunk_fwd_varlen_prologue(const void* q_raw, const void* k_raw, const void* v,
+                                  const void* g_raw, const void* beta_raw,
+                                  const float* initial_state, void* out, float* final_state,
+                                  const int32_t* cu_seqlens, int N, int total_T, int H, int dk,
+                                  int dv, float scale, int dtype, hipStream_t stream) {
+  int rc = check_common(dk, dv, H, dtype);
+  if (rc != KDA_OK) return rc;
+  if (dtype == KDA_F32 && dk != 64) return KDA_ERR_HEAD_DIM;
+  if (N <= 0 || total_T <= 0 || total_T > INT32_MAX / 2) return KDA_ERR_SHAPE;
+  if (static_cast<int64_t>(N) * H > (1 << 24)) return KDA_ERR_SHAPE;
+  if (cu_seqlens == nullptr) return KDA_ERR_NULL;
+  rc = check_prefill_ptrs(q_raw, k_raw, v, g_raw, beta_raw, initial_state, out, final_state, dtype);
+  if (rc == KDA_OK && !aligned(cu_seqlens, 4)) rc = KDA_ERR_ALIGN;
+  if (rc != KDA_OK) return rc;
+  rc = check_device();
+  if (rc != KDA_OK) return rc;
+  kda::PrefillArgs a{q_raw, k_raw, v, g_raw, beta_raw, initial_state, out, final_state, cu_seqlens,
+                     N, 0, total_T, H, dk, scale, dtype == KDA_F32, stream};
+  a.prologue = true;
+  return kda::launch_prefill(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_chunk_fwd_varlen_snapshots(const void* q, const void* k, const void* v, const void* g,
+                                   const void* beta, const float* initial_state, void* out,
+                                   float* final_state, float* snapshots, int snapshot_tokens,
+                                   const int32_t* cu_seqlens, int N, int total_T, int H, int dk,
+                                   int dv, float scale, int dtype, hipStream_t stream) {
+  int rc = check_common(dk, dv, H, dtype);
+  if (rc != KDA_OK) return rc;
+  if (dtype == KDA_F32 && dk != 64) return KDA_ERR_HEAD_DIM;
+  if (N <= 0 || total_T <= 0 || total_T > INT32_MAX / 2) return KDA_ERR_SHAPE;
+  if (static_cast<int64_t>(N) * H > (1 << 24)) return KDA_ERR_SHAPE;
+  if (snapshot_tokens <= 0 || snapshot_tokens % 64 != 0) return KDA_ERR_SHAPE;
+  if (cu_seqlens == nullptr || snapshots == nullptr) return KDA_ERR_NULL;
+  rc = check_prefill_ptrs(q, k, v, g, beta, initial_state, out, final_state, dtype);
+  if (rc == KDA_OK && (!aligned(cu_seqlens, 4) || !aligned(snapshots, 4))) rc = KDA_ERR_ALIGN;
+  if (rc != KDA_OK) return rc;
+  rc = check_device();
+  if (rc != KDA_OK) return rc;
+  kda::PrefillArgs a{q, k, v, g, beta, initial_state, out, final_state, cu_seqlens,
+                     N, 0, total_T, H, dk, scale, dtype == KDA_F32, stream};
+  a.snapshots = snapshots;
+  a.snap_chunks = snapshot_tokens / 64;
+  return kda::launch_prefill(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
                   const float* initial_state, const void* grad_out,
                   const float* grad_final_state, void* grad_q, void* grad_k, void* grad_v,

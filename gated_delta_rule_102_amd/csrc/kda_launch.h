@@ -30,7 +30,8 @@ struct PrefillArgs {
   float scale;
   bool dtype_f32;
   hipStream_t stream;
-  float* snapshots = nullptr;  // fixed length only: [N, H, nsnap, d, d] or null
+  float* snapshots = nullptr;  // [N, H, nsnap, d, d] (fixed length), [sum_n nsnap_n, H, d, d]
+                               // (varlen), or null
   int snap_chunks = 0;         // snapshot every snap_chunks chunks (and at the end)
   int nsnap = 0;
   bool prologue = false;       // q, k, g, beta raw: normalise / gate in the kernel

@@ -1034,6 +1034,27 @@ __device__ __forceinline__ void scan_body(const ScanParams& p, char* smem, const
   if (c_begin >= c_end && c_begin > 0) return;   // the sequence ended in an earlier window
   const int sbase = p.cg > 0 ? n * p.cg - p.c_lo : slot_base(tok0, n);
   const int j0 = split * DVS;
+
+  // Snapshot i of this (sequence, head): fixed length, [N, H, nsnap] order; varlen,
+  // row off_n + i of [snapshots, H], where off_n counts the snapshots of the
+  // sequences before n (ceil(chunks / snap_chunks) each), summed over the lanes.
+  int snap_off = 0, nsnap_n = p.nsnap;
+  if (p.snap != nullptr && p.sa.cu != nullptr) {
+    int part = 0;
+    for (int m = lane; m < n; m += 64) {
+      int t0m, lm;
+      seq_bounds(p.sa, m, t0m, lm);
+      part += ((lm + kC - 1) / kC + p.snap_chunks - 1) / p.snap_chunks;
+    }
+    for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o);
+    snap_off = part;
+    nsnap_n = (nchunks + p.snap_chunks - 1) / p.snap_chunks;
+  }
+  auto snap_ptr = [&](int si) -> float* {
+    return p.sa.cu != nullptr
+               ? p.snap + (static_cast<int64_t>(snap_off + si) * H + h) * D * D
+               : p.snap + ((static_cast<int64_t>(n) * H + h) * p.nsnap + si) * D * D;
+  };
   const float* s_in = c_begin == 0 ? p.s0 : p.sbuf;
   float* s_out = p.c_hi >= nchunks ? p.sT : p.sbuf;
 
@@ -1242,8 +1263,7 @@ __device__ __forceinline__ void scan_body(const ScanParams& p, char* smem, const
     }
     if (p.snap != nullptr && (ci + 1 == nchunks || (ci + 1) % p.snap_chunks == 0)) {
       // state after chunk ci: a prefix-cache snapshot
-      const int si = ci + 1 == nchunks ? p.nsnap - 1 : (ci + 1) / p.snap_chunks - 1;
-      store_state(p.snap + ((static_cast<int64_t>(n) * H + h) * p.nsnap + si) * D * D);
+      store_state(snap_ptr(ci + 1 == nchunks ? nsnap_n - 1 : (ci + 1) / p.snap_chunks - 1));
     }
     __syncthreads();
   };

@@ -21,7 +21,8 @@ KDA_BF16, KDA_F32 = 0, 1
 _lib = None
 
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
-           "kda_chunk_fwd_ws", "kda_chunk_fwd_prologue",
+           "kda_chunk_fwd_ws", "kda_chunk_fwd_prologue", "kda_chunk_fwd_varlen_prologue",
+           "kda_chunk_fwd_varlen_snapshots",
            "kda_chunk_fwd_snapshots", "kda_chunk_fwd_varlen", "kda_decode_step", "kda_chunk_bwd",
            "kda_chunk_transition", "kda_state_compose")
 
@@ -64,6 +65,12 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
                                          i32, i32, f32, i32, vp]
     lib.kda_chunk_fwd_varlen.restype = i32
+    lib.kda_chunk_fwd_varlen_prologue.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,
+                                                  i32, i32, i32, f32, i32, vp]
+    lib.kda_chunk_fwd_varlen_prologue.restype = i32
+    lib.kda_chunk_fwd_varlen_snapshots.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
+                                                   i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.kda_chunk_fwd_varlen_snapshots.restype = i32
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp]
     lib.kda_decode_step.restype = i32
     lib.kda_chunk_bwd.argtypes = [vp] * 14 + [i32, i32, i32, i32, i32, f32, i32, vp]
@@ -261,11 +268,8 @@ def kda_chunk_fwd_snapshots(q, k, v, g, beta, scale=None, initial_state=None,
     return out, final_state, snapshots
 
 
-def kda_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, scale=None, initial_state=None,
-                         output_final_state=True, out=None, final_state=None):
-    """Packed variable-length prefill.  q, k, g: [1,total_T,H,dk] (or [total_T,H,dk]);
-    cu_seqlens: int32 [N+1] on the device.  Returns ``(out, final_state [N,H,dk,dv])``."""
-    lib = load_library()
+def _varlen_prep(q, k, v, g, beta, cu_seqlens, initial_state, output_final_state, out,
+                 final_state):
     H, dk = q.shape[-2], q.shape[-1]
     dv = v.shape[-1]
     total_T = q.numel() // (H * dk)
@@ -284,6 +288,16 @@ def kda_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, scale=None, initial_state
     if final_state is None and output_final_state:
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=device)
     _check_state("final_state", final_state, (N, H, dk, dv), device)
+    return H, dk, dv, total_T, N, out, final_state
+
+
+def kda_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, scale=None, initial_state=None,
+                         output_final_state=True, out=None, final_state=None):
+    """Packed variable-length prefill.  q, k, g: [1,total_T,H,dk] (or [total_T,H,dk]);
+    cu_seqlens: int32 [N+1] on the device.  Returns ``(out, final_state [N,H,dk,dv])``."""
+    lib = load_library()
+    H, dk, dv, total_T, N, out, final_state = _varlen_prep(
+        q, k, v, g, beta, cu_seqlens, initial_state, output_final_state, out, final_state)
     scale = 1.0 / math.sqrt(dk) if scale is None else float(scale)
     rc = lib.kda_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                   _ptr(initial_state), _ptr(out), _ptr(final_state),
@@ -291,6 +305,60 @@ def kda_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, scale=None, initial_state
                                   _dtype_code(q), _stream(q))
     _raise("kda_chunk_fwd_varlen", rc)
     return out, final_state
+
+
+def kda_chunk_fwd_varlen_prologue(q_raw, k_raw, v, g_raw, beta_raw, cu_seqlens, scale=None,
+                                  initial_state=None, output_final_state=True, out=None,
+                                  final_state=None):
+    """kda_chunk_fwd_varlen on raw activations with the fused gate/normalisation
+    prologue (see kda_chunk_fwd_prologue)."""
+    lib = load_library()
+    H, dk, dv, total_T, N, out, final_state = _varlen_prep(
+        q_raw, k_raw, v, g_raw, beta_raw, cu_seqlens, initial_state, output_final_state, out,
+        final_state)
+    scale = 1.0 / math.sqrt(dk) if scale is None else float(scale)
+    rc = lib.kda_chunk_fwd_varlen_prologue(_ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(g_raw),
+                                           _ptr(beta_raw), _ptr(initial_state), _ptr(out),
+                                           _ptr(final_state), _ptr(cu_seqlens.contiguous()), N,
+                                           total_T, H, dk, dv, scale, _dtype_code(q_raw),
+                                           _stream(q_raw))
+    _raise("kda_chunk_fwd_varlen_prologue", rc)
+    return out, final_state
+
+
+def varlen_snapshot_rows(cu_seqlens, snapshot_tokens):
+    """Per-sequence first snapshot row (int64 [N+1], host) of the varlen snapshot layout:
+    sequence n owns rows [rows[n], rows[n+1]), ceil(L_n / snapshot_tokens) of them."""
+    lengths = (cu_seqlens[1:] - cu_seqlens[:-1]).to("cpu", torch.int64).clamp_(min=0)
+    per = (lengths + snapshot_tokens - 1) // snapshot_tokens
+    return torch.cat([torch.zeros(1, dtype=torch.int64), torch.cumsum(per, 0)])
+
+
+def kda_chunk_fwd_varlen_snapshots(q, k, v, g, beta, cu_seqlens, scale=None, initial_state=None,
+                                   snapshot_tokens=512, output_final_state=True, out=None,
+                                   final_state=None, snapshots=None):
+    """kda_chunk_fwd_varlen that also returns each sequence's state every
+    ``snapshot_tokens`` tokens.  Returns ``(out, final_state, snapshots [S_total,H,dk,dv],
+    rows)`` with ``rows = varlen_snapshot_rows(cu_seqlens, snapshot_tokens)`` (reads the
+    lengths back to the host to size the snapshot buffer)."""
+    lib = load_library()
+    H, dk, dv, total_T, N, out, final_state = _varlen_prep(
+        q, k, v, g, beta, cu_seqlens, initial_state, output_final_state, out, final_state)
+    if snapshot_tokens <= 0 or snapshot_tokens % 64 != 0:
+        raise ValueError("snapshot_tokens must be a positive multiple of 64")
+    rows = varlen_snapshot_rows(cu_seqlens, snapshot_tokens)
+    shape = (int(rows[-1]), H, dk, dv)
+    if snapshots is None:
+        snapshots = torch.empty(shape, dtype=torch.float32, device=q.device)
+    _check_state("snapshots", snapshots, shape, q.device)
+    scale = 1.0 / math.sqrt(dk) if scale is None else float(scale)
+    rc = lib.kda_chunk_fwd_varlen_snapshots(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                            _ptr(initial_state), _ptr(out), _ptr(final_state),
+                                            _ptr(snapshots), int(snapshot_tokens),
+                                            _ptr(cu_seqlens.contiguous()), N, total_T, H, dk,
+                                            dv, scale, _dtype_code(q), _stream(q))
+    _raise("kda_chunk_fwd_varlen_snapshots", rc)
+    return out, final_state, snapshots, rows
 
 
 def kda_decode_step(q, k, v, g, beta, state, scale=None, out=None):

@@ -191,6 +191,41 @@ int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void
                          hipStream_t stream);
 
 /*
+ * kda_chunk_fwd_varlen on raw activations, with the gate and normalisation
+ * prologue of kda_chunk_fwd_prologue (same formulas, same rounding) fused into the
+ * loads.  Arguments, layouts and codes are those of kda_chunk_fwd_varlen, with the
+ * raw tensors in place of q, k, g and beta.
+ */
+int kda_chunk_fwd_varlen_prologue(const void* q_raw, const void* k_raw, const void* v,
+                                  const void* g_raw, const void* beta_raw,
+                                  const float* initial_state, void* out, float* final_state,
+                                  const int32_t* cu_seqlens, int N, int total_T, int H, int dk,
+                                  int dv, float scale, int dtype, hipStream_t stream);
+
+/*
+ * kda_chunk_fwd_varlen that also keeps each sequence's state every
+ * snapshot_tokens tokens, for prefix caching of a packed batch (the sources of
+ * kda_chunk_fwd_snapshots).
+ *  snapshots        fp32, required: [S_total, H, dk, dv] with
+ *                   S_total = sum over sequences n of ceil(L_n / snapshot_tokens),
+ *                   L_n = cu_seqlens[n+1] - cu_seqlens[n].  Sequence n owns rows
+ *                   off_n .. off_n + ceil(L_n / snapshot_tokens) - 1, where off_n is
+ *                   the same sum over the sequences before n; row off_n + i holds,
+ *                   for every head, the state after min((i + 1) * snapshot_tokens,
+ *                   L_n) tokens of sequence n (the last one equals its final state).
+ *                   An empty sequence has no row.  The caller sizes the buffer from
+ *                   its own copy of the lengths.
+ *  snapshot_tokens  > 0 and a multiple of 64, else KDA_ERR_SHAPE.
+ * Every other argument, and the values of out and final_state, are exactly as for
+ * kda_chunk_fwd_varlen.
+ */
+int kda_chunk_fwd_varlen_snapshots(const void* q, const void* k, const void* v, const void* g,
+                                   const void* beta, const float* initial_state, void* out,
+                                   float* final_state, float* snapshots, int snapshot_tokens,
+                                   const int32_t* cu_seqlens, int N, int total_T, int H, int dk,
+                                   int dv, float scale, int dtype, hipStream_t stream);
+
+/*
  * Backward pass of kda_chunk_fwd (fixed length): the gradients of
  *     L = sum over tokens of <grad_out, out> + <grad_final_state, final_state>
  * with respect to q, k, v, g, beta and initial_state.  The pages train KDA at up

@@ -33,7 +33,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "kda_abi_version", "kda_status_string", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
-        "kda_chunk_fwd_ws", "kda_chunk_fwd_prologue",
+        "kda_chunk_fwd_ws", "kda_chunk_fwd_prologue", "kda_chunk_fwd_varlen_prologue",
+        "kda_chunk_fwd_varlen_snapshots",
         "kda_chunk_fwd_snapshots", "kda_chunk_fwd_varlen", "kda_decode_step", "kda_chunk_bwd",
         "kda_chunk_transition", "kda_state_compose"])
 
@@ -82,6 +83,20 @@ def test_argument_checks_precede_any_device_call(lib):
               None) == -8
     assert ws(p, p, p, p, p, None, p, None, 1, 64, 1, 128, 128, 0.1, 0, p, 1024, None) == -8
     assert ws(p, p, p, p, p, None, p, None, 1, 64, 1, 128, 128, 0.1, 0, p, big, None) in (-6, -7)
+    vp_ = lib.kda_chunk_fwd_varlen_prologue
+    vp_.argtypes = [vp] * 9 + [i32] * 5 + [f32, i32, vp]
+    vp_.restype = i32
+    assert vp_(p, p, p, p, p, None, p, None, None, 2, 64, 1, 128, 128, 0.1, 0, None) == -1
+    assert vp_(p, p, p, p, p, None, p, None, p, 0, 64, 1, 128, 128, 0.1, 0, None) == -2
+    assert vp_(p, p, p, p, p, None, p, None, mis, 2, 64, 1, 128, 128, 0.1, 0, None) == -5
+    assert vp_(p, p, p, p, p, None, p, None, p, 2, 64, 1, 128, 128, 0.1, 0, None) in (-6, -7)
+    vs = lib.kda_chunk_fwd_varlen_snapshots
+    vs.argtypes = [vp] * 9 + [i32, vp] + [i32] * 5 + [f32, i32, vp]
+    vs.restype = i32
+    assert vs(p, p, p, p, p, None, p, None, None, 64, p, 2, 64, 1, 128, 128, 0.1, 0, None) == -1
+    assert vs(p, p, p, p, p, None, p, None, p, 100, p, 2, 64, 1, 128, 128, 0.1, 0, None) == -2
+    assert vs(p, p, p, p, p, None, p, None, mis, 64, p, 2, 64, 1, 128, 128, 0.1, 0, None) == -5
+    assert vs(p, p, p, p, p, None, p, None, p, 64, p, 2, 64, 1, 128, 128, 0.1, 0, None) in (-6, -7)
     d = lib.kda_decode_step
     d.argtypes = [vp] * 7 + [i32] * 4 + [f32, i32, vp]
     d.restype = i32

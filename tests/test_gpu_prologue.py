@@ -100,3 +100,27 @@ def test_prologue_4x4096_full_size_sampled():
     ref_sel = np.stack([ref_o[n * T:(n + 1) * T, h] for n, h in pairs])   # [B*T, H, dv] layout
     assert_close("4x4096 out (sampled)", got_o, ref_sel, torch.bfloat16)
     assert_close("4x4096 state (sampled)", got_s, ref_s, torch.bfloat16)
+
+
+@pytest.mark.parametrize("D,dtype", [(128, torch.bfloat16), (64, torch.float32)])
+def test_varlen_prologue_matches_oracle(D, dtype):
+    """kda_chunk_fwd_varlen_prologue: packed sequences (an empty one, ragged tails,
+    nonzero initial states) from raw activations, against prologue_np followed by the
+    oracle."""
+    from gated_delta_rule_102_amd import kda
+    lengths = [77, 0, 130, 1, 200]
+    H, N, total = 3, len(lengths), sum(lengths)
+    d = kin.make_prefill_raw(1, total, H, D, D, dtype=dtype, seed=61, nonzero_state=False)
+    s0 = 0.1 * torch.randn((N, H, D, D), generator=torch.Generator().manual_seed(62))
+    cu = kin.lengths_to_cu(lengths)
+    scale = 1.0 / math.sqrt(D)
+    g = {k: v.to(DEV) for k, v in d.items() if isinstance(v, torch.Tensor)}
+    out, fs = kda.kda_chunk_fwd_varlen_prologue(g["q_raw"], g["k_raw"], g["v"], g["g_raw"],
+                                                g["beta_raw"], cu.to(DEV), scale=scale,
+                                                initial_state=s0.to(DEV))
+    torch.cuda.synchronize()
+    q, k, gg, b = prologue_np(d["q_raw"][0], d["k_raw"][0], d["g_raw"][0], d["beta_raw"][0])
+    ref_o, ref_s = oracle_forward(q, k, widen_np(d["v"][0]), gg, b, scale, cu_seqlens=cu.numpy(),
+                                  initial_state=s0)
+    assert_close("varlen prologue out", out[0], ref_o, dtype)
+    assert_close("varlen prologue state", fs, ref_s.reshape(N, H, D, D), dtype)

@@ -112,3 +112,47 @@ def test_snapshots_across_windows():
         t = min((i + 1) * S, T)
         _, ref_s = oracle_fixed(_prefix(d, t))
         assert_close(f"snapshot {i} (t={t})", snaps[:, :, i], ref_s.reshape(B, H, D, D), torch.bfloat16)
+
+
+@pytest.mark.parametrize("lengths,H,S,D,dtype", [
+    ([300, 0, 64, 1, 190, 700], 3, 128, 128, torch.bfloat16),
+    ([130, 65, 256], 2, 64, 64, torch.float32),
+    ([70 + 13 * i for i in range(48)], 3, 64, 128, torch.bfloat16),   # 144 streams
+])
+def test_varlen_snapshots_match_oracle(lengths, H, S, D, dtype):
+    """kda_chunk_fwd_varlen_snapshots: every snapshot row of every sequence against the
+    oracle's final state on that sequence's prefix; out and final state bitwise equal
+    to kda_chunk_fwd_varlen; each sequence's last row equal to its final state."""
+    from gated_delta_rule_102_amd import kda
+    d = kin.make_varlen(lengths, H, D, D, dtype=dtype, seed=71, nonzero_state=True)
+    d["scale"] = 1.0 / math.sqrt(D)
+    g = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    args = (g["q"], g["k"], g["v"], g["g"], g["beta"], g["cu_seqlens"])
+    out, fs, snaps, rows = kda.kda_chunk_fwd_varlen_snapshots(
+        *args, scale=d["scale"], initial_state=g["initial_state"], snapshot_tokens=S)
+    out2, fs2 = kda.kda_chunk_fwd_varlen(*args, scale=d["scale"],
+                                         initial_state=g["initial_state"])
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(fs, fs2), "snapshots changed the results"
+    assert int(rows[-1]) == sum(-(-L // S) for L in lengths)
+    assert tuple(snaps.shape) == (int(rows[-1]), H, D, D)
+    cu = d["cu_seqlens"].tolist()
+    checked = 0
+    for n, L in enumerate(lengths):
+        r0, r1 = int(rows[n]), int(rows[n + 1])
+        assert r1 - r0 == -(-L // S)
+        if L:
+            assert torch.equal(snaps[r1 - 1], fs[n]), f"sequence {n}: last row != final state"
+        # the oracle on every prefix of the small cases, on three sequences of the large one
+        if len(lengths) > 8 and n not in (0, 23, 47):
+            continue
+        for i in range(r1 - r0):
+            t = min((i + 1) * S, L)
+            sl = {x: d[x][:, cu[n]:cu[n] + t].contiguous() for x in ("q", "k", "v", "g", "beta")}
+            sl["initial_state"] = d["initial_state"][n:n + 1]
+            sl["scale"] = d["scale"]
+            _, ref_s = oracle_fixed(sl)
+            assert_close(f"seq {n} snapshot {i} (t={t})", snaps[r0 + i], ref_s.reshape(H, D, D),
+                         dtype)
+            checked += 1
+    assert checked > 0
