@@ -962,7 +962,8 @@ struct ScanCfg {
   static constexpr int OST = DT + DVS * RBC;
   static constexpr int OSTB = kC * RBO;         // one output stage; two alternate
   static constexpr int ORD = OST + 2 * OSTB;
-  static constexpr int LDS = ORD + 256 * 4;
+  static constexpr int SNAP = ORD + 256 * 4;    // varlen: first snapshot row of the sequence
+  static constexpr int LDS = SNAP + 16;
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -984,8 +985,10 @@ struct ScanParams {
 };
 
 // The chunks of one window of one (sequence, head, dv slice), in order, by one
-// workgroup (`bid` numbers the scan workgroups of the launch from 0).
-template <int D, int DVS, typename TIn>
+// workgroup (`bid` numbers the scan workgroups of the launch from 0).  PACKED =
+// false compiles out what only packed (varlen) input needs, for the windowed
+// schedule, which runs fixed-length input only.
+template <int D, int DVS, typename TIn, bool PACKED = true>
 __device__ __forceinline__ void scan_body(const ScanParams& p, char* smem, const int bid) {
   using CF = ScanCfg<D, DVS, TIn>;
   using SL = Slot<D, CF::F32>;
@@ -1005,7 +1008,7 @@ __device__ __forceinline__ void scan_body(const ScanParams& p, char* smem, const
   if (grp >= N * H) return;
   const int rank = grp / H, h = grp % H;
   int n = rank;
-  if (p.sa.cu != nullptr && N <= 256) {   // longest sequence first
+  if (PACKED && p.sa.cu != nullptr && N <= 256) {   // longest sequence first
     int* ord = reinterpret_cast<int*>(smem + CF::ORD);
     int mylen = 0;
     if (tid < N) {
@@ -1037,9 +1040,10 @@ __device__ __forceinline__ void scan_body(const ScanParams& p, char* smem, const
 
   // Snapshot i of this (sequence, head): fixed length, [N, H, nsnap] order; varlen,
   // row off_n + i of [snapshots, H], where off_n counts the snapshots of the
-  // sequences before n (ceil(chunks / snap_chunks) each), summed over the lanes.
-  int snap_off = 0, nsnap_n = p.nsnap;
-  if (p.snap != nullptr && p.sa.cu != nullptr) {
+  // sequences before n (ceil(chunks / snap_chunks) each).  Wavefront 0 sums off_n
+  // over its lanes into LDS (ordered by the barrier after the state load), where
+  // the snapshot stores read it, so no register holds it across the steps.
+  if (PACKED && p.snap != nullptr && p.sa.cu != nullptr && wave == 0) {
     int part = 0;
     for (int m = lane; m < n; m += 64) {
       int t0m, lm;
@@ -1047,13 +1051,13 @@ __device__ __forceinline__ void scan_body(const ScanParams& p, char* smem, const
       part += ((lm + kC - 1) / kC + p.snap_chunks - 1) / p.snap_chunks;
     }
     for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o);
-    snap_off = part;
-    nsnap_n = (nchunks + p.snap_chunks - 1) / p.snap_chunks;
+    if (lane == 0) *reinterpret_cast<int*>(smem + CF::SNAP) = part;
   }
   auto snap_ptr = [&](int si) -> float* {
-    return p.sa.cu != nullptr
-               ? p.snap + (static_cast<int64_t>(snap_off + si) * H + h) * D * D
-               : p.snap + ((static_cast<int64_t>(n) * H + h) * p.nsnap + si) * D * D;
+    if (!PACKED || p.sa.cu == nullptr)
+      return p.snap + ((static_cast<int64_t>(n) * H + h) * p.nsnap + si) * D * D;
+    const int off = *reinterpret_cast<const int*>(smem + CF::SNAP);
+    return p.snap + (static_cast<int64_t>(off + si) * H + h) * D * D;
   };
   const float* s_in = c_begin == 0 ? p.s0 : p.sbuf;
   float* s_out = p.c_hi >= nchunks ? p.sT : p.sbuf;
@@ -1263,7 +1267,11 @@ __device__ __forceinline__ void scan_body(const ScanParams& p, char* smem, const
     }
     if (p.snap != nullptr && (ci + 1 == nchunks || (ci + 1) % p.snap_chunks == 0)) {
       // state after chunk ci: a prefix-cache snapshot
-      store_state(snap_ptr(ci + 1 == nchunks ? nsnap_n - 1 : (ci + 1) / p.snap_chunks - 1));
+      // the last snapshot is number ceil(nchunks / snap_chunks) - 1 (nsnap - 1 for
+      // fixed length)
+      const int si = ci + 1 != nchunks ? (ci + 1) / p.snap_chunks - 1
+                     : !PACKED || p.sa.cu == nullptr ? p.nsnap - 1 : (nchunks - 1) / p.snap_chunks;
+      store_state(snap_ptr(si));
     }
     __syncthreads();
   };
@@ -1315,7 +1323,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_group_kernel(GroupParams 
   __shared__ __attribute__((aligned(16))) char smem[GroupCfg<D, DVS, TIn>::LDS];
   const int bid = blockIdx.x;
   if (bid < g.nscan) {
-    scan_body<D, DVS, TIn>(g.sp, smem, bid);
+    scan_body<D, DVS, TIn, false>(g.sp, smem, bid);
     return;
   }
   int slot = 0;
