@@ -122,8 +122,8 @@ def decode_bytes(B, H, d, elt):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--decode-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
@@ -227,10 +227,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
                      "traffic": measured_traffic(),
-                     "kernel": "kda_chunk_fwd_ws = 5 launches of prefill_group_kernel<128,32,bf16> "
-                               "(4 windows of 16 chunks: preparation of window k with the "
-                               "state scan of window k-1); time per call from one HIP event "
-                               "pair around the timed steps",
+                     "kernel": "kda_chunk_fwd_ws = chunk_prep8_kernel (chunk operands, 8 "
+                               "wavefronts per (chunk, head)) + state_scan_kernel<128,32,bf16> "
+                               "(serial state scan, 32-column slices); time per call from one "
+                               "HIP event pair around the timed steps",
                      "kernel_ms": kern_avg_s * 1e3, "algorithmic_bytes": nbytes,
                      "kernel_source_sha256": source_digest()},
         "prefill": {

@@ -267,8 +267,8 @@ struct PrepCfg {
   static constexpr int AT = R1;                  // [64][64] fp32: A, then T in place
   static constexpr int MB = AT + kC * kC * 4;    // [64][64] operand: M
   static constexpr int FIJ = MB + kC * RBC;      // [6][D] fp32 pair factors
-  static constexpr int BTOT = FIJ + 6 * D * 4;   // [4][D] fp32 sub-tile totals
-  static constexpr int BETA = BTOT + 4 * D * 4;  // [64] fp32
+  static constexpr int BTOT = FIJ + 6 * D * 4;   // [8][D] fp32 totals per wavefront's rows
+  static constexpr int BETA = BTOT + 8 * D * 4;  // [64] fp32
   static constexpr int LDS = BETA + kC * 4;
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
@@ -289,10 +289,10 @@ template <> struct RawRow<bf16_t, 2> { using type = uint32_t; };
 template <> struct RawRow<bf16_t, 1> { using type = uint16_t; };
 template <> struct RawRow<float, 1> { using type = uint32_t; };
 
-template <typename TIn, int CPL>
+template <typename TIn, int CPL, int ROWS = 16>
 struct RawChunk {
   using R = typename RawRow<TIn, CPL>::type;
-  R g[16], k[16], q[16];
+  R g[ROWS], k[ROWS], q[ROWS];
   uint32_t beta;
 };
 
@@ -337,16 +337,23 @@ __device__ __forceinline__ PrepItem prep_group_item(const PrepParams& p, int ite
 
 // All state-independent work of one (chunk, head) item, by one workgroup; the
 // results go to the workspace slot at `slot_ptr`.
-template <int D, typename TIn>
+// NW = 4 or 8 wavefronts per item.  With 8 (d = 128, bf16 only) a wavefront owns
+// half a 16-row sub-tile in the elementwise phases and one sub-tile pair or two
+// diagonal ones in the decayed products, and the workgroups are small enough in
+// registers for two of them (16 wavefronts) to share a CU.
+template <int D, typename TIn, int NW = 4>
 __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const PrepItem& cur_it,
                                           char* slot_ptr) {
   using CF = PrepCfg<D, TIn>;
   using SL = Slot<D, CF::F32>;
-  using RC = RawChunk<TIn, CF::CPL>;
+  constexpr int RW = kC / NW;                    // token rows per wavefront
+  using RC = RawChunk<TIn, CF::CPL, RW>;
   constexpr bool F32 = CF::F32;
   constexpr int CPL = CF::CPL;
   constexpr int E = CF::E;
   constexpr int EI = CF::EI;
+  constexpr int NT = 64 * NW;                    // threads per item
+  static_assert(NW == 4 || (NW == 8 && D == 128 && !F32), "wavefronts per item");
 
   // the wavefront index is uniform: keeping it scalar makes per-wavefront branches
   // and offsets scalar work
@@ -369,7 +376,7 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
 
   // the strictly-upper sub-tiles of A/T and of M are read as zeros; nothing else
   // writes them, so clearing them once serves every item of this workgroup
-  for (int e = tid; e < 6 * 256; e += kThreads) {
+  for (int e = tid; e < 6 * 256; e += NT) {
     int I, J;
     upper_pair(e >> 8, I, J);
     const int row = 16 * I + ((e >> 4) & 15), col = 16 * J + (e & 15);
@@ -393,8 +400,8 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
 #pragma unroll
     for (int x = 0; x < 3; ++x) {
 #pragma unroll
-      for (int j = 0; j < 16 / RPI; ++j) {
-        const int row0 = 16 * uw + j * RPI;
+      for (int j = 0; j < RW / RPI; ++j) {
+        const int row0 = RW * uw + j * RPI;
         const int row = row0 + lane / LPR;
         char* dst = smem + CF::RAW + x * kC * RBI + row0 * RBI;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -413,9 +420,10 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
     if (p.prologue) {
       // unit L2 norm of q and k per (token, head): two threads per row sum squares
       // over half the channels, straight from the raw tiles (the FIJ region is
-      // free until the decay phase)
+      // free until the decay phase); the first 256 threads
       float* nrm = reinterpret_cast<float*>(smem + CF::FIJ);   // [k, q][64]
-      const int x = 1 + (tid >> 7), row = (tid & 127) >> 1, half = tid & 1;
+      const int tq = tid & 255;
+      const int x = 1 + (tq >> 7), row = (tq & 127) >> 1, half = tq & 1;
       const char* src = smem + CF::RAW + x * kC * RBI + row * RBI + half * (RBI / 2);
       float ss = 0.f;
 #pragma unroll
@@ -436,12 +444,12 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
         }
       }
       ss += __shfl_xor(ss, 1);
-      if (half == 0) nrm[(x - 1) * kC + row] = __builtin_amdgcn_rsqf(ss + kNormEps);
+      if (half == 0 && tid < 256) nrm[(x - 1) * kC + row] = __builtin_amdgcn_rsqf(ss + kNormEps);
       __syncthreads();
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int off = (16 * wave + r) * RBI + lane * CPL * EI;
+    for (int r = 0; r < RW; ++r) {
+      const int off = (RW * wave + r) * RBI + lane * CPL * EI;
       if constexpr (!F32 && CPL == 1) {
         rc.g[r] = *reinterpret_cast<const uint16_t*>(smem + CF::RAW + 0 * kC * RBI + off);
         rc.k[r] = *reinterpret_cast<const uint16_t*>(smem + CF::RAW + 1 * kC * RBI + off);
@@ -453,7 +461,7 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
       }
       if (p.prologue) {   // normalised q, k kept in the input precision
         const float* nrm = reinterpret_cast<const float*>(smem + CF::FIJ);
-        const float fk = nrm[16 * wave + r], fq = nrm[kC + 16 * wave + r];
+        const float fk = nrm[RW * wave + r], fq = nrm[kC + RW * wave + r];
         if constexpr (F32) {
           rc.k[r] = __float_as_uint(__uint_as_float(rc.k[r]) * fk);
           rc.q[r] = __float_as_uint(__uint_as_float(rc.q[r]) * fq);
@@ -474,7 +482,7 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
     const auto rw = make_rsrc(slot_ptr, SL::BYTES);
 
     // ------------------------------------------------ phase E: decay factors
-    // wavefront `wave` owns token rows 16*wave .. +15; lane owns key channels
+    // wavefront `wave` owns token rows RW*wave .. +RW-1; lane owns key channels
     // lane*CPL .. +CPL-1; the cumulative decay is a running product over the rows.
     // q and k stay in their packed input words (cur.q, cur.k) and are widened where
     // used, which keeps the live register set small across the matrix-core phases
@@ -488,11 +496,11 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
       else if constexpr (CPL == 1) return __uint_as_float(uint32_t(cur.q[r]) << 16);
       else return e ? bf16hi(cur.q[r]) : bf16lo(cur.q[r]);
     };
-    float rowf[16][CPL], colf[16][CPL];
+    float rowf[RW][CPL], colf[RW][CPL];
     {
-      float ed[16][CPL];
+      float ed[RW][CPL];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
+      for (int r = 0; r < RW; ++r) {
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
           float gv;
@@ -502,7 +510,7 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
           // prologue: g = max(-5, -softplus(x)), so e^g = max(e^-5, 1 / (1 + e^x));
           // rows past the sequence end keep retention 1, as g = 0 does without it
           ed[r][e] = !p.prologue ? fast_exp2(gv * kLog2e)
-                     : 16 * wave + r < cur_it.nrow
+                     : RW * wave + r < cur_it.nrow
                          ? fmaxf(kMinRetention, __builtin_amdgcn_rcpf(1.f + fast_exp2(gv * kLog2e)))
                          : 1.f;
         }
@@ -514,50 +522,72 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
       }
 #pragma unroll
       for (int e = 0; e < CPL; ++e) {
+        // products over this wavefront's rows, from their start (rowf) and to their
+        // end (colf); for NW = 4 the rows are the sub-tile
         float run = 1.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) { run *= ed[r][e]; rowf[r][e] = run; }      // e^{G_t - R_w}
-        btot[wave * D + lane * CPL + e] = run;                                    // e^{R_{w+1} - R_w}
+        for (int r = 0; r < RW; ++r) { run *= ed[r][e]; rowf[r][e] = run; }
+        btot[wave * D + lane * CPL + e] = run;
         float back = 1.f;
 #pragma unroll
-        for (int r = 15; r >= 0; --r) { colf[r][e] = back; back *= ed[r][e]; }   // e^{R_{w+1} - G_t}
+        for (int r = RW - 1; r >= 0; --r) { colf[r][e] = back; back *= ed[r][e]; }
       }
     }
     __syncthreads();
 
+    // this wavefront's rows lie in sub-tile `sub` (R_{sub+1}: the cumulative decay at
+    // its end); BPS wavefronts share a sub-tile
+    constexpr int BPS = NW / 4;
+    const int sub = wave / BPS;
     float eR1[CPL], fI3[CPL];
 #pragma unroll
     for (int e = 0; e < CPL; ++e) {
       const int c = lane * CPL + e;
-      float b4[4];
+      float bb[NW], b4[4];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) b4[m] = btot[m * D + c];
+      for (int m = 0; m < NW; ++m) bb[m] = btot[m * D + c];
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        b4[I] = bb[I * BPS];
+#pragma unroll
+        for (int x = 1; x < BPS; ++x) b4[I] *= bb[I * BPS + x];   // e^{R_{I+1} - R_I}
+      }
       float pre = 1.f;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) if (m <= wave) pre *= b4[m];
-      eR1[e] = pre;                                    // e^{R_{w+1}}
-      const float inv_bt = __builtin_amdgcn_rcpf(b4[wave]);   // b4 in [e^-80, 1]
+      for (int m = 0; m < 4; ++m) if (m <= sub) pre *= b4[m];
+      eR1[e] = pre;                                    // e^{R_{sub+1}}
+      // the sub-tile's rows before / after this wavefront's (none for NW = 4)
+      float before = 1.f, after = 1.f;
+#pragma unroll
+      for (int m = 0; m < NW; ++m) {
+        if (m / BPS == sub && m < wave) before *= bb[m];
+        if (m / BPS == sub && m > wave) after *= bb[m];
+      }
+      const float inv_bt = __builtin_amdgcn_rcpf(b4[sub]) * before;   // b4 in [e^-80, 1]
       float acc = 1.f;
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
-        if (I > wave) {
+        if (I > sub) {
           acc *= b4[I];
-          fij[offdiag_index(I, wave) * D + c] = acc;   // e^{R_{I+1} - R_{w+1}}
+          if (wave % BPS == 0) fij[offdiag_index(I, sub) * D + c] = acc;   // e^{R_{I+1} - R_{sub+1}}
         }
       }
-      fI3[e] = acc;                                    // e^{G_n - R_{w+1}}
+      fI3[e] = acc;                                    // e^{G_n - R_{sub+1}}
       if (wave == 0) {
         const float lam = b4[0] * b4[1] * b4[2] * b4[3];
         buf_st32(__float_as_uint(lam), rw, SL::LAM + c * 4, 0);
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) rowf[r][e] *= inv_bt;   // now e^{G_t - R_{w+1}} in [1, e^80]
+      for (int r = 0; r < RW; ++r) {
+        rowf[r][e] *= inv_bt;   // now e^{G_t - R_{sub+1}} in [1, e^80]
+        colf[r][e] *= after;    // now e^{R_{sub+1} - G_t}
+      }
     }
     // row-side operands (referenced to the end of the own sub-tile) and the
     // column-side keys of the diagonal pairs
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int t = 16 * wave + r;
+    for (int r = 0; r < RW; ++r) {
+      const int t = RW * wave + r;
       const int byte = lane * CPL * E;
       if constexpr (CPL == 2 && !F32) {
         const float k0 = kval(r, 0), k1 = kval(r, 1), q0 = qval(r, 0), q1 = qval(r, 1);
@@ -577,16 +607,16 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
         }
       }
     }
-    // Kt^T = (K e^{G_n - G})^T straight to the workspace: 16 consecutive tokens per channel
+    // Kt^T = (K e^{G_n - G})^T straight to the workspace: RW consecutive tokens per channel
 #pragma unroll
     for (int e = 0; e < CPL; ++e) {
       const int c = lane * CPL + e;
-      float x[16];
+      float x[RW];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = kval(r, e) * colf[r][e] * fI3[e];
+      for (int r = 0; r < RW; ++r) x[r] = kval(r, e) * colf[r][e] * fI3[e];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        buf_put4<F32>(rw, SL::KT + frag_off<kC, F32>(c, 16 * wave + 4 * q4), x[4 * q4], x[4 * q4 + 1],
+      for (int q4 = 0; q4 < RW / 4; ++q4)
+        buf_put4<F32>(rw, SL::KT + frag_off<kC, F32>(c, RW * wave + 4 * q4), x[4 * q4], x[4 * q4 + 1],
                       x[4 * q4 + 2], x[4 * q4 + 3]);
     }
     __syncthreads();
@@ -595,11 +625,14 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
     // computed transposed (rows s) so each lane stores 4 consecutive s of row t.
     // Off-diagonal pairs cost about twice a diagonal one (their column operand is
     // rescaled), so each wavefront takes two off-diagonal pairs or one off-diagonal
-    // and two diagonal ones: pair numbers from pair_of, -1 = none.
-    constexpr int kPairs[4][3] = {{1, 3, -1}, {4, 6, -1}, {7, 0, 2}, {8, 5, 9}};
+    // and two diagonal ones: pair numbers from pair_of, -1 = none.  With 8
+    // wavefronts each takes one off-diagonal pair or two diagonal ones.
+    constexpr int kPairs4[4][3] = {{1, 3, -1}, {4, 6, -1}, {7, 0, 2}, {8, 5, 9}};
+    constexpr int kPairs8[8][3] = {{1, -1, -1}, {3, -1, -1}, {4, -1, -1}, {6, -1, -1},
+                                   {7, -1, -1}, {8, -1, -1}, {0, 2, -1}, {5, 9, -1}};
 #pragma unroll
-    for (int pp = 0; pp < 3; ++pp) {
-      const int pr = kPairs[wave][pp];
+    for (int pp = 0; pp < (NW == 4 ? 3 : 2); ++pp) {
+      const int pr = NW == 4 ? kPairs4[wave][pp] : kPairs8[wave][pp];
       if (pr >= 0) {
         int I, J;
         pair_of(pr, I, J);
@@ -646,10 +679,10 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
     // ------------------------------------------------ phase E2 + diagonal inverses
     // chunk-referenced Q e^G ([t][c]) and (K e^G)^T ([c][t]) into region 1
     {
-      float kb[CPL][16];
+      float kb[CPL][RW];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = 16 * wave + r;
+      for (int r = 0; r < RW; ++r) {
+        const int t = RW * wave + r;
         float qv[CPL];
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
@@ -667,8 +700,8 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
 #pragma unroll
       for (int e = 0; e < CPL; ++e)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          lds_put4<F32>(smem + CF::KBT + swz<CF::RBC>(lane * CPL + e, (16 * wave + 4 * q4) * E),
+        for (int q4 = 0; q4 < RW / 4; ++q4)
+          lds_put4<F32>(smem + CF::KBT + swz<CF::RBC>(lane * CPL + e, (RW * wave + 4 * q4) * E),
                         kb[e][4 * q4], kb[e][4 * q4 + 1], kb[e][4 * q4 + 2], kb[e][4 * q4 + 3]);
     }
     {   // T_ww = (I + A_ww)^{-1} = (I - A)(I + A^2)(I + A^4)(I + A^8): A_ww is strictly
@@ -677,6 +710,8 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
         // 4*g4 .. +3) and its B operand in the accumulator layout (lane: rows 4*g4 ..
         // +3 of column l16), so a result feeds the next product's B side directly and
         // its A side after a transpose through this wavefront's 16x17 scratch.
+        // Wavefronts 0-3 (one per diagonal block).
+     if (NW == 4 || wave < 4) {
       const int base = 16 * wave;
       float* sc = reinterpret_cast<float*>(smem + CF::XS) + wave * 16 * CF::XLD;
       auto mm = [&](const float (&xr)[4], const float (&yc)[4]) {
@@ -720,6 +755,7 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
       f32x4_t t3 = mm(t2_r, p3_c);                             // T2 (I + A^8)
 #pragma unroll
       for (int i = 0; i < 4; ++i) at_el(base + 4 * g4 + i, base + l16) = t3[i] + t2[i];
+     }
     }
     __syncthreads();
 
@@ -744,8 +780,8 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
     }
     __syncthreads();
     float* xs = reinterpret_cast<float*>(smem + CF::XS);
-    const int bi = 2 + (wave >> 1), bj = wave & 1;      // lower-left 16x16 block of this wave
-    {   // X_{bi,bj} = sum_{m=bj}^{1} A_{bi,m} T_{m,bj}
+    const int bi = 2 + ((wave & 3) >> 1), bj = wave & 1;   // lower-left 16x16 block (waves 0-3)
+    if (NW == 4 || wave < 4) {   // X_{bi,bj} = sum_{m=bj}^{1} A_{bi,m} T_{m,bj}
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
@@ -761,7 +797,7 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
       for (int i = 0; i < 4; ++i) xs[(wave * 16 + 4 * g4 + i) * CF::XLD + l16] = acc[i];
     }
     __syncthreads();
-    {   // T_{bi,bj} = -sum_{m=2}^{bi} T_{bi,m} X_{m,bj}
+    if (NW == 4 || wave < 4) {   // T_{bi,bj} = -sum_{m=2}^{bi} T_{bi,m} X_{m,bj}
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int m = 2; m < 4; ++m) {
@@ -783,33 +819,35 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
     // of the fp32 T, so the later products read whole 16-byte fragments
     char* tbr = atc;
     char* tbt = atc + kC * CF::RBC;
+    // each thread handles VPTH consecutive entries of one row
+    constexpr int TPR = NT / kC, VPTH = kC / TPR;
     if constexpr (!F32) {
-      const int t = tid >> 2, s0 = (tid & 3) * 16;
-      float x[16];
+      const int t = tid / TPR, s0 = (tid % TPR) * VPTH;
+      float x[VPTH];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
+      for (int q4 = 0; q4 < VPTH / 4; ++q4) {
         const float4 u = at_row4(t, s0 + 4 * q4);
         const float4 b = *reinterpret_cast<const float4*>(betas + s0 + 4 * q4);
         x[4 * q4] = u.x * b.x; x[4 * q4 + 1] = u.y * b.y; x[4 * q4 + 2] = u.z * b.z; x[4 * q4 + 3] = u.w * b.w;
       }
       __syncthreads();   // all of T is read before its space is reused
 #pragma unroll
-      for (int h8 = 0; h8 < 2; ++h8) {
+      for (int h8 = 0; h8 < VPTH / 8; ++h8) {
         const int o = 8 * h8;
         *reinterpret_cast<i32x4_t*>(tbr + swz<CF::RBC>(t, (s0 + o) * 2)) = i32x4_t{
             static_cast<int>(pack_bf16x2(x[o], x[o + 1])), static_cast<int>(pack_bf16x2(x[o + 2], x[o + 3])),
             static_cast<int>(pack_bf16x2(x[o + 4], x[o + 5])), static_cast<int>(pack_bf16x2(x[o + 6], x[o + 7]))};
       }
 #pragma unroll
-      for (int e = 0; e < 16; ++e) lds_set1<false>(tbt + swz<CF::RBC>(s0 + e, t * 2), x[e]);
+      for (int e = 0; e < VPTH; ++e) lds_set1<false>(tbt + swz<CF::RBC>(s0 + e, t * 2), x[e]);
       __syncthreads();
     }
 
     // ------------------------------------------------ P = scale M Tb, stored as P[t][t']
     // computed transposed: P^T[t'][t] = sum_s Tb[s][t'] M[t][s], nonzero for t' <= t
 #pragma unroll
-    for (int pp = 0; pp < 3; ++pp) {
-      const int pr = wave + 4 * pp;
+    for (int pp = 0; pp < (10 + NW - 1) / NW; ++pp) {
+      const int pr = wave + NW * pp;
       if (pr < 10) {
         int C, R;
         pair_of(pr, C, R);
@@ -836,7 +874,7 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
                       p.scale * acc[2], p.scale * acc[3]);
       }
     }
-    for (int e = tid; e < 6 * 64; e += kThreads) {   // P[t][t'] = 0 for t' sub-tile > t sub-tile
+    for (int e = tid; e < 6 * 64; e += NT) {   // P[t][t'] = 0 for t' sub-tile > t sub-tile
       int C, R;
       upper_pair(e >> 6, C, R);
       const int t = 16 * C + ((e >> 2) & 15), tp = 16 * R + 4 * (e & 3);
@@ -849,7 +887,7 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
     // W^T = (K e^G)^T Tb^T and Q'^T = scale ((Q e^G)^T - (K e^G)^T P^T); lane holds
     // 4 consecutive channels of one token row -> 4-element stores of W[t][c], Q'[t][c]
     {
-      constexpr int RPW = D / 64;        // 16-row channel tiles per wavefront
+      constexpr int RPW = D / (16 * NW);  // 16-row channel tiles per wavefront
       f32x4_t aw[RPW][4], aq[RPW][4];
 #pragma unroll
       for (int rr = 0; rr < RPW; ++rr)
@@ -905,11 +943,11 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
         }
       }
     }
-    // Tb = T Diag(beta) -> workspace, 16 consecutive entries per thread
+    // Tb = T Diag(beta) -> workspace, VPTH consecutive entries per thread
     if constexpr (!F32) {
-      const int t = tid >> 2, s0 = (tid & 3) * 16;
+      const int t = tid / TPR, s0 = (tid % TPR) * VPTH;
 #pragma unroll
-      for (int h8 = 0; h8 < 2; ++h8) {
+      for (int h8 = 0; h8 < VPTH / 8; ++h8) {
         const i32x4_t w = *reinterpret_cast<const i32x4_t*>(tbr + swz<CF::RBC>(t, (s0 + 8 * h8) * 2));
         buf_st64(i32x2_t{w[0], w[1]}, rw, SL::TB + frag_off<kC, F32>(t, s0 + 8 * h8), 0);
         buf_st64(i32x2_t{w[2], w[3]}, rw, SL::TB + frag_off<kC, F32>(t, s0 + 8 * h8 + 4), 0);
@@ -940,6 +978,17 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepParams p) {
   prep_body<D, TIn>(p, smem, it,
                     p.ws + (static_cast<int64_t>(it.slot) * p.sa.H + it.h) *
                                Slot<D, std::is_same<TIn, float>::value>::BYTES);
+}
+
+// The same with 8 wavefronts per item (d = 128, bf16): two workgroups, 16
+// wavefronts, share a CU.
+__global__ __launch_bounds__(2 * kThreads, 2) void chunk_prep8_kernel(PrepParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[PrepCfg<128, bf16_t>::LDS];
+  const PrepItem it = prep_item(p, blockIdx.x);
+  if (!it.valid) return;         // unused workspace slot
+  prep_body<128, bf16_t, 8>(p, smem, it,
+                            p.ws + (static_cast<int64_t>(it.slot) * p.sa.H + it.h) *
+                                       Slot<128, false>::BYTES);
 }
 
 // ================================================================= kernel 2
@@ -1445,12 +1494,20 @@ hipError_t launch_grouped(const PrefillArgs& a, int cg) {
 // the scan's time follows the operand bytes each CU moves).
 constexpr int kWideStreams = 128;
 
-// Chunks per window of a fixed-length call; 0 selects the two-kernel schedule
-// (always used for varlen input and from kWideStreams streams on).
+// Chunks per window of a fixed-length call; 0 selects the two-kernel schedule:
+// always for varlen input and from kWideStreams streams on; for bf16 at d = 128
+// also from 64 streams on when the sequences have at most 64 chunks, where the
+// windowed schedule's first and last launches (preparation alone, scan alone) are
+// a large share of the call and the 8-wavefront preparation is available instead.
 inline int prefill_cg(const PrefillArgs& a) {
   if (a.cu_seqlens != nullptr) return 0;
-  const int cg = group_chunks((a.T + kC - 1) / kC);
-  return forced_group_chunks() < 0 && a.N * a.H >= kWideStreams ? 0 : cg;
+  const int nchunks = (a.T + kC - 1) / kC;
+  const int cg = group_chunks(nchunks);
+  if (forced_group_chunks() >= 0) return cg;
+  const int streams = a.N * a.H;
+  if (streams >= kWideStreams) return 0;
+  if (!a.dtype_f32 && a.d == 128 && streams >= 64 && nchunks <= 64) return 0;
+  return cg;
 }
 
 template <int D, typename TIn>
@@ -1478,7 +1535,10 @@ hipError_t launch_all(const PrefillArgs& a) {
   PrepParams pp{a.q, a.k, a.g, a.beta, ws, sa, a.scale, static_cast<int>(items), 0, 0,
                 a.prologue ? 1 : 0};
   const unsigned prep_grid = static_cast<unsigned>(items);
-  hipLaunchKernelGGL((chunk_prep_kernel<D, TIn>), dim3(prep_grid), dim3(kThreads), 0, a.stream, pp);
+  if (D == 128 && std::is_same<TIn, bf16_t>::value)
+    hipLaunchKernelGGL(chunk_prep8_kernel, dim3(prep_grid), dim3(2 * kThreads), 0, a.stream, pp);
+  else
+    hipLaunchKernelGGL((chunk_prep_kernel<D, TIn>), dim3(prep_grid), dim3(kThreads), 0, a.stream, pp);
   err = hipGetLastError();
   if (err == hipSuccess) {
     // enough (sequence, head, dv slice) workgroups to cover the machine's 256 CUs;

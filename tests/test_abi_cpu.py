@@ -179,12 +179,15 @@ def test_binding_fails_loudly_without_library(tmp_path):
 
 def test_workspace_size_is_host_arithmetic(lib):
     """kda_chunk_fwd_workspace_size needs no device and follows the slot layout: 66,048
-    bytes per (chunk, head) for bf16 at d = 128 in two windows of 16 chunks plus the
-    carried fp32 states for B=4, T=4096, H=16; one slot per chunk for T=64."""
+    bytes per (chunk, head) for bf16 at d = 128, one slot per chunk (plus one per
+    sequence) on the two-kernel schedule (B=4, T=4096, H=16), two windows of 16 chunks
+    plus the carried fp32 states on the windowed one (B=1, T=4096, H=16), one window
+    for T=64."""
     f = lib.kda_chunk_fwd_workspace_size
     f.argtypes = [ctypes.c_int] * 6
     f.restype = ctypes.c_size_t
-    assert f(4, 4096, 16, 128, 128, 0) == 2 * 4 * 16 * 16 * 66048 + 4 * 16 * 128 * 128 * 4
+    assert f(4, 4096, 16, 128, 128, 0) == (4 * 4096 // 64 + 4) * 16 * 66048
+    assert f(1, 4096, 16, 128, 128, 0) == 2 * 1 * 16 * 16 * 66048 + 16 * 128 * 128 * 4
     assert f(2, 64, 3, 128, 128, 0) == 2 * 3 * 66048
     assert f(1, 64, 1, 128, 128, 1) == 0     # fp32 prefill is d = 64 only
     assert f(1, 64, 1, 100, 100, 0) == 0
