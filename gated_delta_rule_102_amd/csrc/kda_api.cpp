@@ -378,4 +378,24 @@ int kda_decode_step(const void* q, const void* k, const void* v, const void* g,
   return kda::launch_decode(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+int kda_decode_step_prologue(const void* q_raw, const void* k_raw, const void* v,
+                             const void* g_raw, const void* beta_raw, float* state, void* out,
+                             int B, int H, int dk, int dv, float scale, int dtype,
+                             hipStream_t stream) {
+  int rc = check_common(dk, dv, H, dtype);
+  if (rc != KDA_OK) return rc;
+  if (B <= 0) return KDA_ERR_SHAPE;
+  if (static_cast<int64_t>(B) * H > INT32_MAX / 2) return KDA_ERR_SHAPE;
+  const uintptr_t elt = dtype == KDA_F32 ? 4 : 2;
+  rc = check_ptrs({{q_raw, elt, true}, {k_raw, elt, true}, {v, elt, true}, {g_raw, elt, true},
+                   {beta_raw, elt, true}, {state, 16, true}, {out, elt, true}});
+  if (rc != KDA_OK) return rc;
+  rc = check_device();
+  if (rc != KDA_OK) return rc;
+  kda::DecodeArgs a{q_raw, k_raw, v, g_raw, beta_raw, state, out, B, H, dk, scale,
+                    dtype == KDA_F32, stream};
+  a.prologue = true;
+  return kda::launch_decode(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 }  // extern "C"

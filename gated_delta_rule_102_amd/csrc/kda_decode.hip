@@ -17,6 +17,11 @@
 // column reductions over rows (S'^T k, S'^T q) are summed inside the thread over
 // its R rows, then across the row groups through LDS.  The state makes exactly
 // one trip through registers: load, decay, reduce, update, store (non-temporal).
+//
+// PRO = true takes raw activations and applies the gate/normalisation prologue of
+// the prefill (q, k divided by sqrt(|x|^2 + 1e-6) and rounded to the input type,
+// e^g = max(e^-5, 1 / (1 + e^x)), beta = sigmoid(x)); the norms over dk are summed
+// over the row groups through LDS before the state products.
 
 #include "kda_device.h"
 #include "kda_launch.h"
@@ -25,7 +30,7 @@ namespace kda {
 
 namespace {
 
-template <int D, typename T>
+template <int D, typename T, bool PRO>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ g, const T* __restrict__ beta, float* __restrict__ state,
@@ -38,6 +43,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   __shared__ float red_u[RG][D];
   __shared__ float red_p[RG][D];
   __shared__ float red_kq[RG];
+  __shared__ float red_nrm[2][RG];
 
   const int bh = blockIdx.x;         // b * H + h
   const int tid = threadIdx.x;
@@ -55,13 +61,34 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   for (int r = 0; r < R; ++r) s[r] = S[(row0 + r) * CG + cg];
 
   float kr[R], qr[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    kr[r] = to_f32(kh[row0 + r]);
+    qr[r] = to_f32(qh[row0 + r]);
+  }
+  if constexpr (PRO) {   // unit L2 norm of k and q over dk, rounded to the input type
+    float nk = 0.f, nq = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) { nk += kr[r] * kr[r]; nq += qr[r] * qr[r]; }
+    if (cg == 0) { red_nrm[0][rg] = nk; red_nrm[1][rg] = nq; }
+    __syncthreads();
+    nk = 0.f; nq = 0.f;
+#pragma unroll
+    for (int j = 0; j < RG; ++j) { nk += red_nrm[0][j]; nq += red_nrm[1][j]; }
+    const float ik = __builtin_amdgcn_rsqf(nk + kNormEps), iq = __builtin_amdgcn_rsqf(nq + kNormEps);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      kr[r] = to_f32(Elem<T>::from(kr[r] * ik));
+      qr[r] = to_f32(Elem<T>::from(qr[r] * iq));
+    }
+  }
   float4 u = {0.f, 0.f, 0.f, 0.f}, p = {0.f, 0.f, 0.f, 0.f};
   float kq = 0.f;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const float dec = fast_exp2(to_f32(gh[row0 + r]) * kLog2e);
-    kr[r] = to_f32(kh[row0 + r]);
-    qr[r] = to_f32(qh[row0 + r]);
+    const float gx = to_f32(gh[row0 + r]);
+    const float dec = PRO ? fmaxf(kMinRetention, __builtin_amdgcn_rcpf(1.f + fast_exp2(gx * kLog2e)))
+                          : fast_exp2(gx * kLog2e);
     s[r].x *= dec; s[r].y *= dec; s[r].z *= dec; s[r].w *= dec;
     u.x += s[r].x * kr[r]; u.y += s[r].y * kr[r]; u.z += s[r].z * kr[r]; u.w += s[r].w * kr[r];
     p.x += s[r].x * qr[r]; p.y += s[r].y * qr[r]; p.z += s[r].z * qr[r]; p.w += s[r].w * qr[r];
@@ -84,7 +111,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     kq += red_kq[j];
   }
 
-  const float b = to_f32(beta[bh]);
+  const float bx = to_f32(beta[bh]);
+  const float b = PRO ? __builtin_amdgcn_rcpf(1.f + fast_exp2(-bx * kLog2e)) : bx;
   const T* vh = v + static_cast<int64_t>(bh) * D + 4 * cg;
   float4 dl;
   dl.x = b * (to_f32(vh[0]) - u.x);
@@ -115,7 +143,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 template <int D, typename T>
 hipError_t launch_decode_t(const DecodeArgs& a) {
   const int nbh = a.B * a.H;
-  hipLaunchKernelGGL((decode_step_kernel<D, T>), dim3(nbh), dim3(256), 0, a.stream,
+  auto kern = a.prologue ? decode_step_kernel<D, T, true> : decode_step_kernel<D, T, false>;
+  hipLaunchKernelGGL(kern, dim3(nbh), dim3(256), 0, a.stream,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                      static_cast<const T*>(a.v), static_cast<const T*>(a.g),
                      static_cast<const T*>(a.beta), a.state, static_cast<T*>(a.out), a.scale);

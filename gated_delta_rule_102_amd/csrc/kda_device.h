@@ -47,6 +47,11 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Gate and normalisation prologue constants: the retention factor's lower bound
+// e^-5 (log-decay >= -5) and the epsilon inside the L2 norm of q and k.
+constexpr float kMinRetention = 0.006737946999085467f;
+constexpr float kNormEps = 1e-6f;
+
 }  // namespace kda
 
 namespace kda {

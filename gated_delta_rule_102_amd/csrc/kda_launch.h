@@ -15,6 +15,7 @@ struct DecodeArgs {
   float scale;
   bool dtype_f32;
   hipStream_t stream;
+  bool prologue = false;       // q, k, g, beta raw: normalise / gate in the kernel
 };
 
 struct PrefillArgs {

@@ -43,10 +43,6 @@ namespace kda {
 namespace {
 
 constexpr int kC = 64;
-// Prologue constants: the retention factor's lower bound e^-5 (log-decay >= -5) and
-// the epsilon inside the L2 norm of q and k.
-constexpr float kMinRetention = 0.006737946999085467f;
-constexpr float kNormEps = 1e-6f;
 constexpr int kThreads = 256;
 
 // ---------------------------------------------------------------- helpers

@@ -22,7 +22,7 @@ _lib = None
 
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
            "kda_chunk_fwd_ws", "kda_chunk_fwd_prologue", "kda_chunk_fwd_varlen_prologue",
-           "kda_chunk_fwd_varlen_snapshots",
+           "kda_chunk_fwd_varlen_snapshots", "kda_decode_step_prologue",
            "kda_chunk_fwd_snapshots", "kda_chunk_fwd_varlen", "kda_decode_step", "kda_chunk_bwd",
            "kda_chunk_transition", "kda_state_compose")
 
@@ -73,6 +73,9 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd_varlen_snapshots.restype = i32
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp]
     lib.kda_decode_step.restype = i32
+    lib.kda_decode_step_prologue.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
+                                             i32, vp]
+    lib.kda_decode_step_prologue.restype = i32
     lib.kda_chunk_bwd.argtypes = [vp] * 14 + [i32, i32, i32, i32, i32, f32, i32, vp]
     lib.kda_chunk_bwd.restype = i32
     lib.kda_chunk_transition.argtypes = [vp] * 5 + [i32] * 6 + [vp]
@@ -361,9 +364,7 @@ def kda_chunk_fwd_varlen_snapshots(q, k, v, g, beta, cu_seqlens, scale=None, ini
     return out, final_state, snapshots, rows
 
 
-def kda_decode_step(q, k, v, g, beta, state, scale=None, out=None):
-    """One decode token.  q, k, g: [B,H,dk]; v: [B,H,dv]; beta: [B,H];
-    state: [B,H,dk,dv] fp32, updated in place.  Returns out [B,H,dv]."""
+def _decode(fn, q, k, v, g, beta, state, scale, out):
     lib = load_library()
     B, H, dk = q.shape
     dv = v.shape[-1]
@@ -377,10 +378,22 @@ def kda_decode_step(q, k, v, g, beta, state, scale=None, out=None):
         out = torch.empty((B, H, dv), dtype=dtype, device=device)
     _check(dict(out=out), dtype, device)
     scale = 1.0 / math.sqrt(dk) if scale is None else float(scale)
-    rc = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
-                             _ptr(out), B, H, dk, dv, scale, _dtype_code(q), _stream(q))
-    _raise("kda_decode_step", rc)
+    rc = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
+                          _ptr(out), B, H, dk, dv, scale, _dtype_code(q), _stream(q))
+    _raise(fn, rc)
     return out
+
+
+def kda_decode_step(q, k, v, g, beta, state, scale=None, out=None):
+    """One decode token.  q, k, g: [B,H,dk]; v: [B,H,dv]; beta: [B,H];
+    state: [B,H,dk,dv] fp32, updated in place.  Returns out [B,H,dv]."""
+    return _decode("kda_decode_step", q, k, v, g, beta, state, scale, out)
+
+
+def kda_decode_step_prologue(q_raw, k_raw, v, g_raw, beta_raw, state, scale=None, out=None):
+    """kda_decode_step on raw activations with the fused gate/normalisation prologue."""
+    return _decode("kda_decode_step_prologue", q_raw, k_raw, v, g_raw, beta_raw, state, scale,
+                   out)
 
 
 def kda_chunk_bwd(q, k, v, g, beta, grad_out, scale=None, initial_state=None,

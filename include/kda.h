@@ -322,6 +322,19 @@ int kda_decode_step(const void* q, const void* k, const void* v, const void* g,
                     const void* beta, float* state, void* out, int B, int H, int dk,
                     int dv, float scale, int dtype, hipStream_t stream);
 
+/*
+ * kda_decode_step on raw activations, with the gate and normalisation prologue of
+ * kda_chunk_fwd_prologue (same formulas: q and k divided by sqrt(|x|^2 + 1e-6)
+ * over dk and rounded to the input precision, g = max(-5, -softplus(g_raw)),
+ * beta = sigmoid(beta_raw)) applied inside the step.  Arguments, layouts and codes
+ * are those of kda_decode_step, with the raw tensors in place of q, k, g and beta.
+ * Same result as kda_chunk_fwd_prologue with T = 1 and final_state == initial_state.
+ */
+int kda_decode_step_prologue(const void* q_raw, const void* k_raw, const void* v,
+                             const void* g_raw, const void* beta_raw, float* state, void* out,
+                             int B, int H, int dk, int dv, float scale, int dtype,
+                             hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

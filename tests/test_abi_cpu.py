@@ -34,7 +34,7 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "kda_abi_version", "kda_status_string", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
         "kda_chunk_fwd_ws", "kda_chunk_fwd_prologue", "kda_chunk_fwd_varlen_prologue",
-        "kda_chunk_fwd_varlen_snapshots",
+        "kda_chunk_fwd_varlen_snapshots", "kda_decode_step_prologue",
         "kda_chunk_fwd_snapshots", "kda_chunk_fwd_varlen", "kda_decode_step", "kda_chunk_bwd",
         "kda_chunk_transition", "kda_state_compose"])
 
@@ -102,6 +102,14 @@ def test_argument_checks_precede_any_device_call(lib):
     d.restype = i32
     assert d(p, p, p, p, p, None, p, 2, 2, 128, 128, 0.1, 0, None) == -1
     assert d(p, p, p, p, p, vp(4104), p, 2, 2, 128, 128, 0.1, 0, None) == -5
+    dp = lib.kda_decode_step_prologue
+    dp.argtypes = [vp] * 7 + [i32] * 4 + [f32, i32, vp]
+    dp.restype = i32
+    assert dp(p, p, p, p, p, None, p, 2, 2, 128, 128, 0.1, 0, None) == -1
+    assert dp(p, p, p, p, p, p, p, 0, 2, 128, 128, 0.1, 0, None) == -2
+    assert dp(p, p, p, p, p, p, p, 2, 2, 96, 96, 0.1, 0, None) == -3
+    assert dp(p, p, p, p, p, vp(4104), p, 2, 2, 128, 128, 0.1, 0, None) == -5
+    assert dp(p, p, p, p, p, p, p, 2, 2, 128, 128, 0.1, 0, None) in (-6, -7)
     v = lib.kda_chunk_fwd_varlen
     v.argtypes = [vp] * 9 + [i32] * 5 + [f32, i32, vp]
     v.restype = i32

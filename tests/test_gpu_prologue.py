@@ -124,3 +124,26 @@ def test_varlen_prologue_matches_oracle(D, dtype):
                                   initial_state=s0)
     assert_close("varlen prologue out", out[0], ref_o, dtype)
     assert_close("varlen prologue state", fs, ref_s.reshape(N, H, D, D), dtype)
+
+
+@pytest.mark.parametrize("D,dtype", [(128, torch.bfloat16), (64, torch.bfloat16),
+                                     (64, torch.float32)])
+def test_decode_prologue_matches_oracle(D, dtype):
+    """kda_decode_step_prologue: 5 consecutive raw-activation steps on 3 sequences x 2
+    heads from a nonzero state, against prologue_np followed by the oracle over the
+    same 5 tokens (each step's output and the final state)."""
+    from gated_delta_rule_102_amd import kda
+    B, H, steps = 3, 2, 5
+    d = kin.make_prefill_raw(B, steps, H, D, D, dtype=dtype, seed=81, nonzero_state=True)
+    scale = 1.0 / math.sqrt(D)
+    g = {k: v.to(DEV) for k, v in d.items() if isinstance(v, torch.Tensor)}
+    st = g["initial_state"].clone()
+    outs = []
+    for t in range(steps):
+        outs.append(kda.kda_decode_step_prologue(
+            *(g[x][:, t].contiguous() for x in ("q_raw", "k_raw", "v", "g_raw", "beta_raw")),
+            st, scale=scale))
+    torch.cuda.synchronize()
+    ref_o, ref_s = _oracle(d, scale)
+    assert_close("decode prologue out", torch.stack(outs, 1), ref_o.reshape(B, steps, H, D), dtype)
+    assert_close("decode prologue state", st, ref_s.reshape(B, H, D, D), dtype)
