@@ -239,8 +239,9 @@ def main():
             "kernel_ms_avg": kern_avg_s * 1e3,
             "self_allocating_kda_chunk_fwd": {
                 "ms_per_call_events": self_alloc_ms, "ms_per_call_wall": self_alloc_wall * 1e3,
-                "note": "workspace from the library pool per call; hipFreeAsync blocks the "
-                        "host until the call's kernels ran, so the next call is enqueued late"},
+                "note": "workspace from the blocks the library keeps per device (taken after "
+                        "an event wait, released with an event record; nothing allocated or "
+                        "freed once warm)"},
             "token_heads_per_s": tokens * H / kern_avg_s,
             "tflops_tri": fl_tri / kern_avg_s / 1e12, "tflops_full": fl_full / kern_avg_s / 1e12,
             "mfma_frac_tri": fl_tri / kern_avg_s / 1e12 / BF16_MFMA_PEAK_TFLOPS,

@@ -10,6 +10,7 @@
 #include <cstdint>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "kda_launch.h"
 
@@ -100,18 +101,86 @@ hipError_t device_pool(hipMemPool_t* out) {
   return hipSuccess;
 }
 
+// Workspace blocks kept for reuse.  A call takes a free block of its device that
+// is large enough, after making its stream wait for the event recorded when the
+// block was last released (on whatever stream that was), or else allocates a new
+// block from the pool; releasing records that event and keeps the block.  No call
+// therefore frees memory (hipFreeAsync blocks the host on ROCm 7 until the stream
+// has drained), except free blocks too small for a request, which are returned to
+// the pool when a larger one is allocated.  Blocks live until the process ends.
+struct WsBlock {
+  void* p;
+  size_t bytes;
+  int dev;
+  bool busy;
+  bool used;          // `done` has been recorded
+  hipEvent_t done;
+  hipStream_t last;   // stream of the last release
+};
+std::mutex g_ws_mu;
+std::vector<WsBlock> g_ws;
+
 }  // namespace
 
 namespace kda {
 
 hipError_t ws_alloc(void** p, size_t bytes, hipStream_t stream) {
-  hipMemPool_t pool = nullptr;
-  const hipError_t err = device_pool(&pool);
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
-  return hipMallocFromPoolAsync(p, bytes, pool, stream);
+  hipMemPool_t pool = nullptr;
+  err = device_pool(&pool);
+  if (err != hipSuccess) return err;
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  int best = -1;
+  for (int i = 0; i < static_cast<int>(g_ws.size()); ++i) {
+    const WsBlock& b = g_ws[i];
+    if (b.busy || b.dev != dev || b.bytes < bytes) continue;
+    // prefer the block last used on this stream, then the smallest
+    if (best < 0 || (b.last == stream && g_ws[best].last != stream) ||
+        ((b.last == stream) == (g_ws[best].last == stream) && b.bytes < g_ws[best].bytes))
+      best = i;
+  }
+  if (best >= 0) {
+    WsBlock& b = g_ws[best];
+    if (b.used && (err = hipStreamWaitEvent(stream, b.done, 0)) != hipSuccess) return err;
+    b.busy = true;
+    *p = b.p;
+    return hipSuccess;
+  }
+  // free blocks of this device are all too small: give them back, then allocate
+  for (int i = static_cast<int>(g_ws.size()) - 1; i >= 0; --i) {
+    WsBlock& b = g_ws[i];
+    if (b.busy || b.dev != dev) continue;
+    if (b.used && (err = hipStreamWaitEvent(stream, b.done, 0)) != hipSuccess) return err;
+    if ((err = hipFreeAsync(b.p, stream)) != hipSuccess) return err;
+    hipEventDestroy(b.done);
+    g_ws.erase(g_ws.begin() + i);
+  }
+  WsBlock nb{nullptr, bytes, dev, true, false, nullptr, stream};
+  if ((err = hipEventCreateWithFlags(&nb.done, hipEventDisableTiming)) != hipSuccess) return err;
+  if ((err = hipMallocFromPoolAsync(&nb.p, bytes, pool, stream)) != hipSuccess) {
+    hipEventDestroy(nb.done);
+    return err;
+  }
+  g_ws.push_back(nb);
+  *p = nb.p;
+  return hipSuccess;
 }
 
-hipError_t ws_free(void* p, hipStream_t stream) { return hipFreeAsync(p, stream); }
+hipError_t ws_free(void* p, hipStream_t stream) {
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  for (WsBlock& b : g_ws) {
+    if (b.p != p || !b.busy) continue;
+    const hipError_t err = hipEventRecord(b.done, stream);
+    if (err != hipSuccess) return err;   // the block stays taken: never reused unordered
+    b.busy = false;
+    b.used = true;
+    b.last = stream;
+    return hipSuccess;
+  }
+  return hipErrorInvalidValue;
+}
 
 }  // namespace kda
 

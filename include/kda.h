@@ -25,16 +25,20 @@
  *
  * Conventions shared by every entry point
  *  - All tensor pointers are DEVICE pointers owned by the caller, contiguous and
- *    row-major.  The prefill, backward and transition entry points take one
- *    stream-ordered workspace per call from a memory pool the library creates on
- *    each device it runs on (hipMallocFromPoolAsync on `stream`, returned with
- *    hipFreeAsync on the same stream; the pool keeps freed memory for later
- *    calls until the process ends).  Prefill needs 66,048 bytes per 64-token
- *    chunk per head for bf16 at d = 128 (kda_chunk_fwd_workspace_size gives the
- *    exact figure); an allocation failure returns KDA_ERR_HIP.  On ROCm 7
- *    hipFreeAsync blocks the host until the call's kernels have run, so a caller
- *    that enqueues calls back to back passes its own workspace to
- *    kda_chunk_fwd_ws instead.  Decode allocates nothing.
+ *    row-major.  The prefill, backward and transition entry points use one
+ *    workspace per call, a block the library keeps for reuse on each device: a
+ *    call takes a free block at least as large as it needs, its stream first
+ *    waiting for the event recorded when the block was last released, or
+ *    allocates a new one (hipMallocFromPoolAsync on `stream` from a pool the
+ *    library creates per device); at the end it records that event on `stream`
+ *    and keeps the block.  Blocks are not freed until the process ends, except
+ *    free blocks too small for a request, returned with hipFreeAsync (which on
+ *    ROCm 7 blocks the host until the stream has drained) when a larger one is
+ *    allocated.  Concurrent calls on several streams take distinct blocks.
+ *    Prefill needs 66,048 bytes per 64-token chunk per head for bf16 at
+ *    d = 128 (kda_chunk_fwd_workspace_size gives the exact figure); an
+ *    allocation failure returns KDA_ERR_HIP.  kda_chunk_fwd_ws runs on a
+ *    workspace the caller owns instead.  Decode allocates nothing.
  *  - Alignment (KDA_ERR_ALIGN otherwise): prefill v and out 16 bytes, q, k, g and
  *    the states 4 bytes, beta its element size; decode state 16 bytes, every
  *    other pointer its element size.
@@ -49,9 +53,9 @@
  *    |k| <= 1.  Outside them the result is unspecified (never a memory fault).
  *  - Work is enqueued on `stream` and returns immediately; execution errors
  *    surface at the caller's next synchronisation.  No entry point keeps state
- *    between calls other than the workspace pool above (stream-ordered, so
- *    calls on different streams never share a live workspace); calls on
- *    different streams may overlap when their buffers do not.
+ *    between calls other than the workspace blocks above (event-ordered, so
+ *    calls never share a live workspace); calls on different streams may
+ *    overlap when their buffers do not.
  *  - Return value: KDA_OK, or a negative KDA_ERR_* code.  When a code other
  *    than KDA_OK is returned nothing was launched.
  */
@@ -247,9 +251,9 @@ int kda_chunk_fwd_varlen_snapshots(const void* q, const void* k, const void* v, 
  * (fp32 matrix cores).  bf16 inputs: every product over 32 or more terms takes
  * bf16 operands rounded from fp32 values, with fp32 accumulation, and the
  * per-chunk states, state gradients, Delta and dU are kept as bf16; the inverse,
- * the 16-term sub-tile products and the decayed products stay fp32.  The call
- * allocates a workspace with hipMallocAsync on `stream` and frees it on the same
- * stream, per 64-token chunk per head: 418,304 bytes for bf16 and 410,112 for
+ * the 16-term sub-tile products and the decayed products stay fp32.  The call's
+ * workspace (a reused block, see the conventions above) takes, per 64-token
+ * chunk per head, 418,304 bytes for bf16 and 410,112 for
  * fp32 at d = 128 (246,016 and 213,248 at d = 64), so T = 65,536 with 32 heads
  * needs about 14 GB; an allocation failure returns KDA_ERR_HIP.
  * Outputs must not alias inputs.
@@ -287,10 +291,9 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, co
  *                  token leftmost.
  * dk == dv in {64, 128} for both dtypes.  fp32 inputs are computed on fp32
  * operands; bf16 inputs on bf16 matrix-core operands with fp32 accumulation and
- * an fp32 state, the precision of the bf16 prefill.  Allocates a workspace per
- * 64-token chunk per head of 213,504 bytes for fp32 and 320,000 for bf16 at
- * d = 128 (147,712 and 213,248 at d = 64) with hipMallocAsync on `stream`, freed
- * on the same stream.
+ * an fp32 state, the precision of the bf16 prefill.  Its workspace (a reused
+ * block, see the conventions above) takes, per 64-token chunk per head, 213,504
+ * bytes for fp32 and 320,000 for bf16 at d = 128 (147,712 and 213,248 at d = 64).
  */
 int kda_chunk_transition(const void* q, const void* k, const void* g, const void* beta,
                          float* transition, int B, int T, int H, int dk, int dv, int dtype,

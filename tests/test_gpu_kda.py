@@ -410,3 +410,37 @@ def test_workspace_too_small_is_rejected():
     with pytest.raises(kda.KDAError) as e:
         kda.kda_chunk_fwd(g["q"], g["k"], g["v"], g["g"], g["beta"], workspace=small)
     assert e.value.status == -8
+
+
+def test_workspace_blocks_across_streams():
+    """Self-allocating calls reuse the library's workspace blocks: calls on two
+    streams, interleaved, a larger call after smaller ones (the free blocks that are
+    too small go back to the pool), and smaller ones again; every result is bitwise
+    equal to the same call run alone on the default stream."""
+    from gated_delta_rule_102_amd import kda
+    shapes = [(2, 300, 4), (1, 1100, 8), (4, 640, 16), (2, 130, 2)]
+    data = []
+    for i, (B, T, H) in enumerate(shapes):
+        d = kin.make_prefill(B, T, H, 128, 128, dtype=torch.bfloat16, seed=90 + i,
+                             nonzero_state=True)
+        data.append(_to(d, DEV))
+
+    def call(g):
+        return kda.kda_chunk_fwd(g["q"], g["k"], g["v"], g["g"], g["beta"],
+                                 initial_state=g["initial_state"])
+
+    refs = []
+    for g in data:
+        o, s = call(g)
+        torch.cuda.synchronize()
+        refs.append((o.clone(), s.clone()))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    results = []
+    for rep in range(3):
+        for i, g in enumerate(data):
+            with torch.cuda.stream(streams[(i + rep) % 2]):
+                o, s = call(g)
+                results.append((i, o, s))
+    torch.cuda.synchronize()
+    for i, o, s in results:
+        assert torch.equal(o, refs[i][0]) and torch.equal(s, refs[i][1]), f"call {i} differs"
