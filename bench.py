@@ -20,7 +20,8 @@ fp32 matrix peaks.  "snapshots" times the same prefill keeping the state every
 1024 tokens (kda_chunk_fwd_snapshots).  "context" times each step of the
 context-parallel schedule (segment prefill, kda_chunk_transition,
 kda_state_compose) at B=1, T=65536, H=32 in 8 segments, and the whole schedule
-on one GPU.  "cpu_baseline" times the fp64 CPU oracle on a bounded sample of the
+on one GPU.  "varlen" times kda_chunk_fwd_varlen on 64 packed sequences of
+log-uniform lengths in [1024, 65536] (32 heads).  "cpu_baseline" times the fp64 CPU oracle on a bounded sample of the
 same workload.  One JSON line is printed.
 """
 from __future__ import annotations
@@ -131,6 +132,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-snapshots", action="store_true")
     ap.add_argument("--no-context", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--pmc-copy", action="store_true",
                     help="only run a plain 256 MiB copy (counter calibration)")
     args = ap.parse_args()
@@ -350,6 +352,35 @@ def main():
                                "the products over 32 or more terms, fp32 for the rest",
         }
         del bset, cot
+        torch.cuda.empty_cache()
+
+    if not args.no_varlen:
+        # packed variable-length prefill: 64 sequences, log-uniform lengths in
+        # [1024, 65536], 32 heads, half at g = -5 (kda_chunk_fwd_varlen)
+        wv = kin.WORKLOADS["varlen_64seq"]
+        dvl = kin.make_workload(wv, device=dev)
+        vargs = [dvl[x] for x in ("q", "k", "v", "g", "beta")]
+        vscale = wv.scale_value()
+        total = int(dvl["cu_seqlens"][-1])
+        for _ in range(2):
+            kda.kda_chunk_fwd_varlen(*vargs, dvl["cu_seqlens"], vscale)
+        torch.cuda.synchronize()
+        nv = 3
+        va, vb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        va.record(stream)
+        for _ in range(nv):
+            kda.kda_chunk_fwd_varlen(*vargs, dvl["cu_seqlens"], vscale)
+        vb.record(stream)
+        torch.cuda.synchronize()
+        v_s = va.elapsed_time(vb) / nv / 1e3
+        vbytes = total * wv.H * (5 * wv.dk + 1) * 2 + 64 * wv.H * wv.dk * wv.dv * 4
+        result["varlen"] = {
+            "entry_point": "kda_chunk_fwd_varlen", "workload": "varlen_64seq",
+            "sequences": 64, "tokens": total, "H": wv.H, "d": wv.dk, "calls": nv,
+            "call_ms_avg": v_s * 1e3, "tokens_per_s": total / v_s,
+            "achieved_GBps": vbytes / v_s / 1e9, "hbm_frac": vbytes / v_s / 1e9 / HBM_PEAK_GBS,
+        }
+        del dvl, vargs
         torch.cuda.empty_cache()
 
     if not args.no_context:
