@@ -395,6 +395,36 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, co
   return kda::launch_backward(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+int kda_chunk_bwd_varlen(const void* q, const void* k, const void* v, const void* g,
+                         const void* beta, const float* initial_state, const void* grad_out,
+                         const float* grad_final_state, void* grad_q, void* grad_k, void* grad_v,
+                         void* grad_g, void* grad_beta, float* grad_initial_state,
+                         const int32_t* cu_seqlens, int N, int total_T, int H, int dk, int dv,
+                         float scale, int dtype, hipStream_t stream) {
+  int rc = check_common(dk, dv, H, dtype);
+  if (rc != KDA_OK) return rc;
+  if (N <= 0 || total_T <= 0 || total_T > INT32_MAX / 2) return KDA_ERR_SHAPE;
+  if (static_cast<int64_t>(N) * H > (1 << 24)) return KDA_ERR_SHAPE;
+  if ((static_cast<int64_t>(total_T) / 64 + N + 1) * H > INT32_MAX) return KDA_ERR_SHAPE;
+  if (cu_seqlens == nullptr) return KDA_ERR_NULL;
+  const uintptr_t elt = dtype == KDA_F32 ? 4 : 2;
+  rc = check_ptrs({{q, 16, true}, {k, 16, true}, {v, 16, true}, {g, 16, true},
+                   {beta, elt, true}, {grad_out, 16, true}, {grad_q, elt, true},
+                   {grad_k, elt, true}, {grad_v, elt, true}, {grad_g, elt, true},
+                   {grad_beta, elt, true}, {initial_state, 4, false},
+                   {grad_final_state, 4, false}, {grad_initial_state, 4, false},
+                   {cu_seqlens, 4, true}});
+  if (rc != KDA_OK) return rc;
+  rc = check_device();
+  if (rc != KDA_OK) return rc;
+  kda::BackwardArgs a{q, k, v, g, beta, initial_state, grad_out, grad_final_state,
+                      grad_q, grad_k, grad_v, grad_g, grad_beta, grad_initial_state,
+                      N, 0, H, dk, scale, dtype == KDA_F32, stream};
+  a.cu_seqlens = cu_seqlens;
+  a.total_T = total_T;
+  return kda::launch_backward(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 int kda_chunk_transition(const void* q, const void* k, const void* g, const void* beta,
                          float* transition, int B, int T, int H, int dk, int dv, int dtype,
                          hipStream_t stream) {

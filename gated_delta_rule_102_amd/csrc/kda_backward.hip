@@ -42,8 +42,8 @@ __global__ __launch_bounds__(kScanThreads) void bwd_fwd_scan_kernel(const TIn* _
                                                            const float* __restrict__ s0,
                                                            const float* __restrict__ ws,
                                                            float* __restrict__ st,
-                                                           float* __restrict__ dl, int T, int H,
-                                                           int nc, int BH) {
+                                                           float* __restrict__ dl, SeqMap m,
+                                                           int BH) {
   constexpr bool BF = IsBf16<TIn>::value;   // bf16 matrix-core operands for bf16 inputs
   using L = BwdLayout<D>;
   using ST = ScanTiles<D>;
@@ -61,7 +61,8 @@ __global__ __launch_bounds__(kScanThreads) void bwd_fwd_scan_kernel(const TIn* _
   constexpr int NSL = D / SL;
   int bh, c0;
   if (!scan_block<NSL>(BH, bh, c0)) return;
-  const int b = bh / H, h = bh - b * H;
+  const int H = m.H, h = bh % m.H;
+  const StreamPos sp = stream_pos(m, bh);
 
   f32x4_t S[ST::NTW];
 #pragma unroll
@@ -75,17 +76,17 @@ __global__ __launch_bounds__(kScanThreads) void bwd_fwd_scan_kernel(const TIn* _
   ITile<kScanThreads, SL, TIn> t_v;
   float lm;
   auto issue = [&](int c) {
-    const float* w = ws + (static_cast<int64_t>(bh) * nc + c) * L::WS;
-    const int64_t row0 = (static_cast<int64_t>(b) * T + static_cast<int64_t>(c) * CR) * H + h;
+    const float* w = ws + (sp.item0 + c * sp.istride) * L::WS;
+    const int64_t row0 = (static_cast<int64_t>(sp.tok0) + static_cast<int64_t>(c) * CR) * H + h;
     t_tb.load(w + L::TB, CR);
     t_w.load(w + L::W, D);
     t_kt.load(w + L::KT, D);
-    t_v.load(v + row0 * D + c0, static_cast<int64_t>(H) * D, min(CR, T - c * CR));
+    t_v.load(v + row0 * D + c0, static_cast<int64_t>(H) * D, min(CR, sp.len - c * CR));
     lm = w[L::LAM + (tid & (D - 1))];
   };
-  issue(0);
-  for (int c = 0; c < nc; ++c) {
-    const int64_t item = static_cast<int64_t>(bh) * nc + c;
+  if (sp.nch > 0) issue(0);
+  for (int c = 0; c < sp.nch; ++c) {
+    const int64_t item = sp.item0 + c * sp.istride;
     {
       t_tb.pin_all();
       t_w.pin_all();
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(kScanThreads) void bwd_fwd_scan_kernel(const TIn* _
     }
     // the next chunk's loads go out before this step's stores: loads and stores
     // retire in order, so the next wait for those loads does not wait for the stores
-    if (c + 1 < nc) issue(c + 1);
+    if (c + 1 < sp.nch) issue(c + 1);
 #pragma unroll
     for (int x = 0; x < ST::NTW; ++x) {
       const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
@@ -139,8 +140,8 @@ __global__ __launch_bounds__(kScanThreads) void bwd_scan_kernel(const TIn* __res
                                                        float* __restrict__ dst,
                                                        float* __restrict__ du,
                                                        TIn* __restrict__ dv,
-                                                       float* __restrict__ ds0, int T, int H,
-                                                       int nc, int BH) {
+                                                       float* __restrict__ ds0, SeqMap m,
+                                                       int BH) {
   // fp32 operands throughout: the bf16 form needs more registers than the two
   // wavefronts per SIMD leave, and spills cost more than it saves
   using L = BwdLayout<D>;
@@ -160,7 +161,8 @@ __global__ __launch_bounds__(kScanThreads) void bwd_scan_kernel(const TIn* __res
   constexpr int NSL = D / SL;
   int bh, c0;
   if (!scan_block<NSL>(BH, bh, c0)) return;
-  const int b = bh / H, h = bh - b * H;
+  const int H = m.H, h = bh % m.H;
+  const StreamPos sp = stream_pos(m, bh);
   const int64_t rs = static_cast<int64_t>(H) * D;
 
   f32x4_t dS[ST::NTW];
@@ -175,20 +177,20 @@ __global__ __launch_bounds__(kScanThreads) void bwd_scan_kernel(const TIn* __res
   ITile<kScanThreads, SL, TIn> t_do;
   float lm;
   auto issue = [&](int c) {
-    const float* w = ws + (static_cast<int64_t>(bh) * nc + c) * L::WS;
-    const int64_t row0 = (static_cast<int64_t>(b) * T + static_cast<int64_t>(c) * CR) * H + h;
+    const float* w = ws + (sp.item0 + c * sp.istride) * L::WS;
+    const int64_t row0 = (static_cast<int64_t>(sp.tok0) + static_cast<int64_t>(c) * CR) * H + h;
     t_kt.load(w + L::KT, D);
     t_w.load(w + L::W, D);
     t_p.load(w + L::PP, CR);
     t_tb.load(w + L::TB, CR);
-    t_do.load(dout + row0 * D + c0, rs, min(CR, T - c * CR));
+    t_do.load(dout + row0 * D + c0, rs, min(CR, sp.len - c * CR));
     lm = w[L::LAM + (tid & (D - 1))];
   };
-  issue(nc - 1);
-  for (int c = nc - 1; c >= 0; --c) {
-    const int64_t item = static_cast<int64_t>(bh) * nc + c;
-    const int nrow = min(CR, T - c * CR);
-    const int64_t row0 = (static_cast<int64_t>(b) * T + static_cast<int64_t>(c) * CR) * H + h;
+  if (sp.nch > 0) issue(sp.nch - 1);
+  for (int c = sp.nch - 1; c >= 0; --c) {
+    const int64_t item = sp.item0 + c * sp.istride;
+    const int nrow = min(CR, sp.len - c * CR);
+    const int64_t row0 = (static_cast<int64_t>(sp.tok0) + static_cast<int64_t>(c) * CR) * H + h;
     {
       t_kt.pin_all();
       t_w.pin_all();
@@ -292,8 +294,8 @@ __device__ __forceinline__ void stage_bf16_t(const ITile<NT, COLS, bf16_t>& t, _
 template <int D>
 __global__ __launch_bounds__(kScanThreads) void bwd_fwd_scan_bf16_kernel(
     const bf16_t* __restrict__ v, const float* __restrict__ s0, const float* __restrict__ ws,
-    const __bf16* __restrict__ wsb, __bf16* __restrict__ st, __bf16* __restrict__ dl, int T, int H,
-    int nc, int BH) {
+    const __bf16* __restrict__ wsb, __bf16* __restrict__ st, __bf16* __restrict__ dl, SeqMap m,
+    int BH) {
   using L = BwdLayout<D>;
   using ST = ScanTiles<D>;
   constexpr int LB = D + 8, L64 = CR + 8;   // bf16 leading dimensions (16-byte rows)
@@ -310,7 +312,8 @@ __global__ __launch_bounds__(kScanThreads) void bwd_fwd_scan_bf16_kernel(
   constexpr int NSL = D / SL;
   int bh, c0;
   if (!scan_block<NSL>(BH, bh, c0)) return;
-  const int b = bh / H, h = bh - b * H;
+  const int H = m.H, h = bh % m.H;
+  const StreamPos sp = stream_pos(m, bh);
 
   f32x4_t S[ST::NTW];
 #pragma unroll
@@ -324,18 +327,18 @@ __global__ __launch_bounds__(kScanThreads) void bwd_fwd_scan_bf16_kernel(
   ITile<kScanThreads, SL, bf16_t> t_v;
   float lm;
   auto issue = [&](int c) {
-    const int64_t item = static_cast<int64_t>(bh) * nc + c;
+    const int64_t item = sp.item0 + c * sp.istride;
     const __bf16* wb = wsb + item * L::WSB;
-    const int64_t row0 = (static_cast<int64_t>(b) * T + static_cast<int64_t>(c) * CR) * H + h;
+    const int64_t row0 = (static_cast<int64_t>(sp.tok0) + static_cast<int64_t>(c) * CR) * H + h;
     t_tb.load(wb + L::BTB);
     t_w.load(wb + L::BW);
     t_ktt.load(wb + L::BKTT);
-    t_v.load(v + row0 * D + c0, static_cast<int64_t>(H) * D, min(CR, T - c * CR));
+    t_v.load(v + row0 * D + c0, static_cast<int64_t>(H) * D, min(CR, sp.len - c * CR));
     lm = ws[item * L::WS + L::LAM + (tid & (D - 1))];
   };
-  issue(0);
-  for (int c = 0; c < nc; ++c) {
-    const int64_t item = static_cast<int64_t>(bh) * nc + c;
+  if (sp.nch > 0) issue(0);
+  for (int c = 0; c < sp.nch; ++c) {
+    const int64_t item = sp.item0 + c * sp.istride;
     t_tb.pin_all();
     t_w.pin_all();
     t_ktt.pin_all();
@@ -347,7 +350,7 @@ __global__ __launch_bounds__(kScanThreads) void bwd_fwd_scan_bf16_kernel(
     stage_bf16_t(t_v, VT, L64);
     if (tid < D) Lm[tid] = lm;
     // the next chunk's loads go out before this step's global stores
-    if (c + 1 < nc) issue(c + 1);
+    if (c + 1 < sp.nch) issue(c + 1);
 #pragma unroll
     for (int x = 0; x < ST::NTW; ++x) {
       const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
@@ -382,7 +385,7 @@ template <int D>
 __global__ __launch_bounds__(kScanThreads) void bwd_scan_bf16_kernel(
     const bf16_t* __restrict__ dout, const float* __restrict__ dsT, const float* __restrict__ ws,
     const __bf16* __restrict__ wsb, __bf16* __restrict__ dst, __bf16* __restrict__ du,
-    bf16_t* __restrict__ dv, float* __restrict__ ds0, int T, int H, int nc, int BH) {
+    bf16_t* __restrict__ dv, float* __restrict__ ds0, SeqMap m, int BH) {
   using L = BwdLayout<D>;
   using ST = ScanTiles<D>;
   constexpr int LB = D + 8, L64 = CR + 8;
@@ -401,7 +404,8 @@ __global__ __launch_bounds__(kScanThreads) void bwd_scan_bf16_kernel(
   constexpr int NSL = D / SL;
   int bh, c0;
   if (!scan_block<NSL>(BH, bh, c0)) return;
-  const int b = bh / H, h = bh - b * H;
+  const int H = m.H, h = bh % m.H;
+  const StreamPos sp = stream_pos(m, bh);
   const int64_t rs = static_cast<int64_t>(H) * D;
 
   f32x4_t dS[ST::NTW];
@@ -416,22 +420,22 @@ __global__ __launch_bounds__(kScanThreads) void bwd_scan_bf16_kernel(
   ITile<kScanThreads, SL, bf16_t> t_do;
   float lm;
   auto issue = [&](int c) {
-    const int64_t item = static_cast<int64_t>(bh) * nc + c;
+    const int64_t item = sp.item0 + c * sp.istride;
     const __bf16* wb = wsb + item * L::WSB;
-    const int64_t row0 = (static_cast<int64_t>(b) * T + static_cast<int64_t>(c) * CR) * H + h;
+    const int64_t row0 = (static_cast<int64_t>(sp.tok0) + static_cast<int64_t>(c) * CR) * H + h;
     t_kt.load(wb + L::BKT);
     t_wt.load(wb + L::BWT);
     t_qpt.load(wb + L::BQPT);
     t_pt.load(wb + L::BPT);
     t_tbt.load(wb + L::BTBT);
-    t_do.load(dout + row0 * D + c0, rs, min(CR, T - c * CR));
+    t_do.load(dout + row0 * D + c0, rs, min(CR, sp.len - c * CR));
     lm = ws[item * L::WS + L::LAM + (tid & (D - 1))];
   };
-  issue(nc - 1);
-  for (int c = nc - 1; c >= 0; --c) {
-    const int64_t item = static_cast<int64_t>(bh) * nc + c;
-    const int nrow = min(CR, T - c * CR);
-    const int64_t row0 = (static_cast<int64_t>(b) * T + static_cast<int64_t>(c) * CR) * H + h;
+  if (sp.nch > 0) issue(sp.nch - 1);
+  for (int c = sp.nch - 1; c >= 0; --c) {
+    const int64_t item = sp.item0 + c * sp.istride;
+    const int nrow = min(CR, sp.len - c * CR);
+    const int64_t row0 = (static_cast<int64_t>(sp.tok0) + static_cast<int64_t>(c) * CR) * H + h;
     t_kt.pin_all();
     t_wt.pin_all();
     t_qpt.pin_all();
@@ -736,7 +740,7 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_chunk_kernel(
     const TIn* __restrict__ v, const TIn* __restrict__ dout, const StateElem<TIn>* __restrict__ st,
     const StateElem<TIn>* __restrict__ dst, const StateElem<TIn>* __restrict__ dl,
     const StateElem<TIn>* __restrict__ du, const float* __restrict__ ws, TIn* __restrict__ dq,
-    TIn* __restrict__ dk, TIn* __restrict__ dg, TIn* __restrict__ dbeta, int T, int H, int nc,
+    TIn* __restrict__ dk, TIn* __restrict__ dg, TIn* __restrict__ dbeta, SeqMap m,
     float scale) {
   constexpr bool BF = IsBf16<TIn>::value;   // bf16 matrix-core operands for bf16 inputs
   using L = BwdLayout<D>;
@@ -768,10 +772,12 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_chunk_kernel(
   float* FP = Rf + 4 * D;        // [6][D] e^{R_I - R_J}
   const int tid = threadIdx.x, wave = tid >> 6;
   const int l16 = lane16(), g4 = lane_g4();
+  const int H = m.H;
   const int64_t rs = static_cast<int64_t>(H) * D;
   constexpr int CT = D / 16;
   const int64_t item = blockIdx.x;
-  const ChunkPos p = chunk_pos(blockIdx.x, T, H, nc);
+  const ChunkPos p = chunk_pos(blockIdx.x, m);
+  if (!p.valid) return;            // unused item of packed sequences
   const float* w = ws + item * L::WS;
 
   GTile<kNnThreads, CR, D> t_g;
@@ -1072,8 +1078,13 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_chunk_kernel(
 template <int D, typename TIn>
 hipError_t launch_backward_t(const BackwardArgs& a) {
   using L = BwdLayout<D>;
-  const int nc = (a.T + CR - 1) / CR;
-  const int64_t items = static_cast<int64_t>(a.B) * a.H * nc;
+  const int nc = a.cu_seqlens == nullptr ? (a.T + CR - 1) / CR : 0;
+  const SeqMap sm{a.cu_seqlens, a.B, a.T, a.cu_seqlens == nullptr ? a.B * a.T : a.total_T, a.H, nc};
+  // fixed length: every chunk of every stream; packed: the slot numbering of the
+  // forward (some items unused)
+  const int64_t items = a.cu_seqlens == nullptr
+                            ? static_cast<int64_t>(a.B) * a.H * nc
+                            : (static_cast<int64_t>(a.total_T + CR - 1) / CR + a.B) * a.H;
   constexpr bool BF = IsBf16<TIn>::value;
   // per chunk, in floats: the fp32 operands, then the states, state gradients, Delta
   // and dU (fp32, or bf16 for bf16 inputs: half the floats), then for bf16 inputs the
@@ -1104,27 +1115,27 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
   const int BH = a.B * a.H;
   const int scan_blocks = scan_grid(BH, D / SL);
   hipLaunchKernelGGL((chunk_ops_kernel<D, TIn, false, true>), dim3(items), dim3(kOpsThreads), 0, a.stream, q, k, g, beta,
-                     ws, wsb, a.T, a.H, nc, a.scale);
+                     ws, wsb, sm, a.scale);
   if constexpr (IsBf16<TIn>::value) {
     hipLaunchKernelGGL((bwd_fwd_scan_bf16_kernel<D>), dim3(scan_blocks), dim3(kScanThreads), 0,
-                       a.stream, v, a.initial_state, ws, wsb, stb, dlb, a.T, a.H, nc, BH);
+                       a.stream, v, a.initial_state, ws, wsb, stb, dlb, sm, BH);
     hipLaunchKernelGGL((bwd_scan_bf16_kernel<D>), dim3(scan_blocks), dim3(kScanThreads), 0,
                        a.stream, dout, a.d_final_state, ws, wsb, dstb, dub,
-                       static_cast<TIn*>(a.dv), a.d_initial_state, a.T, a.H, nc, BH);
+                       static_cast<TIn*>(a.dv), a.d_initial_state, sm, BH);
     hipLaunchKernelGGL((bwd_grad_chunk_kernel<D, TIn>), dim3(items), dim3(kNnThreads), 0, a.stream, q,
                        k, beta, v, dout, stb, dstb, dlb, dub, ws, static_cast<TIn*>(a.dq),
                        static_cast<TIn*>(a.dk), static_cast<TIn*>(a.dg), static_cast<TIn*>(a.dbeta),
-                       a.T, a.H, nc, a.scale);
+                       sm, a.scale);
   } else {
     hipLaunchKernelGGL((bwd_fwd_scan_kernel<D, TIn>), dim3(scan_blocks), dim3(kScanThreads), 0, a.stream, v,
-                       a.initial_state, ws, st, dl, a.T, a.H, nc, BH);
+                       a.initial_state, ws, st, dl, sm, BH);
     hipLaunchKernelGGL((bwd_scan_kernel<D, TIn>), dim3(scan_blocks), dim3(kScanThreads), 0, a.stream, dout,
                        a.d_final_state, ws, dst, du, static_cast<TIn*>(a.dv), a.d_initial_state,
-                       a.T, a.H, nc, BH);
+                       sm, BH);
     hipLaunchKernelGGL((bwd_grad_chunk_kernel<D, TIn>), dim3(items), dim3(kNnThreads), 0, a.stream, q,
                        k, beta, v, dout, st, dst, dl, du, ws, static_cast<TIn*>(a.dq),
                        static_cast<TIn*>(a.dk), static_cast<TIn*>(a.dg), static_cast<TIn*>(a.dbeta),
-                       a.T, a.H, nc, a.scale);
+                       sm, a.scale);
   }
   err = hipGetLastError();
   const hipError_t ferr = ws_free(buf, a.stream);

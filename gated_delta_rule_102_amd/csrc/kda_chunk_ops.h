@@ -374,18 +374,81 @@ __device__ __forceinline__ f32x4_t mmb(f32x4_t acc, const __bf16* a, int lda, co
 // sub-tile pairs J < I of a 64-row chunk -> 0..5
 __device__ __forceinline__ int pair_index(int I, int J) { return I * (I - 1) / 2 + J; }
 
+// The sequences of a call: N sequences of T tokens (cu == null; chunk c of stream
+// (n, h) is item (n * H + h) * nc + c), or N packed sequences whose tokens are
+// [cu[n], cu[n+1]) of total_T (clamped into [0, total_T]; chunk c of stream (n, h)
+// is item (floor(cu[n] / 64) + n + c) * H + h, ranges that never overlap).
+struct SeqMap {
+  const int32_t* cu;
+  int N, T, total_T, H, nc;
+};
+
+__device__ __forceinline__ void seq_span(const SeqMap& m, int n, int& tok0, int& len) {
+  if (m.cu == nullptr) {
+    tok0 = n * m.T;
+    len = m.T;
+  } else {
+    const int x0 = min(max(m.cu[n], 0), m.total_T);
+    const int x1 = min(max(m.cu[n + 1], x0), m.total_T);
+    tok0 = x0;
+    len = x1 - x0;
+  }
+}
+
+// Stream bh = n * H + h: its tokens, chunk count, and the items of its chunks.
+struct StreamPos {
+  int tok0, len, nch;
+  int64_t item0, istride;   // item of chunk c: item0 + c * istride
+};
+__device__ __forceinline__ StreamPos stream_pos(const SeqMap& m, int bh) {
+  StreamPos s;
+  const int n = bh / m.H, h = bh - n * m.H;
+  seq_span(m, n, s.tok0, s.len);
+  s.nch = (s.len + CR - 1) / CR;
+  if (m.cu == nullptr) {
+    s.item0 = static_cast<int64_t>(bh) * m.nc;
+    s.istride = 1;
+  } else {
+    s.item0 = (static_cast<int64_t>(s.tok0 / CR) + n) * m.H + h;
+    s.istride = m.H;
+  }
+  return s;
+}
+
 struct ChunkPos {
   int b, h, c, nrow;
-  int64_t row0;   // (b * T + first token) * H + h: token-row index of the chunk's row 0
+  int64_t row0;   // (first token of the chunk) * H + h: token-row index of its row 0
+  bool valid;     // false for the unused items of packed sequences
 };
-__device__ __forceinline__ ChunkPos chunk_pos(int item, int T, int H, int nc) {
+__device__ __forceinline__ ChunkPos chunk_pos(int item, const SeqMap& m) {
   ChunkPos p;
-  p.c = item % nc;
-  const int bh = item / nc;
-  p.b = bh / H;
-  p.h = bh - p.b * H;
-  p.nrow = min(CR, T - p.c * CR);
-  p.row0 = (static_cast<int64_t>(p.b) * T + static_cast<int64_t>(p.c) * CR) * H + p.h;
+  const int H = m.H;
+  if (m.cu == nullptr) {
+    p.c = item % m.nc;
+    const int bh = item / m.nc;
+    p.b = bh / H;
+    p.h = bh - p.b * H;
+    p.nrow = min(CR, m.T - p.c * CR);
+    p.row0 = (static_cast<int64_t>(p.b) * m.T + static_cast<int64_t>(p.c) * CR) * H + p.h;
+    p.valid = true;
+    return p;
+  }
+  const int slot = item / H;
+  p.h = item - slot * H;
+  int lo = 0, hi = m.N - 1;   // largest n whose first slot is at most `slot`
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    int t0, l;
+    seq_span(m, mid, t0, l);
+    if (t0 / CR + mid <= slot) lo = mid; else hi = mid - 1;
+  }
+  int t0, len;
+  seq_span(m, lo, t0, len);
+  p.b = lo;
+  p.c = slot - (t0 / CR + lo);
+  p.valid = p.c >= 0 && p.c * CR < len;
+  p.nrow = p.valid ? min(CR, len - p.c * CR) : 0;
+  p.row0 = (static_cast<int64_t>(t0) + static_cast<int64_t>(p.c) * CR) * H + p.h;
   return p;
 }
 
@@ -407,8 +470,8 @@ __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __res
                                                        const TIn* __restrict__ g,
                                                        const TIn* __restrict__ beta,
                                                        float* __restrict__ ws,
-                                                       __bf16* __restrict__ wsb, int T, int H,
-                                                       int nc, float scale) {
+                                                       __bf16* __restrict__ wsb, SeqMap sm_,
+                                                       float scale) {
   constexpr bool BF = IsBf16<TIn>::value && !EXACT;
   using L = BwdLayout<D>;
   constexpr int LD = L::LD;
@@ -423,7 +486,9 @@ __global__ __launch_bounds__(kOpsThreads) void chunk_ops_kernel(const TIn* __res
   float* BT = FP + 6 * D;         // beta
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane16(), g4 = lane_g4();
-  const ChunkPos p = chunk_pos(blockIdx.x, T, H, nc);
+  const ChunkPos p = chunk_pos(blockIdx.x, sm_);
+  if (!p.valid) return;            // unused item of packed sequences
+  const int H = sm_.H;
   const int64_t rs = static_cast<int64_t>(H) * D;
   const TIn* qc = q + p.row0 * D;
   const TIn* kc = k + p.row0 * D;

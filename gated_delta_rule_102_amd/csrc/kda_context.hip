@@ -240,15 +240,15 @@ hipError_t launch_transition_t(const TransitionArgs& a) {
   if constexpr (BF) {   // bf16 operands, the prefill's precision
     hipLaunchKernelGGL((chunk_ops_kernel<D, TIn, false, false>), dim3(items), dim3(kOpsThreads), 0,
                        a.stream, static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
-                       static_cast<const TIn*>(a.g), static_cast<const TIn*>(a.beta), ws, wsb, a.T,
-                       a.H, nc, 1.0f);
+                       static_cast<const TIn*>(a.g), static_cast<const TIn*>(a.beta), ws, wsb,
+                       SeqMap{nullptr, a.B, a.T, a.B * a.T, a.H, nc}, 1.0f);
     hipLaunchKernelGGL((transition_scan_bf16_kernel<D>), dim3(scan_grid(BH, D / SL)),
                        dim3(kScanThreads), 0, a.stream, ws, wsb, a.transition, nc, BH);
   } else {
     hipLaunchKernelGGL((chunk_ops_kernel<D, TIn, true, false>), dim3(items), dim3(kOpsThreads), 0,
                        a.stream, static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
                        static_cast<const TIn*>(a.g), static_cast<const TIn*>(a.beta), ws, nullptr,
-                       a.T, a.H, nc, 1.0f);
+                       SeqMap{nullptr, a.B, a.T, a.B * a.T, a.H, nc}, 1.0f);
     hipLaunchKernelGGL((transition_scan_kernel<D>), dim3(scan_grid(BH, D / SL)), dim3(256), 0,
                        a.stream, ws, a.transition, nc, BH);
   }

@@ -51,6 +51,8 @@ struct BackwardArgs {
   float scale;
   bool dtype_f32;
   hipStream_t stream;
+  const int32_t* cu_seqlens = nullptr;   // packed sequences: B offsets + 1 (device); T unused
+  int total_T = 0;                       // tokens in the packed buffers
 };
 
 struct TransitionArgs {

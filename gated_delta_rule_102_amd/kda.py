@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 KDA_BF16, KDA_F32 = 0, 1
 _lib = None
 
-EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
+EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_bwd_varlen", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
            "kda_chunk_fwd_ws", "kda_chunk_fwd_prologue", "kda_chunk_fwd_varlen_prologue",
            "kda_chunk_fwd_varlen_snapshots", "kda_decode_step_prologue",
            "kda_chunk_fwd_snapshots", "kda_chunk_fwd_varlen", "kda_decode_step", "kda_chunk_bwd",
@@ -78,6 +78,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_decode_step_prologue.restype = i32
     lib.kda_chunk_bwd.argtypes = [vp] * 14 + [i32, i32, i32, i32, i32, f32, i32, vp]
     lib.kda_chunk_bwd.restype = i32
+    lib.kda_chunk_bwd_varlen.argtypes = [vp] * 15 + [i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.kda_chunk_bwd_varlen.restype = i32
     lib.kda_chunk_transition.argtypes = [vp] * 5 + [i32] * 6 + [vp]
     lib.kda_chunk_transition.restype = i32
     lib.kda_state_compose.argtypes = [vp] * 4 + [i32] * 5 + [vp]
@@ -420,6 +422,39 @@ def kda_chunk_bwd(q, k, v, g, beta, grad_out, scale=None, initial_state=None,
                            _ptr(grad_out), _ptr(grad_final_state), *(_ptr(x) for x in grads),
                            _ptr(ds0), B, T, H, dk, dv, scale, _dtype_code(q), _stream(q))
     _raise("kda_chunk_bwd", rc)
+    return (*grads, ds0)
+
+
+def kda_chunk_bwd_varlen(q, k, v, g, beta, grad_out, cu_seqlens, scale=None, initial_state=None,
+                         grad_final_state=None, need_initial_state_grad=True):
+    """kda_chunk_bwd for packed sequences (layouts of kda_chunk_fwd_varlen: q, k, g
+    [1,total_T,H,dk] or [total_T,H,dk]; cu_seqlens int32 [N+1] on the device).
+    Returns ``(grad_q, grad_k, grad_v, grad_g, grad_beta, grad_initial_state [N,H,dk,dv]
+    or None)``; token gradients outside every sequence are zero."""
+    lib = load_library()
+    H, dk = q.shape[-2], q.shape[-1]
+    dv = v.shape[-1]
+    total_T = q.numel() // (H * dk)
+    N = cu_seqlens.numel() - 1
+    dtype, device = q.dtype, q.device
+    _check(dict(q=q, k=k, v=v, g=g, beta=beta, grad_out=grad_out), dtype, device)
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != device:
+        raise ValueError("cu_seqlens must be int32 on the same device")
+    if k.shape != q.shape or g.shape != q.shape or v.numel() != total_T * H * dv \
+            or beta.numel() != total_T * H or grad_out.shape != v.shape:
+        raise ValueError("shape mismatch among q, k, v, g, beta, grad_out")
+    _check_state("initial_state", initial_state, (N, H, dk, dv), device)
+    _check_state("grad_final_state", grad_final_state, (N, H, dk, dv), device)
+    grads = [torch.zeros_like(x) for x in (q, k, v, g, beta)]
+    ds0 = torch.empty((N, H, dk, dv), dtype=torch.float32, device=device) \
+        if need_initial_state_grad else None
+    scale = 1.0 / math.sqrt(dk) if scale is None else float(scale)
+    rc = lib.kda_chunk_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                  _ptr(initial_state), _ptr(grad_out), _ptr(grad_final_state),
+                                  *(_ptr(x) for x in grads), _ptr(ds0),
+                                  _ptr(cu_seqlens.contiguous()), N, total_T, H, dk, dv, scale,
+                                  _dtype_code(q), _stream(q))
+    _raise("kda_chunk_bwd_varlen", rc)
     return (*grads, ds0)
 
 

@@ -265,6 +265,27 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, co
                   int dk, int dv, float scale, int dtype, hipStream_t stream);
 
 /*
+ * kda_chunk_bwd for packed variable-length input (the layout of
+ * kda_chunk_fwd_varlen): the gradients of
+ *     L = sum over tokens of <grad_out, out> + <grad_final_state, final_state>
+ * for kda_chunk_fwd_varlen's inputs.
+ *  q, k, g, grad_q, grad_k, grad_g [total_T, H, dk];  v, grad_out, grad_v
+ *  [total_T, H, dv];  beta, grad_beta [total_T, H]  (dtype);
+ *  initial_state, grad_final_state, grad_initial_state  [N, H, dk, dv] fp32 or NULL;
+ *  cu_seqlens       int32 [N + 1] on the device, as for kda_chunk_fwd_varlen.
+ * Chunks start at each sequence's first token; no state crosses a sequence
+ * boundary.  Tokens outside every sequence get no gradient written.  Precision,
+ * alignment, head sizes and codes are those of kda_chunk_bwd; the workspace
+ * takes the same bytes per chunk per head for ceil(total_T / 64) + N chunks.
+ */
+int kda_chunk_bwd_varlen(const void* q, const void* k, const void* v, const void* g,
+                         const void* beta, const float* initial_state, const void* grad_out,
+                         const float* grad_final_state, void* grad_q, void* grad_k, void* grad_v,
+                         void* grad_g, void* grad_beta, float* grad_initial_state,
+                         const int32_t* cu_seqlens, int N, int total_T, int H, int dk, int dv,
+                         float scale, int dtype, hipStream_t stream);
+
+/*
  * Context parallelism for one long sequence split into R segments (design for
  * several GPUs, one segment per GPU; every step also runs on one GPU).  A
  * segment maps its entry state affinely to its exit state,

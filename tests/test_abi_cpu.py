@@ -34,7 +34,7 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "kda_abi_version", "kda_status_string", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
         "kda_chunk_fwd_ws", "kda_chunk_fwd_prologue", "kda_chunk_fwd_varlen_prologue",
-        "kda_chunk_fwd_varlen_snapshots", "kda_decode_step_prologue",
+        "kda_chunk_fwd_varlen_snapshots", "kda_decode_step_prologue", "kda_chunk_bwd_varlen",
         "kda_chunk_fwd_snapshots", "kda_chunk_fwd_varlen", "kda_decode_step", "kda_chunk_bwd",
         "kda_chunk_transition", "kda_state_compose"])
 

@@ -444,3 +444,22 @@ def test_workspace_blocks_across_streams():
     torch.cuda.synchronize()
     for i, o, s in results:
         assert torch.equal(o, refs[i][0]) and torch.equal(s, refs[i][1]), f"call {i} differs"
+
+
+def test_prefill_seeded_random_shapes():
+    """Twelve seeded random shapes (batch, length, heads, head size, dtype, initial
+    state present or not) through kda_chunk_fwd, each against the oracle: lengths
+    1..2300 hit one or several windows with ragged tails, stream counts 1..160 hit
+    every scan slice width and both schedules."""
+    rng = np.random.default_rng(20261203)
+    for case in range(12):
+        dtype = torch.float32 if rng.random() < 0.25 else torch.bfloat16
+        D = 64 if dtype == torch.float32 else int(rng.choice([64, 128]))
+        B = int(rng.integers(1, 9))
+        H = int(rng.integers(1, 21))
+        T = int(rng.integers(1, 2301)) if B * H <= 16 else int(rng.integers(1, 400))
+        d = kin.make_prefill(B, T, H, D, D, dtype=dtype, seed=500 + case,
+                             nonzero_state=bool(rng.random() < 0.7))
+        d["scale"] = 1.0 / math.sqrt(D)
+        print(f"case {case}: B={B} T={T} H={H} D={D} {dtype}", flush=True)
+        _compare_fixed(d, f"random case {case} (B={B} T={T} H={H} D={D} {dtype})")
