@@ -201,3 +201,28 @@ def test_workspace_size_is_host_arithmetic(lib):
     assert f(1, 64, 1, 100, 100, 0) == 0
     assert f(0, 64, 1, 128, 128, 0) == 0
     assert f(1, 64, 1, 64, 64, 1) > 0
+
+
+def test_varlen_snapshot_rows_host_logic():
+    """The binding's snapshot row table for packed input: sequence n owns
+    ceil(L_n / S) rows starting at the sum over earlier sequences (an empty sequence
+    owns none)."""
+    import torch
+    from gated_delta_rule_102_amd import kda
+    cu = torch.tensor([0, 300, 300, 364, 365, 1065], dtype=torch.int32)
+    rows = kda.varlen_snapshot_rows(cu, 128)
+    assert rows.tolist() == [0, 3, 3, 4, 5, 11]
+    rows64 = kda.varlen_snapshot_rows(cu, 64)
+    assert rows64.tolist() == [0, 5, 5, 6, 7, 18]
+
+
+def test_chunk_fwd_workspace_tensor_size():
+    """chunk_fwd_workspace allocates the library's figure plus 256 bytes of alignment
+    slack, on the inputs' device."""
+    import torch
+    from gated_delta_rule_102_amd import kda
+    q = torch.empty((2, 300, 3, 128), dtype=torch.bfloat16)
+    v = torch.empty((2, 300, 3, 128), dtype=torch.bfloat16)
+    ws = kda.chunk_fwd_workspace(q, v)
+    assert ws.dtype == torch.uint8 and ws.device == q.device
+    assert ws.numel() == kda.kda_chunk_fwd_workspace_size(2, 300, 3, 128, 128) + 256
