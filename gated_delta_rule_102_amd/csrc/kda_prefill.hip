@@ -18,8 +18,9 @@
 // Unrolling the recurrence inside the chunk gives (I + A) Delta = Diag(beta)(V -
 // (K e^G) S), so the result equals the token-by-token one up to rounding.
 //
-// Kernel 1 (chunk_prep_kernel) does all state-independent work, one workgroup
-// per (chunk, head), fully parallel: the elementwise decay factors, A and M on
+// Kernel 1 (chunk_prep_kernel, or chunk_prep8_kernel with 8 wavefronts per item
+// for bf16 at d = 128) does all state-independent work, one workgroup per
+// (chunk, head), fully parallel: the elementwise decay factors, A and M on
 // v_mfma_f32_16x16x32_bf16, the fp32 inverse, and W, Q', P, Tb.  It writes them,
 // in the layouts the matrix cores read, to a stream-ordered workspace.
 // Kernel 2 (state_scan_kernel) walks the chunks of one (sequence, head) and one
