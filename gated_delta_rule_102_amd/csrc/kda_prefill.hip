@@ -19,9 +19,8 @@
 // (K e^G) S), so the result equals the token-by-token one up to rounding.
 //
 // Kernel 1 (chunk_prep_kernel, or chunk_prep8_kernel with 8 wavefronts per item
-// for bf16 at d = 128) does all state-independent work per (chunk, head), fully
-// parallel, over a resident grid of two workgroups per CU that each take items
-// in turn: the elementwise decay factors, A and M on
+// for bf16 at d = 128) does all state-independent work, one workgroup per
+// (chunk, head), fully parallel: the elementwise decay factors, A and M on
 // v_mfma_f32_16x16x32_bf16, the fp32 inverse, and W, Q', P, Tb.  It writes them,
 // in the layouts the matrix cores read, to a stream-ordered workspace.
 // Kernel 2 (state_scan_kernel) walks the chunks of one (sequence, head) and one
@@ -34,7 +33,6 @@
 // referenced to the cumulative decay at the end of their own sub-tile -- row side
 // e^{G_t - R_I} in [1, e^80], column side e^{R_I - G_s} <= 1, both in bf16 range.
 
-#include <atomic>
 #include <cstdlib>
 #include <type_traits>
 
@@ -968,32 +966,26 @@ __device__ __forceinline__ void prep_body(const PrepParams& p, char* smem, const
   }
 }
 
-// (workspace slot, head) items, strided over the workgroups of a grid sized to
-// stay resident (two workgroups per CU): each workgroup works through its items
-// one after another, without a workgroup launch between them.
-template <int D, typename TIn, int NW>
-__device__ __forceinline__ void prep_items(const PrepParams& p, char* smem) {
-  for (int item = blockIdx.x; item < p.items; item += gridDim.x) {
-    const PrepItem it = prep_item(p, item);
-    if (!it.valid) continue;       // unused workspace slot
-    if (item != static_cast<int>(blockIdx.x)) __syncthreads();   // LDS of the previous item
-    prep_body<D, TIn, NW>(p, smem, it,
-                          p.ws + (static_cast<int64_t>(it.slot) * p.sa.H + it.h) *
-                                     Slot<D, std::is_same<TIn, float>::value>::BYTES);
-  }
-}
-
+// One workgroup per (workspace slot, head) item.
 template <int D, typename TIn>
 __global__ __launch_bounds__(kThreads, 2) void chunk_prep_kernel(PrepParams p) {
   __shared__ __attribute__((aligned(16))) char smem[PrepCfg<D, TIn>::LDS];
-  prep_items<D, TIn, 4>(p, smem);
+  const PrepItem it = prep_item(p, blockIdx.x);
+  if (!it.valid) return;         // unused workspace slot
+  prep_body<D, TIn>(p, smem, it,
+                    p.ws + (static_cast<int64_t>(it.slot) * p.sa.H + it.h) *
+                               Slot<D, std::is_same<TIn, float>::value>::BYTES);
 }
 
 // The same with 8 wavefronts per item (d = 128, bf16): two workgroups, 16
 // wavefronts, share a CU.
 __global__ __launch_bounds__(2 * kThreads, 2) void chunk_prep8_kernel(PrepParams p) {
   __shared__ __attribute__((aligned(16))) char smem[PrepCfg<128, bf16_t>::LDS];
-  prep_items<128, bf16_t, 8>(p, smem);
+  const PrepItem it = prep_item(p, blockIdx.x);
+  if (!it.valid) return;         // unused workspace slot
+  prep_body<128, bf16_t, 8>(p, smem, it,
+                            p.ws + (static_cast<int64_t>(it.slot) * p.sa.H + it.h) *
+                                       Slot<128, false>::BYTES);
 }
 
 // ================================================================= kernel 2
@@ -1390,24 +1382,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_group_kernel(GroupParams 
 
 // ---------------------------------------------------------------- launch
 
-// Workgroups of a two-kernel preparation launch: two per CU of the current
-// device (both preparation kernels keep two resident per CU), each working
-// through its share of the items.  KDA_PREP_GRID overrides it for tuning runs.
-int prep_resident_grid() {
-  static const int forced = [] { const char* e = std::getenv("KDA_PREP_GRID"); return e ? std::atoi(e) : 0; }();
-  if (forced > 0) return forced;
-  static std::atomic<int> cached[64];   // per device, 0 until first asked
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  int cus = cached[dev].load(std::memory_order_relaxed);
-  if (cus <= 0) {
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-    cached[dev].store(cus, std::memory_order_relaxed);
-  }
-  return 2 * cus;
-}
-
 // Scan workgroups for N*H (sequence, head) streams cut into D/DVS slices, padded so
 // that the slices of one stream share an XCD.
 template <int D, int DVS>
@@ -1557,7 +1531,7 @@ hipError_t launch_all(const PrefillArgs& a) {
   const int64_t items = slots * a.H;
   PrepParams pp{a.q, a.k, a.g, a.beta, ws, sa, a.scale, static_cast<int>(items), 0, 0,
                 a.prologue ? 1 : 0};
-  const unsigned prep_grid = static_cast<unsigned>(std::min<int64_t>(items, prep_resident_grid()));
+  const unsigned prep_grid = static_cast<unsigned>(items);
   if (D == 128 && std::is_same<TIn, bf16_t>::value)
     hipLaunchKernelGGL(chunk_prep8_kernel, dim3(prep_grid), dim3(2 * kThreads), 0, a.stream, pp);
   else
