@@ -233,6 +233,17 @@ size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int dty
   return kda::prefill_workspace_bytes(a);
 }
 
+const char* kda_chunk_fwd_schedule(int N, int T, int total_T, int H, int dk, int dv, int dtype,
+                                   int varlen) {
+  if (check_common(dk, dv, H, dtype) != KDA_OK || N <= 0) return "";
+  if (varlen ? total_T <= 0 : T <= 0) return "";
+  kda::PrefillArgs a{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                     varlen ? reinterpret_cast<const int32_t*>(uintptr_t{16}) : nullptr,
+                     N, varlen ? 0 : T, varlen ? total_T : N * T, H, dk, 1.f, dtype == KDA_F32,
+                     nullptr};
+  return kda::prefill_schedule(a);
+}
+
 int kda_chunk_fwd_ws(const void* q, const void* k, const void* v, const void* g,
                      const void* beta, const float* initial_state, void* out,
                      float* final_state, int B, int T, int H, int dk, int dv, float scale,

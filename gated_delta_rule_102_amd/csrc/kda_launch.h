@@ -78,6 +78,8 @@ hipError_t launch_compose(const ComposeArgs& a);
 hipError_t launch_backward(const BackwardArgs& a);
 
 hipError_t launch_prefill(const PrefillArgs& a);
+// Kernels launch_prefill runs for these arguments (static text, for reports).
+const char* prefill_schedule(const PrefillArgs& a);
 // Workspace bytes launch_prefill needs for these arguments (0 if unsupported).
 size_t prefill_workspace_bytes(const PrefillArgs& a);
 

@@ -33,6 +33,7 @@
 // referenced to the cumulative decay at the end of their own sub-tile -- row side
 // e^{G_t - R_I} in [1, e^80], column side e^{R_I - G_s} <= 1, both in bf16 range.
 
+#include <cstdio>
 #include <cstdlib>
 #include <type_traits>
 
@@ -1396,20 +1397,8 @@ hipError_t launch_scan(const PrefillArgs& a, const SeqArgs& sa, const char* ws) 
   return hipGetLastError();
 }
 
-// KDA_GROUP_CHUNKS overrides the window size for tuning runs (0 selects the
-// two-kernel schedule); -1 when it is not set.
-inline int forced_group_chunks() {
-  static const int forced = [] {
-    const char* e = std::getenv("KDA_GROUP_CHUNKS");
-    return e ? std::atoi(e) : -1;
-  }();
-  return forced;
-}
-
 // Chunks per window of the grouped launch.
 inline int group_chunks(int nchunks) {
-  const int forced = forced_group_chunks();
-  if (forced >= 0) return forced == 0 ? 0 : std::min(forced, nchunks);
   // at most 8 windows (each launch boundary drains the machine) and at least 16
   // chunks per window (the scan role needs enough steps to amortise its state
   // round trip through memory)
@@ -1500,7 +1489,6 @@ inline int prefill_cg(const PrefillArgs& a) {
   if (a.cu_seqlens != nullptr) return 0;
   const int nchunks = (a.T + kC - 1) / kC;
   const int cg = group_chunks(nchunks);
-  if (forced_group_chunks() >= 0) return cg;
   const int streams = a.N * a.H;
   if (streams >= kWideStreams) return 0;
   if (!a.dtype_f32 && a.d == 128 && streams >= 64 && nchunks <= 64) return 0;
@@ -1542,12 +1530,7 @@ hipError_t launch_all(const PrefillArgs& a) {
     // 32-column slices from 64 streams on (within 256 registers; at 2048 packed
     // streams the scan took 11.7 ms against 16.5 ms with whole-state workgroups)
     const int streams = a.N * a.H;
-    // KDA_SCAN_DVS (16/32/64) overrides the slice width for tuning runs
-    static const int forced = [] { const char* e = std::getenv("KDA_SCAN_DVS"); return e ? std::atoi(e) : 0; }();
-    if (forced == 16) err = launch_scan<D, 16, TIn>(a, sa, ws);
-    else if (forced == 32) err = launch_scan<D, 32, TIn>(a, sa, ws);
-    else if (forced == 64) err = launch_scan<D, 64, TIn>(a, sa, ws);
-    else if (streams < 64) err = launch_scan<D, 16, TIn>(a, sa, ws);
+    if (streams < 64) err = launch_scan<D, 16, TIn>(a, sa, ws);
     else if (streams < kWideStreams) err = launch_scan<D, 32, TIn>(a, sa, ws);
     else err = launch_scan<D, 64, TIn>(a, sa, ws);
   }
@@ -1561,6 +1544,31 @@ size_t prefill_workspace_bytes(const PrefillArgs& a) {
   if (a.dtype_f32) return a.d == 64 ? workspace_bytes<64, float>(a) : 0;
   if (a.d == 128) return workspace_bytes<128, bf16_t>(a);
   return workspace_bytes<64, bf16_t>(a);
+}
+
+const char* prefill_schedule(const PrefillArgs& a) {
+  const bool f32 = a.dtype_f32;
+  const int D = a.d;
+  const int cg = prefill_cg(a);
+  if (cg > 0) {
+    const int nchunks = (a.T + kC - 1) / kC;
+    const int windows = (nchunks + cg - 1) / cg;
+    const int dvs = a.N * a.H < 32 ? 16 : 32;
+    static thread_local char buf[160];
+    std::snprintf(buf, sizeof buf,
+                  "prefill_group_kernel<%d,%d,%s> x %d launches (windows of %d chunks: "
+                  "scan of window k-1 beside preparation of window k)",
+                  D, dvs, f32 ? "f32" : "bf16", windows + 1, cg);
+    return buf;
+  }
+  const int streams = a.N * a.H;
+  const int dvs = streams < 64 ? 16 : streams < kWideStreams ? 32 : 64;
+  static thread_local char buf2[160];
+  std::snprintf(buf2, sizeof buf2, "%s + state_scan_kernel<%d,%d,%s>",
+                (D == 128 && !f32) ? "chunk_prep8_kernel" : (D == 128 ? "chunk_prep_kernel<128,f32>"
+                 : f32 ? "chunk_prep_kernel<64,f32>" : "chunk_prep_kernel<64,bf16>"),
+                D, dvs, f32 ? "f32" : "bf16");
+  return buf2;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a) {

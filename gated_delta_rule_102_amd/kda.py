@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 KDA_BF16, KDA_F32 = 0, 1
 _lib = None
 
-EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_bwd_varlen", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
+EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_schedule", "kda_chunk_bwd_varlen", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
            "kda_chunk_fwd_ws", "kda_chunk_fwd_prologue", "kda_chunk_fwd_varlen_prologue",
            "kda_chunk_fwd_varlen_snapshots", "kda_decode_step_prologue",
            "kda_chunk_fwd_snapshots", "kda_chunk_fwd_varlen", "kda_decode_step", "kda_chunk_bwd",
@@ -51,6 +51,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                   f32, i32, vp]
     lib.kda_chunk_fwd.restype = i32
+    lib.kda_chunk_fwd_schedule.argtypes = [i32] * 8
+    lib.kda_chunk_fwd_schedule.restype = ctypes.c_char_p
     lib.kda_chunk_fwd_workspace_size.argtypes = [i32] * 6
     lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_size_t
     lib.kda_chunk_fwd_ws.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
@@ -134,9 +136,28 @@ def _check_state(name, t, shape, device):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
+def _check_out(t, shape, dtype, device):
+    """A caller-supplied output must match exactly: the kernels size their stores from
+    the call's sizes, not from the tensor."""
+    _check(dict(out=t), dtype, device)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"out has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
 def _raise(fn, rc):
     if rc != 0:
         raise KDAError(fn, rc)
+
+
+def prefill_schedule_name(N, T, H, d, dtype=torch.bfloat16, varlen=False, total_T=0):
+    """Kernels a prefill call with these sizes launches (kda_chunk_fwd_schedule)."""
+    code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
+    return load_library().kda_chunk_fwd_schedule(int(N), int(T), int(total_T or N * max(T, 1)),
+                                                 int(H), int(d), int(d), code,
+                                                 1 if varlen else 0).decode()
+
+
+kda_chunk_fwd_schedule = prefill_schedule_name
 
 
 def kda_chunk_fwd_workspace_size(B, T, H, dk, dv, dtype=torch.bfloat16) -> int:
@@ -184,7 +205,7 @@ def kda_chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final
     _check_state("initial_state", initial_state, (B, H, dk, dv), device)
     if out is None:
         out = torch.empty((B, T, H, dv), dtype=dtype, device=device)
-    _check(dict(out=out), dtype, device)
+    _check_out(out, (B, T, H, dv), dtype, device)
     if final_state is None and output_final_state:
         final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=device)
     _check_state("final_state", final_state, (B, H, dk, dv), device)
@@ -225,7 +246,7 @@ def kda_chunk_fwd_prologue(q_raw, k_raw, v, g_raw, beta_raw, scale=None, initial
     _check_state("initial_state", initial_state, (B, H, dk, dv), device)
     if out is None:
         out = torch.empty((B, T, H, dv), dtype=dtype, device=device)
-    _check(dict(out=out), dtype, device)
+    _check_out(out, (B, T, H, dv), dtype, device)
     if final_state is None and output_final_state:
         final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=device)
     _check_state("final_state", final_state, (B, H, dk, dv), device)
@@ -257,7 +278,7 @@ def kda_chunk_fwd_snapshots(q, k, v, g, beta, scale=None, initial_state=None,
     nsnap = -(-T // snapshot_tokens) if snapshot_tokens > 0 else 0
     if out is None:
         out = torch.empty((B, T, H, dv), dtype=dtype, device=device)
-    _check(dict(out=out), dtype, device)
+    _check_out(out, (B, T, H, dv), dtype, device)
     if final_state is None and output_final_state:
         final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=device)
     _check_state("final_state", final_state, (B, H, dk, dv), device)
@@ -289,7 +310,7 @@ def _varlen_prep(q, k, v, g, beta, cu_seqlens, initial_state, output_final_state
     _check_state("initial_state", initial_state, (N, H, dk, dv), device)
     if out is None:
         out = torch.empty(v.shape, dtype=dtype, device=device)
-    _check(dict(out=out), dtype, device)
+    _check_out(out, v.shape, dtype, device)
     if final_state is None and output_final_state:
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=device)
     _check_state("final_state", final_state, (N, H, dk, dv), device)
@@ -378,7 +399,7 @@ def _decode(fn, q, k, v, g, beta, state, scale, out):
     _check_state("state", state, (B, H, dk, dv), device)
     if out is None:
         out = torch.empty((B, H, dv), dtype=dtype, device=device)
-    _check(dict(out=out), dtype, device)
+    _check_out(out, (B, H, dv), dtype, device)
     scale = 1.0 / math.sqrt(dk) if scale is None else float(scale)
     rc = getattr(lib, fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
                           _ptr(out), B, H, dk, dv, scale, _dtype_code(q), _stream(q))

@@ -112,6 +112,15 @@ int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
                   float scale, int dtype, hipStream_t stream);
 
 /*
+ * Names of the kernels a prefill call with these sizes launches, for reports and
+ * profiling (N sequences; fixed length: T tokens each; varlen != 0: packed, total_T
+ * tokens).  Static, thread-local text, valid until the calling thread calls this
+ * again; "" when the sizes or dtype are not accepted.  Pure host logic.
+ */
+const char* kda_chunk_fwd_schedule(int N, int T, int total_T, int H, int dk, int dv,
+                                   int dtype, int varlen);
+
+/*
  * Bytes of workspace kda_chunk_fwd_ws needs for these sizes (the same schedule
  * kda_chunk_fwd runs), or 0 when the sizes or dtype are not accepted by
  * kda_chunk_fwd.  Pure host arithmetic: no device call.

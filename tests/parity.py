@@ -74,3 +74,47 @@ def oracle_pair_slices(d, pairs, bounds, workers=8):
 
     with ThreadPoolExecutor(max_workers=workers) as ex:
         return list(ex.map(one, pairs))
+
+
+class ErrAccum:
+    """Max-abs and rel-L2 over a tensor compared piece by piece.
+
+    rel-L2 = sqrt(sum (x - y)^2) / sqrt(sum y^2) over every piece added, so a whole
+    full-size tensor is held to the same bar as in ``assert_close`` without ever
+    holding all of it in fp64 at once."""
+
+    def __init__(self, name, dtype):
+        self.name, self.dtype = name, dtype
+        self.sq_diff = 0.0
+        self.sq_ref = 0.0
+        self.max_abs = 0.0
+        self.count = 0
+
+    def add(self, got, ref):
+        got = got.detach().float().cpu().numpy() if isinstance(got, torch.Tensor) else got
+        x = np.asarray(got, dtype=np.float64)
+        y = np.asarray(ref, dtype=np.float64)
+        if x.shape != y.shape:
+            raise ValueError(f"{self.name}: shapes {x.shape} and {y.shape} differ")
+        assert np.all(np.isfinite(x)), f"{self.name}: non-finite values"
+        diff = x - y
+        self.sq_diff += float(np.dot(diff.ravel(), diff.ravel()))
+        self.sq_ref += float(np.dot(y.ravel(), y.ravel()))
+        if diff.size:
+            self.max_abs = max(self.max_abs, float(np.max(np.abs(diff))))
+        self.count += x.size
+
+    def rel_l2(self):
+        return (self.sq_diff ** 0.5) / (self.sq_ref ** 0.5 if self.sq_ref > 0 else 1.0)
+
+    def check(self):
+        tol = TOL[self.dtype]
+        rel = self.rel_l2()
+        msg = (f"{self.name}: max_abs={self.max_abs:.3e} rel_l2={rel:.3e} over "
+               f"{self.count} values (tol {tol})")
+        print(msg, flush=True)
+        assert self.count > 0, f"{self.name}: nothing compared"
+        assert rel <= tol["rel_l2"], msg
+        if tol["max_abs"] is not None:
+            assert self.max_abs <= tol["max_abs"], msg
+        return self.max_abs, rel

@@ -33,6 +33,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "kda_abi_version", "kda_status_string", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
+        "kda_chunk_fwd_schedule",
         "kda_chunk_fwd_ws", "kda_chunk_fwd_prologue", "kda_chunk_fwd_varlen_prologue",
         "kda_chunk_fwd_varlen_snapshots", "kda_decode_step_prologue", "kda_chunk_bwd_varlen",
         "kda_chunk_fwd_snapshots", "kda_chunk_fwd_varlen", "kda_decode_step", "kda_chunk_bwd",
@@ -226,3 +227,27 @@ def test_chunk_fwd_workspace_tensor_size():
     ws = kda.chunk_fwd_workspace(q, v)
     assert ws.dtype == torch.uint8 and ws.device == q.device
     assert ws.numel() == kda.kda_chunk_fwd_workspace_size(2, 300, 3, 128, 128) + 256
+
+
+def test_binding_rejects_wrong_output_shape_before_any_call():
+    """A caller-supplied ``out`` whose shape differs from the call's sizes is refused
+    by the binding (the kernels size their stores from the sizes, not the tensor);
+    CPU tensors suffice, because the check runs before the library is called."""
+    import torch
+    from gated_delta_rule_102_amd import kda
+    B, T, H, D = 1, 8, 2, 64
+    q = torch.zeros((B, T, H, D), dtype=torch.bfloat16)
+    beta = torch.zeros((B, T, H), dtype=torch.bfloat16)
+    for bad in ((B, T - 1, H, D), (B, T, H, D // 2), (B * T * H * D,)):
+        with pytest.raises(ValueError, match="out has shape"):
+            kda.kda_chunk_fwd(q, q, q, q, beta, out=torch.zeros(bad, dtype=torch.bfloat16))
+    cu = torch.tensor([0, 3, 8], dtype=torch.int32)
+    with pytest.raises(ValueError, match="out has shape"):
+        kda.kda_chunk_fwd_varlen(q, q, q, q, beta, cu, out=torch.zeros((1, 7, H, D),
+                                                                     dtype=torch.bfloat16))
+    qd = torch.zeros((B, H, D), dtype=torch.bfloat16)
+    bd = torch.zeros((B, H), dtype=torch.bfloat16)
+    st = torch.zeros((B, H, D, D), dtype=torch.float32)
+    with pytest.raises(ValueError, match="out has shape"):
+        kda.kda_decode_step(qd, qd, qd, qd, bd, st, out=torch.zeros((B, H, D + 1),
+                                                                  dtype=torch.bfloat16))

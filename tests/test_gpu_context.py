@@ -34,32 +34,41 @@ def _gpu():
     yield
 
 
-@pytest.mark.parametrize("dtype,D,T", [(torch.bfloat16, 128, 150), (torch.bfloat16, 64, 64),
-                                       (torch.float32, 64, 131), (torch.bfloat16, 128, 1),
-                                       (torch.float32, 128, 100)])
-def test_transition_matches_oracle(dtype, D, T):
-    """Standard decays (g = max(-5, -softplus(N(0,1)))) forget fast: after ~100 tokens
-    every entry of P lies below fp32's normal range (max |P| ~ 1e-42 at T = 150), so
-    the check there is absolute.  With slow decay (g ~ U(-0.05, 0)) P stays O(1) and
-    a relative bar applies: fp32 inputs run on fp32 operands (rel-L2 <= 1e-4), bf16
-    inputs on bf16 operands with fp32 accumulation, the bf16 prefill's precision
-    (its bars: max-abs <= 2e-2, rel-L2 <= 1e-2)."""
+@pytest.mark.parametrize("dtype,D,T,decay", [
+    (torch.bfloat16, 128, 40, "standard"), (torch.bfloat16, 128, 64, "standard"),
+    (torch.bfloat16, 64, 64, "standard"), (torch.float32, 64, 40, "standard"),
+    (torch.float32, 128, 64, "standard"), (torch.bfloat16, 128, 1, "standard"),
+    (torch.bfloat16, 128, 150, "slow"), (torch.bfloat16, 64, 64, "slow"),
+    (torch.float32, 64, 131, "slow"), (torch.float32, 128, 100, "slow")])
+def test_transition_matches_oracle(dtype, D, T, decay):
+    """P = M_{T-1} ... M_0 (M_t = (I - beta_t k_t k_t^T) Diag(e^{g_t})) against the
+    oracle's transition_np.  Standard decays (g = max(-5, -softplus(N(0,1)))) shrink P
+    by about e^-0.8 a token, so they are taken over at most 64 tokens, where max |P|
+    is still far inside fp32's normal range (the test asserts it); slow decays (g ~
+    U(-0.05, 0)) keep P of order one over 150 tokens.  Both are held to relative bars:
+    rel-L2 <= 1e-2 and max-abs <= 2e-2 * max |P| for bf16 inputs (bf16 operands with
+    fp32 accumulation, the bf16 prefill's precision), rel-L2 <= 1e-4 for fp32."""
     from gated_delta_rule_102_amd import kda
     B, H = 2, 2
     d = kin.make_prefill(B, T, H, D, D, dtype=dtype, seed=500 + T + D)
-    gen = torch.Generator().manual_seed(600 + T + D)
-    slow = (-0.05 * torch.rand(d["g"].shape, generator=gen)).to(dtype)
-    abs_bar, rel_bar = (1e-5, 1e-4) if dtype == torch.float32 else (2e-2, 1e-2)
-    for name, g, check_rel in (("standard decay", d["g"], False), ("slow decay", slow, True)):
-        P = kda.kda_chunk_transition(d["q"].to(DEV), d["k"].to(DEV), g.to(DEV), d["beta"].to(DEV))
-        torch.cuda.synchronize()
-        for b in range(B):
-            ref = transition_np(d["k"][b], g[b], d["beta"][b])
-            mx, rel = errors(P[b].cpu().numpy(), ref)
-            print(f"{name} b={b}: max_abs {mx:.2e} rel_l2 {rel:.2e}", flush=True)
-            assert mx <= abs_bar, f"{name} b={b}: max_abs {mx:.3e}"
-            if check_rel:
-                assert rel <= rel_bar, f"{name} b={b}: rel_l2 {rel:.3e}"
+    g = d["g"]
+    if decay == "slow":
+        gen = torch.Generator().manual_seed(600 + T + D)
+        g = (-0.05 * torch.rand(d["g"].shape, generator=gen)).to(dtype)
+    P = kda.kda_chunk_transition(d["q"].to(DEV), d["k"].to(DEV), g.to(DEV), d["beta"].to(DEV))
+    torch.cuda.synchronize()
+    for b in range(B):
+        ref = transition_np(d["k"][b], g[b], d["beta"][b])
+        peak = float(np.max(np.abs(ref)))
+        assert peak > 1e-30, f"b={b}: max |P| = {peak:.2e} leaves nothing to compare"
+        mx, rel = errors(P[b].cpu().numpy(), ref)
+        print(f"{decay} decay b={b}: max|P| {peak:.2e} max_abs {mx:.2e} rel_l2 {rel:.2e}",
+              flush=True)
+        if dtype == torch.float32:
+            assert rel <= 1e-4, f"b={b}: rel_l2 {rel:.3e}"
+        else:
+            assert rel <= 1e-2, f"b={b}: rel_l2 {rel:.3e}"
+            assert mx <= 2e-2 * peak, f"b={b}: max_abs {mx:.3e} against max |P| {peak:.3e}"
 
 
 def test_compose_matches_numpy():

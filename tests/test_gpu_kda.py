@@ -2,9 +2,8 @@
 
 Every case feeds bit-identical seeded inputs to both sides and compares outputs
 and final states element by element with the tolerances in tests/parity.py.
-Small cases span several 64-token chunks and ragged tails; full-size cases
-compare every output of sampled (sequence, head) pairs, which the oracle
-computes one pair at a time.
+Cases here span several 64-token chunks and ragged tails; the four full-size
+workloads are compared in full in test_gpu_full_size.py.
 """
 import math
 
@@ -13,7 +12,7 @@ import pytest
 import torch
 
 from gated_delta_rule_102_amd import inputs as kin
-from tests.parity import assert_close, oracle_fixed, oracle_pair_slices
+from tests.parity import assert_close, oracle_fixed
 
 pytestmark = pytest.mark.gpu
 
@@ -77,38 +76,6 @@ def test_decode_steps_match_oracle(D, dtype):
     assert_close("decode state", state, ref_s.reshape(B, H, D, D), dtype)
 
 
-def test_decode_full_size_sampled():
-    """256 sequences x 32 heads, d = 128: the full decode batch, 4 steps, all
-    outputs and the states of sampled heads checked."""
-    from gated_delta_rule_102_amd import kda
-    w = kin.WORKLOADS["decode_256x32"]
-    steps = 4
-    d = kin.make_decode(steps, w.B, w.H, w.dk, w.dv, dtype=w.dtype, seed=w.seed, device=DEV)
-    s0 = d["state"].clone()
-    state = d["state"]
-    outs = []
-    for s in range(steps):
-        outs.append(kda.kda_decode_step(d["q"][s], d["k"][s], d["v"][s], d["g"][s],
-                                        d["beta"][s], state, scale=w.scale_value()))
-    torch.cuda.synchronize()
-    out = torch.stack(outs)
-    rng = np.random.default_rng(0)
-    pairs = [(int(b), int(h)) for b, h in zip(rng.integers(0, w.B, 24), rng.integers(0, w.H, 24))]
-    seq = {x: d[x].transpose(0, 1) for x in ("q", "k", "v", "g", "beta")}
-    cpu = {x: seq[x][[p[0] for p in pairs]].cpu() for x in seq}
-    got_o, ref_o, got_s, ref_s = [], [], [], []
-    for i, (b, h) in enumerate(pairs):
-        from oracle import oracle_forward
-        o, st = oracle_forward(cpu["q"][i:i + 1, :, h:h + 1], cpu["k"][i:i + 1, :, h:h + 1],
-                               cpu["v"][i:i + 1, :, h:h + 1], cpu["g"][i:i + 1, :, h:h + 1],
-                               cpu["beta"][i:i + 1, :, h:h + 1], w.scale_value(),
-                               initial_state=s0[b, h][None, None].cpu())
-        ref_o.append(o[:, 0]); ref_s.append(st[0])
-        got_o.append(out[:, b, h].float().cpu().numpy()); got_s.append(state[b, h].cpu().numpy())
-    assert_close("decode out (sampled)", np.stack(got_o), np.stack(ref_o), w.dtype)
-    assert_close("decode state (sampled)", np.stack(got_s), np.stack(ref_s), w.dtype)
-
-
 # ------------------------------------------------------------------ prefill
 
 
@@ -169,34 +136,6 @@ def test_prefill_decay_extremes(mode):
     _compare_fixed(d, f"decay {mode}")
 
 
-def test_prefill_4x4096_full_size_sampled():
-    """B=4, H=16, T=4096, d=128, bf16, S0 ~ 0.1 N(0,1): the benchmarked workload at
-    full size; every output and final state of 6 sampled (b, h) pairs checked."""
-    w = kin.WORKLOADS["prefill_4x4096"]
-    d = kin.make_workload(w, device=DEV)
-    out, fs = _run_prefill(d)
-    pairs = [(0, 0), (1, 5), (2, 9), (3, 15), (3, 3), (0, 12)]
-    refs = oracle_pair_slices(d, pairs, [(b * w.T, w.T) for b in range(w.B)])
-    got_o = np.stack([out[b, :, h].float().cpu().numpy() for b, h in pairs])
-    got_s = np.stack([fs[b, h].cpu().numpy() for b, h in pairs])
-    assert_close("4x4096 out", got_o, np.stack([r[0] for r in refs]), w.dtype)
-    assert_close("4x4096 state", got_s, np.stack([r[1] for r in refs]), w.dtype)
-    assert torch.isfinite(out.float()).all()
-
-
-def test_prefill_1x65536_full_size_sampled():
-    """B=1, H=32, T=65536 (1024 chunks of inter-chunk propagation), zero state."""
-    w = kin.WORKLOADS["prefill_1x65536"]
-    d = kin.make_workload(w, device=DEV)
-    out, fs = _run_prefill(d)
-    pairs = [(0, 0), (0, 17), (0, 31)]
-    refs = oracle_pair_slices(d, pairs, [(0, w.T)], workers=3)
-    got_o = np.stack([out[0, :, h].float().cpu().numpy() for _, h in pairs])
-    got_s = np.stack([fs[0, h].cpu().numpy() for _, h in pairs])
-    assert_close("1x65536 out", got_o, np.stack([r[0] for r in refs]), w.dtype)
-    assert_close("1x65536 state", got_s, np.stack([r[1] for r in refs]), w.dtype)
-
-
 # ------------------------------------------------------------------ varlen
 
 
@@ -224,26 +163,6 @@ def test_varlen_matches_oracle(dtype, D):
                                     initial_state=d["initial_state"])
     assert_close("varlen out", out[0], ref_out, dtype)
     assert_close("varlen state", fs, ref_s.reshape(fs.shape), dtype)
-
-
-def test_varlen_64seq_full_size_sampled():
-    """64 packed sequences, log-uniform lengths in [1024, 65536] (about a million
-    tokens), H=32, half the heads at g = -5, half in [-0.05, 0].  Checked on the
-    shortest and longest sequence and three others, at a floor head and a slow head."""
-    w = kin.WORKLOADS["varlen_64seq"]
-    d = kin.make_workload(w, device=DEV)
-    out, fs = _run_varlen(d)
-    lens = d["lengths"].tolist()
-    cu = d["cu_seqlens"].cpu().tolist()
-    order = np.argsort(lens)
-    seqs = [int(order[0]), int(order[-1]), int(order[20]), int(order[40]), int(order[55])]
-    pairs = [(n, h) for n in seqs for h in (3, 20)]
-    bounds = [(cu[n], lens[n]) for n in range(len(lens))]
-    refs = oracle_pair_slices(d, pairs, bounds)
-    for (n, h), (ro, rs) in zip(pairs, refs):
-        got = out[0, cu[n]:cu[n] + lens[n], h]
-        assert_close(f"varlen64 out seq {n} head {h}", got, ro, w.dtype)
-        assert_close(f"varlen64 state seq {n} head {h}", fs[n, h], rs, w.dtype)
 
 
 # ------------------------------------------------------------------ invariants
