@@ -1,0 +1,681 @@
+// Fused chunked KDA prefill on gfx950: one workgroup per (sequence, head) walks the
+// sequence's 64-token chunks, computes each chunk's operands in LDS and applies
+// them to the state held in registers.  Nothing leaves the CU but q, k, v, g, beta
+// (read once), the output (written once) and the states.
+//
+// The token rule (neurohive.io Kimi K3 review, section "Sequence length: hybrid KDA
+// and Gated MLA attention": a delta rule that forgets per key channel and writes,
+// the log of the retention factor bounded below at -5)
+//     S_t = (I - beta_t k_t k_t^T) Diag(exp g_t) S_{t-1} + beta_t k_t v_t^T,
+//     o_t = S_t^T (scale q_t)
+// is applied a chunk at a time.  With L the cumulative log-decay inside the chunk
+// (per token and key channel, zero before the chunk) and Ln its value at the end:
+//     A[t,s] = beta_t sum_c k_tc k_sc e^{L_tc - L_sc}     (s < t)
+//     M[t,s] = scale sum_c q_tc k_sc e^{L_tc - L_sc}      (s <= t)
+//     Tb = (I + A)^{-1} Diag(beta)
+//     Kb = K e^L,  Qb = scale Q e^L,  Kt = K e^{Ln - L},  Lambda = e^{Ln}
+// and, from the state S at the chunk start,
+//     X = V - Kb S,   Delta = Tb X,   O = Qb S + M Delta,
+//     S <- Diag(Lambda) S + Kt^T Delta.
+// Unrolling the token rule inside the chunk gives (I + A) Delta = Diag(beta)(V - Kb S),
+// so this equals the token-by-token result up to rounding.
+//
+// The -5 bound is what lets every tile be a plain bf16 matrix-core product.  Over a
+// whole chunk e^{-L} reaches e^{320}, so A and M are built from 16-row sub-tiles I
+// referenced to the cumulative decay R_I at the end of the sub-tile: the row side
+// carries e^{L_t - R_I} in [1, e^80], the column side e^{R_I - L_s} <= 1, both within
+// bf16 range; off-diagonal sub-tile pairs (I > J) scale the column side of J by
+// e^{R_I - R_J} <= 1.
+//
+// Layout inside the workgroup (8 wavefronts):
+//  - Elementwise and sub-tile products: wavefront w owns rows 16 (w/2) .. +15 of the
+//    chunk and the key channels of 32-channel blocks 2 (w%2) and 2 (w%2) + 1; lane
+//    (r, g) holds row r and, in each block b, the 8 channels
+//        32 b + 4 g + {0, 1, 2, 3} and 32 b + 16 + 4 g + {0, 1, 2, 3},
+//    which is exactly the operand fragment of v_mfma_f32_16x16x32_bf16 with the
+//    contraction index taken in that order.  Every product contracting over key
+//    channels (or over tokens) uses this order on both sides.
+//  - State: wavefront w owns value columns 16 w .. +15 of S for all 128 key channels,
+//    as 8 accumulator tiles.  An accumulator tile pair (rows 32 b .. +31) holds, per
+//    lane, rows 32 b + 4 g + i and 32 b + 16 + 4 g + i -- the same order -- so the state
+//    (and X and Delta, accumulators over tokens) feed the next products as operands
+//    with one conversion to bf16 and no transpose.  The output is produced
+//    transposed (rows = value columns), so each lane holds 4 consecutive values of
+//    one token's output row and writes them with one 8-byte store.
+
+#include "kda_device.h"
+#include "kda_launch.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int kD = 128;      // dk = dv
+constexpr int kCh = 64;      // chunk
+constexpr int kThreadsF = 512;
+
+// LDS regions (bytes).  Fragment-ordered operands are [tile][block][lane][16 B].
+namespace fl {
+constexpr int KBN = 0;                      // -Kb       [4 t-tiles][4 c-blocks]
+constexpr int QB = KBN + 16384;             // Qb        [4 t-tiles][4 c-blocks]
+constexpr int KTT = QB + 16384;             // Kt^T      [8 c-tiles][2 s-blocks]
+constexpr int TBF = KTT + 16384;            // Tb        [4 t-tiles][2 s-blocks]
+constexpr int MF = TBF + 8192;              // M         [4 t-tiles][2 s-blocks]
+constexpr int LAM = MF + 8192;              // Lambda    [128] fp32
+constexpr int OFF = LAM + 512;              // column side of pair (I, J < I): [6][4][64][16]
+constexpr int PART = OFF + 6 * 4096;        // partial A^T, M^T of 10 pairs: [10][2][64][16]
+constexpr int AT = PART + 10 * 2048;        // A, then T in place: [64][64] fp32, swizzled
+constexpr int XS = AT + 16384;              // inverse scratch: 4 x [16][17] fp32
+constexpr int TOT = XS + 4 * 16 * 17 * 4;   // sub-tile decay totals [4][128] fp32
+constexpr int FAC = TOT + 4 * 128 * 4;      // per (sub-tile, channel) factors [4][4][128]
+constexpr int FOFF = FAC + 4 * 4 * 128 * 4; // e^{R_I - R_J}, I > J: [6][128]
+constexpr int BETA = FOFF + 6 * 128 * 4;    // [64] fp32
+constexpr int ORD = BETA + 256;             // sequence order (packed input) [<= 256]
+constexpr int BYTES = ORD + 1024;
+static_assert(BYTES <= 160 * 1024, "LDS budget");
+}  // namespace fl
+
+struct FusedParams {
+  const bf16_t *q, *k, *v, *g, *beta;
+  const float* s0;        // [N, H, D, D] or null (zero)
+  bf16_t* out;
+  float* sT;              // [N, H, D, D] or null
+  const int32_t* cu;      // packed sequence offsets [N + 1], or null (fixed length T)
+  int N, T, total_T, H;
+  float scale;
+};
+
+__device__ __forceinline__ void fused_seq(const FusedParams& p, int n, int& tok0, int& len) {
+  if (p.cu == nullptr) {
+    tok0 = n * p.T;
+    len = p.T;
+  } else {
+    const int x0 = min(max(p.cu[n], 0), p.total_T);
+    const int x1 = min(max(p.cu[n + 1], x0), p.total_T);
+    tok0 = x0;
+    len = x1 - x0;
+  }
+}
+
+// Channel of element e (0..7) of the fragment of 32-channel block b held by lane group g.
+__device__ __forceinline__ constexpr int perm_ch(int b, int g, int e) {
+  return 32 * b + 4 * g + (e & 3) + 16 * (e >> 2);
+}
+
+// Byte offset of fragment (tile, blk) of an operand with NB blocks per tile, for `lane`.
+__device__ __forceinline__ int frag_at(int tile, int blk, int nb, int lane) {
+  return ((tile * nb + blk) * 64 + lane) * 16;
+}
+
+// (row, byte) of the swizzled fp32 [64][64] A/T array: the 16-byte pieces of each row
+// are permuted by the row index so column reads do not collide on banks.
+__device__ __forceinline__ int at_off(int row, int col) {
+  const int byte = col * 4;
+  return row * 256 + ((((byte >> 4) ^ (row & 15))) << 4) + (byte & 15);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_shr(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Inclusive prefix sum over the 16 lanes of a DPP row (lane & 15 = row index).
+__device__ __forceinline__ float row_scan16(float x) {
+  x += dpp_shr<0x111>(x);   // row_shr:1
+  x += dpp_shr<0x112>(x);   // row_shr:2
+  x += dpp_shr<0x114>(x);   // row_shr:4
+  x += dpp_shr<0x118>(x);   // row_shr:8
+  return x;
+}
+
+__device__ __forceinline__ bf16x8_t to_frag(const float (&x)[8]) {
+  bf16x8_t f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = static_cast<__bf16>(x[e]);
+  return f;
+}
+
+// Accumulator tiles (2 b, 2 b + 1) as one operand fragment in the channel order above.
+__device__ __forceinline__ bf16x8_t acc_frag(const f32x4_t& lo, const f32x4_t& hi) {
+  bf16x8_t f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[i] = static_cast<__bf16>(lo[i]);
+    f[4 + i] = static_cast<__bf16>(hi[i]);
+  }
+  return f;
+}
+
+__device__ __forceinline__ bf16x8_t lds_frag(const char* smem, int off) {
+  return *reinterpret_cast<const bf16x8_t*>(smem + off);
+}
+
+__device__ __forceinline__ f32x4_t mma(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Pair number of sub-tile pair (I, J), J <= I: (0,0),(1,0),(1,1),(2,0),...,(3,3).
+__device__ __forceinline__ constexpr int pair_id(int I, int J) { return I * (I + 1) / 2 + J; }
+// Off-diagonal pairs J < I -> 0..5.
+__device__ __forceinline__ constexpr int off_id(int I, int J) { return I * (I - 1) / 2 + J; }
+
+// Key-side inputs of one chunk as loaded: q, k, g (16 channels of one row per lane,
+// 8-byte pieces in fragment order) and beta of the row.  v is loaded separately.
+struct ChunkIn {
+  i32x2_t q[2][2], k[2][2], g[2][2];
+  uint32_t beta;
+};
+
+__global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[fl::BYTES];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+  const int H = p.H;
+  const int I = wave >> 1, hf = wave & 1;     // elementwise role: sub-tile, channel half
+  const int jt = wave;                        // state role: value columns 16 jt .. +15
+
+  // ---------------------------------------------------------------- which sequence
+  const int rank = blockIdx.x / H, h = blockIdx.x % H;
+  int n = rank;
+  if (p.cu != nullptr && p.N <= 256) {   // longest sequence first
+    int* ord = reinterpret_cast<int*>(smem + fl::ORD);
+    int mylen = 0;
+    if (tid < p.N) {
+      int a, l;
+      fused_seq(p, tid, a, l);
+      mylen = l;
+      ord[tid] = l;
+    }
+    __syncthreads();
+    int rk = 0;
+    if (tid < p.N)
+      for (int m = 0; m < p.N; ++m) {
+        const int lm = ord[m];
+        rk += (lm > mylen) || (lm == mylen && m < tid);
+      }
+    __syncthreads();
+    if (tid < p.N) ord[rk] = tid;
+    __syncthreads();
+    n = ord[rank];
+    __syncthreads();
+  }
+  int tok0, len;
+  fused_seq(p, n, tok0, len);
+  const int nchunks = (len + kCh - 1) / kCh;
+
+  // upper sub-tiles of A/T and M are read as zeros; nothing else writes them
+  for (int e = tid; e < 64 * 64; e += kThreadsF)
+    *reinterpret_cast<float*>(smem + fl::AT + at_off(e >> 6, e & 63)) = 0.f;
+  for (int e = tid; e < 8192 / 16; e += kThreadsF)
+    *reinterpret_cast<i32x4_t*>(smem + fl::MF + e * 16) = i32x4_t{0, 0, 0, 0};
+
+  // ---------------------------------------------------------------- state
+  f32x4_t S[8];
+  {
+    const float* s0 = p.s0 ? p.s0 + (static_cast<int64_t>(n) * H + h) * kD * kD : nullptr;
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        S[ct][i] = s0 ? s0[(16 * ct + 4 * g4 + i) * kD + 16 * jt + l16] : 0.f;
+  }
+
+  const uint32_t rs = static_cast<uint32_t>(H) * kD * 2;   // token row stride (bytes)
+
+  auto load_chunk = [&](int c, ChunkIn& in) {
+    const int t0 = tok0 + c * kCh;
+    const int nrow = min(kCh, len - c * kCh);
+    const int64_t base = (static_cast<int64_t>(t0) * H + h) * kD;
+    const uint32_t bytes = (nrow - 1) * rs + kD * 2;   // rows past the end read 0
+    const auto rq = make_rsrc(p.q + base, bytes);
+    const auto rk = make_rsrc(p.k + base, bytes);
+    const auto rg = make_rsrc(p.g + base, bytes);
+    const uint32_t row = (16 * I + l16) * rs;
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const uint32_t off = row + (32 * (2 * hf + b2) + 16 * hh + 4 * g4) * 2;
+        in.q[b2][hh] = buf_ld64(rq, off, 0);
+        in.k[b2][hh] = buf_ld64(rk, off, 0);
+        in.g[b2][hh] = buf_ld64(rg, off, 0);
+      }
+    const auto rb = make_rsrc(p.beta + static_cast<int64_t>(t0) * H + h, (nrow - 1) * H * 2 + 2);
+    in.beta = buf_ld16(rb, (16 * I + l16) * H * 2, 0);
+  };
+
+  ChunkIn cur;
+  if (nchunks > 0) load_chunk(0, cur);
+
+  for (int c = 0; c < nchunks; ++c) {
+    const int t0 = tok0 + c * kCh;
+    const int nrow = min(kCh, len - c * kCh);
+    // v in accumulator order (rows 16 tt + 4 g + i of value column 16 jt + l16), used
+    // by the state step at the end of the chunk
+    uint32_t vin[4][4];
+    {
+      const auto rv = make_rsrc(p.v + (static_cast<int64_t>(t0) * H + h) * kD, (nrow - 1) * rs + kD * 2);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          vin[tt][i] = buf_ld16(rv, (16 * tt + 4 * g4 + i) * rs + (16 * jt + l16) * 2, 0);
+    }
+
+    // ============================================ E1: cumulative log-decay per sub-tile
+    float L[2][8];          // inclusive sum of g over the sub-tile's rows up to this one
+    float kf[2][8], qf[2][8];
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t wg = static_cast<uint32_t>(cur.g[b2][e >> 2][(e >> 1) & 1]);
+        const uint32_t wk = static_cast<uint32_t>(cur.k[b2][e >> 2][(e >> 1) & 1]);
+        const uint32_t wq = static_cast<uint32_t>(cur.q[b2][e >> 2][(e >> 1) & 1]);
+        const float gv = (e & 1) ? bf16hi(wg) : bf16lo(wg);
+        kf[b2][e] = (e & 1) ? bf16hi(wk) : bf16lo(wk);
+        qf[b2][e] = (e & 1) ? bf16hi(wq) : bf16lo(wq);
+        L[b2][e] = row_scan16(gv);
+      }
+    const float beta_t = bf16lo(cur.beta);
+    if (l16 == 15) {   // sub-tile totals R_I - R_{I-1}
+      float* tot = reinterpret_cast<float*>(smem + fl::TOT) + I * kD;
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          *reinterpret_cast<float4*>(tot + 32 * (2 * hf + b2) + 16 * hh + 4 * g4) =
+              float4{L[b2][4 * hh], L[b2][4 * hh + 1], L[b2][4 * hh + 2], L[b2][4 * hh + 3]};
+    }
+    if (hf == 0 && g4 == 0) reinterpret_cast<float*>(smem + fl::BETA)[16 * I + l16] = beta_t;
+    __syncthreads();                                                          // B1
+
+    // ============================================ E2: sub-tile referenced operands
+    // rowf = e^{L_t - R_I} >= 1, colf = e^{R_I - L_t} <= 1 (R_I: end of the sub-tile)
+    float kr[2][8], kc[2][8];
+    bf16x8_t fKr[2], fQr[2], fKc[2];
+    {
+      const float* tot = reinterpret_cast<const float*>(smem + fl::TOT) + I * kD;
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) {
+        float qr[8];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const float4 t4 = *reinterpret_cast<const float4*>(tot + 32 * (2 * hf + b2) + 16 * hh + 4 * g4);
+          const float tv[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = 4 * hh + i;
+            const float d = (L[b2][e] - tv[i]) * kLog2e;      // >= 0
+            const float rowf = fast_exp2(d), colf = fast_exp2(-d);
+            kr[b2][e] = kf[b2][e] * rowf;
+            qr[e] = qf[b2][e] * rowf;
+            kc[b2][e] = kf[b2][e] * colf;
+          }
+        }
+        fKr[b2] = to_frag(kr[b2]);
+        fQr[b2] = to_frag(qr);
+        fKc[b2] = to_frag(kc[b2]);
+        // q is only needed through Qr and Qb: keep the factor in qf
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[b2][e] = qr[e];
+      }
+    }
+    // per-channel factors, one thread per channel
+    if (tid < kD) {
+      const float* tot = reinterpret_cast<const float*>(smem + fl::TOT);
+      float t4[4], R[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) t4[m] = tot[m * kD + tid];
+      R[0] = t4[0];
+#pragma unroll
+      for (int m = 1; m < 4; ++m) R[m] = R[m - 1] + t4[m];
+      float* fac = reinterpret_cast<float*>(smem + fl::FAC);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float rb = m == 0 ? 0.f : R[m - 1];          // decay before sub-tile m
+        const float ep = fast_exp2(rb * kLog2e);
+        fac[(m * 4 + 0) * kD + tid] = fast_exp2(t4[m] * kLog2e);          // e^{tot_m}
+        fac[(m * 4 + 1) * kD + tid] = -ep;                                 // -e^{R_{m-1}}
+        fac[(m * 4 + 2) * kD + tid] = p.scale * ep;                        // scale e^{R_{m-1}}
+        fac[(m * 4 + 3) * kD + tid] = fast_exp2((R[3] - R[m]) * kLog2e);   // e^{Ln - R_m}
+      }
+      float* foff = reinterpret_cast<float*>(smem + fl::FOFF);
+#pragma unroll
+      for (int a = 1; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < a; ++b) foff[off_id(a, b) * kD + tid] = fast_exp2((R[a] - R[b]) * kLog2e);
+      reinterpret_cast<float*>(smem + fl::LAM)[tid] = fast_exp2(R[3] * kLog2e);
+    }
+    __syncthreads();                                                          // B2
+
+    // ============================================ E3: chunk operands to LDS
+    {
+      const float* fac = reinterpret_cast<const float*>(smem + fl::FAC);
+      const float* foff = reinterpret_cast<const float*>(smem + fl::FOFF);
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) {
+        const int blk = 2 * hf + b2;
+        float kb[8], qb[8], kt[8];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int c0 = 32 * blk + 16 * hh + 4 * g4;
+          const float4 fT = *reinterpret_cast<const float4*>(fac + (I * 4 + 0) * kD + c0);
+          const float4 fK = *reinterpret_cast<const float4*>(fac + (I * 4 + 1) * kD + c0);
+          const float4 fQ = *reinterpret_cast<const float4*>(fac + (I * 4 + 2) * kD + c0);
+          const float4 fN = *reinterpret_cast<const float4*>(fac + (I * 4 + 3) * kD + c0);
+          const float vT[4] = {fT.x, fT.y, fT.z, fT.w}, vK[4] = {fK.x, fK.y, fK.z, fK.w};
+          const float vQ[4] = {fQ.x, fQ.y, fQ.z, fQ.w}, vN[4] = {fN.x, fN.y, fN.z, fN.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = 4 * hh + i;
+            kb[e] = kr[b2][e] * vT[i] * vK[i];     // -K e^{L}
+            qb[e] = qf[b2][e] * vT[i] * vQ[i];     // scale Q e^{L}
+            kt[e] = kc[b2][e] * vN[i];             // K e^{Ln - L}
+          }
+        }
+        *reinterpret_cast<bf16x8_t*>(smem + fl::KBN + frag_at(I, blk, 4, lane)) = to_frag(kb);
+        *reinterpret_cast<bf16x8_t*>(smem + fl::QB + frag_at(I, blk, 4, lane)) = to_frag(qb);
+        // Kt^T: row = channel, contraction over tokens; token 16 I + l16 sits in
+        // s-block I/2 at lane group l16/4, element (l16 % 4) + 4 (I % 2)
+        {
+          const int sblk = I >> 1, eo = (l16 & 3) + 4 * (I & 1), gq = l16 >> 2;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int ch = perm_ch(blk, g4, e);
+            const int off = frag_at(ch >> 4, sblk, 2, (ch & 15) + 16 * gq) + eo * 2;
+            *reinterpret_cast<__bf16*>(smem + fl::KTT + off) = static_cast<__bf16>(kt[e]);
+          }
+        }
+        // column side of the off-diagonal pairs (I' > I, I): K e^{R_I' - L}
+#pragma unroll
+        for (int a = 1; a < 4; ++a) {
+          if (a > I) {
+            float x[8];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const float4 f4 = *reinterpret_cast<const float4*>(
+                  foff + off_id(a, I) * kD + 32 * blk + 16 * hh + 4 * g4);
+              x[4 * hh] = kc[b2][4 * hh] * f4.x;
+              x[4 * hh + 1] = kc[b2][4 * hh + 1] * f4.y;
+              x[4 * hh + 2] = kc[b2][4 * hh + 2] * f4.z;
+              x[4 * hh + 3] = kc[b2][4 * hh + 3] * f4.w;
+            }
+            *reinterpret_cast<bf16x8_t*>(smem + fl::OFF + off_id(a, I) * 4096 + frag_at(0, blk, 4, lane)) =
+                to_frag(x);
+          }
+        }
+      }
+    }
+    __syncthreads();                                                          // B3
+
+    // ============================================ P: decayed sub-tile products
+    // transposed: C[s, t] = sum_c colside[s, c] rowside[t, c]; lane (t, g) holds
+    // s = 16 J + 4 g + i.  Partial over this wavefront's channel half.
+    {
+      f32x4_t pa[4], pm[4];
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        pa[J] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        pm[J] = pa[J];
+        if (J <= I) {
+#pragma unroll
+          for (int b2 = 0; b2 < 2; ++b2) {
+            const bf16x8_t cs = J == I ? fKc[b2]
+                                       : lds_frag(smem, fl::OFF + off_id(I, J) * 4096 +
+                                                            frag_at(0, 2 * hf + b2, 4, lane));
+            pa[J] = mma(cs, fKr[b2], pa[J]);
+            pm[J] = mma(cs, fQr[b2], pm[J]);
+          }
+        }
+      }
+      if (hf == 1) {
+#pragma unroll
+        for (int J = 0; J < 4; ++J)
+          if (J <= I) {
+            *reinterpret_cast<f32x4_t*>(smem + fl::PART + (pair_id(I, J) * 2 + 0) * 1024 + lane * 16) = pa[J];
+            *reinterpret_cast<f32x4_t*>(smem + fl::PART + (pair_id(I, J) * 2 + 1) * 1024 + lane * 16) = pm[J];
+          }
+      }
+      __syncthreads();                                                        // B4
+      if (hf == 0) {
+        const int t = 16 * I + l16;
+#pragma unroll
+        for (int J = 0; J < 4; ++J)
+          if (J <= I) {
+            const f32x4_t oa = *reinterpret_cast<const f32x4_t*>(smem + fl::PART + (pair_id(I, J) * 2 + 0) * 1024 + lane * 16);
+            const f32x4_t om = *reinterpret_cast<const f32x4_t*>(smem + fl::PART + (pair_id(I, J) * 2 + 1) * 1024 + lane * 16);
+            float av[4], mv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int s = 16 * J + 4 * g4 + i;
+              av[i] = s < t ? beta_t * (pa[J][i] + oa[i]) : 0.f;
+              mv[i] = s <= t ? p.scale * (pm[J][i] + om[i]) : 0.f;
+            }
+            *reinterpret_cast<float4*>(smem + fl::AT + at_off(t, 16 * J + 4 * g4)) =
+                float4{av[0], av[1], av[2], av[3]};
+            // M[t][s]: fragment (t-tile I, s-block J/2), elements 4 (J%2) .. +3
+            *reinterpret_cast<uint2*>(smem + fl::MF + frag_at(I, J >> 1, 2, l16 + 16 * g4) + 8 * (J & 1)) =
+                uint2{pack_bf16x2(mv[0], mv[1]), pack_bf16x2(mv[2], mv[3])};
+          }
+      }
+    }
+    __syncthreads();                                                          // B5
+
+    // ============================================ T = (I + A)^{-1}
+    auto at_el = [&](int row, int col) -> float& {
+      return *reinterpret_cast<float*>(smem + fl::AT + at_off(row, col));
+    };
+    auto at_row4 = [&](int row, int col0) -> float4 {
+      return *reinterpret_cast<const float4*>(smem + fl::AT + at_off(row, col0));
+    };
+    if (wave < 4) {
+      // diagonal blocks: A_ww strictly lower, so (I + A)^{-1} = (I - A)(I + A^2)(I + A^4)(I + A^8)
+      // on fp32 16x16x4 matrix cores.  A product's A operand is read in row layout (lane:
+      // row l16, columns 4 g4 .. +3), its B operand in accumulator layout (lane: rows
+      // 4 g4 .. +3 of column l16): a result feeds the next B side directly and its A
+      // side after a transpose through this wavefront's 16 x 17 scratch.
+      const int base = 16 * wave;
+      float* sc = reinterpret_cast<float*>(smem + fl::XS) + wave * 16 * 17;
+      auto mm = [&](const float (&xr)[4], const float (&yc)[4]) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xr[st], yc[st], acc, 0, 0, 0);
+        return acc;
+      };
+      auto to_row = [&](const f32x4_t& cc, float (&r)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[(4 * g4 + i) * 17 + l16] = cc[i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = sc[l16 * 17 + 4 * g4 + i];
+      };
+      const float4 ar4 = at_row4(base + l16, base + 4 * g4);
+      const float a_r[4] = {ar4.x, ar4.y, ar4.z, ar4.w};
+      float a_c[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a_c[i] = at_el(base + 4 * g4 + i, base + l16);
+      const f32x4_t p1 = mm(a_r, a_c);                           // A^2
+      const float p1_c[4] = {p1[0], p1[1], p1[2], p1[3]};
+      float p1_r[4];
+      to_row(p1, p1_r);
+      const f32x4_t p2 = mm(p1_r, p1_c);                         // A^4
+      const f32x4_t a3 = mm(a_r, p1_c);                          // A^3
+      const float p2_c[4] = {p2[0], p2[1], p2[2], p2[3]};
+      float p2_r[4];
+      to_row(p2, p2_r);
+      const f32x4_t p3 = mm(p2_r, p2_c);                         // A^8
+      const float p3_c[4] = {p3[0], p3[1], p3[2], p3[3]};
+      f32x4_t t1;                                                // I - A + A^2 - A^3
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t1[i] = (4 * g4 + i == l16 ? 1.f : 0.f) - a_c[i] + p1[i] - a3[i];
+      float t1_r[4];
+      to_row(t1, t1_r);
+      f32x4_t t2 = mm(t1_r, p2_c);                               // T1 (I + A^4)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t2[i] += t1[i];
+      float t2_r[4];
+      to_row(t2, t2_r);
+      f32x4_t t3 = mm(t2_r, p3_c);                               // T2 (I + A^8)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) at_el(base + 4 * g4 + i, base + l16) = t3[i] + t2[i];
+    }
+    __syncthreads();                                                          // B6
+    // I + A in 32 x 32 halves [[L1, 0], [B, L2]] has inverse [[L1^-1, 0], [-L2^-1 B L1^-1, L2^-1]]
+    if (wave < 2) {   // T_10 = -T_11 A_10 T_00 and T_32 = -T_33 A_32 T_22
+      const int bi = wave ? 3 : 1, bj = bi - 1;
+      f32x4_t y = {0.f, 0.f, 0.f, 0.f}, tt = y;
+      const float4 aIJ = at_row4(16 * bi + l16, 16 * bj + 4 * g4);
+      const float4 aII = at_row4(16 * bi + l16, 16 * bi + 4 * g4);
+      const float aij[4] = {aIJ.x, aIJ.y, aIJ.z, aIJ.w}, aii[4] = {aII.x, aII.y, aII.z, aII.w};
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        y = __builtin_amdgcn_mfma_f32_16x16x4f32(aij[st], at_el(16 * bj + 4 * g4 + st, 16 * bj + l16), y, 0, 0, 0);
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        tt = __builtin_amdgcn_mfma_f32_16x16x4f32(aii[st], y[st], tt, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) at_el(16 * bi + 4 * g4 + i, 16 * bj + l16) = -tt[i];
+    }
+    __syncthreads();                                                          // B7
+    float* xs = reinterpret_cast<float*>(smem + fl::XS);
+    const int qi = 2 + ((wave & 3) >> 1), qj = wave & 1;   // lower-left 16x16 block (waves 0-3)
+    if (wave < 4) {   // X_{qi,qj} = sum_{m=qj}^{1} A_{qi,m} T_{m,qj}
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        if (m >= qj) {
+          const float4 a4 = at_row4(16 * qi + l16, 16 * m + 4 * g4);
+          const float a[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+          for (int st = 0; st < 4; ++st)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], at_el(16 * m + 4 * g4 + st, 16 * qj + l16), acc, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xs[(wave * 16 + 4 * g4 + i) * 17 + l16] = acc[i];
+    }
+    __syncthreads();                                                          // B8
+    if (wave < 4) {   // T_{qi,qj} = -sum_{m=2}^{qi} T_{qi,m} X_{m,qj}
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 2; m < 4; ++m) {
+        if (m <= qi) {
+          const int xw = (m - 2) * 2 + qj;
+          const float4 a4 = at_row4(16 * qi + l16, 16 * m + 4 * g4);
+          const float a[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+          for (int st = 0; st < 4; ++st)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], xs[(xw * 16 + 4 * g4 + st) * 17 + l16], acc, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) at_el(16 * qi + 4 * g4 + i, 16 * qj + l16) = -acc[i];
+    }
+    __syncthreads();                                                          // B9
+    {   // Tb = T Diag(beta) as fragments: thread -> (t-tile, s-block, lane)
+      const int ttile = tid >> 7, sblk = (tid >> 6) & 1;
+      const int row = 16 * ttile + l16;
+      const float* bet = reinterpret_cast<const float*>(smem + fl::BETA);
+      float x[8];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int s0 = 32 * sblk + 16 * hh + 4 * g4;
+        const float4 tv = at_row4(row, s0);
+        const float4 bv = *reinterpret_cast<const float4*>(bet + s0);
+        x[4 * hh] = tv.x * bv.x;
+        x[4 * hh + 1] = tv.y * bv.y;
+        x[4 * hh + 2] = tv.z * bv.z;
+        x[4 * hh + 3] = tv.w * bv.w;
+      }
+      *reinterpret_cast<bf16x8_t*>(smem + fl::TBF + frag_at(ttile, sblk, 2, lane)) = to_frag(x);
+    }
+    __syncthreads();                                                          // B10
+
+    // ============================================ state step
+    ChunkIn nxt;
+    if (c + 1 < nchunks) load_chunk(c + 1, nxt);
+
+    bf16x8_t Sb[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) Sb[b] = acc_frag(S[2 * b], S[2 * b + 1]);
+    // X = V - Kb S (the stored -Kb makes it an accumulation onto V)
+    f32x4_t X[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) X[tt][i] = __uint_as_float(vin[tt][i] << 16);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) X[tt] = mma(lds_frag(smem, fl::KBN + frag_at(tt, b, 4, lane)), Sb[b], X[tt]);
+    }
+    bf16x8_t Xb[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) Xb[b] = acc_frag(X[2 * b], X[2 * b + 1]);
+    // Delta = Tb X (Tb lower triangular: t-tiles 0, 1 need s-block 0 only)
+    f32x4_t Dl[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      Dl[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        if (b <= (tt >> 1)) Dl[tt] = mma(lds_frag(smem, fl::TBF + frag_at(tt, b, 2, lane)), Xb[b], Dl[tt]);
+    }
+    bf16x8_t Db[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) Db[b] = acc_frag(Dl[2 * b], Dl[2 * b + 1]);
+    // O^T = S^T Qb^T + Delta^T M^T: lane (t, g) holds value columns 16 jt + 4 g .. +3
+    {
+      const auto ro = make_rsrc(p.out + (static_cast<int64_t>(t0) * H + h) * kD, (nrow - 1) * rs + kD * 2);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < 4; ++b) o = mma(Sb[b], lds_frag(smem, fl::QB + frag_at(tt, b, 4, lane)), o);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          if (b <= (tt >> 1)) o = mma(Db[b], lds_frag(smem, fl::MF + frag_at(tt, b, 2, lane)), o);
+        buf_st64_nt(i32x2_t{static_cast<int>(pack_bf16x2(o[0], o[1])), static_cast<int>(pack_bf16x2(o[2], o[3]))},
+                    ro, (16 * tt + l16) * rs + (16 * jt + 4 * g4) * 2, 0);
+      }
+    }
+    // S <- Diag(Lambda) S + Kt^T Delta
+    {
+      const float* lam = reinterpret_cast<const float*>(smem + fl::LAM);
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        const float4 l4 = *reinterpret_cast<const float4*>(lam + 16 * ct + 4 * g4);
+        f32x4_t acc = {S[ct][0] * l4.x, S[ct][1] * l4.y, S[ct][2] * l4.z, S[ct][3] * l4.w};
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc = mma(lds_frag(smem, fl::KTT + frag_at(ct, b, 2, lane)), Db[b], acc);
+        S[ct] = acc;
+      }
+    }
+    if (c + 1 < nchunks) cur = nxt;
+  }
+
+  if (p.sT != nullptr) {
+    float* dst = p.sT + (static_cast<int64_t>(n) * H + h) * kD * kD;
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[(16 * ct + 4 * g4 + i) * kD + 16 * jt + l16] = S[ct][i];
+  }
+}
+
+}  // namespace
+
+bool fused_prefill_supported(const PrefillArgs& a) {
+  return !a.dtype_f32 && a.d == kD && !a.prologue && a.snapshots == nullptr;
+}
+
+hipError_t launch_fused_prefill(const PrefillArgs& a) {
+  FusedParams fp{static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),
+                 static_cast<const bf16_t*>(a.v), static_cast<const bf16_t*>(a.g),
+                 static_cast<const bf16_t*>(a.beta), a.initial_state, static_cast<bf16_t*>(a.out),
+                 a.final_state, a.cu_seqlens, a.N, a.T, a.total_T, a.H, a.scale};
+  hipLaunchKernelGGL(fused_prefill_kernel, dim3(static_cast<unsigned>(a.N) * a.H), dim3(kThreadsF), 0,
+                     a.stream, fp);
+  return hipGetLastError();
+}
+
+}  // namespace kda

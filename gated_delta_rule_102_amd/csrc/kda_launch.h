@@ -78,6 +78,10 @@ hipError_t launch_compose(const ComposeArgs& a);
 hipError_t launch_backward(const BackwardArgs& a);
 
 hipError_t launch_prefill(const PrefillArgs& a);
+// Fused prefill (one workgroup per (sequence, head), no workspace): bf16, d = 128,
+// without the prologue or snapshots.
+bool fused_prefill_supported(const PrefillArgs& a);
+hipError_t launch_fused_prefill(const PrefillArgs& a);
 // Kernels launch_prefill runs for these arguments (static text, for reports).
 const char* prefill_schedule(const PrefillArgs& a);
 // Workspace bytes launch_prefill needs for these arguments (0 if unsupported).

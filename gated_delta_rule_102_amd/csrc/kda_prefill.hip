@@ -1495,8 +1495,18 @@ inline int prefill_cg(const PrefillArgs& a) {
   return cg;
 }
 
+// Streams from which bf16 d = 128 prefill runs fused (fused_prefill_kernel): one
+// workgroup per (sequence, head) keeps every CU busy and no chunk operand goes
+// through memory.
+constexpr int kFusedStreams = 256;
+
+inline bool use_fused(const PrefillArgs& a) {
+  return fused_prefill_supported(a) && static_cast<int64_t>(a.N) * a.H >= kFusedStreams;
+}
+
 template <int D, typename TIn>
 size_t workspace_bytes(const PrefillArgs& a) {
+  if (use_fused(a)) return 0;
   const int cg = prefill_cg(a);
   return cg > 0 ? grouped_bytes<D, TIn>(a, cg) : all_chunks_bytes<D, TIn>(a);
 }
@@ -1547,6 +1557,7 @@ size_t prefill_workspace_bytes(const PrefillArgs& a) {
 }
 
 const char* prefill_schedule(const PrefillArgs& a) {
+  if (use_fused(a)) return "fused_prefill_kernel (one workgroup per (sequence, head))";
   const bool f32 = a.dtype_f32;
   const int D = a.d;
   const int cg = prefill_cg(a);
@@ -1576,7 +1587,7 @@ hipError_t launch_prefill(const PrefillArgs& a) {
     if (a.d == 64) return launch_all<64, float>(a);
     return hipErrorNotSupported;
   }
-  if (a.d == 128) return launch_all<128, bf16_t>(a);
+  if (a.d == 128) return use_fused(a) ? launch_fused_prefill(a) : launch_all<128, bf16_t>(a);
   return launch_all<64, bf16_t>(a);
 }
 
