@@ -30,18 +30,24 @@
 // Layout inside the workgroup (8 wavefronts):
 //  - Elementwise and sub-tile products: wavefront w owns rows 16 (w/2) .. +15 of the
 //    chunk and the key channels of 32-channel blocks 2 (w%2) and 2 (w%2) + 1; lane
-//    (r, g) holds row r and, in each block b, the 8 channels
-//        32 b + 4 g + {0, 1, 2, 3} and 32 b + 16 + 4 g + {0, 1, 2, 3},
-//    which is exactly the operand fragment of v_mfma_f32_16x16x32_bf16 with the
-//    contraction index taken in that order.  Every product contracting over key
-//    channels (or over tokens) uses this order on both sides.
+//    (r, g) holds row r and, in each block b, the 8 channels 32 b + 8 g .. +7 -- one
+//    operand fragment of v_mfma_f32_16x16x32_bf16, loaded with one 16-byte load.
 //  - State: wavefront w owns value columns 16 w .. +15 of S for all 128 key channels,
-//    as 8 accumulator tiles.  An accumulator tile pair (rows 32 b .. +31) holds, per
-//    lane, rows 32 b + 4 g + i and 32 b + 16 + 4 g + i -- the same order -- so the state
-//    (and X and Delta, accumulators over tokens) feed the next products as operands
-//    with one conversion to bf16 and no transpose.  The output is produced
-//    transposed (rows = value columns), so each lane holds 4 consecutive values of
-//    one token's output row and writes them with one 8-byte store.
+//    as 8 accumulator tiles.  Accumulator row r holds key channel
+//        sigma(r) = 32 b + 8 g + 4 h + i   for r = 32 b + 16 h + 4 g + i,
+//    so that an accumulator tile pair (2 b, 2 b + 1) read as one operand fragment
+//    holds channels 32 b + 8 g .. +7 in order: the state feeds the products with the
+//    key-side operands with one conversion to bf16 and no transpose.  Products that
+//    contract over the chunk's tokens take X and Delta the same way, with the tokens
+//    of a 32-token block in the order 4 g + i, 16 + 4 g + i on both sides.
+//  - Delta = (I + A)^{-1} Diag(beta) X is a block forward substitution over the four
+//    16-token sub-tiles, in each wavefront for its own value columns (16x16x16
+//    products): Delta_i = T_ii (Y_i - sum_{m<i} A_im Delta_m), Y = Diag(beta) X, with
+//    the 16 x 16 inverses T_ii = (I + A_ii)^{-1} = (I - A)(I + A^2)(I + A^4)(I + A^8)
+//    (A_ii is strictly lower, so A^16 = 0).
+//  - The output is produced transposed (rows = value columns), so each lane holds 4
+//    consecutive values of one token's output row and writes them with one 8-byte
+//    store.
 
 #include "kda_device.h"
 #include "kda_launch.h"
@@ -54,23 +60,25 @@ constexpr int kD = 128;      // dk = dv
 constexpr int kCh = 64;      // chunk
 constexpr int kThreadsF = 512;
 
-// LDS regions (bytes).  Fragment-ordered operands are [tile][block][lane][16 B].
+// LDS regions (bytes).  Fragment-ordered operands are [tile][block][lane][bytes].
 namespace fl {
-constexpr int KBN = 0;                      // -Kb       [4 t-tiles][4 c-blocks]
-constexpr int QB = KBN + 16384;             // Qb        [4 t-tiles][4 c-blocks]
-constexpr int KTT = QB + 16384;             // Kt^T      [8 c-tiles][2 s-blocks]
-constexpr int TBF = KTT + 16384;            // Tb        [4 t-tiles][2 s-blocks]
-constexpr int MF = TBF + 8192;              // M         [4 t-tiles][2 s-blocks]
-constexpr int LAM = MF + 8192;              // Lambda    [128] fp32
-constexpr int OFF = LAM + 512;              // column side of pair (I, J < I): [6][4][64][16]
+constexpr int KBN = 0;                      // -Kb       [4 t-tiles][4 c-blocks] x 16 B
+constexpr int QB = KBN + 16384;             // Qb        [4 t-tiles][4 c-blocks] x 16 B
+constexpr int KTT = QB + 16384;             // Kt^T      [8 state tiles][2 s-blocks] x 16 B
+constexpr int MF = KTT + 16384;             // M         [4 t-tiles][2 s-blocks] x 16 B
+constexpr int AOF = MF + 8192;              // -A_IJ, J < I: [6][64 lanes] x 8 B (16x16x16 A)
+constexpr int TDF = AOF + 6 * 512;          // T_II:        [4][64 lanes] x 8 B
+constexpr int LAM = TDF + 4 * 512;          // Lambda, state row order [128] fp32
+constexpr int VRB = 1024 + 32;              // v staging: 4 rows (1 KB) + pad per group
+constexpr int VST = LAM + 512;              // v of the chunk, [16 groups][VRB]
+constexpr int OFF = VST + 16 * VRB;         // column side of pair (I, J < I): [6][4][64][16]
 constexpr int PART = OFF + 6 * 4096;        // partial A^T, M^T of 10 pairs: [10][2][64][16]
-constexpr int AT = PART + 10 * 2048;        // A, then T in place: [64][64] fp32, swizzled
-constexpr int XS = AT + 16384;              // inverse scratch: 4 x [16][17] fp32
+constexpr int XS = PART + 10 * 2048;        // 16 x 17 fp32 transpose scratch, 4 wavefronts
 constexpr int TOT = XS + 4 * 16 * 17 * 4;   // sub-tile decay totals [4][128] fp32
-constexpr int FAC = TOT + 4 * 128 * 4;      // per (sub-tile, channel) factors [4][4][128]
-constexpr int FOFF = FAC + 4 * 4 * 128 * 4; // e^{R_I - R_J}, I > J: [6][128]
-constexpr int BETA = FOFF + 6 * 128 * 4;    // [64] fp32
-constexpr int ORD = BETA + 256;             // sequence order (packed input) [<= 256]
+constexpr int FAC = TOT + 4 * 128 * 4;      // per (sub-tile, channel) factors [4][3][128]
+constexpr int FOFF = FAC + 4 * 3 * 128 * 4; // e^{R_I - R_J}, I > J: [6][128]
+constexpr int BETA = FOFF + 6 * 128 * 4;    // [2 parities][64] fp32
+constexpr int ORD = BETA + 512;             // sequence order (packed input) [<= 256]
 constexpr int BYTES = ORD + 1024;
 static_assert(BYTES <= 160 * 1024, "LDS budget");
 }  // namespace fl
@@ -97,9 +105,9 @@ __device__ __forceinline__ void fused_seq(const FusedParams& p, int n, int& tok0
   }
 }
 
-// Channel of element e (0..7) of the fragment of 32-channel block b held by lane group g.
-__device__ __forceinline__ constexpr int perm_ch(int b, int g, int e) {
-  return 32 * b + 4 * g + (e & 3) + 16 * (e >> 2);
+// Key channel held by state accumulator row r (see the layout notes above).
+__device__ __forceinline__ constexpr int sigma(int r) {
+  return 32 * (r >> 5) + 8 * ((r >> 2) & 3) + 4 * ((r >> 4) & 1) + (r & 3);
 }
 
 // Byte offset of fragment (tile, blk) of an operand with NB blocks per tile, for `lane`.
@@ -107,11 +115,11 @@ __device__ __forceinline__ int frag_at(int tile, int blk, int nb, int lane) {
   return ((tile * nb + blk) * 64 + lane) * 16;
 }
 
-// (row, byte) of the swizzled fp32 [64][64] A/T array: the 16-byte pieces of each row
-// are permuted by the row index so column reads do not collide on banks.
-__device__ __forceinline__ int at_off(int row, int col) {
-  const int byte = col * 4;
-  return row * 256 + ((((byte >> 4) ^ (row & 15))) << 4) + (byte & 15);
+// Workgroup barrier ordering LDS only: this wavefront's LDS operations complete, then
+// s_barrier.  (__syncthreads() also waits for every global load in flight, the next
+// chunk's prefetch and the loads whose destination is LDS included.)
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 template <int CTRL>
@@ -135,7 +143,7 @@ __device__ __forceinline__ bf16x8_t to_frag(const float (&x)[8]) {
   return f;
 }
 
-// Accumulator tiles (2 b, 2 b + 1) as one operand fragment in the channel order above.
+// Accumulator tiles (2 b, 2 b + 1) as one 32-deep operand fragment.
 __device__ __forceinline__ bf16x8_t acc_frag(const f32x4_t& lo, const f32x4_t& hi) {
   bf16x8_t f;
 #pragma unroll
@@ -146,12 +154,25 @@ __device__ __forceinline__ bf16x8_t acc_frag(const f32x4_t& lo, const f32x4_t& h
   return f;
 }
 
+typedef __attribute__((ext_vector_type(4))) short bf16x4_t;   // 16x16x16 operand
+
+// One accumulator tile as a 16-deep operand fragment.
+__device__ __forceinline__ bf16x4_t acc_frag4(const f32x4_t& a) {
+  return __builtin_bit_cast(bf16x4_t, uint2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])});
+}
+
 __device__ __forceinline__ bf16x8_t lds_frag(const char* smem, int off) {
   return *reinterpret_cast<const bf16x8_t*>(smem + off);
+}
+__device__ __forceinline__ bf16x4_t lds_frag4(const char* smem, int off) {
+  return *reinterpret_cast<const bf16x4_t*>(smem + off);
 }
 
 __device__ __forceinline__ f32x4_t mma(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mma16(const bf16x4_t& a, const bf16x4_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
 // Pair number of sub-tile pair (I, J), J <= I: (0,0),(1,0),(1,1),(2,0),...,(3,3).
@@ -160,9 +181,9 @@ __device__ __forceinline__ constexpr int pair_id(int I, int J) { return I * (I +
 __device__ __forceinline__ constexpr int off_id(int I, int J) { return I * (I - 1) / 2 + J; }
 
 // Key-side inputs of one chunk as loaded: q, k, g (16 channels of one row per lane,
-// 8-byte pieces in fragment order) and beta of the row.  v is loaded separately.
+// two 16-byte fragments each) and beta of the row.
 struct ChunkIn {
-  i32x2_t q[2][2], k[2][2], g[2][2];
+  i32x4_t q[2], k[2], g[2];
   uint32_t beta;
 };
 
@@ -204,9 +225,8 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
   fused_seq(p, n, tok0, len);
   const int nchunks = (len + kCh - 1) / kCh;
 
-  // upper sub-tiles of A/T and M are read as zeros; nothing else writes them
-  for (int e = tid; e < 64 * 64; e += kThreadsF)
-    *reinterpret_cast<float*>(smem + fl::AT + at_off(e >> 6, e & 63)) = 0.f;
+  // M is lower triangular: the upper halves of fragments (0, 0) and (2, 1) are read as
+  // zeros and nothing else writes them
   for (int e = tid; e < 8192 / 16; e += kThreadsF)
     *reinterpret_cast<i32x4_t*>(smem + fl::MF + e * 16) = i32x4_t{0, 0, 0, 0};
 
@@ -218,7 +238,7 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
     for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        S[ct][i] = s0 ? s0[(16 * ct + 4 * g4 + i) * kD + 16 * jt + l16] : 0.f;
+        S[ct][i] = s0 ? s0[sigma(16 * ct + 4 * g4 + i) * kD + 16 * jt + l16] : 0.f;
   }
 
   const uint32_t rs = static_cast<uint32_t>(H) * kD * 2;   // token row stride (bytes)
@@ -233,14 +253,12 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
     const auto rg = make_rsrc(p.g + base, bytes);
     const uint32_t row = (16 * I + l16) * rs;
 #pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const uint32_t off = row + (32 * (2 * hf + b2) + 16 * hh + 4 * g4) * 2;
-        in.q[b2][hh] = buf_ld64(rq, off, 0);
-        in.k[b2][hh] = buf_ld64(rk, off, 0);
-        in.g[b2][hh] = buf_ld64(rg, off, 0);
-      }
+    for (int b2 = 0; b2 < 2; ++b2) {
+      const uint32_t off = row + (32 * (2 * hf + b2) + 8 * g4) * 2;
+      in.q[b2] = buf_ld128(rq, off, 0);
+      in.k[b2] = buf_ld128(rk, off, 0);
+      in.g[b2] = buf_ld128(rg, off, 0);
+    }
     const auto rb = make_rsrc(p.beta + static_cast<int64_t>(t0) * H + h, (nrow - 1) * H * 2 + 2);
     in.beta = buf_ld16(rb, (16 * I + l16) * H * 2, 0);
   };
@@ -251,77 +269,53 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
   for (int c = 0; c < nchunks; ++c) {
     const int t0 = tok0 + c * kCh;
     const int nrow = min(kCh, len - c * kCh);
-    // v in accumulator order (rows 16 tt + 4 g + i of value column 16 jt + l16), used
-    // by the state step at the end of the chunk
-    uint32_t vin[4][4];
-    {
-      const auto rv = make_rsrc(p.v + (static_cast<int64_t>(t0) * H + h) * kD, (nrow - 1) * rs + kD * 2);
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          vin[tt][i] = buf_ld16(rv, (16 * tt + 4 * g4 + i) * rs + (16 * jt + l16) * 2, 0);
-    }
+    float* betas = reinterpret_cast<float*>(smem + fl::BETA) + (c & 1) * kCh;
 
     // ============================================ E1: cumulative log-decay per sub-tile
     float L[2][8];          // inclusive sum of g over the sub-tile's rows up to this one
-    float kf[2][8], qf[2][8];
+    uint32_t kw[2][4], qw[2][4];   // k and q as loaded (bf16 pairs, channel order)
 #pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2)
+    for (int b2 = 0; b2 < 2; ++b2) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t wg = static_cast<uint32_t>(cur.g[b2][e >> 2][(e >> 1) & 1]);
-        const uint32_t wk = static_cast<uint32_t>(cur.k[b2][e >> 2][(e >> 1) & 1]);
-        const uint32_t wq = static_cast<uint32_t>(cur.q[b2][e >> 2][(e >> 1) & 1]);
-        const float gv = (e & 1) ? bf16hi(wg) : bf16lo(wg);
-        kf[b2][e] = (e & 1) ? bf16hi(wk) : bf16lo(wk);
-        qf[b2][e] = (e & 1) ? bf16hi(wq) : bf16lo(wq);
-        L[b2][e] = row_scan16(gv);
+        const uint32_t wg = static_cast<uint32_t>(cur.g[b2][e >> 1]);
+        L[b2][e] = row_scan16((e & 1) ? bf16hi(wg) : bf16lo(wg));
       }
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        kw[b2][w] = static_cast<uint32_t>(cur.k[b2][w]);
+        qw[b2][w] = static_cast<uint32_t>(cur.q[b2][w]);
+      }
+    }
     const float beta_t = bf16lo(cur.beta);
+    // the key-side registers are free again: the next chunk's loads go out now and
+    // have the rest of this chunk to arrive
+    if (c + 1 < nchunks) load_chunk(c + 1, cur);
     if (l16 == 15) {   // sub-tile totals R_I - R_{I-1}
       float* tot = reinterpret_cast<float*>(smem + fl::TOT) + I * kD;
 #pragma unroll
       for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
-          *reinterpret_cast<float4*>(tot + 32 * (2 * hf + b2) + 16 * hh + 4 * g4) =
+          *reinterpret_cast<float4*>(tot + 32 * (2 * hf + b2) + 8 * g4 + 4 * hh) =
               float4{L[b2][4 * hh], L[b2][4 * hh + 1], L[b2][4 * hh + 2], L[b2][4 * hh + 3]};
     }
-    if (hf == 0 && g4 == 0) reinterpret_cast<float*>(smem + fl::BETA)[16 * I + l16] = beta_t;
-    __syncthreads();                                                          // B1
+    if (hf == 0 && g4 == 0) betas[16 * I + l16] = beta_t;
+    lds_barrier();                                                          // B1
 
-    // ============================================ E2: sub-tile referenced operands
-    // rowf = e^{L_t - R_I} >= 1, colf = e^{R_I - L_t} <= 1 (R_I: end of the sub-tile)
-    float kr[2][8], kc[2][8];
-    bf16x8_t fKr[2], fQr[2], fKc[2];
+    // v of this chunk straight into LDS (16-byte loads whose destination is LDS; 4
+    // rows per wavefront instruction, each group of 4 rows padded by 32 bytes)
     {
-      const float* tot = reinterpret_cast<const float*>(smem + fl::TOT) + I * kD;
+      const auto rv = make_rsrc(p.v + (static_cast<int64_t>(t0) * H + h) * kD, (nrow - 1) * rs + kD * 2);
 #pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2) {
-        float qr[8];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const float4 t4 = *reinterpret_cast<const float4*>(tot + 32 * (2 * hf + b2) + 16 * hh + 4 * g4);
-          const float tv[4] = {t4.x, t4.y, t4.z, t4.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int e = 4 * hh + i;
-            const float d = (L[b2][e] - tv[i]) * kLog2e;      // >= 0
-            const float rowf = fast_exp2(d), colf = fast_exp2(-d);
-            kr[b2][e] = kf[b2][e] * rowf;
-            qr[e] = qf[b2][e] * rowf;
-            kc[b2][e] = kf[b2][e] * colf;
-          }
-        }
-        fKr[b2] = to_frag(kr[b2]);
-        fQr[b2] = to_frag(qr);
-        fKc[b2] = to_frag(kc[b2]);
-        // q is only needed through Qr and Qb: keep the factor in qf
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[b2][e] = qr[e];
+      for (int x = 0; x < 2; ++x) {
+        const int grp = 2 * wave + x;                  // rows 4 grp .. +3
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rv, (__attribute__((address_space(3))) void*)(smem + fl::VST + grp * fl::VRB), 16,
+            (4 * grp + (lane >> 4)) * rs + (lane & 15) * 16, 0, 0, 0);
       }
     }
+
     // per-channel factors, one thread per channel
     if (tid < kD) {
       const float* tot = reinterpret_cast<const float*>(smem + fl::TOT);
@@ -335,56 +329,72 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const float rb = m == 0 ? 0.f : R[m - 1];          // decay before sub-tile m
-        const float ep = fast_exp2(rb * kLog2e);
-        fac[(m * 4 + 0) * kD + tid] = fast_exp2(t4[m] * kLog2e);          // e^{tot_m}
-        fac[(m * 4 + 1) * kD + tid] = -ep;                                 // -e^{R_{m-1}}
-        fac[(m * 4 + 2) * kD + tid] = p.scale * ep;                        // scale e^{R_{m-1}}
-        fac[(m * 4 + 3) * kD + tid] = fast_exp2((R[3] - R[m]) * kLog2e);   // e^{Ln - R_m}
+        // e^{R_m} as e^{tot_m} e^{R_{m-1}}: each factor alone is in range
+        const float em = fast_exp2(t4[m] * kLog2e) * fast_exp2(rb * kLog2e);
+        fac[(m * 3 + 0) * kD + tid] = -em;                                 // -e^{R_m}
+        fac[(m * 3 + 1) * kD + tid] = p.scale * em;                        // scale e^{R_m}
+        fac[(m * 3 + 2) * kD + tid] = fast_exp2((R[3] - R[m]) * kLog2e);   // e^{Ln - R_m}
       }
       float* foff = reinterpret_cast<float*>(smem + fl::FOFF);
 #pragma unroll
       for (int a = 1; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < a; ++b) foff[off_id(a, b) * kD + tid] = fast_exp2((R[a] - R[b]) * kLog2e);
-      reinterpret_cast<float*>(smem + fl::LAM)[tid] = fast_exp2(R[3] * kLog2e);
+      // Lambda in state row order: row r holds channel sigma(r)
+      const int r = 32 * (tid >> 5) + 16 * ((tid >> 2) & 1) + 4 * ((tid >> 3) & 3) + (tid & 3);
+      reinterpret_cast<float*>(smem + fl::LAM)[r] = fast_exp2(R[3] * kLog2e);
     }
-    __syncthreads();                                                          // B2
+    lds_barrier();                                                          // B2
 
-    // ============================================ E3: chunk operands to LDS
+    // ============================================ E2: chunk operands
+    // rowf = e^{L_t - R_I} >= 1, colf = e^{R_I - L_t} <= 1 (R_I: end of the sub-tile)
+    bf16x8_t fKr[2], fQr[2], fKc[2];
     {
+      const float* tot = reinterpret_cast<const float*>(smem + fl::TOT) + I * kD;
       const float* fac = reinterpret_cast<const float*>(smem + fl::FAC);
       const float* foff = reinterpret_cast<const float*>(smem + fl::FOFF);
 #pragma unroll
       for (int b2 = 0; b2 < 2; ++b2) {
         const int blk = 2 * hf + b2;
-        float kb[8], qb[8], kt[8];
+        float kr[8], qr[8], kc[8], kb[8], qb[8], kt[8];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const int c0 = 32 * blk + 16 * hh + 4 * g4;
-          const float4 fT = *reinterpret_cast<const float4*>(fac + (I * 4 + 0) * kD + c0);
-          const float4 fK = *reinterpret_cast<const float4*>(fac + (I * 4 + 1) * kD + c0);
-          const float4 fQ = *reinterpret_cast<const float4*>(fac + (I * 4 + 2) * kD + c0);
-          const float4 fN = *reinterpret_cast<const float4*>(fac + (I * 4 + 3) * kD + c0);
-          const float vT[4] = {fT.x, fT.y, fT.z, fT.w}, vK[4] = {fK.x, fK.y, fK.z, fK.w};
+          const int c0 = 32 * blk + 8 * g4 + 4 * hh;
+          const float4 t4 = *reinterpret_cast<const float4*>(tot + c0);
+          const float4 fK = *reinterpret_cast<const float4*>(fac + (I * 3 + 0) * kD + c0);
+          const float4 fQ = *reinterpret_cast<const float4*>(fac + (I * 3 + 1) * kD + c0);
+          const float4 fN = *reinterpret_cast<const float4*>(fac + (I * 3 + 2) * kD + c0);
+          const float tv[4] = {t4.x, t4.y, t4.z, t4.w}, vK[4] = {fK.x, fK.y, fK.z, fK.w};
           const float vQ[4] = {fQ.x, fQ.y, fQ.z, fQ.w}, vN[4] = {fN.x, fN.y, fN.z, fN.w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int e = 4 * hh + i;
-            kb[e] = kr[b2][e] * vT[i] * vK[i];     // -K e^{L}
-            qb[e] = qf[b2][e] * vT[i] * vQ[i];     // scale Q e^{L}
-            kt[e] = kc[b2][e] * vN[i];             // K e^{Ln - L}
+            const float kv = (e & 1) ? bf16hi(kw[b2][e >> 1]) : bf16lo(kw[b2][e >> 1]);
+            const float qv = (e & 1) ? bf16hi(qw[b2][e >> 1]) : bf16lo(qw[b2][e >> 1]);
+            const float d = (L[b2][e] - tv[i]) * kLog2e;      // >= 0
+            const float rowf = fast_exp2(d), colf = fast_exp2(-d);
+            kr[e] = kv * rowf;
+            qr[e] = qv * rowf;
+            kc[e] = kv * colf;
+            kb[e] = kr[e] * vK[i];     // -K e^{L}
+            qb[e] = qr[e] * vQ[i];     // scale Q e^{L}
+            kt[e] = kc[e] * vN[i];     // K e^{Ln - L}
           }
         }
+        fKr[b2] = to_frag(kr);
+        fQr[b2] = to_frag(qr);
+        fKc[b2] = to_frag(kc);
         *reinterpret_cast<bf16x8_t*>(smem + fl::KBN + frag_at(I, blk, 4, lane)) = to_frag(kb);
         *reinterpret_cast<bf16x8_t*>(smem + fl::QB + frag_at(I, blk, 4, lane)) = to_frag(qb);
-        // Kt^T: row = channel, contraction over tokens; token 16 I + l16 sits in
-        // s-block I/2 at lane group l16/4, element (l16 % 4) + 4 (I % 2)
+        // Kt^T: rows in state row order, contraction over tokens; channel 32 b + 8 g + e
+        // is state row 32 b + 16 (e/4) + 4 g + e%4; token 16 I + l16 sits in s-block
+        // I/2 at lane group l16/4, element (l16 % 4) + 4 (I % 2)
         {
           const int sblk = I >> 1, eo = (l16 & 3) + 4 * (I & 1), gq = l16 >> 2;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const int ch = perm_ch(blk, g4, e);
-            const int off = frag_at(ch >> 4, sblk, 2, (ch & 15) + 16 * gq) + eo * 2;
+            const int r = 32 * blk + 16 * (e >> 2) + 4 * g4 + (e & 3);
+            const int off = frag_at(r >> 4, sblk, 2, (r & 15) + 16 * gq) + eo * 2;
             *reinterpret_cast<__bf16*>(smem + fl::KTT + off) = static_cast<__bf16>(kt[e]);
           }
         }
@@ -396,11 +406,11 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
               const float4 f4 = *reinterpret_cast<const float4*>(
-                  foff + off_id(a, I) * kD + 32 * blk + 16 * hh + 4 * g4);
-              x[4 * hh] = kc[b2][4 * hh] * f4.x;
-              x[4 * hh + 1] = kc[b2][4 * hh + 1] * f4.y;
-              x[4 * hh + 2] = kc[b2][4 * hh + 2] * f4.z;
-              x[4 * hh + 3] = kc[b2][4 * hh + 3] * f4.w;
+                  foff + off_id(a, I) * kD + 32 * blk + 8 * g4 + 4 * hh);
+              x[4 * hh] = kc[4 * hh] * f4.x;
+              x[4 * hh + 1] = kc[4 * hh + 1] * f4.y;
+              x[4 * hh + 2] = kc[4 * hh + 2] * f4.z;
+              x[4 * hh + 3] = kc[4 * hh + 3] * f4.w;
             }
             *reinterpret_cast<bf16x8_t*>(smem + fl::OFF + off_id(a, I) * 4096 + frag_at(0, blk, 4, lane)) =
                 to_frag(x);
@@ -408,7 +418,7 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
         }
       }
     }
-    __syncthreads();                                                          // B3
+    lds_barrier();                                                          // B3
 
     // ============================================ P: decayed sub-tile products
     // transposed: C[s, t] = sum_c colside[s, c] rowside[t, c]; lane (t, g) holds
@@ -438,7 +448,7 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
             *reinterpret_cast<f32x4_t*>(smem + fl::PART + (pair_id(I, J) * 2 + 1) * 1024 + lane * 16) = pm[J];
           }
       }
-      __syncthreads();                                                        // B4
+      lds_barrier();                                                        // B4
       if (hf == 0) {
         const int t = 16 * I + l16;
 #pragma unroll
@@ -446,179 +456,113 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
           if (J <= I) {
             const f32x4_t oa = *reinterpret_cast<const f32x4_t*>(smem + fl::PART + (pair_id(I, J) * 2 + 0) * 1024 + lane * 16);
             const f32x4_t om = *reinterpret_cast<const f32x4_t*>(smem + fl::PART + (pair_id(I, J) * 2 + 1) * 1024 + lane * 16);
-            float av[4], mv[4];
+            f32x4_t av;
+            float mv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int s = 16 * J + 4 * g4 + i;
               av[i] = s < t ? beta_t * (pa[J][i] + oa[i]) : 0.f;
               mv[i] = s <= t ? p.scale * (pm[J][i] + om[i]) : 0.f;
             }
-            *reinterpret_cast<float4*>(smem + fl::AT + at_off(t, 16 * J + 4 * g4)) =
-                float4{av[0], av[1], av[2], av[3]};
             // M[t][s]: fragment (t-tile I, s-block J/2), elements 4 (J%2) .. +3
             *reinterpret_cast<uint2*>(smem + fl::MF + frag_at(I, J >> 1, 2, l16 + 16 * g4) + 8 * (J & 1)) =
                 uint2{pack_bf16x2(mv[0], mv[1]), pack_bf16x2(mv[2], mv[3])};
+            if (J < I) {
+              // -A_IJ as a 16x16x16 A operand: lane (t, g) holds columns 4 g .. +3
+              *reinterpret_cast<uint2*>(smem + fl::AOF + off_id(I, J) * 512 + lane * 8) =
+                  uint2{pack_bf16x2(-av[0], -av[1]), pack_bf16x2(-av[2], -av[3])};
+            } else {
+              // T_II = (I + A_II)^{-1}, computed as T^T = (I + B)^{-1} with B = A_II^T,
+              // which this lane holds in accumulator layout (rows 4 g + i, column l16);
+              // fp32 16x16x4 matrix-core products, whose A operand is read in row layout
+              // (lane: row l16, columns 4 g .. +3) and B operand in accumulator layout,
+              // so a result feeds the next B side directly and its A side after a
+              // transpose through this wavefront's 16 x 17 scratch.
+              float* sc = reinterpret_cast<float*>(smem + fl::XS) + I * 16 * 17;
+              auto mm = [&](const float (&xr)[4], const float (&yc)[4]) {
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int st = 0; st < 4; ++st) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xr[st], yc[st], acc, 0, 0, 0);
+                return acc;
+              };
+              auto to_row = [&](const f32x4_t& cc, float (&r)[4]) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sc[(4 * g4 + i) * 17 + l16] = cc[i];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) r[i] = sc[l16 * 17 + 4 * g4 + i];
+              };
+              const float b_c[4] = {av[0], av[1], av[2], av[3]};
+              float b_r[4];
+              to_row(av, b_r);
+              const f32x4_t p1 = mm(b_r, b_c);                         // B^2
+              const float p1_c[4] = {p1[0], p1[1], p1[2], p1[3]};
+              float p1_r[4];
+              to_row(p1, p1_r);
+              const f32x4_t p2 = mm(p1_r, p1_c);                       // B^4
+              const f32x4_t b3 = mm(b_r, p1_c);                        // B^3
+              const float p2_c[4] = {p2[0], p2[1], p2[2], p2[3]};
+              float p2_r[4];
+              to_row(p2, p2_r);
+              const f32x4_t p3 = mm(p2_r, p2_c);                       // B^8
+              const float p3_c[4] = {p3[0], p3[1], p3[2], p3[3]};
+              f32x4_t t1;                                              // I - B + B^2 - B^3
+#pragma unroll
+              for (int i = 0; i < 4; ++i) t1[i] = (4 * g4 + i == l16 ? 1.f : 0.f) - b_c[i] + p1[i] - b3[i];
+              float t1_r[4];
+              to_row(t1, t1_r);
+              f32x4_t t2 = mm(t1_r, p2_c);                             // T1 (I + B^4)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) t2[i] += t1[i];
+              float t2_r[4];
+              to_row(t2, t2_r);
+              f32x4_t t3 = mm(t2_r, p3_c);                             // T2 (I + B^8)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) t3[i] += t2[i];
+              // lane (l16, g) holds T^T[4 g + i][l16] = T[l16][4 g + i]: the A operand
+              *reinterpret_cast<uint2*>(smem + fl::TDF + I * 512 + lane * 8) =
+                  uint2{pack_bf16x2(t3[0], t3[1]), pack_bf16x2(t3[2], t3[3])};
+            }
           }
       }
     }
-    __syncthreads();                                                          // B5
-
-    // ============================================ T = (I + A)^{-1}
-    auto at_el = [&](int row, int col) -> float& {
-      return *reinterpret_cast<float*>(smem + fl::AT + at_off(row, col));
-    };
-    auto at_row4 = [&](int row, int col0) -> float4 {
-      return *reinterpret_cast<const float4*>(smem + fl::AT + at_off(row, col0));
-    };
-    if (wave < 4) {
-      // diagonal blocks: A_ww strictly lower, so (I + A)^{-1} = (I - A)(I + A^2)(I + A^4)(I + A^8)
-      // on fp32 16x16x4 matrix cores.  A product's A operand is read in row layout (lane:
-      // row l16, columns 4 g4 .. +3), its B operand in accumulator layout (lane: rows
-      // 4 g4 .. +3 of column l16): a result feeds the next B side directly and its A
-      // side after a transpose through this wavefront's 16 x 17 scratch.
-      const int base = 16 * wave;
-      float* sc = reinterpret_cast<float*>(smem + fl::XS) + wave * 16 * 17;
-      auto mm = [&](const float (&xr)[4], const float (&yc)[4]) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int st = 0; st < 4; ++st) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xr[st], yc[st], acc, 0, 0, 0);
-        return acc;
-      };
-      auto to_row = [&](const f32x4_t& cc, float (&r)[4]) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc[(4 * g4 + i) * 17 + l16] = cc[i];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) r[i] = sc[l16 * 17 + 4 * g4 + i];
-      };
-      const float4 ar4 = at_row4(base + l16, base + 4 * g4);
-      const float a_r[4] = {ar4.x, ar4.y, ar4.z, ar4.w};
-      float a_c[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a_c[i] = at_el(base + 4 * g4 + i, base + l16);
-      const f32x4_t p1 = mm(a_r, a_c);                           // A^2
-      const float p1_c[4] = {p1[0], p1[1], p1[2], p1[3]};
-      float p1_r[4];
-      to_row(p1, p1_r);
-      const f32x4_t p2 = mm(p1_r, p1_c);                         // A^4
-      const f32x4_t a3 = mm(a_r, p1_c);                          // A^3
-      const float p2_c[4] = {p2[0], p2[1], p2[2], p2[3]};
-      float p2_r[4];
-      to_row(p2, p2_r);
-      const f32x4_t p3 = mm(p2_r, p2_c);                         // A^8
-      const float p3_c[4] = {p3[0], p3[1], p3[2], p3[3]};
-      f32x4_t t1;                                                // I - A + A^2 - A^3
-#pragma unroll
-      for (int i = 0; i < 4; ++i) t1[i] = (4 * g4 + i == l16 ? 1.f : 0.f) - a_c[i] + p1[i] - a3[i];
-      float t1_r[4];
-      to_row(t1, t1_r);
-      f32x4_t t2 = mm(t1_r, p2_c);                               // T1 (I + A^4)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) t2[i] += t1[i];
-      float t2_r[4];
-      to_row(t2, t2_r);
-      f32x4_t t3 = mm(t2_r, p3_c);                               // T2 (I + A^8)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) at_el(base + 4 * g4 + i, base + l16) = t3[i] + t2[i];
-    }
-    __syncthreads();                                                          // B6
-    // I + A in 32 x 32 halves [[L1, 0], [B, L2]] has inverse [[L1^-1, 0], [-L2^-1 B L1^-1, L2^-1]]
-    if (wave < 2) {   // T_10 = -T_11 A_10 T_00 and T_32 = -T_33 A_32 T_22
-      const int bi = wave ? 3 : 1, bj = bi - 1;
-      f32x4_t y = {0.f, 0.f, 0.f, 0.f}, tt = y;
-      const float4 aIJ = at_row4(16 * bi + l16, 16 * bj + 4 * g4);
-      const float4 aII = at_row4(16 * bi + l16, 16 * bi + 4 * g4);
-      const float aij[4] = {aIJ.x, aIJ.y, aIJ.z, aIJ.w}, aii[4] = {aII.x, aII.y, aII.z, aII.w};
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-        y = __builtin_amdgcn_mfma_f32_16x16x4f32(aij[st], at_el(16 * bj + 4 * g4 + st, 16 * bj + l16), y, 0, 0, 0);
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-        tt = __builtin_amdgcn_mfma_f32_16x16x4f32(aii[st], y[st], tt, 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) at_el(16 * bi + 4 * g4 + i, 16 * bj + l16) = -tt[i];
-    }
-    __syncthreads();                                                          // B7
-    float* xs = reinterpret_cast<float*>(smem + fl::XS);
-    const int qi = 2 + ((wave & 3) >> 1), qj = wave & 1;   // lower-left 16x16 block (waves 0-3)
-    if (wave < 4) {   // X_{qi,qj} = sum_{m=qj}^{1} A_{qi,m} T_{m,qj}
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        if (m >= qj) {
-          const float4 a4 = at_row4(16 * qi + l16, 16 * m + 4 * g4);
-          const float a[4] = {a4.x, a4.y, a4.z, a4.w};
-#pragma unroll
-          for (int st = 0; st < 4; ++st)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], at_el(16 * m + 4 * g4 + st, 16 * qj + l16), acc, 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xs[(wave * 16 + 4 * g4 + i) * 17 + l16] = acc[i];
-    }
-    __syncthreads();                                                          // B8
-    if (wave < 4) {   // T_{qi,qj} = -sum_{m=2}^{qi} T_{qi,m} X_{m,qj}
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int m = 2; m < 4; ++m) {
-        if (m <= qi) {
-          const int xw = (m - 2) * 2 + qj;
-          const float4 a4 = at_row4(16 * qi + l16, 16 * m + 4 * g4);
-          const float a[4] = {a4.x, a4.y, a4.z, a4.w};
-#pragma unroll
-          for (int st = 0; st < 4; ++st)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], xs[(xw * 16 + 4 * g4 + st) * 17 + l16], acc, 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) at_el(16 * qi + 4 * g4 + i, 16 * qj + l16) = -acc[i];
-    }
-    __syncthreads();                                                          // B9
-    {   // Tb = T Diag(beta) as fragments: thread -> (t-tile, s-block, lane)
-      const int ttile = tid >> 7, sblk = (tid >> 6) & 1;
-      const int row = 16 * ttile + l16;
-      const float* bet = reinterpret_cast<const float*>(smem + fl::BETA);
-      float x[8];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int s0 = 32 * sblk + 16 * hh + 4 * g4;
-        const float4 tv = at_row4(row, s0);
-        const float4 bv = *reinterpret_cast<const float4*>(bet + s0);
-        x[4 * hh] = tv.x * bv.x;
-        x[4 * hh + 1] = tv.y * bv.y;
-        x[4 * hh + 2] = tv.z * bv.z;
-        x[4 * hh + 3] = tv.w * bv.w;
-      }
-      *reinterpret_cast<bf16x8_t*>(smem + fl::TBF + frag_at(ttile, sblk, 2, lane)) = to_frag(x);
-    }
-    __syncthreads();                                                          // B10
+    // this wavefront's v rows are in LDS (loads whose destination is LDS count in vmcnt)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();                                                          // B5
 
     // ============================================ state step
-    ChunkIn nxt;
-    if (c + 1 < nchunks) load_chunk(c + 1, nxt);
-
     bf16x8_t Sb[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) Sb[b] = acc_frag(S[2 * b], S[2 * b + 1]);
-    // X = V - Kb S (the stored -Kb makes it an accumulation onto V)
-    f32x4_t X[4];
+    // Y = Diag(beta) (V - Kb S) (the stored -Kb makes it an accumulation onto V)
+    f32x4_t Y[4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) X[tt][i] = __uint_as_float(vin[tt][i] << 16);
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * tt + 4 * g4 + i;
+        const uint16_t vb = *reinterpret_cast<const uint16_t*>(
+            smem + fl::VST + (row >> 2) * fl::VRB + (row & 3) * 256 + (16 * jt + l16) * 2);
+        Y[tt][i] = __uint_as_float(static_cast<uint32_t>(vb) << 16);
+      }
 #pragma unroll
-      for (int b = 0; b < 4; ++b) X[tt] = mma(lds_frag(smem, fl::KBN + frag_at(tt, b, 4, lane)), Sb[b], X[tt]);
+      for (int b = 0; b < 4; ++b) Y[tt] = mma(lds_frag(smem, fl::KBN + frag_at(tt, b, 4, lane)), Sb[b], Y[tt]);
+      const float4 b4 = *reinterpret_cast<const float4*>(betas + 16 * tt + 4 * g4);
+      Y[tt][0] *= b4.x;
+      Y[tt][1] *= b4.y;
+      Y[tt][2] *= b4.z;
+      Y[tt][3] *= b4.w;
     }
-    bf16x8_t Xb[2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) Xb[b] = acc_frag(X[2 * b], X[2 * b + 1]);
-    // Delta = Tb X (Tb lower triangular: t-tiles 0, 1 need s-block 0 only)
+    // Delta_i = T_ii (Y_i - sum_{m<i} A_im Delta_m)
     f32x4_t Dl[4];
+    bf16x4_t Dq[4];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      Dl[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 4; ++i) {
+      f32x4_t w = Y[i];
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-        if (b <= (tt >> 1)) Dl[tt] = mma(lds_frag(smem, fl::TBF + frag_at(tt, b, 2, lane)), Xb[b], Dl[tt]);
+      for (int m = 0; m < 4; ++m)
+        if (m < i) w = mma16(lds_frag4(smem, fl::AOF + off_id(i, m) * 512 + lane * 8), Dq[m], w);
+      Dl[i] = mma16(lds_frag4(smem, fl::TDF + i * 512 + lane * 8), acc_frag4(w), f32x4_t{0.f, 0.f, 0.f, 0.f});
+      Dq[i] = acc_frag4(Dl[i]);
     }
     bf16x8_t Db[2];
 #pragma unroll
@@ -650,7 +594,6 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
         S[ct] = acc;
       }
     }
-    if (c + 1 < nchunks) cur = nxt;
   }
 
   if (p.sT != nullptr) {
@@ -658,7 +601,7 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[(16 * ct + 4 * g4 + i) * kD + 16 * jt + l16] = S[ct][i];
+      for (int i = 0; i < 4; ++i) dst[sigma(16 * ct + 4 * g4 + i) * kD + 16 * jt + l16] = S[ct][i];
   }
 }
 
