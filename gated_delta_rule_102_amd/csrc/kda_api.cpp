@@ -1,4 +1,4 @@
-// C ABI of libkda.so: argument checks, then one kernel launch on the caller's
+// C ABI of libkda.so: argument checks, then the kernel launches on the caller's
 // stream.  The contract of every entry point is documented in include/kda.h.
 
 #include "kda.h"
@@ -6,9 +6,9 @@
 #include <hip/hip_runtime_api.h>
 
 #include <atomic>
-#include <initializer_list>
 #include <cstdint>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 #include <vector>
 
@@ -20,6 +20,9 @@ constexpr int kMaxDevices = 64;
 // 0 = not checked yet, 1 = gfx950, -1 = another architecture.
 std::atomic<int> g_arch_ok[kMaxDevices];
 
+// The current device is gfx950.  Runs right before a call's first launch; it also
+// clears an error an earlier HIP call left pending on this thread, so that a launch
+// check reports this call's own launches only.
 int check_device() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return KDA_ERR_HIP;
@@ -31,7 +34,9 @@ int check_device() {
     state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
     g_arch_ok[dev].store(state, std::memory_order_relaxed);
   }
-  return state == 1 ? KDA_OK : KDA_ERR_NO_DEVICE;
+  if (state != 1) return KDA_ERR_NO_DEVICE;
+  (void)hipGetLastError();
+  return KDA_OK;
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -60,17 +65,118 @@ int check_ptrs(std::initializer_list<PtrReq> ptrs) {
   return KDA_OK;
 }
 
-// Prefill pointer rules: q, k, g are read two elements at a time (4 bytes),
-// beta one element at a time, v and out 16 bytes at a time, states as fp32.
-int check_prefill_ptrs(const void* q, const void* k, const void* v, const void* g,
-                       const void* beta, const void* s0, const void* out, const void* sT,
-                       int dtype) {
-  const uintptr_t elt = dtype == KDA_F32 ? 4 : 2;
-  return check_ptrs({{q, 4, true}, {k, 4, true}, {g, 4, true}, {beta, elt, true},
-                     {v, 16, true}, {out, 16, true}, {s0, 4, false}, {sT, 4, false}});
+// Sizes of a fixed-length (B sequences of T tokens) or packed (N sequences, total_T
+// tokens) call.
+int check_sizes(bool packed, int N, int T, int total_T, int H) {
+  if (N <= 0) return KDA_ERR_SHAPE;
+  if (static_cast<int64_t>(N) * H > (1 << 24)) return KDA_ERR_SHAPE;
+  if (packed) {
+    if (total_T <= 0 || total_T > INT32_MAX / 2) return KDA_ERR_SHAPE;
+    if ((static_cast<int64_t>(total_T) / 64 + N + 1) * H > INT32_MAX) return KDA_ERR_SHAPE;
+  } else {
+    if (T <= 0 || static_cast<int64_t>(N) * T > INT32_MAX / 2) return KDA_ERR_SHAPE;
+    if (static_cast<int64_t>(N) * ((T + 63) / 64) * H > INT32_MAX) return KDA_ERR_SHAPE;
+  }
+  return KDA_OK;
 }
 
-// One workspace pool per device, created on first use and kept for the process.
+// Everything a prefill call is checked for, except the workspace and the device.
+int check_prefill(const kda_prefill_desc& d) {
+  int rc = check_common(d.dk, d.dv, d.H, d.dtype);
+  if (rc != KDA_OK) return rc;
+  if (d.dtype == KDA_F32 && d.dk != 64) return KDA_ERR_HEAD_DIM;
+  const bool packed = d.cu_seqlens != nullptr;
+  rc = check_sizes(packed, d.N, d.T, d.total_T, d.H);
+  if (rc != KDA_OK) return rc;
+  if (d.snapshots != nullptr || d.snapshot_tokens != 0) {
+    if (d.snapshot_tokens <= 0 || d.snapshot_tokens % 64 != 0) return KDA_ERR_SHAPE;
+    if (d.snapshots == nullptr) return KDA_ERR_NULL;
+  }
+  // q, k, g are read two elements at a time (4 bytes), beta one element at a time,
+  // v and out 16 bytes at a time, states and snapshots as fp32
+  const uintptr_t elt = d.dtype == KDA_F32 ? 4 : 2;
+  return check_ptrs({{d.q, 4, true}, {d.k, 4, true}, {d.g, 4, true}, {d.beta, elt, true},
+                     {d.v, 16, true}, {d.out, 16, true}, {d.initial_state, 4, false},
+                     {d.final_state, 4, false}, {d.snapshots, 4, false},
+                     {d.cu_seqlens, 4, false}});
+}
+
+kda::PrefillArgs prefill_args(const kda_prefill_desc& d, hipStream_t stream) {
+  const bool packed = d.cu_seqlens != nullptr;
+  kda::PrefillArgs a{d.q, d.k, d.v, d.g, d.beta, d.initial_state, d.out, d.final_state,
+                     d.cu_seqlens, d.N, packed ? 0 : d.T, packed ? d.total_T : d.N * d.T, d.H,
+                     d.dk, d.scale, d.dtype == KDA_F32, stream};
+  a.prologue = d.prologue != 0;
+  if (d.snapshots != nullptr) {
+    a.snapshots = d.snapshots;
+    a.snap_chunks = d.snapshot_tokens / 64;
+    a.nsnap = packed ? 0 : (d.T + d.snapshot_tokens - 1) / d.snapshot_tokens;
+  }
+  return a;
+}
+
+// A checked prefill: with `caller_ws` the call runs on the caller's workspace (which
+// must be large enough) and allocates nothing; without, it takes a kept block.
+int run_prefill(const kda_prefill_desc& d, bool caller_ws, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+  int rc = check_prefill(d);
+  if (rc != KDA_OK) return rc;
+  kda::PrefillArgs a = prefill_args(d, stream);
+  if (caller_ws) {
+    const size_t need = kda::prefill_workspace_bytes(a);
+    if (need > 0 && (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < need))
+      return KDA_ERR_WORKSPACE;
+    if (need > 0) {
+      a.workspace = workspace;
+      a.workspace_bytes = workspace_bytes;
+    }
+  }
+  rc = check_device();
+  if (rc != KDA_OK) return rc;
+  return kda::launch_prefill(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_prefill_desc fixed_desc(const void* q, const void* k, const void* v, const void* g,
+                            const void* beta, const float* s0, void* out, float* sT, int B,
+                            int T, int H, int dk, int dv, float scale, int dtype) {
+  kda_prefill_desc d;
+  std::memset(&d, 0, sizeof d);
+  d.q = q; d.k = k; d.v = v; d.g = g; d.beta = beta;
+  d.initial_state = s0; d.out = out; d.final_state = sT;
+  d.N = B; d.T = T; d.H = H; d.dk = dk; d.dv = dv; d.scale = scale; d.dtype = dtype;
+  return d;
+}
+
+kda_prefill_desc packed_desc(const void* q, const void* k, const void* v, const void* g,
+                             const void* beta, const float* s0, void* out, float* sT,
+                             const int32_t* cu, int N, int total_T, int H, int dk, int dv,
+                             float scale, int dtype) {
+  kda_prefill_desc d = fixed_desc(q, k, v, g, beta, s0, out, sT, N, 0, H, dk, dv, scale, dtype);
+  d.cu_seqlens = cu;
+  d.total_T = total_T;
+  return d;
+}
+
+// The code a packed call without offsets returns: size and head errors first, as a
+// call with offsets would report them, else KDA_ERR_NULL.
+int packed_without_offsets(int N, int total_T, int H, int dk, int dv, int dtype) {
+  int rc = check_common(dk, dv, H, dtype);
+  if (rc == KDA_OK && dtype == KDA_F32 && dk != 64) rc = KDA_ERR_HEAD_DIM;
+  if (rc == KDA_OK) rc = check_sizes(true, N, 0, total_T, H);
+  return rc != KDA_OK ? rc : KDA_ERR_NULL;
+}
+
+// Snapshot tokens out of range: the checks that come before, else KDA_ERR_SHAPE.
+int bad_snapshot_tokens(const kda_prefill_desc& d) {
+  int rc = check_common(d.dk, d.dv, d.H, d.dtype);
+  if (rc == KDA_OK && d.dtype == KDA_F32 && d.dk != 64) rc = KDA_ERR_HEAD_DIM;
+  if (rc == KDA_OK) rc = check_sizes(d.cu_seqlens != nullptr, d.N, d.T, d.total_T, d.H);
+  return rc != KDA_OK ? rc : KDA_ERR_SHAPE;
+}
+
+// ---------------------------------------------------------------- kept workspace blocks
+
+// One memory pool per device, created on first use and kept for the process.
 std::mutex g_pool_mu;
 hipMemPool_t g_pool[kMaxDevices];
 
@@ -92,7 +198,7 @@ hipError_t device_pool(hipMemPool_t* out) {
     uint64_t keep = UINT64_MAX;
     err = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
     if (err != hipSuccess) {
-      hipMemPoolDestroy(pool);
+      (void)hipMemPoolDestroy(pool);
       return err;
     }
     g_pool[dev] = pool;
@@ -101,13 +207,16 @@ hipError_t device_pool(hipMemPool_t* out) {
   return hipSuccess;
 }
 
-// Workspace blocks kept for reuse.  A call takes a free block of its device that
-// is large enough, after making its stream wait for the event recorded when the
-// block was last released (on whatever stream that was), or else allocates a new
-// block from the pool; releasing records that event and keeps the block.  No call
-// therefore frees memory (hipFreeAsync blocks the host on ROCm 7 until the stream
-// has drained), except free blocks too small for a request, which are returned to
-// the pool when a larger one is allocated.  Blocks live until the process ends.
+// Workspace blocks for the entry points that take no workspace.  A call takes a free
+// block of its device that is large enough, after making its stream wait for the
+// event recorded when the block was last released (on whatever stream that was), or
+// else allocates a new block from the device's pool; releasing records that event
+// and keeps the block.  Free blocks of a device are kept while they total at most
+// kKeepBytes; beyond that the largest free blocks are returned to the pool
+// (hipFreeAsync, ordered after their last use).  Blocks too small for a request are
+// returned the same way when a larger one is allocated.
+constexpr size_t kKeepBytes = size_t{4} << 30;
+
 struct WsBlock {
   void* p;
   size_t bytes;
@@ -119,6 +228,17 @@ struct WsBlock {
 };
 std::mutex g_ws_mu;
 std::vector<WsBlock> g_ws;
+
+// Return free block i to the pool on `stream`, after its last use.  Caller holds g_ws_mu.
+hipError_t drop_block(int i, hipStream_t stream) {
+  WsBlock& b = g_ws[i];
+  hipError_t err = hipSuccess;
+  if (b.used) err = hipStreamWaitEvent(stream, b.done, 0);
+  if (err == hipSuccess) err = hipFreeAsync(b.p, stream);
+  (void)hipEventDestroy(b.done);
+  g_ws.erase(g_ws.begin() + i);
+  return err;
+}
 
 }  // namespace
 
@@ -150,17 +270,13 @@ hipError_t ws_alloc(void** p, size_t bytes, hipStream_t stream) {
   }
   // free blocks of this device are all too small: give them back, then allocate
   for (int i = static_cast<int>(g_ws.size()) - 1; i >= 0; --i) {
-    WsBlock& b = g_ws[i];
-    if (b.busy || b.dev != dev) continue;
-    if (b.used && (err = hipStreamWaitEvent(stream, b.done, 0)) != hipSuccess) return err;
-    if ((err = hipFreeAsync(b.p, stream)) != hipSuccess) return err;
-    hipEventDestroy(b.done);
-    g_ws.erase(g_ws.begin() + i);
+    if (g_ws[i].busy || g_ws[i].dev != dev) continue;
+    if ((err = drop_block(i, stream)) != hipSuccess) return err;
   }
   WsBlock nb{nullptr, bytes, dev, true, false, nullptr, stream};
   if ((err = hipEventCreateWithFlags(&nb.done, hipEventDisableTiming)) != hipSuccess) return err;
   if ((err = hipMallocFromPoolAsync(&nb.p, bytes, pool, stream)) != hipSuccess) {
-    hipEventDestroy(nb.done);
+    (void)hipEventDestroy(nb.done);
     return err;
   }
   g_ws.push_back(nb);
@@ -170,13 +286,35 @@ hipError_t ws_alloc(void** p, size_t bytes, hipStream_t stream) {
 
 hipError_t ws_free(void* p, hipStream_t stream) {
   std::lock_guard<std::mutex> lock(g_ws_mu);
-  for (WsBlock& b : g_ws) {
+  for (int i = 0; i < static_cast<int>(g_ws.size()); ++i) {
+    WsBlock& b = g_ws[i];
     if (b.p != p || !b.busy) continue;
     const hipError_t err = hipEventRecord(b.done, stream);
-    if (err != hipSuccess) return err;   // the block stays taken: never reused unordered
+    if (err != hipSuccess) {
+      // the block's last use cannot be ordered by its event: return it to the pool
+      // on the stream instead, after the work enqueued there
+      (void)hipFreeAsync(b.p, stream);
+      (void)hipEventDestroy(b.done);
+      g_ws.erase(g_ws.begin() + i);
+      return err;
+    }
     b.busy = false;
     b.used = true;
     b.last = stream;
+    const int dev = b.dev;
+    // keep at most kKeepBytes of free blocks on this device: give back the largest
+    for (;;) {
+      size_t kept = 0;
+      int largest = -1;
+      for (int j = 0; j < static_cast<int>(g_ws.size()); ++j) {
+        if (g_ws[j].busy || g_ws[j].dev != dev) continue;
+        kept += g_ws[j].bytes;
+        if (largest < 0 || g_ws[j].bytes > g_ws[largest].bytes) largest = j;
+      }
+      if (kept <= kKeepBytes || largest < 0) break;
+      const hipError_t derr = drop_block(largest, stream);
+      if (derr != hipSuccess) return derr;
+    }
     return hipSuccess;
   }
   return hipErrorInvalidValue;
@@ -203,35 +341,7 @@ const char* kda_status_string(int status) {
   }
 }
 
-int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
-                  const void* beta, const float* initial_state, void* out,
-                  float* final_state, int B, int T, int H, int dk, int dv, float scale,
-                  int dtype, hipStream_t stream) {
-  int rc = check_common(dk, dv, H, dtype);
-  if (rc != KDA_OK) return rc;
-  if (dtype == KDA_F32 && dk != 64) return KDA_ERR_HEAD_DIM;
-  if (B <= 0 || T <= 0) return KDA_ERR_SHAPE;
-  if (static_cast<int64_t>(B) * T > INT32_MAX / 2) return KDA_ERR_SHAPE;
-  if (static_cast<int64_t>(B) * H > (1 << 24)) return KDA_ERR_SHAPE;
-  rc = check_prefill_ptrs(q, k, v, g, beta, initial_state, out, final_state, dtype);
-  if (rc != KDA_OK) return rc;
-  rc = check_device();
-  if (rc != KDA_OK) return rc;
-  kda::PrefillArgs a{q, k, v, g, beta, initial_state, out, final_state, nullptr,
-                     B, T, B * T, H, dk, scale, dtype == KDA_F32, stream};
-  return kda::launch_prefill(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
-}
-
-size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int dtype) {
-  if (check_common(dk, dv, H, dtype) != KDA_OK) return 0;
-  if (dtype == KDA_F32 && dk != 64) return 0;
-  if (B <= 0 || T <= 0) return 0;
-  if (static_cast<int64_t>(B) * T > INT32_MAX / 2) return 0;
-  if (static_cast<int64_t>(B) * H > (1 << 24)) return 0;
-  kda::PrefillArgs a{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
-                     B, T, B * T, H, dk, 1.f, dtype == KDA_F32, nullptr};
-  return kda::prefill_workspace_bytes(a);
-}
+// ---------------------------------------------------------------- prefill
 
 const char* kda_chunk_fwd_schedule(int N, int T, int total_T, int H, int dk, int dv, int dtype,
                                    int varlen) {
@@ -244,48 +354,55 @@ const char* kda_chunk_fwd_schedule(int N, int T, int total_T, int H, int dk, int
   return kda::prefill_schedule(a);
 }
 
+int kda_prefill_workspace_size(const kda_prefill_desc* desc, size_t* bytes) {
+  if (desc == nullptr || bytes == nullptr) return KDA_ERR_NULL;
+  const int rc = check_prefill(*desc);
+  if (rc != KDA_OK) return rc;
+  *bytes = kda::prefill_workspace_bytes(prefill_args(*desc, nullptr));
+  return KDA_OK;
+}
+
+int kda_prefill(const kda_prefill_desc* desc, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+  if (desc == nullptr) return KDA_ERR_NULL;
+  return run_prefill(*desc, true, workspace, workspace_bytes, stream);
+}
+
+int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
+                  const void* beta, const float* initial_state, void* out,
+                  float* final_state, int B, int T, int H, int dk, int dv, float scale,
+                  int dtype, hipStream_t stream) {
+  return run_prefill(fixed_desc(q, k, v, g, beta, initial_state, out, final_state, B, T, H, dk,
+                                dv, scale, dtype),
+                     false, nullptr, 0, stream);
+}
+
+size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int dk, int dv, int dtype) {
+  // sizes only: stand-in pointers satisfy the pointer checks and are never used
+  const void* p = reinterpret_cast<const void*>(uintptr_t{256});
+  kda_prefill_desc d = fixed_desc(p, p, p, p, p, nullptr, const_cast<void*>(p), nullptr, B, T,
+                                  H, dk, dv, 1.f, dtype);
+  size_t bytes = 0;
+  return kda_prefill_workspace_size(&d, &bytes) == KDA_OK ? bytes : 0;
+}
+
 int kda_chunk_fwd_ws(const void* q, const void* k, const void* v, const void* g,
                      const void* beta, const float* initial_state, void* out,
                      float* final_state, int B, int T, int H, int dk, int dv, float scale,
                      int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  int rc = check_common(dk, dv, H, dtype);
-  if (rc != KDA_OK) return rc;
-  if (dtype == KDA_F32 && dk != 64) return KDA_ERR_HEAD_DIM;
-  if (B <= 0 || T <= 0) return KDA_ERR_SHAPE;
-  if (static_cast<int64_t>(B) * T > INT32_MAX / 2) return KDA_ERR_SHAPE;
-  if (static_cast<int64_t>(B) * H > (1 << 24)) return KDA_ERR_SHAPE;
-  rc = check_prefill_ptrs(q, k, v, g, beta, initial_state, out, final_state, dtype);
-  if (rc != KDA_OK) return rc;
-  if (workspace == nullptr || !aligned(workspace, 256) ||
-      workspace_bytes < kda_chunk_fwd_workspace_size(B, T, H, dk, dv, dtype))
-    return KDA_ERR_WORKSPACE;
-  rc = check_device();
-  if (rc != KDA_OK) return rc;
-  kda::PrefillArgs a{q, k, v, g, beta, initial_state, out, final_state, nullptr,
-                     B, T, B * T, H, dk, scale, dtype == KDA_F32, stream};
-  a.workspace = workspace;
-  a.workspace_bytes = workspace_bytes;
-  return kda::launch_prefill(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  return run_prefill(fixed_desc(q, k, v, g, beta, initial_state, out, final_state, B, T, H, dk,
+                                dv, scale, dtype),
+                     true, workspace, workspace_bytes, stream);
 }
 
 int kda_chunk_fwd_prologue(const void* q_raw, const void* k_raw, const void* v,
                            const void* g_raw, const void* beta_raw, const float* initial_state,
                            void* out, float* final_state, int B, int T, int H, int dk, int dv,
                            float scale, int dtype, hipStream_t stream) {
-  int rc = check_common(dk, dv, H, dtype);
-  if (rc != KDA_OK) return rc;
-  if (dtype == KDA_F32 && dk != 64) return KDA_ERR_HEAD_DIM;
-  if (B <= 0 || T <= 0) return KDA_ERR_SHAPE;
-  if (static_cast<int64_t>(B) * T > INT32_MAX / 2) return KDA_ERR_SHAPE;
-  if (static_cast<int64_t>(B) * H > (1 << 24)) return KDA_ERR_SHAPE;
-  rc = check_prefill_ptrs(q_raw, k_raw, v, g_raw, beta_raw, initial_state, out, final_state, dtype);
-  if (rc != KDA_OK) return rc;
-  rc = check_device();
-  if (rc != KDA_OK) return rc;
-  kda::PrefillArgs a{q_raw, k_raw, v, g_raw, beta_raw, initial_state, out, final_state, nullptr,
-                     B, T, B * T, H, dk, scale, dtype == KDA_F32, stream};
-  a.prologue = true;
-  return kda::launch_prefill(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  kda_prefill_desc d = fixed_desc(q_raw, k_raw, v, g_raw, beta_raw, initial_state, out,
+                                  final_state, B, T, H, dk, dv, scale, dtype);
+  d.prologue = 1;
+  return run_prefill(d, false, nullptr, 0, stream);
 }
 
 int kda_chunk_fwd_snapshots(const void* q, const void* k, const void* v, const void* g,
@@ -293,25 +410,12 @@ int kda_chunk_fwd_snapshots(const void* q, const void* k, const void* v, const v
                             float* final_state, float* snapshots, int snapshot_tokens, int B,
                             int T, int H, int dk, int dv, float scale, int dtype,
                             hipStream_t stream) {
-  int rc = check_common(dk, dv, H, dtype);
-  if (rc != KDA_OK) return rc;
-  if (dtype == KDA_F32 && dk != 64) return KDA_ERR_HEAD_DIM;
-  if (B <= 0 || T <= 0) return KDA_ERR_SHAPE;
-  if (static_cast<int64_t>(B) * T > INT32_MAX / 2) return KDA_ERR_SHAPE;
-  if (static_cast<int64_t>(B) * H > (1 << 24)) return KDA_ERR_SHAPE;
-  if (snapshot_tokens <= 0 || snapshot_tokens % 64 != 0) return KDA_ERR_SHAPE;
-  if (snapshots == nullptr) return KDA_ERR_NULL;
-  rc = check_prefill_ptrs(q, k, v, g, beta, initial_state, out, final_state, dtype);
-  if (rc == KDA_OK && !aligned(snapshots, 4)) rc = KDA_ERR_ALIGN;
-  if (rc != KDA_OK) return rc;
-  rc = check_device();
-  if (rc != KDA_OK) return rc;
-  kda::PrefillArgs a{q, k, v, g, beta, initial_state, out, final_state, nullptr,
-                     B, T, B * T, H, dk, scale, dtype == KDA_F32, stream};
-  a.snapshots = snapshots;
-  a.snap_chunks = snapshot_tokens / 64;
-  a.nsnap = (T + snapshot_tokens - 1) / snapshot_tokens;
-  return kda::launch_prefill(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  kda_prefill_desc d = fixed_desc(q, k, v, g, beta, initial_state, out, final_state, B, T, H,
+                                  dk, dv, scale, dtype);
+  if (snapshot_tokens <= 0 || snapshot_tokens % 64 != 0) return bad_snapshot_tokens(d);
+  d.snapshots = snapshots;
+  d.snapshot_tokens = snapshot_tokens;
+  return run_prefill(d, false, nullptr, 0, stream);
 }
 
 int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void* g,
@@ -319,20 +423,29 @@ int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void
                          float* final_state, const int32_t* cu_seqlens, int N,
                          int total_T, int H, int dk, int dv, float scale, int dtype,
                          hipStream_t stream) {
-  int rc = check_common(dk, dv, H, dtype);
-  if (rc != KDA_OK) return rc;
-  if (dtype == KDA_F32 && dk != 64) return KDA_ERR_HEAD_DIM;
-  if (N <= 0 || total_T <= 0 || total_T > INT32_MAX / 2) return KDA_ERR_SHAPE;
-  if (static_cast<int64_t>(N) * H > (1 << 24)) return KDA_ERR_SHAPE;
-  if (cu_seqlens == nullptr) return KDA_ERR_NULL;
-  rc = check_prefill_ptrs(q, k, v, g, beta, initial_state, out, final_state, dtype);
-  if (rc == KDA_OK && !aligned(cu_seqlens, 4)) rc = KDA_ERR_ALIGN;
-  if (rc != KDA_OK) return rc;
-  rc = check_device();
-  if (rc != KDA_OK) return rc;
-  kda::PrefillArgs a{q, k, v, g, beta, initial_state, out, final_state, cu_seqlens,
-                     N, 0, total_T, H, dk, scale, dtype == KDA_F32, stream};
-  return kda::launch_prefill(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  kda_prefill_desc d = packed_desc(q, k, v, g, beta, initial_state, out, final_state, cu_seqlens,
+                                   N, total_T, H, dk, dv, scale, dtype);
+  if (cu_seqlens == nullptr) return packed_without_offsets(N, total_T, H, dk, dv, dtype);
+  return run_prefill(d, false, nullptr, 0, stream);
+}
+
+size_t kda_chunk_fwd_varlen_workspace_size(int N, int total_T, int H, int dk, int dv, int dtype) {
+  const void* p = reinterpret_cast<const void*>(uintptr_t{256});
+  kda_prefill_desc d = packed_desc(p, p, p, p, p, nullptr, const_cast<void*>(p), nullptr,
+                                   static_cast<const int32_t*>(p), N, total_T, H, dk, dv, 1.f, dtype);
+  size_t bytes = 0;
+  return kda_prefill_workspace_size(&d, &bytes) == KDA_OK ? bytes : 0;
+}
+
+int kda_chunk_fwd_varlen_ws(const void* q, const void* k, const void* v, const void* g,
+                            const void* beta, const float* initial_state, void* out,
+                            float* final_state, const int32_t* cu_seqlens, int N, int total_T,
+                            int H, int dk, int dv, float scale, int dtype, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  kda_prefill_desc d = packed_desc(q, k, v, g, beta, initial_state, out, final_state, cu_seqlens,
+                                   N, total_T, H, dk, dv, scale, dtype);
+  if (cu_seqlens == nullptr) return packed_without_offsets(N, total_T, H, dk, dv, dtype);
+  return run_prefill(d, true, workspace, workspace_bytes, stream);
 }
 
 int kda_chunk_fwd_varlen_prologue(const void* q_raw, const void* k_raw, const void* v,
@@ -340,21 +453,11 @@ int kda_chunk_fwd_varlen_prologue(const void* q_raw, const void* k_raw, const vo
                                   const float* initial_state, void* out, float* final_state,
                                   const int32_t* cu_seqlens, int N, int total_T, int H, int dk,
                                   int dv, float scale, int dtype, hipStream_t stream) {
-  int rc = check_common(dk, dv, H, dtype);
-  if (rc != KDA_OK) return rc;
-  if (dtype == KDA_F32 && dk != 64) return KDA_ERR_HEAD_DIM;
-  if (N <= 0 || total_T <= 0 || total_T > INT32_MAX / 2) return KDA_ERR_SHAPE;
-  if (static_cast<int64_t>(N) * H > (1 << 24)) return KDA_ERR_SHAPE;
-  if (cu_seqlens == nullptr) return KDA_ERR_NULL;
-  rc = check_prefill_ptrs(q_raw, k_raw, v, g_raw, beta_raw, initial_state, out, final_state, dtype);
-  if (rc == KDA_OK && !aligned(cu_seqlens, 4)) rc = KDA_ERR_ALIGN;
-  if (rc != KDA_OK) return rc;
-  rc = check_device();
-  if (rc != KDA_OK) return rc;
-  kda::PrefillArgs a{q_raw, k_raw, v, g_raw, beta_raw, initial_state, out, final_state, cu_seqlens,
-                     N, 0, total_T, H, dk, scale, dtype == KDA_F32, stream};
-  a.prologue = true;
-  return kda::launch_prefill(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  kda_prefill_desc d = packed_desc(q_raw, k_raw, v, g_raw, beta_raw, initial_state, out,
+                                   final_state, cu_seqlens, N, total_T, H, dk, dv, scale, dtype);
+  if (cu_seqlens == nullptr) return packed_without_offsets(N, total_T, H, dk, dv, dtype);
+  d.prologue = 1;
+  return run_prefill(d, false, nullptr, 0, stream);
 }
 
 int kda_chunk_fwd_varlen_snapshots(const void* q, const void* k, const void* v, const void* g,
@@ -362,23 +465,64 @@ int kda_chunk_fwd_varlen_snapshots(const void* q, const void* k, const void* v, 
                                    float* final_state, float* snapshots, int snapshot_tokens,
                                    const int32_t* cu_seqlens, int N, int total_T, int H, int dk,
                                    int dv, float scale, int dtype, hipStream_t stream) {
+  kda_prefill_desc d = packed_desc(q, k, v, g, beta, initial_state, out, final_state, cu_seqlens,
+                                   N, total_T, H, dk, dv, scale, dtype);
+  if (snapshot_tokens <= 0 || snapshot_tokens % 64 != 0) return bad_snapshot_tokens(d);
+  if (cu_seqlens == nullptr) return packed_without_offsets(N, total_T, H, dk, dv, dtype);
+  d.snapshots = snapshots;
+  d.snapshot_tokens = snapshot_tokens;
+  return run_prefill(d, false, nullptr, 0, stream);
+}
+
+// ---------------------------------------------------------------- backward
+
+namespace {
+
+int check_backward(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                   const float* s0, const void* dout, const float* dsT, void* dq, void* dk_,
+                   void* dv_, void* dg, void* dbeta, float* ds0, const int32_t* cu, bool packed,
+                   int N, int T, int total_T, int H, int dk, int dv, int dtype) {
   int rc = check_common(dk, dv, H, dtype);
   if (rc != KDA_OK) return rc;
-  if (dtype == KDA_F32 && dk != 64) return KDA_ERR_HEAD_DIM;
-  if (N <= 0 || total_T <= 0 || total_T > INT32_MAX / 2) return KDA_ERR_SHAPE;
-  if (static_cast<int64_t>(N) * H > (1 << 24)) return KDA_ERR_SHAPE;
-  if (snapshot_tokens <= 0 || snapshot_tokens % 64 != 0) return KDA_ERR_SHAPE;
-  if (cu_seqlens == nullptr || snapshots == nullptr) return KDA_ERR_NULL;
-  rc = check_prefill_ptrs(q, k, v, g, beta, initial_state, out, final_state, dtype);
-  if (rc == KDA_OK && (!aligned(cu_seqlens, 4) || !aligned(snapshots, 4))) rc = KDA_ERR_ALIGN;
+  if (packed && cu == nullptr) return KDA_ERR_NULL;
+  rc = check_sizes(packed, N, T, total_T, H);
   if (rc != KDA_OK) return rc;
-  rc = check_device();
+  const uintptr_t elt = dtype == KDA_F32 ? 4 : 2;
+  return check_ptrs({{q, 16, true}, {k, 16, true}, {v, 16, true}, {g, 16, true},
+                     {beta, elt, true}, {dout, 16, true}, {dq, elt, true}, {dk_, elt, true},
+                     {dv_, elt, true}, {dg, elt, true}, {dbeta, elt, true}, {s0, 4, false},
+                     {dsT, 4, false}, {ds0, 4, false}, {cu, 4, false}});
+}
+
+int run_backward(kda::BackwardArgs a, bool caller_ws, void* workspace, size_t workspace_bytes) {
+  if (caller_ws) {
+    const size_t need = kda::backward_workspace_bytes(a);
+    if (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < need)
+      return KDA_ERR_WORKSPACE;
+    a.workspace = workspace;
+    a.workspace_bytes = workspace_bytes;
+  }
+  const int rc = check_device();
   if (rc != KDA_OK) return rc;
-  kda::PrefillArgs a{q, k, v, g, beta, initial_state, out, final_state, cu_seqlens,
-                     N, 0, total_T, H, dk, scale, dtype == KDA_F32, stream};
-  a.snapshots = snapshots;
-  a.snap_chunks = snapshot_tokens / 64;
-  return kda::launch_prefill(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  return kda::launch_backward(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+int kda_chunk_bwd_ws(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                     const float* initial_state, const void* grad_out,
+                     const float* grad_final_state, void* grad_q, void* grad_k, void* grad_v,
+                     void* grad_g, void* grad_beta, float* grad_initial_state, int B, int T,
+                     int H, int dk, int dv, float scale, int dtype, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  const int rc = check_backward(q, k, v, g, beta, initial_state, grad_out, grad_final_state,
+                                grad_q, grad_k, grad_v, grad_g, grad_beta, grad_initial_state,
+                                nullptr, false, B, T, 0, H, dk, dv, dtype);
+  if (rc != KDA_OK) return rc;
+  kda::BackwardArgs a{q, k, v, g, beta, initial_state, grad_out, grad_final_state,
+                      grad_q, grad_k, grad_v, grad_g, grad_beta, grad_initial_state,
+                      B, T, H, dk, scale, dtype == KDA_F32, stream};
+  return run_backward(a, workspace != nullptr || workspace_bytes != 0, workspace, workspace_bytes);
 }
 
 int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
@@ -386,24 +530,36 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, co
                   const float* grad_final_state, void* grad_q, void* grad_k, void* grad_v,
                   void* grad_g, void* grad_beta, float* grad_initial_state, int B, int T, int H,
                   int dk, int dv, float scale, int dtype, hipStream_t stream) {
-  int rc = check_common(dk, dv, H, dtype);
-  if (rc != KDA_OK) return rc;
-  if (B <= 0 || T <= 0) return KDA_ERR_SHAPE;
-  if (static_cast<int64_t>(B) * T > INT32_MAX / 2) return KDA_ERR_SHAPE;
-  if (static_cast<int64_t>(B) * H > (1 << 24)) return KDA_ERR_SHAPE;
-  const uintptr_t elt = dtype == KDA_F32 ? 4 : 2;
-  rc = check_ptrs({{q, 16, true}, {k, 16, true}, {v, 16, true}, {g, 16, true},
-                   {beta, elt, true}, {grad_out, 16, true}, {grad_q, elt, true},
-                   {grad_k, elt, true}, {grad_v, elt, true}, {grad_g, elt, true},
-                   {grad_beta, elt, true}, {initial_state, 4, false},
-                   {grad_final_state, 4, false}, {grad_initial_state, 4, false}});
-  if (rc != KDA_OK) return rc;
-  rc = check_device();
+  return kda_chunk_bwd_ws(q, k, v, g, beta, initial_state, grad_out, grad_final_state, grad_q,
+                          grad_k, grad_v, grad_g, grad_beta, grad_initial_state, B, T, H, dk, dv,
+                          scale, dtype, nullptr, 0, stream);
+}
+
+size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int dk, int dv, int dtype) {
+  if (check_common(dk, dv, H, dtype) != KDA_OK || check_sizes(false, B, T, 0, H) != KDA_OK) return 0;
+  kda::BackwardArgs a{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                      nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                      B, T, H, dk, 1.f, dtype == KDA_F32, nullptr};
+  return kda::backward_workspace_bytes(a);
+}
+
+int kda_chunk_bwd_varlen_ws(const void* q, const void* k, const void* v, const void* g,
+                            const void* beta, const float* initial_state, const void* grad_out,
+                            const float* grad_final_state, void* grad_q, void* grad_k,
+                            void* grad_v, void* grad_g, void* grad_beta,
+                            float* grad_initial_state, const int32_t* cu_seqlens, int N,
+                            int total_T, int H, int dk, int dv, float scale, int dtype,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int rc = check_backward(q, k, v, g, beta, initial_state, grad_out, grad_final_state,
+                                grad_q, grad_k, grad_v, grad_g, grad_beta, grad_initial_state,
+                                cu_seqlens, true, N, 0, total_T, H, dk, dv, dtype);
   if (rc != KDA_OK) return rc;
   kda::BackwardArgs a{q, k, v, g, beta, initial_state, grad_out, grad_final_state,
                       grad_q, grad_k, grad_v, grad_g, grad_beta, grad_initial_state,
-                      B, T, H, dk, scale, dtype == KDA_F32, stream};
-  return kda::launch_backward(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+                      N, 0, H, dk, scale, dtype == KDA_F32, stream};
+  a.cu_seqlens = cu_seqlens;
+  a.total_T = total_T;
+  return run_backward(a, workspace != nullptr || workspace_bytes != 0, workspace, workspace_bytes);
 }
 
 int kda_chunk_bwd_varlen(const void* q, const void* k, const void* v, const void* g,
@@ -412,46 +568,61 @@ int kda_chunk_bwd_varlen(const void* q, const void* k, const void* v, const void
                          void* grad_g, void* grad_beta, float* grad_initial_state,
                          const int32_t* cu_seqlens, int N, int total_T, int H, int dk, int dv,
                          float scale, int dtype, hipStream_t stream) {
+  return kda_chunk_bwd_varlen_ws(q, k, v, g, beta, initial_state, grad_out, grad_final_state,
+                                 grad_q, grad_k, grad_v, grad_g, grad_beta, grad_initial_state,
+                                 cu_seqlens, N, total_T, H, dk, dv, scale, dtype, nullptr, 0,
+                                 stream);
+}
+
+size_t kda_chunk_bwd_varlen_workspace_size(int N, int total_T, int H, int dk, int dv, int dtype) {
+  if (check_common(dk, dv, H, dtype) != KDA_OK || check_sizes(true, N, 0, total_T, H) != KDA_OK)
+    return 0;
+  kda::BackwardArgs a{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                      nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                      N, 0, H, dk, 1.f, dtype == KDA_F32, nullptr};
+  a.cu_seqlens = reinterpret_cast<const int32_t*>(uintptr_t{256});
+  a.total_T = total_T;
+  return kda::backward_workspace_bytes(a);
+}
+
+// ---------------------------------------------------------------- context parallelism
+
+int kda_chunk_transition_ws(const void* q, const void* k, const void* g, const void* beta,
+                            float* transition, int B, int T, int H, int dk, int dv, int dtype,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int rc = check_common(dk, dv, H, dtype);
   if (rc != KDA_OK) return rc;
-  if (N <= 0 || total_T <= 0 || total_T > INT32_MAX / 2) return KDA_ERR_SHAPE;
-  if (static_cast<int64_t>(N) * H > (1 << 24)) return KDA_ERR_SHAPE;
-  if ((static_cast<int64_t>(total_T) / 64 + N + 1) * H > INT32_MAX) return KDA_ERR_SHAPE;
-  if (cu_seqlens == nullptr) return KDA_ERR_NULL;
-  const uintptr_t elt = dtype == KDA_F32 ? 4 : 2;
-  rc = check_ptrs({{q, 16, true}, {k, 16, true}, {v, 16, true}, {g, 16, true},
-                   {beta, elt, true}, {grad_out, 16, true}, {grad_q, elt, true},
-                   {grad_k, elt, true}, {grad_v, elt, true}, {grad_g, elt, true},
-                   {grad_beta, elt, true}, {initial_state, 4, false},
-                   {grad_final_state, 4, false}, {grad_initial_state, 4, false},
-                   {cu_seqlens, 4, true}});
+  rc = check_sizes(false, B, T, 0, H);
   if (rc != KDA_OK) return rc;
+  const uintptr_t elt = dtype == KDA_F32 ? 4 : 2;
+  rc = check_ptrs({{q, 16, false}, {k, 16, true}, {g, 16, true}, {beta, elt, true},
+                   {transition, 4, true}});
+  if (rc != KDA_OK) return rc;
+  kda::TransitionArgs a{q, k, g, beta, transition, B, T, H, dk, dtype == KDA_F32, stream};
+  if (workspace != nullptr || workspace_bytes != 0) {
+    if (workspace == nullptr || !aligned(workspace, 256) ||
+        workspace_bytes < kda::transition_workspace_bytes(a))
+      return KDA_ERR_WORKSPACE;
+    a.workspace = workspace;
+    a.workspace_bytes = workspace_bytes;
+  }
   rc = check_device();
   if (rc != KDA_OK) return rc;
-  kda::BackwardArgs a{q, k, v, g, beta, initial_state, grad_out, grad_final_state,
-                      grad_q, grad_k, grad_v, grad_g, grad_beta, grad_initial_state,
-                      N, 0, H, dk, scale, dtype == KDA_F32, stream};
-  a.cu_seqlens = cu_seqlens;
-  a.total_T = total_T;
-  return kda::launch_backward(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  return kda::launch_transition(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 int kda_chunk_transition(const void* q, const void* k, const void* g, const void* beta,
                          float* transition, int B, int T, int H, int dk, int dv, int dtype,
                          hipStream_t stream) {
-  int rc = check_common(dk, dv, H, dtype);
-  if (rc != KDA_OK) return rc;
-  if (B <= 0 || T <= 0) return KDA_ERR_SHAPE;
-  if (static_cast<int64_t>(B) * T > INT32_MAX / 2) return KDA_ERR_SHAPE;
-  if (static_cast<int64_t>(B) * H > (1 << 24)) return KDA_ERR_SHAPE;
-  const uintptr_t elt = dtype == KDA_F32 ? 4 : 2;
-  rc = check_ptrs({{q, 16, false}, {k, 16, true}, {g, 16, true}, {beta, elt, true},
-                   {transition, 4, true}});
-  if (rc != KDA_OK) return rc;
-  rc = check_device();
-  if (rc != KDA_OK) return rc;
-  kda::TransitionArgs a{q, k, g, beta, transition, B, T, H, dk, dtype == KDA_F32, stream};
-  return kda::launch_transition(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  return kda_chunk_transition_ws(q, k, g, beta, transition, B, T, H, dk, dv, dtype, nullptr, 0,
+                                 stream);
+}
+
+size_t kda_chunk_transition_workspace_size(int B, int T, int H, int dk, int dv, int dtype) {
+  if (check_common(dk, dv, H, dtype) != KDA_OK || check_sizes(false, B, T, 0, H) != KDA_OK) return 0;
+  kda::TransitionArgs a{nullptr, nullptr, nullptr, nullptr, nullptr, B, T, H, dk,
+                        dtype == KDA_F32, nullptr};
+  return kda::transition_workspace_bytes(a);
 }
 
 int kda_state_compose(const float* transitions, const float* partial_states,
@@ -471,9 +642,13 @@ int kda_state_compose(const float* transitions, const float* partial_states,
   return kda::launch_compose(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
-int kda_decode_step(const void* q, const void* k, const void* v, const void* g,
-                    const void* beta, float* state, void* out, int B, int H, int dk, int dv,
-                    float scale, int dtype, hipStream_t stream) {
+// ---------------------------------------------------------------- decode
+
+namespace {
+
+int run_decode(const void* q, const void* k, const void* v, const void* g, const void* beta,
+               float* state, void* out, int B, int H, int dk, int dv, float scale, int dtype,
+               bool prologue, hipStream_t stream) {
   int rc = check_common(dk, dv, H, dtype);
   if (rc != KDA_OK) return rc;
   if (B <= 0) return KDA_ERR_SHAPE;
@@ -485,27 +660,24 @@ int kda_decode_step(const void* q, const void* k, const void* v, const void* g,
   rc = check_device();
   if (rc != KDA_OK) return rc;
   kda::DecodeArgs a{q, k, v, g, beta, state, out, B, H, dk, scale, dtype == KDA_F32, stream};
+  a.prologue = prologue;
   return kda::launch_decode(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+int kda_decode_step(const void* q, const void* k, const void* v, const void* g,
+                    const void* beta, float* state, void* out, int B, int H, int dk, int dv,
+                    float scale, int dtype, hipStream_t stream) {
+  return run_decode(q, k, v, g, beta, state, out, B, H, dk, dv, scale, dtype, false, stream);
 }
 
 int kda_decode_step_prologue(const void* q_raw, const void* k_raw, const void* v,
                              const void* g_raw, const void* beta_raw, float* state, void* out,
                              int B, int H, int dk, int dv, float scale, int dtype,
                              hipStream_t stream) {
-  int rc = check_common(dk, dv, H, dtype);
-  if (rc != KDA_OK) return rc;
-  if (B <= 0) return KDA_ERR_SHAPE;
-  if (static_cast<int64_t>(B) * H > INT32_MAX / 2) return KDA_ERR_SHAPE;
-  const uintptr_t elt = dtype == KDA_F32 ? 4 : 2;
-  rc = check_ptrs({{q_raw, elt, true}, {k_raw, elt, true}, {v, elt, true}, {g_raw, elt, true},
-                   {beta_raw, elt, true}, {state, 16, true}, {out, elt, true}});
-  if (rc != KDA_OK) return rc;
-  rc = check_device();
-  if (rc != KDA_OK) return rc;
-  kda::DecodeArgs a{q_raw, k_raw, v, g_raw, beta_raw, state, out, B, H, dk, scale,
-                    dtype == KDA_F32, stream};
-  a.prologue = true;
-  return kda::launch_decode(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  return run_decode(q_raw, k_raw, v, g_raw, beta_raw, state, out, B, H, dk, dv, scale, dtype, true,
+                    stream);
 }
 
 }  // extern "C"

@@ -1075,26 +1075,37 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_chunk_kernel(
   }
 }
 
+// Chunk items of a backward call: fixed length, every chunk of every stream; packed,
+// the slot numbering of the forward (some items unused).
+inline int64_t backward_items(const BackwardArgs& a) {
+  const int nc = a.cu_seqlens == nullptr ? (a.T + CR - 1) / CR : 0;
+  return a.cu_seqlens == nullptr ? static_cast<int64_t>(a.B) * a.H * nc
+                                 : (static_cast<int64_t>(a.total_T + CR - 1) / CR + a.B) * a.H;
+}
+
+// Floats of workspace per chunk item: the fp32 operands, then the states, state
+// gradients, Delta and dU (fp32, or bf16 for bf16 inputs: half the floats), then for
+// bf16 inputs the bf16 scan operands.
+template <int D, typename TIn>
+constexpr int64_t backward_floats_per_item() {
+  using L = BwdLayout<D>;
+  constexpr bool BF = IsBf16<TIn>::value;
+  return L::WS + (BF ? 1 : 2) * (D * D + CR * D) + (BF ? L::WSB / 2 : 0);
+}
+
 template <int D, typename TIn>
 hipError_t launch_backward_t(const BackwardArgs& a) {
   using L = BwdLayout<D>;
   const int nc = a.cu_seqlens == nullptr ? (a.T + CR - 1) / CR : 0;
   const SeqMap sm{a.cu_seqlens, a.B, a.T, a.cu_seqlens == nullptr ? a.B * a.T : a.total_T, a.H, nc};
-  // fixed length: every chunk of every stream; packed: the slot numbering of the
-  // forward (some items unused)
-  const int64_t items = a.cu_seqlens == nullptr
-                            ? static_cast<int64_t>(a.B) * a.H * nc
-                            : (static_cast<int64_t>(a.total_T + CR - 1) / CR + a.B) * a.H;
+  const int64_t items = backward_items(a);
   constexpr bool BF = IsBf16<TIn>::value;
-  // per chunk, in floats: the fp32 operands, then the states, state gradients, Delta
-  // and dU (fp32, or bf16 for bf16 inputs: half the floats), then for bf16 inputs the
-  // bf16 scan operands
   const int64_t sdu = (BF ? 1 : 2) * (D * D + CR * D);
-  const int64_t per = L::WS + sdu + (BF ? L::WSB / 2 : 0);
-  float* buf = nullptr;
-  hipError_t err = ws_alloc(reinterpret_cast<void**>(&buf), items * per * sizeof(float), a.stream);
+  char* raw = nullptr;
+  hipError_t err = ws_acquire(a.workspace, a.workspace_bytes,
+                              items * backward_floats_per_item<D, TIn>() * sizeof(float), a.stream, &raw);
   if (err != hipSuccess) return err;
-  float* ws = buf;
+  float* ws = reinterpret_cast<float*>(raw);
   float* sreg = ws + items * L::WS;   // S, dS, Delta, dU in the element type chosen above
   __bf16* wsb = BF ? reinterpret_cast<__bf16*>(sreg + items * sdu) : nullptr;
   float* st = sreg;
@@ -1114,35 +1125,42 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
   const TIn* dout = static_cast<const TIn*>(a.d_out);
   const int BH = a.B * a.H;
   const int scan_blocks = scan_grid(BH, D / SL);
-  hipLaunchKernelGGL((chunk_ops_kernel<D, TIn, false, true>), dim3(items), dim3(kOpsThreads), 0, a.stream, q, k, g, beta,
-                     ws, wsb, sm, a.scale);
+  KDA_TRY_LAUNCH(err, (chunk_ops_kernel<D, TIn, false, true>), dim3(items), dim3(kOpsThreads), 0,
+                 a.stream, q, k, g, beta, ws, wsb, sm, a.scale);
   if constexpr (IsBf16<TIn>::value) {
-    hipLaunchKernelGGL((bwd_fwd_scan_bf16_kernel<D>), dim3(scan_blocks), dim3(kScanThreads), 0,
-                       a.stream, v, a.initial_state, ws, wsb, stb, dlb, sm, BH);
-    hipLaunchKernelGGL((bwd_scan_bf16_kernel<D>), dim3(scan_blocks), dim3(kScanThreads), 0,
-                       a.stream, dout, a.d_final_state, ws, wsb, dstb, dub,
-                       static_cast<TIn*>(a.dv), a.d_initial_state, sm, BH);
-    hipLaunchKernelGGL((bwd_grad_chunk_kernel<D, TIn>), dim3(items), dim3(kNnThreads), 0, a.stream, q,
-                       k, beta, v, dout, stb, dstb, dlb, dub, ws, static_cast<TIn*>(a.dq),
-                       static_cast<TIn*>(a.dk), static_cast<TIn*>(a.dg), static_cast<TIn*>(a.dbeta),
-                       sm, a.scale);
+    KDA_TRY_LAUNCH(err, (bwd_fwd_scan_bf16_kernel<D>), dim3(scan_blocks), dim3(kScanThreads), 0,
+                   a.stream, v, a.initial_state, ws, wsb, stb, dlb, sm, BH);
+    KDA_TRY_LAUNCH(err, (bwd_scan_bf16_kernel<D>), dim3(scan_blocks), dim3(kScanThreads), 0,
+                   a.stream, dout, a.d_final_state, ws, wsb, dstb, dub,
+                   static_cast<TIn*>(a.dv), a.d_initial_state, sm, BH);
+    KDA_TRY_LAUNCH(err, (bwd_grad_chunk_kernel<D, TIn>), dim3(items), dim3(kNnThreads), 0, a.stream,
+                   q, k, beta, v, dout, stb, dstb, dlb, dub, ws, static_cast<TIn*>(a.dq),
+                   static_cast<TIn*>(a.dk), static_cast<TIn*>(a.dg), static_cast<TIn*>(a.dbeta),
+                   sm, a.scale);
   } else {
-    hipLaunchKernelGGL((bwd_fwd_scan_kernel<D, TIn>), dim3(scan_blocks), dim3(kScanThreads), 0, a.stream, v,
-                       a.initial_state, ws, st, dl, sm, BH);
-    hipLaunchKernelGGL((bwd_scan_kernel<D, TIn>), dim3(scan_blocks), dim3(kScanThreads), 0, a.stream, dout,
-                       a.d_final_state, ws, dst, du, static_cast<TIn*>(a.dv), a.d_initial_state,
-                       sm, BH);
-    hipLaunchKernelGGL((bwd_grad_chunk_kernel<D, TIn>), dim3(items), dim3(kNnThreads), 0, a.stream, q,
-                       k, beta, v, dout, st, dst, dl, du, ws, static_cast<TIn*>(a.dq),
-                       static_cast<TIn*>(a.dk), static_cast<TIn*>(a.dg), static_cast<TIn*>(a.dbeta),
-                       sm, a.scale);
+    KDA_TRY_LAUNCH(err, (bwd_fwd_scan_kernel<D, TIn>), dim3(scan_blocks), dim3(kScanThreads), 0,
+                   a.stream, v, a.initial_state, ws, st, dl, sm, BH);
+    KDA_TRY_LAUNCH(err, (bwd_scan_kernel<D, TIn>), dim3(scan_blocks), dim3(kScanThreads), 0, a.stream,
+                   dout, a.d_final_state, ws, dst, du, static_cast<TIn*>(a.dv), a.d_initial_state,
+                   sm, BH);
+    KDA_TRY_LAUNCH(err, (bwd_grad_chunk_kernel<D, TIn>), dim3(items), dim3(kNnThreads), 0, a.stream,
+                   q, k, beta, v, dout, st, dst, dl, du, ws, static_cast<TIn*>(a.dq),
+                   static_cast<TIn*>(a.dk), static_cast<TIn*>(a.dg), static_cast<TIn*>(a.dbeta),
+                   sm, a.scale);
   }
-  err = hipGetLastError();
-  const hipError_t ferr = ws_free(buf, a.stream);
+  const hipError_t ferr = ws_release(a.workspace, raw, a.stream);
   return err != hipSuccess ? err : ferr;
 }
 
 }  // namespace
+
+size_t backward_workspace_bytes(const BackwardArgs& a) {
+  const int64_t items = backward_items(a);
+  int64_t per = 0;
+  if (a.d == 128) per = a.dtype_f32 ? backward_floats_per_item<128, float>() : backward_floats_per_item<128, bf16_t>();
+  else per = a.dtype_f32 ? backward_floats_per_item<64, float>() : backward_floats_per_item<64, bf16_t>();
+  return static_cast<size_t>(items * per) * sizeof(float);
+}
 
 hipError_t launch_backward(const BackwardArgs& a) {
   if (a.d == 128) {

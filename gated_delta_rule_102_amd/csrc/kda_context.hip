@@ -225,39 +225,54 @@ __global__ __launch_bounds__(256) void compose_kernel(const float* __restrict__ 
   }
 }
 
+// Floats of workspace per 64-token chunk per head of a transition call.
+template <int D, typename TIn>
+constexpr int64_t transition_floats_per_item() {
+  using L = BwdLayout<D>;
+  return L::WS + (IsBf16<TIn>::value ? L::WSB / 2 : 0);
+}
+
 template <int D, typename TIn>
 hipError_t launch_transition_t(const TransitionArgs& a) {
   using L = BwdLayout<D>;
   const int nc = (a.T + CR - 1) / CR;
   const int64_t items = static_cast<int64_t>(a.B) * a.H * nc;
   constexpr bool BF = IsBf16<TIn>::value;
-  float* ws = nullptr;
-  const int64_t per = L::WS + (BF ? L::WSB / 2 : 0);   // floats per chunk
-  hipError_t err = ws_alloc(reinterpret_cast<void**>(&ws), items * per * sizeof(float), a.stream);
+  char* raw = nullptr;
+  hipError_t err = ws_acquire(a.workspace, a.workspace_bytes,
+                              items * transition_floats_per_item<D, TIn>() * sizeof(float), a.stream, &raw);
   if (err != hipSuccess) return err;
+  float* ws = reinterpret_cast<float*>(raw);
   __bf16* wsb = BF ? reinterpret_cast<__bf16*>(ws + items * L::WS) : nullptr;
   const int BH = a.B * a.H;
   if constexpr (BF) {   // bf16 operands, the prefill's precision
-    hipLaunchKernelGGL((chunk_ops_kernel<D, TIn, false, false>), dim3(items), dim3(kOpsThreads), 0,
-                       a.stream, static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
-                       static_cast<const TIn*>(a.g), static_cast<const TIn*>(a.beta), ws, wsb,
-                       SeqMap{nullptr, a.B, a.T, a.B * a.T, a.H, nc}, 1.0f);
-    hipLaunchKernelGGL((transition_scan_bf16_kernel<D>), dim3(scan_grid(BH, D / SL)),
-                       dim3(kScanThreads), 0, a.stream, ws, wsb, a.transition, nc, BH);
+    KDA_TRY_LAUNCH(err, (chunk_ops_kernel<D, TIn, false, false>), dim3(items), dim3(kOpsThreads), 0,
+                   a.stream, static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
+                   static_cast<const TIn*>(a.g), static_cast<const TIn*>(a.beta), ws, wsb,
+                   SeqMap{nullptr, a.B, a.T, a.B * a.T, a.H, nc}, 1.0f);
+    KDA_TRY_LAUNCH(err, (transition_scan_bf16_kernel<D>), dim3(scan_grid(BH, D / SL)),
+                   dim3(kScanThreads), 0, a.stream, ws, wsb, a.transition, nc, BH);
   } else {
-    hipLaunchKernelGGL((chunk_ops_kernel<D, TIn, true, false>), dim3(items), dim3(kOpsThreads), 0,
-                       a.stream, static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
-                       static_cast<const TIn*>(a.g), static_cast<const TIn*>(a.beta), ws, nullptr,
-                       SeqMap{nullptr, a.B, a.T, a.B * a.T, a.H, nc}, 1.0f);
-    hipLaunchKernelGGL((transition_scan_kernel<D>), dim3(scan_grid(BH, D / SL)), dim3(256), 0,
-                       a.stream, ws, a.transition, nc, BH);
+    KDA_TRY_LAUNCH(err, (chunk_ops_kernel<D, TIn, true, false>), dim3(items), dim3(kOpsThreads), 0,
+                   a.stream, static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k),
+                   static_cast<const TIn*>(a.g), static_cast<const TIn*>(a.beta), ws, nullptr,
+                   SeqMap{nullptr, a.B, a.T, a.B * a.T, a.H, nc}, 1.0f);
+    KDA_TRY_LAUNCH(err, (transition_scan_kernel<D>), dim3(scan_grid(BH, D / SL)), dim3(256), 0,
+                   a.stream, ws, a.transition, nc, BH);
   }
-  err = hipGetLastError();
-  const hipError_t ferr = ws_free(ws, a.stream);
+  const hipError_t ferr = ws_release(a.workspace, raw, a.stream);
   return err != hipSuccess ? err : ferr;
 }
 
 }  // namespace
+
+size_t transition_workspace_bytes(const TransitionArgs& a) {
+  const int64_t items = static_cast<int64_t>(a.B) * a.H * ((a.T + CR - 1) / CR);
+  int64_t per = 0;
+  if (a.d == 128) per = a.dtype_f32 ? transition_floats_per_item<128, float>() : transition_floats_per_item<128, bf16_t>();
+  else per = a.dtype_f32 ? transition_floats_per_item<64, float>() : transition_floats_per_item<64, bf16_t>();
+  return static_cast<size_t>(items * per) * sizeof(float);
+}
 
 hipError_t launch_transition(const TransitionArgs& a) {
   if (a.d == 128) {

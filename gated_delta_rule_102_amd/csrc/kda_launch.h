@@ -53,6 +53,8 @@ struct BackwardArgs {
   hipStream_t stream;
   const int32_t* cu_seqlens = nullptr;   // packed sequences: B offsets + 1 (device); T unused
   int total_T = 0;                       // tokens in the packed buffers
+  void* workspace = nullptr;             // caller's workspace (null: the call takes a block)
+  size_t workspace_bytes = 0;
 };
 
 struct TransitionArgs {
@@ -61,6 +63,8 @@ struct TransitionArgs {
   int B, T, H, d;
   bool dtype_f32;
   hipStream_t stream;
+  void* workspace = nullptr;    // caller's workspace (null: the call takes a block)
+  size_t workspace_bytes = 0;
 };
 
 struct ComposeArgs {
@@ -76,6 +80,9 @@ hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_transition(const TransitionArgs& a);
 hipError_t launch_compose(const ComposeArgs& a);
 hipError_t launch_backward(const BackwardArgs& a);
+// Workspace bytes launch_backward / launch_transition need for these arguments.
+size_t backward_workspace_bytes(const BackwardArgs& a);
+size_t transition_workspace_bytes(const TransitionArgs& a);
 
 hipError_t launch_prefill(const PrefillArgs& a);
 // Fused prefill (one workgroup per (sequence, head), no workspace): bf16, d = 128,
@@ -87,11 +94,39 @@ const char* prefill_schedule(const PrefillArgs& a);
 // Workspace bytes launch_prefill needs for these arguments (0 if unsupported).
 size_t prefill_workspace_bytes(const PrefillArgs& a);
 
-// Stream-ordered workspace from the library's own memory pool on the current
-// device.  The pool keeps freed memory for reuse (its release threshold is the
-// maximum), so a free never waits for the stream to drain and the next call's
-// allocation of the same size is served from the pool.
+// Workspace blocks the library keeps for the calls that take no workspace (see
+// kda_api.cpp): ws_alloc takes a block of at least `bytes` for work enqueued on
+// `stream`, ws_free gives it back once that work has been enqueued.
 hipError_t ws_alloc(void** p, size_t bytes, hipStream_t stream);
 hipError_t ws_free(void* p, hipStream_t stream);
+
+// The caller's workspace when there is one (too small: invalid value), else a block
+// from ws_alloc; ws_release gives back what ws_acquire took.
+inline hipError_t ws_acquire(void* caller, size_t caller_bytes, size_t need, hipStream_t stream,
+                             char** p) {
+  if (need == 0) {
+    *p = nullptr;
+    return hipSuccess;
+  }
+  if (caller != nullptr) {
+    if (caller_bytes < need) return hipErrorInvalidValue;
+    *p = static_cast<char*>(caller);
+    return hipSuccess;
+  }
+  return ws_alloc(reinterpret_cast<void**>(p), need, stream);
+}
+inline hipError_t ws_release(void* caller, char* p, hipStream_t stream) {
+  return caller != nullptr || p == nullptr ? hipSuccess : ws_free(p, stream);
+}
+
+// Launch a kernel unless an earlier step of the call failed, and record the launch's
+// own error: a call stops at its first failed launch.
+#define KDA_TRY_LAUNCH(err, ...)          \
+  do {                                    \
+    if ((err) == hipSuccess) {            \
+      hipLaunchKernelGGL(__VA_ARGS__);    \
+      (err) = hipGetLastError();          \
+    }                                     \
+  } while (0)
 
 }  // namespace kda

@@ -1427,19 +1427,14 @@ size_t all_chunks_bytes(const PrefillArgs& a) {
   return static_cast<size_t>(slots) * a.H * SL::BYTES;
 }
 
-// The caller's workspace when it passed one (too small: invalid value), else a
-// stream-ordered allocation that ws_release returns.
+// The caller's workspace when it passed one (too small: invalid value), else a block
+// from the library's kept blocks.
 hipError_t ws_acquire(const PrefillArgs& a, size_t bytes, char** p) {
-  if (a.workspace != nullptr) {
-    if (a.workspace_bytes < bytes) return hipErrorInvalidValue;
-    *p = static_cast<char*>(a.workspace);
-    return hipSuccess;
-  }
-  return ws_alloc(reinterpret_cast<void**>(p), bytes, a.stream);
+  return kda::ws_acquire(a.workspace, a.workspace_bytes, bytes, a.stream, p);
 }
 
 hipError_t ws_release(const PrefillArgs& a, char* p) {
-  return a.workspace != nullptr ? hipSuccess : ws_free(p, a.stream);
+  return kda::ws_release(a.workspace, p, a.stream);
 }
 
 template <int D, int DVS, typename TIn>

@@ -20,11 +20,28 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 KDA_BF16, KDA_F32 = 0, 1
 _lib = None
 
-EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_schedule", "kda_chunk_bwd_varlen", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
-           "kda_chunk_fwd_ws", "kda_chunk_fwd_prologue", "kda_chunk_fwd_varlen_prologue",
-           "kda_chunk_fwd_varlen_snapshots", "kda_decode_step_prologue",
-           "kda_chunk_fwd_snapshots", "kda_chunk_fwd_varlen", "kda_decode_step", "kda_chunk_bwd",
-           "kda_chunk_transition", "kda_state_compose")
+EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_schedule",
+           "kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd_ws",
+           "kda_prefill_workspace_size", "kda_prefill",
+           "kda_chunk_fwd_prologue", "kda_chunk_fwd_snapshots",
+           "kda_chunk_fwd_varlen", "kda_chunk_fwd_varlen_workspace_size", "kda_chunk_fwd_varlen_ws",
+           "kda_chunk_fwd_varlen_prologue", "kda_chunk_fwd_varlen_snapshots",
+           "kda_chunk_bwd", "kda_chunk_bwd_workspace_size", "kda_chunk_bwd_ws",
+           "kda_chunk_bwd_varlen", "kda_chunk_bwd_varlen_workspace_size", "kda_chunk_bwd_varlen_ws",
+           "kda_chunk_transition", "kda_chunk_transition_workspace_size", "kda_chunk_transition_ws",
+           "kda_state_compose", "kda_decode_step", "kda_decode_step_prologue")
+
+
+class PrefillDesc(ctypes.Structure):
+    """ctypes mirror of ``kda_prefill_desc`` (include/kda.h)."""
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p),
+                ("initial_state", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("final_state", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
+                ("N", ctypes.c_int), ("T", ctypes.c_int), ("total_T", ctypes.c_int),
+                ("H", ctypes.c_int), ("dk", ctypes.c_int), ("dv", ctypes.c_int),
+                ("scale", ctypes.c_float), ("dtype", ctypes.c_int), ("prologue", ctypes.c_int),
+                ("snapshots", ctypes.c_void_p), ("snapshot_tokens", ctypes.c_int)]
 
 
 class KDAError(RuntimeError):
@@ -58,6 +75,29 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd_ws.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                      f32, i32, vp, ctypes.c_size_t, vp]
     lib.kda_chunk_fwd_ws.restype = i32
+    sz = ctypes.c_size_t
+    lib.kda_prefill_workspace_size.argtypes = [ctypes.POINTER(PrefillDesc), ctypes.POINTER(sz)]
+    lib.kda_prefill_workspace_size.restype = i32
+    lib.kda_prefill.argtypes = [ctypes.POINTER(PrefillDesc), vp, sz, vp]
+    lib.kda_prefill.restype = i32
+    lib.kda_chunk_fwd_varlen_workspace_size.argtypes = [i32] * 6
+    lib.kda_chunk_fwd_varlen_workspace_size.restype = sz
+    lib.kda_chunk_fwd_varlen_ws.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                            i32, i32, f32, i32, vp, sz, vp]
+    lib.kda_chunk_fwd_varlen_ws.restype = i32
+    lib.kda_chunk_bwd_workspace_size.argtypes = [i32] * 6
+    lib.kda_chunk_bwd_workspace_size.restype = sz
+    lib.kda_chunk_bwd_ws.argtypes = [vp] * 14 + [i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    lib.kda_chunk_bwd_ws.restype = i32
+    lib.kda_chunk_bwd_varlen_workspace_size.argtypes = [i32] * 6
+    lib.kda_chunk_bwd_varlen_workspace_size.restype = sz
+    lib.kda_chunk_bwd_varlen_ws.argtypes = [vp] * 15 + [i32, i32, i32, i32, i32, f32, i32, vp, sz,
+                                                        vp]
+    lib.kda_chunk_bwd_varlen_ws.restype = i32
+    lib.kda_chunk_transition_workspace_size.argtypes = [i32] * 6
+    lib.kda_chunk_transition_workspace_size.restype = sz
+    lib.kda_chunk_transition_ws.argtypes = [vp] * 5 + [i32] * 6 + [vp, sz, vp]
+    lib.kda_chunk_transition_ws.restype = i32
     lib.kda_chunk_fwd_prologue.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                            i32, f32, i32, vp]
     lib.kda_chunk_fwd_prologue.restype = i32
@@ -166,23 +206,102 @@ def kda_chunk_fwd_workspace_size(B, T, H, dk, dv, dtype=torch.bfloat16) -> int:
     return int(load_library().kda_chunk_fwd_workspace_size(B, T, H, dk, dv, code))
 
 
+def _ws_arg(workspace, device):
+    """(pointer, bytes) of a caller workspace tensor, 256-byte aligned inside it."""
+    if workspace.device != device or workspace.dtype != torch.uint8:
+        raise ValueError(f"workspace must be a uint8 tensor on {device}")
+    base = workspace.data_ptr()
+    off = (-base) % 256
+    return ctypes.c_void_p(base + off), max(workspace.numel() - off, 0)
+
+
+def _ws_tensor(nbytes, device):
+    """A uint8 device tensor with room for `nbytes` at a 256-byte aligned offset."""
+    return torch.empty(int(nbytes) + 256, dtype=torch.uint8, device=device)
+
+
 def chunk_fwd_workspace(q, v):
     """A uint8 device tensor large enough to serve as the workspace of prefill calls
-    shaped like (q, v); allocated once and passed as ``workspace=`` to kda_chunk_fwd."""
+    shaped like (q, v) (256 bytes of slack only when the call needs none); allocated
+    once and passed as ``workspace=`` to kda_chunk_fwd."""
     B, T, H, dk = q.shape
-    n = kda_chunk_fwd_workspace_size(B, T, H, dk, v.shape[-1], q.dtype)
-    if n == 0:
-        raise ValueError("prefill sizes not accepted by the library")
-    return torch.empty(n + 256, dtype=torch.uint8, device=q.device)
+    d = PrefillDesc(q=256, k=256, v=256, g=256, beta=256, out=256, N=B, T=T, H=H, dk=dk,
+                    dv=v.shape[-1], scale=1.0, dtype=_dtype_code(q))
+    return _ws_tensor(prefill_workspace_size(d), q.device)
 
 
-def kda_chunk_fwd_ws(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=True,
-                     out=None, final_state=None, workspace=None):
-    """kda_chunk_fwd on a caller-owned workspace (``chunk_fwd_workspace``)."""
+def varlen_workspace(q, v, cu_seqlens):
+    """Workspace tensor for kda_chunk_fwd_varlen calls shaped like (q, v, cu_seqlens)."""
+    H, dk = q.shape[-2], q.shape[-1]
+    n = load_library().kda_chunk_fwd_varlen_workspace_size(
+        cu_seqlens.numel() - 1, q.numel() // (H * dk), H, dk, v.shape[-1], _dtype_code(q))
+    return _ws_tensor(n, q.device)
+
+
+def prefill_workspace_size(desc):
+    """Bytes of workspace kda_prefill needs for a PrefillDesc (raises on bad arguments)."""
+    n = ctypes.c_size_t(0)
+    _raise("kda_prefill_workspace_size",
+           load_library().kda_prefill_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    return int(n.value)
+
+
+def kda_prefill(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None,
+                prologue=False, snapshot_tokens=0, output_final_state=True, out=None,
+                final_state=None, snapshots=None, workspace=None):
+    """Every prefill variant through the descriptor entry point kda_prefill, on a
+    caller workspace: fixed length ([B,T,H,.] tensors) or packed (``cu_seqlens``,
+    [1,total_T,H,.] or [total_T,H,.]), raw activations (``prologue``), snapshots every
+    ``snapshot_tokens`` tokens.  ``workspace`` None: a torch tensor of the size the
+    library asks for.  Returns ``(out, final_state, snapshots)``."""
+    lib = load_library()
+    packed = cu_seqlens is not None
+    H, dk = q.shape[-2], q.shape[-1]
+    dv = v.shape[-1]
+    dtype, device = q.dtype, q.device
+    _check(dict(q=q, k=k, v=v, g=g, beta=beta), dtype, device)
+    if packed:
+        H, dk, dv, total_T, N, out, final_state = _varlen_prep(
+            q, k, v, g, beta, cu_seqlens, initial_state, output_final_state, out, final_state)
+        T = 0
+        if snapshot_tokens:
+            rows = varlen_snapshot_rows(cu_seqlens, snapshot_tokens)
+            shape = (int(rows[-1]), H, dk, dv)
+    else:
+        N, T = q.shape[0], q.shape[1]
+        total_T = N * T
+        if k.shape != q.shape or g.shape != q.shape or v.shape[:3] != q.shape[:3] \
+                or beta.shape != q.shape[:3]:
+            raise ValueError("shape mismatch among q, k, v, g, beta")
+        _check_state("initial_state", initial_state, (N, H, dk, dv), device)
+        if out is None:
+            out = torch.empty((N, T, H, dv), dtype=dtype, device=device)
+        _check_out(out, (N, T, H, dv), dtype, device)
+        if final_state is None and output_final_state:
+            final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=device)
+        _check_state("final_state", final_state, (N, H, dk, dv), device)
+        if snapshot_tokens:
+            shape = (N, H, -(-T // snapshot_tokens), dk, dv)
+    if snapshot_tokens:
+        if snapshots is None:
+            snapshots = torch.empty(shape, dtype=torch.float32, device=device)
+        _check_state("snapshots", snapshots, shape, device)
+    scale = 1.0 / math.sqrt(dk) if scale is None else float(scale)
+    d = PrefillDesc(q=q.data_ptr(), k=k.data_ptr(), v=v.data_ptr(), g=g.data_ptr(),
+                    beta=beta.data_ptr(),
+                    initial_state=None if initial_state is None else initial_state.data_ptr(),
+                    out=out.data_ptr(),
+                    final_state=None if final_state is None else final_state.data_ptr(),
+                    cu_seqlens=cu_seqlens.contiguous().data_ptr() if packed else None,
+                    N=N, T=T, total_T=total_T, H=H, dk=dk, dv=dv, scale=scale,
+                    dtype=_dtype_code(q), prologue=1 if prologue else 0,
+                    snapshots=None if snapshots is None else snapshots.data_ptr(),
+                    snapshot_tokens=int(snapshot_tokens))
     if workspace is None:
-        raise ValueError("kda_chunk_fwd_ws needs a workspace tensor")
-    return kda_chunk_fwd(q, k, v, g, beta, scale, initial_state, output_final_state, out,
-                         final_state, workspace=workspace)
+        workspace = _ws_tensor(prefill_workspace_size(d), device)
+    wp, wn = _ws_arg(workspace, device)
+    _raise("kda_prefill", lib.kda_prefill(ctypes.byref(d), wp, wn, _stream(q)))
+    return out, final_state, snapshots
 
 
 def kda_chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=True,
@@ -211,16 +330,10 @@ def kda_chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final
     _check_state("final_state", final_state, (B, H, dk, dv), device)
     scale = 1.0 / math.sqrt(dk) if scale is None else float(scale)
     if workspace is not None:
-        if workspace.device != device or workspace.dtype != torch.uint8:
-            raise ValueError(f"workspace must be a uint8 tensor on {device}")
-        # the library wants 256-byte alignment; chunk_fwd_workspace leaves 256 B of slack
-        base = workspace.data_ptr()
-        off = (-base) % 256
-        nbytes = workspace.numel() - off
+        wp, wn = _ws_arg(workspace, device)
         rc = lib.kda_chunk_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                   _ptr(initial_state), _ptr(out), _ptr(final_state), B, T, H, dk,
-                                  dv, scale, _dtype_code(q), ctypes.c_void_p(base + off),
-                                  max(nbytes, 0), _stream(q))
+                                  dv, scale, _dtype_code(q), wp, wn, _stream(q))
         _raise("kda_chunk_fwd_ws", rc)
         return out, final_state
     rc = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
@@ -318,18 +431,23 @@ def _varlen_prep(q, k, v, g, beta, cu_seqlens, initial_state, output_final_state
 
 
 def kda_chunk_fwd_varlen(q, k, v, g, beta, cu_seqlens, scale=None, initial_state=None,
-                         output_final_state=True, out=None, final_state=None):
+                         output_final_state=True, out=None, final_state=None, workspace=None):
     """Packed variable-length prefill.  q, k, g: [1,total_T,H,dk] (or [total_T,H,dk]);
-    cu_seqlens: int32 [N+1] on the device.  Returns ``(out, final_state [N,H,dk,dv])``."""
+    cu_seqlens: int32 [N+1] on the device.  Returns ``(out, final_state [N,H,dk,dv])``.
+    With ``workspace`` (a tensor from ``varlen_workspace``) the call goes to
+    kda_chunk_fwd_varlen_ws and allocates nothing."""
     lib = load_library()
     H, dk, dv, total_T, N, out, final_state = _varlen_prep(
         q, k, v, g, beta, cu_seqlens, initial_state, output_final_state, out, final_state)
     scale = 1.0 / math.sqrt(dk) if scale is None else float(scale)
-    rc = lib.kda_chunk_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                  _ptr(initial_state), _ptr(out), _ptr(final_state),
-                                  _ptr(cu_seqlens.contiguous()), N, total_T, H, dk, dv, scale,
-                                  _dtype_code(q), _stream(q))
-    _raise("kda_chunk_fwd_varlen", rc)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(out),
+            _ptr(final_state), _ptr(cu_seqlens.contiguous()), N, total_T, H, dk, dv, scale,
+            _dtype_code(q))
+    if workspace is not None:
+        wp, wn = _ws_arg(workspace, q.device)
+        _raise("kda_chunk_fwd_varlen_ws", lib.kda_chunk_fwd_varlen_ws(*args, wp, wn, _stream(q)))
+        return out, final_state
+    _raise("kda_chunk_fwd_varlen", lib.kda_chunk_fwd_varlen(*args, _stream(q)))
     return out, final_state
 
 
@@ -420,11 +538,12 @@ def kda_decode_step_prologue(q_raw, k_raw, v, g_raw, beta_raw, state, scale=None
 
 
 def kda_chunk_bwd(q, k, v, g, beta, grad_out, scale=None, initial_state=None,
-                  grad_final_state=None, need_initial_state_grad=True):
+                  grad_final_state=None, need_initial_state_grad=True, workspace=None):
     """Gradients of sum(grad_out * out) + sum(grad_final_state * final_state) for
     kda_chunk_fwd's inputs (same shapes and dtype).  Returns ``(grad_q, grad_k,
     grad_v, grad_g, grad_beta, grad_initial_state or None)``; the initial-state
-    gradient is fp32 [B,H,dk,dv]."""
+    gradient is fp32 [B,H,dk,dv].  With ``workspace`` (``chunk_bwd_workspace``) the call
+    goes to kda_chunk_bwd_ws and allocates nothing."""
     lib = load_library()
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -439,15 +558,38 @@ def kda_chunk_bwd(q, k, v, g, beta, grad_out, scale=None, initial_state=None,
     ds0 = torch.empty((B, H, dk, dv), dtype=torch.float32, device=device) \
         if need_initial_state_grad else None
     scale = 1.0 / math.sqrt(dk) if scale is None else float(scale)
-    rc = lib.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
-                           _ptr(grad_out), _ptr(grad_final_state), *(_ptr(x) for x in grads),
-                           _ptr(ds0), B, T, H, dk, dv, scale, _dtype_code(q), _stream(q))
-    _raise("kda_chunk_bwd", rc)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(grad_out),
+            _ptr(grad_final_state), *(_ptr(x) for x in grads), _ptr(ds0), B, T, H, dk, dv, scale,
+            _dtype_code(q))
+    if workspace is not None:
+        wp, wn = _ws_arg(workspace, device)
+        _raise("kda_chunk_bwd_ws", lib.kda_chunk_bwd_ws(*args, wp, wn, _stream(q)))
+    else:
+        _raise("kda_chunk_bwd", lib.kda_chunk_bwd(*args, _stream(q)))
     return (*grads, ds0)
 
 
+def chunk_bwd_workspace(q, v):
+    """Workspace tensor for kda_chunk_bwd calls shaped like (q [B,T,H,dk], v)."""
+    B, T, H, dk = q.shape
+    n = load_library().kda_chunk_bwd_workspace_size(B, T, H, dk, v.shape[-1], _dtype_code(q))
+    if n == 0:
+        raise ValueError("backward sizes not accepted by the library")
+    return _ws_tensor(n, q.device)
+
+
+def chunk_bwd_varlen_workspace(q, v, cu_seqlens):
+    """Workspace tensor for kda_chunk_bwd_varlen calls shaped like (q, v, cu_seqlens)."""
+    H, dk = q.shape[-2], q.shape[-1]
+    n = load_library().kda_chunk_bwd_varlen_workspace_size(
+        cu_seqlens.numel() - 1, q.numel() // (H * dk), H, dk, v.shape[-1], _dtype_code(q))
+    if n == 0:
+        raise ValueError("backward sizes not accepted by the library")
+    return _ws_tensor(n, q.device)
+
+
 def kda_chunk_bwd_varlen(q, k, v, g, beta, grad_out, cu_seqlens, scale=None, initial_state=None,
-                         grad_final_state=None, need_initial_state_grad=True):
+                         grad_final_state=None, need_initial_state_grad=True, workspace=None):
     """kda_chunk_bwd for packed sequences (layouts of kda_chunk_fwd_varlen: q, k, g
     [1,total_T,H,dk] or [total_T,H,dk]; cu_seqlens int32 [N+1] on the device).
     Returns ``(grad_q, grad_k, grad_v, grad_g, grad_beta, grad_initial_state [N,H,dk,dv]
@@ -470,16 +612,27 @@ def kda_chunk_bwd_varlen(q, k, v, g, beta, grad_out, cu_seqlens, scale=None, ini
     ds0 = torch.empty((N, H, dk, dv), dtype=torch.float32, device=device) \
         if need_initial_state_grad else None
     scale = 1.0 / math.sqrt(dk) if scale is None else float(scale)
-    rc = lib.kda_chunk_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                  _ptr(initial_state), _ptr(grad_out), _ptr(grad_final_state),
-                                  *(_ptr(x) for x in grads), _ptr(ds0),
-                                  _ptr(cu_seqlens.contiguous()), N, total_T, H, dk, dv, scale,
-                                  _dtype_code(q), _stream(q))
-    _raise("kda_chunk_bwd_varlen", rc)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(grad_out),
+            _ptr(grad_final_state), *(_ptr(x) for x in grads), _ptr(ds0),
+            _ptr(cu_seqlens.contiguous()), N, total_T, H, dk, dv, scale, _dtype_code(q))
+    if workspace is not None:
+        wp, wn = _ws_arg(workspace, device)
+        _raise("kda_chunk_bwd_varlen_ws", lib.kda_chunk_bwd_varlen_ws(*args, wp, wn, _stream(q)))
+    else:
+        _raise("kda_chunk_bwd_varlen", lib.kda_chunk_bwd_varlen(*args, _stream(q)))
     return (*grads, ds0)
 
 
-def kda_chunk_transition(q, k, g, beta, transition=None):
+def transition_workspace(q):
+    """Workspace tensor for kda_chunk_transition calls shaped like q [B,T,H,dk]."""
+    B, T, H, dk = q.shape
+    n = load_library().kda_chunk_transition_workspace_size(B, T, H, dk, dk, _dtype_code(q))
+    if n == 0:
+        raise ValueError("transition sizes not accepted by the library")
+    return _ws_tensor(n, q.device)
+
+
+def kda_chunk_transition(q, k, g, beta, transition=None, workspace=None):
     """Transition of each of B segments: the exit state with v = 0 from the identity,
     P [B,H,dk,dk] fp32 (so that S_exit = P S_entry + the zero-entry exit state)."""
     lib = load_library()
@@ -491,9 +644,13 @@ def kda_chunk_transition(q, k, g, beta, transition=None):
     if transition is None:
         transition = torch.empty((B, H, dk, dk), dtype=torch.float32, device=device)
     _check_state("transition", transition, (B, H, dk, dk), device)
-    rc = lib.kda_chunk_transition(_ptr(q), _ptr(k), _ptr(g), _ptr(beta), _ptr(transition),
-                                  B, T, H, dk, dk, _dtype_code(q), _stream(q))
-    _raise("kda_chunk_transition", rc)
+    args = (_ptr(q), _ptr(k), _ptr(g), _ptr(beta), _ptr(transition), B, T, H, dk, dk,
+            _dtype_code(q))
+    if workspace is not None:
+        wp, wn = _ws_arg(workspace, device)
+        _raise("kda_chunk_transition_ws", lib.kda_chunk_transition_ws(*args, wp, wn, _stream(q)))
+    else:
+        _raise("kda_chunk_transition", lib.kda_chunk_transition(*args, _stream(q)))
     return transition
 
 

@@ -25,20 +25,24 @@
  *
  * Conventions shared by every entry point
  *  - All tensor pointers are DEVICE pointers owned by the caller, contiguous and
- *    row-major.  The prefill, backward and transition entry points use one
- *    workspace per call, a block the library keeps for reuse on each device: a
- *    call takes a free block at least as large as it needs, its stream first
- *    waiting for the event recorded when the block was last released, or
- *    allocates a new one (hipMallocFromPoolAsync on `stream` from a pool the
- *    library creates per device); at the end it records that event on `stream`
- *    and keeps the block.  Blocks are not freed until the process ends, except
- *    free blocks too small for a request, returned with hipFreeAsync (which on
- *    ROCm 7 blocks the host until the stream has drained) when a larger one is
- *    allocated.  Concurrent calls on several streams take distinct blocks.
- *    Prefill needs 66,048 bytes per 64-token chunk per head for bf16 at
- *    d = 128 (kda_chunk_fwd_workspace_size gives the exact figure); an
- *    allocation failure returns KDA_ERR_HIP.  kda_chunk_fwd_ws runs on a
- *    workspace the caller owns instead.  Decode allocates nothing.
+ *    row-major.
+ *  - Workspaces.  Prefill on bf16 input at d = 128 with 256 or more (sequence, head)
+ *    streams runs fused and needs none.  Every other prefill, the backward and the
+ *    transition need one per call, sized by the matching *_workspace_size function
+ *    (pure host arithmetic).  The *_ws entry points and kda_prefill run on a
+ *    workspace the caller owns (256-byte aligned, contents irrelevant, garbage on
+ *    exit; calls that may overlap need distinct ones) and allocate nothing.  The
+ *    entry points without a workspace argument are a convenience layer over them:
+ *    they take a block the library keeps per device.  A call takes a free block at
+ *    least as large as it needs, its stream first waiting for the event recorded
+ *    when the block was last released, or allocates one (hipMallocFromPoolAsync on
+ *    `stream` from a pool the library creates per device); at the end it records
+ *    that event on `stream` and keeps the block while the device's free blocks total
+ *    at most 4 GiB, returning the largest to the pool beyond that (hipFreeAsync,
+ *    which on ROCm 7 blocks the host until the stream has drained).  Blocks too
+ *    small for a request are returned the same way when a larger one is allocated.
+ *    An allocation failure returns KDA_ERR_HIP.  Decode and kda_state_compose
+ *    allocate nothing.
  *  - Alignment (KDA_ERR_ALIGN otherwise): prefill v and out 16 bytes, q, k, g and
  *    the states 4 bytes, beta its element size; decode state 16 bytes, every
  *    other pointer its element size.
@@ -53,11 +57,15 @@
  *    |k| <= 1.  Outside them the result is unspecified (never a memory fault).
  *  - Work is enqueued on `stream` and returns immediately; execution errors
  *    surface at the caller's next synchronisation.  No entry point keeps state
- *    between calls other than the workspace blocks above (event-ordered, so
- *    calls never share a live workspace); calls on different streams may
- *    overlap when their buffers do not.
- *  - Return value: KDA_OK, or a negative KDA_ERR_* code.  When a code other
- *    than KDA_OK is returned nothing was launched.
+ *    between calls other than the kept workspace blocks above (event-ordered, so
+ *    calls never share a live workspace); calls on different streams may overlap
+ *    when their buffers do not.
+ *  - Return value: KDA_OK, or a negative KDA_ERR_* code.  Argument codes
+ *    (everything but KDA_ERR_HIP) are returned before anything is enqueued.
+ *    A call clears any error an earlier HIP call left pending on the calling
+ *    thread, then launches its kernels one after another, checking each launch,
+ *    and stops at the first that fails: KDA_ERR_HIP means some of its kernels may
+ *    already be enqueued, and its outputs are unspecified.
  */
 #ifndef KDA_H_
 #define KDA_H_
@@ -69,7 +77,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 enum kda_dtype { KDA_BF16 = 0, KDA_F32 = 1 };
 
@@ -143,6 +151,52 @@ int kda_chunk_fwd_ws(const void* q, const void* k, const void* v, const void* g,
                      int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Every prefill variant on a caller workspace, in one descriptor: fixed length or
+ * packed, plain or with the gate prologue, with or without snapshots.  The fields
+ * mean exactly what the arguments of the named entry points mean:
+ *  q, k, v, g, beta, initial_state, out, final_state  as for kda_chunk_fwd (raw
+ *                     activations for q, k, g, beta when `prologue` is nonzero,
+ *                     see kda_chunk_fwd_prologue);
+ *  cu_seqlens         NULL: N sequences of T tokens each (fixed length); else the
+ *                     packed offsets of kda_chunk_fwd_varlen, with total_T tokens;
+ *  N                  number of sequences (B for fixed length);
+ *  snapshots, snapshot_tokens  NULL and 0 for none; else as for
+ *                     kda_chunk_fwd_snapshots / kda_chunk_fwd_varlen_snapshots.
+ * kda_prefill_workspace_size writes the bytes of workspace the call needs (0 when
+ * it needs none) after the same argument checks kda_prefill makes, and returns
+ * their code; it makes no device call.  kda_prefill runs the call on `workspace`
+ * (NULL allowed when 0 bytes are needed; else 256-byte aligned and at least that
+ * large, or KDA_ERR_WORKSPACE) and allocates nothing.  Results equal those of the
+ * matching named entry point bit for bit.
+ */
+typedef struct kda_prefill_desc {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;
+  const void* beta;
+  const float* initial_state;
+  void* out;
+  float* final_state;
+  const int32_t* cu_seqlens;
+  int N;
+  int T;
+  int total_T;
+  int H;
+  int dk;
+  int dv;
+  float scale;
+  int dtype;
+  int prologue;
+  float* snapshots;
+  int snapshot_tokens;
+} kda_prefill_desc;
+
+int kda_prefill_workspace_size(const kda_prefill_desc* desc, size_t* bytes);
+int kda_prefill(const kda_prefill_desc* desc, void* workspace, size_t workspace_bytes,
+                hipStream_t stream);
+
+/*
  * kda_chunk_fwd with the gate and normalisation prologue fused into the kernels'
  * loads, so the activations that produce q, k, g and beta are not written out
  * and read back.  The pages bound the log of the per-channel retention factor
@@ -204,6 +258,26 @@ int kda_chunk_fwd_varlen(const void* q, const void* k, const void* v, const void
                          hipStream_t stream);
 
 /*
+ * Workspace bytes kda_chunk_fwd_varlen_ws needs (0: none, the fused schedule, or
+ * sizes not accepted -- kda_prefill_workspace_size tells the two apart).  The
+ * packed schedules that take one need a 64-token slot per chunk per head for
+ * ceil(total_T / 64) + N chunks (66,048 bytes each for bf16 at d = 128), so it is
+ * bounded by the packed tokens, never by the longest sequence alone.
+ */
+size_t kda_chunk_fwd_varlen_workspace_size(int N, int total_T, int H, int dk, int dv,
+                                           int dtype);
+
+/*
+ * kda_chunk_fwd_varlen on a caller workspace (see the conventions above): same
+ * arguments, same results, allocates nothing.
+ */
+int kda_chunk_fwd_varlen_ws(const void* q, const void* k, const void* v, const void* g,
+                            const void* beta, const float* initial_state, void* out,
+                            float* final_state, const int32_t* cu_seqlens, int N, int total_T,
+                            int H, int dk, int dv, float scale, int dtype, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/*
  * kda_chunk_fwd_varlen on raw activations, with the gate and normalisation
  * prologue of kda_chunk_fwd_prologue (same formulas, same rounding) fused into the
  * loads.  Arguments, layouts and codes are those of kda_chunk_fwd_varlen, with the
@@ -261,10 +335,9 @@ int kda_chunk_fwd_varlen_snapshots(const void* q, const void* k, const void* v, 
  * bf16 operands rounded from fp32 values, with fp32 accumulation, and the
  * per-chunk states, state gradients, Delta and dU are kept as bf16; the inverse,
  * the 16-term sub-tile products and the decayed products stay fp32.  The call's
- * workspace (a reused block, see the conventions above) takes, per 64-token
- * chunk per head, 418,304 bytes for bf16 and 410,112 for
- * fp32 at d = 128 (246,016 and 213,248 at d = 64), so T = 65,536 with 32 heads
- * needs about 14 GB; an allocation failure returns KDA_ERR_HIP.
+ * workspace (kda_chunk_bwd_workspace_size) takes, per 64-token chunk per head,
+ * 418,304 bytes for bf16 and 410,112 for fp32 at d = 128 (246,016 and 213,248 at
+ * d = 64), so T = 65,536 with 32 heads needs about 14 GB.
  * Outputs must not alias inputs.
  */
 int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
@@ -272,6 +345,21 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, co
                   const float* grad_final_state, void* grad_q, void* grad_k, void* grad_v,
                   void* grad_g, void* grad_beta, float* grad_initial_state, int B, int T, int H,
                   int dk, int dv, float scale, int dtype, hipStream_t stream);
+
+/* Workspace bytes of kda_chunk_bwd for these sizes (0: sizes not accepted). */
+size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int dk, int dv, int dtype);
+
+/*
+ * kda_chunk_bwd on a caller workspace of at least kda_chunk_bwd_workspace_size
+ * bytes (256-byte aligned, else KDA_ERR_WORKSPACE): same arguments and results,
+ * allocates nothing.
+ */
+int kda_chunk_bwd_ws(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                     const float* initial_state, const void* grad_out,
+                     const float* grad_final_state, void* grad_q, void* grad_k, void* grad_v,
+                     void* grad_g, void* grad_beta, float* grad_initial_state, int B, int T,
+                     int H, int dk, int dv, float scale, int dtype, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
 
 /*
  * kda_chunk_bwd for packed variable-length input (the layout of
@@ -293,6 +381,18 @@ int kda_chunk_bwd_varlen(const void* q, const void* k, const void* v, const void
                          void* grad_g, void* grad_beta, float* grad_initial_state,
                          const int32_t* cu_seqlens, int N, int total_T, int H, int dk, int dv,
                          float scale, int dtype, hipStream_t stream);
+
+/* Workspace bytes of kda_chunk_bwd_varlen for these sizes (0: sizes not accepted). */
+size_t kda_chunk_bwd_varlen_workspace_size(int N, int total_T, int H, int dk, int dv, int dtype);
+
+/* kda_chunk_bwd_varlen on a caller workspace, as kda_chunk_bwd_ws is to kda_chunk_bwd. */
+int kda_chunk_bwd_varlen_ws(const void* q, const void* k, const void* v, const void* g,
+                            const void* beta, const float* initial_state, const void* grad_out,
+                            const float* grad_final_state, void* grad_q, void* grad_k,
+                            void* grad_v, void* grad_g, void* grad_beta,
+                            float* grad_initial_state, const int32_t* cu_seqlens, int N,
+                            int total_T, int H, int dk, int dv, float scale, int dtype,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Context parallelism for one long sequence split into R segments (design for
@@ -321,13 +421,22 @@ int kda_chunk_bwd_varlen(const void* q, const void* k, const void* v, const void
  *                  token leftmost.
  * dk == dv in {64, 128} for both dtypes.  fp32 inputs are computed on fp32
  * operands; bf16 inputs on bf16 matrix-core operands with fp32 accumulation and
- * an fp32 state, the precision of the bf16 prefill.  Its workspace (a reused
- * block, see the conventions above) takes, per 64-token chunk per head, 213,504
- * bytes for fp32 and 320,000 for bf16 at d = 128 (147,712 and 213,248 at d = 64).
+ * an fp32 state, the precision of the bf16 prefill.  Its workspace
+ * (kda_chunk_transition_workspace_size) takes, per 64-token chunk per head,
+ * 213,504 bytes for fp32 and 320,000 for bf16 at d = 128 (147,712 and 213,248 at
+ * d = 64).
  */
 int kda_chunk_transition(const void* q, const void* k, const void* g, const void* beta,
                          float* transition, int B, int T, int H, int dk, int dv, int dtype,
                          hipStream_t stream);
+
+/* Workspace bytes of kda_chunk_transition for these sizes (0: sizes not accepted). */
+size_t kda_chunk_transition_workspace_size(int B, int T, int H, int dk, int dv, int dtype);
+
+/* kda_chunk_transition on a caller workspace: same arguments and results, allocates nothing. */
+int kda_chunk_transition_ws(const void* q, const void* k, const void* g, const void* beta,
+                            float* transition, int B, int T, int H, int dk, int dv, int dtype,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * kda_state_compose: the sequential composition over R segments,

@@ -31,13 +31,9 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == sorted([
-        "kda_abi_version", "kda_status_string", "kda_chunk_fwd", "kda_chunk_fwd_workspace_size",
-        "kda_chunk_fwd_schedule",
-        "kda_chunk_fwd_ws", "kda_chunk_fwd_prologue", "kda_chunk_fwd_varlen_prologue",
-        "kda_chunk_fwd_varlen_snapshots", "kda_decode_step_prologue", "kda_chunk_bwd_varlen",
-        "kda_chunk_fwd_snapshots", "kda_chunk_fwd_varlen", "kda_decode_step", "kda_chunk_bwd",
-        "kda_chunk_transition", "kda_state_compose"])
+    """include/kda.h declares exactly the binding's export list."""
+    from gated_delta_rule_102_amd import kda
+    assert declared_functions() == sorted(kda.EXPORTS)
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -52,7 +48,7 @@ def test_library_exports_every_declared_symbol(lib):
 def test_version_and_status_strings(lib):
     lib.kda_abi_version.restype = ctypes.c_int
     lib.kda_status_string.restype = ctypes.c_char_p
-    assert lib.kda_abi_version() == 2
+    assert lib.kda_abi_version() == 3
     for code in range(-8, 1):
         assert lib.kda_status_string(code)
     assert lib.kda_status_string(-99) == b"unknown status"
@@ -251,3 +247,80 @@ def test_binding_rejects_wrong_output_shape_before_any_call():
     with pytest.raises(ValueError, match="out has shape"):
         kda.kda_decode_step(qd, qd, qd, qd, bd, st, out=torch.zeros((B, H, D + 1),
                                                                   dtype=torch.bfloat16))
+
+
+def test_caller_workspace_sizes_and_checks(lib):
+    """The caller-workspace forms: sizes are host arithmetic (the fused schedule --
+    bf16, d = 128, 256 or more streams -- needs none, packed schedules one 66,048-byte
+    slot per chunk and head for ceil(total_T / 64) + N chunks, the backward and the
+    transition their per-chunk bytes), and a missing, misaligned or short workspace
+    is refused with KDA_ERR_WORKSPACE before any device call."""
+    from gated_delta_rule_102_amd import kda
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    kda.load_library()
+    L = kda._lib
+    # packed prefill
+    assert L.kda_chunk_fwd_varlen_workspace_size(64, 921098, 32, 128, 128, 0) == 0   # fused
+    assert L.kda_chunk_fwd_varlen_workspace_size(4, 1000, 8, 128, 128, 0) == \
+        (1000 // 64 + 1 + 4) * 8 * 66048
+    assert L.kda_chunk_fwd_varlen_workspace_size(4, 1000, 8, 96, 96, 0) == 0        # refused
+    # fixed-length prefill on the fused schedule needs nothing
+    assert L.kda_chunk_fwd_workspace_size(2, 150, 128, 128, 128, 0) == 0
+    # backward: 418,304 B per chunk and head for bf16 at d = 128, 410,112 for fp32
+    assert L.kda_chunk_bwd_workspace_size(4, 4096, 16, 128, 128, 0) == 4 * 64 * 16 * 418304
+    assert L.kda_chunk_bwd_workspace_size(1, 100, 2, 128, 128, 1) == 2 * 2 * 410112
+    assert L.kda_chunk_bwd_varlen_workspace_size(3, 200, 2, 128, 128, 0) == \
+        ((200 + 63) // 64 + 3) * 2 * 418304
+    # transition: 320,000 B per chunk and head for bf16, 213,504 for fp32 at d = 128
+    assert L.kda_chunk_transition_workspace_size(2, 128, 4, 128, 128, 0) == 2 * 2 * 4 * 320000
+    assert L.kda_chunk_transition_workspace_size(1, 64, 1, 128, 128, 1) == 213504
+    assert L.kda_chunk_transition_workspace_size(1, 0, 1, 128, 128, 1) == 0
+    p = vp(4096)
+    big = 1 << 40
+    vw = L.kda_chunk_fwd_varlen_ws
+    assert vw(p, p, p, p, p, None, p, None, p, 4, 1000, 8, 128, 128, 0.1, 0, None, big, None) == -8
+    assert vw(p, p, p, p, p, None, p, None, p, 4, 1000, 8, 128, 128, 0.1, 0, p, 1024, None) == -8
+    assert vw(p, p, p, p, p, None, p, None, None, 4, 1000, 8, 128, 128, 0.1, 0, p, big,
+              None) == -1
+    assert vw(p, p, p, p, p, None, p, None, p, 4, 1000, 8, 128, 128, 0.1, 0, p, big,
+              None) in (-6, -7)
+    # the fused schedule takes no workspace: NULL is accepted and the call reaches the
+    # device check
+    assert vw(p, p, p, p, p, None, p, None, p, 64, 921098, 32, 128, 128, 0.1, 0, None, 0,
+              None) in (-6, -7)
+    bw = L.kda_chunk_bwd_ws
+    ok = [p, p, p, p, p, None, p, None, p, p, p, p, p, None]
+    assert bw(*ok, 1, 64, 1, 128, 128, 0.1, 0, vp(4096 + 64), big, None) == -8
+    assert bw(*ok, 1, 64, 1, 128, 128, 0.1, 0, p, 4096, None) == -8
+    assert bw(*ok, 1, 64, 1, 128, 128, 0.1, 0, p, big, None) in (-6, -7)
+    tw = L.kda_chunk_transition_ws
+    assert tw(p, p, p, p, p, 1, 64, 1, 128, 128, 0, p, 100, None) == -8
+    assert tw(p, p, p, p, p, 1, 64, 1, 128, 128, 0, p, big, None) in (-6, -7)
+
+
+def test_prefill_descriptor_checks(lib):
+    """kda_prefill_workspace_size and kda_prefill check a descriptor like the named
+    entry points check their arguments; the size query makes no device call."""
+    from gated_delta_rule_102_amd import kda
+    kda.load_library()
+    L = kda._lib
+    base = dict(q=4096, k=4096, v=4096, g=4096, beta=4096, out=4096, N=4, T=4096, H=16, dk=128,
+                dv=128, scale=0.1, dtype=0)
+    d = kda.PrefillDesc(**base)
+    assert kda.prefill_workspace_size(d) == (4 * 4096 // 64 + 4) * 16 * 66048
+    assert kda.prefill_workspace_size(kda.PrefillDesc(**{**base, "H": 64})) == 0      # fused
+    packed = kda.PrefillDesc(**{**base, "cu_seqlens": 4096, "T": 0, "total_T": 1000, "H": 8})
+    assert kda.prefill_workspace_size(packed) == (1000 // 64 + 1 + 4) * 8 * 66048
+    n = ctypes.c_size_t(0)
+    for bad, code in ((dict(dk=96, dv=96), -3), (dict(N=0), -2), (dict(dtype=7), -4),
+                      (dict(q=4098), -5), (dict(v=4104), -5), (dict(out=None), -1),
+                      (dict(snapshot_tokens=100, snapshots=4096), -2),
+                      (dict(snapshot_tokens=512), -1), (dict(dtype=1), -3)):
+        dd = kda.PrefillDesc(**{**base, **bad})
+        assert L.kda_prefill_workspace_size(ctypes.byref(dd), ctypes.byref(n)) == code, bad
+        assert L.kda_prefill(ctypes.byref(dd), ctypes.c_void_p(4096), 1 << 40, None) == code, bad
+    assert L.kda_prefill_workspace_size(None, ctypes.byref(n)) == -1
+    assert L.kda_prefill(ctypes.byref(d), None, 0, None) == -8           # workspace needed
+    assert L.kda_prefill(ctypes.byref(d), ctypes.c_void_p(4096), 1 << 40, None) in (-6, -7)
+    fused = kda.PrefillDesc(**{**base, "H": 64})
+    assert L.kda_prefill(ctypes.byref(fused), None, 0, None) in (-6, -7)
