@@ -26,7 +26,7 @@ COMMON = [
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 SOURCES = ["kda_prefill.hip", "kda_fused.hip", "kda_decode.hip", "kda_backward.hip",
-           "kda_context.hip"]
+           "kda_context.hip", "kda_noalloc.hip"]
 HOST_SOURCES = ["kda_api.cpp"]
 
 

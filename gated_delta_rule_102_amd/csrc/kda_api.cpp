@@ -395,6 +395,32 @@ int kda_chunk_fwd_ws(const void* q, const void* k, const void* v, const void* g,
                      true, workspace, workspace_bytes, stream);
 }
 
+int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* g,
+                          const void* beta, const float* initial_state, void* out,
+                          float* final_state, int B, int T, int H, int dk, int dv, float scale,
+                          int dtype, hipStream_t stream) {
+  const kda_prefill_desc d = fixed_desc(q, k, v, g, beta, initial_state, out, final_state, B, T,
+                                        H, dk, dv, scale, dtype);
+  int rc = check_prefill(d);
+  if (rc != KDA_OK) return rc;
+  kda::PrefillArgs a = prefill_args(d, stream);
+  if (kda::prefill_workspace_bytes(a) > 0) {
+    // windows short enough for the scratch array; none fit: refused before any device call
+    const int cg = kda::prefill_fit_window(a, kda::noalloc_scratch_bytes());
+    if (cg <= 0) return KDA_ERR_WORKSPACE;
+    a.window_chunks = cg;
+  }
+  rc = check_device();
+  if (rc != KDA_OK) return rc;
+  if (kda::prefill_workspace_bytes(a) > 0) {
+    void* ptr = nullptr;
+    if (kda::noalloc_scratch(&ptr) != hipSuccess) return KDA_ERR_HIP;
+    a.workspace = ptr;
+    a.workspace_bytes = kda::noalloc_scratch_bytes();
+  }
+  return kda::launch_prefill(a) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 int kda_chunk_fwd_prologue(const void* q_raw, const void* k_raw, const void* v,
                            const void* g_raw, const void* beta_raw, const float* initial_state,
                            void* out, float* final_state, int B, int T, int H, int dk, int dv,

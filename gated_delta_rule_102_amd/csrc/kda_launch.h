@@ -38,6 +38,7 @@ struct PrefillArgs {
   bool prologue = false;       // q, k, g, beta raw: normalise / gate in the kernel
   void* workspace = nullptr;   // caller's workspace (null: the call allocates its own)
   size_t workspace_bytes = 0;
+  int window_chunks = 0;       // > 0: fixed length runs in windows of this many chunks
 };
 
 struct BackwardArgs {
@@ -93,6 +94,14 @@ hipError_t launch_fused_prefill(const PrefillArgs& a);
 const char* prefill_schedule(const PrefillArgs& a);
 // Workspace bytes launch_prefill needs for these arguments (0 if unsupported).
 size_t prefill_workspace_bytes(const PrefillArgs& a);
+// Longest window (in chunks) whose workspace fits in max_bytes, for fixed-length
+// input off the fused schedule; 0 when not even one-chunk windows fit.
+int prefill_fit_window(const PrefillArgs& a, size_t max_bytes);
+
+// The file-scope scratch array of the allocation-free prefill (kda_noalloc.hip): its
+// size, and its address on the current device (looked up once per device).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** p);
 
 // Workspace blocks the library keeps for the calls that take no workspace (see
 // kda_api.cpp): ws_alloc takes a block of at least `bytes` for work enqueued on

@@ -1483,6 +1483,7 @@ constexpr int kWideStreams = 128;
 inline int prefill_cg(const PrefillArgs& a) {
   if (a.cu_seqlens != nullptr) return 0;
   const int nchunks = (a.T + kC - 1) / kC;
+  if (a.window_chunks > 0) return std::min(a.window_chunks, nchunks);
   const int cg = group_chunks(nchunks);
   const int streams = a.N * a.H;
   if (streams >= kWideStreams) return 0;
@@ -1496,7 +1497,8 @@ inline int prefill_cg(const PrefillArgs& a) {
 constexpr int kFusedStreams = 256;
 
 inline bool use_fused(const PrefillArgs& a) {
-  return fused_prefill_supported(a) && static_cast<int64_t>(a.N) * a.H >= kFusedStreams;
+  return a.window_chunks == 0 && fused_prefill_supported(a) &&
+         static_cast<int64_t>(a.N) * a.H >= kFusedStreams;
 }
 
 template <int D, typename TIn>
@@ -1544,6 +1546,20 @@ hipError_t launch_all(const PrefillArgs& a) {
 }
 
 }  // namespace
+
+template <int D, typename TIn>
+int fit_window(const PrefillArgs& a, size_t max_bytes) {
+  for (int cg = group_chunks((a.T + kC - 1) / kC); cg >= 1; --cg)
+    if (grouped_bytes<D, TIn>(a, cg) <= max_bytes) return cg;
+  return 0;
+}
+
+int prefill_fit_window(const PrefillArgs& a, size_t max_bytes) {
+  if (a.cu_seqlens != nullptr || a.T <= 0) return 0;
+  if (a.dtype_f32) return a.d == 64 ? fit_window<64, float>(a, max_bytes) : 0;
+  if (a.d == 128) return fit_window<128, bf16_t>(a, max_bytes);
+  return fit_window<64, bf16_t>(a, max_bytes);
+}
 
 size_t prefill_workspace_bytes(const PrefillArgs& a) {
   if (a.dtype_f32) return a.d == 64 ? workspace_bytes<64, float>(a) : 0;

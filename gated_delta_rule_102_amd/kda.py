@@ -22,6 +22,7 @@ _lib = None
 
 EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_schedule",
            "kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd_ws",
+           "kda_chunk_fwd_noalloc",
            "kda_prefill_workspace_size", "kda_prefill",
            "kda_chunk_fwd_prologue", "kda_chunk_fwd_snapshots",
            "kda_chunk_fwd_varlen", "kda_chunk_fwd_varlen_workspace_size", "kda_chunk_fwd_varlen_ws",
@@ -75,6 +76,9 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd_ws.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                      f32, i32, vp, ctypes.c_size_t, vp]
     lib.kda_chunk_fwd_ws.restype = i32
+    lib.kda_chunk_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                          f32, i32, vp]
+    lib.kda_chunk_fwd_noalloc.restype = i32
     sz = ctypes.c_size_t
     lib.kda_prefill_workspace_size.argtypes = [ctypes.POINTER(PrefillDesc), ctypes.POINTER(sz)]
     lib.kda_prefill_workspace_size.restype = i32
@@ -340,6 +344,35 @@ def kda_chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None, output_final
                            _ptr(out), _ptr(final_state), B, T, H, dk, dv, scale,
                            _dtype_code(q), _stream(q))
     _raise("kda_chunk_fwd", rc)
+    return out, final_state
+
+
+def kda_chunk_fwd_noalloc(q, k, v, g, beta, scale=None, initial_state=None,
+                          output_final_state=True, out=None, final_state=None):
+    """kda_chunk_fwd through kda_chunk_fwd_noalloc, which allocates nothing: its
+    scratch is the library's fixed 64 MiB per-GPU array (calls that overlap on one GPU
+    race on it).  Sizes whose windows do not fit raise KDAError (KDA_ERR_WORKSPACE).
+    Outputs are allocated here when not given, as for kda_chunk_fwd."""
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dtype, device = q.dtype, q.device
+    _check(dict(q=q, k=k, v=v, g=g, beta=beta), dtype, device)
+    if k.shape != q.shape or g.shape != q.shape or v.shape[:3] != q.shape[:3] \
+            or beta.shape != q.shape[:3]:
+        raise ValueError("shape mismatch among q, k, v, g, beta")
+    _check_state("initial_state", initial_state, (B, H, dk, dv), device)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=dtype, device=device)
+    _check_out(out, (B, T, H, dv), dtype, device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=device)
+    _check_state("final_state", final_state, (B, H, dk, dv), device)
+    scale = 1.0 / math.sqrt(dk) if scale is None else float(scale)
+    rc = lib.kda_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                   _ptr(initial_state), _ptr(out), _ptr(final_state), B, T, H, dk,
+                                   dv, scale, _dtype_code(q), _stream(q))
+    _raise("kda_chunk_fwd_noalloc", rc)
     return out, final_state
 
 

@@ -197,6 +197,25 @@ int kda_prefill(const kda_prefill_desc* desc, void* workspace, size_t workspace_
                 hipStream_t stream);
 
 /*
+ * kda_chunk_fwd for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): same arguments and results
+ * within the bf16 / fp32 tolerances of the other entry points, and it calls no
+ * hipMalloc, hipFree or allocating routine.  Its scratch is a fixed 64 MiB device
+ * array inside the library, one per GPU, held until the process ends; the fused
+ * schedule needs none, the others run in windows of chunks short enough for it
+ * (down to one chunk per window).  Sizes for which even one-chunk windows do not
+ * fit (the carried fp32 states plus two windows' chunk operands exceed 64 MiB, e.g.
+ * fp32 at d = 64 with 400 heads) return KDA_ERR_WORKSPACE before anything is
+ * enqueued.  Every call on a GPU uses that GPU's one array and nothing in it needs
+ * clearing between calls; calls that overlap on one GPU (other streams, other
+ * threads) race on it and must be serialised by the caller.
+ */
+int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* g,
+                          const void* beta, const float* initial_state, void* out,
+                          float* final_state, int B, int T, int H, int dk, int dv, float scale,
+                          int dtype, hipStream_t stream);
+
+/*
  * kda_chunk_fwd with the gate and normalisation prologue fused into the kernels'
  * loads, so the activations that produce q, k, g and beta are not written out
  * and read back.  The pages bound the log of the per-channel retention factor

@@ -324,3 +324,18 @@ def test_prefill_descriptor_checks(lib):
     assert L.kda_prefill(ctypes.byref(d), ctypes.c_void_p(4096), 1 << 40, None) in (-6, -7)
     fused = kda.PrefillDesc(**{**base, "H": 64})
     assert L.kda_prefill(ctypes.byref(fused), None, 0, None) in (-6, -7)
+
+
+def test_noalloc_refuses_sizes_beyond_its_scratch(lib):
+    """kda_chunk_fwd_noalloc checks its fixed scratch against the sizes on the host: fp32
+    at d = 64, 1000 tokens, 400 heads needs more than 64 MiB even in one-chunk windows
+    (KDA_ERR_WORKSPACE before any device call); sizes that fit reach the device check."""
+    from gated_delta_rule_102_amd import kda
+    L = kda.load_library()
+    p = ctypes.c_void_p(4096)
+    assert L.kda_chunk_fwd_noalloc(p, p, p, p, p, None, p, None, 1, 1000, 400, 64, 64, 0.1, 1,
+                                   None) == -8
+    assert L.kda_chunk_fwd_noalloc(p, p, p, p, p, None, p, None, 4, 4096, 16, 128, 128, 0.1, 0,
+                                   None) in (-6, -7)
+    assert L.kda_chunk_fwd_noalloc(None, p, p, p, p, None, p, None, 4, 4096, 16, 128, 128, 0.1, 0,
+                                   None) == -1
