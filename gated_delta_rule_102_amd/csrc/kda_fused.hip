@@ -263,6 +263,80 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
     in.beta = buf_ld16(rb, (16 * I + l16) * H * 2, 0);
   };
 
+  // The state step of chunk cs, whose operands are in LDS: run at the top of the next
+  // chunk's iteration, in the same barrier window as that chunk's first elementwise
+  // phase (which writes nothing this step reads), so the matrix-core work of one chunk
+  // and the vector work of the next overlap.
+  auto state_step = [&](const int cs) {
+    const int t0 = tok0 + cs * kCh;
+    const int nrow = min(kCh, len - cs * kCh);
+    const float* betas = reinterpret_cast<const float*>(smem + fl::BETA) + (cs & 1) * kCh;
+    bf16x8_t Sb[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) Sb[b] = acc_frag(S[2 * b], S[2 * b + 1]);
+    // Y = Diag(beta) (V - Kb S) (the stored -Kb makes it an accumulation onto V)
+    f32x4_t Y[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * tt + 4 * g4 + i;
+        const uint16_t vb = *reinterpret_cast<const uint16_t*>(
+            smem + fl::VST + (row >> 2) * fl::VRB + (row & 3) * 256 + (16 * jt + l16) * 2);
+        Y[tt][i] = __uint_as_float(static_cast<uint32_t>(vb) << 16);
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b) Y[tt] = mma(lds_frag(smem, fl::KBN + frag_at(tt, b, 4, lane)), Sb[b], Y[tt]);
+      const float4 b4 = *reinterpret_cast<const float4*>(betas + 16 * tt + 4 * g4);
+      Y[tt][0] *= b4.x;
+      Y[tt][1] *= b4.y;
+      Y[tt][2] *= b4.z;
+      Y[tt][3] *= b4.w;
+    }
+    // Delta_i = T_ii (Y_i - sum_{m<i} A_im Delta_m)
+    f32x4_t Dl[4];
+    bf16x4_t Dq[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x4_t w = Y[i];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        if (m < i) w = mma16(lds_frag4(smem, fl::AOF + off_id(i, m) * 512 + lane * 8), Dq[m], w);
+      Dl[i] = mma16(lds_frag4(smem, fl::TDF + i * 512 + lane * 8), acc_frag4(w), f32x4_t{0.f, 0.f, 0.f, 0.f});
+      Dq[i] = acc_frag4(Dl[i]);
+    }
+    bf16x8_t Db[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) Db[b] = acc_frag(Dl[2 * b], Dl[2 * b + 1]);
+    // O^T = S^T Qb^T + Delta^T M^T: lane (t, g) holds value columns 16 jt + 4 g .. +3
+    {
+      const auto ro = make_rsrc(p.out + (static_cast<int64_t>(t0) * H + h) * kD, (nrow - 1) * rs + kD * 2);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < 4; ++b) o = mma(Sb[b], lds_frag(smem, fl::QB + frag_at(tt, b, 4, lane)), o);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          if (b <= (tt >> 1)) o = mma(Db[b], lds_frag(smem, fl::MF + frag_at(tt, b, 2, lane)), o);
+        buf_st64_nt(i32x2_t{static_cast<int>(pack_bf16x2(o[0], o[1])), static_cast<int>(pack_bf16x2(o[2], o[3]))},
+                    ro, (16 * tt + l16) * rs + (16 * jt + 4 * g4) * 2, 0);
+      }
+    }
+    // S <- Diag(Lambda) S + Kt^T Delta
+    {
+      const float* lam = reinterpret_cast<const float*>(smem + fl::LAM);
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        const float4 l4 = *reinterpret_cast<const float4*>(lam + 16 * ct + 4 * g4);
+        f32x4_t acc = {S[ct][0] * l4.x, S[ct][1] * l4.y, S[ct][2] * l4.z, S[ct][3] * l4.w};
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc = mma(lds_frag(smem, fl::KTT + frag_at(ct, b, 2, lane)), Db[b], acc);
+        S[ct] = acc;
+      }
+    }
+  };
+
   ChunkIn cur;
   if (nchunks > 0) load_chunk(0, cur);
 
@@ -270,6 +344,7 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
     const int t0 = tok0 + c * kCh;
     const int nrow = min(kCh, len - c * kCh);
     float* betas = reinterpret_cast<float*>(smem + fl::BETA) + (c & 1) * kCh;
+    if (c > 0) state_step(c - 1);
 
     // ============================================ E1: cumulative log-decay per sub-tile
     float L[2][8];          // inclusive sum of g over the sub-tile's rows up to this one
@@ -316,33 +391,29 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
       }
     }
 
-    // per-channel factors, one thread per channel
-    if (tid < kD) {
+    // per-channel factors: thread (m, c) for sub-tile m and channel c
+    {
+      const int m = tid >> 7, ch = tid & (kD - 1);
       const float* tot = reinterpret_cast<const float*>(smem + fl::TOT);
-      float t4[4], R[4];
+      float R[4];
+      R[0] = tot[ch];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) t4[m] = tot[m * kD + tid];
-      R[0] = t4[0];
-#pragma unroll
-      for (int m = 1; m < 4; ++m) R[m] = R[m - 1] + t4[m];
+      for (int x = 1; x < 4; ++x) R[x] = R[x - 1] + tot[x * kD + ch];
+      const float rb = m == 0 ? 0.f : R[m - 1];          // decay before sub-tile m
+      // e^{R_m} as e^{tot_m} e^{R_{m-1}}: each factor alone is in range
+      const float em = fast_exp2(tot[m * kD + ch] * kLog2e) * fast_exp2(rb * kLog2e);
       float* fac = reinterpret_cast<float*>(smem + fl::FAC);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const float rb = m == 0 ? 0.f : R[m - 1];          // decay before sub-tile m
-        // e^{R_m} as e^{tot_m} e^{R_{m-1}}: each factor alone is in range
-        const float em = fast_exp2(t4[m] * kLog2e) * fast_exp2(rb * kLog2e);
-        fac[(m * 3 + 0) * kD + tid] = -em;                                 // -e^{R_m}
-        fac[(m * 3 + 1) * kD + tid] = p.scale * em;                        // scale e^{R_m}
-        fac[(m * 3 + 2) * kD + tid] = fast_exp2((R[3] - R[m]) * kLog2e);   // e^{Ln - R_m}
-      }
+      fac[(m * 3 + 0) * kD + ch] = -em;                                 // -e^{R_m}
+      fac[(m * 3 + 1) * kD + ch] = p.scale * em;                        // scale e^{R_m}
+      fac[(m * 3 + 2) * kD + ch] = fast_exp2((R[3] - R[m]) * kLog2e);   // e^{Ln - R_m}
       float* foff = reinterpret_cast<float*>(smem + fl::FOFF);
 #pragma unroll
       for (int a = 1; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < a; ++b) foff[off_id(a, b) * kD + tid] = fast_exp2((R[a] - R[b]) * kLog2e);
-      // Lambda in state row order: row r holds channel sigma(r)
-      const int r = 32 * (tid >> 5) + 16 * ((tid >> 2) & 1) + 4 * ((tid >> 3) & 3) + (tid & 3);
-      reinterpret_cast<float*>(smem + fl::LAM)[r] = fast_exp2(R[3] * kLog2e);
+        if (a > m) foff[off_id(a, m) * kD + ch] = fast_exp2((R[a] - R[m]) * kLog2e);
+      if (m == 0) {   // Lambda in state row order: row r holds channel sigma(r)
+        const int r = 32 * (ch >> 5) + 16 * ((ch >> 2) & 1) + 4 * ((ch >> 3) & 3) + (ch & 3);
+        reinterpret_cast<float*>(smem + fl::LAM)[r] = fast_exp2(R[3] * kLog2e);
+      }
     }
     lds_barrier();                                                          // B2
 
@@ -528,73 +599,8 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
     // this wavefront's v rows are in LDS (loads whose destination is LDS count in vmcnt)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();                                                          // B5
-
-    // ============================================ state step
-    bf16x8_t Sb[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) Sb[b] = acc_frag(S[2 * b], S[2 * b + 1]);
-    // Y = Diag(beta) (V - Kb S) (the stored -Kb makes it an accumulation onto V)
-    f32x4_t Y[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * tt + 4 * g4 + i;
-        const uint16_t vb = *reinterpret_cast<const uint16_t*>(
-            smem + fl::VST + (row >> 2) * fl::VRB + (row & 3) * 256 + (16 * jt + l16) * 2);
-        Y[tt][i] = __uint_as_float(static_cast<uint32_t>(vb) << 16);
-      }
-#pragma unroll
-      for (int b = 0; b < 4; ++b) Y[tt] = mma(lds_frag(smem, fl::KBN + frag_at(tt, b, 4, lane)), Sb[b], Y[tt]);
-      const float4 b4 = *reinterpret_cast<const float4*>(betas + 16 * tt + 4 * g4);
-      Y[tt][0] *= b4.x;
-      Y[tt][1] *= b4.y;
-      Y[tt][2] *= b4.z;
-      Y[tt][3] *= b4.w;
-    }
-    // Delta_i = T_ii (Y_i - sum_{m<i} A_im Delta_m)
-    f32x4_t Dl[4];
-    bf16x4_t Dq[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f32x4_t w = Y[i];
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        if (m < i) w = mma16(lds_frag4(smem, fl::AOF + off_id(i, m) * 512 + lane * 8), Dq[m], w);
-      Dl[i] = mma16(lds_frag4(smem, fl::TDF + i * 512 + lane * 8), acc_frag4(w), f32x4_t{0.f, 0.f, 0.f, 0.f});
-      Dq[i] = acc_frag4(Dl[i]);
-    }
-    bf16x8_t Db[2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) Db[b] = acc_frag(Dl[2 * b], Dl[2 * b + 1]);
-    // O^T = S^T Qb^T + Delta^T M^T: lane (t, g) holds value columns 16 jt + 4 g .. +3
-    {
-      const auto ro = make_rsrc(p.out + (static_cast<int64_t>(t0) * H + h) * kD, (nrow - 1) * rs + kD * 2);
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        f32x4_t o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int b = 0; b < 4; ++b) o = mma(Sb[b], lds_frag(smem, fl::QB + frag_at(tt, b, 4, lane)), o);
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-          if (b <= (tt >> 1)) o = mma(Db[b], lds_frag(smem, fl::MF + frag_at(tt, b, 2, lane)), o);
-        buf_st64_nt(i32x2_t{static_cast<int>(pack_bf16x2(o[0], o[1])), static_cast<int>(pack_bf16x2(o[2], o[3]))},
-                    ro, (16 * tt + l16) * rs + (16 * jt + 4 * g4) * 2, 0);
-      }
-    }
-    // S <- Diag(Lambda) S + Kt^T Delta
-    {
-      const float* lam = reinterpret_cast<const float*>(smem + fl::LAM);
-#pragma unroll
-      for (int ct = 0; ct < 8; ++ct) {
-        const float4 l4 = *reinterpret_cast<const float4*>(lam + 16 * ct + 4 * g4);
-        f32x4_t acc = {S[ct][0] * l4.x, S[ct][1] * l4.y, S[ct][2] * l4.z, S[ct][3] * l4.w};
-#pragma unroll
-        for (int b = 0; b < 2; ++b) acc = mma(lds_frag(smem, fl::KTT + frag_at(ct, b, 2, lane)), Db[b], acc);
-        S[ct] = acc;
-      }
-    }
   }
+  if (nchunks > 0) state_step(nchunks - 1);
 
   if (p.sT != nullptr) {
     float* dst = p.sT + (static_cast<int64_t>(n) * H + h) * kD * kD;

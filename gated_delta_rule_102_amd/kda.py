@@ -711,17 +711,40 @@ def chunk_fwd_context_parallel(q, k, v, g, beta, segment_tokens, scale=None,
                                initial_state=None):
     """kda_chunk_fwd over segments of ``segment_tokens`` tokens scheduled as context
     parallelism would place them on several GPUs, here all on q's device:
-      1. per segment (independent): its zero-entry exit state (kda_chunk_fwd) and
-         its transition (kda_chunk_transition);
+      1. every segment (independent): its exit state from a zero entry state
+         (kda_chunk_fwd) and its transition (kda_chunk_transition);
       2. the entry state of every segment (kda_state_compose) -- across GPUs this
          is where the per-segment (transition, exit state) pairs are all-gathered;
-      3. per segment (independent): kda_chunk_fwd from its entry state.
-    Returns ``(out [B,T,H,dv], final_state [B,H,dk,dv], entry_states [R+1,B,H,dk,dv])``."""
+      3. every segment (independent): kda_chunk_fwd from its entry state.
+    When ``segment_tokens`` divides T the R segments of each sequence run as one
+    batch: [B, T, H, .] is viewed, without a copy, as [B*R, T/R, H, .] and every phase
+    is a single call over all B*R segments.  Otherwise the segments run one after
+    another.  Returns ``(out [B,T,H,dv], final_state [B,H,dk,dv], entry_states
+    [R+1,B,H,dk,dv])``."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     seg = int(segment_tokens)
     if seg <= 0:
         raise ValueError("segment_tokens must be positive")
+    if T % seg == 0:
+        R = T // seg
+
+        def view(x):
+            return x.reshape(B * R, seg, *x.shape[2:])
+
+        sq, sk, sv, sg, sb = (view(x) for x in (q, k, v, g, beta))
+        # phase 1: exit states from zero entry states and transitions, all segments at once
+        _, exits = kda_chunk_fwd(sq, sk, sv, sg, sb, scale, None)
+        trans = kda_chunk_transition(sq, sk, sg, sb)
+        # [B*R, ...] in (b, r) order -> [R, B, ...] for the composition
+        tr = trans.reshape(B, R, H, dk, dk).transpose(0, 1).contiguous()
+        ex = exits.reshape(B, R, H, dk, dv).transpose(0, 1).contiguous()
+        entry = kda_state_compose(tr, ex, initial_state)                     # phase 2
+        s0 = entry[:R].transpose(0, 1).reshape(B * R, H, dk, dv).contiguous()
+        out = torch.empty((B, T, H, dv), dtype=v.dtype, device=v.device)
+        kda_chunk_fwd(sq, sk, sv, sg, sb, scale, s0, output_final_state=False,
+                      out=out.reshape(B * R, seg, H, dv))                      # phase 3
+        return out, entry[R], entry
     bounds = [(t0, min(T, t0 + seg)) for t0 in range(0, T, seg)]
     R = len(bounds)
 
