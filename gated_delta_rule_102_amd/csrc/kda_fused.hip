@@ -47,7 +47,15 @@
 //    (A_ii is strictly lower, so A^16 = 0).
 //  - The output is produced transposed (rows = value columns), so each lane holds 4
 //    consecutive values of one token's output row and writes them with one 8-byte
-//    store.
+//    store.  v is read the same way (4 consecutive values of a token row per lane)
+//    and brought into the accumulator layout by a product with the 16 x 16 identity.
+//  - Per chunk: the previous chunk's state step and this chunk's cumulative decay
+//    share the first barrier window; the products of the sub-tile pairs are summed
+//    over the two channel halves by the wavefront that finishes the pair (the
+//    diagonal pair and its inverse in one, the pairs J < I in the other).  Global
+//    traffic is spread over the chunk: the next chunk's q, k, g, beta right after the
+//    decay scan, the previous chunk's output during the pair products, the next v at
+//    the end.
 
 #include "kda_device.h"
 #include "kda_launch.h"
@@ -69,9 +77,7 @@ constexpr int MF = KTT + 16384;             // M         [4 t-tiles][2 s-blocks]
 constexpr int AOF = MF + 8192;              // -A_IJ, J < I: [6][64 lanes] x 8 B (16x16x16 A)
 constexpr int TDF = AOF + 6 * 512;          // T_II:        [4][64 lanes] x 8 B
 constexpr int LAM = TDF + 4 * 512;          // Lambda, state row order [128] fp32
-constexpr int VRB = 1024 + 32;              // v staging: 4 rows (1 KB) + pad per group
-constexpr int VST = LAM + 512;              // v of the chunk, [16 groups][VRB]
-constexpr int OFF = VST + 16 * VRB;         // column side of pair (I, J < I): [6][4][64][16]
+constexpr int OFF = LAM + 512;              // column side of pair (I, J < I): [6][4][64][16]
 constexpr int PART = OFF + 6 * 4096;        // partial A^T, M^T of 10 pairs: [10][2][64][16]
 constexpr int XS = PART + 10 * 2048;        // 16 x 17 fp32 transpose scratch, 4 wavefronts
 constexpr int TOT = XS + 4 * 16 * 17 * 4;   // sub-tile decay totals [4][128] fp32
@@ -194,7 +200,7 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
   const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
   const int H = p.H;
   const int I = wave >> 1, hf = wave & 1;     // elementwise role: sub-tile, channel half
-  const int jt = wave;                        // state role: value columns 16 jt .. +15
+  // state role: wavefront w owns value columns 16 w .. +15
 
   // ---------------------------------------------------------------- which sequence
   const int rank = blockIdx.x / H, h = blockIdx.x % H;
@@ -218,7 +224,7 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
     __syncthreads();
     if (tid < p.N) ord[rk] = tid;
     __syncthreads();
-    n = ord[rank];
+    n = __builtin_amdgcn_readfirstlane(ord[rank]);   // uniform: keeps addresses scalar
     __syncthreads();
   }
   int tok0, len;
@@ -238,7 +244,7 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
     for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        S[ct][i] = s0 ? s0[sigma(16 * ct + 4 * g4 + i) * kD + 16 * jt + l16] : 0.f;
+        S[ct][i] = s0 ? s0[sigma(16 * ct + 4 * g4 + i) * kD + 16 * wave + l16] : 0.f;
   }
 
   const uint32_t rs = static_cast<uint32_t>(H) * kD * 2;   // token row stride (bytes)
@@ -263,80 +269,143 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
     in.beta = buf_ld16(rb, (16 * I + l16) * H * 2, 0);
   };
 
-  // The state step of chunk cs, whose operands are in LDS: run at the top of the next
-  // chunk's iteration, in the same barrier window as that chunk's first elementwise
-  // phase (which writes nothing this step reads), so the matrix-core work of one chunk
-  // and the vector work of the next overlap.
-  auto state_step = [&](const int cs) {
-    const int t0 = tok0 + cs * kCh;
-    const int nrow = min(kCh, len - cs * kCh);
+  // B operand of the 16 x 16 identity for 16x16x16 products (lane: column l16, rows
+  // 4 g .. +3)
+  bf16x4_t eye;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) eye[i] = 4 * g4 + i == l16 ? 0x3F80 : 0;
+
+  // The state step of chunk cs, whose operands are in LDS.  It runs at the top of the
+  // next chunk's iteration, in the barrier window of that chunk's first elementwise
+  // phase (which writes nothing read here).  The output rows come back packed in
+  // registers and are stored later in the iteration, spread away from the other
+  // global memory traffic.  Operand fragments are read from LDS one batch ahead of the
+  // products that use them.
+  auto state_step = [&](const int cs, const i32x2_t (&vin)[4], uint32_t (&opk)[4][2]) {
     const float* betas = reinterpret_cast<const float*>(smem + fl::BETA) + (cs & 1) * kCh;
+    bf16x4_t fa[6], ft[4];   // -A_IJ (J < I) and T_II, for the substitution below
+#pragma unroll
+    for (int x = 0; x < 6; ++x) fa[x] = lds_frag4(smem, fl::AOF + x * 512 + lane * 8);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) ft[x] = lds_frag4(smem, fl::TDF + x * 512 + lane * 8);
     bf16x8_t Sb[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) Sb[b] = acc_frag(S[2 * b], S[2 * b + 1]);
-    // Y = Diag(beta) (V - Kb S) (the stored -Kb makes it an accumulation onto V)
+
+    // Y = Diag(beta) (V - Kb S) (the stored -Kb makes the product an addition).  V
+    // arrives row-major (lane: token l16, value columns 4 g .. +3) and enters the
+    // accumulator layout as the product V I_16, exact in fp32; the two products are
+    // summed by the vector unit (a 16x16x16 result is not fed to a 16x16x32 product as
+    // its accumulator).
     f32x4_t Y[4];
+    bf16x8_t F[2][4];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+    for (int tt = 0; tt < 4; ++tt) F[0][tt] = lds_frag(smem, fl::KBN + frag_at(tt, 0, 4, lane));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * tt + 4 * g4 + i;
-        const uint16_t vb = *reinterpret_cast<const uint16_t*>(
-            smem + fl::VST + (row >> 2) * fl::VRB + (row & 3) * 256 + (16 * jt + l16) * 2);
-        Y[tt][i] = __uint_as_float(static_cast<uint32_t>(vb) << 16);
+    for (int tt = 0; tt < 4; ++tt) Y[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      if (b < 3) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) F[(b + 1) & 1][tt] = lds_frag(smem, fl::KBN + frag_at(tt, b + 1, 4, lane));
+      } else {   // the first batch of Qb
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) F[0][tt] = lds_frag(smem, fl::QB + frag_at(tt, 0, 4, lane));
       }
 #pragma unroll
-      for (int b = 0; b < 4; ++b) Y[tt] = mma(lds_frag(smem, fl::KBN + frag_at(tt, b, 4, lane)), Sb[b], Y[tt]);
+      for (int tt = 0; tt < 4; ++tt) Y[tt] = mma(F[b & 1][tt], Sb[b], Y[tt]);
+    }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const f32x4_t vt = mma16(__builtin_bit_cast(bf16x4_t, vin[tt]), eye, f32x4_t{0.f, 0.f, 0.f, 0.f});
       const float4 b4 = *reinterpret_cast<const float4*>(betas + 16 * tt + 4 * g4);
-      Y[tt][0] *= b4.x;
-      Y[tt][1] *= b4.y;
-      Y[tt][2] *= b4.z;
-      Y[tt][3] *= b4.w;
+      Y[tt][0] = (Y[tt][0] + vt[0]) * b4.x;
+      Y[tt][1] = (Y[tt][1] + vt[1]) * b4.y;
+      Y[tt][2] = (Y[tt][2] + vt[2]) * b4.z;
+      Y[tt][3] = (Y[tt][3] + vt[3]) * b4.w;
+    }
+    // O^T = S^T Qb^T + Delta^T M^T, the first term while the substitution below waits
+    // on its own chain: lane (t, g) holds value columns 16 w + 4 g .. +3 of token t
+    f32x4_t o[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) o[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      if (b < 3) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) F[(b + 1) & 1][tt] = lds_frag(smem, fl::QB + frag_at(tt, b + 1, 4, lane));
+      } else {   // M: fragments (tt, b <= tt / 2)
+        F[0][0] = lds_frag(smem, fl::MF + frag_at(0, 0, 2, lane));
+        F[0][1] = lds_frag(smem, fl::MF + frag_at(1, 0, 2, lane));
+        F[0][2] = lds_frag(smem, fl::MF + frag_at(2, 0, 2, lane));
+        F[0][3] = lds_frag(smem, fl::MF + frag_at(3, 0, 2, lane));
+      }
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) o[tt] = mma(Sb[b], F[b & 1][tt], o[tt]);
     }
     // Delta_i = T_ii (Y_i - sum_{m<i} A_im Delta_m)
-    f32x4_t Dl[4];
     bf16x4_t Dq[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       f32x4_t w = Y[i];
 #pragma unroll
       for (int m = 0; m < 4; ++m)
-        if (m < i) w = mma16(lds_frag4(smem, fl::AOF + off_id(i, m) * 512 + lane * 8), Dq[m], w);
-      Dl[i] = mma16(lds_frag4(smem, fl::TDF + i * 512 + lane * 8), acc_frag4(w), f32x4_t{0.f, 0.f, 0.f, 0.f});
-      Dq[i] = acc_frag4(Dl[i]);
+        if (m < i) w = mma16(fa[off_id(i, m)], Dq[m], w);
+      Dq[i] = acc_frag4(mma16(ft[i], acc_frag4(w), f32x4_t{0.f, 0.f, 0.f, 0.f}));
     }
+    // Delta as 32-deep fragments: tiles (2 b, 2 b + 1) side by side
     bf16x8_t Db[2];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) Db[b] = acc_frag(Dl[2 * b], Dl[2 * b + 1]);
-    // O^T = S^T Qb^T + Delta^T M^T: lane (t, g) holds value columns 16 jt + 4 g .. +3
-    {
-      const auto ro = make_rsrc(p.out + (static_cast<int64_t>(t0) * H + h) * kD, (nrow - 1) * rs + kD * 2);
+    for (int b = 0; b < 2; ++b)
+      Db[b] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(Dq[2 * b], Dq[2 * b + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+    F[1][0] = lds_frag(smem, fl::MF + frag_at(2, 1, 2, lane));
+    F[1][1] = lds_frag(smem, fl::MF + frag_at(3, 1, 2, lane));
+    F[1][2] = lds_frag(smem, fl::KTT + frag_at(0, 0, 2, lane));
+    F[1][3] = lds_frag(smem, fl::KTT + frag_at(0, 1, 2, lane));
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < 4; ++tt) o[tt] = mma(Db[0], F[0][tt], o[tt]);
+    o[2] = mma(Db[1], F[1][0], o[2]);
+    o[3] = mma(Db[1], F[1][1], o[3]);
 #pragma unroll
-        for (int b = 0; b < 4; ++b) o = mma(Sb[b], lds_frag(smem, fl::QB + frag_at(tt, b, 4, lane)), o);
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-          if (b <= (tt >> 1)) o = mma(Db[b], lds_frag(smem, fl::MF + frag_at(tt, b, 2, lane)), o);
-        buf_st64_nt(i32x2_t{static_cast<int>(pack_bf16x2(o[0], o[1])), static_cast<int>(pack_bf16x2(o[2], o[3]))},
-                    ro, (16 * tt + l16) * rs + (16 * jt + 4 * g4) * 2, 0);
-      }
+    for (int tt = 0; tt < 4; ++tt) {
+      opk[tt][0] = pack_bf16x2(o[tt][0], o[tt][1]);
+      opk[tt][1] = pack_bf16x2(o[tt][2], o[tt][3]);
     }
-    // S <- Diag(Lambda) S + Kt^T Delta
-    {
-      const float* lam = reinterpret_cast<const float*>(smem + fl::LAM);
+    // S <- Diag(Lambda) S + Kt^T Delta, Kt fragments one accumulator tile ahead
+    const float* lam = reinterpret_cast<const float*>(smem + fl::LAM);
+    bf16x8_t K2[2][2] = {{F[1][2], F[1][3]}, {F[1][2], F[1][3]}};
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct) {
-        const float4 l4 = *reinterpret_cast<const float4*>(lam + 16 * ct + 4 * g4);
-        f32x4_t acc = {S[ct][0] * l4.x, S[ct][1] * l4.y, S[ct][2] * l4.z, S[ct][3] * l4.w};
-#pragma unroll
-        for (int b = 0; b < 2; ++b) acc = mma(lds_frag(smem, fl::KTT + frag_at(ct, b, 2, lane)), Db[b], acc);
-        S[ct] = acc;
+    for (int ct = 0; ct < 8; ++ct) {
+      if (ct < 7) {
+        K2[(ct + 1) & 1][0] = lds_frag(smem, fl::KTT + frag_at(ct + 1, 0, 2, lane));
+        K2[(ct + 1) & 1][1] = lds_frag(smem, fl::KTT + frag_at(ct + 1, 1, 2, lane));
       }
+      const float4 l4 = *reinterpret_cast<const float4*>(lam + 16 * ct + 4 * g4);
+      f32x4_t acc = {S[ct][0] * l4.x, S[ct][1] * l4.y, S[ct][2] * l4.z, S[ct][3] * l4.w};
+      acc = mma(K2[ct & 1][0], Db[0], acc);
+      S[ct] = mma(K2[ct & 1][1], Db[1], acc);
     }
   };
+  // v of chunk cs for this wavefront's value columns: lane (t, g) loads token 16 tt + t,
+  // columns 16 w + 4 g .. +3 (rows past the end read 0)
+  auto load_v = [&](const int cs, i32x2_t (&vin)[4]) {
+    const int t0 = tok0 + cs * kCh;
+    const int nrow = min(kCh, len - cs * kCh);
+    const auto rv = make_rsrc(p.v + (static_cast<int64_t>(t0) * H + h) * kD, (nrow - 1) * rs + kD * 2);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) vin[tt] = buf_ld64(rv, (16 * tt + l16) * rs + (16 * wave + 4 * g4) * 2, 0);
+  };
+  auto store_out = [&](const int cs, const uint32_t (&opk)[4][2]) {
+    const int t0 = tok0 + cs * kCh;
+    const int nrow = min(kCh, len - cs * kCh);
+    const auto ro = make_rsrc(p.out + (static_cast<int64_t>(t0) * H + h) * kD, (nrow - 1) * rs + kD * 2);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+      buf_st64_nt(i32x2_t{static_cast<int>(opk[tt][0]), static_cast<int>(opk[tt][1])}, ro,
+                  (16 * tt + l16) * rs + (16 * wave + 4 * g4) * 2, 0);
+  };
 
+  i32x2_t vin[4];
   ChunkIn cur;
   if (nchunks > 0) load_chunk(0, cur);
 
@@ -344,7 +413,8 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
     const int t0 = tok0 + c * kCh;
     const int nrow = min(kCh, len - c * kCh);
     float* betas = reinterpret_cast<float*>(smem + fl::BETA) + (c & 1) * kCh;
-    if (c > 0) state_step(c - 1);
+    uint32_t opk[4][2];
+    if (c > 0) state_step(c - 1, vin, opk);
 
     // ============================================ E1: cumulative log-decay per sub-tile
     float L[2][8];          // inclusive sum of g over the sub-tile's rows up to this one
@@ -377,19 +447,6 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
     }
     if (hf == 0 && g4 == 0) betas[16 * I + l16] = beta_t;
     lds_barrier();                                                          // B1
-
-    // v of this chunk straight into LDS (16-byte loads whose destination is LDS; 4
-    // rows per wavefront instruction, each group of 4 rows padded by 32 bytes)
-    {
-      const auto rv = make_rsrc(p.v + (static_cast<int64_t>(t0) * H + h) * kD, (nrow - 1) * rs + kD * 2);
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const int grp = 2 * wave + x;                  // rows 4 grp .. +3
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rv, (__attribute__((address_space(3))) void*)(smem + fl::VST + grp * fl::VRB), 16,
-            (4 * grp + (lane >> 4)) * rs + (lane & 15) * 16, 0, 0, 0);
-      }
-    }
 
     // per-channel factors: thread (m, c) for sub-tile m and channel c
     {
@@ -490,6 +547,10 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
       }
     }
     lds_barrier();                                                          // B3
+    // the previous chunk's output goes out during the products below, which issue no
+    // other memory traffic (measured: stores and loads issued together in the first
+    // phase, behind the prefetch, cost about a fifth of the chunk time)
+    if (c > 0) store_out(c - 1, opk);
 
     // ============================================ P: decayed sub-tile products
     // transposed: C[s, t] = sum_c colside[s, c] rowside[t, c]; lane (t, g) holds
@@ -511,103 +572,117 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
           }
         }
       }
+      // The two channel halves' partials meet in the wavefront that finishes the pair:
+      // the diagonal pair, whose inverse is the longest piece of work, in the half-0
+      // wavefront, the pairs J < I in the half-1 wavefront.
+      auto part = [&](int J, int x) { return smem + fl::PART + (pair_id(I, J) * 2 + x) * 1024 + lane * 16; };
       if (hf == 1) {
+        *reinterpret_cast<f32x4_t*>(part(I, 0)) = pa[I];
+        *reinterpret_cast<f32x4_t*>(part(I, 1)) = pm[I];
+      } else {
 #pragma unroll
-        for (int J = 0; J < 4; ++J)
-          if (J <= I) {
-            *reinterpret_cast<f32x4_t*>(smem + fl::PART + (pair_id(I, J) * 2 + 0) * 1024 + lane * 16) = pa[J];
-            *reinterpret_cast<f32x4_t*>(smem + fl::PART + (pair_id(I, J) * 2 + 1) * 1024 + lane * 16) = pm[J];
+        for (int J = 0; J < 3; ++J)
+          if (J < I) {
+            *reinterpret_cast<f32x4_t*>(part(J, 0)) = pa[J];
+            *reinterpret_cast<f32x4_t*>(part(J, 1)) = pm[J];
           }
       }
       lds_barrier();                                                        // B4
-      if (hf == 0) {
-        const int t = 16 * I + l16;
+      const int t = 16 * I + l16;
+      // sums the halves of pair (I, J), writes M's block and, for J < I, -A_IJ; returns
+      // beta-scaled A_IJ (masked to s < t) in accumulator layout
+      auto finish = [&](const int J) {
+        const f32x4_t oa = *reinterpret_cast<const f32x4_t*>(part(J, 0));
+        const f32x4_t om = *reinterpret_cast<const f32x4_t*>(part(J, 1));
+        f32x4_t av;
+        float mv[4];
 #pragma unroll
-        for (int J = 0; J < 4; ++J)
-          if (J <= I) {
-            const f32x4_t oa = *reinterpret_cast<const f32x4_t*>(smem + fl::PART + (pair_id(I, J) * 2 + 0) * 1024 + lane * 16);
-            const f32x4_t om = *reinterpret_cast<const f32x4_t*>(smem + fl::PART + (pair_id(I, J) * 2 + 1) * 1024 + lane * 16);
-            f32x4_t av;
-            float mv[4];
+        for (int i = 0; i < 4; ++i) {
+          const int s = 16 * J + 4 * g4 + i;
+          av[i] = s < t ? beta_t * (pa[J][i] + oa[i]) : 0.f;
+          mv[i] = s <= t ? p.scale * (pm[J][i] + om[i]) : 0.f;
+        }
+        // M[t][s]: fragment (t-tile I, s-block J/2), elements 4 (J%2) .. +3
+        *reinterpret_cast<uint2*>(smem + fl::MF + frag_at(I, J >> 1, 2, l16 + 16 * g4) + 8 * (J & 1)) =
+            uint2{pack_bf16x2(mv[0], mv[1]), pack_bf16x2(mv[2], mv[3])};
+        if (J < I)   // -A_IJ as a 16x16x16 A operand: lane (t, g) holds columns 4 g .. +3
+          *reinterpret_cast<uint2*>(smem + fl::AOF + off_id(I, J) * 512 + lane * 8) =
+              uint2{pack_bf16x2(-av[0], -av[1]), pack_bf16x2(-av[2], -av[3])};
+        return av;
+      };
+      if (hf == 1) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int s = 16 * J + 4 * g4 + i;
-              av[i] = s < t ? beta_t * (pa[J][i] + oa[i]) : 0.f;
-              mv[i] = s <= t ? p.scale * (pm[J][i] + om[i]) : 0.f;
-            }
-            // M[t][s]: fragment (t-tile I, s-block J/2), elements 4 (J%2) .. +3
-            *reinterpret_cast<uint2*>(smem + fl::MF + frag_at(I, J >> 1, 2, l16 + 16 * g4) + 8 * (J & 1)) =
-                uint2{pack_bf16x2(mv[0], mv[1]), pack_bf16x2(mv[2], mv[3])};
-            if (J < I) {
-              // -A_IJ as a 16x16x16 A operand: lane (t, g) holds columns 4 g .. +3
-              *reinterpret_cast<uint2*>(smem + fl::AOF + off_id(I, J) * 512 + lane * 8) =
-                  uint2{pack_bf16x2(-av[0], -av[1]), pack_bf16x2(-av[2], -av[3])};
-            } else {
-              // T_II = (I + A_II)^{-1}, computed as T^T = (I + B)^{-1} with B = A_II^T,
-              // which this lane holds in accumulator layout (rows 4 g + i, column l16);
-              // fp32 16x16x4 matrix-core products, whose A operand is read in row layout
-              // (lane: row l16, columns 4 g .. +3) and B operand in accumulator layout,
-              // so a result feeds the next B side directly and its A side after a
-              // transpose through this wavefront's 16 x 17 scratch.
-              float* sc = reinterpret_cast<float*>(smem + fl::XS) + I * 16 * 17;
-              auto mm = [&](const float (&xr)[4], const float (&yc)[4]) {
-                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int J = 0; J < 3; ++J)
+          if (J < I) finish(J);
+      } else {
+        const f32x4_t av = finish(I);
+        // T_II = (I + A_II)^{-1}, computed as T^T = (I + B)^{-1} with B = A_II^T,
+        // which this lane holds in accumulator layout (rows 4 g + i, column l16);
+        // fp32 16x16x4 matrix-core products, whose A operand is read in row layout
+        // (lane: row l16, columns 4 g .. +3) and B operand in accumulator layout,
+        // so a result feeds the next B side directly and its A side after a
+        // transpose through this wavefront's 16 x 17 scratch.
+        float* sc = reinterpret_cast<float*>(smem + fl::XS) + I * 16 * 17;
+        auto mm = [&](const float (&xr)[4], const float (&yc)[4]) {
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int st = 0; st < 4; ++st) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xr[st], yc[st], acc, 0, 0, 0);
-                return acc;
-              };
-              auto to_row = [&](const f32x4_t& cc, float (&r)[4]) {
+          for (int st = 0; st < 4; ++st) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xr[st], yc[st], acc, 0, 0, 0);
+          return acc;
+        };
+        auto to_row = [&](const f32x4_t& cc, float (&r)[4]) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sc[(4 * g4 + i) * 17 + l16] = cc[i];
+          for (int i = 0; i < 4; ++i) sc[(4 * g4 + i) * 17 + l16] = cc[i];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) r[i] = sc[l16 * 17 + 4 * g4 + i];
-              };
-              const float b_c[4] = {av[0], av[1], av[2], av[3]};
-              float b_r[4];
-              to_row(av, b_r);
-              const f32x4_t p1 = mm(b_r, b_c);                         // B^2
-              const float p1_c[4] = {p1[0], p1[1], p1[2], p1[3]};
-              float p1_r[4];
-              to_row(p1, p1_r);
-              const f32x4_t p2 = mm(p1_r, p1_c);                       // B^4
-              const f32x4_t b3 = mm(b_r, p1_c);                        // B^3
-              const float p2_c[4] = {p2[0], p2[1], p2[2], p2[3]};
-              float p2_r[4];
-              to_row(p2, p2_r);
-              const f32x4_t p3 = mm(p2_r, p2_c);                       // B^8
-              const float p3_c[4] = {p3[0], p3[1], p3[2], p3[3]};
-              f32x4_t t1;                                              // I - B + B^2 - B^3
+          for (int i = 0; i < 4; ++i) r[i] = sc[l16 * 17 + 4 * g4 + i];
+        };
+        const float b_c[4] = {av[0], av[1], av[2], av[3]};
+        float b_r[4];
+        to_row(av, b_r);
+        const f32x4_t p1 = mm(b_r, b_c);                         // B^2
+        const float p1_c[4] = {p1[0], p1[1], p1[2], p1[3]};
+        float p1_r[4];
+        to_row(p1, p1_r);
+        const f32x4_t p2 = mm(p1_r, p1_c);                       // B^4
+        const f32x4_t b3 = mm(b_r, p1_c);                        // B^3
+        const float p2_c[4] = {p2[0], p2[1], p2[2], p2[3]};
+        float p2_r[4];
+        to_row(p2, p2_r);
+        const f32x4_t p3 = mm(p2_r, p2_c);                       // B^8
+        const float p3_c[4] = {p3[0], p3[1], p3[2], p3[3]};
+        f32x4_t t1;                                              // I - B + B^2 - B^3
 #pragma unroll
-              for (int i = 0; i < 4; ++i) t1[i] = (4 * g4 + i == l16 ? 1.f : 0.f) - b_c[i] + p1[i] - b3[i];
-              float t1_r[4];
-              to_row(t1, t1_r);
-              f32x4_t t2 = mm(t1_r, p2_c);                             // T1 (I + B^4)
+        for (int i = 0; i < 4; ++i) t1[i] = (4 * g4 + i == l16 ? 1.f : 0.f) - b_c[i] + p1[i] - b3[i];
+        float t1_r[4];
+        to_row(t1, t1_r);
+        f32x4_t t2 = mm(t1_r, p2_c);                             // T1 (I + B^4)
 #pragma unroll
-              for (int i = 0; i < 4; ++i) t2[i] += t1[i];
-              float t2_r[4];
-              to_row(t2, t2_r);
-              f32x4_t t3 = mm(t2_r, p3_c);                             // T2 (I + B^8)
+        for (int i = 0; i < 4; ++i) t2[i] += t1[i];
+        float t2_r[4];
+        to_row(t2, t2_r);
+        f32x4_t t3 = mm(t2_r, p3_c);                             // T2 (I + B^8)
 #pragma unroll
-              for (int i = 0; i < 4; ++i) t3[i] += t2[i];
-              // lane (l16, g) holds T^T[4 g + i][l16] = T[l16][4 g + i]: the A operand
-              *reinterpret_cast<uint2*>(smem + fl::TDF + I * 512 + lane * 8) =
-                  uint2{pack_bf16x2(t3[0], t3[1]), pack_bf16x2(t3[2], t3[3])};
-            }
-          }
+        for (int i = 0; i < 4; ++i) t3[i] += t2[i];
+        // lane (l16, g) holds T^T[4 g + i][l16] = T[l16][4 g + i]: the A operand
+        *reinterpret_cast<uint2*>(smem + fl::TDF + I * 512 + lane * 8) =
+            uint2{pack_bf16x2(t3[0], t3[1]), pack_bf16x2(t3[2], t3[3])};
       }
     }
-    // this wavefront's v rows are in LDS (loads whose destination is LDS count in vmcnt)
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // this chunk's v, consumed by its state step at the top of the next iteration
+    load_v(c, vin);
     lds_barrier();                                                          // B5
   }
-  if (nchunks > 0) state_step(nchunks - 1);
+  if (nchunks > 0) {
+    uint32_t opk[4][2];
+    state_step(nchunks - 1, vin, opk);
+    store_out(nchunks - 1, opk);
+  }
 
   if (p.sT != nullptr) {
     float* dst = p.sT + (static_cast<int64_t>(n) * H + h) * kD * kD;
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[sigma(16 * ct + 4 * g4 + i) * kD + 16 * jt + l16] = S[ct][i];
+      for (int i = 0; i < 4; ++i) dst[sigma(16 * ct + 4 * g4 + i) * kD + 16 * wave + l16] = S[ct][i];
   }
 }
 
