@@ -54,8 +54,8 @@
 //    over the two channel halves by the wavefront that finishes the pair (the
 //    diagonal pair and its inverse in one, the pairs J < I in the other).  Global
 //    traffic is spread over the chunk: the next chunk's q, k, g, beta right after the
-//    decay scan, the previous chunk's output during the pair products, the next v at
-//    the end.
+//    decay scan, the previous chunk's output in halves during the operand and the
+//    pair-product phases, the next v at the end.
 
 #include "kda_device.h"
 #include "kda_launch.h"
@@ -79,8 +79,7 @@ constexpr int TDF = AOF + 6 * 512;          // T_II:        [4][64 lanes] x 8 B
 constexpr int LAM = TDF + 4 * 512;          // Lambda, state row order [128] fp32
 constexpr int OFF = LAM + 512;              // column side of pair (I, J < I): [6][4][64][16]
 constexpr int PART = OFF + 6 * 4096;        // partial A^T, M^T of 10 pairs: [10][2][64][16]
-constexpr int XS = PART + 10 * 2048;        // 16 x 17 fp32 transpose scratch, 4 wavefronts
-constexpr int TOT = XS + 4 * 16 * 17 * 4;   // sub-tile decay totals [4][128] fp32
+constexpr int TOT = PART + 10 * 2048;       // sub-tile decay totals [4][128] fp32
 constexpr int FAC = TOT + 4 * 128 * 4;      // per (sub-tile, channel) factors [4][3][128]
 constexpr int FOFF = FAC + 4 * 3 * 128 * 4; // e^{R_I - R_J}, I > J: [6][128]
 constexpr int BETA = FOFF + 6 * 128 * 4;    // [2 parities][64] fp32
@@ -395,12 +394,14 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) vin[tt] = buf_ld64(rv, (16 * tt + l16) * rs + (16 * wave + 4 * g4) * 2, 0);
   };
-  auto store_out = [&](const int cs, const uint32_t (&opk)[4][2]) {
+  // output rows of token tiles t_lo .. t_hi - 1 of chunk cs
+  auto store_out = [&](const int cs, const uint32_t (&opk)[4][2], const int t_lo, const int t_hi) {
     const int t0 = tok0 + cs * kCh;
     const int nrow = min(kCh, len - cs * kCh);
     const auto ro = make_rsrc(p.out + (static_cast<int64_t>(t0) * H + h) * kD, (nrow - 1) * rs + kD * 2);
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
+      if (tt >= t_lo && tt < t_hi)
       buf_st64_nt(i32x2_t{static_cast<int>(opk[tt][0]), static_cast<int>(opk[tt][1])}, ro,
                   (16 * tt + l16) * rs + (16 * wave + 4 * g4) * 2, 0);
   };
@@ -473,6 +474,11 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
       }
     }
     lds_barrier();                                                          // B2
+    // the previous chunk's output goes out in two halves, here and during the pair
+    // products, phases that issue no other global memory traffic (measured: stores
+    // and loads issued together in the first phase, behind the prefetch, cost about a
+    // fifth of the chunk time)
+    if (c > 0) store_out(c - 1, opk, 0, 2);
 
     // ============================================ E2: chunk operands
     // rowf = e^{L_t - R_I} >= 1, colf = e^{R_I - L_t} <= 1 (R_I: end of the sub-tile)
@@ -547,10 +553,7 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
       }
     }
     lds_barrier();                                                          // B3
-    // the previous chunk's output goes out during the products below, which issue no
-    // other memory traffic (measured: stores and loads issued together in the first
-    // phase, behind the prefetch, cost about a fifth of the chunk time)
-    if (c > 0) store_out(c - 1, opk);
+    if (c > 0) store_out(c - 1, opk, 2, 4);
 
     // ============================================ P: decayed sub-tile products
     // transposed: C[s, t] = sum_c colside[s, c] rowside[t, c]; lane (t, g) holds
@@ -616,50 +619,56 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
           if (J < I) finish(J);
       } else {
         const f32x4_t av = finish(I);
-        // T_II = (I + A_II)^{-1}, computed as T^T = (I + B)^{-1} with B = A_II^T,
-        // which this lane holds in accumulator layout (rows 4 g + i, column l16);
-        // fp32 16x16x4 matrix-core products, whose A operand is read in row layout
-        // (lane: row l16, columns 4 g .. +3) and B operand in accumulator layout,
-        // so a result feeds the next B side directly and its A side after a
-        // transpose through this wavefront's 16 x 17 scratch.
-        float* sc = reinterpret_cast<float*>(smem + fl::XS) + I * 16 * 17;
-        auto mm = [&](const float (&xr)[4], const float (&yc)[4]) {
-          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int st = 0; st < 4; ++st) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xr[st], yc[st], acc, 0, 0, 0);
-          return acc;
+        // T_II = (I + A_II)^{-1}, computed as T^T = (I + B)^{-1} with B = A_II^T, which
+        // is strictly lower (B^16 = 0), as (I - B)(I + B^2)(I + B^4)(I + B^8).  This lane
+        // holds B in accumulator layout C(B) (rows 4 g + i, column l16).  A 16x16x16
+        // product takes C(X^T) as its A operand and C(Y) as its B operand and returns
+        // C(X Y), so the powers are carried in both orientations and nothing is
+        // transposed through memory (the first transpose is a product with I).  Each
+        // operand is split into bf16 high and low parts, and a product is three
+        // matrix-core products (high x high, high x low, low x high): about 16 bits,
+        // far finer than the bf16 the inverse is rounded to.
+        struct Split {
+          bf16x4_t h, l;
         };
-        auto to_row = [&](const f32x4_t& cc, float (&r)[4]) {
+        auto split = [](const f32x4_t& x) {
+          Split sp;
+          sp.h = acc_frag4(x);
+          f32x4_t r;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sc[(4 * g4 + i) * 17 + l16] = cc[i];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) r[i] = sc[l16 * 17 + 4 * g4 + i];
+          for (int i = 0; i < 4; ++i)
+            r[i] = x[i] - __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(sp.h[i])) << 16);
+          sp.l = acc_frag4(r);
+          return sp;
         };
-        const float b_c[4] = {av[0], av[1], av[2], av[3]};
-        float b_r[4];
-        to_row(av, b_r);
-        const f32x4_t p1 = mm(b_r, b_c);                         // B^2
-        const float p1_c[4] = {p1[0], p1[1], p1[2], p1[3]};
-        float p1_r[4];
-        to_row(p1, p1_r);
-        const f32x4_t p2 = mm(p1_r, p1_c);                       // B^4
-        const f32x4_t b3 = mm(b_r, p1_c);                        // B^3
-        const float p2_c[4] = {p2[0], p2[1], p2[2], p2[3]};
-        float p2_r[4];
-        to_row(p2, p2_r);
-        const f32x4_t p3 = mm(p2_r, p2_c);                       // B^8
-        const float p3_c[4] = {p3[0], p3[1], p3[2], p3[3]};
-        f32x4_t t1;                                              // I - B + B^2 - B^3
+        auto mm = [](const Split& xt, const Split& y) {   // C(X Y) from C(X^T), C(Y)
+          const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+          return mma16(xt.l, y.h, mma16(xt.h, y.l, mma16(xt.h, y.h, z)));
+        };
+        const Split sB = split(av);
+        const f32x4_t bt = mma16(sB.l, eye, mma16(sB.h, eye, f32x4_t{0.f, 0.f, 0.f, 0.f}));   // C(B^T)
+        const Split sBt = split(bt);
+        const f32x4_t p1 = mm(sBt, sB), p1t = mm(sB, sBt);           // B^2 and its transpose
+        const Split s1 = split(p1), s1t = split(p1t);
+        const f32x4_t p2 = mm(s1t, s1), p2t = mm(s1, s1t);           // B^4
+        const f32x4_t b3 = mm(sBt, s1), b3t = mm(s1, sBt);           // B^3
+        const Split s2 = split(p2), s2t = split(p2t);
+        const f32x4_t p3 = mm(s2t, s2);                               // B^8
+        f32x4_t t1, t1t;                                              // I - B + B^2 - B^3
 #pragma unroll
-        for (int i = 0; i < 4; ++i) t1[i] = (4 * g4 + i == l16 ? 1.f : 0.f) - b_c[i] + p1[i] - b3[i];
-        float t1_r[4];
-        to_row(t1, t1_r);
-        f32x4_t t2 = mm(t1_r, p2_c);                             // T1 (I + B^4)
+        for (int i = 0; i < 4; ++i) {
+          const float d = 4 * g4 + i == l16 ? 1.f : 0.f;
+          t1[i] = d - av[i] + p1[i] - b3[i];
+          t1t[i] = d - bt[i] + p1t[i] - b3t[i];
+        }
+        const Split sT1t = split(t1t);
+        f32x4_t t2 = mm(sT1t, s2), t2t = mm(s2, sT1t);               // T1 (I + B^4)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) t2[i] += t1[i];
-        float t2_r[4];
-        to_row(t2, t2_r);
-        f32x4_t t3 = mm(t2_r, p3_c);                             // T2 (I + B^8)
+        for (int i = 0; i < 4; ++i) {
+          t2[i] += t1[i];
+          t2t[i] += t1t[i];
+        }
+        f32x4_t t3 = mm(split(t2t), split(p3));                       // T2 (I + B^8)
 #pragma unroll
         for (int i = 0; i < 4; ++i) t3[i] += t2[i];
         // lane (l16, g) holds T^T[4 g + i][l16] = T[l16][4 g + i]: the A operand
@@ -674,7 +683,7 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
   if (nchunks > 0) {
     uint32_t opk[4][2];
     state_step(nchunks - 1, vin, opk);
-    store_out(nchunks - 1, opk);
+    store_out(nchunks - 1, opk, 0, 4);
   }
 
   if (p.sT != nullptr) {
