@@ -394,7 +394,10 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) vin[tt] = buf_ld64(rv, (16 * tt + l16) * rs + (16 * wave + 4 * g4) * 2, 0);
   };
-  // output rows of token tiles t_lo .. t_hi - 1 of chunk cs
+  // output rows of token tiles t_lo .. t_hi - 1 of chunk cs: plain stores, so that the
+  // cache joins the eight wavefronts' 32-byte pieces of a row into whole lines (with
+  // the non-temporal hint each piece went to memory alone: twice the output's bytes
+  // written, measured)
   auto store_out = [&](const int cs, const uint32_t (&opk)[4][2], const int t_lo, const int t_hi) {
     const int t0 = tok0 + cs * kCh;
     const int nrow = min(kCh, len - cs * kCh);
@@ -402,7 +405,7 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
       if (tt >= t_lo && tt < t_hi)
-      buf_st64_nt(i32x2_t{static_cast<int>(opk[tt][0]), static_cast<int>(opk[tt][1])}, ro,
+      buf_st64(i32x2_t{static_cast<int>(opk[tt][0]), static_cast<int>(opk[tt][1])}, ro,
                   (16 * tt + l16) * rs + (16 * wave + 4 * g4) * 2, 0);
   };
 

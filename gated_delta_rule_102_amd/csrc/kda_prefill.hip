@@ -1205,9 +1205,11 @@ __device__ __forceinline__ void scan_body(const ScanParams& p, char* smem, const
     for (int pc = tid; pc < kC * PPR; pc += kThreads) {
       const int t = pc / PPR, part = pc % PPR;
       const i32x4_t val = *reinterpret_cast<const i32x4_t*>(ost + t * CF::RBO + part * 16);
-      // outputs are not read again here: non-temporal stores; rows past the
-      // sequence end are dropped by the range check
-      buf_st128_nt(val, ro, t * rs_v + part * 16, 0);
+      // plain stores (a row's other column slices arrive from other workgroups, and
+      // the cache joins the pieces into whole lines: with the non-temporal hint each
+      // piece went to memory on its own, measured as extra write traffic); rows past
+      // the sequence end are dropped by the range check
+      buf_st128(val, ro, t * rs_v + part * 16, 0);
     }
   };
 
