@@ -579,10 +579,13 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
         }
       }
       // The two channel halves' partials meet in the wavefront that finishes the pair:
-      // the diagonal pair, whose inverse is the longest piece of work, in the half-0
-      // wavefront, the pairs J < I in the half-1 wavefront.
+      // the diagonal pair, whose inverse is the longest piece of work, in wavefront
+      // (I, hd) with hd = 1 for I = 1, 2 and 0 otherwise -- wavefronts 0, 3, 5, 6, one
+      // per SIMD when wavefront w runs on SIMD w % 4 -- and the pairs J < I in the
+      // other half's wavefront.
+      const int hd = (I == 1 || I == 2) ? 1 : 0;
       auto part = [&](int J, int x) { return smem + fl::PART + (pair_id(I, J) * 2 + x) * 1024 + lane * 16; };
-      if (hf == 1) {
+      if (hf != hd) {
         *reinterpret_cast<f32x4_t*>(part(I, 0)) = pa[I];
         *reinterpret_cast<f32x4_t*>(part(I, 1)) = pm[I];
       } else {
@@ -616,7 +619,7 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
               uint2{pack_bf16x2(-av[0], -av[1]), pack_bf16x2(-av[2], -av[3])};
         return av;
       };
-      if (hf == 1) {
+      if (hf != hd) {
 #pragma unroll
         for (int J = 0; J < 3; ++J)
           if (J < I) finish(J);
