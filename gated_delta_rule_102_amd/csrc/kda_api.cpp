@@ -520,13 +520,21 @@ int check_backward(const void* q, const void* k, const void* v, const void* g, c
                      {dsT, 4, false}, {ds0, 4, false}, {cu, 4, false}});
 }
 
+// A self-allocating backward takes at most this much workspace; beyond it the call runs
+// in windows of chunks (see kda_chunk_bwd).
+constexpr size_t kBackwardSelfBytes = size_t{2} << 30;
+
 int run_backward(kda::BackwardArgs a, bool caller_ws, void* workspace, size_t workspace_bytes) {
   if (caller_ws) {
-    const size_t need = kda::backward_workspace_bytes(a);
-    if (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < need)
-      return KDA_ERR_WORKSPACE;
+    if (workspace == nullptr || !aligned(workspace, 256)) return KDA_ERR_WORKSPACE;
+    const int cw = kda::backward_fit_window(a, workspace_bytes);
+    if (cw < 0) return KDA_ERR_WORKSPACE;
+    a.window_chunks = cw;
     a.workspace = workspace;
     a.workspace_bytes = workspace_bytes;
+  } else {
+    const int cw = kda::backward_fit_window(a, kBackwardSelfBytes);
+    a.window_chunks = cw < 0 ? 1 : cw;
   }
   const int rc = check_device();
   if (rc != KDA_OK) return rc;
@@ -561,12 +569,20 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, co
                           scale, dtype, nullptr, 0, stream);
 }
 
-size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int dk, int dv, int dtype) {
-  if (check_common(dk, dv, H, dtype) != KDA_OK || check_sizes(false, B, T, 0, H) != KDA_OK) return 0;
+size_t kda_chunk_bwd_window_workspace_size(int B, int T, int H, int dk, int dv, int dtype,
+                                           int window_chunks) {
+  if (check_common(dk, dv, H, dtype) != KDA_OK || check_sizes(false, B, T, 0, H) != KDA_OK ||
+      window_chunks < 0)
+    return 0;
   kda::BackwardArgs a{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                       nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                       B, T, H, dk, 1.f, dtype == KDA_F32, nullptr};
+  a.window_chunks = window_chunks;
   return kda::backward_workspace_bytes(a);
+}
+
+size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int dk, int dv, int dtype) {
+  return kda_chunk_bwd_window_workspace_size(B, T, H, dk, dv, dtype, 0);
 }
 
 int kda_chunk_bwd_varlen_ws(const void* q, const void* k, const void* v, const void* g,
@@ -600,15 +616,22 @@ int kda_chunk_bwd_varlen(const void* q, const void* k, const void* v, const void
                                  stream);
 }
 
-size_t kda_chunk_bwd_varlen_workspace_size(int N, int total_T, int H, int dk, int dv, int dtype) {
-  if (check_common(dk, dv, H, dtype) != KDA_OK || check_sizes(true, N, 0, total_T, H) != KDA_OK)
+size_t kda_chunk_bwd_varlen_window_workspace_size(int N, int total_T, int H, int dk, int dv,
+                                                  int dtype, int window_chunks) {
+  if (check_common(dk, dv, H, dtype) != KDA_OK || check_sizes(true, N, 0, total_T, H) != KDA_OK ||
+      window_chunks < 0)
     return 0;
   kda::BackwardArgs a{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                       nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                       N, 0, H, dk, 1.f, dtype == KDA_F32, nullptr};
   a.cu_seqlens = reinterpret_cast<const int32_t*>(uintptr_t{256});
   a.total_T = total_T;
+  a.window_chunks = window_chunks;
   return kda::backward_workspace_bytes(a);
+}
+
+size_t kda_chunk_bwd_varlen_workspace_size(int N, int total_T, int H, int dk, int dv, int dtype) {
+  return kda_chunk_bwd_varlen_window_workspace_size(N, total_T, H, dk, dv, dtype, 0);
 }
 
 // ---------------------------------------------------------------- context parallelism

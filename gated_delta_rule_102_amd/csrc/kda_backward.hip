@@ -43,7 +43,7 @@ __global__ __launch_bounds__(kScanThreads) void bwd_fwd_scan_kernel(const TIn* _
                                                            const float* __restrict__ ws,
                                                            float* __restrict__ st,
                                                            float* __restrict__ dl, SeqMap m,
-                                                           int BH) {
+                                                           int BH, float* __restrict__ s_end) {
   constexpr bool BF = IsBf16<TIn>::value;   // bf16 matrix-core operands for bf16 inputs
   using L = BwdLayout<D>;
   using ST = ScanTiles<D>;
@@ -129,6 +129,13 @@ __global__ __launch_bounds__(kScanThreads) void bwd_fwd_scan_kernel(const TIn* _
       S[x] = mmx<BF, true, false>(acc, KTs + 16 * rt, LD, Dls + 16 * ct, LV, CR);
     }
     __syncthreads();
+  }
+  if (s_end) {   // the state after the last chunk (a window's end, for the next window)
+#pragma unroll
+    for (int x = 0; x < ST::NTW; ++x) {
+      const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
+      put(s_end + static_cast<int64_t>(bh) * D * D + 16 * rt * D + c0 + 16 * ct, D, S[x]);
+    }
   }
   (void)l16;
 }
@@ -295,7 +302,7 @@ template <int D>
 __global__ __launch_bounds__(kScanThreads) void bwd_fwd_scan_bf16_kernel(
     const bf16_t* __restrict__ v, const float* __restrict__ s0, const float* __restrict__ ws,
     const __bf16* __restrict__ wsb, __bf16* __restrict__ st, __bf16* __restrict__ dl, SeqMap m,
-    int BH) {
+    int BH, float* __restrict__ s_end) {
   using L = BwdLayout<D>;
   using ST = ScanTiles<D>;
   constexpr int LB = D + 8, L64 = CR + 8;   // bf16 leading dimensions (16-byte rows)
@@ -378,6 +385,13 @@ __global__ __launch_bounds__(kScanThreads) void bwd_fwd_scan_bf16_kernel(
       S[x] = mmb<CR>(acc, KTT + 16 * rt * L64, L64, DT + 16 * ct * L64, L64);
     }
     __syncthreads();
+  }
+  if (s_end) {   // the state after the last chunk (a window's end, for the next window)
+#pragma unroll
+    for (int x = 0; x < ST::NTW; ++x) {
+      const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
+      put(s_end + static_cast<int64_t>(bh) * D * D + 16 * rt * D + c0 + 16 * ct, D, S[x]);
+    }
   }
 }
 
@@ -1083,6 +1097,12 @@ inline int64_t backward_items(const BackwardArgs& a) {
                                  : (static_cast<int64_t>(a.total_T + CR - 1) / CR + a.B) * a.H;
 }
 
+// Most chunks any sequence of the call can have (for packed input the lengths are on
+// the device: ceil(total_T / 64) bounds them).
+inline int backward_chunks_max(const BackwardArgs& a) {
+  return a.cu_seqlens == nullptr ? (a.T + CR - 1) / CR : (a.total_T + CR - 1) / CR;
+}
+
 // Floats of workspace per chunk item: the fp32 operands, then the states, state
 // gradients, Delta and dU (fp32, or bf16 for bf16 inputs: half the floats), then for
 // bf16 inputs the bf16 scan operands.
@@ -1093,17 +1113,47 @@ constexpr int64_t backward_floats_per_item() {
   return L::WS + (BF ? 1 : 2) * (D * D + CR * D) + (BF ? L::WSB / 2 : 0);
 }
 
+// Workspace bytes with windows of cw chunks (cw = 0: every chunk at once).  A window
+// holds its chunks' items, plus, over the call, the state at the start of every window
+// but the first and two state-gradient buffers.
+template <int D, typename TIn>
+size_t backward_bytes_t(const BackwardArgs& a, int cw) {
+  const int64_t items = cw == 0 ? backward_items(a) : static_cast<int64_t>(a.B) * a.H * cw;
+  int64_t floats = items * backward_floats_per_item<D, TIn>();
+  if (cw > 0) {
+    const int64_t nwin = (backward_chunks_max(a) + cw - 1) / cw;
+    floats += (nwin - 1 + 2) * a.B * a.H * D * D;
+  }
+  return static_cast<size_t>(floats) * sizeof(float);
+}
+
+size_t backward_bytes(const BackwardArgs& a, int cw) {
+  if (a.d == 128) return a.dtype_f32 ? backward_bytes_t<128, float>(a, cw) : backward_bytes_t<128, bf16_t>(a, cw);
+  return a.dtype_f32 ? backward_bytes_t<64, float>(a, cw) : backward_bytes_t<64, bf16_t>(a, cw);
+}
+
+// Windowed form of the backward (cw > 0 chunks per window, fewer than the longest
+// sequence has): a first pass walks the windows forwards, each computing its chunks'
+// operands and its forward scan from the state the previous window ended with, and
+// keeps only that end state; the second pass walks the windows backwards, recomputing
+// each window's operands and forward scan from its stored start state, then its
+// reverse scan (from the state gradient the later window left) and its gradients.
+// The result equals the one-pass backward's up to rounding; the workspace no longer
+// grows with the sequence but by one state per window.
 template <int D, typename TIn>
 hipError_t launch_backward_t(const BackwardArgs& a) {
   using L = BwdLayout<D>;
   const int nc = a.cu_seqlens == nullptr ? (a.T + CR - 1) / CR : 0;
   const SeqMap sm{a.cu_seqlens, a.B, a.T, a.cu_seqlens == nullptr ? a.B * a.T : a.total_T, a.H, nc};
-  const int64_t items = backward_items(a);
+  const int nc_max = backward_chunks_max(a);
+  const int cw = a.window_chunks > 0 && a.window_chunks < nc_max ? a.window_chunks : 0;
+  const int nwin = cw == 0 ? 1 : (nc_max + cw - 1) / cw;
+  const int64_t items = cw == 0 ? backward_items(a) : static_cast<int64_t>(a.B) * a.H * cw;
   constexpr bool BF = IsBf16<TIn>::value;
   const int64_t sdu = (BF ? 1 : 2) * (D * D + CR * D);
   char* raw = nullptr;
-  hipError_t err = ws_acquire(a.workspace, a.workspace_bytes,
-                              items * backward_floats_per_item<D, TIn>() * sizeof(float), a.stream, &raw);
+  hipError_t err = ws_acquire(a.workspace, a.workspace_bytes, backward_bytes_t<D, TIn>(a, cw),
+                              a.stream, &raw);
   if (err != hipSuccess) return err;
   float* ws = reinterpret_cast<float*>(raw);
   float* sreg = ws + items * L::WS;   // S, dS, Delta, dU in the element type chosen above
@@ -1117,36 +1167,63 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
   __bf16* dstb = stb + items * D * D;
   __bf16* dlb = dstb + items * D * D;
   __bf16* dub = dlb + items * CR * D;
+  const int BH = a.B * a.H;
+  const int64_t state = static_cast<int64_t>(D) * D;
+  float* ckpt = ws + items * backward_floats_per_item<D, TIn>();   // windows 1 .. nwin - 1
+  float* pp = ckpt + static_cast<int64_t>(nwin - 1) * BH * state;  // two dS buffers
   const TIn* q = static_cast<const TIn*>(a.q);
   const TIn* k = static_cast<const TIn*>(a.k);
   const TIn* v = static_cast<const TIn*>(a.v);
   const TIn* g = static_cast<const TIn*>(a.g);
   const TIn* beta = static_cast<const TIn*>(a.beta);
   const TIn* dout = static_cast<const TIn*>(a.d_out);
-  const int BH = a.B * a.H;
   const int scan_blocks = scan_grid(BH, D / SL);
-  KDA_TRY_LAUNCH(err, (chunk_ops_kernel<D, TIn, false, true>), dim3(items), dim3(kOpsThreads), 0,
-                 a.stream, q, k, g, beta, ws, wsb, sm, a.scale);
-  if constexpr (IsBf16<TIn>::value) {
-    KDA_TRY_LAUNCH(err, (bwd_fwd_scan_bf16_kernel<D>), dim3(scan_blocks), dim3(kScanThreads), 0,
-                   a.stream, v, a.initial_state, ws, wsb, stb, dlb, sm, BH);
-    KDA_TRY_LAUNCH(err, (bwd_scan_bf16_kernel<D>), dim3(scan_blocks), dim3(kScanThreads), 0,
-                   a.stream, dout, a.d_final_state, ws, wsb, dstb, dub,
-                   static_cast<TIn*>(a.dv), a.d_initial_state, sm, BH);
-    KDA_TRY_LAUNCH(err, (bwd_grad_chunk_kernel<D, TIn>), dim3(items), dim3(kNnThreads), 0, a.stream,
-                   q, k, beta, v, dout, stb, dstb, dlb, dub, ws, static_cast<TIn*>(a.dq),
-                   static_cast<TIn*>(a.dk), static_cast<TIn*>(a.dg), static_cast<TIn*>(a.dbeta),
-                   sm, a.scale);
+  const unsigned grid = static_cast<unsigned>(items);
+  // one window: operands and forward scan from s0 (end state to s_end if given); with
+  // `grads`, then the reverse scan from dsT (state gradient at its start to ds0) and
+  // the gradients
+  auto window = [&](const SeqMap& m, const float* s0, float* s_end, bool grads, const float* dsT,
+                    float* ds0) {
+    KDA_TRY_LAUNCH(err, (chunk_ops_kernel<D, TIn, false, true>), dim3(grid), dim3(kOpsThreads), 0,
+                   a.stream, q, k, g, beta, ws, wsb, m, a.scale);
+    if constexpr (IsBf16<TIn>::value) {
+      KDA_TRY_LAUNCH(err, (bwd_fwd_scan_bf16_kernel<D>), dim3(scan_blocks), dim3(kScanThreads), 0,
+                     a.stream, v, s0, ws, wsb, stb, dlb, m, BH, s_end);
+      if (!grads) return;
+      KDA_TRY_LAUNCH(err, (bwd_scan_bf16_kernel<D>), dim3(scan_blocks), dim3(kScanThreads), 0,
+                     a.stream, dout, dsT, ws, wsb, dstb, dub, static_cast<TIn*>(a.dv), ds0, m, BH);
+      KDA_TRY_LAUNCH(err, (bwd_grad_chunk_kernel<D, TIn>), dim3(grid), dim3(kNnThreads), 0, a.stream,
+                     q, k, beta, v, dout, stb, dstb, dlb, dub, ws, static_cast<TIn*>(a.dq),
+                     static_cast<TIn*>(a.dk), static_cast<TIn*>(a.dg), static_cast<TIn*>(a.dbeta),
+                     m, a.scale);
+    } else {
+      KDA_TRY_LAUNCH(err, (bwd_fwd_scan_kernel<D, TIn>), dim3(scan_blocks), dim3(kScanThreads), 0,
+                     a.stream, v, s0, ws, st, dl, m, BH, s_end);
+      if (!grads) return;
+      KDA_TRY_LAUNCH(err, (bwd_scan_kernel<D, TIn>), dim3(scan_blocks), dim3(kScanThreads), 0,
+                     a.stream, dout, dsT, ws, dst, du, static_cast<TIn*>(a.dv), ds0, m, BH);
+      KDA_TRY_LAUNCH(err, (bwd_grad_chunk_kernel<D, TIn>), dim3(grid), dim3(kNnThreads), 0, a.stream,
+                     q, k, beta, v, dout, st, dst, dl, du, ws, static_cast<TIn*>(a.dq),
+                     static_cast<TIn*>(a.dk), static_cast<TIn*>(a.dg), static_cast<TIn*>(a.dbeta),
+                     m, a.scale);
+    }
+  };
+  if (cw == 0) {
+    window(sm, a.initial_state, nullptr, true, a.d_final_state, a.d_initial_state);
   } else {
-    KDA_TRY_LAUNCH(err, (bwd_fwd_scan_kernel<D, TIn>), dim3(scan_blocks), dim3(kScanThreads), 0,
-                   a.stream, v, a.initial_state, ws, st, dl, sm, BH);
-    KDA_TRY_LAUNCH(err, (bwd_scan_kernel<D, TIn>), dim3(scan_blocks), dim3(kScanThreads), 0, a.stream,
-                   dout, a.d_final_state, ws, dst, du, static_cast<TIn*>(a.dv), a.d_initial_state,
-                   sm, BH);
-    KDA_TRY_LAUNCH(err, (bwd_grad_chunk_kernel<D, TIn>), dim3(items), dim3(kNnThreads), 0, a.stream,
-                   q, k, beta, v, dout, st, dst, dl, du, ws, static_cast<TIn*>(a.dq),
-                   static_cast<TIn*>(a.dk), static_cast<TIn*>(a.dg), static_cast<TIn*>(a.dbeta),
-                   sm, a.scale);
+    auto wmap = [&](int w) {
+      SeqMap m = sm;
+      m.c_lo = w * cw;
+      m.cw = cw;
+      return m;
+    };
+    auto start = [&](int w) -> const float* { return w == 0 ? a.initial_state : ckpt + (w - 1) * BH * state; };
+    for (int w = 0; w + 1 < nwin && err == hipSuccess; ++w)
+      window(wmap(w), start(w), ckpt + static_cast<int64_t>(w) * BH * state, false, nullptr, nullptr);
+    for (int w = nwin - 1; w >= 0 && err == hipSuccess; --w)
+      window(wmap(w), start(w), nullptr, true,
+             w == nwin - 1 ? a.d_final_state : pp + static_cast<int64_t>((w + 1) & 1) * BH * state,
+             w == 0 ? a.d_initial_state : pp + static_cast<int64_t>(w & 1) * BH * state);
   }
   const hipError_t ferr = ws_release(a.workspace, raw, a.stream);
   return err != hipSuccess ? err : ferr;
@@ -1155,11 +1232,16 @@ hipError_t launch_backward_t(const BackwardArgs& a) {
 }  // namespace
 
 size_t backward_workspace_bytes(const BackwardArgs& a) {
-  const int64_t items = backward_items(a);
-  int64_t per = 0;
-  if (a.d == 128) per = a.dtype_f32 ? backward_floats_per_item<128, float>() : backward_floats_per_item<128, bf16_t>();
-  else per = a.dtype_f32 ? backward_floats_per_item<64, float>() : backward_floats_per_item<64, bf16_t>();
-  return static_cast<size_t>(items * per) * sizeof(float);
+  const int nc_max = backward_chunks_max(a);
+  return backward_bytes(a, a.window_chunks > 0 && a.window_chunks < nc_max ? a.window_chunks : 0);
+}
+
+int backward_fit_window(const BackwardArgs& a, size_t bytes) {
+  const int nc_max = backward_chunks_max(a);
+  if (bytes >= backward_bytes(a, 0)) return 0;
+  for (int cw = nc_max - 1; cw >= 1; --cw)
+    if (backward_bytes(a, cw) <= bytes) return cw;
+  return -1;
 }
 
 hipError_t launch_backward(const BackwardArgs& a) {

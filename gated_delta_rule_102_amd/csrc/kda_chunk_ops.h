@@ -378,9 +378,13 @@ __device__ __forceinline__ int pair_index(int I, int J) { return I * (I - 1) / 2
 // (n, h) is item (n * H + h) * nc + c), or N packed sequences whose tokens are
 // [cu[n], cu[n+1]) of total_T (clamped into [0, total_T]; chunk c of stream (n, h)
 // is item (floor(cu[n] / 64) + n + c) * H + h, ranges that never overlap).
+// A window (cw > 0) restricts every sequence to its chunks c_lo .. c_lo + cw - 1 and
+// numbers the items window-locally: chunk c_lo + l of stream (n, h) is item
+// (n * H + h) * cw + l for fixed length, (n * cw + l) * H + h for packed input.
 struct SeqMap {
   const int32_t* cu;
   int N, T, total_T, H, nc;
+  int c_lo = 0, cw = 0;
 };
 
 __device__ __forceinline__ void seq_span(const SeqMap& m, int n, int& tok0, int& len) {
@@ -395,7 +399,8 @@ __device__ __forceinline__ void seq_span(const SeqMap& m, int n, int& tok0, int&
   }
 }
 
-// Stream bh = n * H + h: its tokens, chunk count, and the items of its chunks.
+// Stream bh = n * H + h: its tokens, chunk count, and the items of its chunks (in a
+// window: the tokens of the window's chunks only).
 struct StreamPos {
   int tok0, len, nch;
   int64_t item0, istride;   // item of chunk c: item0 + c * istride
@@ -404,6 +409,15 @@ __device__ __forceinline__ StreamPos stream_pos(const SeqMap& m, int bh) {
   StreamPos s;
   const int n = bh / m.H, h = bh - n * m.H;
   seq_span(m, n, s.tok0, s.len);
+  if (m.cw > 0) {
+    const int skip = min(s.len, m.c_lo * CR);
+    s.tok0 += skip;
+    s.len = min(s.len - skip, m.cw * CR);
+    s.nch = (s.len + CR - 1) / CR;
+    s.item0 = m.cu == nullptr ? static_cast<int64_t>(bh) * m.cw : static_cast<int64_t>(n) * m.cw * m.H + h;
+    s.istride = m.cu == nullptr ? 1 : m.H;
+    return s;
+  }
   s.nch = (s.len + CR - 1) / CR;
   if (m.cu == nullptr) {
     s.item0 = static_cast<int64_t>(bh) * m.nc;
@@ -423,6 +437,28 @@ struct ChunkPos {
 __device__ __forceinline__ ChunkPos chunk_pos(int item, const SeqMap& m) {
   ChunkPos p;
   const int H = m.H;
+  if (m.cw > 0) {   // window: items are (stream, local chunk), the chunk may lie past the end
+    int n, l;
+    if (m.cu == nullptr) {
+      l = item % m.cw;
+      const int bh = item / m.cw;
+      n = bh / H;
+      p.h = bh - n * H;
+    } else {
+      const int slot = item / H;
+      p.h = item - slot * H;
+      n = slot / m.cw;
+      l = slot - n * m.cw;
+    }
+    int t0, len;
+    seq_span(m, n, t0, len);
+    p.b = n;
+    p.c = m.c_lo + l;
+    p.valid = p.c * CR < len;
+    p.nrow = p.valid ? min(CR, len - p.c * CR) : 0;
+    p.row0 = (static_cast<int64_t>(t0) + static_cast<int64_t>(p.c) * CR) * H + p.h;
+    return p;
+  }
   if (m.cu == nullptr) {
     p.c = item % m.nc;
     const int bh = item / m.nc;

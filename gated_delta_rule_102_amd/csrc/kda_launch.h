@@ -56,6 +56,7 @@ struct BackwardArgs {
   int total_T = 0;                       // tokens in the packed buffers
   void* workspace = nullptr;             // caller's workspace (null: the call takes a block)
   size_t workspace_bytes = 0;
+  int window_chunks = 0;                 // > 0: run in windows of this many chunks
 };
 
 struct TransitionArgs {
@@ -83,6 +84,9 @@ hipError_t launch_compose(const ComposeArgs& a);
 hipError_t launch_backward(const BackwardArgs& a);
 // Workspace bytes launch_backward / launch_transition need for these arguments.
 size_t backward_workspace_bytes(const BackwardArgs& a);
+// Largest window (chunks) whose backward workspace fits in `bytes`: 0 when the whole
+// call fits, -1 when not even one-chunk windows do.
+int backward_fit_window(const BackwardArgs& a, size_t bytes);
 size_t transition_workspace_bytes(const TransitionArgs& a);
 
 hipError_t launch_prefill(const PrefillArgs& a);

@@ -27,8 +27,9 @@ EXPORTS = ("kda_abi_version", "kda_status_string", "kda_chunk_fwd_schedule",
            "kda_chunk_fwd_prologue", "kda_chunk_fwd_snapshots",
            "kda_chunk_fwd_varlen", "kda_chunk_fwd_varlen_workspace_size", "kda_chunk_fwd_varlen_ws",
            "kda_chunk_fwd_varlen_prologue", "kda_chunk_fwd_varlen_snapshots",
-           "kda_chunk_bwd", "kda_chunk_bwd_workspace_size", "kda_chunk_bwd_ws",
-           "kda_chunk_bwd_varlen", "kda_chunk_bwd_varlen_workspace_size", "kda_chunk_bwd_varlen_ws",
+           "kda_chunk_bwd", "kda_chunk_bwd_workspace_size", "kda_chunk_bwd_window_workspace_size",
+           "kda_chunk_bwd_ws", "kda_chunk_bwd_varlen", "kda_chunk_bwd_varlen_workspace_size",
+           "kda_chunk_bwd_varlen_window_workspace_size", "kda_chunk_bwd_varlen_ws",
            "kda_chunk_transition", "kda_chunk_transition_workspace_size", "kda_chunk_transition_ws",
            "kda_state_compose", "kda_decode_step", "kda_decode_step_prologue")
 
@@ -91,10 +92,14 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd_varlen_ws.restype = i32
     lib.kda_chunk_bwd_workspace_size.argtypes = [i32] * 6
     lib.kda_chunk_bwd_workspace_size.restype = sz
+    lib.kda_chunk_bwd_window_workspace_size.argtypes = [i32] * 7
+    lib.kda_chunk_bwd_window_workspace_size.restype = sz
     lib.kda_chunk_bwd_ws.argtypes = [vp] * 14 + [i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
     lib.kda_chunk_bwd_ws.restype = i32
     lib.kda_chunk_bwd_varlen_workspace_size.argtypes = [i32] * 6
     lib.kda_chunk_bwd_varlen_workspace_size.restype = sz
+    lib.kda_chunk_bwd_varlen_window_workspace_size.argtypes = [i32] * 7
+    lib.kda_chunk_bwd_varlen_window_workspace_size.restype = sz
     lib.kda_chunk_bwd_varlen_ws.argtypes = [vp] * 15 + [i32, i32, i32, i32, i32, f32, i32, vp, sz,
                                                         vp]
     lib.kda_chunk_bwd_varlen_ws.restype = i32
@@ -602,20 +607,25 @@ def kda_chunk_bwd(q, k, v, g, beta, grad_out, scale=None, initial_state=None,
     return (*grads, ds0)
 
 
-def chunk_bwd_workspace(q, v):
-    """Workspace tensor for kda_chunk_bwd calls shaped like (q [B,T,H,dk], v)."""
+def chunk_bwd_workspace(q, v, window_chunks=0):
+    """Workspace tensor for kda_chunk_bwd calls shaped like (q [B,T,H,dk], v): the
+    one-pass size, or with ``window_chunks`` > 0 the size of windows of that many chunks
+    (a call given it runs in such windows)."""
     B, T, H, dk = q.shape
-    n = load_library().kda_chunk_bwd_workspace_size(B, T, H, dk, v.shape[-1], _dtype_code(q))
+    n = load_library().kda_chunk_bwd_window_workspace_size(B, T, H, dk, v.shape[-1], _dtype_code(q),
+                                                           int(window_chunks))
     if n == 0:
         raise ValueError("backward sizes not accepted by the library")
     return _ws_tensor(n, q.device)
 
 
-def chunk_bwd_varlen_workspace(q, v, cu_seqlens):
-    """Workspace tensor for kda_chunk_bwd_varlen calls shaped like (q, v, cu_seqlens)."""
+def chunk_bwd_varlen_workspace(q, v, cu_seqlens, window_chunks=0):
+    """Workspace tensor for kda_chunk_bwd_varlen calls shaped like (q, v, cu_seqlens),
+    one-pass or for windows of ``window_chunks`` chunks."""
     H, dk = q.shape[-2], q.shape[-1]
-    n = load_library().kda_chunk_bwd_varlen_workspace_size(
-        cu_seqlens.numel() - 1, q.numel() // (H * dk), H, dk, v.shape[-1], _dtype_code(q))
+    n = load_library().kda_chunk_bwd_varlen_window_workspace_size(
+        cu_seqlens.numel() - 1, q.numel() // (H * dk), H, dk, v.shape[-1], _dtype_code(q),
+        int(window_chunks))
     if n == 0:
         raise ValueError("backward sizes not accepted by the library")
     return _ws_tensor(n, q.device)

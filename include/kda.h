@@ -354,9 +354,11 @@ int kda_chunk_fwd_varlen_snapshots(const void* q, const void* k, const void* v, 
  * bf16 operands rounded from fp32 values, with fp32 accumulation, and the
  * per-chunk states, state gradients, Delta and dU are kept as bf16; the inverse,
  * the 16-term sub-tile products and the decayed products stay fp32.  The call's
- * workspace (kda_chunk_bwd_workspace_size) takes, per 64-token chunk per head,
- * 418,304 bytes for bf16 and 410,112 for fp32 at d = 128 (246,016 and 213,248 at
- * d = 64), so T = 65,536 with 32 heads needs about 14 GB.
+ * one-pass workspace (kda_chunk_bwd_workspace_size) takes, per 64-token chunk per
+ * head, 418,304 bytes for bf16 and 410,112 for fp32 at d = 128 (246,016 and 213,248
+ * at d = 64), so T = 65,536 with 32 heads would need about 14 GB: this call takes at
+ * most 2 GiB and runs in windows of chunks beyond that (see
+ * kda_chunk_bwd_window_workspace_size).
  * Outputs must not alias inputs.
  */
 int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, const void* beta,
@@ -369,9 +371,25 @@ int kda_chunk_bwd(const void* q, const void* k, const void* v, const void* g, co
 size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int dk, int dv, int dtype);
 
 /*
- * kda_chunk_bwd on a caller workspace of at least kda_chunk_bwd_workspace_size
- * bytes (256-byte aligned, else KDA_ERR_WORKSPACE): same arguments and results,
- * allocates nothing.
+ * Workspace bytes of kda_chunk_bwd run in windows of window_chunks 64-token chunks
+ * (0: no windows, the same as kda_chunk_bwd_workspace_size; 0 returned for sizes not
+ * accepted or a negative window).  In windows the call keeps one window's chunk items
+ * plus one [B, H, dk, dv] fp32 state per window and two state-gradient buffers, so the
+ * workspace no longer grows by a chunk's items per 64 tokens (training at long
+ * contexts, best.xiaohu.ai "Kimi K3 tech report", context-curriculum section); the
+ * cost is a second pass over each window's operands and forward scan.
+ */
+size_t kda_chunk_bwd_window_workspace_size(int B, int T, int H, int dk, int dv, int dtype,
+                                           int window_chunks);
+
+/*
+ * kda_chunk_bwd on a caller workspace (256-byte aligned): same arguments and results,
+ * allocates nothing.  With at least kda_chunk_bwd_workspace_size bytes the call runs
+ * in one pass; with less it runs in the largest windows whose
+ * kda_chunk_bwd_window_workspace_size fits (results equal to the one-pass call's,
+ * bit for bit); below the one-chunk-window size it returns KDA_ERR_WORKSPACE.  The
+ * self-allocating kda_chunk_bwd (and kda_chunk_bwd_varlen) take at most 2 GiB and
+ * run in windows beyond that.
  */
 int kda_chunk_bwd_ws(const void* q, const void* k, const void* v, const void* g, const void* beta,
                      const float* initial_state, const void* grad_out,
@@ -404,7 +422,13 @@ int kda_chunk_bwd_varlen(const void* q, const void* k, const void* v, const void
 /* Workspace bytes of kda_chunk_bwd_varlen for these sizes (0: sizes not accepted). */
 size_t kda_chunk_bwd_varlen_workspace_size(int N, int total_T, int H, int dk, int dv, int dtype);
 
-/* kda_chunk_bwd_varlen on a caller workspace, as kda_chunk_bwd_ws is to kda_chunk_bwd. */
+/* kda_chunk_bwd_window_workspace_size for kda_chunk_bwd_varlen (windows count chunks
+ * from each sequence's start; ceil(total_T / 64) bounds every sequence's chunks). */
+size_t kda_chunk_bwd_varlen_window_workspace_size(int N, int total_T, int H, int dk, int dv,
+                                                  int dtype, int window_chunks);
+
+/* kda_chunk_bwd_varlen on a caller workspace, as kda_chunk_bwd_ws is to kda_chunk_bwd
+ * (windows as there). */
 int kda_chunk_bwd_varlen_ws(const void* q, const void* k, const void* v, const void* g,
                             const void* beta, const float* initial_state, const void* grad_out,
                             const float* grad_final_state, void* grad_q, void* grad_k,

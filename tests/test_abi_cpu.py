@@ -293,6 +293,12 @@ def test_caller_workspace_sizes_and_checks(lib):
     assert bw(*ok, 1, 64, 1, 128, 128, 0.1, 0, vp(4096 + 64), big, None) == -8
     assert bw(*ok, 1, 64, 1, 128, 128, 0.1, 0, p, 4096, None) == -8
     assert bw(*ok, 1, 64, 1, 128, 128, 0.1, 0, p, big, None) in (-6, -7)
+    # a workspace below the one-pass size but above the one-chunk-window size is
+    # accepted (the call runs in windows and reaches the device check)
+    small = L.kda_chunk_bwd_window_workspace_size(1, 640, 1, 128, 128, 0, 1)
+    assert 0 < small < L.kda_chunk_bwd_workspace_size(1, 640, 1, 128, 128, 0)
+    assert bw(*ok, 1, 640, 1, 128, 128, 0.1, 0, p, small, None) in (-6, -7)
+    assert bw(*ok, 1, 640, 1, 128, 128, 0.1, 0, p, small - 256, None) == -8
     tw = L.kda_chunk_transition_ws
     assert tw(p, p, p, p, p, 1, 64, 1, 128, 128, 0, p, 100, None) == -8
     assert tw(p, p, p, p, p, 1, 64, 1, 128, 128, 0, p, big, None) in (-6, -7)
@@ -339,3 +345,31 @@ def test_noalloc_refuses_sizes_beyond_its_scratch(lib):
                                    None) in (-6, -7)
     assert L.kda_chunk_fwd_noalloc(None, p, p, p, p, None, p, None, 4, 4096, 16, 128, 128, 0.1, 0,
                                    None) == -1
+
+
+def test_backward_window_workspace_sizes(lib):
+    """Windowed backward workspace: one window's chunk items (B H cw of them, the
+    per-item bytes of the one-pass form) plus one [B, H, d, d] fp32 state per window
+    after the first and two state-gradient buffers; window 0, or one as long as the
+    longest sequence, is the one-pass size; a negative window is refused (0)."""
+    from gated_delta_rule_102_amd import kda
+    kda.load_library()
+    L = kda._lib
+    item, state = 418304, 128 * 128 * 4
+    B, T, H = 1, 65536, 32
+    full = L.kda_chunk_bwd_workspace_size(B, T, H, 128, 128, 0)
+    assert full == B * H * (T // 64) * item
+    for cw in (1, 16, 64, 256):
+        nwin = (T // 64 + cw - 1) // cw
+        assert L.kda_chunk_bwd_window_workspace_size(B, T, H, 128, 128, 0, cw) == \
+            B * H * cw * item + (nwin - 1 + 2) * B * H * state
+    assert L.kda_chunk_bwd_window_workspace_size(B, T, H, 128, 128, 0, 0) == full
+    assert L.kda_chunk_bwd_window_workspace_size(B, T, H, 128, 128, 0, T // 64) == full
+    assert L.kda_chunk_bwd_window_workspace_size(B, T, H, 128, 128, 0, -1) == 0
+    # 64-chunk windows at 65,536 tokens and 32 heads: under 1 GB instead of 14 GB
+    assert L.kda_chunk_bwd_window_workspace_size(B, T, H, 128, 128, 0, 64) < 1 << 30
+    # packed: windows count each sequence's chunks; ceil(total_T / 64) bounds them
+    N, tot = 3, 1000
+    nwin = ((tot + 63) // 64 + 3) // 4
+    assert L.kda_chunk_bwd_varlen_window_workspace_size(N, tot, 2, 128, 128, 0, 4) == \
+        N * 2 * 4 * item + (nwin - 1 + 2) * N * 2 * state
