@@ -434,7 +434,19 @@ def extras(torch, kin, kda, timer, result, args, only=""):
             "flop_convention": "3 x the forward's triangle-aware count (recompute + two "
                                "products per forward product), against the bf16 peak",
         }
-        del bset, cot
+        # the same gradients run in windows of 16 chunks on a caller workspace (the form
+        # a long-context training step takes when the one-pass workspace does not fit)
+        cw = 16
+        wsw = kda.chunk_bwd_workspace(bset["q"], bset["v"], window_chunks=cw)
+        msw = statistics.median(timer.reps(lambda: kda.kda_chunk_bwd(
+            bset["q"], bset["k"], bset["v"], bset["g"], bset["beta"], cot["grad_out"], scale,
+            bset["initial_state"], cot["grad_final_state"], workspace=wsw), nreps))
+        result["backward"]["windowed"] = {
+            "window_chunks": cw, "call_ms_median": msw,
+            "workspace_bytes": int(wsw.numel()) - 256,
+            "one_pass_workspace_bytes": int(kda.chunk_bwd_workspace(bset["q"], bset["v"]).numel()) - 256,
+        }
+        del bset, cot, wsw
         torch.cuda.empty_cache()
 
     if not only or only == "context":
