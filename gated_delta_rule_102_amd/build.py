@@ -25,8 +25,8 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
-SOURCES = ["kda_prefill.hip", "kda_fused.hip", "kda_decode.hip", "kda_backward.hip",
-           "kda_context.hip", "kda_noalloc.hip"]
+SOURCES = ["kda_prefill.hip", "kda_fused.hip", "kda_prefill_fp32.hip", "kda_decode.hip",
+           "kda_backward.hip", "kda_context.hip", "kda_noalloc.hip"]
 HOST_SOURCES = ["kda_api.cpp"]
 
 

@@ -84,7 +84,10 @@ int check_sizes(bool packed, int N, int T, int total_T, int H) {
 int check_prefill(const kda_prefill_desc& d) {
   int rc = check_common(d.dk, d.dv, d.H, d.dtype);
   if (rc != KDA_OK) return rc;
-  if (d.dtype == KDA_F32 && d.dk != 64) return KDA_ERR_HEAD_DIM;
+  // fp32 at d = 128 has the plain forms only (no gate prologue, no snapshots)
+  if (d.dtype == KDA_F32 && d.dk != 64 && (d.prologue != 0 || d.snapshots != nullptr ||
+                                           d.snapshot_tokens != 0))
+    return KDA_ERR_HEAD_DIM;
   const bool packed = d.cu_seqlens != nullptr;
   rc = check_sizes(packed, d.N, d.T, d.total_T, d.H);
   if (rc != KDA_OK) return rc;
@@ -122,7 +125,15 @@ int run_prefill(const kda_prefill_desc& d, bool caller_ws, void* workspace,
   int rc = check_prefill(d);
   if (rc != KDA_OK) return rc;
   kda::PrefillArgs a = prefill_args(d, stream);
-  if (caller_ws) {
+  if (caller_ws && kda::exact_prefill_path(a)) {
+    // fp32 at d = 128 runs in windows of chunks: the largest that fit the workspace
+    if (workspace == nullptr || !aligned(workspace, 256)) return KDA_ERR_WORKSPACE;
+    const int cw = kda::prefill_fit_window(a, workspace_bytes);
+    if (cw <= 0) return KDA_ERR_WORKSPACE;
+    a.window_chunks = cw;
+    a.workspace = workspace;
+    a.workspace_bytes = workspace_bytes;
+  } else if (caller_ws) {
     const size_t need = kda::prefill_workspace_bytes(a);
     if (need > 0 && (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < need))
       return KDA_ERR_WORKSPACE;
@@ -161,7 +172,6 @@ kda_prefill_desc packed_desc(const void* q, const void* k, const void* v, const 
 // call with offsets would report them, else KDA_ERR_NULL.
 int packed_without_offsets(int N, int total_T, int H, int dk, int dv, int dtype) {
   int rc = check_common(dk, dv, H, dtype);
-  if (rc == KDA_OK && dtype == KDA_F32 && dk != 64) rc = KDA_ERR_HEAD_DIM;
   if (rc == KDA_OK) rc = check_sizes(true, N, 0, total_T, H);
   return rc != KDA_OK ? rc : KDA_ERR_NULL;
 }
@@ -331,7 +341,8 @@ const char* kda_status_string(int status) {
     case KDA_OK: return "ok";
     case KDA_ERR_NULL: return "a required pointer is NULL";
     case KDA_ERR_SHAPE: return "a size is non-positive or too large";
-    case KDA_ERR_HEAD_DIM: return "dk and dv must be equal and 64 or 128 (64 for fp32 prefill)";
+    case KDA_ERR_HEAD_DIM:
+      return "dk and dv must be equal and 64 or 128 (64 for the fp32 prologue and snapshot forms)";
     case KDA_ERR_DTYPE: return "dtype must be KDA_BF16 or KDA_F32";
     case KDA_ERR_ALIGN: return "a pointer is not aligned as required";
     case KDA_ERR_HIP: return "the HIP runtime reported an error";

@@ -84,6 +84,13 @@ hipError_t launch_compose(const ComposeArgs& a);
 hipError_t launch_backward(const BackwardArgs& a);
 // Workspace bytes launch_backward / launch_transition need for these arguments.
 size_t backward_workspace_bytes(const BackwardArgs& a);
+// fp32 prefill at d = 128 (kda_prefill_fp32.hip): chunk operands of kda_chunk_ops.h
+// and a scan that writes the outputs, in windows of chunks.
+bool exact_prefill_path(const PrefillArgs& a);
+size_t exact_prefill_workspace_bytes(const PrefillArgs& a);
+int exact_prefill_fit_window(const PrefillArgs& a, size_t bytes);
+const char* exact_prefill_schedule(const PrefillArgs& a);
+hipError_t launch_exact_prefill(const PrefillArgs& a);
 // Largest window (chunks) whose backward workspace fits in `bytes`: 0 when the whole
 // call fits, -1 when not even one-chunk windows do.
 int backward_fit_window(const BackwardArgs& a, size_t bytes);

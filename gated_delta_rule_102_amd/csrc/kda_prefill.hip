@@ -1557,6 +1557,7 @@ int fit_window(const PrefillArgs& a, size_t max_bytes) {
 }
 
 int prefill_fit_window(const PrefillArgs& a, size_t max_bytes) {
+  if (exact_prefill_path(a)) return exact_prefill_fit_window(a, max_bytes);
   if (a.cu_seqlens != nullptr || a.T <= 0) return 0;
   if (a.dtype_f32) return a.d == 64 ? fit_window<64, float>(a, max_bytes) : 0;
   if (a.d == 128) return fit_window<128, bf16_t>(a, max_bytes);
@@ -1564,6 +1565,7 @@ int prefill_fit_window(const PrefillArgs& a, size_t max_bytes) {
 }
 
 size_t prefill_workspace_bytes(const PrefillArgs& a) {
+  if (exact_prefill_path(a)) return exact_prefill_workspace_bytes(a);
   if (a.dtype_f32) return a.d == 64 ? workspace_bytes<64, float>(a) : 0;
   if (a.d == 128) return workspace_bytes<128, bf16_t>(a);
   return workspace_bytes<64, bf16_t>(a);
@@ -1571,6 +1573,7 @@ size_t prefill_workspace_bytes(const PrefillArgs& a) {
 
 const char* prefill_schedule(const PrefillArgs& a) {
   if (use_fused(a)) return "fused_prefill_kernel (one workgroup per (sequence, head))";
+  if (exact_prefill_path(a)) return exact_prefill_schedule(a);
   const bool f32 = a.dtype_f32;
   const int D = a.d;
   const int cg = prefill_cg(a);
@@ -1598,7 +1601,7 @@ const char* prefill_schedule(const PrefillArgs& a) {
 hipError_t launch_prefill(const PrefillArgs& a) {
   if (a.dtype_f32) {
     if (a.d == 64) return launch_all<64, float>(a);
-    return hipErrorNotSupported;
+    return launch_exact_prefill(a);
   }
   if (a.d == 128) return use_fused(a) ? launch_fused_prefill(a) : launch_all<128, bf16_t>(a);
   return launch_all<64, bf16_t>(a);

@@ -85,8 +85,8 @@ enum kda_status {
   KDA_OK = 0,
   KDA_ERR_NULL = -1,        /* a required pointer is NULL                    */
   KDA_ERR_SHAPE = -2,       /* a size is <= 0, or too large for 32-bit grids */
-  KDA_ERR_HEAD_DIM = -3,    /* dk or dv not in {64, 128}, dk != dv, or fp32
-                               prefill with dk != 64                        */
+  KDA_ERR_HEAD_DIM = -3,    /* dk or dv not in {64, 128}, dk != dv, or the
+                               fp32 prologue / snapshot prefill at dk = 128 */
   KDA_ERR_DTYPE = -4,       /* dtype is not KDA_BF16 or KDA_F32              */
   KDA_ERR_ALIGN = -5,       /* a pointer is not aligned as required          */
   KDA_ERR_HIP = -6,         /* the HIP runtime reported a launch error       */
@@ -111,8 +111,11 @@ const char* kda_status_string(int status);
  *  final_state    [B, H, dk, dv] fp32, or NULL to skip; may equal
  *                 initial_state (updated in place)
  *  scale          multiplies q (typically 1/sqrt(dk))
- * dk == dv, both 64 or 128 (KDA_F32: 64 only).  Produces the same result as
- * running the recurrence token by token, up to floating-point rounding.
+ * dk == dv, both 64 or 128.  Produces the same result as running the recurrence
+ * token by token, up to floating-point rounding.  KDA_F32 at d = 128 runs on fp32
+ * chunk operands (the backward's) in windows of up to 16 chunks, one fp32 state per
+ * (sequence, head) carried between windows; its gate-prologue and snapshot forms
+ * are not provided (KDA_ERR_HEAD_DIM).
  */
 int kda_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
                   const void* beta, const float* initial_state, void* out,

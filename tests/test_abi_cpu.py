@@ -65,8 +65,10 @@ def test_argument_checks_precede_any_device_call(lib):
     assert f(None, p, p, p, p, None, p, None, 1, 64, 1, 128, 128, 0.1, 0, None) == -1
     assert f(p, p, p, p, p, None, p, None, 0, 64, 1, 128, 128, 0.1, 0, None) == -2
     assert f(p, p, p, p, p, None, p, None, 1, 64, 1, 100, 100, 0.1, 0, None) == -3
-    assert f(p, p, p, p, p, None, p, None, 1, 64, 1, 128, 128, 0.1, 1, None) == -3
+    assert f(p, p, p, p, p, None, p, None, 1, 64, 1, 128, 64, 0.1, 1, None) == -3
     assert f(p, p, p, p, p, None, p, None, 1, 64, 1, 128, 128, 0.1, 9, None) == -4
+    # fp32 at d = 128 is a valid plain prefill (it reaches the device check)
+    assert f(p, p, p, p, p, None, p, None, 1, 64, 1, 128, 128, 0.1, 1, None) in (-6, -7)
     assert f(mis, p, p, p, p, None, p, None, 1, 64, 1, 128, 128, 0.1, 0, None) == -5
     # valid arguments reach the device check, which fails without a gfx950 device
     assert f(p, p, p, p, p, None, p, None, 1, 64, 1, 128, 128, 0.1, 0, None) in (-6, -7)
@@ -194,7 +196,10 @@ def test_workspace_size_is_host_arithmetic(lib):
     assert f(4, 4096, 16, 128, 128, 0) == (4 * 4096 // 64 + 4) * 16 * 66048
     assert f(1, 4096, 16, 128, 128, 0) == 2 * 1 * 16 * 16 * 66048 + 16 * 128 * 128 * 4
     assert f(2, 64, 3, 128, 128, 0) == 2 * 3 * 66048
-    assert f(1, 64, 1, 128, 128, 1) == 0     # fp32 prefill is d = 64 only
+    # fp32 at d = 128: windows of up to 16 chunks of fp32 chunk operands (213,504 B per
+    # chunk and head) plus the state carried between windows
+    assert f(1, 64, 1, 128, 128, 1) == 213504 + 128 * 128 * 4
+    assert f(2, 2000, 3, 128, 128, 1) == 6 * 16 * 213504 + 6 * 128 * 128 * 4
     assert f(1, 64, 1, 100, 100, 0) == 0
     assert f(0, 64, 1, 128, 128, 0) == 0
     assert f(1, 64, 1, 64, 64, 1) > 0
@@ -321,7 +326,9 @@ def test_prefill_descriptor_checks(lib):
     for bad, code in ((dict(dk=96, dv=96), -3), (dict(N=0), -2), (dict(dtype=7), -4),
                       (dict(q=4098), -5), (dict(v=4104), -5), (dict(out=None), -1),
                       (dict(snapshot_tokens=100, snapshots=4096), -2),
-                      (dict(snapshot_tokens=512), -1), (dict(dtype=1), -3)):
+                      (dict(snapshot_tokens=512), -1),
+                      (dict(dtype=1, snapshot_tokens=512, snapshots=4096), -3),
+                      (dict(dtype=1, prologue=1), -3)):
         dd = kda.PrefillDesc(**{**base, **bad})
         assert L.kda_prefill_workspace_size(ctypes.byref(dd), ctypes.byref(n)) == code, bad
         assert L.kda_prefill(ctypes.byref(dd), ctypes.c_void_p(4096), 1 << 40, None) == code, bad

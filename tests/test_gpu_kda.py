@@ -266,7 +266,7 @@ def test_abi_error_codes_launch_nothing():
     assert f(p, p, p, p, p, None, po, None, 0, 64, 2, 128, 128, 0.1, 0, s) == -2
     assert f(p, p, p, p, p, None, po, None, 2, 64, 2, 96, 96, 0.1, 0, s) == -3
     assert f(p, p, p, p, p, None, po, None, 2, 64, 2, 128, 64, 0.1, 0, s) == -3
-    assert f(p, p, p, p, p, None, po, None, 2, 64, 2, 128, 128, 0.1, 1, s) == -3
+    assert f(p, p, p, p, p, None, po, None, 2, 64, 2, 64, 128, 0.1, 1, s) == -3
     assert f(p, p, p, p, p, None, po, None, 2, 64, 2, 128, 128, 0.1, 5, s) == -4
     assert f(mis, p, p, p, p, None, po, None, 2, 64, 2, 128, 128, 0.1, 0, s) == -5
     assert lib.kda_decode_step(p, p, p, p, p, None, po, 2, 2, 128, 128, 0.1, 0, s) == -1
