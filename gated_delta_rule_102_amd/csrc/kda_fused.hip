@@ -27,35 +27,35 @@
 // bf16 range; off-diagonal sub-tile pairs (I > J) scale the column side of J by
 // e^{R_I - R_J} <= 1.
 //
-// Layout inside the workgroup (8 wavefronts):
-//  - Elementwise and sub-tile products: wavefront w owns rows 16 (w/2) .. +15 of the
-//    chunk and the key channels of 32-channel blocks 2 (w%2) and 2 (w%2) + 1; lane
-//    (r, g) holds row r and, in each block b, the 8 channels 32 b + 8 g .. +7 -- one
+// Two roles share the workgroup's 8 wavefronts, one of each on every SIMD (wavefront
+// w runs on SIMD w % 4), so that one role's vector-ALU work and the other's
+// matrix-core work issue side by side:
+//  - Operand wavefronts 0-3 build the operands of chunk c.  Wavefront I owns the
+//    chunk's rows 16 I .. +15 (sub-tile I) and all 128 key channels; lane (r, g)
+//    holds row r and, in each 32-channel block b, channels 32 b + 8 g .. +7 -- one
 //    operand fragment of v_mfma_f32_16x16x32_bf16, loaded with one 16-byte load.
-//  - State: wavefront w owns value columns 16 w .. +15 of S for all 128 key channels,
-//    as 8 accumulator tiles.  Accumulator row r holds key channel
+//  - State wavefronts 4-7 apply chunk c - 1 to the state.  Wavefront 4 + j owns value
+//    columns 32 j .. +31 of S for all 128 key channels, as two 16-column halves of 8
+//    accumulator tiles.  Accumulator row r holds key channel
 //        sigma(r) = 32 b + 8 g + 4 h + i   for r = 32 b + 16 h + 4 g + i,
 //    so that an accumulator tile pair (2 b, 2 b + 1) read as one operand fragment
 //    holds channels 32 b + 8 g .. +7 in order: the state feeds the products with the
 //    key-side operands with one conversion to bf16 and no transpose.  Products that
-//    contract over the chunk's tokens take X and Delta the same way, with the tokens
-//    of a 32-token block in the order 4 g + i, 16 + 4 g + i on both sides.
-//  - Delta = (I + A)^{-1} Diag(beta) X is a block forward substitution over the four
-//    16-token sub-tiles, in each wavefront for its own value columns (16x16x16
-//    products): Delta_i = T_ii (Y_i - sum_{m<i} A_im Delta_m), Y = Diag(beta) X, with
-//    the 16 x 16 inverses T_ii = (I + A_ii)^{-1} = (I - A)(I + A^2)(I + A^4)(I + A^8)
-//    (A_ii is strictly lower, so A^16 = 0).
-//  - The output is produced transposed (rows = value columns), so each lane holds 4
-//    consecutive values of one token's output row and writes them with one 8-byte
-//    store.  v is read the same way (4 consecutive values of a token row per lane)
-//    and brought into the accumulator layout by a product with the 16 x 16 identity.
-//  - Per chunk: the previous chunk's state step and this chunk's cumulative decay
-//    share the first barrier window; the products of the sub-tile pairs are summed
-//    over the two channel halves by the wavefront that finishes the pair (the
-//    diagonal pair and its inverse in one, the pairs J < I in the other).  Global
-//    traffic is spread over the chunk: the next chunk's q, k, g, beta right after the
-//    decay scan, the previous chunk's output in halves during the operand and the
-//    pair-product phases, the next v at the end.
+//    contract over the chunk's tokens take Delta and Kt^T with the tokens of a
+//    32-token block in the order 4 g + i, 16 + 4 g + i on both sides.
+// Every iteration has four barrier windows; iteration c runs
+//   A: operand: E2, the decayed operands of chunk c (Kb, Qb, Kt^T to LDS; the row and
+//      column sides of the sub-tile products kept in registers);
+//      state: chunk c - 1's output and state step (O = Qb S + M Delta, Delta by block
+//      forward substitution, S <- Lambda S + Kt^T Delta);
+//   B: operand: the decayed sub-tile products (A, M) of chunk c, then the cumulative
+//      log-decay of chunk c + 1;  state: X = Diag(beta)(V - Kb S) of chunk c;
+//   C: operand: per-channel decay factors of chunk c + 1;  state: the four 16 x 16
+//      diagonal inverses (I + A_II)^{-1} of chunk c, one per wavefront;
+//   D: nothing (the last window closes the factors).
+// Operands read by the state role one iteration after they were written (Qb, Kt^T,
+// Lambda, beta) alternate between two LDS copies by chunk parity; the rest are
+// written and read in windows that a barrier separates.
 
 #include "kda_device.h"
 #include "kda_launch.h"
@@ -71,20 +71,20 @@ constexpr int kThreadsF = 512;
 // LDS regions (bytes).  Fragment-ordered operands are [tile][block][lane][bytes].
 namespace fl {
 constexpr int KBN = 0;                      // -Kb       [4 t-tiles][4 c-blocks] x 16 B
-constexpr int QB = KBN + 16384;             // Qb        [4 t-tiles][4 c-blocks] x 16 B
-constexpr int KTT = QB + 16384;             // Kt^T      [8 state tiles][2 s-blocks] x 16 B
-constexpr int MF = KTT + 16384;             // M         [4 t-tiles][2 s-blocks] x 16 B
+constexpr int QB = KBN + 16384;             // Qb        [2 parities][4 t-tiles][4 c-blocks] x 16 B
+constexpr int KTT = QB + 2 * 16384;         // Kt^T      [2 parities][8 state tiles][2 s-blocks] x 16 B
+constexpr int MF = KTT + 2 * 16384;         // M         [4 t-tiles][2 s-blocks] x 16 B
 constexpr int AOF = MF + 8192;              // -A_IJ, J < I: [6][64 lanes] x 8 B (16x16x16 A)
 constexpr int TDF = AOF + 6 * 512;          // T_II:        [4][64 lanes] x 8 B
-constexpr int LAM = TDF + 4 * 512;          // Lambda, state row order [128] fp32
-constexpr int OFF = LAM + 512;              // column side of pair (I, J < I): [6][4][64][16]
-constexpr int PART = OFF + 6 * 4096;        // partial A^T, M^T of 10 pairs: [10][2][64][16]
-constexpr int TOT = PART + 10 * 2048;       // sub-tile decay totals [4][128] fp32
+constexpr int AII = TDF + 4 * 512;          // beta-scaled A_II^T, accumulator layout [4][64] x 16 B
+constexpr int LAM = AII + 4 * 1024;         // Lambda, state row order [2 parities][128] fp32
+constexpr int BETA = LAM + 2 * 512;         // [2 parities][64] fp32
+constexpr int OFF = BETA + 512;             // column side of pair (I, J < I): [6][4][64][16]
+constexpr int TOT = OFF + 6 * 4096;         // sub-tile decay totals [4][128] fp32
 constexpr int FAC = TOT + 4 * 128 * 4;      // per (sub-tile, channel) factors [4][3][128]
 constexpr int FOFF = FAC + 4 * 3 * 128 * 4; // e^{R_I - R_J}, I > J: [6][128]
-constexpr int BETA = FOFF + 6 * 128 * 4;    // [2 parities][64] fp32
-constexpr int ORD = BETA + 512;             // sequence order (packed input) [<= 256]
-constexpr int BYTES = ORD + 1024;
+constexpr int BYTES = FOFF + 6 * 128 * 4;
+constexpr int ORD = OFF;                    // sequence order (packed input) [<= 256], start only
 static_assert(BYTES <= 160 * 1024, "LDS budget");
 }  // namespace fl
 
@@ -122,7 +122,8 @@ __device__ __forceinline__ int frag_at(int tile, int blk, int nb, int lane) {
 
 // Workgroup barrier ordering LDS only: this wavefront's LDS operations complete, then
 // s_barrier.  (__syncthreads() also waits for every global load in flight, the next
-// chunk's prefetch and the loads whose destination is LDS included.)
+// chunk's prefetch included.)  The two roles run separate loops that pass the same
+// number of these barriers.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
@@ -180,26 +181,559 @@ __device__ __forceinline__ f32x4_t mma16(const bf16x4_t& a, const bf16x4_t& b, c
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-// Pair number of sub-tile pair (I, J), J <= I: (0,0),(1,0),(1,1),(2,0),...,(3,3).
-__device__ __forceinline__ constexpr int pair_id(int I, int J) { return I * (I + 1) / 2 + J; }
-// Off-diagonal pairs J < I -> 0..5.
+// Off-diagonal sub-tile pairs J < I -> 0..5.
 __device__ __forceinline__ constexpr int off_id(int I, int J) { return I * (I - 1) / 2 + J; }
 
-// Key-side inputs of one chunk as loaded: q, k, g (16 channels of one row per lane,
-// two 16-byte fragments each) and beta of the row.
-struct ChunkIn {
-  i32x4_t q[2], k[2], g[2];
+// Key-side inputs of one chunk for one operand wavefront as loaded (32 channels of
+// one row per lane, four 16-byte fragments each): g and beta, loaded an iteration
+// before the decay scan that reads them, and q, k, loaded an iteration before the
+// operand phase that reads them.
+struct DecayIn {
+  i32x4_t g[4];
   uint32_t beta;
 };
+struct KeyIn {
+  i32x4_t q[4], k[4];
+};
+
+// ------------------------------------------------------------------ operand role
+// Wavefront I (0..3) of the workgroup, sub-tile I of every chunk.
+__device__ __forceinline__ void operand_role(const FusedParams& p, char* smem, const int I,
+                                             const int h, const int tok0, const int len,
+                                             const int nchunks) {
+  const int tid = threadIdx.x;   // 0..255 in this role
+  // lane-derived values are recomputed every iteration from an opaque copy (see the
+  // loop), so the compiler does not hoist address and mask arithmetic out of the loop
+  // and keep it in registers across it
+  int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
+  const int H = p.H;
+  const uint32_t rs = static_cast<uint32_t>(H) * kD * 2;   // token row stride (bytes)
+
+  auto rows = [&](const int c, int64_t& base, uint32_t& bytes) {
+    const int t0 = tok0 + c * kCh;
+    const int nrow = min(kCh, len - c * kCh);
+    base = static_cast<int64_t>(t0) * H + h;
+    bytes = (nrow - 1) * rs + kD * 2;   // rows past the end read 0
+    return nrow;
+  };
+  const uint32_t row = (16 * I + l16) * rs;
+  auto load_decay = [&](const int c, DecayIn& in) {
+    int64_t base;
+    uint32_t bytes;
+    const int nrow = rows(c, base, bytes);
+    const auto rg = make_rsrc(p.g + base * kD, bytes);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) in.g[b] = buf_ld128(rg, row + (32 * b + 8 * g4) * 2, 0);
+    const auto rb = make_rsrc(p.beta + base, (nrow - 1) * H * 2 + 2);
+    in.beta = buf_ld16(rb, (16 * I + l16) * H * 2, 0);
+  };
+  auto load_keys = [&](const int c, KeyIn& in) {
+    int64_t base;
+    uint32_t bytes;
+    rows(c, base, bytes);
+    const auto rq = make_rsrc(p.q + base * kD, bytes);
+    const auto rk = make_rsrc(p.k + base * kD, bytes);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      in.k[b] = buf_ld128(rk, row + (32 * b + 8 * g4) * 2, 0);
+      in.q[b] = buf_ld128(rq, row + (32 * b + 8 * g4) * 2, 0);
+    }
+  };
+
+  // B operands that pick channels 8 (n / 4) + 4 hs + n % 4 of a 32-channel block into
+  // column n: the product of a token-major fragment with them lands in accumulator
+  // layout with channels as columns, i.e. transposed.
+  bf16x8_t sel[2];
+#pragma unroll
+  for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      sel[hs][j] = static_cast<__bf16>(g4 == (l16 >> 2) && j == 4 * hs + (l16 & 3) ? 1.f : 0.f);
+
+  DecayIn dn;
+  KeyIn kq;
+  float L[4][8];             // inclusive sum of g over the sub-tile's rows up to this one
+  float beta_t = 0.f;
+
+  // E1: cumulative log-decay of chunk c from the loaded inputs, sub-tile totals and
+  // beta to LDS.
+  auto e1 = [&](const int c) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t wg = static_cast<uint32_t>(dn.g[b][e >> 1]);
+        L[b][e] = row_scan16((e & 1) ? bf16hi(wg) : bf16lo(wg));
+      }
+    beta_t = bf16lo(dn.beta);
+    if (l16 == 15) {   // sub-tile totals R_I - R_{I-1}
+      float* tot = reinterpret_cast<float*>(smem + fl::TOT) + I * kD;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          *reinterpret_cast<float4*>(tot + 32 * b + 8 * g4 + 4 * hh) =
+              float4{L[b][4 * hh], L[b][4 * hh + 1], L[b][4 * hh + 2], L[b][4 * hh + 3]};
+    }
+    if (g4 == 0) reinterpret_cast<float*>(smem + fl::BETA)[(c & 1) * kCh + 16 * I + l16] = beta_t;
+  };
+
+  // Per-channel factors of chunk c: thread (m, ch) for sub-tiles m = tid / 128 and
+  // m + 2, channel ch.
+  auto factors = [&](const int c) {
+    const int ch = tid & (kD - 1);
+    const float* tot = reinterpret_cast<const float*>(smem + fl::TOT);
+    float R[4];
+    R[0] = tot[ch];
+#pragma unroll
+    for (int x = 1; x < 4; ++x) R[x] = R[x - 1] + tot[x * kD + ch];
+    float* fac = reinterpret_cast<float*>(smem + fl::FAC);
+    float* foff = reinterpret_cast<float*>(smem + fl::FOFF);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int m = (tid >> 7) + 2 * u;
+      const float rb = m == 0 ? 0.f : R[m - 1];          // decay before sub-tile m
+      // e^{R_m} as e^{tot_m} e^{R_{m-1}}: each factor alone is in range
+      const float em = fast_exp2(tot[m * kD + ch] * kLog2e) * fast_exp2(rb * kLog2e);
+      fac[(m * 3 + 0) * kD + ch] = -em;                                 // -e^{R_m}
+      fac[(m * 3 + 1) * kD + ch] = p.scale * em;                        // scale e^{R_m}
+      fac[(m * 3 + 2) * kD + ch] = fast_exp2((R[3] - R[m]) * kLog2e);   // e^{Ln - R_m}
+#pragma unroll
+      for (int a = 1; a < 4; ++a)
+        if (a > m) foff[off_id(a, m) * kD + ch] = fast_exp2((R[a] - R[m]) * kLog2e);
+      if (m == 0) {   // Lambda in state row order: row r holds channel sigma(r)
+        const int r = 32 * (ch >> 5) + 16 * ((ch >> 2) & 1) + 4 * ((ch >> 3) & 3) + (ch & 3);
+        reinterpret_cast<float*>(smem + fl::LAM)[(c & 1) * kD + r] = fast_exp2(R[3] * kLog2e);
+      }
+    }
+  };
+
+  // E2: decayed operands of chunk c.  rowf = e^{L_t - R_I} >= 1, colf = e^{R_I - L_t}
+  // <= 1 (R_I: end of the sub-tile).
+  auto e2 = [&](const int c, bf16x8_t (&fKr)[4], bf16x8_t (&fQr)[4], bf16x8_t (&fKc)[4]) {
+    const float* tot = reinterpret_cast<const float*>(smem + fl::TOT) + I * kD;
+    const float* fac = reinterpret_cast<const float*>(smem + fl::FAC);
+    const float* foff = reinterpret_cast<const float*>(smem + fl::FOFF);
+    const int qb_off = fl::QB + (c & 1) * 16384, kt_off = fl::KTT + (c & 1) * 16384;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      float kr[8], qr[8], kc[8], kb[8], qb[8], kt[8];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int c0 = 32 * b + 8 * g4 + 4 * hh;
+        const float4 t4 = *reinterpret_cast<const float4*>(tot + c0);
+        const float4 fK = *reinterpret_cast<const float4*>(fac + (I * 3 + 0) * kD + c0);
+        const float4 fQ = *reinterpret_cast<const float4*>(fac + (I * 3 + 1) * kD + c0);
+        const float4 fN = *reinterpret_cast<const float4*>(fac + (I * 3 + 2) * kD + c0);
+        const float tv[4] = {t4.x, t4.y, t4.z, t4.w}, vK[4] = {fK.x, fK.y, fK.z, fK.w};
+        const float vQ[4] = {fQ.x, fQ.y, fQ.z, fQ.w}, vN[4] = {fN.x, fN.y, fN.z, fN.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = 4 * hh + i;
+          const uint32_t kw = static_cast<uint32_t>(kq.k[b][e >> 1]);
+          const uint32_t qw = static_cast<uint32_t>(kq.q[b][e >> 1]);
+          const float kv = (e & 1) ? bf16hi(kw) : bf16lo(kw);
+          const float qv = (e & 1) ? bf16hi(qw) : bf16lo(qw);
+          const float d = (L[b][e] - tv[i]) * kLog2e;      // >= 0
+          const float rowf = fast_exp2(d), colf = fast_exp2(-d);
+          kr[e] = kv * rowf;
+          qr[e] = qv * rowf;
+          kc[e] = kv * colf;
+          kb[e] = kr[e] * vK[i];     // -K e^{L}
+          qb[e] = qr[e] * vQ[i];     // scale Q e^{L}
+          kt[e] = kc[e] * vN[i];     // K e^{Ln - L}
+        }
+      }
+      fKr[b] = to_frag(kr);
+      fQr[b] = to_frag(qr);
+      fKc[b] = to_frag(kc);
+      *reinterpret_cast<bf16x8_t*>(smem + fl::KBN + frag_at(I, b, 4, lane)) = to_frag(kb);
+      *reinterpret_cast<bf16x8_t*>(smem + qb_off + frag_at(I, b, 4, lane)) = to_frag(qb);
+      // Kt^T: the products with sel[hs] give, in lane (l16, g), tokens 16 I + 4 g .. +3
+      // of the channel of state row 16 (2 b + hs) + l16 -- half of that lane's
+      // fragment (state tile 2 b + hs, s-block I / 2), elements 4 (I % 2) .. +3
+      {
+        const bf16x8_t fkt = to_frag(kt);
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+          const f32x4_t tr = mma(fkt, sel[hs], f32x4_t{0.f, 0.f, 0.f, 0.f});
+          *reinterpret_cast<uint2*>(smem + kt_off + frag_at(2 * b + hs, I >> 1, 2, lane) + 8 * (I & 1)) =
+              uint2{pack_bf16x2(tr[0], tr[1]), pack_bf16x2(tr[2], tr[3])};
+        }
+      }
+      // column side of the off-diagonal pairs (I' > I, I): K e^{R_I' - L}
+#pragma unroll
+      for (int a = 1; a < 4; ++a) {
+        if (a > I) {
+          float x[8];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const float4 f4 = *reinterpret_cast<const float4*>(foff + off_id(a, I) * kD + 32 * b + 8 * g4 + 4 * hh);
+            x[4 * hh] = kc[4 * hh] * f4.x;
+            x[4 * hh + 1] = kc[4 * hh + 1] * f4.y;
+            x[4 * hh + 2] = kc[4 * hh + 2] * f4.z;
+            x[4 * hh + 3] = kc[4 * hh + 3] * f4.w;
+          }
+          *reinterpret_cast<bf16x8_t*>(smem + fl::OFF + off_id(a, I) * 4096 + frag_at(0, b, 4, lane)) = to_frag(x);
+        }
+      }
+    }
+  };
+
+  // Decayed sub-tile products of chunk c, transposed: C[s, t] = sum_c colside[s, c]
+  // rowside[t, c]; lane (t, g) holds s = 16 J + 4 g + i.  Writes M's blocks, -A_IJ
+  // (J < I) and the beta-scaled diagonal block A_II (masked to s < t) for its inverse.
+  auto products = [&](const bf16x8_t (&fKr)[4], const bf16x8_t (&fQr)[4], const bf16x8_t (&fKc)[4]) {
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      if (J <= I) {
+        f32x4_t pa = {0.f, 0.f, 0.f, 0.f}, pm = pa;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const bf16x8_t cs = J == I ? fKc[b] : lds_frag(smem, fl::OFF + off_id(I, J) * 4096 + frag_at(0, b, 4, lane));
+          pa = mma(cs, fKr[b], pa);
+          pm = mma(cs, fQr[b], pm);
+        }
+        // masks only on the diagonal pair (s = 16 I + 4 g + i against t = 16 I + l16)
+        f32x4_t av;
+        float mv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          av[i] = beta_t * pa[i];
+          mv[i] = p.scale * pm[i];
+          if (J == I) {
+            av[i] = 4 * g4 + i < l16 ? av[i] : 0.f;
+            mv[i] = 4 * g4 + i <= l16 ? mv[i] : 0.f;
+          }
+        }
+        // M[t][s]: fragment (t-tile I, s-block J/2), elements 4 (J%2) .. +3
+        *reinterpret_cast<uint2*>(smem + fl::MF + frag_at(I, J >> 1, 2, lane) + 8 * (J & 1)) =
+            uint2{pack_bf16x2(mv[0], mv[1]), pack_bf16x2(mv[2], mv[3])};
+        if (J < I)   // -A_IJ as a 16x16x16 A operand: lane (t, g) holds columns 4 g .. +3
+          *reinterpret_cast<uint2*>(smem + fl::AOF + off_id(I, J) * 512 + lane * 8) =
+              uint2{pack_bf16x2(-av[0], -av[1]), pack_bf16x2(-av[2], -av[3])};
+        else
+          *reinterpret_cast<f32x4_t*>(smem + fl::AII + I * 1024 + lane * 16) = av;
+      }
+    }
+  };
+
+  // prologue: chunk 0's decay and factors
+  if (nchunks > 0) {
+    load_decay(0, dn);
+    load_keys(0, kq);
+    e1(0);
+    if (nchunks > 1) load_decay(1, dn);
+  }
+  lds_barrier();
+  if (nchunks > 0) factors(0);
+  lds_barrier();
+
+  for (int c = 0; c <= nchunks; ++c) {
+    asm volatile("" : "+v"(lane));
+    l16 = lane & 15;
+    g4 = lane >> 4;
+    bf16x8_t fKr[4], fQr[4], fKc[4];
+    if (c < nchunks) {
+      e2(c, fKr, fQr, fKc);
+      if (c + 1 < nchunks) load_keys(c + 1, kq);
+    }
+    lds_barrier();                                                          // A
+    if (c < nchunks) products(fKr, fQr, fKc);
+    if (c + 1 < nchunks) {
+      e1(c + 1);
+      if (c + 2 < nchunks) load_decay(c + 2, dn);
+    }
+    lds_barrier();                                                          // B
+    if (c + 1 < nchunks) factors(c + 1);
+    lds_barrier();                                                          // C
+    lds_barrier();                                                          // D
+  }
+}
+
+// ------------------------------------------------------------------ state role
+// Wavefront 4 + j, value columns 32 j .. +31.
+__device__ __forceinline__ void state_role(const FusedParams& p, char* smem, const int j,
+                                           const int n, const int h, const int tok0, const int len,
+                                           const int nchunks) {
+  const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
+  const int H = p.H;
+  const uint32_t rs = static_cast<uint32_t>(H) * kD * 2;   // token row stride (bytes)
+  const int col0 = 32 * j;
+
+  f32x4_t S[2][8];
+  {
+    const float* s0 = p.s0 ? p.s0 + (static_cast<int64_t>(n) * H + h) * kD * kD : nullptr;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          S[u][ct][i] = s0 ? s0[sigma(16 * ct + 4 * g4 + i) * kD + col0 + 16 * u + l16] : 0.f;
+  }
+
+  // B operand of the 16 x 16 identity for 16x16x16 products (lane: column l16, rows
+  // 4 g .. +3)
+  bf16x4_t eye;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) eye[i] = 4 * g4 + i == l16 ? 0x3F80 : 0;
+
+  // v of chunk c for this wavefront's value columns: lane (t, g) loads token 16 tt + t,
+  // columns col0 + 16 u + 4 g .. +3 (rows past the end read 0)
+  i32x2_t vin[2][4];
+  auto load_v = [&](const int c) {
+    const int t0 = tok0 + c * kCh;
+    const int nrow = min(kCh, len - c * kCh);
+    const auto rv = make_rsrc(p.v + (static_cast<int64_t>(t0) * H + h) * kD, (nrow - 1) * rs + kD * 2);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+        vin[u][tt] = buf_ld64(rv, (16 * tt + l16) * rs + (col0 + 16 * u + 4 * g4) * 2, 0);
+  };
+
+  f32x4_t Y[2][4];      // Diag(beta)(V - Kb S) of the chunk being applied
+
+  // X of chunk c: Y = Diag(beta) (V - Kb S) (the stored -Kb makes the product an
+  // addition).  V arrives row-major (lane: token l16, value columns 4 g .. +3) and
+  // enters the accumulator layout as the product V I_16, exact in fp32; the two
+  // products are summed by the vector unit (a 16x16x16 result is not fed to a
+  // 16x16x32 product as its accumulator).
+  auto x_step = [&](const int c) {
+    bf16x8_t Sb[2][4];    // the state at the chunk start, as bf16 operand fragments
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) Sb[u][b] = acc_frag(S[u][2 * b], S[u][2 * b + 1]);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) Y[u][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    bf16x8_t F[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) F[0][tt] = lds_frag(smem, fl::KBN + frag_at(tt, 0, 4, lane));
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      if (b < 3) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) F[(b + 1) & 1][tt] = lds_frag(smem, fl::KBN + frag_at(tt, b + 1, 4, lane));
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) Y[u][tt] = mma(F[b & 1][tt], Sb[u][b], Y[u][tt]);
+    }
+    const float* betas = reinterpret_cast<const float*>(smem + fl::BETA) + (c & 1) * kCh;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const float4 b4 = *reinterpret_cast<const float4*>(betas + 16 * tt + 4 * g4);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const f32x4_t vt = mma16(__builtin_bit_cast(bf16x4_t, vin[u][tt]), eye, f32x4_t{0.f, 0.f, 0.f, 0.f});
+        Y[u][tt][0] = (Y[u][tt][0] + vt[0]) * b4.x;
+        Y[u][tt][1] = (Y[u][tt][1] + vt[1]) * b4.y;
+        Y[u][tt][2] = (Y[u][tt][2] + vt[2]) * b4.z;
+        Y[u][tt][3] = (Y[u][tt][3] + vt[3]) * b4.w;
+      }
+    }
+  };
+
+  // T_II = (I + A_II)^{-1} of chunk c's sub-tile j, written as the A operand of the
+  // substitution.  Computed as T^T = (I + B)^{-1} with B = A_II^T, which is strictly
+  // lower (B^16 = 0), as (I - B)(I + B^2)(I + B^4)(I + B^8).  This lane holds B in
+  // accumulator layout C(B) (rows 4 g + i, column l16).  A 16x16x16 product takes
+  // C(X^T) as its A operand and C(Y) as its B operand and returns C(X Y), so the
+  // powers are carried in both orientations and nothing is transposed through memory
+  // (the first transpose is a product with I).  Each operand is split into bf16 high
+  // and low parts, and a product is three matrix-core products (high x high, high x
+  // low, low x high): about 16 bits, far finer than the bf16 the inverse is rounded to.
+  auto inverse = [&]() {
+    const f32x4_t av = *reinterpret_cast<const f32x4_t*>(smem + fl::AII + j * 1024 + lane * 16);
+    struct Split {
+      bf16x4_t h, l;
+    };
+    auto split = [](const f32x4_t& x) {
+      Split sp;
+      sp.h = acc_frag4(x);
+      f32x4_t r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        r[i] = x[i] - __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(sp.h[i])) << 16);
+      sp.l = acc_frag4(r);
+      return sp;
+    };
+    auto mm = [](const Split& xt, const Split& y) {   // C(X Y) from C(X^T), C(Y)
+      const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+      return mma16(xt.l, y.h, mma16(xt.h, y.l, mma16(xt.h, y.h, z)));
+    };
+    const Split sB = split(av);
+    const f32x4_t bt = mma16(sB.l, eye, mma16(sB.h, eye, f32x4_t{0.f, 0.f, 0.f, 0.f}));   // C(B^T)
+    const Split sBt = split(bt);
+    const f32x4_t p1 = mm(sBt, sB), p1t = mm(sB, sBt);           // B^2 and its transpose
+    const Split s1 = split(p1), s1t = split(p1t);
+    const f32x4_t p2 = mm(s1t, s1), p2t = mm(s1, s1t);           // B^4
+    const f32x4_t b3 = mm(sBt, s1), b3t = mm(s1, sBt);           // B^3
+    const Split s2 = split(p2), s2t = split(p2t);
+    const f32x4_t p3 = mm(s2t, s2);                               // B^8
+    f32x4_t t1, t1t;                                              // I - B + B^2 - B^3
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float d = 4 * g4 + i == l16 ? 1.f : 0.f;
+      t1[i] = d - av[i] + p1[i] - b3[i];
+      t1t[i] = d - bt[i] + p1t[i] - b3t[i];
+    }
+    const Split sT1t = split(t1t);
+    f32x4_t t2 = mm(sT1t, s2), t2t = mm(s2, sT1t);               // T1 (I + B^4)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      t2[i] += t1[i];
+      t2t[i] += t1t[i];
+    }
+    f32x4_t t3 = mm(split(t2t), split(p3));                       // T2 (I + B^8)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t3[i] += t2[i];
+    // lane (l16, g) holds T^T[4 g + i][l16] = T[l16][4 g + i]: the A operand
+    *reinterpret_cast<uint2*>(smem + fl::TDF + j * 512 + lane * 8) =
+        uint2{pack_bf16x2(t3[0], t3[1]), pack_bf16x2(t3[2], t3[3])};
+  };
+
+  // Output and state step of chunk cs, whose operands are in LDS; Y holds its X and S
+  // its starting state.
+  auto apply = [&](const int cs) {
+    const int qb_off = fl::QB + (cs & 1) * 16384, kt_off = fl::KTT + (cs & 1) * 16384;
+    bf16x8_t Sb[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) Sb[u][b] = acc_frag(S[u][2 * b], S[u][2 * b + 1]);
+    // O^T = S^T Qb^T + Delta^T M^T: lane (t, g) holds value columns 4 g .. +3 of token t
+    f32x4_t o[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) o[u][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    bf16x8_t F[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) F[0][tt] = lds_frag(smem, qb_off + frag_at(tt, 0, 4, lane));
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      if (b < 3) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) F[(b + 1) & 1][tt] = lds_frag(smem, qb_off + frag_at(tt, b + 1, 4, lane));
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) o[u][tt] = mma(Sb[u][b], F[b & 1][tt], o[u][tt]);
+    }
+    // Delta_i = T_ii (Y_i - sum_{m<i} A_im Delta_m), both column halves interleaved
+    bf16x4_t fa[6], ft[4];
+#pragma unroll
+    for (int x = 0; x < 6; ++x) fa[x] = lds_frag4(smem, fl::AOF + x * 512 + lane * 8);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) ft[x] = lds_frag4(smem, fl::TDF + x * 512 + lane * 8);
+    bf16x4_t Dq[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        f32x4_t w = Y[u][i];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          if (m < i) w = mma16(fa[off_id(i, m)], Dq[u][m], w);
+        Dq[u][i] = acc_frag4(mma16(ft[i], acc_frag4(w), f32x4_t{0.f, 0.f, 0.f, 0.f}));
+      }
+    }
+    // Delta as 32-deep fragments: tiles (2 b, 2 b + 1) side by side
+    bf16x8_t Db[2][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        Db[u][b] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(Dq[u][2 * b], Dq[u][2 * b + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+    // + Delta^T M^T: M fragments (tt, 0) for every tt, (2, 1) and (3, 1)
+    {
+      bf16x8_t M0[4], M1[2];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) M0[tt] = lds_frag(smem, fl::MF + frag_at(tt, 0, 2, lane));
+      M1[0] = lds_frag(smem, fl::MF + frag_at(2, 1, 2, lane));
+      M1[1] = lds_frag(smem, fl::MF + frag_at(3, 1, 2, lane));
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) o[u][tt] = mma(Db[u][0], M0[tt], o[u][tt]);
+        o[u][2] = mma(Db[u][1], M1[0], o[u][2]);
+        o[u][3] = mma(Db[u][1], M1[1], o[u][3]);
+      }
+    }
+    // output rows of chunk cs: plain stores, so that the cache joins the wavefronts'
+    // pieces of a row into whole lines
+    {
+      const int t0 = tok0 + cs * kCh;
+      const int nrow = min(kCh, len - cs * kCh);
+      const auto ro = make_rsrc(p.out + (static_cast<int64_t>(t0) * H + h) * kD, (nrow - 1) * rs + kD * 2);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+          buf_st64(i32x2_t{static_cast<int>(pack_bf16x2(o[u][tt][0], o[u][tt][1])),
+                           static_cast<int>(pack_bf16x2(o[u][tt][2], o[u][tt][3]))},
+                   ro, (16 * tt + l16) * rs + (col0 + 16 * u + 4 * g4) * 2, 0);
+    }
+    // S <- Diag(Lambda) S + Kt^T Delta, Kt fragments one accumulator tile ahead
+    const float* lam = reinterpret_cast<const float*>(smem + fl::LAM) + (cs & 1) * kD;
+    bf16x8_t K2[2][2];
+    K2[0][0] = lds_frag(smem, kt_off + frag_at(0, 0, 2, lane));
+    K2[0][1] = lds_frag(smem, kt_off + frag_at(0, 1, 2, lane));
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+      if (ct < 7) {
+        K2[(ct + 1) & 1][0] = lds_frag(smem, kt_off + frag_at(ct + 1, 0, 2, lane));
+        K2[(ct + 1) & 1][1] = lds_frag(smem, kt_off + frag_at(ct + 1, 1, 2, lane));
+      }
+      const float4 l4 = *reinterpret_cast<const float4*>(lam + 16 * ct + 4 * g4);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        f32x4_t acc = {S[u][ct][0] * l4.x, S[u][ct][1] * l4.y, S[u][ct][2] * l4.z, S[u][ct][3] * l4.w};
+        acc = mma(K2[ct & 1][0], Db[u][0], acc);
+        S[u][ct] = mma(K2[ct & 1][1], Db[u][1], acc);
+      }
+    }
+  };
+
+  if (nchunks > 0) load_v(0);
+  lds_barrier();
+  lds_barrier();
+  for (int c = 0; c <= nchunks; ++c) {
+    if (c > 0) apply(c - 1);
+    lds_barrier();                                                          // A
+    if (c < nchunks) {
+      x_step(c);
+      if (c + 1 < nchunks) load_v(c + 1);
+    }
+    lds_barrier();                                                          // B
+    if (c < nchunks) inverse();
+    lds_barrier();                                                          // C
+    lds_barrier();                                                          // D
+  }
+
+  if (p.sT != nullptr) {
+    float* dst = p.sT + (static_cast<int64_t>(n) * H + h) * kD * kD;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[sigma(16 * ct + 4 * g4 + i) * kD + col0 + 16 * u + l16] = S[u][ct][i];
+  }
+}
 
 __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams p) {
   __shared__ __attribute__((aligned(16))) char smem[fl::BYTES];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, l16 = lane & 15, g4 = lane >> 4;
   const int H = p.H;
-  const int I = wave >> 1, hf = wave & 1;     // elementwise role: sub-tile, channel half
-  // state role: wavefront w owns value columns 16 w .. +15
 
   // ---------------------------------------------------------------- which sequence
   const int rank = blockIdx.x / H, h = blockIdx.x % H;
@@ -235,470 +769,10 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
   for (int e = tid; e < 8192 / 16; e += kThreadsF)
     *reinterpret_cast<i32x4_t*>(smem + fl::MF + e * 16) = i32x4_t{0, 0, 0, 0};
 
-  // ---------------------------------------------------------------- state
-  f32x4_t S[8];
-  {
-    const float* s0 = p.s0 ? p.s0 + (static_cast<int64_t>(n) * H + h) * kD * kD : nullptr;
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        S[ct][i] = s0 ? s0[sigma(16 * ct + 4 * g4 + i) * kD + 16 * wave + l16] : 0.f;
-  }
-
-  const uint32_t rs = static_cast<uint32_t>(H) * kD * 2;   // token row stride (bytes)
-
-  auto load_chunk = [&](int c, ChunkIn& in) {
-    const int t0 = tok0 + c * kCh;
-    const int nrow = min(kCh, len - c * kCh);
-    const int64_t base = (static_cast<int64_t>(t0) * H + h) * kD;
-    const uint32_t bytes = (nrow - 1) * rs + kD * 2;   // rows past the end read 0
-    const auto rq = make_rsrc(p.q + base, bytes);
-    const auto rk = make_rsrc(p.k + base, bytes);
-    const auto rg = make_rsrc(p.g + base, bytes);
-    const uint32_t row = (16 * I + l16) * rs;
-#pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2) {
-      const uint32_t off = row + (32 * (2 * hf + b2) + 8 * g4) * 2;
-      in.q[b2] = buf_ld128(rq, off, 0);
-      in.k[b2] = buf_ld128(rk, off, 0);
-      in.g[b2] = buf_ld128(rg, off, 0);
-    }
-    const auto rb = make_rsrc(p.beta + static_cast<int64_t>(t0) * H + h, (nrow - 1) * H * 2 + 2);
-    in.beta = buf_ld16(rb, (16 * I + l16) * H * 2, 0);
-  };
-
-  // B operand of the 16 x 16 identity for 16x16x16 products (lane: column l16, rows
-  // 4 g .. +3)
-  bf16x4_t eye;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) eye[i] = 4 * g4 + i == l16 ? 0x3F80 : 0;
-
-  // The state step of chunk cs, whose operands are in LDS.  It runs at the top of the
-  // next chunk's iteration, in the barrier window of that chunk's first elementwise
-  // phase (which writes nothing read here).  The output rows come back packed in
-  // registers and are stored later in the iteration, spread away from the other
-  // global memory traffic.  Operand fragments are read from LDS one batch ahead of the
-  // products that use them.
-  auto state_step = [&](const int cs, const i32x2_t (&vin)[4], uint32_t (&opk)[4][2]) {
-    const float* betas = reinterpret_cast<const float*>(smem + fl::BETA) + (cs & 1) * kCh;
-    bf16x4_t fa[6], ft[4];   // -A_IJ (J < I) and T_II, for the substitution below
-#pragma unroll
-    for (int x = 0; x < 6; ++x) fa[x] = lds_frag4(smem, fl::AOF + x * 512 + lane * 8);
-#pragma unroll
-    for (int x = 0; x < 4; ++x) ft[x] = lds_frag4(smem, fl::TDF + x * 512 + lane * 8);
-    bf16x8_t Sb[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) Sb[b] = acc_frag(S[2 * b], S[2 * b + 1]);
-
-    // Y = Diag(beta) (V - Kb S) (the stored -Kb makes the product an addition).  V
-    // arrives row-major (lane: token l16, value columns 4 g .. +3) and enters the
-    // accumulator layout as the product V I_16, exact in fp32; the two products are
-    // summed by the vector unit (a 16x16x16 result is not fed to a 16x16x32 product as
-    // its accumulator).
-    f32x4_t Y[4];
-    bf16x8_t F[2][4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) F[0][tt] = lds_frag(smem, fl::KBN + frag_at(tt, 0, 4, lane));
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) Y[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      if (b < 3) {
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) F[(b + 1) & 1][tt] = lds_frag(smem, fl::KBN + frag_at(tt, b + 1, 4, lane));
-      } else {   // the first batch of Qb
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) F[0][tt] = lds_frag(smem, fl::QB + frag_at(tt, 0, 4, lane));
-      }
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) Y[tt] = mma(F[b & 1][tt], Sb[b], Y[tt]);
-    }
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const f32x4_t vt = mma16(__builtin_bit_cast(bf16x4_t, vin[tt]), eye, f32x4_t{0.f, 0.f, 0.f, 0.f});
-      const float4 b4 = *reinterpret_cast<const float4*>(betas + 16 * tt + 4 * g4);
-      Y[tt][0] = (Y[tt][0] + vt[0]) * b4.x;
-      Y[tt][1] = (Y[tt][1] + vt[1]) * b4.y;
-      Y[tt][2] = (Y[tt][2] + vt[2]) * b4.z;
-      Y[tt][3] = (Y[tt][3] + vt[3]) * b4.w;
-    }
-    // O^T = S^T Qb^T + Delta^T M^T, the first term while the substitution below waits
-    // on its own chain: lane (t, g) holds value columns 16 w + 4 g .. +3 of token t
-    f32x4_t o[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) o[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      if (b < 3) {
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) F[(b + 1) & 1][tt] = lds_frag(smem, fl::QB + frag_at(tt, b + 1, 4, lane));
-      } else {   // M: fragments (tt, b <= tt / 2)
-        F[0][0] = lds_frag(smem, fl::MF + frag_at(0, 0, 2, lane));
-        F[0][1] = lds_frag(smem, fl::MF + frag_at(1, 0, 2, lane));
-        F[0][2] = lds_frag(smem, fl::MF + frag_at(2, 0, 2, lane));
-        F[0][3] = lds_frag(smem, fl::MF + frag_at(3, 0, 2, lane));
-      }
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) o[tt] = mma(Sb[b], F[b & 1][tt], o[tt]);
-    }
-    // Delta_i = T_ii (Y_i - sum_{m<i} A_im Delta_m)
-    bf16x4_t Dq[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f32x4_t w = Y[i];
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        if (m < i) w = mma16(fa[off_id(i, m)], Dq[m], w);
-      Dq[i] = acc_frag4(mma16(ft[i], acc_frag4(w), f32x4_t{0.f, 0.f, 0.f, 0.f}));
-    }
-    // Delta as 32-deep fragments: tiles (2 b, 2 b + 1) side by side
-    bf16x8_t Db[2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-      Db[b] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(Dq[2 * b], Dq[2 * b + 1], 0, 1, 2, 3, 4, 5, 6, 7));
-    F[1][0] = lds_frag(smem, fl::MF + frag_at(2, 1, 2, lane));
-    F[1][1] = lds_frag(smem, fl::MF + frag_at(3, 1, 2, lane));
-    F[1][2] = lds_frag(smem, fl::KTT + frag_at(0, 0, 2, lane));
-    F[1][3] = lds_frag(smem, fl::KTT + frag_at(0, 1, 2, lane));
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) o[tt] = mma(Db[0], F[0][tt], o[tt]);
-    o[2] = mma(Db[1], F[1][0], o[2]);
-    o[3] = mma(Db[1], F[1][1], o[3]);
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      opk[tt][0] = pack_bf16x2(o[tt][0], o[tt][1]);
-      opk[tt][1] = pack_bf16x2(o[tt][2], o[tt][3]);
-    }
-    // S <- Diag(Lambda) S + Kt^T Delta, Kt fragments one accumulator tile ahead
-    const float* lam = reinterpret_cast<const float*>(smem + fl::LAM);
-    bf16x8_t K2[2][2] = {{F[1][2], F[1][3]}, {F[1][2], F[1][3]}};
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) {
-      if (ct < 7) {
-        K2[(ct + 1) & 1][0] = lds_frag(smem, fl::KTT + frag_at(ct + 1, 0, 2, lane));
-        K2[(ct + 1) & 1][1] = lds_frag(smem, fl::KTT + frag_at(ct + 1, 1, 2, lane));
-      }
-      const float4 l4 = *reinterpret_cast<const float4*>(lam + 16 * ct + 4 * g4);
-      f32x4_t acc = {S[ct][0] * l4.x, S[ct][1] * l4.y, S[ct][2] * l4.z, S[ct][3] * l4.w};
-      acc = mma(K2[ct & 1][0], Db[0], acc);
-      S[ct] = mma(K2[ct & 1][1], Db[1], acc);
-    }
-  };
-  // v of chunk cs for this wavefront's value columns: lane (t, g) loads token 16 tt + t,
-  // columns 16 w + 4 g .. +3 (rows past the end read 0)
-  auto load_v = [&](const int cs, i32x2_t (&vin)[4]) {
-    const int t0 = tok0 + cs * kCh;
-    const int nrow = min(kCh, len - cs * kCh);
-    const auto rv = make_rsrc(p.v + (static_cast<int64_t>(t0) * H + h) * kD, (nrow - 1) * rs + kD * 2);
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) vin[tt] = buf_ld64(rv, (16 * tt + l16) * rs + (16 * wave + 4 * g4) * 2, 0);
-  };
-  // output rows of token tiles t_lo .. t_hi - 1 of chunk cs: plain stores, so that the
-  // cache joins the eight wavefronts' 32-byte pieces of a row into whole lines (with
-  // the non-temporal hint each piece went to memory alone: twice the output's bytes
-  // written, measured)
-  auto store_out = [&](const int cs, const uint32_t (&opk)[4][2], const int t_lo, const int t_hi) {
-    const int t0 = tok0 + cs * kCh;
-    const int nrow = min(kCh, len - cs * kCh);
-    const auto ro = make_rsrc(p.out + (static_cast<int64_t>(t0) * H + h) * kD, (nrow - 1) * rs + kD * 2);
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-      if (tt >= t_lo && tt < t_hi)
-      buf_st64(i32x2_t{static_cast<int>(opk[tt][0]), static_cast<int>(opk[tt][1])}, ro,
-                  (16 * tt + l16) * rs + (16 * wave + 4 * g4) * 2, 0);
-  };
-
-  i32x2_t vin[4];
-  ChunkIn cur;
-  if (nchunks > 0) load_chunk(0, cur);
-
-  for (int c = 0; c < nchunks; ++c) {
-    const int t0 = tok0 + c * kCh;
-    const int nrow = min(kCh, len - c * kCh);
-    float* betas = reinterpret_cast<float*>(smem + fl::BETA) + (c & 1) * kCh;
-    uint32_t opk[4][2];
-    if (c > 0) state_step(c - 1, vin, opk);
-
-    // ============================================ E1: cumulative log-decay per sub-tile
-    float L[2][8];          // inclusive sum of g over the sub-tile's rows up to this one
-    uint32_t kw[2][4], qw[2][4];   // k and q as loaded (bf16 pairs, channel order)
-#pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t wg = static_cast<uint32_t>(cur.g[b2][e >> 1]);
-        L[b2][e] = row_scan16((e & 1) ? bf16hi(wg) : bf16lo(wg));
-      }
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        kw[b2][w] = static_cast<uint32_t>(cur.k[b2][w]);
-        qw[b2][w] = static_cast<uint32_t>(cur.q[b2][w]);
-      }
-    }
-    const float beta_t = bf16lo(cur.beta);
-    // the key-side registers are free again: the next chunk's loads go out now and
-    // have the rest of this chunk to arrive
-    if (c + 1 < nchunks) load_chunk(c + 1, cur);
-    if (l16 == 15) {   // sub-tile totals R_I - R_{I-1}
-      float* tot = reinterpret_cast<float*>(smem + fl::TOT) + I * kD;
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-          *reinterpret_cast<float4*>(tot + 32 * (2 * hf + b2) + 8 * g4 + 4 * hh) =
-              float4{L[b2][4 * hh], L[b2][4 * hh + 1], L[b2][4 * hh + 2], L[b2][4 * hh + 3]};
-    }
-    if (hf == 0 && g4 == 0) betas[16 * I + l16] = beta_t;
-    lds_barrier();                                                          // B1
-
-    // per-channel factors: thread (m, c) for sub-tile m and channel c
-    {
-      const int m = tid >> 7, ch = tid & (kD - 1);
-      const float* tot = reinterpret_cast<const float*>(smem + fl::TOT);
-      float R[4];
-      R[0] = tot[ch];
-#pragma unroll
-      for (int x = 1; x < 4; ++x) R[x] = R[x - 1] + tot[x * kD + ch];
-      const float rb = m == 0 ? 0.f : R[m - 1];          // decay before sub-tile m
-      // e^{R_m} as e^{tot_m} e^{R_{m-1}}: each factor alone is in range
-      const float em = fast_exp2(tot[m * kD + ch] * kLog2e) * fast_exp2(rb * kLog2e);
-      float* fac = reinterpret_cast<float*>(smem + fl::FAC);
-      fac[(m * 3 + 0) * kD + ch] = -em;                                 // -e^{R_m}
-      fac[(m * 3 + 1) * kD + ch] = p.scale * em;                        // scale e^{R_m}
-      fac[(m * 3 + 2) * kD + ch] = fast_exp2((R[3] - R[m]) * kLog2e);   // e^{Ln - R_m}
-      float* foff = reinterpret_cast<float*>(smem + fl::FOFF);
-#pragma unroll
-      for (int a = 1; a < 4; ++a)
-        if (a > m) foff[off_id(a, m) * kD + ch] = fast_exp2((R[a] - R[m]) * kLog2e);
-      if (m == 0) {   // Lambda in state row order: row r holds channel sigma(r)
-        const int r = 32 * (ch >> 5) + 16 * ((ch >> 2) & 1) + 4 * ((ch >> 3) & 3) + (ch & 3);
-        reinterpret_cast<float*>(smem + fl::LAM)[r] = fast_exp2(R[3] * kLog2e);
-      }
-    }
-    lds_barrier();                                                          // B2
-    // the previous chunk's output goes out in two halves, here and during the pair
-    // products, phases that issue no other global memory traffic (measured: stores
-    // and loads issued together in the first phase, behind the prefetch, cost about a
-    // fifth of the chunk time)
-    if (c > 0) store_out(c - 1, opk, 0, 2);
-
-    // ============================================ E2: chunk operands
-    // rowf = e^{L_t - R_I} >= 1, colf = e^{R_I - L_t} <= 1 (R_I: end of the sub-tile)
-    bf16x8_t fKr[2], fQr[2], fKc[2];
-    {
-      const float* tot = reinterpret_cast<const float*>(smem + fl::TOT) + I * kD;
-      const float* fac = reinterpret_cast<const float*>(smem + fl::FAC);
-      const float* foff = reinterpret_cast<const float*>(smem + fl::FOFF);
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2) {
-        const int blk = 2 * hf + b2;
-        float kr[8], qr[8], kc[8], kb[8], qb[8], kt[8];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int c0 = 32 * blk + 8 * g4 + 4 * hh;
-          const float4 t4 = *reinterpret_cast<const float4*>(tot + c0);
-          const float4 fK = *reinterpret_cast<const float4*>(fac + (I * 3 + 0) * kD + c0);
-          const float4 fQ = *reinterpret_cast<const float4*>(fac + (I * 3 + 1) * kD + c0);
-          const float4 fN = *reinterpret_cast<const float4*>(fac + (I * 3 + 2) * kD + c0);
-          const float tv[4] = {t4.x, t4.y, t4.z, t4.w}, vK[4] = {fK.x, fK.y, fK.z, fK.w};
-          const float vQ[4] = {fQ.x, fQ.y, fQ.z, fQ.w}, vN[4] = {fN.x, fN.y, fN.z, fN.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int e = 4 * hh + i;
-            const float kv = (e & 1) ? bf16hi(kw[b2][e >> 1]) : bf16lo(kw[b2][e >> 1]);
-            const float qv = (e & 1) ? bf16hi(qw[b2][e >> 1]) : bf16lo(qw[b2][e >> 1]);
-            const float d = (L[b2][e] - tv[i]) * kLog2e;      // >= 0
-            const float rowf = fast_exp2(d), colf = fast_exp2(-d);
-            kr[e] = kv * rowf;
-            qr[e] = qv * rowf;
-            kc[e] = kv * colf;
-            kb[e] = kr[e] * vK[i];     // -K e^{L}
-            qb[e] = qr[e] * vQ[i];     // scale Q e^{L}
-            kt[e] = kc[e] * vN[i];     // K e^{Ln - L}
-          }
-        }
-        fKr[b2] = to_frag(kr);
-        fQr[b2] = to_frag(qr);
-        fKc[b2] = to_frag(kc);
-        *reinterpret_cast<bf16x8_t*>(smem + fl::KBN + frag_at(I, blk, 4, lane)) = to_frag(kb);
-        *reinterpret_cast<bf16x8_t*>(smem + fl::QB + frag_at(I, blk, 4, lane)) = to_frag(qb);
-        // Kt^T: rows in state row order, contraction over tokens; channel 32 b + 8 g + e
-        // is state row 32 b + 16 (e/4) + 4 g + e%4; token 16 I + l16 sits in s-block
-        // I/2 at lane group l16/4, element (l16 % 4) + 4 (I % 2)
-        {
-          const int sblk = I >> 1, eo = (l16 & 3) + 4 * (I & 1), gq = l16 >> 2;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int r = 32 * blk + 16 * (e >> 2) + 4 * g4 + (e & 3);
-            const int off = frag_at(r >> 4, sblk, 2, (r & 15) + 16 * gq) + eo * 2;
-            *reinterpret_cast<__bf16*>(smem + fl::KTT + off) = static_cast<__bf16>(kt[e]);
-          }
-        }
-        // column side of the off-diagonal pairs (I' > I, I): K e^{R_I' - L}
-#pragma unroll
-        for (int a = 1; a < 4; ++a) {
-          if (a > I) {
-            float x[8];
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              const float4 f4 = *reinterpret_cast<const float4*>(
-                  foff + off_id(a, I) * kD + 32 * blk + 8 * g4 + 4 * hh);
-              x[4 * hh] = kc[4 * hh] * f4.x;
-              x[4 * hh + 1] = kc[4 * hh + 1] * f4.y;
-              x[4 * hh + 2] = kc[4 * hh + 2] * f4.z;
-              x[4 * hh + 3] = kc[4 * hh + 3] * f4.w;
-            }
-            *reinterpret_cast<bf16x8_t*>(smem + fl::OFF + off_id(a, I) * 4096 + frag_at(0, blk, 4, lane)) =
-                to_frag(x);
-          }
-        }
-      }
-    }
-    lds_barrier();                                                          // B3
-    if (c > 0) store_out(c - 1, opk, 2, 4);
-
-    // ============================================ P: decayed sub-tile products
-    // transposed: C[s, t] = sum_c colside[s, c] rowside[t, c]; lane (t, g) holds
-    // s = 16 J + 4 g + i.  Partial over this wavefront's channel half.
-    {
-      f32x4_t pa[4], pm[4];
-#pragma unroll
-      for (int J = 0; J < 4; ++J) {
-        pa[J] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        pm[J] = pa[J];
-        if (J <= I) {
-#pragma unroll
-          for (int b2 = 0; b2 < 2; ++b2) {
-            const bf16x8_t cs = J == I ? fKc[b2]
-                                       : lds_frag(smem, fl::OFF + off_id(I, J) * 4096 +
-                                                            frag_at(0, 2 * hf + b2, 4, lane));
-            pa[J] = mma(cs, fKr[b2], pa[J]);
-            pm[J] = mma(cs, fQr[b2], pm[J]);
-          }
-        }
-      }
-      // The two channel halves' partials meet in the wavefront that finishes the pair:
-      // the diagonal pair, whose inverse is the longest piece of work, in wavefront
-      // (I, hd) with hd = 1 for I = 1, 2 and 0 otherwise -- wavefronts 0, 3, 5, 6, one
-      // per SIMD when wavefront w runs on SIMD w % 4 -- and the pairs J < I in the
-      // other half's wavefront.
-      const int hd = (I == 1 || I == 2) ? 1 : 0;
-      auto part = [&](int J, int x) { return smem + fl::PART + (pair_id(I, J) * 2 + x) * 1024 + lane * 16; };
-      if (hf != hd) {
-        *reinterpret_cast<f32x4_t*>(part(I, 0)) = pa[I];
-        *reinterpret_cast<f32x4_t*>(part(I, 1)) = pm[I];
-      } else {
-#pragma unroll
-        for (int J = 0; J < 3; ++J)
-          if (J < I) {
-            *reinterpret_cast<f32x4_t*>(part(J, 0)) = pa[J];
-            *reinterpret_cast<f32x4_t*>(part(J, 1)) = pm[J];
-          }
-      }
-      lds_barrier();                                                        // B4
-      const int t = 16 * I + l16;
-      // sums the halves of pair (I, J), writes M's block and, for J < I, -A_IJ; returns
-      // beta-scaled A_IJ (masked to s < t) in accumulator layout
-      auto finish = [&](const int J) {
-        const f32x4_t oa = *reinterpret_cast<const f32x4_t*>(part(J, 0));
-        const f32x4_t om = *reinterpret_cast<const f32x4_t*>(part(J, 1));
-        f32x4_t av;
-        float mv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int s = 16 * J + 4 * g4 + i;
-          av[i] = s < t ? beta_t * (pa[J][i] + oa[i]) : 0.f;
-          mv[i] = s <= t ? p.scale * (pm[J][i] + om[i]) : 0.f;
-        }
-        // M[t][s]: fragment (t-tile I, s-block J/2), elements 4 (J%2) .. +3
-        *reinterpret_cast<uint2*>(smem + fl::MF + frag_at(I, J >> 1, 2, l16 + 16 * g4) + 8 * (J & 1)) =
-            uint2{pack_bf16x2(mv[0], mv[1]), pack_bf16x2(mv[2], mv[3])};
-        if (J < I)   // -A_IJ as a 16x16x16 A operand: lane (t, g) holds columns 4 g .. +3
-          *reinterpret_cast<uint2*>(smem + fl::AOF + off_id(I, J) * 512 + lane * 8) =
-              uint2{pack_bf16x2(-av[0], -av[1]), pack_bf16x2(-av[2], -av[3])};
-        return av;
-      };
-      if (hf != hd) {
-#pragma unroll
-        for (int J = 0; J < 3; ++J)
-          if (J < I) finish(J);
-      } else {
-        const f32x4_t av = finish(I);
-        // T_II = (I + A_II)^{-1}, computed as T^T = (I + B)^{-1} with B = A_II^T, which
-        // is strictly lower (B^16 = 0), as (I - B)(I + B^2)(I + B^4)(I + B^8).  This lane
-        // holds B in accumulator layout C(B) (rows 4 g + i, column l16).  A 16x16x16
-        // product takes C(X^T) as its A operand and C(Y) as its B operand and returns
-        // C(X Y), so the powers are carried in both orientations and nothing is
-        // transposed through memory (the first transpose is a product with I).  Each
-        // operand is split into bf16 high and low parts, and a product is three
-        // matrix-core products (high x high, high x low, low x high): about 16 bits,
-        // far finer than the bf16 the inverse is rounded to.
-        struct Split {
-          bf16x4_t h, l;
-        };
-        auto split = [](const f32x4_t& x) {
-          Split sp;
-          sp.h = acc_frag4(x);
-          f32x4_t r;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            r[i] = x[i] - __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(sp.h[i])) << 16);
-          sp.l = acc_frag4(r);
-          return sp;
-        };
-        auto mm = [](const Split& xt, const Split& y) {   // C(X Y) from C(X^T), C(Y)
-          const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-          return mma16(xt.l, y.h, mma16(xt.h, y.l, mma16(xt.h, y.h, z)));
-        };
-        const Split sB = split(av);
-        const f32x4_t bt = mma16(sB.l, eye, mma16(sB.h, eye, f32x4_t{0.f, 0.f, 0.f, 0.f}));   // C(B^T)
-        const Split sBt = split(bt);
-        const f32x4_t p1 = mm(sBt, sB), p1t = mm(sB, sBt);           // B^2 and its transpose
-        const Split s1 = split(p1), s1t = split(p1t);
-        const f32x4_t p2 = mm(s1t, s1), p2t = mm(s1, s1t);           // B^4
-        const f32x4_t b3 = mm(sBt, s1), b3t = mm(s1, sBt);           // B^3
-        const Split s2 = split(p2), s2t = split(p2t);
-        const f32x4_t p3 = mm(s2t, s2);                               // B^8
-        f32x4_t t1, t1t;                                              // I - B + B^2 - B^3
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float d = 4 * g4 + i == l16 ? 1.f : 0.f;
-          t1[i] = d - av[i] + p1[i] - b3[i];
-          t1t[i] = d - bt[i] + p1t[i] - b3t[i];
-        }
-        const Split sT1t = split(t1t);
-        f32x4_t t2 = mm(sT1t, s2), t2t = mm(s2, sT1t);               // T1 (I + B^4)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          t2[i] += t1[i];
-          t2t[i] += t1t[i];
-        }
-        f32x4_t t3 = mm(split(t2t), split(p3));                       // T2 (I + B^8)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) t3[i] += t2[i];
-        // lane (l16, g) holds T^T[4 g + i][l16] = T[l16][4 g + i]: the A operand
-        *reinterpret_cast<uint2*>(smem + fl::TDF + I * 512 + lane * 8) =
-            uint2{pack_bf16x2(t3[0], t3[1]), pack_bf16x2(t3[2], t3[3])};
-      }
-    }
-    // this chunk's v, consumed by its state step at the top of the next iteration
-    load_v(c, vin);
-    lds_barrier();                                                          // B5
-  }
-  if (nchunks > 0) {
-    uint32_t opk[4][2];
-    state_step(nchunks - 1, vin, opk);
-    store_out(nchunks - 1, opk, 0, 4);
-  }
-
-  if (p.sT != nullptr) {
-    float* dst = p.sT + (static_cast<int64_t>(n) * H + h) * kD * kD;
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dst[sigma(16 * ct + 4 * g4 + i) * kD + 16 * wave + l16] = S[ct][i];
-  }
+  if (wave < 4)
+    operand_role(p, smem, wave, h, tok0, len, nchunks);
+  else
+    state_role(p, smem, wave - 4, n, h, tok0, len, nchunks);
 }
 
 }  // namespace
