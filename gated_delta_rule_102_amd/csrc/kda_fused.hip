@@ -43,7 +43,7 @@
 //    key-side operands with one conversion to bf16 and no transpose.  Products that
 //    contract over the chunk's tokens take Delta and Kt^T with the tokens of a
 //    32-token block in the order 4 g + i, 16 + 4 g + i on both sides.
-// Every iteration has four barrier windows; iteration c runs
+// Every iteration has three barrier windows; iteration c runs
 //   A: operand: E2, the decayed operands of chunk c (Kb, Qb, Kt^T to LDS; the row and
 //      column sides of the sub-tile products kept in registers);
 //      state: chunk c - 1's output and state step (O = Qb S + M Delta, Delta by block
@@ -51,8 +51,7 @@
 //   B: operand: the decayed sub-tile products (A, M) of chunk c, then the cumulative
 //      log-decay of chunk c + 1;  state: X = Diag(beta)(V - Kb S) of chunk c;
 //   C: operand: per-channel decay factors of chunk c + 1;  state: the four 16 x 16
-//      diagonal inverses (I + A_II)^{-1} of chunk c, one per wavefront;
-//   D: nothing (the last window closes the factors).
+//      diagonal inverses (I + A_II)^{-1} of chunk c, one per wavefront.
 // Operands read by the state role one iteration after they were written (Qb, Kt^T,
 // Lambda, beta) alternate between two LDS copies by chunk parity; the rest are
 // written and read in windows that a barrier separates.
@@ -81,7 +80,8 @@ constexpr int LAM = AII + 4 * 1024;         // Lambda, state row order [2 pariti
 constexpr int BETA = LAM + 2 * 512;         // [2 parities][64] fp32
 constexpr int OFF = BETA + 512;             // column side of pair (I, J < I): [6][4][64][16]
 constexpr int TOT = OFF + 6 * 4096;         // sub-tile decay totals [4][128] fp32
-constexpr int FAC = TOT + 4 * 128 * 4;      // per (sub-tile, channel) factors [4][3][128]
+constexpr int TOTL = TOT + 4 * 128 * 4;     // the same times log2 e
+constexpr int FAC = TOTL + 4 * 128 * 4;     // per (sub-tile, channel) factors [4][3][128]
 constexpr int FOFF = FAC + 4 * 3 * 128 * 4; // e^{R_I - R_J}, I > J: [6][128]
 constexpr int BYTES = FOFF + 6 * 128 * 4;
 constexpr int ORD = OFF;                    // sequence order (packed input) [<= 256], start only
@@ -128,20 +128,6 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_shr(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
-}
-
-// Inclusive prefix sum over the 16 lanes of a DPP row (lane & 15 = row index).
-__device__ __forceinline__ float row_scan16(float x) {
-  x += dpp_shr<0x111>(x);   // row_shr:1
-  x += dpp_shr<0x112>(x);   // row_shr:2
-  x += dpp_shr<0x114>(x);   // row_shr:4
-  x += dpp_shr<0x118>(x);   // row_shr:8
-  return x;
-}
-
 __device__ __forceinline__ bf16x8_t to_frag(const float (&x)[8]) {
   bf16x8_t f;
 #pragma unroll
@@ -181,6 +167,12 @@ __device__ __forceinline__ f32x4_t mma16(const bf16x4_t& a, const bf16x4_t& b, c
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
+// Compile-time sub-tile index for the per-sub-tile variants.
+template <int N>
+struct Ic {
+  static constexpr int value = N;
+};
+
 // Off-diagonal sub-tile pairs J < I -> 0..5.
 __device__ __forceinline__ constexpr int off_id(int I, int J) { return I * (I - 1) / 2 + J; }
 
@@ -209,11 +201,14 @@ __device__ __forceinline__ void operand_role(const FusedParams& p, char* smem, c
   const int H = p.H;
   const uint32_t rs = static_cast<uint32_t>(H) * kD * 2;   // token row stride (bytes)
 
+  // Prefetches are issued every iteration, past the last chunk too (an empty range:
+  // every load returns 0 and touches no memory), so that the loop issues the same
+  // sequence of loads on every path and the compiler's wait counts stay exact.
   auto rows = [&](const int c, int64_t& base, uint32_t& bytes) {
     const int t0 = tok0 + c * kCh;
     const int nrow = min(kCh, len - c * kCh);
     base = static_cast<int64_t>(t0) * H + h;
-    bytes = (nrow - 1) * rs + kD * 2;   // rows past the end read 0
+    bytes = nrow > 0 ? (nrow - 1) * rs + kD * 2 : 0;   // rows past the end read 0
     return nrow;
   };
   const uint32_t row = (16 * I + l16) * rs;
@@ -224,7 +219,7 @@ __device__ __forceinline__ void operand_role(const FusedParams& p, char* smem, c
     const auto rg = make_rsrc(p.g + base * kD, bytes);
 #pragma unroll
     for (int b = 0; b < 4; ++b) in.g[b] = buf_ld128(rg, row + (32 * b + 8 * g4) * 2, 0);
-    const auto rb = make_rsrc(p.beta + base, (nrow - 1) * H * 2 + 2);
+    const auto rb = make_rsrc(p.beta + base, nrow > 0 ? (nrow - 1) * H * 2 + 2 : 0);
     in.beta = buf_ld16(rb, (16 * I + l16) * H * 2, 0);
   };
   auto load_keys = [&](const int c, KeyIn& in) {
@@ -255,25 +250,42 @@ __device__ __forceinline__ void operand_role(const FusedParams& p, char* smem, c
   float L[4][8];             // inclusive sum of g over the sub-tile's rows up to this one
   float beta_t = 0.f;
 
-  // E1: cumulative log-decay of chunk c from the loaded inputs, sub-tile totals and
-  // beta to LDS.
+  // E1: cumulative log-decay of chunk c from the loaded g, sub-tile totals and beta to
+  // LDS.  On the matrix cores: the product of g's fragment with sel[hs] gives, in
+  // accumulator layout, g transposed (lane (t, g): tokens 4 g .. +3 of channel
+  // 32 b + 8 (l16 / 4) + 4 hs + l16 % 4); read back as a 16-deep A operand that is G^T,
+  // and its product with the lower-triangular ones U[s][t] = (s <= t) is L^T, which in
+  // accumulator layout puts token l16's channels 32 b + 8 g + 4 hs .. +3 in lane
+  // (l16, g) -- the fragment layout.  g is exact in bf16 and the sums are fp32.
+  bf16x4_t tri;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) tri[i] = 4 * g4 + i <= l16 ? 0x3F80 : 0;
   auto e1 = [&](const int c) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < 4; ++b) {
+      const bf16x8_t gf = __builtin_bit_cast(bf16x8_t, dn.g[b]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t wg = static_cast<uint32_t>(dn.g[b][e >> 1]);
-        L[b][e] = row_scan16((e & 1) ? bf16hi(wg) : bf16lo(wg));
+      for (int hs = 0; hs < 2; ++hs) {
+        const f32x4_t gt = mma(gf, sel[hs], f32x4_t{0.f, 0.f, 0.f, 0.f});
+        const f32x4_t lt = mma16(acc_frag4(gt), tri, f32x4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int i = 0; i < 4; ++i) L[b][4 * hs + i] = lt[i];
       }
+    }
     beta_t = bf16lo(dn.beta);
-    if (l16 == 15) {   // sub-tile totals R_I - R_{I-1}
+    if (l16 == 15) {   // sub-tile totals R_I - R_{I-1}, and times log2 e
       float* tot = reinterpret_cast<float*>(smem + fl::TOT) + I * kD;
+      float* totl = reinterpret_cast<float*>(smem + fl::TOTL) + I * kD;
 #pragma unroll
       for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
+        for (int hh = 0; hh < 2; ++hh) {
           *reinterpret_cast<float4*>(tot + 32 * b + 8 * g4 + 4 * hh) =
               float4{L[b][4 * hh], L[b][4 * hh + 1], L[b][4 * hh + 2], L[b][4 * hh + 3]};
+          *reinterpret_cast<float4*>(totl + 32 * b + 8 * g4 + 4 * hh) =
+              float4{L[b][4 * hh] * kLog2e, L[b][4 * hh + 1] * kLog2e, L[b][4 * hh + 2] * kLog2e,
+                     L[b][4 * hh + 3] * kLog2e};
+        }
     }
     if (g4 == 0) reinterpret_cast<float*>(smem + fl::BETA)[(c & 1) * kCh + 16 * I + l16] = beta_t;
   };
@@ -309,122 +321,164 @@ __device__ __forceinline__ void operand_role(const FusedParams& p, char* smem, c
   };
 
   // E2: decayed operands of chunk c.  rowf = e^{L_t - R_I} >= 1, colf = e^{R_I - L_t}
-  // <= 1 (R_I: end of the sub-tile).
-  auto e2 = [&](const int c, bf16x8_t (&fKr)[4], bf16x8_t (&fQr)[4], bf16x8_t (&fKc)[4]) {
-    const float* tot = reinterpret_cast<const float*>(smem + fl::TOT) + I * kD;
+  // <= 1 (R_I: end of the sub-tile).  One variant per sub-tile (IC = I): the factors of
+  // the off-diagonal column sides it writes are read at the top of each block, ahead of
+  // the exponentials.
+  auto e2_t = [&](auto Ic_, const int c, bf16x8_t (&fKr)[4], bf16x8_t (&fQr)[4], bf16x8_t (&fKc)[4]) {
+    constexpr int IC = decltype(Ic_)::value;
+    constexpr int NOFF = 3 - IC;   // pairs (a, IC), a = IC + 1 .. 3
+    const float* totl = reinterpret_cast<const float*>(smem + fl::TOTL) + IC * kD;
     const float* fac = reinterpret_cast<const float*>(smem + fl::FAC);
     const float* foff = reinterpret_cast<const float*>(smem + fl::FOFF);
     const int qb_off = fl::QB + (c & 1) * 16384, kt_off = fl::KTT + (c & 1) * 16384;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      float kr[8], qr[8], kc[8], kb[8], qb[8], kt[8];
+      float4 fo[NOFF > 0 ? NOFF : 1][2];
+#pragma unroll
+      for (int x = 0; x < NOFF; ++x)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          fo[x][hh] = *reinterpret_cast<const float4*>(foff + off_id(IC + 1 + x, IC) * kD + 32 * b + 8 * g4 + 4 * hh);
+      // results are packed to bf16 pairs as soon as a pair of channels is done, which
+      // keeps the fp32 intermediates of only two channels live
+      uint32_t pkr[4], pqr[4], pkc[4], pkb[4], pqb[4], pkt[4];
+      uint32_t poff[NOFF > 0 ? NOFF : 1][4];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int c0 = 32 * b + 8 * g4 + 4 * hh;
-        const float4 t4 = *reinterpret_cast<const float4*>(tot + c0);
-        const float4 fK = *reinterpret_cast<const float4*>(fac + (I * 3 + 0) * kD + c0);
-        const float4 fQ = *reinterpret_cast<const float4*>(fac + (I * 3 + 1) * kD + c0);
-        const float4 fN = *reinterpret_cast<const float4*>(fac + (I * 3 + 2) * kD + c0);
+        const float4 t4 = *reinterpret_cast<const float4*>(totl + c0);
+        const float4 fK = *reinterpret_cast<const float4*>(fac + (IC * 3 + 0) * kD + c0);
+        const float4 fQ = *reinterpret_cast<const float4*>(fac + (IC * 3 + 1) * kD + c0);
+        const float4 fN = *reinterpret_cast<const float4*>(fac + (IC * 3 + 2) * kD + c0);
         const float tv[4] = {t4.x, t4.y, t4.z, t4.w}, vK[4] = {fK.x, fK.y, fK.z, fK.w};
         const float vQ[4] = {fQ.x, fQ.y, fQ.z, fQ.w}, vN[4] = {fN.x, fN.y, fN.z, fN.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int e = 4 * hh + i;
-          const uint32_t kw = static_cast<uint32_t>(kq.k[b][e >> 1]);
-          const uint32_t qw = static_cast<uint32_t>(kq.q[b][e >> 1]);
-          const float kv = (e & 1) ? bf16hi(kw) : bf16lo(kw);
-          const float qv = (e & 1) ? bf16hi(qw) : bf16lo(qw);
-          const float d = (L[b][e] - tv[i]) * kLog2e;      // >= 0
-          const float rowf = fast_exp2(d), colf = fast_exp2(-d);
-          kr[e] = kv * rowf;
-          qr[e] = qv * rowf;
-          kc[e] = kv * colf;
-          kb[e] = kr[e] * vK[i];     // -K e^{L}
-          qb[e] = qr[e] * vQ[i];     // scale Q e^{L}
-          kt[e] = kc[e] * vN[i];     // K e^{Ln - L}
+        for (int i2 = 0; i2 < 2; ++i2) {
+          float kr[2], qr[2], kc[2], kb[2], qb[2], kt[2];
+          const uint32_t kw = static_cast<uint32_t>(kq.k[b][2 * hh + i2]);
+          const uint32_t qw = static_cast<uint32_t>(kq.q[b][2 * hh + i2]);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int i = 2 * i2 + j, e = 4 * hh + i;
+            const float kv = j ? bf16hi(kw) : bf16lo(kw);
+            const float qv = j ? bf16hi(qw) : bf16lo(qw);
+            const float d = __builtin_fmaf(L[b][e], kLog2e, -tv[i]);   // (L - R_I) log2 e >= 0
+            const float rowf = fast_exp2(d), colf = fast_exp2(-d);
+            kr[j] = kv * rowf;
+            qr[j] = qv * rowf;
+            kc[j] = kv * colf;
+            kb[j] = kr[j] * vK[i];     // -K e^{L}
+            qb[j] = qr[j] * vQ[i];     // scale Q e^{L}
+            kt[j] = kc[j] * vN[i];     // K e^{Ln - L}
+          }
+          const int w = 2 * hh + i2;   // dword of the fragment
+          pkr[w] = pack_bf16x2(kr[0], kr[1]);
+          pqr[w] = pack_bf16x2(qr[0], qr[1]);
+          pkc[w] = pack_bf16x2(kc[0], kc[1]);
+          pkb[w] = pack_bf16x2(kb[0], kb[1]);
+          pqb[w] = pack_bf16x2(qb[0], qb[1]);
+          pkt[w] = pack_bf16x2(kt[0], kt[1]);
+          // column side of the off-diagonal pairs (a > I, I): K e^{R_a - L}
+#pragma unroll
+          for (int x = 0; x < NOFF; ++x) {
+            const float f0 = i2 ? fo[x][hh].z : fo[x][hh].x, f1 = i2 ? fo[x][hh].w : fo[x][hh].y;
+            poff[x][w] = pack_bf16x2(kc[0] * f0, kc[1] * f1);
+          }
         }
       }
-      fKr[b] = to_frag(kr);
-      fQr[b] = to_frag(qr);
-      fKc[b] = to_frag(kc);
-      *reinterpret_cast<bf16x8_t*>(smem + fl::KBN + frag_at(I, b, 4, lane)) = to_frag(kb);
-      *reinterpret_cast<bf16x8_t*>(smem + qb_off + frag_at(I, b, 4, lane)) = to_frag(qb);
+      auto frag = [](const uint32_t (&w)[4]) { return __builtin_bit_cast(bf16x8_t, uint4{w[0], w[1], w[2], w[3]}); };
+      fKr[b] = frag(pkr);
+      fQr[b] = frag(pqr);
+      fKc[b] = frag(pkc);
+      *reinterpret_cast<bf16x8_t*>(smem + fl::KBN + frag_at(IC, b, 4, lane)) = frag(pkb);
+      *reinterpret_cast<bf16x8_t*>(smem + qb_off + frag_at(IC, b, 4, lane)) = frag(pqb);
       // Kt^T: the products with sel[hs] give, in lane (l16, g), tokens 16 I + 4 g .. +3
       // of the channel of state row 16 (2 b + hs) + l16 -- half of that lane's
       // fragment (state tile 2 b + hs, s-block I / 2), elements 4 (I % 2) .. +3
       {
-        const bf16x8_t fkt = to_frag(kt);
+        const bf16x8_t fkt = frag(pkt);
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs) {
           const f32x4_t tr = mma(fkt, sel[hs], f32x4_t{0.f, 0.f, 0.f, 0.f});
-          *reinterpret_cast<uint2*>(smem + kt_off + frag_at(2 * b + hs, I >> 1, 2, lane) + 8 * (I & 1)) =
+          *reinterpret_cast<uint2*>(smem + kt_off + frag_at(2 * b + hs, IC >> 1, 2, lane) + 8 * (IC & 1)) =
               uint2{pack_bf16x2(tr[0], tr[1]), pack_bf16x2(tr[2], tr[3])};
         }
       }
-      // column side of the off-diagonal pairs (I' > I, I): K e^{R_I' - L}
 #pragma unroll
-      for (int a = 1; a < 4; ++a) {
-        if (a > I) {
-          float x[8];
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const float4 f4 = *reinterpret_cast<const float4*>(foff + off_id(a, I) * kD + 32 * b + 8 * g4 + 4 * hh);
-            x[4 * hh] = kc[4 * hh] * f4.x;
-            x[4 * hh + 1] = kc[4 * hh + 1] * f4.y;
-            x[4 * hh + 2] = kc[4 * hh + 2] * f4.z;
-            x[4 * hh + 3] = kc[4 * hh + 3] * f4.w;
-          }
-          *reinterpret_cast<bf16x8_t*>(smem + fl::OFF + off_id(a, I) * 4096 + frag_at(0, b, 4, lane)) = to_frag(x);
-        }
-      }
+      for (int x = 0; x < NOFF; ++x)
+        *reinterpret_cast<bf16x8_t*>(smem + fl::OFF + off_id(IC + 1 + x, IC) * 4096 + frag_at(0, b, 4, lane)) = frag(poff[x]);
+    }
+  };
+  auto e2 = [&](const int c, bf16x8_t (&fKr)[4], bf16x8_t (&fQr)[4], bf16x8_t (&fKc)[4]) {
+    switch (I) {
+      case 0: e2_t(Ic<0>{}, c, fKr, fQr, fKc); break;
+      case 1: e2_t(Ic<1>{}, c, fKr, fQr, fKc); break;
+      case 2: e2_t(Ic<2>{}, c, fKr, fQr, fKc); break;
+      default: e2_t(Ic<3>{}, c, fKr, fQr, fKc); break;
     }
   };
 
   // Decayed sub-tile products of chunk c, transposed: C[s, t] = sum_c colside[s, c]
   // rowside[t, c]; lane (t, g) holds s = 16 J + 4 g + i.  Writes M's blocks, -A_IJ
   // (J < I) and the beta-scaled diagonal block A_II (masked to s < t) for its inverse.
-  auto products = [&](const bf16x8_t (&fKr)[4], const bf16x8_t (&fQr)[4], const bf16x8_t (&fKc)[4]) {
+  // One straight-line variant per sub-tile (IC = I), so that the I + 1 pairs' product
+  // chains interleave.
+  auto products_t = [&](auto Ic, const bf16x8_t (&fKr)[4], const bf16x8_t (&fQr)[4],
+                        const bf16x8_t (&fKc)[4]) {
+    constexpr int IC = decltype(Ic)::value;
+    f32x4_t pa[IC + 1], pm[IC + 1];
 #pragma unroll
-    for (int J = 0; J < 4; ++J) {
-      if (J <= I) {
-        f32x4_t pa = {0.f, 0.f, 0.f, 0.f}, pm = pa;
+    for (int J = 0; J <= IC; ++J) {
+      pa[J] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      pm[J] = pa[J];
+    }
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const bf16x8_t cs = J == I ? fKc[b] : lds_frag(smem, fl::OFF + off_id(I, J) * 4096 + frag_at(0, b, 4, lane));
-          pa = mma(cs, fKr[b], pa);
-          pm = mma(cs, fQr[b], pm);
-        }
-        // masks only on the diagonal pair (s = 16 I + 4 g + i against t = 16 I + l16)
-        f32x4_t av;
-        float mv[4];
+    for (int b = 0; b < 4; ++b) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          av[i] = beta_t * pa[i];
-          mv[i] = p.scale * pm[i];
-          if (J == I) {
-            av[i] = 4 * g4 + i < l16 ? av[i] : 0.f;
-            mv[i] = 4 * g4 + i <= l16 ? mv[i] : 0.f;
-          }
-        }
-        // M[t][s]: fragment (t-tile I, s-block J/2), elements 4 (J%2) .. +3
-        *reinterpret_cast<uint2*>(smem + fl::MF + frag_at(I, J >> 1, 2, lane) + 8 * (J & 1)) =
-            uint2{pack_bf16x2(mv[0], mv[1]), pack_bf16x2(mv[2], mv[3])};
-        if (J < I)   // -A_IJ as a 16x16x16 A operand: lane (t, g) holds columns 4 g .. +3
-          *reinterpret_cast<uint2*>(smem + fl::AOF + off_id(I, J) * 512 + lane * 8) =
-              uint2{pack_bf16x2(-av[0], -av[1]), pack_bf16x2(-av[2], -av[3])};
-        else
-          *reinterpret_cast<f32x4_t*>(smem + fl::AII + I * 1024 + lane * 16) = av;
+      for (int J = 0; J <= IC; ++J) {
+        const bf16x8_t cs = J == IC ? fKc[b] : lds_frag(smem, fl::OFF + off_id(IC, J) * 4096 + frag_at(0, b, 4, lane));
+        pa[J] = mma(cs, fKr[b], pa[J]);
+        pm[J] = mma(cs, fQr[b], pm[J]);
       }
+    }
+#pragma unroll
+    for (int J = 0; J <= IC; ++J) {
+      // masks only on the diagonal pair (s = 16 I + 4 g + i against t = 16 I + l16)
+      f32x4_t av;
+      float mv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        av[i] = beta_t * pa[J][i];
+        mv[i] = p.scale * pm[J][i];
+        if (J == IC) {
+          av[i] = 4 * g4 + i < l16 ? av[i] : 0.f;
+          mv[i] = 4 * g4 + i <= l16 ? mv[i] : 0.f;
+        }
+      }
+      // M[t][s]: fragment (t-tile I, s-block J/2), elements 4 (J%2) .. +3
+      *reinterpret_cast<uint2*>(smem + fl::MF + frag_at(IC, J >> 1, 2, lane) + 8 * (J & 1)) =
+          uint2{pack_bf16x2(mv[0], mv[1]), pack_bf16x2(mv[2], mv[3])};
+      if (J < IC)   // -A_IJ as a 16x16x16 A operand: lane (t, g) holds columns 4 g .. +3
+        *reinterpret_cast<uint2*>(smem + fl::AOF + off_id(IC, J) * 512 + lane * 8) =
+            uint2{pack_bf16x2(-av[0], -av[1]), pack_bf16x2(-av[2], -av[3])};
+      else
+        *reinterpret_cast<f32x4_t*>(smem + fl::AII + IC * 1024 + lane * 16) = av;
+    }
+  };
+  auto products = [&](const bf16x8_t (&fKr)[4], const bf16x8_t (&fQr)[4], const bf16x8_t (&fKc)[4]) {
+    switch (I) {
+      case 0: products_t(Ic<0>{}, fKr, fQr, fKc); break;
+      case 1: products_t(Ic<1>{}, fKr, fQr, fKc); break;
+      case 2: products_t(Ic<2>{}, fKr, fQr, fKc); break;
+      default: products_t(Ic<3>{}, fKr, fQr, fKc); break;
     }
   };
 
   // prologue: chunk 0's decay and factors
-  if (nchunks > 0) {
-    load_decay(0, dn);
-    load_keys(0, kq);
-    e1(0);
-    if (nchunks > 1) load_decay(1, dn);
-  }
+  load_keys(0, kq);
+  load_decay(0, dn);
+  if (nchunks > 0) e1(0);
+  load_decay(1, dn);
   lds_barrier();
   if (nchunks > 0) factors(0);
   lds_barrier();
@@ -434,20 +488,15 @@ __device__ __forceinline__ void operand_role(const FusedParams& p, char* smem, c
     l16 = lane & 15;
     g4 = lane >> 4;
     bf16x8_t fKr[4], fQr[4], fKc[4];
-    if (c < nchunks) {
-      e2(c, fKr, fQr, fKc);
-      if (c + 1 < nchunks) load_keys(c + 1, kq);
-    }
+    if (c < nchunks) e2(c, fKr, fQr, fKc);
+    load_keys(c + 1, kq);
     lds_barrier();                                                          // A
     if (c < nchunks) products(fKr, fQr, fKc);
-    if (c + 1 < nchunks) {
-      e1(c + 1);
-      if (c + 2 < nchunks) load_decay(c + 2, dn);
-    }
+    if (c + 1 < nchunks) e1(c + 1);
+    load_decay(c + 2, dn);
     lds_barrier();                                                          // B
     if (c + 1 < nchunks) factors(c + 1);
     lds_barrier();                                                          // C
-    lds_barrier();                                                          // D
   }
 }
 
@@ -482,10 +531,12 @@ __device__ __forceinline__ void state_role(const FusedParams& p, char* smem, con
   // v of chunk c for this wavefront's value columns: lane (t, g) loads token 16 tt + t,
   // columns col0 + 16 u + 4 g .. +3 (rows past the end read 0)
   i32x2_t vin[2][4];
+  // v loads and output stores are issued every iteration (empty ranges outside the
+  // sequence), for the same reason as the operand role's prefetches.
   auto load_v = [&](const int c) {
     const int t0 = tok0 + c * kCh;
     const int nrow = min(kCh, len - c * kCh);
-    const auto rv = make_rsrc(p.v + (static_cast<int64_t>(t0) * H + h) * kD, (nrow - 1) * rs + kD * 2);
+    const auto rv = make_rsrc(p.v + (static_cast<int64_t>(t0) * H + h) * kD, nrow > 0 ? (nrow - 1) * rs + kD * 2 : 0);
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -599,80 +650,84 @@ __device__ __forceinline__ void state_role(const FusedParams& p, char* smem, con
   };
 
   // Output and state step of chunk cs, whose operands are in LDS; Y holds its X and S
-  // its starting state.
+  // its starting state.  With cs < 0 only the (empty) stores are issued.
   auto apply = [&](const int cs) {
-    const int qb_off = fl::QB + (cs & 1) * 16384, kt_off = fl::KTT + (cs & 1) * 16384;
-    bf16x8_t Sb[2][4];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) Sb[u][b] = acc_frag(S[u][2 * b], S[u][2 * b + 1]);
+    const bool act = cs >= 0;
     // O^T = S^T Qb^T + Delta^T M^T: lane (t, g) holds value columns 4 g .. +3 of token t
     f32x4_t o[2][4];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) o[u][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    bf16x8_t F[2][4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) F[0][tt] = lds_frag(smem, qb_off + frag_at(tt, 0, 4, lane));
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      if (b < 3) {
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) F[(b + 1) & 1][tt] = lds_frag(smem, qb_off + frag_at(tt, b + 1, 4, lane));
-      }
+    bf16x8_t Db[2][2];
+    const int qb_off = fl::QB + (cs & 1) * 16384, kt_off = fl::KTT + (cs & 1) * 16384;
+    if (act) {
+      bf16x8_t Sb[2][4];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) o[u][tt] = mma(Sb[u][b], F[b & 1][tt], o[u][tt]);
-    }
-    // Delta_i = T_ii (Y_i - sum_{m<i} A_im Delta_m), both column halves interleaved
-    bf16x4_t fa[6], ft[4];
+        for (int b = 0; b < 4; ++b) Sb[u][b] = acc_frag(S[u][2 * b], S[u][2 * b + 1]);
+      bf16x8_t F[2][4];
 #pragma unroll
-    for (int x = 0; x < 6; ++x) fa[x] = lds_frag4(smem, fl::AOF + x * 512 + lane * 8);
+      for (int tt = 0; tt < 4; ++tt) F[0][tt] = lds_frag(smem, qb_off + frag_at(tt, 0, 4, lane));
 #pragma unroll
-    for (int x = 0; x < 4; ++x) ft[x] = lds_frag4(smem, fl::TDF + x * 512 + lane * 8);
-    bf16x4_t Dq[2][4];
+      for (int b = 0; b < 4; ++b) {
+        if (b < 3) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+          for (int tt = 0; tt < 4; ++tt) F[(b + 1) & 1][tt] = lds_frag(smem, qb_off + frag_at(tt, b + 1, 4, lane));
+        }
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        f32x4_t w = Y[u][i];
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-          if (m < i) w = mma16(fa[off_id(i, m)], Dq[u][m], w);
-        Dq[u][i] = acc_frag4(mma16(ft[i], acc_frag4(w), f32x4_t{0.f, 0.f, 0.f, 0.f}));
+          for (int tt = 0; tt < 4; ++tt) o[u][tt] = mma(Sb[u][b], F[b & 1][tt], o[u][tt]);
       }
-    }
-    // Delta as 32-deep fragments: tiles (2 b, 2 b + 1) side by side
-    bf16x8_t Db[2][2];
+      // Delta_i = T_ii (Y_i - sum_{m<i} A_im Delta_m), both column halves interleaved
+      bf16x4_t fa[6], ft[4];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+      for (int x = 0; x < 6; ++x) fa[x] = lds_frag4(smem, fl::AOF + x * 512 + lane * 8);
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-        Db[u][b] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(Dq[u][2 * b], Dq[u][2 * b + 1], 0, 1, 2, 3, 4, 5, 6, 7));
-    // + Delta^T M^T: M fragments (tt, 0) for every tt, (2, 1) and (3, 1)
-    {
-      bf16x8_t M0[4], M1[2];
+      for (int x = 0; x < 4; ++x) ft[x] = lds_frag4(smem, fl::TDF + x * 512 + lane * 8);
+      bf16x4_t Dq[2][4];
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) M0[tt] = lds_frag(smem, fl::MF + frag_at(tt, 0, 2, lane));
-      M1[0] = lds_frag(smem, fl::MF + frag_at(2, 1, 2, lane));
-      M1[1] = lds_frag(smem, fl::MF + frag_at(3, 1, 2, lane));
+      for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < 2; ++u) {
+          f32x4_t w = Y[u][i];
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) o[u][tt] = mma(Db[u][0], M0[tt], o[u][tt]);
-        o[u][2] = mma(Db[u][1], M1[0], o[u][2]);
-        o[u][3] = mma(Db[u][1], M1[1], o[u][3]);
+          for (int m = 0; m < 4; ++m)
+            if (m < i) w = mma16(fa[off_id(i, m)], Dq[u][m], w);
+          Dq[u][i] = acc_frag4(mma16(ft[i], acc_frag4(w), f32x4_t{0.f, 0.f, 0.f, 0.f}));
+        }
+      }
+      // Delta as 32-deep fragments: tiles (2 b, 2 b + 1) side by side
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          Db[u][b] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(Dq[u][2 * b], Dq[u][2 * b + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+      // + Delta^T M^T: M fragments (tt, 0) for every tt, (2, 1) and (3, 1)
+      {
+        bf16x8_t M0[4], M1[2];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) M0[tt] = lds_frag(smem, fl::MF + frag_at(tt, 0, 2, lane));
+        M1[0] = lds_frag(smem, fl::MF + frag_at(2, 1, 2, lane));
+        M1[1] = lds_frag(smem, fl::MF + frag_at(3, 1, 2, lane));
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) o[u][tt] = mma(Db[u][0], M0[tt], o[u][tt]);
+          o[u][2] = mma(Db[u][1], M1[0], o[u][2]);
+          o[u][3] = mma(Db[u][1], M1[1], o[u][3]);
+        }
       }
     }
     // output rows of chunk cs: plain stores, so that the cache joins the wavefronts'
     // pieces of a row into whole lines
     {
       const int t0 = tok0 + cs * kCh;
-      const int nrow = min(kCh, len - cs * kCh);
-      const auto ro = make_rsrc(p.out + (static_cast<int64_t>(t0) * H + h) * kD, (nrow - 1) * rs + kD * 2);
+      const int nrow = act ? min(kCh, len - cs * kCh) : 0;
+      const auto ro = make_rsrc(p.out + (static_cast<int64_t>(act ? t0 : tok0) * H + h) * kD,
+                                nrow > 0 ? (nrow - 1) * rs + kD * 2 : 0);
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -681,6 +736,7 @@ __device__ __forceinline__ void state_role(const FusedParams& p, char* smem, con
                            static_cast<int>(pack_bf16x2(o[u][tt][2], o[u][tt][3]))},
                    ro, (16 * tt + l16) * rs + (col0 + 16 * u + 4 * g4) * 2, 0);
     }
+    if (!act) return;
     // S <- Diag(Lambda) S + Kt^T Delta, Kt fragments one accumulator tile ahead
     const float* lam = reinterpret_cast<const float*>(smem + fl::LAM) + (cs & 1) * kD;
     bf16x8_t K2[2][2];
@@ -702,20 +758,22 @@ __device__ __forceinline__ void state_role(const FusedParams& p, char* smem, con
     }
   };
 
-  if (nchunks > 0) load_v(0);
+  // The state role's work is a chain of dependent matrix-core products; the operand
+  // role on the same SIMD streams independent vector-ALU work.  Issuing the state
+  // role's instructions first whenever they are ready keeps its chain moving and lets
+  // the operand role fill the gaps.
+  __builtin_amdgcn_s_setprio(3);
+  load_v(0);
   lds_barrier();
   lds_barrier();
   for (int c = 0; c <= nchunks; ++c) {
-    if (c > 0) apply(c - 1);
+    apply(c - 1);
     lds_barrier();                                                          // A
-    if (c < nchunks) {
-      x_step(c);
-      if (c + 1 < nchunks) load_v(c + 1);
-    }
+    if (c < nchunks) x_step(c);
+    load_v(c + 1);
     lds_barrier();                                                          // B
     if (c < nchunks) inverse();
     lds_barrier();                                                          // C
-    lds_barrier();                                                          // D
   }
 
   if (p.sT != nullptr) {
