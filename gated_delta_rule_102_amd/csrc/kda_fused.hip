@@ -545,14 +545,13 @@ __device__ __forceinline__ void state_role(const FusedParams& p, char* smem, con
   };
 
   f32x4_t Y[2][4];      // Diag(beta)(V - Kb S) of the chunk being applied
+  bf16x8_t Sb[2][4];    // its starting state as bf16 operand fragments
 
   // X of chunk c: Y = Diag(beta) (V - Kb S) (the stored -Kb makes the product an
   // addition).  V arrives row-major (lane: token l16, value columns 4 g .. +3) and
-  // enters the accumulator layout as the product V I_16, exact in fp32; the two
-  // products are summed by the vector unit (a 16x16x16 result is not fed to a
-  // 16x16x32 product as its accumulator).
+  // enters the accumulator layout as the product V I_16, exact in fp32; that product
+  // (the same 16 x 16 accumulator layout) is the accumulator the -Kb S products add to.
   auto x_step = [&](const int c) {
-    bf16x8_t Sb[2][4];    // the state at the chunk start, as bf16 operand fragments
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -560,7 +559,8 @@ __device__ __forceinline__ void state_role(const FusedParams& p, char* smem, con
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) Y[u][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int tt = 0; tt < 4; ++tt)
+        Y[u][tt] = mma16(__builtin_bit_cast(bf16x4_t, vin[u][tt]), eye, f32x4_t{0.f, 0.f, 0.f, 0.f});
     bf16x8_t F[2][4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) F[0][tt] = lds_frag(smem, fl::KBN + frag_at(tt, 0, 4, lane));
@@ -581,11 +581,10 @@ __device__ __forceinline__ void state_role(const FusedParams& p, char* smem, con
       const float4 b4 = *reinterpret_cast<const float4*>(betas + 16 * tt + 4 * g4);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const f32x4_t vt = mma16(__builtin_bit_cast(bf16x4_t, vin[u][tt]), eye, f32x4_t{0.f, 0.f, 0.f, 0.f});
-        Y[u][tt][0] = (Y[u][tt][0] + vt[0]) * b4.x;
-        Y[u][tt][1] = (Y[u][tt][1] + vt[1]) * b4.y;
-        Y[u][tt][2] = (Y[u][tt][2] + vt[2]) * b4.z;
-        Y[u][tt][3] = (Y[u][tt][3] + vt[3]) * b4.w;
+        Y[u][tt][0] *= b4.x;
+        Y[u][tt][1] *= b4.y;
+        Y[u][tt][2] *= b4.z;
+        Y[u][tt][3] *= b4.w;
       }
     }
   };
@@ -649,8 +648,8 @@ __device__ __forceinline__ void state_role(const FusedParams& p, char* smem, con
         uint2{pack_bf16x2(t3[0], t3[1]), pack_bf16x2(t3[2], t3[3])};
   };
 
-  // Output and state step of chunk cs, whose operands are in LDS; Y holds its X and S
-  // its starting state.  With cs < 0 only the (empty) stores are issued.
+  // Output and state step of chunk cs, whose operands are in LDS; Y holds its X, S and
+  // Sb its starting state.  With cs < 0 only the (empty) stores are issued.
   auto apply = [&](const int cs) {
     const bool act = cs >= 0;
     // O^T = S^T Qb^T + Delta^T M^T: lane (t, g) holds value columns 4 g .. +3 of token t
@@ -662,11 +661,6 @@ __device__ __forceinline__ void state_role(const FusedParams& p, char* smem, con
     bf16x8_t Db[2][2];
     const int qb_off = fl::QB + (cs & 1) * 16384, kt_off = fl::KTT + (cs & 1) * 16384;
     if (act) {
-      bf16x8_t Sb[2][4];
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) Sb[u][b] = acc_frag(S[u][2 * b], S[u][2 * b + 1]);
       bf16x8_t F[2][4];
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) F[0][tt] = lds_frag(smem, qb_off + frag_at(tt, 0, 4, lane));
