@@ -167,6 +167,16 @@ __device__ __forceinline__ f32x4_t mma16(const bf16x4_t& a, const bf16x4_t& b, c
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
+// Two 16-deep operands side by side as one 32-deep operand: lane (l16, g) carries
+// x's elements 4 g .. +3 then y's.  With both sides of a 16x16x32 product built this
+// way the contraction runs over x's 16 and y's 16 terms, so
+//     mma(cat(a1, a2), cat(b1, b2), c) = a1 b1 + a2 b2 + c,
+// one instruction where two 16x16x16 products take twice as long (on gfx950 a
+// 16x16x16 bf16 product occupies the matrix core as long as a 16x16x32 one).
+__device__ __forceinline__ bf16x8_t cat(const bf16x4_t& x, const bf16x4_t& y) {
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // Compile-time sub-tile index for the per-sub-tile variants.
 template <int N>
 struct Ic {
@@ -311,7 +321,7 @@ __device__ __forceinline__ void operand_role(const FusedParams& p, char* smem, c
       fac[(m * 3 + 1) * kD + ch] = p.scale * em;                        // scale e^{R_m}
       fac[(m * 3 + 2) * kD + ch] = fast_exp2((R[3] - R[m]) * kLog2e);   // e^{Ln - R_m}
 #pragma unroll
-      for (int a = 1; a < 4; ++a)
+      for (int a = 1; a < 3; ++a)   // (3, m) needs none: its column side is Kt
         if (a > m) foff[off_id(a, m) * kD + ch] = fast_exp2((R[a] - R[m]) * kLog2e);
       if (m == 0) {   // Lambda in state row order: row r holds channel sigma(r)
         const int r = 32 * (ch >> 5) + 16 * ((ch >> 2) & 1) + 4 * ((ch >> 3) & 3) + (ch & 3);
@@ -326,7 +336,9 @@ __device__ __forceinline__ void operand_role(const FusedParams& p, char* smem, c
   // the exponentials.
   auto e2_t = [&](auto Ic_, const int c, bf16x8_t (&fKr)[4], bf16x8_t (&fQr)[4], bf16x8_t (&fKc)[4]) {
     constexpr int IC = decltype(Ic_)::value;
-    constexpr int NOFF = 3 - IC;   // pairs (a, IC), a = IC + 1 .. 3
+    // pairs (a, IC), a = IC + 1 .. 2, scaled here; the column side of (3, IC) is
+    // K e^{R_3 - L} = K e^{Ln - L} = Kt itself
+    constexpr int NOFF = IC < 2 ? 2 - IC : 0;
     const float* totl = reinterpret_cast<const float*>(smem + fl::TOTL) + IC * kD;
     const float* fac = reinterpret_cast<const float*>(smem + fl::FAC);
     const float* foff = reinterpret_cast<const float*>(smem + fl::FOFF);
@@ -378,7 +390,7 @@ __device__ __forceinline__ void operand_role(const FusedParams& p, char* smem, c
           pkb[w] = pack_bf16x2(kb[0], kb[1]);
           pqb[w] = pack_bf16x2(qb[0], qb[1]);
           pkt[w] = pack_bf16x2(kt[0], kt[1]);
-          // column side of the off-diagonal pairs (a > I, I): K e^{R_a - L}
+          // column side of the off-diagonal pairs (a = I + 1 .. 2, I): K e^{R_a - L}
 #pragma unroll
           for (int x = 0; x < NOFF; ++x) {
             const float f0 = i2 ? fo[x][hh].z : fo[x][hh].x, f1 = i2 ? fo[x][hh].w : fo[x][hh].y;
@@ -407,6 +419,8 @@ __device__ __forceinline__ void operand_role(const FusedParams& p, char* smem, c
 #pragma unroll
       for (int x = 0; x < NOFF; ++x)
         *reinterpret_cast<bf16x8_t*>(smem + fl::OFF + off_id(IC + 1 + x, IC) * 4096 + frag_at(0, b, 4, lane)) = frag(poff[x]);
+      if (IC < 3)
+        *reinterpret_cast<bf16x8_t*>(smem + fl::OFF + off_id(3, IC < 3 ? IC : 0) * 4096 + frag_at(0, b, 4, lane)) = frag(pkt);
     }
   };
   auto e2 = [&](const int c, bf16x8_t (&fKr)[4], bf16x8_t (&fQr)[4], bf16x8_t (&fKc)[4]) {
@@ -687,9 +701,11 @@ __device__ __forceinline__ void state_role(const FusedParams& p, char* smem, con
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           f32x4_t w = Y[u][i];
-#pragma unroll
-          for (int m = 0; m < 4; ++m)
-            if (m < i) w = mma16(fa[off_id(i, m)], Dq[u][m], w);
+          if (i >= 2)   // A_i0 Delta_0 + A_i1 Delta_1 in one 32-deep product
+            w = mma(cat(fa[off_id(i, 0)], fa[off_id(i, 1)]), cat(Dq[u][0], Dq[u][1]), w);
+          else if (i == 1)
+            w = mma16(fa[off_id(1, 0)], Dq[u][0], w);
+          if (i == 3) w = mma16(fa[off_id(3, 2)], Dq[u][2], w);
           Dq[u][i] = acc_frag4(mma16(ft[i], acc_frag4(w), f32x4_t{0.f, 0.f, 0.f, 0.f}));
         }
       }
