@@ -24,8 +24,11 @@
 // whole chunk e^{-L} reaches e^{320}, so A and M are built from 16-row sub-tiles I
 // referenced to the cumulative decay R_I at the end of the sub-tile: the row side
 // carries e^{L_t - R_I} in [1, e^80], the column side e^{R_I - L_s} <= 1, both within
-// bf16 range; off-diagonal sub-tile pairs (I > J) scale the column side of J by
-// e^{R_I - R_J} <= 1.
+// bf16 range.  Off-diagonal pairs (I > J): for J = 0 the decay from the chunk start is
+// itself in range (L >= -80 over 16 tokens), so the pairs (I, 0), the diagonal (0, 0)
+// included, take Kb and Qb (the state step's operands) as row sides and K e^{-L} as
+// the column side; pairs (3, J) take Kt = K e^{Ln - L} = K e^{R_3 - L} as their column
+// side; pair (2, 1) scales sub-tile 1's column side by e^{R_2 - R_1} <= 1.
 //
 // Two roles share the workgroup's 8 wavefronts, one of each on every SIMD (wavefront
 // w runs on SIMD w % 4), so that one role's vector-ALU work and the other's
@@ -78,13 +81,15 @@ constexpr int TDF = AOF + 6 * 512;          // T_II:        [4][64 lanes] x 8 B
 constexpr int AII = TDF + 4 * 512;          // beta-scaled A_II^T, accumulator layout [4][64] x 16 B
 constexpr int LAM = AII + 4 * 1024;         // Lambda, state row order [2 parities][128] fp32
 constexpr int BETA = LAM + 2 * 512;         // [2 parities][64] fp32
-constexpr int OFF = BETA + 512;             // column side of pair (I, J < I): [6][4][64][16]
-constexpr int TOT = OFF + 6 * 4096;         // sub-tile decay totals [4][128] fp32
+constexpr int CS = BETA + 512;              // off-diagonal column sides [4][4 c-blocks][64][16]:
+                                            //   0: K e^{-L} of sub-tile 0 (pairs (I, 0)),
+                                            //   1: pair (2, 1), 2: pair (3, 1), 3: pair (3, 2)
+constexpr int TOT = CS + 4 * 4096;          // sub-tile decay totals [4][128] fp32
 constexpr int TOTL = TOT + 4 * 128 * 4;     // the same times log2 e
 constexpr int FAC = TOTL + 4 * 128 * 4;     // per (sub-tile, channel) factors [4][3][128]
-constexpr int FOFF = FAC + 4 * 3 * 128 * 4; // e^{R_I - R_J}, I > J: [6][128]
-constexpr int BYTES = FOFF + 6 * 128 * 4;
-constexpr int ORD = OFF;                    // sequence order (packed input) [<= 256], start only
+constexpr int F21 = FAC + 4 * 3 * 128 * 4;  // e^{R_2 - R_1} [128]
+constexpr int BYTES = F21 + 128 * 4;
+constexpr int ORD = CS;                     // sequence order (packed input) [<= 256], start only
 static_assert(BYTES <= 160 * 1024, "LDS budget");
 }  // namespace fl
 
@@ -310,97 +315,120 @@ __device__ __forceinline__ void operand_role(const FusedParams& p, char* smem, c
 #pragma unroll
     for (int x = 1; x < 4; ++x) R[x] = R[x - 1] + tot[x * kD + ch];
     float* fac = reinterpret_cast<float*>(smem + fl::FAC);
-    float* foff = reinterpret_cast<float*>(smem + fl::FOFF);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int m = (tid >> 7) + 2 * u;
-      const float rb = m == 0 ? 0.f : R[m - 1];          // decay before sub-tile m
-      // e^{R_m} as e^{tot_m} e^{R_{m-1}}: each factor alone is in range
-      const float em = fast_exp2(tot[m * kD + ch] * kLog2e) * fast_exp2(rb * kLog2e);
-      fac[(m * 3 + 0) * kD + ch] = -em;                                 // -e^{R_m}
-      fac[(m * 3 + 1) * kD + ch] = p.scale * em;                        // scale e^{R_m}
-      fac[(m * 3 + 2) * kD + ch] = fast_exp2((R[3] - R[m]) * kLog2e);   // e^{Ln - R_m}
-#pragma unroll
-      for (int a = 1; a < 3; ++a)   // (3, m) needs none: its column side is Kt
-        if (a > m) foff[off_id(a, m) * kD + ch] = fast_exp2((R[a] - R[m]) * kLog2e);
-      if (m == 0) {   // Lambda in state row order: row r holds channel sigma(r)
+      if (m == 0) {   // sub-tile 0 is referenced to the chunk start: only e^{Ln}
+        const float eln = fast_exp2(R[3] * kLog2e);
+        fac[2 * kD + ch] = eln;
+        // Lambda in state row order: row r holds channel sigma(r)
         const int r = 32 * (ch >> 5) + 16 * ((ch >> 2) & 1) + 4 * ((ch >> 3) & 3) + (ch & 3);
-        reinterpret_cast<float*>(smem + fl::LAM)[(c & 1) * kD + r] = fast_exp2(R[3] * kLog2e);
+        reinterpret_cast<float*>(smem + fl::LAM)[(c & 1) * kD + r] = eln;
+      } else {
+        // e^{R_m} as e^{tot_m} e^{R_{m-1}}: each factor alone is in range
+        const float em = fast_exp2(tot[m * kD + ch] * kLog2e) * fast_exp2(R[m - 1] * kLog2e);
+        fac[(m * 3 + 0) * kD + ch] = -em;                                 // -e^{R_m}
+        fac[(m * 3 + 1) * kD + ch] = p.scale * em;                        // scale e^{R_m}
+        fac[(m * 3 + 2) * kD + ch] = fast_exp2((R[3] - R[m]) * kLog2e);   // e^{Ln - R_m}
+        if (m == 1)
+          reinterpret_cast<float*>(smem + fl::F21)[ch] = fast_exp2((R[2] - R[1]) * kLog2e);
       }
     }
   };
 
-  // E2: decayed operands of chunk c.  rowf = e^{L_t - R_I} >= 1, colf = e^{R_I - L_t}
-  // <= 1 (R_I: end of the sub-tile).  One variant per sub-tile (IC = I): the factors of
-  // the off-diagonal column sides it writes are read at the top of each block, ahead of
-  // the exponentials.
+  // E2: decayed operands of chunk c.  Sub-tiles 1-3: rowf = e^{L_t - R_I} >= 1, colf =
+  // e^{R_I - L_t} <= 1 (R_I: end of the sub-tile), the sub-tile products' row sides
+  // k rowf, q rowf and column side k colf kept in registers, -Kb, Qb, Kt to LDS.
+  // Sub-tile 0: ef = e^{L_t} <= 1 and eb = e^{-L_t} <= e^80 (chunk start reference):
+  // -Kb and Qb are also its products' row sides and K e^{-L} their column side (LDS too,
+  // for the pairs (I, 0) of the other sub-tiles).  One variant per sub-tile (IC = I).
   auto e2_t = [&](auto Ic_, const int c, bf16x8_t (&fKr)[4], bf16x8_t (&fQr)[4], bf16x8_t (&fKc)[4]) {
     constexpr int IC = decltype(Ic_)::value;
-    // pairs (a, IC), a = IC + 1 .. 2, scaled here; the column side of (3, IC) is
-    // K e^{R_3 - L} = K e^{Ln - L} = Kt itself
-    constexpr int NOFF = IC < 2 ? 2 - IC : 0;
     const float* totl = reinterpret_cast<const float*>(smem + fl::TOTL) + IC * kD;
     const float* fac = reinterpret_cast<const float*>(smem + fl::FAC);
-    const float* foff = reinterpret_cast<const float*>(smem + fl::FOFF);
+    const float* f21 = reinterpret_cast<const float*>(smem + fl::F21);
     const int qb_off = fl::QB + (c & 1) * 16384, kt_off = fl::KTT + (c & 1) * 16384;
+    auto frag = [](const uint32_t (&w)[4]) { return __builtin_bit_cast(bf16x8_t, uint4{w[0], w[1], w[2], w[3]}); };
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      float4 fo[NOFF > 0 ? NOFF : 1][2];
+      float4 fo[2];   // e^{R_2 - R_1} (sub-tile 1 only), read ahead of the exponentials
+      if (IC == 1) {
 #pragma unroll
-      for (int x = 0; x < NOFF; ++x)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-          fo[x][hh] = *reinterpret_cast<const float4*>(foff + off_id(IC + 1 + x, IC) * kD + 32 * b + 8 * g4 + 4 * hh);
+        for (int hh = 0; hh < 2; ++hh) fo[hh] = *reinterpret_cast<const float4*>(f21 + 32 * b + 8 * g4 + 4 * hh);
+      }
       // results are packed to bf16 pairs as soon as a pair of channels is done, which
       // keeps the fp32 intermediates of only two channels live
-      uint32_t pkr[4], pqr[4], pkc[4], pkb[4], pqb[4], pkt[4];
-      uint32_t poff[NOFF > 0 ? NOFF : 1][4];
+      uint32_t pkr[4], pqr[4], pkc[4], pkb[4], pqb[4], pkt[4], p21[4];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int c0 = 32 * b + 8 * g4 + 4 * hh;
-        const float4 t4 = *reinterpret_cast<const float4*>(totl + c0);
-        const float4 fK = *reinterpret_cast<const float4*>(fac + (IC * 3 + 0) * kD + c0);
-        const float4 fQ = *reinterpret_cast<const float4*>(fac + (IC * 3 + 1) * kD + c0);
-        const float4 fN = *reinterpret_cast<const float4*>(fac + (IC * 3 + 2) * kD + c0);
-        const float tv[4] = {t4.x, t4.y, t4.z, t4.w}, vK[4] = {fK.x, fK.y, fK.z, fK.w};
-        const float vQ[4] = {fQ.x, fQ.y, fQ.z, fQ.w}, vN[4] = {fN.x, fN.y, fN.z, fN.w};
+        float tv[4], vK[4], vQ[4], vN[4];
+        {
+          const float4 fN = *reinterpret_cast<const float4*>(fac + (IC * 3 + 2) * kD + c0);
+          vN[0] = fN.x; vN[1] = fN.y; vN[2] = fN.z; vN[3] = fN.w;
+        }
+        if (IC > 0) {
+          const float4 t4 = *reinterpret_cast<const float4*>(totl + c0);
+          const float4 fK = *reinterpret_cast<const float4*>(fac + (IC * 3 + 0) * kD + c0);
+          const float4 fQ = *reinterpret_cast<const float4*>(fac + (IC * 3 + 1) * kD + c0);
+          tv[0] = t4.x; tv[1] = t4.y; tv[2] = t4.z; tv[3] = t4.w;
+          vK[0] = fK.x; vK[1] = fK.y; vK[2] = fK.z; vK[3] = fK.w;
+          vQ[0] = fQ.x; vQ[1] = fQ.y; vQ[2] = fQ.z; vQ[3] = fQ.w;
+        }
 #pragma unroll
         for (int i2 = 0; i2 < 2; ++i2) {
-          float kr[2], qr[2], kc[2], kb[2], qb[2], kt[2];
           const uint32_t kw = static_cast<uint32_t>(kq.k[b][2 * hh + i2]);
           const uint32_t qw = static_cast<uint32_t>(kq.q[b][2 * hh + i2]);
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int i = 2 * i2 + j, e = 4 * hh + i;
-            const float kv = j ? bf16hi(kw) : bf16lo(kw);
-            const float qv = j ? bf16hi(qw) : bf16lo(qw);
-            const float d = __builtin_fmaf(L[b][e], kLog2e, -tv[i]);   // (L - R_I) log2 e >= 0
-            const float rowf = fast_exp2(d), colf = fast_exp2(-d);
-            kr[j] = kv * rowf;
-            qr[j] = qv * rowf;
-            kc[j] = kv * colf;
-            kb[j] = kr[j] * vK[i];     // -K e^{L}
-            qb[j] = qr[j] * vQ[i];     // scale Q e^{L}
-            kt[j] = kc[j] * vN[i];     // K e^{Ln - L}
-          }
           const int w = 2 * hh + i2;   // dword of the fragment
-          pkr[w] = pack_bf16x2(kr[0], kr[1]);
-          pqr[w] = pack_bf16x2(qr[0], qr[1]);
-          pkc[w] = pack_bf16x2(kc[0], kc[1]);
-          pkb[w] = pack_bf16x2(kb[0], kb[1]);
-          pqb[w] = pack_bf16x2(qb[0], qb[1]);
-          pkt[w] = pack_bf16x2(kt[0], kt[1]);
-          // column side of the off-diagonal pairs (a = I + 1 .. 2, I): K e^{R_a - L}
+          if (IC == 0) {
+            float kb[2], qb[2], cs[2], kt[2];
 #pragma unroll
-          for (int x = 0; x < NOFF; ++x) {
-            const float f0 = i2 ? fo[x][hh].z : fo[x][hh].x, f1 = i2 ? fo[x][hh].w : fo[x][hh].y;
-            poff[x][w] = pack_bf16x2(kc[0] * f0, kc[1] * f1);
+            for (int j = 0; j < 2; ++j) {
+              const int i = 2 * i2 + j, e = 4 * hh + i;
+              const float kv = j ? bf16hi(kw) : bf16lo(kw);
+              const float qv = j ? bf16hi(qw) : bf16lo(qw);
+              const float d = L[b][e] * kLog2e;           // L log2 e <= 0
+              const float ef = fast_exp2(d), eb = fast_exp2(-d);
+              kb[j] = -(kv * ef);            // -K e^{L}
+              qb[j] = (qv * ef) * p.scale;   // scale Q e^{L}
+              cs[j] = kv * eb;               // K e^{-L}
+              kt[j] = cs[j] * vN[i];         // K e^{Ln - L}
+            }
+            pkb[w] = pack_bf16x2(kb[0], kb[1]);
+            pqb[w] = pack_bf16x2(qb[0], qb[1]);
+            pkc[w] = pack_bf16x2(cs[0], cs[1]);
+            pkt[w] = pack_bf16x2(kt[0], kt[1]);
+          } else {
+            float kr[2], qr[2], kc[2], kb[2], qb[2], kt[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const int i = 2 * i2 + j, e = 4 * hh + i;
+              const float kv = j ? bf16hi(kw) : bf16lo(kw);
+              const float qv = j ? bf16hi(qw) : bf16lo(qw);
+              const float d = __builtin_fmaf(L[b][e], kLog2e, -tv[i]);   // (L - R_I) log2 e >= 0
+              const float rowf = fast_exp2(d), colf = fast_exp2(-d);
+              kr[j] = kv * rowf;
+              qr[j] = qv * rowf;
+              kc[j] = kv * colf;
+              kb[j] = kr[j] * vK[i];     // -K e^{L}
+              qb[j] = qr[j] * vQ[i];     // scale Q e^{L}
+              kt[j] = kc[j] * vN[i];     // K e^{Ln - L}
+            }
+            pkr[w] = pack_bf16x2(kr[0], kr[1]);
+            pqr[w] = pack_bf16x2(qr[0], qr[1]);
+            pkc[w] = pack_bf16x2(kc[0], kc[1]);
+            pkb[w] = pack_bf16x2(kb[0], kb[1]);
+            pqb[w] = pack_bf16x2(qb[0], qb[1]);
+            pkt[w] = pack_bf16x2(kt[0], kt[1]);
+            if (IC == 1) {   // column side of pair (2, 1): K e^{R_2 - L}
+              const float f0 = i2 ? fo[hh].z : fo[hh].x, f1 = i2 ? fo[hh].w : fo[hh].y;
+              p21[w] = pack_bf16x2(kc[0] * f0, kc[1] * f1);
+            }
           }
         }
       }
-      auto frag = [](const uint32_t (&w)[4]) { return __builtin_bit_cast(bf16x8_t, uint4{w[0], w[1], w[2], w[3]}); };
-      fKr[b] = frag(pkr);
-      fQr[b] = frag(pqr);
+      fKr[b] = frag(IC == 0 ? pkb : pkr);
+      fQr[b] = frag(IC == 0 ? pqb : pqr);
       fKc[b] = frag(pkc);
       *reinterpret_cast<bf16x8_t*>(smem + fl::KBN + frag_at(IC, b, 4, lane)) = frag(pkb);
       *reinterpret_cast<bf16x8_t*>(smem + qb_off + frag_at(IC, b, 4, lane)) = frag(pqb);
@@ -416,11 +444,15 @@ __device__ __forceinline__ void operand_role(const FusedParams& p, char* smem, c
               uint2{pack_bf16x2(tr[0], tr[1]), pack_bf16x2(tr[2], tr[3])};
         }
       }
-#pragma unroll
-      for (int x = 0; x < NOFF; ++x)
-        *reinterpret_cast<bf16x8_t*>(smem + fl::OFF + off_id(IC + 1 + x, IC) * 4096 + frag_at(0, b, 4, lane)) = frag(poff[x]);
-      if (IC < 3)
-        *reinterpret_cast<bf16x8_t*>(smem + fl::OFF + off_id(3, IC < 3 ? IC : 0) * 4096 + frag_at(0, b, 4, lane)) = frag(pkt);
+      // column sides for the other sub-tiles' pairs
+      if (IC == 0)
+        *reinterpret_cast<bf16x8_t*>(smem + fl::CS + 0 * 4096 + frag_at(0, b, 4, lane)) = frag(pkc);
+      if (IC == 1) {
+        *reinterpret_cast<bf16x8_t*>(smem + fl::CS + 1 * 4096 + frag_at(0, b, 4, lane)) = frag(p21);
+        *reinterpret_cast<bf16x8_t*>(smem + fl::CS + 2 * 4096 + frag_at(0, b, 4, lane)) = frag(pkt);
+      }
+      if (IC == 2)
+        *reinterpret_cast<bf16x8_t*>(smem + fl::CS + 3 * 4096 + frag_at(0, b, 4, lane)) = frag(pkt);
     }
   };
   auto e2 = [&](const int c, bf16x8_t (&fKr)[4], bf16x8_t (&fQr)[4], bf16x8_t (&fKc)[4]) {
@@ -435,56 +467,77 @@ __device__ __forceinline__ void operand_role(const FusedParams& p, char* smem, c
   // Decayed sub-tile products of chunk c, transposed: C[s, t] = sum_c colside[s, c]
   // rowside[t, c]; lane (t, g) holds s = 16 J + 4 g + i.  Writes M's blocks, -A_IJ
   // (J < I) and the beta-scaled diagonal block A_II (masked to s < t) for its inverse.
-  // One straight-line variant per sub-tile (IC = I), so that the I + 1 pairs' product
-  // chains interleave.
-  auto products_t = [&](auto Ic, const bf16x8_t (&fKr)[4], const bf16x8_t (&fQr)[4],
+  // The ten pairs are spread 3, 2, 2, 3 over the wavefronts: wavefront W takes pairs
+  // (PI, PJ)[W] below.  Pairs (I, J >= 1) need the row sides k rowf, q rowf of sub-tile
+  // I, which only wavefront I holds; pairs (I, 0) take -Kb and Qb of sub-tile I from
+  // LDS (or registers for (0, 0)) and the column side K e^{-L} of sub-tile 0, so any
+  // wavefront can run them.  One straight-line variant per wavefront.
+  auto products_t = [&](auto Wc, const int c, const bf16x8_t (&fKr)[4], const bf16x8_t (&fQr)[4],
                         const bf16x8_t (&fKc)[4]) {
-    constexpr int IC = decltype(Ic)::value;
-    f32x4_t pa[IC + 1], pm[IC + 1];
+    constexpr int W = decltype(Wc)::value;
+    constexpr int NP = (W == 0 || W == 3) ? 3 : 2;
+    constexpr int PI[4][3] = {{0, 2, 3}, {1, 1, 0}, {2, 2, 0}, {3, 3, 3}};
+    constexpr int PJ[4][3] = {{0, 0, 0}, {1, 0, 0}, {2, 1, 0}, {3, 1, 2}};
+    const int qb_off = fl::QB + (c & 1) * 16384;
+    f32x4_t pa[NP], pm[NP];
 #pragma unroll
-    for (int J = 0; J <= IC; ++J) {
-      pa[J] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      pm[J] = pa[J];
+    for (int x = 0; x < NP; ++x) {
+      pa[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      pm[x] = pa[x];
     }
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
 #pragma unroll
-      for (int J = 0; J <= IC; ++J) {
-        const bf16x8_t cs = J == IC ? fKc[b] : lds_frag(smem, fl::OFF + off_id(IC, J) * 4096 + frag_at(0, b, 4, lane));
-        pa[J] = mma(cs, fKr[b], pa[J]);
-        pm[J] = mma(cs, fQr[b], pm[J]);
+      for (int x = 0; x < NP; ++x) {
+        const int I = PI[W][x], J = PJ[W][x];
+        // row sides: registers, except the pairs (I >= 1, 0), which take -Kb and Qb
+        const bool rows_lds = J == 0 && I > 0;
+        const bf16x8_t rk = rows_lds ? lds_frag(smem, fl::KBN + frag_at(I, b, 4, lane)) : fKr[b];
+        const bf16x8_t rq = rows_lds ? lds_frag(smem, qb_off + frag_at(I, b, 4, lane)) : fQr[b];
+        // column side: the own sub-tile's for the diagonal and, on wavefront 0, for
+        // (I, 0); otherwise the region written by the column's owner
+        const int cs_id = J == 0 ? 0 : (I == 2 ? 1 : J + 1);   // (2,1) -> 1, (3,1) -> 2, (3,2) -> 3
+        const bool cols_reg = J == I || (J == 0 && W == 0);
+        const bf16x8_t cs = cols_reg ? fKc[b] : lds_frag(smem, fl::CS + cs_id * 4096 + frag_at(0, b, 4, lane));
+        pa[x] = mma(cs, rk, pa[x]);
+        pm[x] = mma(cs, rq, pm[x]);
       }
     }
+    const float* betas = reinterpret_cast<const float*>(smem + fl::BETA) + (c & 1) * kCh;
 #pragma unroll
-    for (int J = 0; J <= IC; ++J) {
+    for (int x = 0; x < NP; ++x) {
+      const int I = PI[W][x], J = PJ[W][x];
+      const float bt = I == W ? beta_t : betas[16 * I + l16];
+      // J = 0: the row sides are -Kb (A's sign flips) and Qb (scale included)
+      const float fa_ = J == 0 ? -bt : bt, fm_ = J == 0 ? 1.f : p.scale;
       // masks only on the diagonal pair (s = 16 I + 4 g + i against t = 16 I + l16)
       f32x4_t av;
       float mv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        av[i] = beta_t * pa[J][i];
-        mv[i] = p.scale * pm[J][i];
-        if (J == IC) {
+        av[i] = fa_ * pa[x][i];
+        mv[i] = fm_ * pm[x][i];
+        if (J == I) {
           av[i] = 4 * g4 + i < l16 ? av[i] : 0.f;
           mv[i] = 4 * g4 + i <= l16 ? mv[i] : 0.f;
         }
       }
       // M[t][s]: fragment (t-tile I, s-block J/2), elements 4 (J%2) .. +3
-      *reinterpret_cast<uint2*>(smem + fl::MF + frag_at(IC, J >> 1, 2, lane) + 8 * (J & 1)) =
+      *reinterpret_cast<uint2*>(smem + fl::MF + frag_at(I, J >> 1, 2, lane) + 8 * (J & 1)) =
           uint2{pack_bf16x2(mv[0], mv[1]), pack_bf16x2(mv[2], mv[3])};
-      if (J < IC)   // -A_IJ as a 16x16x16 A operand: lane (t, g) holds columns 4 g .. +3
-        *reinterpret_cast<uint2*>(smem + fl::AOF + off_id(IC, J) * 512 + lane * 8) =
+      if (J < I)   // -A_IJ as a 16x16x16 A operand: lane (t, g) holds columns 4 g .. +3
+        *reinterpret_cast<uint2*>(smem + fl::AOF + off_id(I, J) * 512 + lane * 8) =
             uint2{pack_bf16x2(-av[0], -av[1]), pack_bf16x2(-av[2], -av[3])};
       else
-        *reinterpret_cast<f32x4_t*>(smem + fl::AII + IC * 1024 + lane * 16) = av;
+        *reinterpret_cast<f32x4_t*>(smem + fl::AII + I * 1024 + lane * 16) = av;
     }
   };
-  auto products = [&](const bf16x8_t (&fKr)[4], const bf16x8_t (&fQr)[4], const bf16x8_t (&fKc)[4]) {
+  auto products = [&](const int c, const bf16x8_t (&fKr)[4], const bf16x8_t (&fQr)[4], const bf16x8_t (&fKc)[4]) {
     switch (I) {
-      case 0: products_t(Ic<0>{}, fKr, fQr, fKc); break;
-      case 1: products_t(Ic<1>{}, fKr, fQr, fKc); break;
-      case 2: products_t(Ic<2>{}, fKr, fQr, fKc); break;
-      default: products_t(Ic<3>{}, fKr, fQr, fKc); break;
+      case 0: products_t(Ic<0>{}, c, fKr, fQr, fKc); break;
+      case 1: products_t(Ic<1>{}, c, fKr, fQr, fKc); break;
+      case 2: products_t(Ic<2>{}, c, fKr, fQr, fKc); break;
+      default: products_t(Ic<3>{}, c, fKr, fQr, fKc); break;
     }
   };
 
@@ -505,7 +558,7 @@ __device__ __forceinline__ void operand_role(const FusedParams& p, char* smem, c
     if (c < nchunks) e2(c, fKr, fQr, fKc);
     load_keys(c + 1, kq);
     lds_barrier();                                                          // A
-    if (c < nchunks) products(fKr, fQr, fKc);
+    if (c < nchunks) products(c, fKr, fQr, fKc);
     if (c + 1 < nchunks) e1(c + 1);
     load_decay(c + 2, dn);
     lds_barrier();                                                          // B
