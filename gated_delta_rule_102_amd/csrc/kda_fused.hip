@@ -53,8 +53,9 @@
 //      forward substitution, S <- Lambda S + Kt^T Delta);
 //   B: operand: the decayed sub-tile products (A, M) of chunk c, then the cumulative
 //      log-decay of chunk c + 1;  state: X = Diag(beta)(V - Kb S) of chunk c;
-//   C: operand: per-channel decay factors of chunk c + 1;  state: the four 16 x 16
-//      diagonal inverses (I + A_II)^{-1} of chunk c, one per wavefront.
+//   C: per-channel decay factors of chunk c + 1, all 512 threads.
+// The state role starts the diagonal inverses (I + A_II)^{-1} of chunk c, one per
+// wavefront, inside window B, each as soon as its block is written (an LDS flag).
 // Operands read by the state role one iteration after they were written (Qb, Kt^T,
 // Lambda, beta) alternate between two LDS copies by chunk parity; the rest are
 // written and read in windows that a barrier separates.
@@ -88,7 +89,8 @@ constexpr int TOT = CS + 4 * 4096;          // sub-tile decay totals [4][128] fp
 constexpr int TOTL = TOT + 4 * 128 * 4;     // the same times log2 e
 constexpr int FAC = TOTL + 4 * 128 * 4;     // per (sub-tile, channel) factors [4][3][128]
 constexpr int F21 = FAC + 4 * 3 * 128 * 4;  // e^{R_2 - R_1} [128]
-constexpr int BYTES = F21 + 128 * 4;
+constexpr int AIIF = F21 + 128 * 4;         // per sub-tile: 1 + the last chunk whose A_II is in AII [4] int
+constexpr int BYTES = AIIF + 16;
 constexpr int ORD = CS;                     // sequence order (packed input) [<= 256], start only
 static_assert(BYTES <= 160 * 1024, "LDS budget");
 }  // namespace fl
@@ -203,6 +205,51 @@ struct KeyIn {
   i32x4_t q[4], k[4];
 };
 
+// Per-channel factors of chunk c for sub-tile m and channel ch (one item; the 512
+// items are spread over all threads of the workgroup).
+__device__ __forceinline__ void factor_item(const FusedParams& p, char* smem, const int c, const int m,
+                                            const int ch) {
+  const float* tot = reinterpret_cast<const float*>(smem + fl::TOT);
+  float R[4];
+  R[0] = tot[ch];
+#pragma unroll
+  for (int x = 1; x < 4; ++x) R[x] = R[x - 1] + tot[x * kD + ch];
+  float* fac = reinterpret_cast<float*>(smem + fl::FAC);
+  if (m == 0) {   // sub-tile 0 is referenced to the chunk start: only e^{Ln}
+    const float eln = fast_exp2(R[3] * kLog2e);
+    fac[2 * kD + ch] = eln;
+    // Lambda in state row order: row r holds channel sigma(r)
+    const int r = 32 * (ch >> 5) + 16 * ((ch >> 2) & 1) + 4 * ((ch >> 3) & 3) + (ch & 3);
+    reinterpret_cast<float*>(smem + fl::LAM)[(c & 1) * kD + r] = eln;
+  } else {
+    // e^{R_m} as e^{tot_m} e^{R_{m-1}}: each factor alone is in range
+    const float em = fast_exp2(tot[m * kD + ch] * kLog2e) * fast_exp2(R[m - 1] * kLog2e);
+    fac[(m * 3 + 0) * kD + ch] = -em;                                 // -e^{R_m}
+    fac[(m * 3 + 1) * kD + ch] = p.scale * em;                        // scale e^{R_m}
+    fac[(m * 3 + 2) * kD + ch] = fast_exp2((R[3] - R[m]) * kLog2e);   // e^{Ln - R_m}
+    if (m == 1) reinterpret_cast<float*>(smem + fl::F21)[ch] = fast_exp2((R[2] - R[1]) * kLog2e);
+  }
+}
+
+// LDS flag handoff inside a barrier window: the writer's LDS stores complete, then it
+// publishes `value`; the reader polls until the flag reaches it.  The poll is bounded
+// (about 2^20 polls) so that a wavefront always leaves it; the writer never waits on
+// the reader, so the flag is set within the window.
+__device__ __forceinline__ void flag_set(char* smem, const int off, const int value) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  if ((threadIdx.x & 63) == 0) __hip_atomic_store(reinterpret_cast<int*>(smem + off), value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+__device__ __forceinline__ void flag_wait(char* smem, const int off, const int value) {
+  for (int n = 0; n < (1 << 20); ++n) {
+    const int v = __builtin_amdgcn_readfirstlane(
+        __hip_atomic_load(reinterpret_cast<int*>(smem + off), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+    if (v >= value) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");
+}
+
 // ------------------------------------------------------------------ operand role
 // Wavefront I (0..3) of the workgroup, sub-tile I of every chunk.
 __device__ __forceinline__ void operand_role(const FusedParams& p, char* smem, const int I,
@@ -305,36 +352,6 @@ __device__ __forceinline__ void operand_role(const FusedParams& p, char* smem, c
     if (g4 == 0) reinterpret_cast<float*>(smem + fl::BETA)[(c & 1) * kCh + 16 * I + l16] = beta_t;
   };
 
-  // Per-channel factors of chunk c: thread (m, ch) for sub-tiles m = tid / 128 and
-  // m + 2, channel ch.
-  auto factors = [&](const int c) {
-    const int ch = tid & (kD - 1);
-    const float* tot = reinterpret_cast<const float*>(smem + fl::TOT);
-    float R[4];
-    R[0] = tot[ch];
-#pragma unroll
-    for (int x = 1; x < 4; ++x) R[x] = R[x - 1] + tot[x * kD + ch];
-    float* fac = reinterpret_cast<float*>(smem + fl::FAC);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int m = (tid >> 7) + 2 * u;
-      if (m == 0) {   // sub-tile 0 is referenced to the chunk start: only e^{Ln}
-        const float eln = fast_exp2(R[3] * kLog2e);
-        fac[2 * kD + ch] = eln;
-        // Lambda in state row order: row r holds channel sigma(r)
-        const int r = 32 * (ch >> 5) + 16 * ((ch >> 2) & 1) + 4 * ((ch >> 3) & 3) + (ch & 3);
-        reinterpret_cast<float*>(smem + fl::LAM)[(c & 1) * kD + r] = eln;
-      } else {
-        // e^{R_m} as e^{tot_m} e^{R_{m-1}}: each factor alone is in range
-        const float em = fast_exp2(tot[m * kD + ch] * kLog2e) * fast_exp2(R[m - 1] * kLog2e);
-        fac[(m * 3 + 0) * kD + ch] = -em;                                 // -e^{R_m}
-        fac[(m * 3 + 1) * kD + ch] = p.scale * em;                        // scale e^{R_m}
-        fac[(m * 3 + 2) * kD + ch] = fast_exp2((R[3] - R[m]) * kLog2e);   // e^{Ln - R_m}
-        if (m == 1)
-          reinterpret_cast<float*>(smem + fl::F21)[ch] = fast_exp2((R[2] - R[1]) * kLog2e);
-      }
-    }
-  };
 
   // E2: decayed operands of chunk c.  Sub-tiles 1-3: rowf = e^{L_t - R_I} >= 1, colf =
   // e^{R_I - L_t} <= 1 (R_I: end of the sub-tile), the sub-tile products' row sides
@@ -525,11 +542,15 @@ __device__ __forceinline__ void operand_role(const FusedParams& p, char* smem, c
       // M[t][s]: fragment (t-tile I, s-block J/2), elements 4 (J%2) .. +3
       *reinterpret_cast<uint2*>(smem + fl::MF + frag_at(I, J >> 1, 2, lane) + 8 * (J & 1)) =
           uint2{pack_bf16x2(mv[0], mv[1]), pack_bf16x2(mv[2], mv[3])};
-      if (J < I)   // -A_IJ as a 16x16x16 A operand: lane (t, g) holds columns 4 g .. +3
+      if (J < I) {   // -A_IJ as a 16x16x16 A operand: lane (t, g) holds columns 4 g .. +3
         *reinterpret_cast<uint2*>(smem + fl::AOF + off_id(I, J) * 512 + lane * 8) =
             uint2{pack_bf16x2(-av[0], -av[1]), pack_bf16x2(-av[2], -av[3])};
-      else
+      } else {
+        // the diagonal block (the first pair each wavefront finishes) goes to its
+        // inverse on the state role right away
         *reinterpret_cast<f32x4_t*>(smem + fl::AII + I * 1024 + lane * 16) = av;
+        flag_set(smem, fl::AIIF + 4 * I, c + 1);
+      }
     }
   };
   auto products = [&](const int c, const bf16x8_t (&fKr)[4], const bf16x8_t (&fQr)[4], const bf16x8_t (&fKc)[4]) {
@@ -547,7 +568,7 @@ __device__ __forceinline__ void operand_role(const FusedParams& p, char* smem, c
   if (nchunks > 0) e1(0);
   load_decay(1, dn);
   lds_barrier();
-  if (nchunks > 0) factors(0);
+  if (nchunks > 0) factor_item(p, smem, 0, tid >> 7, tid & (kD - 1));   // sub-tiles 0, 1
   lds_barrier();
 
   for (int c = 0; c <= nchunks; ++c) {
@@ -562,7 +583,7 @@ __device__ __forceinline__ void operand_role(const FusedParams& p, char* smem, c
     if (c + 1 < nchunks) e1(c + 1);
     load_decay(c + 2, dn);
     lds_barrier();                                                          // B
-    if (c + 1 < nchunks) factors(c + 1);
+    if (c + 1 < nchunks) factor_item(p, smem, c + 1, tid >> 7, tid & (kD - 1));   // sub-tiles 0, 1
     lds_barrier();                                                          // C
   }
 }
@@ -828,14 +849,26 @@ __device__ __forceinline__ void state_role(const FusedParams& p, char* smem, con
   __builtin_amdgcn_s_setprio(3);
   load_v(0);
   lds_barrier();
+  if (nchunks > 0)   // chunk 0's factors of sub-tiles 2, 3
+    factor_item(p, smem, 0, 2 + ((threadIdx.x - 256) >> 7), threadIdx.x & (kD - 1));
   lds_barrier();
   for (int c = 0; c <= nchunks; ++c) {
     apply(c - 1);
     lds_barrier();                                                          // A
     if (c < nchunks) x_step(c);
     load_v(c + 1);
+    // this chunk's inverse as soon as its diagonal block is written
+    if (c < nchunks) {
+      flag_wait(smem, fl::AIIF + 4 * j, c + 1);
+      // it shares the window with the operand role's products and decay scan: no
+      // precedence over them
+      __builtin_amdgcn_s_setprio(0);
+      inverse();
+      __builtin_amdgcn_s_setprio(3);
+    }
     lds_barrier();                                                          // B
-    if (c < nchunks) inverse();
+    if (c + 1 < nchunks)   // factors of sub-tiles 2, 3
+      factor_item(p, smem, c + 1, 2 + ((threadIdx.x - 256) >> 7), threadIdx.x & (kD - 1));
     lds_barrier();                                                          // C
   }
 
@@ -885,6 +918,7 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
   fused_seq(p, n, tok0, len);
   const int nchunks = (len + kCh - 1) / kCh;
 
+  if (tid < 4) reinterpret_cast<int*>(smem + fl::AIIF)[tid] = 0;
   // M is lower triangular: the upper halves of fragments (0, 0) and (2, 1) are read as
   // zeros and nothing else writes them
   for (int e = tid; e < 8192 / 16; e += kThreadsF)
