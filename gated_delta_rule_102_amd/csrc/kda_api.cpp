@@ -415,7 +415,7 @@ int kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const voi
   int rc = check_prefill(d);
   if (rc != KDA_OK) return rc;
   kda::PrefillArgs a = prefill_args(d, stream);
-  if (kda::prefill_workspace_bytes(a) > 0) {
+  if (kda::prefill_workspace_bytes(a) > kda::noalloc_scratch_bytes()) {
     // windows short enough for the scratch array; none fit: refused before any device call
     const int cg = kda::prefill_fit_window(a, kda::noalloc_scratch_bytes());
     if (cg <= 0) return KDA_ERR_WORKSPACE;

@@ -103,10 +103,41 @@ struct FusedParams {
   const int32_t* cu;      // packed sequence offsets [N + 1], or null (fixed length T)
   int N, T, total_T, H;
   float scale;
+  // Segmented fixed-length input (segR > 0): sequence n is cut into segR segments of
+  // whole chunks, segment r covering chunks floor(r nc / segR) .. floor((r + 1) nc /
+  // segR) - 1; the launch covers segments 0 .. segs - 1 of every sequence, workgroup
+  // ((n segs + r) H + h).  States are indexed r N + n; with sT_last only the last
+  // segment writes its final state, at index n.  s0_eye: the initial state is the
+  // identity.  v_on = 0: v reads as zero (with the identity, the run gives the
+  // segment's transition); out_on = 0: nothing is written to out.
+  int segR = 0, segs = 0;
+  int s0_eye = 0, sT_last = 0;
+  int v_on = 1, out_on = 1;
 };
 
+// The kD x kD identity, the initial state from which a segment's run gives its
+// transition.
+struct EyeMatrix {
+  float v[kD * kD];
+  constexpr EyeMatrix() : v() {
+    for (int i = 0; i < kD; ++i) v[i * (kD + 1)] = 1.f;
+  }
+};
+__device__ const EyeMatrix kEye{};
+
+// Chunk that starts segment r of a sequence of nc chunks cut into R segments.
+__device__ __forceinline__ int seg_chunk(const int r, const int nc, const int R) {
+  return static_cast<int>((static_cast<int64_t>(r) * nc) / R);
+}
+
 __device__ __forceinline__ void fused_seq(const FusedParams& p, int n, int& tok0, int& len) {
-  if (p.cu == nullptr) {
+  if (p.segR > 0) {   // n is (sequence, segment) here: n = s segs + r
+    const int sq = n / p.segs, r = n % p.segs;
+    const int nc = (p.T + kCh - 1) / kCh;
+    const int c0 = seg_chunk(r, nc, p.segR), c1 = seg_chunk(r + 1, nc, p.segR);
+    tok0 = sq * p.T + c0 * kCh;
+    len = min(c1 * kCh, p.T) - c0 * kCh;
+  } else if (p.cu == nullptr) {
     tok0 = n * p.T;
     len = p.T;
   } else {
@@ -591,16 +622,19 @@ __device__ __forceinline__ void operand_role(const FusedParams& p, char* smem, c
 // ------------------------------------------------------------------ state role
 // Wavefront 4 + j, value columns 32 j .. +31.
 __device__ __forceinline__ void state_role(const FusedParams& p, char* smem, const int j,
-                                           const int n, const int h, const int tok0, const int len,
-                                           const int nchunks) {
+                                           const int s0_idx, const int sT_idx, const int h,
+                                           const int tok0, const int len, const int nchunks) {
   const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
   const int H = p.H;
   const uint32_t rs = static_cast<uint32_t>(H) * kD * 2;   // token row stride (bytes)
+  // all ones, or zero when v reads as zero / nothing is written to out (buffer ranges)
+  const uint32_t v_mask = p.v_on ? ~0u : 0u, out_mask = p.out_on ? ~0u : 0u;
   const int col0 = 32 * j;
 
   f32x4_t S[2][8];
   {
-    const float* s0 = p.s0 ? p.s0 + (static_cast<int64_t>(n) * H + h) * kD * kD : nullptr;
+    const float* s0 = p.s0_eye ? kEye.v
+                      : p.s0 ? p.s0 + (static_cast<int64_t>(s0_idx) * H + h) * kD * kD : nullptr;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -624,7 +658,8 @@ __device__ __forceinline__ void state_role(const FusedParams& p, char* smem, con
   auto load_v = [&](const int c) {
     const int t0 = tok0 + c * kCh;
     const int nrow = min(kCh, len - c * kCh);
-    const auto rv = make_rsrc(p.v + (static_cast<int64_t>(t0) * H + h) * kD, nrow > 0 ? (nrow - 1) * rs + kD * 2 : 0);
+    const auto rv = make_rsrc(p.v + (static_cast<int64_t>(t0) * H + h) * kD,
+                              (nrow > 0 ? (nrow - 1) * rs + kD * 2 : 0) & v_mask);
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -811,7 +846,7 @@ __device__ __forceinline__ void state_role(const FusedParams& p, char* smem, con
       const int t0 = tok0 + cs * kCh;
       const int nrow = act ? min(kCh, len - cs * kCh) : 0;
       const auto ro = make_rsrc(p.out + (static_cast<int64_t>(act ? t0 : tok0) * H + h) * kD,
-                                nrow > 0 ? (nrow - 1) * rs + kD * 2 : 0);
+                                (nrow > 0 ? (nrow - 1) * rs + kD * 2 : 0) & out_mask);
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -872,8 +907,8 @@ __device__ __forceinline__ void state_role(const FusedParams& p, char* smem, con
     lds_barrier();                                                          // C
   }
 
-  if (p.sT != nullptr) {
-    float* dst = p.sT + (static_cast<int64_t>(n) * H + h) * kD * kD;
+  if (p.sT != nullptr && sT_idx >= 0) {
+    float* dst = p.sT + (static_cast<int64_t>(sT_idx) * H + h) * kD * kD;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -924,10 +959,17 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
   for (int e = tid; e < 8192 / 16; e += kThreadsF)
     *reinterpret_cast<i32x4_t*>(smem + fl::MF + e * 16) = i32x4_t{0, 0, 0, 0};
 
-  if (wave < 4)
+  if (wave < 4) {
     operand_role(p, smem, wave, h, tok0, len, nchunks);
-  else
-    state_role(p, smem, wave - 4, n, h, tok0, len, nchunks);
+  } else {
+    int s0_idx = n, sT_idx = n;
+    if (p.segR > 0) {   // n = s segs + r; states indexed r N + s
+      const int sq = n / p.segs, r = n % p.segs;
+      s0_idx = r * p.N + sq;
+      sT_idx = p.sT_last ? (r == p.segR - 1 ? sq : -1) : r * p.N + sq;
+    }
+    state_role(p, smem, wave - 4, s0_idx, sT_idx, h, tok0, len, nchunks);
+  }
 }
 
 }  // namespace
@@ -944,6 +986,55 @@ hipError_t launch_fused_prefill(const PrefillArgs& a) {
   hipLaunchKernelGGL(fused_prefill_kernel, dim3(static_cast<unsigned>(a.N) * a.H), dim3(kThreadsF), 0,
                      a.stream, fp);
   return hipGetLastError();
+}
+
+size_t fused_segmented_bytes(const PrefillArgs& a, int R) {
+  // exit states and transitions of segments 0 .. R-2, entry states of all R segments
+  return static_cast<size_t>(3 * R - 2) * a.N * a.H * kD * kD * sizeof(float);
+}
+
+// Few long sequences: every sequence cut into R segments so that N H R workgroups fill
+// the machine.  A segment maps its entry state affinely to its exit state, S_exit =
+// P S_entry + X (the token rule is linear in (S, v)); X is its exit state from a zero
+// entry and P the exit state from the identity with v = 0.  Four launches: X and P
+// of segments 0 .. R-2, their composition into every segment's entry state, then the
+// output of every segment from its entry state (the last one also writes the final
+// state).
+hipError_t launch_fused_segmented(const PrefillArgs& a, int R) {
+  char* ws = nullptr;
+  hipError_t err = ws_acquire(a.workspace, a.workspace_bytes, fused_segmented_bytes(a, R), a.stream, &ws);
+  if (err != hipSuccess) return err;
+  const size_t per = static_cast<size_t>(a.N) * a.H * kD * kD;
+  float* exits = reinterpret_cast<float*>(ws);
+  float* trans = exits + (R - 1) * per;
+  float* entry = trans + (R - 1) * per;
+  // v and out stay valid pointers in every launch; v_on / out_on = 0 make their
+  // buffer ranges empty (loads return zero, stores are dropped)
+  auto params = [&](int v_on, const float* s0, int out_on, float* sT, int segs, int eye, int last) {
+    FusedParams fp{static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),
+                   static_cast<const bf16_t*>(a.v), static_cast<const bf16_t*>(a.g),
+                   static_cast<const bf16_t*>(a.beta), s0, static_cast<bf16_t*>(a.out), sT,
+                   nullptr, a.N, a.T, a.N * a.T, a.H, a.scale};
+    fp.segR = R;
+    fp.segs = segs;
+    fp.s0_eye = eye;
+    fp.sT_last = last;
+    fp.v_on = v_on;
+    fp.out_on = out_on;
+    return fp;
+  };
+  const unsigned g1 = static_cast<unsigned>(a.N) * (R - 1) * a.H;
+  const FusedParams px = params(1, nullptr, 0, exits, R - 1, 0, 0);
+  KDA_TRY_LAUNCH(err, fused_prefill_kernel, dim3(g1), dim3(kThreadsF), 0, a.stream, px);
+  const FusedParams pp = params(0, nullptr, 0, trans, R - 1, 1, 0);
+  KDA_TRY_LAUNCH(err, fused_prefill_kernel, dim3(g1), dim3(kThreadsF), 0, a.stream, pp);
+  if (err == hipSuccess)
+    err = launch_compose(ComposeArgs{trans, exits, a.initial_state, entry, R - 1, a.N, a.H, kD, a.stream});
+  const FusedParams po = params(1, entry, 1, a.final_state, R, 0, 1);
+  KDA_TRY_LAUNCH(err, fused_prefill_kernel, dim3(static_cast<unsigned>(a.N) * R * a.H), dim3(kThreadsF), 0,
+                 a.stream, po);
+  const hipError_t ferr = ws_release(a.workspace, ws, a.stream);
+  return err != hipSuccess ? err : ferr;
 }
 
 }  // namespace kda

@@ -101,6 +101,11 @@ hipError_t launch_prefill(const PrefillArgs& a);
 // without the prologue or snapshots.
 bool fused_prefill_supported(const PrefillArgs& a);
 hipError_t launch_fused_prefill(const PrefillArgs& a);
+// The same kernel over R segments of every fixed-length sequence (R >= 2): exit
+// states and transitions of the first R - 1 segments, their composition into entry
+// states, then every segment's output; fused_segmented_bytes of workspace.
+size_t fused_segmented_bytes(const PrefillArgs& a, int R);
+hipError_t launch_fused_segmented(const PrefillArgs& a, int R);
 // Kernels launch_prefill runs for these arguments (static text, for reports).
 const char* prefill_schedule(const PrefillArgs& a);
 // Workspace bytes launch_prefill needs for these arguments (0 if unsupported).

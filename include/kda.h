@@ -27,7 +27,9 @@
  *  - All tensor pointers are DEVICE pointers owned by the caller, contiguous and
  *    row-major.
  *  - Workspaces.  Prefill on bf16 input at d = 128 with 256 or more (sequence, head)
- *    streams runs fused and needs none.  Every other prefill, the backward and the
+ *    streams runs fused and needs none.  Fixed-length bf16 prefill at d = 128 with 4
+ *    to 32 streams and long sequences cuts each sequence into R segments and needs
+ *    3R - 2 fp32 [dk, dv] states per stream.  Every other prefill, the backward and the
  *    transition need one per call, sized by the matching *_workspace_size function
  *    (pure host arithmetic).  The *_ws entry points and kda_prefill run on a
  *    workspace the caller owns (256-byte aligned, contents irrelevant, garbage on
@@ -205,8 +207,9 @@ int kda_prefill(const kda_prefill_desc* desc, void* workspace, size_t workspace_
  * within the bf16 / fp32 tolerances of the other entry points, and it calls no
  * hipMalloc, hipFree or allocating routine.  Its scratch is a fixed 64 MiB device
  * array inside the library, one per GPU, held until the process ends; the fused
- * schedule needs none, the others run in windows of chunks short enough for it
- * (down to one chunk per window).  Sizes for which even one-chunk windows do not
+ * schedule needs none, a schedule whose workspace fits it runs as kda_chunk_fwd
+ * would, the others run in windows of chunks short enough for it (down to one
+ * chunk per window).  Sizes for which even one-chunk windows do not
  * fit (the carried fp32 states plus two windows' chunk operands exceed 64 MiB, e.g.
  * fp32 at d = 64 with 400 heads) return KDA_ERR_WORKSPACE before anything is
  * enqueued.  Every call on a GPU uses that GPU's one array and nothing in it needs

@@ -189,12 +189,17 @@ def test_workspace_size_is_host_arithmetic(lib):
     bytes per (chunk, head) for bf16 at d = 128, one slot per chunk (plus one per
     sequence) on the two-kernel schedule (B=4, T=4096, H=16), two windows of 16 chunks
     plus the carried fp32 states on the windowed one (B=1, T=4096, H=16), one window
-    for T=64."""
+    for T=64; on the segmented schedule (4 to 32 streams, segments of at least 16
+    chunks) 3R - 2 fp32 states per stream for R segments: R = 8 at 32 streams, 32 at
+    8 streams."""
     f = lib.kda_chunk_fwd_workspace_size
     f.argtypes = [ctypes.c_int] * 6
     f.restype = ctypes.c_size_t
+    st = 128 * 128 * 4
     assert f(4, 4096, 16, 128, 128, 0) == (4 * 4096 // 64 + 4) * 16 * 66048
-    assert f(1, 4096, 16, 128, 128, 0) == 2 * 1 * 16 * 16 * 66048 + 16 * 128 * 128 * 4
+    assert f(1, 4096, 16, 128, 128, 0) == 2 * 1 * 16 * 16 * 66048 + 16 * st
+    assert f(1, 65536, 32, 128, 128, 0) == (3 * 8 - 2) * 32 * st
+    assert f(1, 65536, 8, 128, 128, 0) == (3 * 32 - 2) * 8 * st
     assert f(2, 64, 3, 128, 128, 0) == 2 * 3 * 66048
     # fp32 at d = 128: windows of up to 16 chunks of fp32 chunk operands (213,504 B per
     # chunk and head) plus the state carried between windows
@@ -319,6 +324,8 @@ def test_prefill_descriptor_checks(lib):
                 dv=128, scale=0.1, dtype=0)
     d = kda.PrefillDesc(**base)
     assert kda.prefill_workspace_size(d) == (4 * 4096 // 64 + 4) * 16 * 66048
+    seg = kda.PrefillDesc(**{**base, "N": 1, "T": 65536, "H": 32})    # 8 segments
+    assert kda.prefill_workspace_size(seg) == (3 * 8 - 2) * 32 * 128 * 128 * 4
     assert kda.prefill_workspace_size(kda.PrefillDesc(**{**base, "H": 64})) == 0      # fused
     packed = kda.PrefillDesc(**{**base, "cu_seqlens": 4096, "T": 0, "total_T": 1000, "H": 8})
     assert kda.prefill_workspace_size(packed) == (1000 // 64 + 1 + 4) * 8 * 66048

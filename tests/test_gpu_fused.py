@@ -75,6 +75,31 @@ def test_fused_fixed_length(B, T, H):
     assert_close(f"fused {B}x{T}x{H} state", fs, ref_s.reshape(fs.shape), torch.bfloat16)
 
 
+@pytest.mark.parametrize("B,T,H,with_state", [(1, 8200, 32, True),    # 8 segments, 8-token tail
+                                               (1, 16400, 16, True),   # 16 segments
+                                               (3, 11000, 8, True),    # 10 unequal segments
+                                               (1, 32800, 4, False)])  # 32 segments
+def test_fused_segmented(B, T, H, with_state):
+    """Few long sequences: each cut into segments whose exit states and transitions
+    compose into every segment's entry state before the outputs run."""
+    from gated_delta_rule_102_amd import kda
+    assert "segments" in kda.prefill_schedule_name(B, T, H, 128)
+    d = kin.make_prefill(B, T, H, 128, 128, seed=80 + T + H, nonzero_state=with_state)
+    d["scale"] = 1.0 / math.sqrt(128)
+    g = _dev(d)
+    args = [g[x] for x in ("q", "k", "v", "g", "beta")]
+    out, fs = kda.kda_chunk_fwd(*args, d["scale"], g.get("initial_state"))
+    torch.cuda.synchronize()
+    ref_o, ref_s = oracle_fixed(d)
+    assert_close(f"segmented {B}x{T}x{H} out", out, ref_o.reshape(out.shape), torch.bfloat16)
+    assert_close(f"segmented {B}x{T}x{H} state", fs, ref_s.reshape(fs.shape), torch.bfloat16)
+    if with_state:   # the final state may overwrite the initial state
+        st = g["initial_state"].clone()
+        out2, _ = kda.kda_chunk_fwd(*args, d["scale"], st, final_state=st)
+        torch.cuda.synchronize()
+        assert torch.equal(out, out2) and torch.equal(fs, st)
+
+
 @pytest.mark.parametrize("mode", ["floor", "slow", "zero"])
 def test_fused_decay_extremes(mode):
     """g = -5 everywhere (sub-tile factors reach e^75, the chunk's e^-320 underflows),

@@ -1,7 +1,8 @@
 """kda_chunk_fwd_noalloc (scratch in a fixed per-GPU array, nothing allocated) against
 kda_chunk_fwd and the fp64 oracle, through the C ABI: two calls in a row, the second
-with a smaller input, so the second runs on what the first left in the array; plus
-the fused schedule (no scratch) and the refusal of sizes whose windows do not fit.
+with a smaller input, so the second runs on what the first left in the array (the
+segmented schedule's states, the windowed schedule's chunk operands); plus the fused
+schedule (no scratch) and the refusal of sizes whose windows do not fit.
 Tolerances of tests/parity.py."""
 import ctypes
 import math
@@ -28,6 +29,7 @@ def _gpu():
 
 
 @pytest.mark.parametrize("first,second", [((4, 4096, 16), (2, 700, 16)),     # windows of 7
+                                          ((1, 16400, 16), (1, 300, 24)),    # segmented, windowed
                                           ((2, 150, 128), (1, 300, 24))])    # fused, windowed
 def test_noalloc_two_calls_match_kda_chunk_fwd(first, second):
     from gated_delta_rule_102_amd import kda
