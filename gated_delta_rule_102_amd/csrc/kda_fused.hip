@@ -283,6 +283,12 @@ __device__ __forceinline__ void flag_wait(char* smem, const int off, const int v
 
 // ------------------------------------------------------------------ operand role
 // Wavefront I (0..3) of the workgroup, sub-tile I of every chunk.
+// OUT = false: the run's output is not wanted (a segment's exit state or transition,
+// launched with out_on = 0), so the operand role computes nothing that only the output
+// needs: no q loads, Qb or q row sides, no M products.  The state role is the same in
+// both forms; without these operands its output products read whatever LDS holds and
+// their stores are dropped.
+template <bool OUT>
 __device__ __forceinline__ void operand_role(const FusedParams& p, char* smem, const int I,
                                              const int h, const int tok0, const int len,
                                              const int nchunks) {
@@ -324,7 +330,7 @@ __device__ __forceinline__ void operand_role(const FusedParams& p, char* smem, c
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       in.k[b] = buf_ld128(rk, row + (32 * b + 8 * g4) * 2, 0);
-      in.q[b] = buf_ld128(rq, row + (32 * b + 8 * g4) * 2, 0);
+      if constexpr (OUT) in.q[b] = buf_ld128(rq, row + (32 * b + 8 * g4) * 2, 0);
     }
   };
 
@@ -434,16 +440,18 @@ __device__ __forceinline__ void operand_role(const FusedParams& p, char* smem, c
             for (int j = 0; j < 2; ++j) {
               const int i = 2 * i2 + j, e = 4 * hh + i;
               const float kv = j ? bf16hi(kw) : bf16lo(kw);
-              const float qv = j ? bf16hi(qw) : bf16lo(qw);
               const float d = L[b][e] * kLog2e;           // L log2 e <= 0
               const float ef = fast_exp2(d), eb = fast_exp2(-d);
               kb[j] = -(kv * ef);            // -K e^{L}
-              qb[j] = (qv * ef) * p.scale;   // scale Q e^{L}
+              if constexpr (OUT) {
+                const float qv = j ? bf16hi(qw) : bf16lo(qw);
+                qb[j] = (qv * ef) * p.scale;   // scale Q e^{L}
+              }
               cs[j] = kv * eb;               // K e^{-L}
               kt[j] = cs[j] * vN[i];         // K e^{Ln - L}
             }
             pkb[w] = pack_bf16x2(kb[0], kb[1]);
-            pqb[w] = pack_bf16x2(qb[0], qb[1]);
+            if constexpr (OUT) pqb[w] = pack_bf16x2(qb[0], qb[1]);
             pkc[w] = pack_bf16x2(cs[0], cs[1]);
             pkt[w] = pack_bf16x2(kt[0], kt[1]);
           } else {
@@ -452,21 +460,23 @@ __device__ __forceinline__ void operand_role(const FusedParams& p, char* smem, c
             for (int j = 0; j < 2; ++j) {
               const int i = 2 * i2 + j, e = 4 * hh + i;
               const float kv = j ? bf16hi(kw) : bf16lo(kw);
-              const float qv = j ? bf16hi(qw) : bf16lo(qw);
               const float d = __builtin_fmaf(L[b][e], kLog2e, -tv[i]);   // (L - R_I) log2 e >= 0
               const float rowf = fast_exp2(d), colf = fast_exp2(-d);
               kr[j] = kv * rowf;
-              qr[j] = qv * rowf;
+              if constexpr (OUT) {
+                const float qv = j ? bf16hi(qw) : bf16lo(qw);
+                qr[j] = qv * rowf;
+              }
               kc[j] = kv * colf;
               kb[j] = kr[j] * vK[i];     // -K e^{L}
-              qb[j] = qr[j] * vQ[i];     // scale Q e^{L}
+              if constexpr (OUT) qb[j] = qr[j] * vQ[i];     // scale Q e^{L}
               kt[j] = kc[j] * vN[i];     // K e^{Ln - L}
             }
             pkr[w] = pack_bf16x2(kr[0], kr[1]);
-            pqr[w] = pack_bf16x2(qr[0], qr[1]);
+            if constexpr (OUT) pqr[w] = pack_bf16x2(qr[0], qr[1]);
             pkc[w] = pack_bf16x2(kc[0], kc[1]);
             pkb[w] = pack_bf16x2(kb[0], kb[1]);
-            pqb[w] = pack_bf16x2(qb[0], qb[1]);
+            if constexpr (OUT) pqb[w] = pack_bf16x2(qb[0], qb[1]);
             pkt[w] = pack_bf16x2(kt[0], kt[1]);
             if (IC == 1) {   // column side of pair (2, 1): K e^{R_2 - L}
               const float f0 = i2 ? fo[hh].z : fo[hh].x, f1 = i2 ? fo[hh].w : fo[hh].y;
@@ -476,10 +486,10 @@ __device__ __forceinline__ void operand_role(const FusedParams& p, char* smem, c
         }
       }
       fKr[b] = frag(IC == 0 ? pkb : pkr);
-      fQr[b] = frag(IC == 0 ? pqb : pqr);
+      if constexpr (OUT) fQr[b] = frag(IC == 0 ? pqb : pqr);
       fKc[b] = frag(pkc);
       *reinterpret_cast<bf16x8_t*>(smem + fl::KBN + frag_at(IC, b, 4, lane)) = frag(pkb);
-      *reinterpret_cast<bf16x8_t*>(smem + qb_off + frag_at(IC, b, 4, lane)) = frag(pqb);
+      if constexpr (OUT) *reinterpret_cast<bf16x8_t*>(smem + qb_off + frag_at(IC, b, 4, lane)) = frag(pqb);
       // Kt^T: the products with sel[hs] give, in lane (l16, g), tokens 16 I + 4 g .. +3
       // of the channel of state row 16 (2 b + hs) + l16 -- half of that lane's
       // fragment (state tile 2 b + hs, s-block I / 2), elements 4 (I % 2) .. +3
@@ -541,14 +551,15 @@ __device__ __forceinline__ void operand_role(const FusedParams& p, char* smem, c
         // row sides: registers, except the pairs (I >= 1, 0), which take -Kb and Qb
         const bool rows_lds = J == 0 && I > 0;
         const bf16x8_t rk = rows_lds ? lds_frag(smem, fl::KBN + frag_at(I, b, 4, lane)) : fKr[b];
-        const bf16x8_t rq = rows_lds ? lds_frag(smem, qb_off + frag_at(I, b, 4, lane)) : fQr[b];
+        bf16x8_t rq;
+        if constexpr (OUT) rq = rows_lds ? lds_frag(smem, qb_off + frag_at(I, b, 4, lane)) : fQr[b];
         // column side: the own sub-tile's for the diagonal and, on wavefront 0, for
         // (I, 0); otherwise the region written by the column's owner
         const int cs_id = J == 0 ? 0 : (I == 2 ? 1 : J + 1);   // (2,1) -> 1, (3,1) -> 2, (3,2) -> 3
         const bool cols_reg = J == I || (J == 0 && W == 0);
         const bf16x8_t cs = cols_reg ? fKc[b] : lds_frag(smem, fl::CS + cs_id * 4096 + frag_at(0, b, 4, lane));
         pa[x] = mma(cs, rk, pa[x]);
-        pm[x] = mma(cs, rq, pm[x]);
+        if constexpr (OUT) pm[x] = mma(cs, rq, pm[x]);
       }
     }
     const float* betas = reinterpret_cast<const float*>(smem + fl::BETA) + (c & 1) * kCh;
@@ -571,8 +582,9 @@ __device__ __forceinline__ void operand_role(const FusedParams& p, char* smem, c
         }
       }
       // M[t][s]: fragment (t-tile I, s-block J/2), elements 4 (J%2) .. +3
-      *reinterpret_cast<uint2*>(smem + fl::MF + frag_at(I, J >> 1, 2, lane) + 8 * (J & 1)) =
-          uint2{pack_bf16x2(mv[0], mv[1]), pack_bf16x2(mv[2], mv[3])};
+      if constexpr (OUT)
+        *reinterpret_cast<uint2*>(smem + fl::MF + frag_at(I, J >> 1, 2, lane) + 8 * (J & 1)) =
+            uint2{pack_bf16x2(mv[0], mv[1]), pack_bf16x2(mv[2], mv[3])};
       if (J < I) {   // -A_IJ as a 16x16x16 A operand: lane (t, g) holds columns 4 g .. +3
         *reinterpret_cast<uint2*>(smem + fl::AOF + off_id(I, J) * 512 + lane * 8) =
             uint2{pack_bf16x2(-av[0], -av[1]), pack_bf16x2(-av[2], -av[3])};
@@ -918,6 +930,7 @@ __device__ __forceinline__ void state_role(const FusedParams& p, char* smem, con
   }
 }
 
+template <bool OUT>
 __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams p) {
   __shared__ __attribute__((aligned(16))) char smem[fl::BYTES];
   const int tid = threadIdx.x;
@@ -960,7 +973,7 @@ __global__ __launch_bounds__(kThreadsF, 1) void fused_prefill_kernel(FusedParams
     *reinterpret_cast<i32x4_t*>(smem + fl::MF + e * 16) = i32x4_t{0, 0, 0, 0};
 
   if (wave < 4) {
-    operand_role(p, smem, wave, h, tok0, len, nchunks);
+    operand_role<OUT>(p, smem, wave, h, tok0, len, nchunks);
   } else {
     int s0_idx = n, sT_idx = n;
     if (p.segR > 0) {   // n = s segs + r; states indexed r N + s
@@ -983,7 +996,7 @@ hipError_t launch_fused_prefill(const PrefillArgs& a) {
                  static_cast<const bf16_t*>(a.v), static_cast<const bf16_t*>(a.g),
                  static_cast<const bf16_t*>(a.beta), a.initial_state, static_cast<bf16_t*>(a.out),
                  a.final_state, a.cu_seqlens, a.N, a.T, a.total_T, a.H, a.scale};
-  hipLaunchKernelGGL(fused_prefill_kernel, dim3(static_cast<unsigned>(a.N) * a.H), dim3(kThreadsF), 0,
+  hipLaunchKernelGGL(fused_prefill_kernel<true>, dim3(static_cast<unsigned>(a.N) * a.H), dim3(kThreadsF), 0,
                      a.stream, fp);
   return hipGetLastError();
 }
@@ -1025,13 +1038,13 @@ hipError_t launch_fused_segmented(const PrefillArgs& a, int R) {
   };
   const unsigned g1 = static_cast<unsigned>(a.N) * (R - 1) * a.H;
   const FusedParams px = params(1, nullptr, 0, exits, R - 1, 0, 0);
-  KDA_TRY_LAUNCH(err, fused_prefill_kernel, dim3(g1), dim3(kThreadsF), 0, a.stream, px);
+  KDA_TRY_LAUNCH(err, fused_prefill_kernel<false>, dim3(g1), dim3(kThreadsF), 0, a.stream, px);
   const FusedParams pp = params(0, nullptr, 0, trans, R - 1, 1, 0);
-  KDA_TRY_LAUNCH(err, fused_prefill_kernel, dim3(g1), dim3(kThreadsF), 0, a.stream, pp);
+  KDA_TRY_LAUNCH(err, fused_prefill_kernel<false>, dim3(g1), dim3(kThreadsF), 0, a.stream, pp);
   if (err == hipSuccess)
     err = launch_compose(ComposeArgs{trans, exits, a.initial_state, entry, R - 1, a.N, a.H, kD, a.stream});
   const FusedParams po = params(1, entry, 1, a.final_state, R, 0, 1);
-  KDA_TRY_LAUNCH(err, fused_prefill_kernel, dim3(static_cast<unsigned>(a.N) * R * a.H), dim3(kThreadsF), 0,
+  KDA_TRY_LAUNCH(err, fused_prefill_kernel<true>, dim3(static_cast<unsigned>(a.N) * R * a.H), dim3(kThreadsF), 0,
                  a.stream, po);
   const hipError_t ferr = ws_release(a.workspace, ws, a.stream);
   return err != hipSuccess ? err : ferr;
