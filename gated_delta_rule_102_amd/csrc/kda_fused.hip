@@ -123,7 +123,7 @@ struct EyeMatrix {
     for (int i = 0; i < kD; ++i) v[i * (kD + 1)] = 1.f;
   }
 };
-__device__ const EyeMatrix kEye{};
+__device__ EyeMatrix kEye{};   // global (not constant) memory: the initial state loads stay global loads
 
 // Chunk that starts segment r of a sequence of nc chunks cut into R segments.
 __device__ __forceinline__ int seg_chunk(const int r, const int nc, const int R) {
