@@ -537,11 +537,26 @@ __device__ __forceinline__ void operand_role(const FusedParams& p, char* smem, c
     constexpr int PI[4][3] = {{0, 2, 3}, {1, 1, 0}, {2, 2, 0}, {3, 3, 3}};
     constexpr int PJ[4][3] = {{0, 0, 0}, {1, 0, 0}, {2, 1, 0}, {3, 1, 2}};
     const int qb_off = fl::QB + (c & 1) * 16384;
+    const float* betas = reinterpret_cast<const float*>(smem + fl::BETA) + (c & 1) * kCh;
     f32x4_t pa[NP], pm[NP];
 #pragma unroll
     for (int x = 0; x < NP; ++x) {
       pa[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       pm[x] = pa[x];
+    }
+    // The diagonal block first (pair x = 0 on every wavefront; its row and column
+    // sides are the wavefront's own registers): A_II goes to the state role's inverse
+    // while the other products run.  For (0, 0) the row side is -Kb, so A's sign flips.
+    {
+      constexpr int I = PI[W][0];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) pa[0] = mma(fKc[b], fKr[b], pa[0]);
+      const float fa_ = I == 0 ? -beta_t : beta_t;
+      f32x4_t av;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = 4 * g4 + i < l16 ? fa_ * pa[0][i] : 0.f;
+      *reinterpret_cast<f32x4_t*>(smem + fl::AII + I * 1024 + lane * 16) = av;
+      flag_set(smem, fl::AIIF + 4 * I, c + 1);
     }
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
@@ -558,41 +573,34 @@ __device__ __forceinline__ void operand_role(const FusedParams& p, char* smem, c
         const int cs_id = J == 0 ? 0 : (I == 2 ? 1 : J + 1);   // (2,1) -> 1, (3,1) -> 2, (3,2) -> 3
         const bool cols_reg = J == I || (J == 0 && W == 0);
         const bf16x8_t cs = cols_reg ? fKc[b] : lds_frag(smem, fl::CS + cs_id * 4096 + frag_at(0, b, 4, lane));
-        pa[x] = mma(cs, rk, pa[x]);
+        if (x > 0) pa[x] = mma(cs, rk, pa[x]);
         if constexpr (OUT) pm[x] = mma(cs, rq, pm[x]);
       }
     }
-    const float* betas = reinterpret_cast<const float*>(smem + fl::BETA) + (c & 1) * kCh;
 #pragma unroll
     for (int x = 0; x < NP; ++x) {
       const int I = PI[W][x], J = PJ[W][x];
       const float bt = I == W ? beta_t : betas[16 * I + l16];
       // J = 0: the row sides are -Kb (A's sign flips) and Qb (scale included)
       const float fa_ = J == 0 ? -bt : bt, fm_ = J == 0 ? 1.f : p.scale;
-      // masks only on the diagonal pair (s = 16 I + 4 g + i against t = 16 I + l16)
-      f32x4_t av;
-      float mv[4];
+      // M[t][s]: fragment (t-tile I, s-block J/2), elements 4 (J%2) .. +3; the
+      // diagonal pair's masked to s <= t
+      if constexpr (OUT) {
+        float mv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        av[i] = fa_ * pa[x][i];
-        mv[i] = fm_ * pm[x][i];
-        if (J == I) {
-          av[i] = 4 * g4 + i < l16 ? av[i] : 0.f;
-          mv[i] = 4 * g4 + i <= l16 ? mv[i] : 0.f;
+        for (int i = 0; i < 4; ++i) {
+          mv[i] = fm_ * pm[x][i];
+          if (J == I) mv[i] = 4 * g4 + i <= l16 ? mv[i] : 0.f;
         }
-      }
-      // M[t][s]: fragment (t-tile I, s-block J/2), elements 4 (J%2) .. +3
-      if constexpr (OUT)
         *reinterpret_cast<uint2*>(smem + fl::MF + frag_at(I, J >> 1, 2, lane) + 8 * (J & 1)) =
             uint2{pack_bf16x2(mv[0], mv[1]), pack_bf16x2(mv[2], mv[3])};
+      }
       if (J < I) {   // -A_IJ as a 16x16x16 A operand: lane (t, g) holds columns 4 g .. +3
+        float av[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) av[i] = fa_ * pa[x][i];
         *reinterpret_cast<uint2*>(smem + fl::AOF + off_id(I, J) * 512 + lane * 8) =
             uint2{pack_bf16x2(-av[0], -av[1]), pack_bf16x2(-av[2], -av[3])};
-      } else {
-        // the diagonal block (the first pair each wavefront finishes) goes to its
-        // inverse on the state role right away
-        *reinterpret_cast<f32x4_t*>(smem + fl::AII + I * 1024 + lane * 16) = av;
-        flag_set(smem, fl::AIIF + 4 * I, c + 1);
       }
     }
   };
