@@ -387,3 +387,27 @@ def test_backward_window_workspace_sizes(lib):
     nwin = ((tot + 63) // 64 + 3) // 4
     assert L.kda_chunk_bwd_varlen_window_workspace_size(N, tot, 2, 128, 128, 0, 4) == \
         N * 2 * 4 * item + (nwin - 1 + 2) * N * 2 * state
+
+
+def test_prefill_schedule_selection_host_logic(lib):
+    """kda_chunk_fwd_schedule (host arithmetic, no device): bf16 at d = 128 runs fused
+    from 256 (sequence, head) streams on; fixed length with 4 to 32 streams and
+    segments of at least 16 chunks runs segmented, R = min(32, 256 / streams); the rest
+    two-kernel (from 64 streams at 64 chunks or fewer) or windowed."""
+    import torch
+    from gated_delta_rule_102_amd import kda
+    name = kda.prefill_schedule_name
+    assert name(2, 150, 128, 128).startswith("fused_prefill_kernel (one workgroup")
+    assert "in 8 segments" in name(1, 65536, 32, 128)          # 32 streams, 128 chunks each
+    assert "in 16 segments" in name(1, 16384, 16, 128)         # exactly 16 chunks per segment
+    assert "segments" not in name(1, 16320, 16, 128)           # 255 chunks: 15.9 per segment
+    assert "in 32 segments" in name(1, 65536, 4, 128)          # 256 / 4 = 64, capped at 32
+    assert "in 10 segments" in name(3, 11000, 8, 128)          # 24 streams: 256 / 24 = 10
+    assert "segments" not in name(1, 65536, 2, 128)            # fewer than 4 streams
+    assert "segments" not in name(4, 4096, 16, 128)            # 64 streams
+    assert name(4, 4096, 16, 128).startswith("chunk_prep8_kernel")
+    assert name(1, 4096, 32, 128).startswith("prefill_group_kernel")
+    # packed input, fp32 and d = 64 never run segmented
+    assert "segments" not in name(1, 65536, 32, 128, varlen=True, total_T=65536)
+    assert "segments" not in name(1, 65536, 32, 128, torch.float32)
+    assert "segments" not in name(1, 65536, 32, 64)
