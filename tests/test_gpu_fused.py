@@ -98,6 +98,16 @@ def test_fused_segmented(B, T, H, with_state):
         out2, _ = kda.kda_chunk_fwd(*args, d["scale"], st, final_state=st)
         torch.cuda.synchronize()
         assert torch.equal(out, out2) and torch.equal(fs, st)
+    # on a caller workspace of exactly the stated size, and without a final state:
+    # the same outputs bit for bit
+    ws = kda.chunk_fwd_workspace(g["q"], g["v"])
+    assert ws.numel() - 256 == kda.kda_chunk_fwd_workspace_size(B, T, H, 128, 128)
+    out3, fs3 = kda.kda_chunk_fwd(*args, d["scale"], g.get("initial_state"), workspace=ws)
+    out4, none = kda.kda_chunk_fwd(*args, d["scale"], g.get("initial_state"),
+                                   output_final_state=False)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.equal(out, out3) and torch.equal(fs, fs3) and torch.equal(out, out4)
 
 
 @pytest.mark.parametrize("mode", ["floor", "slow", "zero"])
