@@ -267,6 +267,7 @@ hipError_t launch_transition_t(const TransitionArgs& a) {
 }  // namespace
 
 size_t transition_workspace_bytes(const TransitionArgs& a) {
+  if (fused_transition_supported(a)) return 0;
   const int64_t items = static_cast<int64_t>(a.B) * a.H * ((a.T + CR - 1) / CR);
   int64_t per = 0;
   if (a.d == 128) per = a.dtype_f32 ? transition_floats_per_item<128, float>() : transition_floats_per_item<128, bf16_t>();
@@ -275,6 +276,7 @@ size_t transition_workspace_bytes(const TransitionArgs& a) {
 }
 
 hipError_t launch_transition(const TransitionArgs& a) {
+  if (fused_transition_supported(a)) return launch_fused_transition(a);
   if (a.d == 128) {
     return a.dtype_f32 ? launch_transition_t<128, float>(a) : launch_transition_t<128, bf16_t>(a);
   }

@@ -1009,6 +1009,26 @@ hipError_t launch_fused_prefill(const PrefillArgs& a) {
   return hipGetLastError();
 }
 
+bool fused_transition_supported(const TransitionArgs& a) {
+  return !a.dtype_f32 && a.d == kD && static_cast<int64_t>(a.B) * a.H >= 256;
+}
+
+// A segment's transition with the fused kernel: the run from the identity with v read
+// as zero, its exit state written to `transition`; q and v are not read (their
+// pointers only stand in for valid addresses), nothing is written but the state.
+hipError_t launch_fused_transition(const TransitionArgs& a) {
+  const bf16_t* k = static_cast<const bf16_t*>(a.k);
+  FusedParams fp{k, k, k, static_cast<const bf16_t*>(a.g), static_cast<const bf16_t*>(a.beta), nullptr,
+                 reinterpret_cast<bf16_t*>(a.transition), a.transition, nullptr, a.B, a.T, a.B * a.T, a.H,
+                 1.f};
+  fp.s0_eye = 1;
+  fp.v_on = 0;
+  fp.out_on = 0;
+  hipLaunchKernelGGL(fused_prefill_kernel<false>, dim3(static_cast<unsigned>(a.B) * a.H), dim3(kThreadsF), 0,
+                     a.stream, fp);
+  return hipGetLastError();
+}
+
 size_t fused_segmented_bytes(const PrefillArgs& a, int R) {
   // exit states and transitions of segments 0 .. R-2, entry states of all R segments
   return static_cast<size_t>(3 * R - 2) * a.N * a.H * kD * kD * sizeof(float);

@@ -106,6 +106,10 @@ hipError_t launch_fused_prefill(const PrefillArgs& a);
 // states, then every segment's output; fused_segmented_bytes of workspace.
 size_t fused_segmented_bytes(const PrefillArgs& a, int R);
 hipError_t launch_fused_segmented(const PrefillArgs& a, int R);
+// Transitions with the fused kernel (bf16, d = 128, 256 or more (segment, head)
+// streams; no workspace).
+bool fused_transition_supported(const TransitionArgs& a);
+hipError_t launch_fused_transition(const TransitionArgs& a);
 // Kernels launch_prefill runs for these arguments (static text, for reports).
 const char* prefill_schedule(const PrefillArgs& a);
 // Workspace bytes launch_prefill needs for these arguments (0 if unsupported).

@@ -473,7 +473,8 @@ int kda_chunk_bwd_varlen_ws(const void* q, const void* k, const void* v, const v
  * an fp32 state, the precision of the bf16 prefill.  Its workspace
  * (kda_chunk_transition_workspace_size) takes, per 64-token chunk per head,
  * 213,504 bytes for fp32 and 320,000 for bf16 at d = 128 (147,712 and 213,248 at
- * d = 64).
+ * d = 64); none for bf16 at d = 128 with B H >= 256, which runs on the fused
+ * prefill kernel (one workgroup per (segment, head)).
  */
 int kda_chunk_transition(const void* q, const void* k, const void* g, const void* beta,
                          float* transition, int B, int T, int H, int dk, int dv, int dtype,

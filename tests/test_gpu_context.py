@@ -71,6 +71,35 @@ def test_transition_matches_oracle(dtype, D, T, decay):
             assert mx <= 2e-2 * peak, f"b={b}: max_abs {mx:.3e} against max |P| {peak:.3e}"
 
 
+@pytest.mark.parametrize("T,decay", [(150, "slow"), (64, "standard")])
+def test_transition_fused_matches_oracle(T, decay):
+    """256 (segment, head) streams of bf16 at d = 128: the transitions run on the fused
+    prefill kernel (from the identity, v switched off, no workspace).  Same bars as
+    above; every segment and head is checked."""
+    from gated_delta_rule_102_amd import kda
+    B, H, D = 16, 16, 128
+    assert kda.load_library().kda_chunk_transition_workspace_size(B, T, H, D, D, 0) == 0
+    d = kin.make_prefill(B, T, H, D, D, dtype=torch.bfloat16, seed=540 + T)
+    g = d["g"]
+    if decay == "slow":
+        gen = torch.Generator().manual_seed(640 + T)
+        g = (-0.05 * torch.rand(d["g"].shape, generator=gen)).to(torch.bfloat16)
+    args = [d["q"].to(DEV), d["k"].to(DEV), g.to(DEV), d["beta"].to(DEV)]
+    P = kda.kda_chunk_transition(*args)
+    P2 = kda.kda_chunk_transition(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(P, P2)
+    worst = 0.0
+    for b in range(B):
+        ref = transition_np(d["k"][b], g[b], d["beta"][b])
+        peak = float(np.max(np.abs(ref)))
+        mx, rel = errors(P[b].cpu().numpy(), ref)
+        worst = max(worst, rel)
+        assert rel <= 1e-2, f"b={b}: rel_l2 {rel:.3e}"
+        assert mx <= 2e-2 * peak, f"b={b}: max_abs {mx:.3e} against max |P| {peak:.3e}"
+    print(f"fused transitions, {decay} decay: worst rel_l2 {worst:.2e}", flush=True)
+
+
 def test_compose_matches_numpy():
     from gated_delta_rule_102_amd import kda
     R, B, H, D = 5, 2, 3, 128
