@@ -133,6 +133,35 @@ def test_fused_decay_extremes(mode):
     assert_close(f"fused decay {mode} state", fs, ref_s.reshape(fs.shape), torch.bfloat16)
 
 
+@pytest.mark.parametrize("mode", ["floor", "slow", "zero"])
+def test_fused_segmented_decay_extremes(mode):
+    """The segmented schedule where the segments' transitions matter most: g = 0
+    (plain delta rule, the transitions do not decay) and g in [-0.05, 0], and at the
+    floor g = -5 (the transitions underflow to zero), 16 segments of 16 chunks, with
+    an initial state."""
+    from gated_delta_rule_102_amd import kda
+    B, T, H = 1, 16400, 16
+    assert "in 16 segments" in kda.prefill_schedule_name(B, T, H, 128)
+    d = kin.make_prefill(B, T, H, 128, 128, seed=83, nonzero_state=True)
+    if mode == "floor":
+        d["g"] = torch.full_like(d["g"], -5.0)
+    elif mode == "slow":
+        d["g"] = (-0.05 * torch.rand(d["g"].shape, generator=torch.Generator().manual_seed(5))
+                  ).to(torch.bfloat16)
+    else:
+        d["g"] = torch.zeros_like(d["g"])
+    d["scale"] = 1.0 / math.sqrt(128)
+    g = _dev(d)
+    out, fs = kda.kda_chunk_fwd(g["q"], g["k"], g["v"], g["g"], g["beta"], d["scale"],
+                                g["initial_state"])
+    torch.cuda.synchronize()
+    ref_o, ref_s = oracle_fixed(d)
+    eo = assert_close(f"segmented decay {mode} out", out, ref_o.reshape(out.shape), torch.bfloat16)
+    es = assert_close(f"segmented decay {mode} state", fs, ref_s.reshape(fs.shape), torch.bfloat16)
+    print(f"segmented decay {mode}: out max_abs {eo[0]:.2e} rel_l2 {eo[1]:.2e}; "
+          f"state max_abs {es[0]:.2e} rel_l2 {es[1]:.2e}", flush=True)
+
+
 def test_fused_in_place_and_no_final_state():
     from gated_delta_rule_102_amd import kda
     d = _dev(kin.make_prefill(2, 130, 128, 128, 128, seed=91, nonzero_state=True))
