@@ -59,13 +59,28 @@ def test_snapshots_many_streams():
     _check_snapshots(8, 16, 200, 64, 128, torch.bfloat16)
 
 
+def test_snapshots_256_streams():
+    """2 sequences x 128 heads (a plain call of this shape runs the fused kernel): a
+    44-token tail after the last full interval."""
+    _check_snapshots(2, 128, 300, 128, 128, torch.bfloat16)
+
+
 def _check_snapshots(B, H, T, S, D, dtype):
     d = kin.make_prefill(B, T, H, D, D, dtype=dtype, seed=31 + T, nonzero_state=True)
     d["scale"] = 1.0 / math.sqrt(D)
     out, fs, snaps, out2, fs2 = _run(d, S)
     nsnap = -(-T // S)
     assert tuple(snaps.shape) == (B, H, nsnap, D, D)
-    assert torch.equal(out, out2) and torch.equal(fs, fs2), "snapshots changed the results"
+    from gated_delta_rule_102_amd import kda
+    if kda.prefill_schedule_name(B, T, H, D).startswith("fused"):
+        # the plain call runs the fused kernel, the snapshot call the two-kernel
+        # schedule: both against the oracle
+        ref_o, ref_f = oracle_fixed(d)
+        assert_close("output", out, ref_o.reshape(out.shape), dtype)
+        assert_close("final state", fs, ref_f.reshape(fs.shape), dtype)
+        assert_close("output (plain call)", out2, ref_o.reshape(out.shape), dtype)
+    else:
+        assert torch.equal(out, out2) and torch.equal(fs, fs2), "snapshots changed the results"
     assert torch.equal(snaps[:, :, -1], fs), "last snapshot differs from the final state"
     for i in range(nsnap):
         t = min((i + 1) * S, T)
@@ -118,11 +133,14 @@ def test_snapshots_across_windows():
     ([300, 0, 64, 1, 190, 700], 3, 128, 128, torch.bfloat16),
     ([130, 65, 256], 2, 64, 64, torch.float32),
     ([70 + 13 * i for i in range(48)], 3, 64, 128, torch.bfloat16),   # 144 streams
+    ([300, 0, 64, 1, 190, 700, 129, 65, 256, 17, 1000, 3, 128, 511, 77, 640], 16, 128, 128,
+     torch.bfloat16),                                                 # 256 streams
 ])
 def test_varlen_snapshots_match_oracle(lengths, H, S, D, dtype):
     """kda_chunk_fwd_varlen_snapshots: every snapshot row of every sequence against the
     oracle's final state on that sequence's prefix; out and final state bitwise equal
-    to kda_chunk_fwd_varlen; each sequence's last row equal to its final state."""
+    to kda_chunk_fwd_varlen (or, where that call runs the fused kernel, both against the
+    oracle); each sequence's last row equal to its final state."""
     from gated_delta_rule_102_amd import kda
     d = kin.make_varlen(lengths, H, D, D, dtype=dtype, seed=71, nonzero_state=True)
     d["scale"] = 1.0 / math.sqrt(D)
@@ -133,7 +151,11 @@ def test_varlen_snapshots_match_oracle(lengths, H, S, D, dtype):
     out2, fs2 = kda.kda_chunk_fwd_varlen(*args, scale=d["scale"],
                                          initial_state=g["initial_state"])
     torch.cuda.synchronize()
-    assert torch.equal(out, out2) and torch.equal(fs, fs2), "snapshots changed the results"
+    # a plain call that runs the fused kernel is checked against the oracle below
+    fused = kda.prefill_schedule_name(len(lengths), max(lengths), H, D, dtype, varlen=True,
+                                      total_T=sum(lengths)).startswith("fused")
+    if not fused:
+        assert torch.equal(out, out2) and torch.equal(fs, fs2), "snapshots changed the results"
     assert int(rows[-1]) == sum(-(-L // S) for L in lengths)
     assert tuple(snaps.shape) == (int(rows[-1]), H, D, D)
     cu = d["cu_seqlens"].tolist()
@@ -143,9 +165,19 @@ def test_varlen_snapshots_match_oracle(lengths, H, S, D, dtype):
         assert r1 - r0 == -(-L // S)
         if L:
             assert torch.equal(snaps[r1 - 1], fs[n]), f"sequence {n}: last row != final state"
-        # the oracle on every prefix of the small cases, on three sequences of the large one
-        if len(lengths) > 8 and n not in (0, 23, 47):
+        # the oracle on every prefix of the small cases, on a few sequences of the large
+        # ones (the longest among them)
+        if len(lengths) > 8 and n not in (0, 5, 10, 13, 23, 47):
             continue
+        if fused and L:
+            sl = {x: d[x][:, cu[n]:cu[n] + L].contiguous() for x in ("q", "k", "v", "g", "beta")}
+            sl["initial_state"] = d["initial_state"][n:n + 1]
+            sl["scale"] = d["scale"]
+            ref_o, ref_f = oracle_fixed(sl)
+            for name, o in (("", out), (" (plain call)", out2)):
+                assert_close(f"seq {n} output{name}", o[:, cu[n]:cu[n] + L],
+                             ref_o.reshape(1, L, H, D), dtype)
+            assert_close(f"seq {n} final state", fs[n], ref_f.reshape(H, D, D), dtype)
         for i in range(r1 - r0):
             t = min((i + 1) * S, L)
             sl = {x: d[x][:, cu[n]:cu[n] + t].contiguous() for x in ("q", "k", "v", "g", "beta")}
