@@ -295,7 +295,7 @@ __device__ __forceinline__ void stage_bf16_t(const ITile<NT, COLS, bf16_t>& t, _
   for (int j = 0; j < I::PER; ++j) {
     const int e = static_cast<int>(threadIdx.x) + j * NT;
     const int rr = e / COLS, c = e - rr * COLS;
-    dst[c * ld + rr] = static_cast<__bf16>(t.r[j]);
+    dst[c * ld + rr] = static_cast<__bf16>(t.val(j));
   }
 }
 template <int D>
@@ -602,8 +602,10 @@ template <int NT, int ROWS, int COLS>
 struct BTileS {   // ROWS x COLS bf16 slice of a matrix with row stride gld
   static constexpr int C8 = COLS / 8, N = ROWS * C8, PER = (N + NT - 1) / NT;
   bf16x8_t r[PER];
+  int nrow_;   // rows >= nrow_ are stored as zero (masked at the store, not the load)
   static __device__ __forceinline__ bool live(int e) { return N % NT == 0 || e < N; }
   __device__ __forceinline__ void load(const __bf16* src, int64_t gld) {
+    nrow_ = ROWS;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int e = static_cast<int>(threadIdx.x) + j * NT, rr = e / C8, c = (e - rr * C8) * 8;
@@ -612,14 +614,12 @@ struct BTileS {   // ROWS x COLS bf16 slice of a matrix with row stride gld
   }
   // 64 input rows (row stride gld), rows >= nrow as zero (clamped loads)
   __device__ __forceinline__ void load_rows(const bf16_t* src, int64_t gld, int nrow) {
+    nrow_ = nrow;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int e = static_cast<int>(threadIdx.x) + j * NT, rr = e / C8, c = (e - rr * C8) * 8;
-      if (live(e)) {
-        const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(
-            src + static_cast<int64_t>(min(rr, nrow - 1)) * gld + c);
-        r[j] = rr < nrow ? x : bf16x8_t{};
-      }
+      if (live(e))
+        r[j] = *reinterpret_cast<const bf16x8_t*>(src + static_cast<int64_t>(min(rr, nrow - 1)) * gld + c);
     }
   }
   __device__ __forceinline__ void pin_all() {
@@ -630,7 +630,7 @@ struct BTileS {   // ROWS x COLS bf16 slice of a matrix with row stride gld
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int e = static_cast<int>(threadIdx.x) + j * NT, rr = e / C8, c = (e - rr * C8) * 8;
-      if (live(e)) *reinterpret_cast<bf16x8_t*>(dst + rr * ld + c) = r[j];
+      if (live(e)) *reinterpret_cast<bf16x8_t*>(dst + rr * ld + c) = rr < nrow_ ? r[j] : bf16x8_t{};
     }
   }
 };
@@ -1078,12 +1078,34 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_chunk_kernel(
       }
     }
     __syncthreads();
-    if (tid < D) {   // dg = reverse running sum of dG, with the last row's extra terms
-      float run = dlam * w[L::LAM + tid];
-      for (int t = 0; t < CR; ++t) run += Qo[t * LD + tid];
-      for (int t = CR - 1; t >= 0; --t) {
-        run += Ko[t * LD + tid];
-        if (t < p.nrow) dg[(p.row0 + static_cast<int64_t>(t) * H) * D + tid] = Elem<TIn>::from(run);
+    // dg = reverse running sum of dG plus the last row's terms (dlam Lambda and the
+    // sum of the Qo column), in 512 / D row segments per column: segment sums to LDS
+    // (over k colf, dead since the pair products), then each thread runs its own rows
+    // from the sums of the segments below it.
+    {
+      constexpr int NSEG = kNnThreads / D, SR = CR / NSEG;
+      static_assert(NSEG * D == kNnThreads && NSEG * SR == CR, "dg segments");
+      const int c = tid % D, sg = tid / D, t0 = SR * sg;
+      float* segq = Ki;                 // [NSEG][D] column sums of Qo per segment
+      float* segk = Ki + NSEG * D;      // [NSEG][D] column sums of Ko per segment
+      float* base = Ki + 2 * NSEG * D;  // [D] dlam Lambda (dlam lives in threads < D)
+      float sq = 0.f, sk = 0.f;
+#pragma unroll
+      for (int t = 0; t < SR; ++t) {
+        sq += Qo[(t0 + t) * LD + c];
+        sk += Ko[(t0 + t) * LD + c];
+      }
+      segq[sg * D + c] = sq;
+      segk[sg * D + c] = sk;
+      if (tid < D) base[tid] = dlam * w[L::LAM + tid];
+      __syncthreads();
+      float run = base[c];
+#pragma unroll
+      for (int u = 0; u < NSEG; ++u) run += segq[u * D + c] + (u > sg ? segk[u * D + c] : 0.f);
+#pragma unroll
+      for (int t = SR - 1; t >= 0; --t) {
+        run += Ko[(t0 + t) * LD + c];
+        if (t0 + t < p.nrow) dg[(p.row0 + static_cast<int64_t>(t0 + t) * H) * D + c] = Elem<TIn>::from(run);
       }
     }
   }

@@ -217,31 +217,47 @@ __device__ __forceinline__ void l2g(float* dst, int64_t gld, const float* src, i
 }
 // 64 x COLS input rows (bf16 or fp32) -> fp32 in LDS; rows >= nrow read as zero.
 // The row index is clamped so every load is unconditional (a load under a
-// branch is waited for inside the branch, which serialises the loads).
+// branch is waited for inside the branch, which serialises the loads).  The
+// elements stay raw until they are read (val, store): converting or masking them
+// right after the load would wait for the load there, and a prefetch issued a step
+// ahead would then be waited for at once.
 template <int NT, int COLS, typename TIn>
 struct ITile {
   static constexpr int N = CR * COLS, PER = N / NT;
   static_assert(N % NT == 0, "tile split");
-  float r[PER];
+  static constexpr bool BF = IsBf16<TIn>::value;
+  using Raw = typename std::conditional<BF, uint32_t, float>::type;   // bf16: the bits
+  Raw r[PER];
+  int nrow_;
   __device__ __forceinline__ void load(const TIn* src, int64_t row_stride, int nrow) {
+    nrow_ = nrow;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int e = static_cast<int>(threadIdx.x) + j * NT;
       const int rr = e / COLS, c = e - rr * COLS;
-      const float x = to_f32(src[min(rr, nrow - 1) * row_stride + c]);
-      r[j] = rr < nrow ? x : 0.f;
+      const TIn x = src[min(rr, nrow - 1) * row_stride + c];
+      if constexpr (BF) r[j] = x.bits;
+      else r[j] = x;
     }
   }
   __device__ __forceinline__ void pin_all() {
 #pragma unroll
     for (int j = 0; j < PER; ++j) pin(r[j]);
   }
+  // element j as fp32 (zero for rows past nrow)
+  __device__ __forceinline__ float val(int j) const {
+    const int rr = (static_cast<int>(threadIdx.x) + j * NT) / COLS;
+    float x;
+    if constexpr (BF) x = __uint_as_float(r[j] << 16);
+    else x = r[j];
+    return rr < nrow_ ? x : 0.f;
+  }
   __device__ __forceinline__ void store(float* dst, int lld) const {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int e = static_cast<int>(threadIdx.x) + j * NT;
       const int rr = e / COLS, c = e - rr * COLS;
-      dst[rr * lld + c] = r[j];
+      dst[rr * lld + c] = val(j);
     }
   }
 };
