@@ -813,18 +813,41 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_chunk_kernel(
   else
     dv_accumulate<D, TIn>(sm, v, dout, st, dst, dl, du, item, p, rs, acc, dlam);
 
+  // bf16 inputs: the operands of the next products go to LDS once as bf16 (rounded
+  // as the products would round them), each in the orientations its products read
+  // with 16-byte runs of k: dQ' and -dW by rows and by columns, Kg by rows, P^T and
+  // Tb^T; the products are then the bf16 ones bit for bit
+  constexpr int LDB = D + 8, LT = CR + 8;
+  __bf16* smb = reinterpret_cast<__bf16*>(sm);
+  __bf16* KgB = smb;                          // [64][LDB] Kg
+  __bf16* dQB = KgB + CR * LDB;               // [64][LDB] dQ'
+  __bf16* dWB = dQB + CR * LDB;               // [64][LDB] -dW
+  __bf16* dQT = dWB + CR * LDB;               // [D][LT]  dQ'^T
+  __bf16* dWT = dQT + D * LT;                 // [D][LT]  -dW^T
+  __bf16* PT = dWT + D * LT;                  // [64][LT] P^T
+  __bf16* TBT = PT + CR * LT;                 // [64][LT] Tb^T
+  static_assert(3 * CR * LDB + 2 * D * LT + 2 * CR * LT <= 2 * NL::FRONT, "bf16 operands fit");
+
   // dQ' and dW to LDS; dQ' and dKt also stay in registers for the decayed products
 #pragma unroll
   for (int x = 0; x < 2 * DT::NBIG / 8; ++x) {
     const int j = wave + 8 * x;
     const int m = j / DT::NBIG, r = j - m * DT::NBIG, rt = r / CT, ct = r - rt * CT;
-    if (m == 0) {
-      put(dQ + 16 * rt * LD + 16 * ct, LD, acc[x]);
-    } else {
-      f32x4_t vv = acc[x];
+    f32x4_t vv = acc[x];
+    if (m != 0) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) vv[i] = -vv[i];
-      put(dW + 16 * rt * LD + 16 * ct, LD, vv);
+    }
+    if constexpr (BF) {
+      __bf16* rows = (m == 0 ? dQB : dWB) + 16 * rt * LDB + 16 * ct;
+      __bf16* cols = (m == 0 ? dQT : dWT) + 16 * ct * LT + 16 * rt;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rows[(4 * g4 + i) * LDB + l16] = static_cast<__bf16>(vv[i]);
+      *reinterpret_cast<bf16x4_t*>(cols + l16 * LT + 4 * g4) =
+          bf16x4_t{static_cast<__bf16>(vv[0]), static_cast<__bf16>(vv[1]),
+                   static_cast<__bf16>(vv[2]), static_cast<__bf16>(vv[3])};
+    } else {
+      put((m == 0 ? dQ : dW) + 16 * rt * LD + 16 * ct, LD, vv);
     }
   }
 
@@ -840,8 +863,27 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_chunk_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) t_g.r[j][i] = kv[i] * fexp(t_g.r[j][i]);
     }
-    t_g.store(Kg, LD);
-    t_p.store(Ps, LS);
+    if constexpr (BF) {
+#pragma unroll
+      for (int j = 0; j < t_g.PER; ++j) {   // element order of GTile<512, 64, D>
+        const int e = tid + j * kNnThreads, rr = e / (D / 4), c = (e - rr * (D / 4)) * 4;
+        *reinterpret_cast<bf16x4_t*>(KgB + rr * LDB + c) =
+            bf16x4_t{static_cast<__bf16>(t_g.r[j][0]), static_cast<__bf16>(t_g.r[j][1]),
+                     static_cast<__bf16>(t_g.r[j][2]), static_cast<__bf16>(t_g.r[j][3])};
+      }
+#pragma unroll
+      for (int j = 0; j < t_p.PER; ++j) {   // element order of GTile<512, 64, 64>
+        const int e = tid + j * kNnThreads, rr = e / (CR / 4), c = (e - rr * (CR / 4)) * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          PT[(c + i) * LT + rr] = static_cast<__bf16>(t_p.r[j][i]);
+          TBT[(c + i) * LT + rr] = static_cast<__bf16>(t_tb.r[j][i]);
+        }
+      }
+    } else {
+      t_g.store(Kg, LD);
+      t_p.store(Ps, LS);
+    }
     t_tb.store(TBs, LS);
     __syncthreads();
 
@@ -850,8 +892,14 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_chunk_kernel(
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       const int j = wave + 8 * x, rt = j >> 2, ct = j & 3;
-      const f32x4_t qk = mmx<BF, false, true>(zero4(), dQ + 16 * rt * LD, LD, Kg + 16 * ct * LD, LD, D);
-      const f32x4_t wk = mmx<BF, false, true>(zero4(), dW + 16 * rt * LD, LD, Kg + 16 * ct * LD, LD, D);
+      f32x4_t qk, wk;
+      if constexpr (BF) {
+        qk = mmb<D>(zero4(), dQB + 16 * rt * LDB, LDB, KgB + 16 * ct * LDB, LDB);
+        wk = mmb<D>(zero4(), dWB + 16 * rt * LDB, LDB, KgB + 16 * ct * LDB, LDB);
+      } else {
+        qk = mmx<BF, false, true>(zero4(), dQ + 16 * rt * LD, LD, Kg + 16 * ct * LD, LD, D);
+        wk = mmx<BF, false, true>(zero4(), dW + 16 * rt * LD, LD, Kg + 16 * ct * LD, LD, D);
+      }
       dPt[x] = acc[DT::XP + x];
       dTt[x] = acc[DT::XP + 2 + x];
 #pragma unroll
@@ -865,8 +913,14 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_chunk_kernel(
 #pragma unroll
     for (int x = 0; x < DT::NBIG / 8; ++x) {
       const int j = wave + 8 * x, rt = j / CT, ct = j - rt * CT;
-      const f32x4_t pq = mmx<BF, true, false>(zero4(), Ps + 16 * rt, LS, dQ + 16 * ct, LD, CR);
-      dkg[x] = mmx<BF, true, false>(zero4(), TBs + 16 * rt, LS, dW + 16 * ct, LD, CR);
+      f32x4_t pq;
+      if constexpr (BF) {
+        pq = mmb<CR>(zero4(), PT + 16 * rt * LT, LT, dQT + 16 * ct * LT, LT);
+        dkg[x] = mmb<CR>(zero4(), TBT + 16 * rt * LT, LT, dWT + 16 * ct * LT, LT);
+      } else {
+        pq = mmx<BF, true, false>(zero4(), Ps + 16 * rt, LS, dQ + 16 * ct, LD, CR);
+        dkg[x] = mmx<BF, true, false>(zero4(), TBs + 16 * rt, LS, dW + 16 * ct, LD, CR);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) dkg[x][i] -= pq[i];
     }
