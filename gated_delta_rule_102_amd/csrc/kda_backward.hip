@@ -36,6 +36,11 @@ namespace kda {
 namespace {
 
 // ---------------------------------------------------------------- scans
+// Each scan step loads the next chunk's operands before it issues its own global
+// stores. The step's memory operations form one fixed sequence without branches:
+// the next-chunk load is unconditional (the last step reloads its own chunk), and
+// rows past a chunk's end fall outside a store's buffer range instead of being
+// skipped by a branch.
 
 template <int D, typename TIn>
 __global__ __launch_bounds__(kScanThreads) void bwd_fwd_scan_kernel(const TIn* __restrict__ v,
@@ -101,7 +106,7 @@ __global__ __launch_bounds__(kScanThreads) void bwd_fwd_scan_kernel(const TIn* _
     }
     // the next chunk's loads go out before this step's stores: loads and stores
     // retire in order, so the next wait for those loads does not wait for the stores
-    if (c + 1 < sp.nch) issue(c + 1);
+    issue(min(c + 1, sp.nch - 1));   // unconditional: the last step reloads its own chunk
 #pragma unroll
     for (int x = 0; x < ST::NTW; ++x) {
       const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
@@ -229,7 +234,7 @@ __global__ __launch_bounds__(kScanThreads) void bwd_scan_kernel(const TIn* __res
         // out before this step's global stores, so no wait holds for those stores
       GTile<kScanThreads, CR, D> t_qp;
       t_qp.load(ws + item * L::WS + L::QP, D);
-      if (c > 0) issue(c - 1);
+      issue(c > 0 ? c - 1 : 0);   // unconditional: the last step reloads its own chunk
       t_qp.pin_all();
       t_qp.store(KQs, LD);
     }
@@ -357,7 +362,7 @@ __global__ __launch_bounds__(kScanThreads) void bwd_fwd_scan_bf16_kernel(
     stage_bf16_t(t_v, VT, L64);
     if (tid < D) Lm[tid] = lm;
     // the next chunk's loads go out before this step's global stores
-    if (c + 1 < sp.nch) issue(c + 1);
+    issue(min(c + 1, sp.nch - 1));   // unconditional: the last step reloads its own chunk
 #pragma unroll
     for (int x = 0; x < ST::NTW; ++x) {
       const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
@@ -465,7 +470,7 @@ __global__ __launch_bounds__(kScanThreads) void bwd_scan_bf16_kernel(
     stage_bf16_t(t_do, dOT, L64);
     if (tid < D) Lm[tid] = lm;
     // the previous chunk's loads go out before this step's global stores
-    if (c > 0) issue(c - 1);
+    issue(c > 0 ? c - 1 : 0);   // unconditional: the last step reloads its own chunk
 #pragma unroll
     for (int x = 0; x < ST::NTW; ++x) {
       const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
@@ -480,14 +485,18 @@ __global__ __launch_bounds__(kScanThreads) void bwd_scan_bf16_kernel(
       put_bf16(du + item * CR * D + 16 * rt * D + c0 + 16 * ct, D, u);
     }
     __syncthreads();
-    {   // dV = P^T dO + Tb^T dU
+    {   // dV = P^T dO + Tb^T dU; rows past the chunk's end fall outside the store
+        // range (no branch, so the stores per step are a fixed count)
       const int rt = wave >> 1, ct = wave & 1;
       f32x4_t acc = mmb<CR>(zero4(), PT + 16 * rt * L64, L64, dOT + 16 * ct * L64, L64);
       acc = mmb<CR>(acc, TBT + 16 * rt * L64, L64, dUT + 16 * ct * L64, L64);
+      const uint32_t rsb = static_cast<uint32_t>(H) * D * 2;   // token row stride (bytes)
+      const auto rdv = make_rsrc(dv + row0 * D, (nrow - 1) * rsb + D * 2);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 16 * rt + 4 * g4 + i;
-        if (t < nrow) dv[(row0 + static_cast<int64_t>(t) * H) * D + c0 + 16 * ct + l16] = Elem<bf16_t>::from(acc[i]);
+        __builtin_amdgcn_raw_buffer_store_b16(Elem<bf16_t>::from(acc[i]).bits, rdv,
+                                              t * rsb + (c0 + 16 * ct + l16) * 2, 0, 0);
       }
     }
 #pragma unroll

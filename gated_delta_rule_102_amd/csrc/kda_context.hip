@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kScanThreads) void transition_scan_bf16_kernel(
     t_w.store(Ws, LB);
     t_ktt.store(KTT, L64);
     if (tid < D) Lm[tid] = lm;
-    if (c + 1 < nc) issue(c + 1);
+    issue(min(c + 1, nc - 1));   // unconditional: the last step reloads its own chunk
 #pragma unroll
     for (int x = 0; x < ST::NTW; ++x) {
       const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kScanThreads) void exact_scan_kernel(const float* _
     t_kt.store(KTs, LD);
     t_v.store(Vs, LV);
     if (tid < D) Lm[tid] = lm;
-    if (c + 1 < sp.nch) issue(c + 1);
+    issue(min(c + 1, sp.nch - 1));   // unconditional: the last step reloads its own chunk
 #pragma unroll
     for (int x = 0; x < ST::NTW; ++x) {
       const int rt = ST::rt(wave, x), ct = ST::ct(wave, x);
