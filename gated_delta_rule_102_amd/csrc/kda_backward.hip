@@ -35,6 +35,14 @@ namespace kda {
 
 namespace {
 
+// One element through a buffer range (stores past the range are dropped).
+__device__ __forceinline__ void store_elem(bf16_t x, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b16(x.bits, r, off, 0, 0);
+}
+__device__ __forceinline__ void store_elem(float x, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, x), r, off, 0, 0);
+}
+
 // ---------------------------------------------------------------- scans
 // Each scan step loads the next chunk's operands before it issues its own global
 // stores. The step's memory operations form one fixed sequence without branches:
@@ -1088,6 +1096,10 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_chunk_kernel(
     // the element inputs of two tiles are loaded first (rows clamped into the chunk,
     // all loads in flight together), then those elements are formed and stored
     constexpr int XG = 2;
+    const uint32_t rsb = static_cast<uint32_t>(H) * D * static_cast<uint32_t>(sizeof(TIn));
+    const uint32_t range = (p.nrow - 1) * rsb + D * static_cast<uint32_t>(sizeof(TIn));
+    const auto rdq = make_rsrc(dq + p.row0 * D, range);
+    const auto rdk = make_rsrc(dk + p.row0 * D, range);
 #pragma unroll
     for (int x0 = 0; x0 < NTD; x0 += XG) {
       float eG[XG][4], eq[XG][4], ek[XG][4];
@@ -1133,10 +1145,10 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_chunk_kernel(
           const float dkv = kg + kt + XA + ZA + ZM;
           Ko[t * LD + col] = qv * dqv + kv * (kg + XA - kt - ZA - ZM);
           Qo[t * LD + col] = kv * kt;
-          if (ok) {
-            dq[(p.row0 + static_cast<int64_t>(t) * H) * D + col] = Elem<TIn>::from(dqv);
-            dk[(p.row0 + static_cast<int64_t>(t) * H) * D + col] = Elem<TIn>::from(dkv);
-          }
+          // rows past the chunk's end fall outside the store ranges (no branch)
+          const uint32_t off = t * rsb + col * static_cast<uint32_t>(sizeof(TIn));
+          store_elem(Elem<TIn>::from(dqv), rdq, off);
+          store_elem(Elem<TIn>::from(dkv), rdk, off);
         }
       }
     }
@@ -1162,13 +1174,14 @@ __global__ __launch_bounds__(kNnThreads) void bwd_grad_chunk_kernel(
       segk[sg * D + c] = sk;
       if (tid < D) base[tid] = dlam * w[L::LAM + tid];
       __syncthreads();
+      const auto rdg = make_rsrc(dg + p.row0 * D, range);   // rows past the end: dropped
       float run = base[c];
 #pragma unroll
       for (int u = 0; u < NSEG; ++u) run += segq[u * D + c] + (u > sg ? segk[u * D + c] : 0.f);
 #pragma unroll
       for (int t = SR - 1; t >= 0; --t) {
         run += Ko[(t0 + t) * LD + c];
-        if (t0 + t < p.nrow) dg[(p.row0 + static_cast<int64_t>(t0 + t) * H) * D + c] = Elem<TIn>::from(run);
+        store_elem(Elem<TIn>::from(run), rdg, (t0 + t) * rsb + c * static_cast<uint32_t>(sizeof(TIn)));
       }
     }
   }
